@@ -1,0 +1,213 @@
+"""Seeded synthetic inputs for the QEvict decode path.
+
+This module only draws numbers: it holds none of the method's arithmetic (no
+attention, no scores, no quantization, no routing).  Both the HIP path and the
+fp64 oracle are fed from it, so the two always see identical bf16 bytes.
+
+Recipe (the pages publish no inputs; these stand in for their workloads):
+
+* Every value is a float32 ``standard_normal`` draw rounded once to bf16
+  (round-to-nearest-even, as ``torch.Tensor.to(torch.bfloat16)`` does).
+* Outliers: per (layer, kv-head), ``n_outlier`` key channels drawn without
+  replacement are multiplied by 10 before the bf16 rounding.
+* Planted topics: ``n_topics`` disjoint prompt windows outside the sinks and the
+  final recent region.  Per (layer, sequence, kv-head, topic) a unit direction
+  ``u`` is drawn and the keys of that window get ``beta * u`` added (beta = 8).
+* Drift: decode query ``t`` of q-head ``h`` is ``cos(phi) g + sin(phi) sqrt(d) u``
+  where ``g ~ N(0, I)`` and ``u`` is the direction of topic ``(t // period) mod
+  n_topics`` for the head's kv group; ``phi`` ramps linearly from 0 to 60
+  degrees over the first half of each period and then holds.
+* Prompt queries are plain ``N(0, 1)``.
+
+Streams are keyed by ``(seed, layer, sequence, stream-id)`` so any slice can be
+regenerated on its own (``torch.Generator`` seeded from a hash of the key).
+"""
+from __future__ import annotations
+
+import hashlib
+import math
+from dataclasses import dataclass, field, replace
+from typing import Optional, Sequence
+
+import torch
+
+# stream ids
+_S_QP, _S_KP, _S_VP, _S_QD, _S_KD, _S_VD, _S_OUT, _S_TOPIC_WIN, _S_TOPIC_DIR, _S_LEN = range(10)
+
+
+@dataclass(frozen=True)
+class Workload:
+    """Shape and schedule of one synthetic QEvict decode workload."""
+
+    name: str
+    n_layers: int
+    batch: int
+    h_q: int
+    h_kv: int
+    d_head: int
+    prompt_len: int            # maximum prompt length
+    n_decode: int              # generated tokens
+    window: int
+    n_sink: int
+    n_local: int
+    omega: int
+    budget_frac: float
+    quant_frac: float
+    prompt_len_min: Optional[int] = None   # ragged prompts ~ U[min, max] when set
+    n_outlier: int = 0
+    n_topics: int = 0
+    topic_period: int = 64
+    beta: float = 8.0
+    seed: int = 0
+
+    def prompt_lens(self) -> list[int]:
+        """Per-sequence prompt lengths (ragged when ``prompt_len_min`` is set)."""
+        if self.prompt_len_min is None:
+            return [self.prompt_len] * self.batch
+        g = _gen(self.seed, 0, 0, _S_LEN)
+        lo, hi = self.prompt_len_min, self.prompt_len
+        return [int(x) for x in torch.randint(lo, hi + 1, (self.batch,), generator=g)]
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+# The five workloads of the decode benchmark.  Sinks / recent sizes that a
+# workload does not name are taken from the 32K one (4 sinks, 256 recent).
+TINY = Workload("tiny_512p64", 1, 1, 4, 1, 64, 512, 64, 16, 4, 64, 8, 0.40, 0.70)
+LLAMA8B_32K = Workload("llama8b_32k", 32, 1, 32, 8, 128, 32768, 512, 32, 4, 256, 8, 0.20, 0.70,
+                       n_outlier=4, n_topics=8, topic_period=64)
+BATCHED_16K = Workload("batched_8k16k_b16", 32, 16, 32, 8, 128, 16384, 256, 32, 4, 256, 8, 0.25, 0.70,
+                       prompt_len_min=8192, n_outlier=4, n_topics=8, topic_period=32)
+CHURN_4K = Workload("churn_4k_4096gen_b64", 32, 64, 32, 8, 128, 4096, 4096, 16, 4, 256, 8, 0.15, 0.70,
+                    n_outlier=4, n_topics=8, topic_period=256)
+LLAMA70B_128K = Workload("llama70b_128k_b4", 80, 4, 64, 8, 128, 131072, 256, 64, 4, 512, 8, 0.10, 0.70,
+                         n_outlier=4, n_topics=16, topic_period=16)
+
+ALL_WORKLOADS = (TINY, LLAMA8B_32K, BATCHED_16K, CHURN_4K, LLAMA70B_128K)
+
+
+def _gen(seed: int, layer: int, b: int, stream: int, device="cpu") -> torch.Generator:
+    key = f"{seed}/{layer}/{b}/{stream}".encode()
+    s = int.from_bytes(hashlib.sha256(key).digest()[:8], "little") & ((1 << 63) - 1)
+    g = torch.Generator(device=device)
+    g.manual_seed(s)
+    return g
+
+
+def _normal(shape, gen, device) -> torch.Tensor:
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+
+
+def _topic_windows(wl: Workload, layer: int, b: int, prompt_len: int) -> list[int]:
+    """Disjoint prompt windows (indices) that carry a planted topic direction."""
+    if wl.n_topics == 0:
+        return []
+    n_hist = (prompt_len - wl.n_local - wl.n_sink) // wl.window
+    if n_hist < wl.n_topics:
+        return []
+    g = _gen(wl.seed, layer, b, _S_TOPIC_WIN)
+    perm = torch.randperm(n_hist, generator=g)[: wl.n_topics]
+    return sorted(int(x) for x in perm)
+
+
+def _topic_dirs(wl: Workload, layer: int, b: int, device) -> torch.Tensor:
+    """Unit directions [h_kv][n_topics][d] (float32)."""
+    g = _gen(wl.seed, layer, b, _S_TOPIC_DIR, "cpu")
+    u = torch.randn((wl.h_kv, max(wl.n_topics, 1), wl.d_head), generator=g, dtype=torch.float64)
+    u = u / u.norm(dim=-1, keepdim=True)
+    return u.to(torch.float32).to(device)
+
+
+def _outlier_channels(wl: Workload, layer: int) -> torch.Tensor:
+    g = _gen(wl.seed, layer, 0, _S_OUT)
+    rows = [torch.randperm(wl.d_head, generator=g)[: wl.n_outlier] for _ in range(wl.h_kv)]
+    return torch.stack(rows) if rows and wl.n_outlier > 0 else torch.zeros((wl.h_kv, 0), dtype=torch.long)
+
+
+def prompt(wl: Workload, layer: int, device="cpu") -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Prompt tensors for one layer, bf16, zero-padded past each prompt length.
+
+    Returns ``q [B][H_q][S][d]``, ``k, v [B][H_kv][S][d]`` with ``S = wl.prompt_len``.
+    """
+    S, d = wl.prompt_len, wl.d_head
+    lens = wl.prompt_lens()
+    gen_dev = device if str(device).startswith("cuda") else "cpu"
+    qs, ks, vs = [], [], []
+    outl = _outlier_channels(wl, layer)
+    for b in range(wl.batch):
+        q = _normal((wl.h_q, S, d), _gen(wl.seed, layer, b, _S_QP, gen_dev), gen_dev)
+        k = _normal((wl.h_kv, S, d), _gen(wl.seed, layer, b, _S_KP, gen_dev), gen_dev)
+        v = _normal((wl.h_kv, S, d), _gen(wl.seed, layer, b, _S_VP, gen_dev), gen_dev)
+        if wl.n_outlier:
+            for h in range(wl.h_kv):
+                k[h][:, outl[h].to(k.device)] *= 10.0
+        tw = _topic_windows(wl, layer, b, lens[b])
+        if tw:
+            u = _topic_dirs(wl, layer, b, k.device)
+            for j, w in enumerate(tw):
+                s0 = wl.n_sink + w * wl.window
+                k[:, s0:s0 + wl.window, :] += wl.beta * u[:, j:j + 1, :]
+        L = lens[b]
+        if L < S:
+            q[:, L:, :] = 0
+            k[:, L:, :] = 0
+            v[:, L:, :] = 0
+        qs.append(q.to(torch.bfloat16))
+        ks.append(k.to(torch.bfloat16))
+        vs.append(v.to(torch.bfloat16))
+    return (torch.stack(qs).to(device), torch.stack(ks).to(device), torch.stack(vs).to(device))
+
+
+def _phase(wl: Workload, step: int) -> tuple[int, float]:
+    P = max(wl.topic_period, 1)
+    j = (step // P) % max(wl.n_topics, 1)
+    r = (step % P) / (P / 2.0)
+    phi = math.radians(60.0) * min(r, 1.0)
+    return j, phi
+
+
+def decode_step(wl: Workload, layer: int, step: int, device="cpu") -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Decode inputs for one step of one layer: ``q [B][H_q][d]``, ``k, v [B][H_kv][d]`` (bf16)."""
+    d = wl.d_head
+    gen_dev = device if str(device).startswith("cuda") else "cpu"
+    G = wl.h_q // wl.h_kv
+    outl = _outlier_channels(wl, layer)
+    qs, ks, vs = [], [], []
+    for b in range(wl.batch):
+        # one generator per (layer, b, step) so steps are independent slices
+        gq = _gen(wl.seed, layer, b * 1_000_003 + step, _S_QD, gen_dev)
+        gk = _gen(wl.seed, layer, b * 1_000_003 + step, _S_KD, gen_dev)
+        gv = _gen(wl.seed, layer, b * 1_000_003 + step, _S_VD, gen_dev)
+        q = _normal((wl.h_q, d), gq, gen_dev)
+        k = _normal((wl.h_kv, d), gk, gen_dev)
+        v = _normal((wl.h_kv, d), gv, gen_dev)
+        if wl.n_outlier:
+            for h in range(wl.h_kv):
+                k[h][outl[h].to(k.device)] *= 10.0
+        if wl.n_topics:
+            j, phi = _phase(wl, step)
+            u = _topic_dirs(wl, layer, b, q.device)[:, j, :]          # [h_kv][d]
+            uq = u.repeat_interleave(G, dim=0)                        # [h_q][d]
+            q = math.cos(phi) * q + math.sin(phi) * math.sqrt(d) * uq
+        qs.append(q.to(torch.bfloat16))
+        ks.append(k.to(torch.bfloat16))
+        vs.append(v.to(torch.bfloat16))
+    return (torch.stack(qs).to(device), torch.stack(ks).to(device), torch.stack(vs).to(device))
+
+
+def init_scores(wl: Workload, layer: int, n_windows: int, device="cpu") -> torch.Tensor:
+    """Synthetic initial window scores ``[B][n_windows]`` (float64), for callers that
+    supply their own prefill estimate instead of the prompt-attention column sums.
+
+    Drawn as |N(0,1)| * 10 so ties have probability zero; planted topic windows get +100.
+    """
+    out = torch.empty((wl.batch, n_windows), dtype=torch.float64)
+    lens = wl.prompt_lens()
+    for b in range(wl.batch):
+        g = _gen(wl.seed, layer, b, _S_LEN + 1)
+        out[b] = torch.randn((n_windows,), generator=g, dtype=torch.float64).abs() * 10.0
+        for w in _topic_windows(wl, layer, b, lens[b]):
+            if w < n_windows:
+                out[b, w] += 100.0
+    return out.to(device)

@@ -1,0 +1,101 @@
+"""Plant plausible mistakes in the oracle (on the CPU, via monkeypatch) and check
+that at least one pin catches each of them."""
+import numpy as np
+import pytest
+
+from oracle import qevict_oracle as O
+from tests import test_oracle_codec as TC
+from tests import test_oracle_state as TS
+
+
+def _fails(fn, *args):
+    with pytest.raises((AssertionError, ValueError)):
+        fn(*args)
+
+
+def test_swapped_tier_shares_are_caught(monkeypatch):
+    real = O.capacities
+
+    def swapped(cfg, prompt_len):
+        c = real(cfg, prompt_len)
+        c["K_f"] = int(np.floor(cfg.quant_frac * c["B_hist"] / c["M_f"]))
+        c["K_q"] = int(np.floor((1 - cfg.quant_frac) * c["B_hist"] / c["M_q"]))
+        return c
+
+    monkeypatch.setattr(O, "capacities", swapped)
+    _fails(TS.test_quant_share_goes_to_quantized_tier)
+
+
+def test_missing_param_bytes_are_caught(monkeypatch):
+    monkeypatch.setattr(O, "quant_window_bytes", lambda cfg: cfg.window * cfg.h_kv * cfg.d // 2 + 20)
+    _fails(TS.test_printed_diagnostic_capacities)
+
+
+def test_wrong_logit_scale_is_caught(monkeypatch):
+    real = O.softmax
+    monkeypatch.setattr(O, "softmax", lambda x, axis=-1: real(x * 1.25, axis))
+    _fails(TS.test_dense_equivalence_when_budget_covers_cache)
+
+
+def test_reversed_tie_break_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "route_order", lambda cand, s: sorted(cand, key=lambda w: (-s[w], -w)))
+    _fails(TS.test_route_order_equals_full_sort_and_heap_selection)
+
+
+def test_nearest_offset_rounding_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "rd_fp16", lambda x: np.asarray(x, np.float64).astype(np.float16).astype(np.float64))
+    _fails(TC.test_group_quantization_exact_definition)
+
+
+def test_ties_down_code_rounding_is_caught(monkeypatch):
+    real = O.quantize_groups
+
+    def ties_down(x, axis):
+        codes, off, scl = real(x, axis)
+        t = 2.0 * (np.asarray(x, np.float64) - np.expand_dims(off, axis))
+        s = np.expand_dims(scl, axis)
+        c2 = (t > s).astype(np.uint8) + (t > 3 * s) + (t > 5 * s)
+        return np.where(s == 0, 0, c2).astype(np.uint8), off, scl
+
+    monkeypatch.setattr(O, "quantize_groups", ties_down)
+    _fails(TC.test_midpoints_round_up)
+
+
+def test_row_sums_instead_of_column_sums_are_caught(monkeypatch):
+    real = O.prefill_column_sums
+
+    def rows(qp, kp):
+        col = real(qp, kp)
+        S = col.shape[1]
+        return np.ones_like(col) * (S / S)                 # every row of a softmax sums to one
+
+    monkeypatch.setattr(O, "prefill_column_sums", rows)
+    _fails(TS.test_prefill_scores_against_torch_column_sums)
+
+
+def test_missing_head_average_is_caught(monkeypatch):
+    real_decode = O.UnitOracle.decode
+
+    def no_avg(self, q, k, v):
+        before = dict(self.score)
+        out = real_decode(self, q, k, v)
+        for w, u in out["mass"].items():
+            self.score[w] = before.get(w, 0.0) + u * self.cfg.h_q
+            out["mass"][w] = u * self.cfg.h_q
+        return out
+
+    monkeypatch.setattr(O.UnitOracle, "decode", no_avg)
+    _fails(TS.test_window_mass_against_independent_softmax)
+
+
+def test_requantizing_on_redemotion_is_caught(monkeypatch):
+    real_route = O.UnitOracle.route
+
+    def requant(self):
+        for W in self.win.values():
+            if W.state == O.FULL and W.ledger is not None:
+                W.ledger = None                       # forget the write-once record
+        return real_route(self)
+
+    monkeypatch.setattr(O.UnitOracle, "route", requant)
+    _fails(TS.test_write_once_ledger_and_promoted_values)
