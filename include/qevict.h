@@ -1,0 +1,215 @@
+/*
+ * qevict.h — C ABI of the MI355X (gfx950) QEvict decode hot path.
+ *
+ * QEvict keeps a per-layer KV cache as a protected sink prefix, a protected
+ * recent region and fixed-size windows of W tokens, each window in one of
+ * three tiers: Full (bf16), Quantized (INT2, recoverable) or Evicted.
+ * Source: "QEvict: Recoverable Quantized KV Eviction for Attention-Drift-Robust
+ * Long-Context Decoding" (arXiv 2608.05326), §4.1-§4.3 and Appendix A
+ * (Algorithm 1); byte accounting Appendix B.4.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked [host].
+ *   - The caller owns all memory.  The library never allocates device memory:
+ *     qevict_plan() reports the sizes, the caller allocates them (e.g. with
+ *     PyTorch) and passes them in.  Host-side bookkeeping (the qevict_state
+ *     object, a few hundred bytes) is the only allocation the library makes.
+ *   - Work is enqueued on the caller's `stream` (a hipStream_t, passed as
+ *     void*; NULL = the default stream).  Only the calls marked "syncs" wait.
+ *   - Argument and shape errors return a negative qevict_status at once and
+ *     enqueue nothing; qevict_last_error() then holds a message for the
+ *     calling thread.  Errors found on the device (pool overflow, a decode
+ *     step that runs past the windows prepared by the last route, an fp16
+ *     range overflow while quantizing) set bits of a per-(sequence, layer)
+ *     status word that qevict_poll_status() reads.
+ *   - bf16 tensors are raw 16-bit bfloat16 values; fp32 outputs are IEEE float.
+ *   - Calls for different layers touch disjoint state and may run on different
+ *     streams concurrently; calls for one layer must be ordered on one stream.
+ */
+#ifndef QEVICT_H
+#define QEVICT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QEVICT_OK = 0,
+    QEVICT_E_INVALID = -1,   /* bad argument, unsupported shape */
+    QEVICT_E_BUDGET = -2,    /* protected regions exceed the budget: B_hist < 0 (§4.3 Eq. 3) */
+    QEVICT_E_CAPACITY = -3,  /* a buffer is smaller than qevict_plan() requires */
+    QEVICT_E_RANGE = -4,     /* value outside the fp16 range of the quantization parameters */
+    QEVICT_E_STATE = -5,     /* call out of order (e.g. decode before prefill) */
+    QEVICT_E_HIP = -6        /* a HIP runtime call failed */
+} qevict_status;
+
+/* device status bits (qevict_poll_status) */
+#define QEVICT_DEV_E_POOL   1u   /* page or slot pool exhausted */
+#define QEVICT_DEV_E_WINDOW 2u   /* decode wrote past the windows prepared by the last route */
+#define QEVICT_DEV_E_RANGE  4u   /* |x| > 65504 in a window being quantized */
+#define QEVICT_DEV_E_LIST   8u   /* accessible list or work list overflow */
+
+/* flags */
+#define QEVICT_F_NO_PROMOTE        1u  /* one-way variant Full -> Quantized -> Evicted (App. K) */
+#define QEVICT_F_SCORE_ROUTE_ONLY  2u  /* accumulate Eq. 1 only at the routing step itself */
+
+typedef struct {
+    int32_t batch;        /* B sequences */
+    int32_t n_layers;     /* L */
+    int32_t h_q;          /* query heads; h_q % h_kv == 0, h_q / h_kv in {1,2,4,8} */
+    int32_t h_kv;         /* KV heads (GQA groups) */
+    int32_t d_head;       /* 64 or 128 */
+    int32_t window;       /* W tokens per window: 16, 32 or 64 */
+    int32_t n_sink;       /* protected sink prefix, 0 < n_sink <= 64 */
+    int32_t n_local;      /* R_loc: protected recent tokens (nominal) */
+    int32_t omega;        /* routing interval (generated tokens between routing events) */
+    double quant_frac;    /* q: share of the historical budget given to the Quantized tier */
+    double budget_frac;   /* rho: KV budget as a fraction of the full bf16 cache */
+    int32_t max_prompt;   /* S_max: prompt buffers are [..][S_max][d] */
+    int32_t max_new;      /* N_g: generated tokens; B_total covers prompt_len + max_new */
+    uint32_t flags;       /* QEVICT_F_* */
+    int32_t n_splits;     /* decode splits per (sequence, KV head); 0 = choose */
+} qevict_config;
+
+typedef struct {
+    size_t arena_bytes;          /* one device buffer holding all persistent state */
+    size_t prefill_ws_bytes;     /* device workspace for qevict_prefill_init (reusable across layers) */
+    size_t export_bytes;         /* host buffer size for qevict_export_unit */
+    int32_t n_windows;           /* window slots per (sequence, layer) */
+    int32_t n_pages;             /* bf16 pages per (sequence, layer) */
+    int32_t n_slots;             /* INT2 slots per (sequence, layer) */
+    int32_t n_acc_max;           /* accessible-list capacity */
+    int32_t n_splits;            /* decode splits actually used */
+    int32_t max_K_f, max_K_q;    /* largest capacities over the batch */
+} qevict_plan_info;
+
+typedef struct qevict_state qevict_state;
+
+/*
+ * Tier capacities of one sequence (§4.3 Eq. 3, budget inequality of §4.1):
+ *   b_tok   = 4 * h_kv * d_head                       bf16 K+V bytes per token
+ *   B_total = budget_frac * b_tok * (prompt_len + max_new)
+ *   B_hist  = B_total - (n_sink + n_local) * b_tok
+ *   M_f     = W * b_tok + 8
+ *   M_q     = W*h_kv*d/2 (codes) + 4*h_kv*d (K off/scl) + 4*W*h_kv (V off/scl) + 4 + 16
+ *   K_f     = floor((1 - q) * B_hist / M_f),  K_q = floor(q * B_hist / M_q)
+ * All outputs [host].  Returns QEVICT_E_BUDGET when B_hist < 0.  Accepts any
+ * positive geometry (accounting only); qevict_plan checks what the kernels support.
+ */
+qevict_status qevict_capacities(const qevict_config* cfg, int32_t prompt_len,
+                                int32_t* K_f, int32_t* K_q, double* B_total, double* B_hist,
+                                int64_t* M_f, int64_t* M_q);
+
+/* Sizes of every buffer for `cfg` and the per-sequence prompt lengths
+ * prompt_lens[host][batch] (each in [0, max_prompt]).  out [host]. */
+qevict_status qevict_plan(const qevict_config* cfg, const int32_t* prompt_lens,
+                          qevict_plan_info* out);
+
+/* Bind a state object to a caller-allocated arena of >= plan.arena_bytes
+ * (256-byte aligned).  Enqueues the arena's initialisation on `stream`.
+ * *out [host] receives a handle owned by the caller (qevict_destroy). */
+qevict_status qevict_create(const qevict_config* cfg, const int32_t* prompt_lens,
+                            void* arena, size_t arena_bytes, void* stream, qevict_state** out);
+void qevict_destroy(qevict_state* st);
+
+/*
+ * Prefill of one layer (§4.2, last paragraph: prompt attention initialises the
+ * window scores and the first tier assignment).
+ *   q_prompt [B][h_q][S_max][d], k_prompt / v_prompt [B][h_kv][S_max][d] bf16;
+ *   rows >= prompt_lens[b] are ignored.
+ *   score_init: NULL -> S_bar_0(w) = (1/h_q) sum_h sum_{u} sum_{t in w} P_h[u, t],
+ *     the causal prompt-attention column sums (MFMA kernels, fp32 inside a
+ *     tile, fp64 across tiles); otherwise a device array [B][n_windows] of
+ *     fp64 initial scores supplied by the caller (any ranking estimator; the
+ *     hierarchy only needs an order, App. J).
+ *   workspace: >= plan.prefill_ws_bytes of device scratch, free after the call
+ *     completes on `stream`.  When the column sums run it holds, from offset 0,
+ *     the row log-sum-exps in log2 units, fp32 [B][h_q][S_max], then (at the
+ *     next 256-byte boundary) the per-head column sums, fp64 [B][h_q][S_max].
+ * Then routes the aged prompt windows (Eqs. 4-5), packs the Quantized ones
+ * (INT2, write-once) and copies the Full and recent ones into bf16 pages.
+ */
+qevict_status qevict_prefill_init(qevict_state* st, int32_t layer,
+                                  const void* q_prompt, const void* k_prompt, const void* v_prompt,
+                                  const double* score_init, void* workspace, size_t ws_bytes,
+                                  void* stream);
+
+/*
+ * One decode step of one layer (§4.1 accessible-set attention, §4.2 Eq. 1).
+ *   q [B][h_q][d], k_new / v_new [B][h_kv][d] bf16: the new token's query, key, value.
+ *   out [B][h_q][d] fp32: o = softmax(q K_acc^T / sqrt(d)) V_acc over sinks, the
+ *     recent region, Full windows (bf16) and Quantized windows (INT2 values
+ *     off + code * scl, dequantized in registers).
+ * Appends k_new / v_new at position n (recent region), attends, and adds each
+ * accessible window's head-averaged attention mass to its score S_bar(w).
+ */
+qevict_status qevict_decode_attn(qevict_state* st, int32_t layer, const void* q,
+                                 const void* k_new, const void* v_new, float* out, void* stream);
+
+/*
+ * Routing event (§4.3 Eqs. 4-6, Algorithm 1), for one layer or all (layer = -1).
+ * Candidates = Full ∪ Quantized ∪ recent windows whose end is <= n - n_local;
+ * ordered by (S_bar descending, window index ascending); the first K_f become
+ * Full, the next K_q Quantized, the rest Evicted.  Q->F dequantizes the ledger
+ * into a bf16 page and marks it dormant; a first entry into Q packs INT2 codes
+ * once; a dormant ledger is reactivated; Evicted windows release everything.
+ * Also prepares recent-region windows for the next omega positions and
+ * rebuilds the chronological accessible list.  Call after the decode step
+ * j with (j + 1) % omega == 0.
+ */
+qevict_status qevict_route(qevict_state* st, int32_t layer, void* stream);
+
+/*
+ * Demote chosen windows to the Quantized tier (first time: pack INT2 codes and
+ * create the ledger; dormant ledger: reactivate) and release their bf16 pages.
+ * win_ids [B][n] int32 device array, -1 = unused entry; windows must be Full
+ * or aged recent windows.  Capacities are not enforced here: this is the
+ * migration step alone, for callers with their own policy.
+ */
+qevict_status qevict_pack_int2(qevict_state* st, int32_t layer, const int32_t* win_ids, int32_t n,
+                               void* stream);
+
+/* Promote chosen Quantized windows to Full: bf16(off + code*scl), rounded to
+ * nearest-even from the exact value, into a free page; the ledger becomes
+ * dormant (write-once, §4.3).  win_ids as for qevict_pack_int2. */
+qevict_status qevict_promote(qevict_state* st, int32_t layer, const int32_t* win_ids, int32_t n,
+                             void* stream);
+
+/* OR of the device status words of every (sequence, layer) into *status [host].  Syncs. */
+qevict_status qevict_poll_status(qevict_state* st, uint32_t* status, void* stream);
+
+/*
+ * Canonical export of one (sequence b, layer) unit into host_buf [host] of
+ * >= plan.export_bytes.  Syncs `stream`.  Layout (little endian):
+ *   header 20 x int32: magic 0x58564551, n, n_windows_created, K_f, K_q,
+ *     status, counters[8] of the last routing event (aged, promoted, packed,
+ *     reactivated, demoted, evicted, n_full, n_quant), n_acc, prompt_len,
+ *     fp64 head-averaged prefill attention mass on the sink prefix (2 words),
+ *     2 reserved words
+ *   per window w < n_windows_created: int32 state (1 recent, 2 Full,
+ *     3 Quantized, 4 Evicted), int32 has_ledger, int32 dormant, int32 start_pos,
+ *     fp64 score
+ *   per window with a ledger, in window order: per KV head: K codes [W][d/4],
+ *     V codes [W][d/4] (element (i,c) at byte c/4, bits 2(c%4)), K off [d],
+ *     K scl [d], V off [W], V scl [W] (fp16)
+ *   per window in state 1 or 2, in window order: bf16 K [h_kv][W][d] then V
+ *   sink K [h_kv][n_sink][d] then V (bf16)
+ * *written [host] receives the byte count.
+ */
+qevict_status qevict_export_unit(qevict_state* st, int32_t layer, int32_t b, void* host_buf,
+                                 size_t bytes, size_t* written, void* stream);
+
+/* Number of decode kernels launched per qevict_decode_attn call and the name of
+ * the dominant one, for profilers.  */
+const char* qevict_decode_kernel_name(void);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* qevict_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QEVICT_H */

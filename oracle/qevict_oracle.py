@@ -369,7 +369,8 @@ class UnitOracle:
             for w in self.win:
                 self.score[w] = float(score_init[w])
         else:
-            col = prefill_column_sums(qp, kp)                    # [H_q][S]
+            # an empty prompt has no attention rows and contributes no score
+            col = prefill_column_sums(qp, kp) if S > 0 else np.zeros((cfg.h_q, 0))
             info["col"] = col
             for w in self.win:
                 a, b = self.win_start(w), min(self.win_end(w), S)

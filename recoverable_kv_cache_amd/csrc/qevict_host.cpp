@@ -1,0 +1,476 @@
+// Host side of the C ABI: validation, byte accounting (Eq. 3), arena layout,
+// kernel launch order.  No device allocation happens here.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "qevict_internal.h"
+
+using namespace qv;
+
+namespace {
+
+thread_local std::string g_err;
+
+qevict_status fail(qevict_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+#define HIP_TRY(expr)                                                                      \
+    do {                                                                                   \
+        hipError_t e_ = (expr);                                                            \
+        if (e_ != hipSuccess) return fail(QEVICT_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Shape checks for the byte accounting alone (any positive geometry).
+qevict_status validate_accounting(const qevict_config* c) {
+    if (!c) return fail(QEVICT_E_INVALID, "null config");
+    if (c->h_kv < 1 || c->d_head < 4 || c->d_head % 4 || c->window < 1 || c->n_sink < 0 || c->n_local < 0)
+        return fail(QEVICT_E_INVALID, "bad geometry");
+    if (!(c->quant_frac >= 0.0 && c->quant_frac <= 1.0)) return fail(QEVICT_E_INVALID, "quant_frac must be in [0, 1]");
+    if (!(c->budget_frac > 0.0)) return fail(QEVICT_E_INVALID, "budget_frac must be > 0");
+    if (c->max_new < 0) return fail(QEVICT_E_INVALID, "max_new must be >= 0");
+    return QEVICT_OK;
+}
+
+// Shapes the kernels support.
+qevict_status validate(const qevict_config* c) {
+    if (!c) return fail(QEVICT_E_INVALID, "null config");
+    if (c->batch < 1 || c->n_layers < 1) return fail(QEVICT_E_INVALID, "batch and n_layers must be >= 1");
+    if (c->h_kv < 1 || c->h_q < c->h_kv || c->h_q % c->h_kv) return fail(QEVICT_E_INVALID, "h_q must be a multiple of h_kv");
+    int G = c->h_q / c->h_kv;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return fail(QEVICT_E_INVALID, "h_q / h_kv must be 1, 2, 4 or 8");
+    if (c->d_head != 64 && c->d_head != 128) return fail(QEVICT_E_INVALID, "d_head must be 64 or 128");
+    if (c->window != 16 && c->window != 32 && c->window != 64) return fail(QEVICT_E_INVALID, "window must be 16, 32 or 64");
+    if (c->n_sink < 0 || c->n_sink > 64) return fail(QEVICT_E_INVALID, "n_sink must be in [0, 64]");
+    if (c->n_local < 0) return fail(QEVICT_E_INVALID, "n_local must be >= 0");
+    if (c->omega < 1) return fail(QEVICT_E_INVALID, "omega must be >= 1");
+    if (!(c->quant_frac >= 0.0 && c->quant_frac <= 1.0)) return fail(QEVICT_E_INVALID, "quant_frac must be in [0, 1]");
+    if (!(c->budget_frac > 0.0)) return fail(QEVICT_E_INVALID, "budget_frac must be > 0");
+    if (c->max_prompt < 0 || c->max_new < 0) return fail(QEVICT_E_INVALID, "max_prompt / max_new must be >= 0");
+    if (c->n_splits < 0) return fail(QEVICT_E_INVALID, "n_splits must be >= 0");
+    return QEVICT_OK;
+}
+
+struct Caps {
+    int32_t K_f, K_q;
+    double B_total, B_hist;
+    int64_t M_f, M_q;
+};
+
+qevict_status caps_of(const qevict_config* c, int32_t prompt_len, Caps* out) {
+    const int64_t b_tok = 4LL * c->h_kv * c->d_head;
+    const double B_total = c->budget_frac * (double)b_tok * (double)(prompt_len + c->max_new);
+    const double B_hist = B_total - (double)((int64_t)(c->n_sink + c->n_local) * b_tok);
+    const int64_t W = c->window, H = c->h_kv, d = c->d_head;
+    const int64_t M_f = W * b_tok + 8;
+    const int64_t M_q = W * H * d / 2 + 4 * H * d + 4 * W * H + 4 + 16;
+    out->B_total = B_total;
+    out->B_hist = B_hist;
+    out->M_f = M_f;
+    out->M_q = M_q;
+    if (B_hist < 0) return fail(QEVICT_E_BUDGET, "B_hist = %.1f < 0: the protected regions exceed the budget", B_hist);
+    out->K_f = (int32_t)std::floor((1.0 - c->quant_frac) * B_hist / (double)M_f);
+    out->K_q = (int32_t)std::floor(c->quant_frac * B_hist / (double)M_q);
+    return QEVICT_OK;
+}
+
+struct Layout {
+    Geo g;
+    size_t off[20];
+    size_t total;
+    size_t export_bytes;
+    int32_t max_kf, max_kq;
+};
+
+enum { O_HDR, O_WIN, O_SCORE, O_ACC, O_SPLITS, O_FPAGE, O_FSLOT, O_PACK, O_FILL, O_TARGET, O_LSEW, O_LSEG,
+       O_PML, O_PACC, O_PAGES, O_SLOTS, O_SINKS, O_PLENS, O_KF, O_KQ };
+
+qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, Layout* lay) {
+    qevict_status s = validate(c);
+    if (s) return s;
+    if (!prompt_lens) return fail(QEVICT_E_INVALID, "null prompt_lens");
+    int32_t max_kf = 0, max_kq = 0;
+    for (int b = 0; b < c->batch; ++b) {
+        if (prompt_lens[b] < 0 || prompt_lens[b] > c->max_prompt)
+            return fail(QEVICT_E_INVALID, "prompt_lens[%d] = %d outside [0, %d]", b, prompt_lens[b], c->max_prompt);
+        Caps cp;
+        s = caps_of(c, prompt_lens[b], &cp);
+        if (s) return s;
+        max_kf = cp.K_f > max_kf ? cp.K_f : max_kf;
+        max_kq = cp.K_q > max_kq ? cp.K_q : max_kq;
+    }
+    Geo& g = lay->g;
+    g.B = c->batch; g.L = c->n_layers; g.h_q = c->h_q; g.h_kv = c->h_kv; g.d = c->d_head; g.W = c->window;
+    g.n_sink = c->n_sink; g.n_local = c->n_local; g.omega = c->omega; g.S_max = c->max_prompt; g.flags = c->flags;
+    const int64_t span = (int64_t)c->max_prompt + c->max_new + c->omega - c->n_sink;
+    g.n_windows = (int32_t)((span > 0 ? (span + g.W - 1) / g.W : 0) + 1);
+    if (g.n_windows > 4096) return fail(QEVICT_E_INVALID, "%d windows per unit exceed the router's 4096", g.n_windows);
+    const int32_t n_local_pages = (c->n_local + c->omega + g.W - 1) / g.W + 2;
+    g.n_pages = max_kf + n_local_pages + 1;
+    g.n_slots = max_kq + max_kf + 1;
+    g.n_acc_max = 1 + max_kf + max_kq + n_local_pages + 1;
+    if (g.n_acc_max > 4096) return fail(QEVICT_E_INVALID, "accessible list of %d exceeds 4096", g.n_acc_max);
+    int32_t ns = c->n_splits;
+    if (ns == 0) {
+        const int32_t par = g.B * g.h_kv;
+        ns = (512 + par - 1) / par;
+        int32_t cap = g.n_acc_max / 4;
+        if (cap < 1) cap = 1;
+        if (ns > cap) ns = cap;
+        if (ns < 1) ns = 1;
+    }
+    if (ns > 1024) ns = 1024;
+    g.n_splits = ns;
+    g.page_elems = g.h_kv * 2 * g.W * g.d;
+    g.slot_head_bytes = g.W * g.d / 2 + 4 * g.d + 4 * g.W;
+    g.slot_bytes = g.h_kv * g.slot_head_bytes;
+    g.sink_elems = g.h_kv * 2 * (g.n_sink > 0 ? g.n_sink : 1) * g.d;
+    const size_t U = (size_t)g.B * g.L;
+    size_t sz[20];
+    sz[O_HDR] = U * sizeof(UnitHdr);
+    sz[O_WIN] = U * g.n_windows * sizeof(WinRec);
+    sz[O_SCORE] = U * g.n_windows * sizeof(double);
+    sz[O_ACC] = U * g.n_acc_max * sizeof(AccEntry);
+    sz[O_SPLITS] = U * (g.n_splits + 1) * sizeof(int32_t);
+    sz[O_FPAGE] = U * g.n_pages * sizeof(int32_t);
+    sz[O_FSLOT] = U * g.n_slots * sizeof(int32_t);
+    sz[O_PACK] = U * g.n_windows * sizeof(PackItem);
+    sz[O_FILL] = U * g.n_windows * sizeof(FillItem);
+    sz[O_TARGET] = U * g.n_windows;
+    sz[O_LSEW] = U * g.n_acc_max * g.h_q * sizeof(float);
+    sz[O_LSEG] = U * g.h_q * sizeof(float);
+    sz[O_PML] = U * g.n_splits * g.h_q * sizeof(float2);
+    sz[O_PACC] = U * g.n_splits * g.h_q * g.d * sizeof(float);
+    sz[O_PAGES] = U * g.n_pages * (size_t)g.page_elems * 2;
+    sz[O_SLOTS] = U * g.n_slots * (size_t)g.slot_bytes;
+    sz[O_SINKS] = U * (size_t)g.sink_elems * 2;
+    sz[O_PLENS] = sz[O_KF] = sz[O_KQ] = g.B * sizeof(int32_t);
+    size_t at = 0;
+    for (int i = 0; i < 20; ++i) {
+        lay->off[i] = at;
+        at += align256(sz[i]);
+    }
+    lay->total = at;
+    lay->export_bytes = 80 + (size_t)g.n_windows * 24 + (size_t)g.n_windows * g.slot_bytes +
+                        (size_t)g.n_windows * g.page_elems * 2 + (size_t)g.sink_elems * 2;
+    lay->max_kf = max_kf;
+    lay->max_kq = max_kq;
+    return QEVICT_OK;
+}
+
+Bufs bind_bufs(const Layout& lay, void* arena) {
+    char* a = (char*)arena;
+    Bufs b;
+    b.hdr = (UnitHdr*)(a + lay.off[O_HDR]);
+    b.win = (WinRec*)(a + lay.off[O_WIN]);
+    b.score = (double*)(a + lay.off[O_SCORE]);
+    b.acc = (AccEntry*)(a + lay.off[O_ACC]);
+    b.splits = (int32_t*)(a + lay.off[O_SPLITS]);
+    b.free_pages = (int32_t*)(a + lay.off[O_FPAGE]);
+    b.free_slots = (int32_t*)(a + lay.off[O_FSLOT]);
+    b.pack = (PackItem*)(a + lay.off[O_PACK]);
+    b.fill = (FillItem*)(a + lay.off[O_FILL]);
+    b.target = (int8_t*)(a + lay.off[O_TARGET]);
+    b.lse_win = (float*)(a + lay.off[O_LSEW]);
+    b.lse_glob = (float*)(a + lay.off[O_LSEG]);
+    b.part_ml = (float2*)(a + lay.off[O_PML]);
+    b.part_acc = (float*)(a + lay.off[O_PACC]);
+    b.pages = (uint16_t*)(a + lay.off[O_PAGES]);
+    b.slots = (uint8_t*)(a + lay.off[O_SLOTS]);
+    b.sinks = (uint16_t*)(a + lay.off[O_SINKS]);
+    return b;
+}
+
+}  // namespace
+
+struct qevict_state {
+    qevict_config cfg;
+    Layout lay;
+    Bufs bf;
+    char* arena;
+    std::vector<int32_t> prompt_lens, K_f, K_q;
+    std::vector<int32_t> steps;
+    std::vector<uint8_t> prefilled;
+};
+
+extern "C" {
+
+const char* qevict_last_error(void) { return g_err.c_str(); }
+
+const char* qevict_decode_kernel_name(void) { return "qevict_decode_split"; }
+
+qevict_status qevict_capacities(const qevict_config* cfg, int32_t prompt_len, int32_t* K_f, int32_t* K_q,
+                                double* B_total, double* B_hist, int64_t* M_f, int64_t* M_q) {
+    qevict_status s = validate_accounting(cfg);
+    if (s) return s;
+    if (prompt_len < 0) return fail(QEVICT_E_INVALID, "prompt_len < 0");
+    Caps c;
+    s = caps_of(cfg, prompt_len, &c);
+    if (B_total) *B_total = c.B_total;
+    if (B_hist) *B_hist = c.B_hist;
+    if (M_f) *M_f = c.M_f;
+    if (M_q) *M_q = c.M_q;
+    if (s) return s;
+    if (K_f) *K_f = c.K_f;
+    if (K_q) *K_q = c.K_q;
+    return QEVICT_OK;
+}
+
+qevict_status qevict_plan(const qevict_config* cfg, const int32_t* prompt_lens, qevict_plan_info* out) {
+    if (!out) return fail(QEVICT_E_INVALID, "null output");
+    Layout lay;
+    qevict_status s = make_layout(cfg, prompt_lens, &lay);
+    if (s) return s;
+    out->arena_bytes = lay.total;
+    out->prefill_ws_bytes = prefill_ws_bytes(lay.g);
+    out->export_bytes = lay.export_bytes;
+    out->n_windows = lay.g.n_windows;
+    out->n_pages = lay.g.n_pages;
+    out->n_slots = lay.g.n_slots;
+    out->n_acc_max = lay.g.n_acc_max;
+    out->n_splits = lay.g.n_splits;
+    out->max_K_f = lay.max_kf;
+    out->max_K_q = lay.max_kq;
+    return QEVICT_OK;
+}
+
+qevict_status qevict_create(const qevict_config* cfg, const int32_t* prompt_lens, void* arena, size_t arena_bytes,
+                            void* stream, qevict_state** out) {
+    if (!out) return fail(QEVICT_E_INVALID, "null output handle");
+    *out = nullptr;
+    Layout lay;
+    qevict_status s = make_layout(cfg, prompt_lens, &lay);
+    if (s) return s;
+    if (!arena) return fail(QEVICT_E_INVALID, "null arena");
+    if ((uintptr_t)arena % 256) return fail(QEVICT_E_INVALID, "arena must be 256-byte aligned");
+    if (arena_bytes < lay.total)
+        return fail(QEVICT_E_CAPACITY, "arena of %zu bytes < %zu required", arena_bytes, lay.total);
+    qevict_state* st = new qevict_state();
+    st->cfg = *cfg;
+    st->lay = lay;
+    st->arena = (char*)arena;
+    st->bf = bind_bufs(lay, arena);
+    st->prompt_lens.assign(prompt_lens, prompt_lens + cfg->batch);
+    st->K_f.resize(cfg->batch);
+    st->K_q.resize(cfg->batch);
+    for (int b = 0; b < cfg->batch; ++b) {
+        Caps c;
+        caps_of(cfg, prompt_lens[b], &c);
+        st->K_f[b] = c.K_f;
+        st->K_q[b] = c.K_q;
+    }
+    st->steps.assign(cfg->n_layers, 0);
+    st->prefilled.assign(cfg->n_layers, 0);
+    hipStream_t hs = (hipStream_t)stream;
+    char* a = (char*)arena;
+    hipError_t e = hipMemcpyAsync(a + lay.off[O_PLENS], st->prompt_lens.data(), cfg->batch * 4, hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(a + lay.off[O_KF], st->K_f.data(), cfg->batch * 4, hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(a + lay.off[O_KQ], st->K_q.data(), cfg->batch * 4, hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess)
+        e = launch_init(lay.g, st->bf, (const int32_t*)(a + lay.off[O_PLENS]), (const int32_t*)(a + lay.off[O_KF]),
+                        (const int32_t*)(a + lay.off[O_KQ]), hs);
+    if (e == hipSuccess) e = hipStreamSynchronize(hs);   // host vectors above are pageable
+    if (e != hipSuccess) {
+        delete st;
+        return fail(QEVICT_E_HIP, "init: %s", hipGetErrorString(e));
+    }
+    *out = st;
+    return QEVICT_OK;
+}
+
+void qevict_destroy(qevict_state* st) { delete st; }
+
+static qevict_status check_layer(qevict_state* st, int32_t layer, bool allow_all) {
+    if (!st) return fail(QEVICT_E_INVALID, "null state");
+    if (allow_all && layer == -1) return QEVICT_OK;
+    if (layer < 0 || layer >= st->cfg.n_layers) return fail(QEVICT_E_INVALID, "layer %d out of range", layer);
+    return QEVICT_OK;
+}
+
+qevict_status qevict_prefill_init(qevict_state* st, int32_t layer, const void* q_prompt, const void* k_prompt,
+                                  const void* v_prompt, const double* score_init, void* workspace, size_t ws_bytes,
+                                  void* stream) {
+    qevict_status s = check_layer(st, layer, false);
+    if (s) return s;
+    if (st->prefilled[layer]) return fail(QEVICT_E_STATE, "layer %d already initialised", layer);
+    if (st->cfg.max_prompt > 0 && (!k_prompt || !v_prompt))
+        return fail(QEVICT_E_INVALID, "null prompt key/value buffer");
+    if (!score_init) {
+        if (st->cfg.max_prompt > 0 && !q_prompt) return fail(QEVICT_E_INVALID, "null prompt query buffer");
+        if (ws_bytes < prefill_ws_bytes(st->lay.g) || (!workspace && prefill_ws_bytes(st->lay.g)))
+            return fail(QEVICT_E_CAPACITY, "prefill workspace of %zu bytes < %zu required", ws_bytes,
+                        prefill_ws_bytes(st->lay.g));
+    }
+    hipStream_t hs = (hipStream_t)stream;
+    const Geo& g = st->lay.g;
+    HIP_TRY(launch_prefill_setup(g, st->bf, layer, (const uint16_t*)k_prompt, (const uint16_t*)v_prompt, hs));
+    HIP_TRY(launch_prefill_scores(g, st->bf, layer, (const uint16_t*)q_prompt, (const uint16_t*)k_prompt, score_init,
+                                  workspace, hs));
+    HIP_TRY(launch_route(g, st->bf, layer, RM_PREFILL, hs));
+    HIP_TRY(launch_migrate(g, st->bf, layer, (const uint16_t*)k_prompt, (const uint16_t*)v_prompt, hs));
+    st->prefilled[layer] = 1;
+    st->steps[layer] = 0;
+    return QEVICT_OK;
+}
+
+qevict_status qevict_decode_attn(qevict_state* st, int32_t layer, const void* q, const void* k_new, const void* v_new,
+                                 float* out, void* stream) {
+    qevict_status s = check_layer(st, layer, false);
+    if (s) return s;
+    if (!st->prefilled[layer]) return fail(QEVICT_E_STATE, "layer %d has no prefill", layer);
+    if (!q || !k_new || !v_new || !out) return fail(QEVICT_E_INVALID, "null decode buffer");
+    if (st->steps[layer] >= st->cfg.max_new)
+        return fail(QEVICT_E_CAPACITY, "layer %d already decoded max_new = %d tokens", layer, st->cfg.max_new);
+    hipStream_t hs = (hipStream_t)stream;
+    const Geo& g = st->lay.g;
+    HIP_TRY(launch_append(g, st->bf, layer, (const uint16_t*)k_new, (const uint16_t*)v_new, hs));
+    HIP_TRY(launch_decode(g, st->bf, layer, (const uint16_t*)q, hs));
+    HIP_TRY(launch_combine(g, st->bf, layer, out, hs));
+    HIP_TRY(launch_mass(g, st->bf, layer, hs));
+    st->steps[layer] += 1;
+    return QEVICT_OK;
+}
+
+qevict_status qevict_route(qevict_state* st, int32_t layer, void* stream) {
+    qevict_status s = check_layer(st, layer, true);
+    if (s) return s;
+    for (int l = 0; l < st->cfg.n_layers; ++l)
+        if ((layer == -1 || layer == l) && !st->prefilled[l]) return fail(QEVICT_E_STATE, "layer %d has no prefill", l);
+    hipStream_t hs = (hipStream_t)stream;
+    HIP_TRY(launch_route(st->lay.g, st->bf, layer, RM_ROUTE, hs));
+    HIP_TRY(launch_migrate(st->lay.g, st->bf, layer, nullptr, nullptr, hs));
+    return QEVICT_OK;
+}
+
+static qevict_status forced(qevict_state* st, int32_t layer, const int32_t* win_ids, int32_t n, int mode,
+                            void* stream) {
+    qevict_status s = check_layer(st, layer, false);
+    if (s) return s;
+    if (!st->prefilled[layer]) return fail(QEVICT_E_STATE, "layer %d has no prefill", layer);
+    if (n < 0 || (n > 0 && !win_ids)) return fail(QEVICT_E_INVALID, "bad window list");
+    if (n == 0) return QEVICT_OK;
+    hipStream_t hs = (hipStream_t)stream;
+    HIP_TRY(launch_force_targets(st->lay.g, st->bf, layer, win_ids, n, mode == RM_FORCE_Q ? ST_QUANT : ST_FULL, hs));
+    HIP_TRY(launch_route(st->lay.g, st->bf, layer, mode, hs));
+    HIP_TRY(launch_migrate(st->lay.g, st->bf, layer, nullptr, nullptr, hs));
+    return QEVICT_OK;
+}
+
+qevict_status qevict_pack_int2(qevict_state* st, int32_t layer, const int32_t* win_ids, int32_t n, void* stream) {
+    return forced(st, layer, win_ids, n, RM_FORCE_Q, stream);
+}
+
+qevict_status qevict_promote(qevict_state* st, int32_t layer, const int32_t* win_ids, int32_t n, void* stream) {
+    return forced(st, layer, win_ids, n, RM_FORCE_F, stream);
+}
+
+qevict_status qevict_poll_status(qevict_state* st, uint32_t* status, void* stream) {
+    if (!st || !status) return fail(QEVICT_E_INVALID, "null argument");
+    const Geo& g = st->lay.g;
+    const size_t U = (size_t)g.B * g.L;
+    std::vector<UnitHdr> h(U);
+    HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
+    HIP_TRY(hipMemcpy(h.data(), st->bf.hdr, U * sizeof(UnitHdr), hipMemcpyDeviceToHost));
+    uint32_t acc = 0;
+    for (auto& x : h) acc |= x.status;
+    *status = acc;
+    return QEVICT_OK;
+}
+
+qevict_status qevict_export_unit(qevict_state* st, int32_t layer, int32_t b, void* host_buf, size_t bytes,
+                                 size_t* written, void* stream) {
+    qevict_status s = check_layer(st, layer, false);
+    if (s) return s;
+    if (b < 0 || b >= st->cfg.batch) return fail(QEVICT_E_INVALID, "sequence %d out of range", b);
+    if (!host_buf) return fail(QEVICT_E_INVALID, "null host buffer");
+    if (bytes < st->lay.export_bytes) return fail(QEVICT_E_CAPACITY, "export buffer < %zu bytes", st->lay.export_bytes);
+    const Geo& g = st->lay.g;
+    const int64_t u = unit_of(g, b, layer);
+    HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
+    UnitHdr hdr;
+    std::vector<WinRec> win(g.n_windows);
+    std::vector<double> score(g.n_windows);
+    std::vector<uint8_t> slots((size_t)g.n_slots * g.slot_bytes);
+    std::vector<uint16_t> pages((size_t)g.n_pages * g.page_elems);
+    std::vector<uint16_t> sinks(g.sink_elems);
+    HIP_TRY(hipMemcpy(&hdr, st->bf.hdr + u, sizeof hdr, hipMemcpyDeviceToHost));
+    HIP_TRY(hipMemcpy(win.data(), st->bf.win + u * g.n_windows, win.size() * sizeof(WinRec), hipMemcpyDeviceToHost));
+    HIP_TRY(hipMemcpy(score.data(), st->bf.score + u * g.n_windows, score.size() * 8, hipMemcpyDeviceToHost));
+    HIP_TRY(hipMemcpy(slots.data(), st->bf.slots + u * (size_t)g.n_slots * g.slot_bytes, slots.size(),
+                      hipMemcpyDeviceToHost));
+    HIP_TRY(hipMemcpy(pages.data(), st->bf.pages + u * (size_t)g.n_pages * g.page_elems, pages.size() * 2,
+                      hipMemcpyDeviceToHost));
+    HIP_TRY(hipMemcpy(sinks.data(), st->bf.sinks + u * (size_t)g.sink_elems, sinks.size() * 2, hipMemcpyDeviceToHost));
+
+    char* o = (char*)host_buf;
+    size_t at = 0;
+    auto put = [&](const void* p, size_t nb) {
+        memcpy(o + at, p, nb);
+        at += nb;
+    };
+    // windows created = those whose first position is below n
+    int32_t n_created = 0;
+    if (hdr.n > g.n_sink) n_created = (hdr.n - g.n_sink + g.W - 1) / g.W;
+    if (n_created > g.n_windows) n_created = g.n_windows;
+    int32_t head[20] = {0x58564551, hdr.n, n_created, hdr.K_f, hdr.K_q, (int32_t)hdr.status};
+    for (int i = 0; i < 8; ++i) head[6 + i] = hdr.ctr[i];
+    head[14] = hdr.n_acc;
+    head[15] = hdr.prompt_len;
+    memcpy(&head[16], &hdr.sink_mass, 8);
+    put(head, sizeof head);
+    for (int w = 0; w < n_created; ++w) {
+        int32_t rec[4] = {win[w].state, (win[w].flags & WF_LEDGER) ? 1 : 0, (win[w].flags & WF_DORMANT) ? 1 : 0,
+                          g.n_sink + w * g.W};
+        put(rec, sizeof rec);
+        put(&score[w], 8);
+    }
+    for (int w = 0; w < n_created; ++w)
+        if ((win[w].flags & WF_LEDGER) && win[w].slot >= 0)
+            put(slots.data() + (size_t)win[w].slot * g.slot_bytes, g.slot_bytes);
+    std::vector<uint16_t> tmp(g.page_elems);
+    for (int w = 0; w < n_created; ++w) {
+        const int st_ = win[w].state;
+        if ((st_ == ST_LOCAL || st_ == ST_FULL) && win[w].page >= 0) {
+            const uint16_t* pg = pages.data() + (size_t)win[w].page * g.page_elems;
+            int ntok = hdr.n - (g.n_sink + w * g.W);
+            if (ntok > g.W) ntok = g.W;
+            // page layout [h][K/V][W][d] -> export [K/V][h][W][d], tokens >= ntok zeroed
+            for (int kv = 0; kv < 2; ++kv)
+                for (int h = 0; h < g.h_kv; ++h)
+                    for (int i = 0; i < g.W; ++i)
+                        for (int c = 0; c < g.d; ++c)
+                            tmp[((size_t)(kv * g.h_kv + h) * g.W + i) * g.d + c] =
+                                i < ntok ? pg[((size_t)(h * 2 + kv) * g.W + i) * g.d + c] : 0;
+            put(tmp.data(), (size_t)g.page_elems * 2);
+        }
+    }
+    {
+        const int ns = g.n_sink > 0 ? g.n_sink : 1;
+        std::vector<uint16_t> sk((size_t)2 * g.h_kv * g.n_sink * g.d);
+        for (int kv = 0; kv < 2; ++kv)
+            for (int h = 0; h < g.h_kv; ++h)
+                for (int i = 0; i < g.n_sink; ++i)
+                    for (int c = 0; c < g.d; ++c)
+                        sk[((size_t)(kv * g.h_kv + h) * g.n_sink + i) * g.d + c] =
+                            i < hdr.n ? sinks[((size_t)(h * 2 + kv) * ns + i) * g.d + c] : 0;
+        put(sk.data(), sk.size() * 2);
+    }
+    if (written) *written = at;
+    return QEVICT_OK;
+}
+
+}  // extern "C"

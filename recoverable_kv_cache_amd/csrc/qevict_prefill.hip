@@ -1,0 +1,267 @@
+// Prefill score initialisation: causal prompt-attention column sums on MFMA.
+//
+// Source: "QEvict: Recoverable Quantized KV Eviction for Attention-Drift-Robust
+// Long-Context Decoding", §4.2 (prompt attention initialises the window scores):
+//   S_bar_0(w) = (1/H_q) sum_h sum_{u < S} sum_{t in w} P_h[u, t],
+//   P_h = softmax_causal(Q_h K_g^T / sqrt(d)).
+// Column sums of P are formed without materialising it, as the notes
+// "Learned KV-cache eviction" describe for their target (log-sum-exp per row,
+// then a second pass with query and key roles swapped):
+//   pass 1: LSE_u = log sum_{t <= u} exp(l(u, t))               (per query row)
+//   pass 2: c_t   = sum_{u >= t} exp(l(u, t) - LSE_u)            (per key column)
+// Both passes run bf16 MFMA 16x16x16 tiles with fp32 accumulation; column sums
+// accumulate in fp32 within a 64-row tile and in fp64 across tiles.
+#include "qevict_common.h"
+#include "qevict_internal.h"
+
+namespace qv {
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int PF_TILE = 64;
+constexpr int PF_PAD = 4;   // LDS row padding (bf16 elements)
+
+__device__ __forceinline__ float4_t mfma16(short4_t a, short4_t b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Row tile [64][D] of a [.., S_max, D] bf16 buffer into LDS, zero past S.
+template <int D>
+__device__ __forceinline__ void load_tile(uint16_t (*dst)[D + PF_PAD], const uint16_t* __restrict__ src, int row0,
+                                          int S) {
+    constexpr int CH = D / 8;   // 16-byte chunks per row
+    for (int i = threadIdx.x; i < PF_TILE * CH; i += blockDim.x) {
+        const int r = i / CH, c = (i % CH) * 8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (row0 + r < S) v = *reinterpret_cast<const uint4*>(src + (int64_t)(row0 + r) * D + c);
+        uint2* d2 = reinterpret_cast<uint2*>(&dst[r][c]);
+        d2[0] = make_uint2(v.x, v.y);
+        d2[1] = make_uint2(v.z, v.w);
+    }
+}
+
+// ---------------------------------------------------------------- pass 1: row log-sum-exp (log2 domain)
+template <int D>
+__global__ void __launch_bounds__(256) k_prefill_lse(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qp,
+                                                    const uint16_t* __restrict__ kp, float* __restrict__ lse2) {
+    __shared__ uint16_t ks[PF_TILE][D + PF_PAD];
+    const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int S = bf.hdr[unit_of(g, b, layer)].prompt_len;
+    if (tile * PF_TILE >= S) return;
+    const int G = g.h_q / g.h_kv, hk = h / G;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lq = lane >> 4;
+    const float scale = 1.4426950408889634f / sqrtf((float)D);
+    const uint16_t* Q = qp + ((int64_t)b * g.h_q + h) * g.S_max * D;
+    const uint16_t* K = kp + ((int64_t)b * g.h_kv + hk) * g.S_max * D;
+    const int r0 = tile * PF_TILE + wave * 16;
+    short4_t qa[D / 16];
+    {
+        const int row = r0 + lr;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            uint2 v = make_uint2(0, 0);
+            if (row < S) v = *reinterpret_cast<const uint2*>(Q + (int64_t)row * D + kk * 16 + 4 * lq);
+            qa[kk] = *reinterpret_cast<short4_t*>(&v);
+        }
+    }
+    float m[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        m[i] = -INFINITY;
+        l[i] = 0.f;
+    }
+    const int last_row = min(tile * PF_TILE + PF_TILE, S) - 1;
+    const int n_kt = last_row / PF_TILE + 1;
+    for (int kt = 0; kt < n_kt; ++kt) {
+        __syncthreads();
+        load_tile<D>(ks, K, kt * PF_TILE, S);
+        __syncthreads();
+        float4_t sacc[4];
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+            float4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                const short4_t bb = *reinterpret_cast<const short4_t*>(&ks[sub * 16 + lr][kk * 16 + 4 * lq]);
+                c = mfma16(qa[kk], bb, c);
+            }
+            sacc[sub] = c;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = r0 + 4 * lq + i;
+            float x[4], mx = -INFINITY;
+#pragma unroll
+            for (int sub = 0; sub < 4; ++sub) {
+                const int key = kt * PF_TILE + sub * 16 + lr;
+                x[sub] = (key <= row && key < S) ? sacc[sub][i] * scale : -INFINITY;
+                mx = fmaxf(mx, x[sub]);
+            }
+            if (mx == -INFINITY) continue;
+            const float mn = fmaxf(m[i], mx);
+            float s = l[i] * (m[i] == -INFINITY ? 0.f : exp2f(m[i] - mn));
+#pragma unroll
+            for (int sub = 0; sub < 4; ++sub) s += x[sub] == -INFINITY ? 0.f : exp2f(x[sub] - mn);
+            l[i] = s;
+            m[i] = mn;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const float m2 = wave_xor(m[i], o), l2 = wave_xor(l[i], o);
+            const float M = fmaxf(m[i], m2);
+            float s = 0.f;
+            if (M > -INFINITY) {
+                s = (m[i] > -INFINITY ? l[i] * exp2f(m[i] - M) : 0.f) + (m2 > -INFINITY ? l2 * exp2f(m2 - M) : 0.f);
+            }
+            m[i] = M;
+            l[i] = s;
+        }
+        const int row = r0 + 4 * lq + i;
+        if (lr == 0 && row < S) lse2[((int64_t)b * g.h_q + h) * g.S_max + row] = m[i] + log2f(l[i]);
+    }
+}
+
+// ---------------------------------------------------------------- pass 2: column sums (roles swapped)
+template <int D>
+__global__ void __launch_bounds__(256) k_prefill_colsum(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qp,
+                                                       const uint16_t* __restrict__ kp,
+                                                       const float* __restrict__ lse2, double* __restrict__ col) {
+    __shared__ uint16_t qs[PF_TILE][D + PF_PAD];
+    __shared__ float ls[PF_TILE];
+    const int ktile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int S = bf.hdr[unit_of(g, b, layer)].prompt_len;
+    if (ktile * PF_TILE >= S) return;
+    const int G = g.h_q / g.h_kv, hk = h / G;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lq = lane >> 4;
+    const float scale = 1.4426950408889634f / sqrtf((float)D);
+    const uint16_t* Q = qp + ((int64_t)b * g.h_q + h) * g.S_max * D;
+    const uint16_t* K = kp + ((int64_t)b * g.h_kv + hk) * g.S_max * D;
+    const float* LS = lse2 + ((int64_t)b * g.h_q + h) * g.S_max;
+    const int k0 = ktile * PF_TILE + wave * 16;
+    short4_t ka[D / 16];
+    {
+        const int key = k0 + lr;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            uint2 v = make_uint2(0, 0);
+            if (key < S) v = *reinterpret_cast<const uint2*>(K + (int64_t)key * D + kk * 16 + 4 * lq);
+            ka[kk] = *reinterpret_cast<short4_t*>(&v);
+        }
+    }
+    double cs[4] = {0.0, 0.0, 0.0, 0.0};
+    const int n_qt = (S - 1) / PF_TILE + 1;
+    for (int qt = ktile; qt < n_qt; ++qt) {
+        __syncthreads();
+        load_tile<D>(qs, Q, qt * PF_TILE, S);
+        for (int r = threadIdx.x; r < PF_TILE; r += blockDim.x) {
+            const int row = qt * PF_TILE + r;
+            ls[r] = row < S ? LS[row] : INFINITY;
+        }
+        __syncthreads();
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+            float4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                const short4_t bb = *reinterpret_cast<const short4_t*>(&qs[sub * 16 + lr][kk * 16 + 4 * lq]);
+                c = mfma16(ka[kk], bb, c);
+            }
+            const int query = qt * PF_TILE + sub * 16 + lr;
+            const float lq_ = ls[sub * 16 + lr];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = k0 + 4 * lq + i;
+                if (query >= key && query < S) part[i] += exp2f(fmaf(c[i], scale, -lq_));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cs[i] += (double)part[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        double v = cs[i];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+        const int key = k0 + 4 * lq + i;
+        if (lr == 0 && key < S) col[((int64_t)b * g.h_q + h) * g.S_max + key] = v;
+    }
+}
+
+// ---------------------------------------------------------------- per-window reduction
+__global__ void k_prefill_windows(Geo g, Bufs bf, int layer, const double* __restrict__ col) {
+    const int b = blockIdx.x;
+    const int64_t u = unit_of(g, b, layer);
+    UnitHdr* hdr = bf.hdr + u;
+    const int S = hdr->prompt_len;
+    const int n_win = S > g.n_sink ? (S - g.n_sink + g.W - 1) / g.W : 0;
+    for (int w = threadIdx.x; w < g.n_windows; w += blockDim.x) {
+        double s = 0.0;
+        if (w < n_win) {
+            const int a = g.n_sink + w * g.W, e = min(a + g.W, S);
+            for (int h = 0; h < g.h_q; ++h) {
+                const double* c = col + ((int64_t)b * g.h_q + h) * g.S_max;
+                for (int t = a; t < e; ++t) s += c[t];
+            }
+            s /= g.h_q;
+        }
+        bf.score[u * g.n_windows + w] = s;
+    }
+    if (threadIdx.x == 0) {
+        double s = 0.0;
+        const int ns = min(g.n_sink, S);
+        for (int h = 0; h < g.h_q; ++h)
+            for (int t = 0; t < ns; ++t) s += col[((int64_t)b * g.h_q + h) * g.S_max + t];
+        hdr->sink_mass = s / g.h_q;
+    }
+}
+
+__global__ void k_score_copy(Geo g, Bufs bf, int layer, const double* __restrict__ init) {
+    const int b = blockIdx.x;
+    const int64_t u = unit_of(g, b, layer);
+    const int S = bf.hdr[u].prompt_len;
+    const int n_win = S > g.n_sink ? (S - g.n_sink + g.W - 1) / g.W : 0;
+    for (int w = threadIdx.x; w < g.n_windows; w += blockDim.x)
+        bf.score[u * g.n_windows + w] = w < n_win ? init[(int64_t)b * g.n_windows + w] : 0.0;
+    if (threadIdx.x == 0) bf.hdr[u].sink_mass = 0.0;
+}
+
+size_t prefill_ws_bytes(const Geo& g) {
+    const size_t n = (size_t)g.B * g.h_q * g.S_max;
+    return ((n * 4 + 255) & ~size_t(255)) + n * 8;
+}
+
+hipError_t launch_prefill_scores(const Geo& g, const Bufs& bf, int layer, const uint16_t* qp, const uint16_t* kp,
+                                 const double* score_init, void* ws, hipStream_t s) {
+    if (score_init) {
+        hipLaunchKernelGGL(k_score_copy, dim3(g.B), dim3(256), 0, s, g, bf, layer, score_init);
+        return hipGetLastError();
+    }
+    if (g.S_max == 0) {
+        hipLaunchKernelGGL(k_prefill_windows, dim3(g.B), dim3(256), 0, s, g, bf, layer, (const double*)nullptr);
+        return hipGetLastError();
+    }
+    const size_t n = (size_t)g.B * g.h_q * g.S_max;
+    float* lse2 = (float*)ws;
+    double* col = (double*)((char*)ws + ((n * 4 + 255) & ~size_t(255)));
+    const dim3 grid((g.S_max + PF_TILE - 1) / PF_TILE, g.h_q, g.B);
+    if (g.d == 128) {
+        hipLaunchKernelGGL((k_prefill_lse<128>), grid, dim3(256), 0, s, g, bf, layer, qp, kp, lse2);
+        hipLaunchKernelGGL((k_prefill_colsum<128>), grid, dim3(256), 0, s, g, bf, layer, qp, kp, lse2, col);
+    } else {
+        hipLaunchKernelGGL((k_prefill_lse<64>), grid, dim3(256), 0, s, g, bf, layer, qp, kp, lse2);
+        hipLaunchKernelGGL((k_prefill_colsum<64>), grid, dim3(256), 0, s, g, bf, layer, qp, kp, lse2, col);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_prefill_windows, dim3(g.B), dim3(256), 0, s, g, bf, layer, col);
+    return hipGetLastError();
+}
+
+}  // namespace qv

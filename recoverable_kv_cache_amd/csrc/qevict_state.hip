@@ -1,0 +1,720 @@
+// State kernels: arena initialisation, token append, prefill setup, the
+// window router (candidate pool + two-stage TopK + migration bookkeeping +
+// chronological compaction) and the INT2 pack / dequantize-promote kernels.
+//
+// Source: "QEvict: Recoverable Quantized KV Eviction for Attention-Drift-Robust
+// Long-Context Decoding", §4.3 (Eq. 3 capacities, "Migration-Stable
+// Quantization", Eqs. 4-6), Appendix A Algorithm 1.
+#include "qevict_common.h"
+#include "qevict_internal.h"
+
+namespace qv {
+
+// ------------------------------------------------------------------------------------ init
+__global__ void k_init(Geo g, Bufs bf, const int32_t* plens, const int32_t* kf, const int32_t* kq) {
+    const int64_t u = blockIdx.x;
+    const int b = (int)(u / g.L);
+    if (threadIdx.x == 0) {
+        UnitHdr h = {};
+        h.prompt_len = plens[b];
+        h.n_free_pages = g.n_pages;
+        h.n_free_slots = g.n_slots;
+        h.K_f = kf[b];
+        h.K_q = kq[b];
+        bf.hdr[u] = h;
+    }
+    for (int i = threadIdx.x; i < g.n_pages; i += blockDim.x) bf.free_pages[u * g.n_pages + i] = g.n_pages - 1 - i;
+    for (int i = threadIdx.x; i < g.n_slots; i += blockDim.x) bf.free_slots[u * g.n_slots + i] = g.n_slots - 1 - i;
+    for (int w = threadIdx.x; w < g.n_windows; w += blockDim.x) {
+        bf.win[u * g.n_windows + w] = WinRec{ST_NONE, -1, -1, 0};
+        bf.score[u * g.n_windows + w] = 0.0;
+        bf.target[u * g.n_windows + w] = 0;
+    }
+    for (int s = threadIdx.x; s <= g.n_splits; s += blockDim.x) bf.splits[u * (g.n_splits + 1) + s] = 0;
+}
+
+hipError_t launch_init(const Geo& g, const Bufs& bf, const int32_t* plens, const int32_t* kf, const int32_t* kq,
+                       hipStream_t s) {
+    hipLaunchKernelGGL(k_init, dim3(g.B * g.L), dim3(256), 0, s, g, bf, plens, kf, kq);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------ append
+// Writes the new token's K/V (bf16) at position n into the sink prefix or the
+// page of its (recent-region) window, then advances n.
+__global__ void k_append(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v) {
+    const int b = blockIdx.x;
+    const int64_t u = unit_of(g, b, layer);
+    UnitHdr* hdr = bf.hdr + u;
+    const int p = hdr->n;
+    uint16_t* dst;
+    int64_t head_stride;
+    if (p < g.n_sink) {
+        const int ns = g.n_sink;
+        dst = bf.sinks + u * g.sink_elems + (int64_t)p * g.d;
+        head_stride = (int64_t)ns * g.d;   // K/V blocks of one head are ns*d apart; heads 2*ns*d apart
+    } else {
+        const int w = (p - g.n_sink) / g.W, i = (p - g.n_sink) % g.W;
+        const WinRec rec = w < g.n_windows ? bf.win[u * g.n_windows + w] : WinRec{ST_NONE, -1, -1, 0};
+        if (rec.state != ST_LOCAL || rec.page < 0) {
+            if (threadIdx.x == 0) atomicOr(&hdr->status, QEVICT_DEV_E_WINDOW);
+            return;
+        }
+        dst = bf.pages + u * (int64_t)g.n_pages * g.page_elems + (int64_t)rec.page * g.page_elems + (int64_t)i * g.d;
+        head_stride = (int64_t)g.W * g.d;
+    }
+    const int n_el = g.h_kv * g.d;
+    for (int e = threadIdx.x; e < n_el; e += blockDim.x) {
+        const int h = e / g.d, c = e % g.d;
+        dst[(2 * h) * head_stride + c] = k[(int64_t)b * n_el + e];
+        dst[(2 * h + 1) * head_stride + c] = v[(int64_t)b * n_el + e];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) hdr->n = p + 1;
+}
+
+hipError_t launch_append(const Geo& g, const Bufs& bf, int layer, const uint16_t* k, const uint16_t* v, hipStream_t s) {
+    hipLaunchKernelGGL(k_append, dim3(g.B), dim3(256), 0, s, g, bf, layer, k, v);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------ prefill setup
+// n = prompt_len; every window holding prompt tokens is marked PROMPT (its
+// data still lives in the caller's buffer); sink tokens are copied.
+__global__ void k_prefill_setup(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ kp,
+                                const uint16_t* __restrict__ vp) {
+    const int b = blockIdx.x;
+    const int64_t u = unit_of(g, b, layer);
+    UnitHdr* hdr = bf.hdr + u;
+    const int S = hdr->prompt_len;
+    const int n_win = S > g.n_sink ? (S - g.n_sink + g.W - 1) / g.W : 0;
+    for (int w = threadIdx.x; w < n_win; w += blockDim.x) bf.win[u * g.n_windows + w].state = ST_PROMPT;
+    const int ns = g.n_sink;
+    const int nsk = S < ns ? S : ns;
+    for (int e = threadIdx.x; e < g.h_kv * nsk * g.d; e += blockDim.x) {
+        const int h = e / (nsk * g.d), t = (e / g.d) % nsk, c = e % g.d;
+        const int64_t src = (((int64_t)b * g.h_kv + h) * g.S_max + t) * g.d + c;
+        uint16_t* dst = bf.sinks + u * g.sink_elems;
+        dst[((int64_t)(2 * h) * ns + t) * g.d + c] = kp[src];
+        dst[((int64_t)(2 * h + 1) * ns + t) * g.d + c] = vp[src];
+    }
+    if (threadIdx.x == 0) {
+        hdr->n = S;
+        hdr->n_win = n_win;
+    }
+}
+
+hipError_t launch_prefill_setup(const Geo& g, const Bufs& bf, int layer, const uint16_t* kp, const uint16_t* vp,
+                                hipStream_t s) {
+    hipLaunchKernelGGL(k_prefill_setup, dim3(g.B), dim3(256), 0, s, g, bf, layer, kp, vp);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------ forced targets
+__global__ void k_force_targets(Geo g, Bufs bf, int layer, const int32_t* __restrict__ ids, int n, int tgt) {
+    const int b = blockIdx.x;
+    const int64_t u = unit_of(g, b, layer);
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int w = ids[(int64_t)b * n + i];
+        if (w >= 0 && w < g.n_windows) bf.target[u * g.n_windows + w] = (int8_t)tgt;
+    }
+}
+
+hipError_t launch_force_targets(const Geo& g, const Bufs& bf, int layer, const int32_t* ids, int n, int tgt,
+                                hipStream_t s) {
+    hipLaunchKernelGGL(k_force_targets, dim3(g.B), dim3(256), 0, s, g, bf, layer, ids, n, tgt);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------ router
+constexpr int RT_THREADS = 1024;
+constexpr int RT_MAXW = 4096;           // windows per unit handled by one workgroup
+constexpr int RT_PER = RT_MAXW / RT_THREADS;
+
+// Exclusive scan of a[0..RT_MAXW) in LDS; returns the total.  All threads call.
+__device__ int block_scan_excl(int* a, int* wsum) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int v[RT_PER];
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < RT_PER; ++i) {
+        v[i] = a[tid * RT_PER + i];
+        s += v[i];
+    }
+    int incl = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    if (tid == 0) {
+        int acc = 0;
+        for (int w = 0; w < RT_THREADS / 64; ++w) {
+            int t = wsum[w];
+            wsum[w] = acc;
+            acc += t;
+        }
+        wsum[RT_THREADS / 64] = acc;
+    }
+    __syncthreads();
+    int run = wsum[wave] + incl - s;
+#pragma unroll
+    for (int i = 0; i < RT_PER; ++i) {
+        a[tid * RT_PER + i] = run;
+        run += v[i];
+    }
+    const int total = wsum[RT_THREADS / 64];
+    __syncthreads();
+    return total;
+}
+
+struct RouteSmem {
+    unsigned long long key[RT_MAXW];
+    int idx[RT_MAXW];
+    int8_t newst[RT_MAXW];
+    int wsum[RT_THREADS / 64 + 1];
+    int misc[8];
+};
+
+__device__ __forceinline__ int per_head_cost(const Geo& g, int kind) {
+    if (kind == EK_SINK) return 4 * g.n_sink * g.d;
+    if (kind == EK_PAGE) return 4 * g.W * g.d;
+    return g.slot_head_bytes;
+}
+
+// One workgroup per (sequence, layer).
+__global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer, int mode) {
+    extern __shared__ unsigned char smem_raw[];
+    RouteSmem& sm = *reinterpret_cast<RouteSmem*>(smem_raw);
+    const int tid = threadIdx.x;
+    const int b = layer >= 0 ? blockIdx.x : blockIdx.x / g.L;
+    const int l = layer >= 0 ? layer : blockIdx.x % g.L;
+    const int64_t u = unit_of(g, b, l);
+    UnitHdr* hdr = bf.hdr + u;
+    WinRec* win = bf.win + u * g.n_windows;
+    double* score = bf.score + u * g.n_windows;
+    int8_t* target = bf.target + u * g.n_windows;
+    const int n = hdr->n;
+    const int K_f = hdr->K_f, K_q = hdr->K_q;
+    const int NW = g.n_windows;
+    int* flag = (int*)sm.key;                // scratch aliasing the (not yet used) key array
+    int* flag2 = flag + RT_MAXW;
+
+    // ---- 1. candidate pool (Eq. 4): previous Full ∪ previous Quantized ∪ aged recent windows
+    for (int w = tid; w < RT_MAXW; w += RT_THREADS) {
+        int c = 0;
+        if (w < NW) {
+            const int st = win[w].state;
+            const bool aged = g.n_sink + (w + 1) * g.W <= n - g.n_local;
+            if (mode == RM_ROUTE || mode == RM_PREFILL)
+                c = (st == ST_FULL || st == ST_QUANT || ((st == ST_LOCAL || st == ST_PROMPT) && aged));
+            else if (mode == RM_FORCE_Q)
+                c = target[w] != 0 && (st == ST_FULL || (st == ST_LOCAL && aged));
+            else
+                c = target[w] != 0 && st == ST_QUANT;
+        }
+        flag[w] = c;
+        flag2[w] = c;
+    }
+    __syncthreads();
+    const int n_cand = block_scan_excl(flag, sm.wsum);
+    // flag[] now holds positions; flag2[] the candidate bits.  Keys: descending score
+    // then ascending window index == ascending (~bits(score), index) for score >= 0.
+    int cand_w[RT_PER], cand_pos[RT_PER];
+#pragma unroll
+    for (int i = 0; i < RT_PER; ++i) {
+        const int w = tid + i * RT_THREADS;
+        cand_w[i] = flag2[w] ? w : -1;
+        cand_pos[i] = flag[w];
+    }
+    __syncthreads();
+    int P = 1;
+    while (P < n_cand) P <<= 1;
+#pragma unroll
+    for (int i = 0; i < RT_PER; ++i) {
+        const int w = cand_w[i];
+        if (w >= 0) {
+            const double s = (mode == RM_ROUTE || mode == RM_PREFILL) ? score[w] : 0.0;
+            sm.key[cand_pos[i]] = ~(unsigned long long)__double_as_longlong(s);
+            sm.idx[cand_pos[i]] = w;
+        }
+    }
+    for (int i = n_cand + tid; i < P; i += RT_THREADS) {
+        sm.key[i] = ~0ull;
+        sm.idx[i] = 0x7fffffff;
+    }
+    __syncthreads();
+    // ---- 2. bitonic sort of (key, idx) ascending over P entries: TopK_{K_f} then TopK_{K_q} (Eq. 5)
+    for (int k = 2; k <= P; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < P; i += RT_THREADS) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const unsigned long long ka = sm.key[i], kb = sm.key[ixj];
+                    const int ia = sm.idx[i], ib = sm.idx[ixj];
+                    const bool a_gt_b = ka > kb || (ka == kb && ia > ib);
+                    const bool up = (i & k) == 0;
+                    if (up == a_gt_b) {
+                        sm.key[i] = kb;
+                        sm.key[ixj] = ka;
+                        sm.idx[i] = ib;
+                        sm.idx[ixj] = ia;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    // ---- 3. new state of every window
+    for (int w = tid; w < RT_MAXW; w += RT_THREADS) {
+        int ns = ST_NONE;
+        if (w < NW) {
+            const int st = win[w].state;
+            ns = st;
+            if (st == ST_PROMPT) ns = ST_LOCAL;  // non-aged prompt windows enter the recent region
+            if (st == ST_NONE && g.n_sink + w * g.W < n + g.omega) ns = ST_LOCAL;   // prepare
+        }
+        sm.newst[w] = (int8_t)ns;
+    }
+    __syncthreads();
+    const bool one_way = (g.flags & QEVICT_F_NO_PROMOTE) != 0;
+    if (mode == RM_ROUTE || mode == RM_PREFILL) {
+        if (!one_way) {
+            for (int r = tid; r < n_cand; r += RT_THREADS)
+                sm.newst[sm.idx[r]] = (int8_t)(r < K_f ? ST_FULL : (r < K_f + K_q ? ST_QUANT : ST_EVICTED));
+            __syncthreads();
+        } else {
+            // one-way: Full = best K_f candidates that are not Quantized; Quantized = next K_q of the rest
+            for (int r = tid; r < RT_MAXW; r += RT_THREADS) flag[r] = (r < n_cand && win[sm.idx[r]].state != ST_QUANT);
+            __syncthreads();
+            for (int r = tid; r < RT_MAXW; r += RT_THREADS) flag2[r] = flag[r];
+            __syncthreads();
+            block_scan_excl(flag, sm.wsum);
+            for (int r = tid; r < RT_MAXW; r += RT_THREADS) {
+                const bool isF = r < n_cand && flag2[r] && flag[r] < K_f;
+                flag2[r] = isF;
+            }
+            __syncthreads();
+            for (int r = tid; r < RT_MAXW; r += RT_THREADS) flag[r] = (r < n_cand && !flag2[r]);
+            __syncthreads();
+            block_scan_excl(flag, sm.wsum);
+            for (int r = tid; r < n_cand; r += RT_THREADS) {
+                int ns;
+                if (flag2[r]) ns = ST_FULL;
+                else ns = flag[r] < K_q ? ST_QUANT : ST_EVICTED;
+                sm.newst[sm.idx[r]] = (int8_t)ns;
+            }
+            __syncthreads();
+        }
+    } else {
+        const int tgt = mode == RM_FORCE_Q ? ST_QUANT : ST_FULL;
+        for (int r = tid; r < n_cand; r += RT_THREADS) sm.newst[sm.idx[r]] = (int8_t)tgt;
+        __syncthreads();
+    }
+
+    // ---- 4. migration actions (Algorithm 1 steps 5-20).  Per window:
+    // bit0 free page, bit1 need page, bit2 free slot, bit3 need slot, bit4 pack, bit5 fill
+    int act[RT_PER];
+    int ctr[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < RT_PER; ++i) {
+        const int w = tid + i * RT_THREADS;
+        int a = 0;
+        if (w < NW) {
+            const WinRec r = win[w];
+            const int os = r.state, ns = sm.newst[w];
+            const bool cand = flag2 != nullptr && cand_w[i] >= 0;
+            if (cand && (os == ST_LOCAL || os == ST_PROMPT)) ctr[C_AGED]++;
+            if (os == ST_LOCAL || os == ST_FULL) {
+                if (ns == ST_QUANT) {
+                    a |= 1;
+                    if (r.flags & WF_LEDGER) ctr[C_REACTIVATED]++;
+                    else { a |= 8 | 16; ctr[C_PACKED]++; }
+                    ctr[C_DEMOTED]++;
+                } else if (ns == ST_EVICTED) {
+                    a |= 1;
+                    if (r.flags & WF_LEDGER) a |= 4;
+                    ctr[C_EVICTED]++;
+                }
+            } else if (os == ST_QUANT) {
+                if (ns == ST_FULL) { a |= 2 | 32; ctr[C_PROMOTED]++; }
+                else if (ns == ST_EVICTED) { a |= 4; ctr[C_EVICTED]++; }
+            } else if (os == ST_PROMPT) {
+                if (ns == ST_FULL || ns == ST_LOCAL) a |= 2 | 32;
+                else if (ns == ST_QUANT) { a |= 8 | 16; ctr[C_PACKED]++; ctr[C_DEMOTED]++; }
+                else if (ns == ST_EVICTED) ctr[C_EVICTED]++;
+            } else if (os == ST_NONE && ns == ST_LOCAL) {
+                a |= 2;
+            }
+            if (ns == ST_FULL) ctr[C_NFULL]++;
+            if (ns == ST_QUANT) ctr[C_NQUANT]++;
+        }
+        act[i] = a;
+    }
+    // counters: block reduction through LDS atomics
+    if (tid < 8) sm.misc[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+        if (ctr[c]) atomicAdd(&sm.misc[c], ctr[c]);
+    __syncthreads();
+    if (tid < 8) hdr->ctr[tid] = sm.misc[tid];
+
+    // ---- 5. slot allocation: push freed slots, then pop for new packs
+    int32_t* fslot = bf.free_slots + u * g.n_slots;
+    int32_t* fpage = bf.free_pages + u * g.n_pages;
+    int nslot_free0 = hdr->n_free_slots, npage_free0 = hdr->n_free_pages;
+    int my_slot[RT_PER], my_page[RT_PER];
+#pragma unroll
+    for (int i = 0; i < RT_PER; ++i) {
+        const int w = tid + i * RT_THREADS;
+        my_slot[i] = w < NW ? win[w].slot : -1;
+        my_page[i] = w < NW ? win[w].page : -1;
+    }
+    __syncthreads();
+    for (int pass = 0; pass < 2; ++pass) {      // pass 0: slots, pass 1: pages
+        const int fbit = pass == 0 ? 4 : 1, nbit = pass == 0 ? 8 : 2;
+        int32_t* stack = pass == 0 ? fslot : fpage;
+        const int cap = pass == 0 ? g.n_slots : g.n_pages;
+        const int cnt0 = pass == 0 ? nslot_free0 : npage_free0;
+#pragma unroll
+        for (int i = 0; i < RT_PER; ++i) flag[tid + i * RT_THREADS] = (act[i] & fbit) ? 1 : 0;
+        __syncthreads();
+        const int n_freed = block_scan_excl(flag, sm.wsum);
+#pragma unroll
+        for (int i = 0; i < RT_PER; ++i) {
+            if (act[i] & fbit) {
+                const int pos = cnt0 + flag[tid + i * RT_THREADS];
+                const int id = pass == 0 ? my_slot[i] : my_page[i];
+                if (pos < cap && id >= 0) stack[pos] = id;
+                if (pass == 0) my_slot[i] = -1;
+                else my_page[i] = -1;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < RT_PER; ++i) flag[tid + i * RT_THREADS] = (act[i] & nbit) ? 1 : 0;
+        __syncthreads();
+        const int n_need = block_scan_excl(flag, sm.wsum);
+        const int avail = min(cnt0 + n_freed, cap);
+#pragma unroll
+        for (int i = 0; i < RT_PER; ++i) {
+            if (act[i] & nbit) {
+                const int k = flag[tid + i * RT_THREADS];
+                const int id = k < avail ? stack[avail - 1 - k] : -1;
+                if (pass == 0) my_slot[i] = id;
+                else my_page[i] = id;
+            }
+        }
+        if (tid == 0) {
+            int left = avail - n_need;
+            if (left < 0) {
+                atomicOr(&hdr->status, QEVICT_DEV_E_POOL);
+                left = 0;
+            }
+            if (pass == 0) hdr->n_free_slots = left;
+            else hdr->n_free_pages = left;
+        }
+        __syncthreads();
+    }
+
+    // ---- 6. work lists: pack (quantize once) and fill (promote / copy prompt)
+#pragma unroll
+    for (int i = 0; i < RT_PER; ++i) {
+        flag[tid + i * RT_THREADS] = (act[i] & 16) ? 1 : 0;
+        flag2[tid + i * RT_THREADS] = (act[i] & 32) ? 1 : 0;
+    }
+    __syncthreads();
+    const int n_pack = block_scan_excl(flag, sm.wsum);
+    const int n_fill = block_scan_excl(flag2, sm.wsum);
+#pragma unroll
+    for (int i = 0; i < RT_PER; ++i) {
+        const int w = tid + i * RT_THREADS;
+        if (w >= NW) continue;
+        const WinRec r = win[w];
+        if (act[i] & 16) {
+            PackItem it;
+            it.win = w;
+            it.src_prompt = r.state == ST_PROMPT ? 1 : 0;
+            it.src_page = r.page;
+            it.dst_slot = my_slot[i];
+            bf.pack[u * g.n_windows + flag[w]] = it;
+        }
+        if (act[i] & 32) {
+            FillItem it;
+            it.win = w;
+            it.dst_page = my_page[i];
+            it.src_slot = r.state == ST_QUANT ? r.slot : -1;
+            it.pad = 0;
+            bf.fill[u * g.n_windows + flag2[w]] = it;
+        }
+    }
+    if (tid == 0) {
+        hdr->n_pack = n_pack;
+        hdr->n_fill = n_fill;
+    }
+    __syncthreads();
+    // ---- 7. commit the new window records
+#pragma unroll
+    for (int i = 0; i < RT_PER; ++i) {
+        const int w = tid + i * RT_THREADS;
+        if (w >= NW) continue;
+        WinRec r = win[w];
+        const int ns = sm.newst[w];
+        int flags = r.flags;
+        if (ns == ST_EVICTED) flags = 0;
+        else if (r.state == ST_QUANT && ns == ST_FULL) flags |= WF_DORMANT;
+        else if (ns == ST_QUANT) flags = WF_LEDGER;           // new or reactivated record is active
+        r.state = ns;
+        r.flags = flags;
+        r.slot = (ns == ST_QUANT || (flags & WF_LEDGER)) ? my_slot[i] : -1;
+        r.page = (ns == ST_FULL || ns == ST_LOCAL) ? my_page[i] : -1;
+        win[w] = r;
+        if (mode == RM_FORCE_Q || mode == RM_FORCE_F) target[w] = 0;
+    }
+    __syncthreads();
+    // ---- 8. chronological accessible list (Algorithm 1 step 21) and byte-balanced splits
+    for (int w = tid; w < RT_MAXW; w += RT_THREADS) {
+        const int ns = w < NW ? sm.newst[w] : ST_NONE;
+        flag[w] = (ns == ST_LOCAL || ns == ST_FULL || ns == ST_QUANT) ? 1 : 0;
+    }
+    __syncthreads();
+    const int n_winacc = block_scan_excl(flag, sm.wsum);
+    const int base = 1;   // entry 0 is the sink prefix
+    int n_acc = base + n_winacc;
+    if (n_acc > g.n_acc_max) {
+        if (tid == 0) atomicOr(&hdr->status, QEVICT_DEV_E_LIST);
+        n_acc = g.n_acc_max;
+    }
+    AccEntry* acc = bf.acc + u * g.n_acc_max;
+    int* cost = flag2;
+    for (int e = tid; e < RT_MAXW; e += RT_THREADS) cost[e] = 0;
+    __syncthreads();
+    if (tid == 0) {
+        acc[0] = AccEntry{EK_SINK, 0, -1, 0};
+        cost[0] = per_head_cost(g, EK_SINK);
+    }
+#pragma unroll
+    for (int i = 0; i < RT_PER; ++i) {
+        const int w = tid + i * RT_THREADS;
+        if (w >= NW) continue;
+        const int ns = sm.newst[w];
+        if (!(ns == ST_LOCAL || ns == ST_FULL || ns == ST_QUANT)) continue;
+        const int e = base + flag[w];
+        if (e >= n_acc) continue;
+        AccEntry en;
+        en.kind = ns == ST_QUANT ? EK_SLOT : EK_PAGE;
+        en.idx = ns == ST_QUANT ? my_slot[i] : my_page[i];
+        en.win = w;
+        en.start = g.n_sink + w * g.W;
+        acc[e] = en;
+        cost[e] = per_head_cost(g, en.kind);
+    }
+    __syncthreads();
+    const int total = block_scan_excl(cost, sm.wsum);   // cost[e] = byte offset of entry e
+    int32_t* splits = bf.splits + u * (g.n_splits + 1);
+    for (int s = tid; s <= g.n_splits; s += RT_THREADS) {
+        int pos;
+        if (s == 0) pos = 0;
+        else if (s == g.n_splits) pos = n_acc;
+        else {
+            const long long tgt = (long long)total * s / g.n_splits;
+            int lo = 0, hi = n_acc;       // first e with cost[e] >= tgt
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (cost[mid] < tgt) lo = mid + 1;
+                else hi = mid;
+            }
+            pos = lo;
+        }
+        splits[s] = pos;
+    }
+    if (tid == 0) {
+        hdr->n_acc = n_acc;
+        int nwin = 0;
+        const int lim = n + g.omega - g.n_sink;
+        if (lim > 0) nwin = (lim + g.W - 1) / g.W;
+        hdr->n_win = nwin < NW ? nwin : NW;
+        const int lastprep = nwin;
+        if (lastprep > NW) atomicOr(&hdr->status, QEVICT_DEV_E_LIST);
+    }
+}
+
+hipError_t launch_route(const Geo& g, const Bufs& bf, int layer, int mode, hipStream_t s) {
+    const int blocks = layer >= 0 ? g.B : g.B * g.L;
+    const size_t smem = sizeof(RouteSmem);
+    hipLaunchKernelGGL(k_route, dim3(blocks), dim3(RT_THREADS), smem, s, g, bf, layer, mode);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------ pack (INT2, once)
+// Keys: per (head, channel) over the window's tokens; values: per (head, token)
+// over channels.  off = RD_fp16(min), scl = RU_fp16((max - off)/3), code =
+// #{k in 1..3 : 2(x - off) >= (2k-1) scl}, 0 when scl == 0.  All comparisons in
+// fp64, where they are exact for bf16 x and fp16 off/scl.
+constexpr int PK_THREADS = 256;
+constexpr int PK_MAXE = 64 * 128;   // W * d
+
+__global__ void __launch_bounds__(PK_THREADS) k_pack(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ kp,
+                                                     const uint16_t* __restrict__ vp) {
+    __shared__ uint16_t sk[PK_MAXE], sv[PK_MAXE];
+    __shared__ uint8_t ck[PK_MAXE], cv[PK_MAXE];
+    const int l = layer >= 0 ? layer : blockIdx.x % g.L;
+    const int b = layer >= 0 ? blockIdx.x : blockIdx.x / g.L;
+    const int64_t u = unit_of(g, b, l);
+    UnitHdr* hdr = bf.hdr + u;
+    const int n_items = hdr->n_pack * g.h_kv;
+    const int W = g.W, d = g.d;
+    for (int it = blockIdx.y; it < n_items; it += gridDim.y) {
+        const PackItem pi = bf.pack[u * g.n_windows + it / g.h_kv];
+        const int h = it % g.h_kv;
+        const int start = g.n_sink + pi.win * W;
+        const uint16_t *srck, *srcv;
+        if (pi.src_prompt) {
+            srck = kp + (((int64_t)b * g.h_kv + h) * g.S_max + start) * d;
+            srcv = vp + (((int64_t)b * g.h_kv + h) * g.S_max + start) * d;
+        } else {
+            const uint16_t* pg = bf.pages + u * (int64_t)g.n_pages * g.page_elems + (int64_t)pi.src_page * g.page_elems;
+            srck = pg + (int64_t)(2 * h) * W * d;
+            srcv = pg + (int64_t)(2 * h + 1) * W * d;
+        }
+        if (pi.dst_slot < 0 || (!pi.src_prompt && pi.src_page < 0)) {
+            if (threadIdx.x == 0) atomicOr(&hdr->status, QEVICT_DEV_E_POOL);
+            continue;
+        }
+        for (int e = threadIdx.x; e < W * d; e += PK_THREADS) {
+            sk[e] = srck[e];
+            sv[e] = srcv[e];
+        }
+        __syncthreads();
+        uint8_t* slot = bf.slots + u * (int64_t)g.n_slots * g.slot_bytes + (int64_t)pi.dst_slot * g.slot_bytes +
+                        (int64_t)h * g.slot_head_bytes;
+        uint16_t* offK = (uint16_t*)(slot + W * d / 2);
+        uint16_t* sclK = offK + d;
+        uint16_t* offV = sclK + d;
+        uint16_t* sclV = offV + W;
+        bool bad = false;
+        // keys: one channel per thread
+        for (int c = threadIdx.x; c < d; c += PK_THREADS) {
+            float mn = bf16_to_f32(sk[c]), mx = mn;
+            for (int i = 1; i < W; ++i) {
+                const float x = bf16_to_f32(sk[i * d + c]);
+                mn = fminf(mn, x);
+                mx = fmaxf(mx, x);
+            }
+            if (fabsf(mn) > 65504.f || fabsf(mx) > 65504.f) bad = true;
+            const double off = fp16_round_down((double)mn);
+            const double scl = fp16_round_up(((double)mx - off) / 3.0);
+            if (fabs(off) > 65504.0 || scl > 65504.0) bad = true;
+            offK[c] = fp16_bits_exact(off);
+            sclK[c] = fp16_bits_exact(scl);
+            for (int i = 0; i < W; ++i) {
+                const double t = 2.0 * ((double)bf16_to_f32(sk[i * d + c]) - off);
+                int code = (t >= scl) + (t >= 3.0 * scl) + (t >= 5.0 * scl);
+                if (scl == 0.0) code = 0;
+                ck[i * d + c] = (uint8_t)code;
+            }
+        }
+        // values: one token per thread
+        for (int i = threadIdx.x; i < W; i += PK_THREADS) {
+            float mn = bf16_to_f32(sv[i * d]), mx = mn;
+            for (int c = 1; c < d; ++c) {
+                const float x = bf16_to_f32(sv[i * d + c]);
+                mn = fminf(mn, x);
+                mx = fmaxf(mx, x);
+            }
+            if (fabsf(mn) > 65504.f || fabsf(mx) > 65504.f) bad = true;
+            const double off = fp16_round_down((double)mn);
+            const double scl = fp16_round_up(((double)mx - off) / 3.0);
+            if (fabs(off) > 65504.0 || scl > 65504.0) bad = true;
+            offV[i] = fp16_bits_exact(off);
+            sclV[i] = fp16_bits_exact(scl);
+            for (int c = 0; c < d; ++c) {
+                const double t = 2.0 * ((double)bf16_to_f32(sv[i * d + c]) - off);
+                int code = (t >= scl) + (t >= 3.0 * scl) + (t >= 5.0 * scl);
+                if (scl == 0.0) code = 0;
+                cv[i * d + c] = (uint8_t)code;
+            }
+        }
+        if (bad) atomicOr(&hdr->status, QEVICT_DEV_E_RANGE);
+        __syncthreads();
+        // pack 4 codes per byte: element (i, c) -> byte i*d/4 + c/4, bits 2*(c%4)
+        for (int e = threadIdx.x; e < W * d / 4; e += PK_THREADS) {
+            const int i = e / (d / 4), c4 = e % (d / 4);
+            const uint8_t* pk = ck + i * d + 4 * c4;
+            const uint8_t* pv = cv + i * d + 4 * c4;
+            slot[e] = (uint8_t)(pk[0] | (pk[1] << 2) | (pk[2] << 4) | (pk[3] << 6));
+            slot[W * d / 4 + e] = (uint8_t)(pv[0] | (pv[1] << 2) | (pv[2] << 4) | (pv[3] << 6));
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------------------------ fill (promote / copy)
+// Promotion writes bf16(off + code*scl), rounded once from the exact fp64 value
+// (§4.3: promotion reconstructs the same low-bit approximation in the execution
+// datatype).  Prefill copies prompt tokens into pages.
+__global__ void __launch_bounds__(PK_THREADS) k_fill(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ kp,
+                                                     const uint16_t* __restrict__ vp) {
+    const int l = layer >= 0 ? layer : blockIdx.x % g.L;
+    const int b = layer >= 0 ? blockIdx.x : blockIdx.x / g.L;
+    const int64_t u = unit_of(g, b, l);
+    UnitHdr* hdr = bf.hdr + u;
+    const int n_items = hdr->n_fill * g.h_kv;
+    const int W = g.W, d = g.d;
+    const int S = hdr->prompt_len;
+    for (int it = blockIdx.y; it < n_items; it += gridDim.y) {
+        const FillItem fi = bf.fill[u * g.n_windows + it / g.h_kv];
+        const int h = it % g.h_kv;
+        if (fi.dst_page < 0) {
+            if (threadIdx.x == 0) atomicOr(&hdr->status, QEVICT_DEV_E_POOL);
+            continue;
+        }
+        uint16_t* pg = bf.pages + u * (int64_t)g.n_pages * g.page_elems + (int64_t)fi.dst_page * g.page_elems;
+        uint16_t* dk = pg + (int64_t)(2 * h) * W * d;
+        uint16_t* dv = pg + (int64_t)(2 * h + 1) * W * d;
+        const int start = g.n_sink + fi.win * W;
+        if (fi.src_slot >= 0) {
+            const uint8_t* slot = bf.slots + u * (int64_t)g.n_slots * g.slot_bytes +
+                                  (int64_t)fi.src_slot * g.slot_bytes + (int64_t)h * g.slot_head_bytes;
+            const uint16_t* offK = (const uint16_t*)(slot + W * d / 2);
+            const uint16_t* sclK = offK + d;
+            const uint16_t* offV = sclK + d;
+            const uint16_t* sclV = offV + W;
+            for (int e = threadIdx.x; e < W * d; e += PK_THREADS) {
+                const int i = e / d, c = e % d;
+                const int kc = (slot[i * (d / 4) + c / 4] >> (2 * (c % 4))) & 3;
+                const int vc = (slot[W * d / 4 + i * (d / 4) + c / 4] >> (2 * (c % 4))) & 3;
+                const double kx = (double)fp16_bits_to_f32(offK[c]) + kc * (double)fp16_bits_to_f32(sclK[c]);
+                const double vx = (double)fp16_bits_to_f32(offV[i]) + vc * (double)fp16_bits_to_f32(sclV[i]);
+                dk[e] = f64_to_bf16(kx);
+                dv[e] = f64_to_bf16(vx);
+            }
+        } else {
+            const uint16_t* sk = kp + (((int64_t)b * g.h_kv + h) * g.S_max + start) * d;
+            const uint16_t* sv = vp + (((int64_t)b * g.h_kv + h) * g.S_max + start) * d;
+            int ntok = S - start;
+            if (ntok > W) ntok = W;
+            for (int e = threadIdx.x; e < W * d; e += PK_THREADS) {
+                const int i = e / d;
+                dk[e] = i < ntok ? sk[e] : (uint16_t)0;
+                dv[e] = i < ntok ? sv[e] : (uint16_t)0;
+            }
+        }
+    }
+}
+
+hipError_t launch_migrate(const Geo& g, const Bufs& bf, int layer, const uint16_t* kp, const uint16_t* vp,
+                          hipStream_t s) {
+    const int units = layer >= 0 ? g.B : g.B * g.L;
+    const int nb = 64;
+    hipLaunchKernelGGL(k_pack, dim3(units, nb), dim3(PK_THREADS), 0, s, g, bf, layer, kp, vp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_fill, dim3(units, nb), dim3(PK_THREADS), 0, s, g, bf, layer, kp, vp);
+    return hipGetLastError();
+}
+
+}  // namespace qv

@@ -1,0 +1,129 @@
+"""Lockstep harness: run the HIP path (through the C ABI) and the fp64 oracle on the
+same seeded inputs and compare after every step and every routing event.
+
+Bars (from the decode hot path's parity contract):
+* routing sets, window states, ledger flags, INT2 codes/params and the bf16
+  contents of Full / recent windows: bit-exact;
+* decode outputs: max_i |o_gpu - o_ref| / ||o_ref||_2 <= 2e-3 per (sequence, head);
+* window scores S_bar: |gpu - ref| <= 1e-4 absolute.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import qevict_oracle as O
+from recoverable_kv_cache_amd import binding as B
+from recoverable_kv_cache_amd import workload as WL
+from tests.oracle_helpers import cfg_from, f64
+
+O_TOL = 2e-3
+S_TOL = 1e-4
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of float64 values that are exactly bf16."""
+    return (np.asarray(x, np.float64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def rel_err(o_gpu: np.ndarray, o_ref: np.ndarray) -> float:
+    """max over heads of max_i |o_gpu - o_ref| / ||o_ref||_2."""
+    num = np.abs(o_gpu - o_ref).max(axis=-1)
+    den = np.linalg.norm(o_ref, axis=-1)
+    return float((num / den).max())
+
+
+def compare_unit(ex: B.UnitExport, unit: O.UnitOracle, tag: str, check_scores=True):
+    n_created = ex.n_windows
+    assert ex.n == unit.n, f"{tag}: n {ex.n} != {unit.n}"
+    assert ex.status == 0, f"{tag}: device status {ex.status}"
+    assert set(range(n_created)) == set(unit.win), f"{tag}: window sets differ"
+    table = unit.window_table()
+    for w in range(n_created):
+        st, has_led, dorm, start = table[w]
+        assert ex.state[w] == st, f"{tag}: window {w} state {ex.state[w]} != {st}"
+        assert bool(ex.has_ledger[w]) == has_led, f"{tag}: window {w} ledger flag"
+        assert bool(ex.dormant[w]) == dorm, f"{tag}: window {w} dormant flag"
+        assert ex.start_pos[w] == start
+        if has_led:
+            ref = O.canonical_ledger_bytes(unit.win[w].ledger)
+            assert ex.ledger[w] == ref, f"{tag}: window {w} ledger bytes differ"
+        if st in (O.LOCAL, O.FULL):
+            k, v = ex.kv[w]
+            W = unit.win[w]
+            np.testing.assert_array_equal(k, bf16_bits(W.k), err_msg=f"{tag}: window {w} K page")
+            np.testing.assert_array_equal(v, bf16_bits(W.v), err_msg=f"{tag}: window {w} V page")
+    ns = min(unit.cfg.n_sink, unit.n)
+    np.testing.assert_array_equal(ex.sink_k[:, :ns], bf16_bits(unit.sink_k[:, :ns]))
+    np.testing.assert_array_equal(ex.sink_v[:, :ns], bf16_bits(unit.sink_v[:, :ns]))
+    if check_scores:
+        ref = np.array([unit.score[w] for w in range(n_created)])
+        err = np.abs(ex.score[:n_created] - ref).max() if n_created else 0.0
+        assert err <= S_TOL, f"{tag}: score error {err}"
+        return float(err)
+    return 0.0
+
+
+class Lockstep:
+    def __init__(self, wl: WL.Workload, layer: int = 0, score_init=None, flags: int = 0, n_splits: int = 0,
+                 ocfg_over=None, device="cuda", n_layers=1):
+        self.wl = wl
+        self.layer = layer
+        self.lens = wl.prompt_lens()
+        cfg = B.make_config(wl, n_splits=n_splits, flags=flags, n_layers=n_layers)
+        self.st = B.QEvictState(cfg, self.lens, device=device)
+        ocfg = cfg_from(wl, promote=not (flags & B.QEVICT_F_NO_PROMOTE),
+                        score_every_step=not (flags & B.QEVICT_F_SCORE_ROUTE_ONLY), **(ocfg_over or {}))
+        self.ocfg = ocfg
+        self.units = [O.UnitOracle(ocfg, S) for S in self.lens]
+        self.score_init = score_init
+        self.max_o_err = 0.0
+        self.max_s_err = 0.0
+        self.events = 0
+        self.dev = device
+
+    def prefill(self):
+        qp, kp, vp = WL.prompt(self.wl, self.layer)
+        si = None
+        if self.score_init is not None:
+            si = torch.zeros((self.wl.batch, self.st.info.n_windows), dtype=torch.float64)
+            si[:, : self.score_init.shape[1]] = self.score_init[:, : si.shape[1]]
+            si = si.to(self.dev)
+        self.st.prefill_init(0, qp.to(self.dev), kp.to(self.dev), vp.to(self.dev), score_init=si)
+        for b, unit in enumerate(self.units):
+            S = self.lens[b]
+            init = None if self.score_init is None else self.score_init[b].numpy()
+            unit.prefill(f64(qp[b, :, :S]), f64(kp[b, :, :S]), f64(vp[b, :, :S]), score_init=init)
+        self.check("prefill")
+
+    def check(self, tag, check_scores=True):
+        torch.cuda.synchronize()
+        for b, unit in enumerate(self.units):
+            ex = self.st.export_unit(0, b)
+            e = compare_unit(ex, unit, f"{tag} b={b}", check_scores)
+            self.max_s_err = max(self.max_s_err, e)
+
+    def step(self, j: int, check_every: int = 1):
+        q, k, v = WL.decode_step(self.wl, self.layer, j)
+        out = torch.empty((self.wl.batch, self.wl.h_q, self.wl.d_head), dtype=torch.float32, device=self.dev)
+        self.st.decode_attn(0, q.to(self.dev), k.to(self.dev), v.to(self.dev), out)
+        o_gpu = out.cpu().numpy().astype(np.float64)
+        for b, unit in enumerate(self.units):
+            ref = unit.decode(f64(q[b]), f64(k[b]), f64(v[b]))
+            err = rel_err(o_gpu[b], ref["o"])
+            self.max_o_err = max(self.max_o_err, err)
+            assert err <= O_TOL, f"step {j} b={b}: output error {err}"
+        routed = (j + 1) % self.wl.omega == 0
+        if routed:
+            self.st.route(0)
+            for unit in self.units:
+                unit.route()
+            self.events += 1
+        if routed or (j + 1) % check_every == 0:
+            self.check(f"step {j}")
+
+    def run(self, steps: int, check_every: int = 1):
+        self.prefill()
+        for j in range(steps):
+            self.step(j, check_every)
+        return self

@@ -1,0 +1,144 @@
+"""GPU parity: the HIP path, called through the C ABI, against the fp64 oracle.
+
+Every case runs prefill + decode steps + routing events in lockstep and checks
+routing sets, ledger and pages bit-exactly, decode outputs within 2e-3 of
+||o||_2 and window scores within 1e-4 (see tests/gpu_harness.py).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import qevict_oracle as O
+from recoverable_kv_cache_amd import binding as B
+from recoverable_kv_cache_amd import workload as WL
+from tests.gpu_harness import Lockstep, bf16_bits, rel_err
+from tests.oracle_helpers import f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def test_tiny_config_full_lockstep():
+    """The tiny single-layer workload: 512-token prompt + 64 decode steps, 8 events."""
+    _print("case: tiny full lockstep")
+    ls = Lockstep(WL.TINY).run(64)
+    _print(f"tiny: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}")
+
+
+@pytest.mark.parametrize("rho,q", [(0.25, 0.70), (0.15, 0.70), (1.0, 0.0)], ids=["evict", "no-full-tier", "dense"])
+def test_tiny_budget_variants(rho, q):
+    _print(f"case: tiny rho={rho} q={q}")
+    wl = WL.TINY.with_(budget_frac=rho, quant_frac=q)
+    ls = Lockstep(wl).run(40)
+    _print(f"rho={rho}: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}")
+
+
+def test_drift_with_promotions_and_splits():
+    """Flat initial scores + drifting topic queries: windows are demoted, promoted
+    (Q -> F dequantize into a page) and re-demoted (reactivation)."""
+    _print("case: drift promotions")
+    wl = WL.TINY.with_(n_topics=4, topic_period=16, n_decode=64, n_outlier=2, budget_frac=0.25)
+    si = torch.zeros((1, 64), dtype=torch.float64)
+    ls = Lockstep(wl, score_init=si, n_splits=5).run(64)
+    unit = ls.units[0]
+    assert sum(e["promoted"] for e in unit.events) > 0
+    ex = ls.st.export_unit(0, 0)
+    assert ex.counters["n_full"] == unit.events[-1]["n_full"]
+
+
+def test_batched_ragged_prompts_gqa8_d128():
+    """Ragged prompt lengths, 8 query heads per KV head, d=128, W=32 (reduced sizes)."""
+    _print("case: ragged batch")
+    wl = WL.Workload("ragged", 1, 3, 16, 2, 128, 640, 24, 32, 4, 64, 8, 0.30, 0.70, prompt_len_min=300,
+                     n_outlier=2, n_topics=2, topic_period=8)
+    ls = Lockstep(wl).run(24)
+    _print(f"ragged: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}")
+
+
+def test_one_way_and_route_step_scoring_flags():
+    _print("case: flags")
+    wl = WL.TINY.with_(n_topics=4, topic_period=16, n_decode=32, budget_frac=0.25)
+    si = torch.zeros((1, 64), dtype=torch.float64)
+    ls = Lockstep(wl, score_init=si, flags=B.QEVICT_F_NO_PROMOTE | B.QEVICT_F_SCORE_ROUTE_ONLY).run(32)
+    assert sum(e["promoted"] for e in ls.units[0].events) == 0
+
+
+def test_short_prompt_edge_cases():
+    """Prompts shorter than the sinks, empty prompts and a prompt that ends on a window edge."""
+    for S in (0, 3, 4, 20):
+        _print(f"case: prompt_len={S}")
+        wl = WL.TINY.with_(prompt_len=S, n_decode=40, n_local=16, budget_frac=2.0)
+        Lockstep(wl).run(40)
+
+
+def test_forced_pack_and_promote_entry_points():
+    """qevict_pack_int2 / qevict_promote against the oracle's codec and Algorithm 1."""
+    _print("case: forced pack/promote")
+    wl = WL.TINY.with_(n_decode=8)
+    ls = Lockstep(wl)
+    ls.prefill()
+    unit = ls.units[0]
+    full = [w for w, W in unit.win.items() if W.state == O.FULL]
+    quant = [w for w, W in unit.win.items() if W.state == O.QUANT]
+    assert full and quant
+    # demote the Full windows, then promote two Quantized ones
+    ids = torch.tensor([full], dtype=torch.int32, device="cuda")
+    ls.st.pack_int2(0, ids)
+    for w in full:
+        W = unit.win[w]
+        W.ledger = O.quantize_window(W.k, W.v, unit.win_start(w)) if W.ledger is None else W.ledger
+        W.ledger.dormant = False
+        W.k = W.v = None
+        W.state = O.QUANT
+    ls.check("after pack")
+    prom = quant[:2]
+    ls.st.promote(0, torch.tensor([prom], dtype=torch.int32, device="cuda"))
+    for w in prom:
+        W = unit.win[w]
+        W.k, W.v = O.to_bf16(W.ledger.k_hat()), O.to_bf16(W.ledger.v_hat())
+        W.ledger.dormant = True
+        W.state = O.FULL
+    ls.check("after promote")
+    for j in range(8):
+        ls.step(j)
+
+
+def test_prefill_column_sums_mid_size():
+    """MFMA column sums vs the oracle's dense causal softmax at S=1536, d=128, G=4."""
+    _print("case: prefill column sums S=1536")
+    wl = WL.Workload("mid", 1, 1, 8, 2, 128, 1536, 8, 32, 4, 256, 8, 0.2, 0.7, n_outlier=4, n_topics=4)
+    cfg = B.make_config(wl)
+    st = B.QEvictState(cfg, [1536])
+    qp, kp, vp = WL.prompt(wl, 0)
+    st.prefill_init(0, qp.cuda(), kp.cuda(), vp.cuda())
+    torch.cuda.synchronize()
+    lse_gpu, col_gpu = (t.cpu().numpy() for t in st.workspace_views())
+    col_ref = O.prefill_column_sums(f64(qp[0]), f64(kp[0]))
+    err = np.abs(col_gpu[0] - col_ref).max()
+    _print(f"column-sum max abs err {err:.2e}")
+    assert err < 2e-5
+    for h, u in [(0, 0), (3, 777), (7, 1535)]:
+        ref = O.row_lse(f64(qp[0])[h][u], f64(kp[0])[h // 4][: u + 1]) / math.log(2)
+        assert abs(lse_gpu[0, h, u] - ref) < 1e-4
+    ex = st.export_unit(0, 0)
+    unit = O.UnitOracle(O.OracleConfig(8, 2, 128, 32, 4, 256, 8, 0.7, 0.2, 8), 1536)
+    unit.prefill(f64(qp[0]), f64(kp[0]), f64(vp[0]))
+    ref = np.array([unit.score[w] for w in range(ex.n_windows)])
+    assert np.abs(ex.score[: ex.n_windows] - ref).max() < 1e-4
+    assert abs(ex.score[: ex.n_windows].sum() + ex.sink_mass - 1536) < 1e-3
+
+
+def test_determinism_bitwise():
+    """Two identical runs give bit-identical state and outputs."""
+    _print("case: determinism")
+    outs = []
+    for _ in range(2):
+        ls = Lockstep(WL.TINY.with_(budget_frac=0.25)).run(16)
+        ex = ls.st.export_unit(0, 0)
+        outs.append((ex.score.tobytes(), b"".join(ex.ledger[w] for w in sorted(ex.ledger)), ex.state.tobytes()))
+    assert outs[0] == outs[1]
