@@ -1,0 +1,256 @@
+"""Decode-attention throughput of the QEvict hot path on one MI355X.
+
+A timed "step" is one generated token of the whole path for every layer:
+qevict_decode_attn (append + split-K attention over sinks / recent / Full bf16 /
+Quantized INT2 windows + combine + window-mass score update) for each of the L
+layers, plus one routing event over all layers (TopK + pack / promote +
+compaction) after every Omega-th step.  Inputs are resident in HBM before the
+timed region starts.  The prompt-attention column sums that initialise the
+scores run once per layer before timing (reported as prefill_s).
+
+Workload: Llama-3-8B-shaped stack, 32 layers, 32 query / 8 KV heads of 128,
+batch 1, 32K-token prompt, windows of 32, 4 sinks, 256 recent, budget 20% of
+the full bf16 cache, quantized share 0.70, INT2.
+
+    python bench.py [--gpus 1] [--steps 128] [--warmup 16]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E peak, GB/s
+METRIC = "decode-attn tokens/s + achieved HBM GB/s (% peak) at 32K ctx; route µs/event"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("qevict_decode.hip", "qevict_common.h", "qevict_internal.h"):
+        h.update(open(os.path.join(ROOT, "recoverable_kv_cache_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(wl, budget_s: float = 20.0) -> dict:
+    """Time the fp64 oracle's decode step on the host (layer 0, sequence 0), with a
+    synthetic initial score instead of the prompt column sums (those alone are
+    ~9 TFLOP of fp64 per layer on a 32K prompt)."""
+    import numpy as np
+    import torch
+    from oracle import qevict_oracle as O
+    from recoverable_kv_cache_amd import workload as WL
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    ocfg = O.OracleConfig(wl.h_q, wl.h_kv, wl.d_head, wl.window, wl.n_sink, wl.n_local, wl.omega,
+                          wl.quant_frac, wl.budget_frac, wl.n_decode)
+    S = wl.prompt_len
+    qp, kp, vp = WL.prompt(wl.with_(batch=1), 0)
+    f = lambda t: t.to(torch.float64).numpy()
+    unit = O.UnitOracle(ocfg, S)
+    n_win = (S - wl.n_sink + wl.window - 1) // wl.window
+    t0 = time.perf_counter()
+    unit.prefill(f(qp[0]), f(kp[0]), f(vp[0]), score_init=WL.init_scores(wl, 0, n_win)[0].numpy())
+    setup_s = time.perf_counter() - t0
+    del qp
+    times = []
+    j = 0
+    t_start = time.perf_counter()
+    while j < wl.n_decode and (time.perf_counter() - t_start < budget_s or j < 2):
+        q, k, v = WL.decode_step(wl.with_(batch=1), 0, j)
+        t1 = time.perf_counter()
+        unit.decode(f(q[0]), f(k[0]), f(v[0]))
+        times.append(time.perf_counter() - t1)
+        j += 1
+    per_layer_step = statistics.mean(times)
+    return {"value": round(wl.batch / (per_layer_step * wl.n_layers), 4), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, layer 0 / sequence 0 of the same workload, {len(times)} decode steps "
+                      f"({per_layer_step * 1e3:.0f} ms per layer-step, setup {setup_s:.1f} s), "
+                      f"extrapolated x{wl.n_layers} layers x batch {wl.batch}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="llama8b_32k")
+    ap.add_argument("--n-splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy (for scaling rocprofv3 byte counters) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from recoverable_kv_cache_amd import binding as B
+    from recoverable_kv_cache_amd import workload as WL
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": a.numel()}))
+        return
+
+    wl = {w.name: w for w in WL.ALL_WORKLOADS}[args.workload]
+    if args.steps + args.warmup > wl.n_decode:
+        sys.exit(f"--steps + --warmup must be <= {wl.n_decode}")
+    cfg = B.make_config(wl, n_splits=args.n_splits)
+    lens = wl.prompt_lens()
+    st = B.QEvictState(cfg, lens, device=dev)
+    log(f"[bench] {wl.name}: arena {st.info.arena_bytes / 2**30:.2f} GiB, splits {st.info.n_splits}, "
+        f"K_f {st.info.max_K_f}, K_q {st.info.max_K_q}")
+
+    # ---- prefill every layer (column sums on MFMA), inputs generated on the GPU
+    torch.cuda.synchronize()
+    t_pf = 0.0
+    for l in range(wl.n_layers):
+        qp, kp, vp = WL.prompt(wl, l, device=dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        st.prefill_init(l, qp, kp, vp)
+        torch.cuda.synchronize()
+        t_pf += time.perf_counter() - t0
+        del qp, kp, vp
+        if l % 8 == 0:
+            log(f"[bench] prefill layer {l} done ({t_pf:.1f} s so far)")
+    assert st.poll_status() == 0, "device status after prefill"
+
+    # ---- decode inputs for every (step, layer), resident in HBM
+    n_total = args.warmup + args.steps
+    inputs = [[WL.decode_step(wl, l, j, device=dev) for l in range(wl.n_layers)] for j in range(n_total)]
+    out = torch.empty((wl.batch, wl.h_q, wl.d_head), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log("[bench] inputs ready")
+
+    def new_event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def run_step(j, timing=None, route_ev=None):
+        for l in range(wl.n_layers):
+            if timing is not None:
+                st.time_next_decode(timing[l][0], timing[l][1])
+            q, k, v = inputs[j][l]
+            st.decode_attn(l, q, k, v, out)
+        if (j + 1) % wl.omega == 0:
+            if route_ev is not None:
+                route_ev[0].record()
+            st.route(-1)
+            if route_ev is not None:
+                route_ev[1].record()
+            return True
+        return False
+
+    for j in range(args.warmup):
+        run_step(j)
+    torch.cuda.synchronize()
+    kv0 = [st.step_bytes(l) for l in range(wl.n_layers)]
+
+    # ---- timed region: wall-clock events around all steps, events around every
+    # split-K kernel and around every routing event
+    kev = [[(new_event(), new_event()) for _ in range(wl.n_layers)] for _ in range(args.steps)]
+    rev = [(new_event(), new_event()) for _ in range(args.steps // wl.omega + 1)]
+    start, stop = new_event(), new_event()
+    torch.cuda.synchronize()
+    start.record()
+    n_route = 0
+    for i in range(args.steps):
+        j = args.warmup + i
+        if run_step(j, timing=kev[i], route_ev=rev[n_route]):
+            n_route += 1
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    route_ms = [rev[r][0].elapsed_time(rev[r][1]) for r in range(n_route)]
+    kern_ms = [kev[i][l][0].elapsed_time(kev[i][l][1]) for i in range(args.steps) for l in range(wl.n_layers)]
+    kv1 = [st.step_bytes(l) for l in range(wl.n_layers)]
+    status = st.poll_status()
+    assert status == 0, f"device status {status}"
+
+    avg_kernel_s = statistics.mean(kern_ms) * 1e-3
+    kv_per_launch = statistics.mean([(a[0] + b[0]) / 2 for a, b in zip(kv0, kv1)])
+    io_per_launch = kv0[0][1]
+    alg_bytes = kv_per_launch + io_per_launch
+    achieved_gbps = alg_bytes / avg_kernel_s / 1e9
+    tokens_per_s = wl.batch * args.steps / (total_ms * 1e-3)
+    decode_ms = total_ms - sum(route_ms)
+    decode_tokens_per_s = wl.batch * args.steps / (decode_ms * 1e-3)
+
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", f"decode_split_{wl.name}_traffic.json")
+    if os.path.exists(tf):
+        rec = json.load(open(tf))
+        if rec.get("source_hash") == source_hash():
+            traffic = rec.get("bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        cpu = cpu_baseline(wl, args.cpu_budget_s)
+
+    rp = sorted(route_ms)
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": wl.n_layers, "batch": wl.batch, "h_q": wl.h_q, "h_kv": wl.h_kv,
+                   "d_head": wl.d_head, "prompt_len": wl.prompt_len, "window": wl.window, "n_sink": wl.n_sink,
+                   "n_local": wl.n_local, "omega": wl.omega, "budget_frac": wl.budget_frac,
+                   "quant_frac": wl.quant_frac, "storage": "bf16 + int2", "n_splits": st.info.n_splits,
+                   "K_f": st.info.max_K_f, "K_q": st.info.max_K_q},
+        "decode_attn_tokens_per_s": round(decode_tokens_per_s, 2),
+        "route_us_per_event": {"mean": round(statistics.mean(route_ms) * 1e3, 2) if route_ms else None,
+                               "p50": round(rp[len(rp) // 2] * 1e3, 2) if rp else None,
+                               "p99": round(rp[min(len(rp) - 1, math.ceil(0.99 * len(rp)) - 1)] * 1e3, 2) if rp else None,
+                               "events": n_route, "scope": f"all {wl.n_layers} layers x batch {wl.batch}"},
+        "hbm_gbps_split_kernel": round(achieved_gbps, 1),
+        "hbm_frac_of_peak": round(achieved_gbps / HBM_PEAK_GBPS, 4),
+        "prefill_s": round(t_pf, 3),
+        "roofline": {"bound": "hbm", "kernel": B.load_library().qevict_decode_kernel_name().decode(),
+                     "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": int(alg_bytes),
+                     "avg_launch_us": round(avg_kernel_s * 1e6, 3), "launches": len(kern_ms)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -202,8 +202,19 @@ qevict_status qevict_poll_status(qevict_state* st, uint32_t* status, void* strea
 qevict_status qevict_export_unit(qevict_state* st, int32_t layer, int32_t b, void* host_buf,
                                  size_t bytes, size_t* written, void* stream);
 
-/* Number of decode kernels launched per qevict_decode_attn call and the name of
- * the dominant one, for profilers.  */
+/* Profiling aid: the next qevict_decode_attn call records ev_before (a
+ * hipEvent_t) on its stream right before the split-K attention kernel and
+ * ev_after right after it; then both are forgotten.  NULL disables. */
+qevict_status qevict_time_next_decode(qevict_state* st, void* ev_before, void* ev_after);
+
+/* Bytes the next decode step of `layer` must move, summed over the batch
+ * [host outputs]: kv_bytes = bf16 K/V of the sink, recent and Full tokens
+ * (4 * h_kv * d per token) + whole INT2 slots of Quantized windows (codes and
+ * fp16 parameters); io_bytes = q in (bf16), o out (fp32), k/v in (bf16).  Syncs. */
+qevict_status qevict_step_bytes(qevict_state* st, int32_t layer, int64_t* kv_bytes, int64_t* io_bytes,
+                                void* stream);
+
+/* Name of the dominant decode kernel (the split-K attention), for profilers. */
 const char* qevict_decode_kernel_name(void);
 
 /* Message of the last failed call on this thread ("" if none). */

@@ -26,7 +26,8 @@ DEV_E_POOL, DEV_E_WINDOW, DEV_E_RANGE, DEV_E_LIST = 1, 2, 4, 8
 EXPORTED_SYMBOLS = (
     "qevict_capacities", "qevict_plan", "qevict_create", "qevict_destroy", "qevict_prefill_init",
     "qevict_decode_attn", "qevict_route", "qevict_pack_int2", "qevict_promote", "qevict_poll_status",
-    "qevict_export_unit", "qevict_decode_kernel_name", "qevict_last_error",
+    "qevict_export_unit", "qevict_decode_kernel_name", "qevict_last_error", "qevict_time_next_decode",
+    "qevict_step_bytes",
 )
 
 
@@ -83,6 +84,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qevict_promote.argtypes = [P, I, P, I, P]
     lib.qevict_poll_status.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
     lib.qevict_export_unit.argtypes = [P, I, I, P, Z, ctypes.POINTER(Z), P]
+    lib.qevict_time_next_decode.argtypes = [P, P, P]
+    lib.qevict_step_bytes.argtypes = [P, I, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64), P]
     lib.qevict_decode_kernel_name.restype = ctypes.c_char_p
     lib.qevict_last_error.restype = ctypes.c_char_p
     for name in EXPORTED_SYMBOLS:
@@ -255,6 +258,16 @@ class QEvictState:
     def promote(self, layer: int, win_ids, stream=None):
         _expect(win_ids, (self.cfg.batch, win_ids.shape[-1]), "int32", self.device, "win_ids")
         _check(self.lib.qevict_promote(self.handle, layer, _ptr(win_ids), win_ids.shape[-1], _stream(stream)))
+
+    def time_next_decode(self, ev_before, ev_after):
+        """Record torch.cuda.Event pair around the split-K kernel of the next decode_attn."""
+        _check(self.lib.qevict_time_next_decode(self.handle, ctypes.c_void_p(ev_before.cuda_event),
+                                                ctypes.c_void_p(ev_after.cuda_event)))
+
+    def step_bytes(self, layer: int, stream=None) -> tuple[int, int]:
+        kv, io = ctypes.c_int64(), ctypes.c_int64()
+        _check(self.lib.qevict_step_bytes(self.handle, layer, ctypes.byref(kv), ctypes.byref(io), _stream(stream)))
+        return kv.value, io.value
 
     def poll_status(self, stream=None) -> int:
         s = ctypes.c_uint32()

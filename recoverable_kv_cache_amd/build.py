@@ -21,6 +21,9 @@ HIPCC_FLAGS = [
     # no packed-FP32 instructions (v_pk_*_f32) anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
+    # keep branch tails apart: merging them into pointer phis would push the decode
+    # kernel's operand buffers out of registers into scratch memory
+    "-mllvm", "-simplifycfg-sink-common=false",
 ]
 
 

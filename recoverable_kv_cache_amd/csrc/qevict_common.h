@@ -54,4 +54,35 @@ __device__ __forceinline__ T wave_xor(T v, int mask) {
     return __shfl_xor(v, mask, 64);
 }
 
+// x from lane (lane ^ M), M a power of two: DPP quad permutes for 1 and 2,
+// ds_swizzle (bit mode, within 32 lanes) for 4..16, ds_bpermute for 32.
+template <int M>
+__device__ __forceinline__ float xor_lane(float x) {
+    const int v = __float_as_int(x);
+    if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));
+    else if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));
+    else if constexpr (M < 32) return __int_as_float(__builtin_amdgcn_ds_swizzle(v, 0x1F | (M << 10)));
+    else return __shfl_xor(x, 32, 64);
+}
+
+// sum / max over the lanes that differ in bits [log2 LO, log2 HI)
+template <int LO, int HI>
+__device__ __forceinline__ float lanes_sum(float x) {
+    if constexpr (LO < HI) {
+        x += xor_lane<LO>(x);
+        return lanes_sum<LO * 2, HI>(x);
+    } else {
+        return x;
+    }
+}
+template <int LO, int HI>
+__device__ __forceinline__ float lanes_max(float x) {
+    if constexpr (LO < HI) {
+        x = fmaxf(x, xor_lane<LO>(x));
+        return lanes_max<LO * 2, HI>(x);
+    } else {
+        return x;
+    }
+}
+
 }  // namespace qv

@@ -1,5 +1,6 @@
 // Host side of the C ABI: validation, byte accounting (Eq. 3), arena layout,
 // kernel launch order.  No device allocation happens here.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -51,6 +52,7 @@ qevict_status validate(const qevict_config* c) {
     if (c->h_kv < 1 || c->h_q < c->h_kv || c->h_q % c->h_kv) return fail(QEVICT_E_INVALID, "h_q must be a multiple of h_kv");
     int G = c->h_q / c->h_kv;
     if (G != 1 && G != 2 && G != 4 && G != 8) return fail(QEVICT_E_INVALID, "h_q / h_kv must be 1, 2, 4 or 8");
+    if (c->h_q > 64) return fail(QEVICT_E_INVALID, "h_q must be <= 64");
     if (c->d_head != 64 && c->d_head != 128) return fail(QEVICT_E_INVALID, "d_head must be 64 or 128");
     if (c->window != 16 && c->window != 32 && c->window != 64) return fail(QEVICT_E_INVALID, "window must be 16, 32 or 64");
     if (c->n_sink < 0 || c->n_sink > 64) return fail(QEVICT_E_INVALID, "n_sink must be in [0, 64]");
@@ -136,7 +138,7 @@ qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, La
     g.page_elems = g.h_kv * 2 * g.W * g.d;
     g.slot_head_bytes = g.W * g.d / 2 + 4 * g.d + 4 * g.W;
     g.slot_bytes = g.h_kv * g.slot_head_bytes;
-    g.sink_elems = g.h_kv * 2 * (g.n_sink > 0 ? g.n_sink : 1) * g.d;
+    g.sink_elems = g.h_kv * 2 * sink_width(g.n_sink) * g.d;
     const size_t U = (size_t)g.B * g.L;
     size_t sz[20];
     sz[O_HDR] = U * sizeof(UnitHdr);
@@ -203,6 +205,7 @@ struct qevict_state {
     std::vector<int32_t> prompt_lens, K_f, K_q;
     std::vector<int32_t> steps;
     std::vector<uint8_t> prefilled;
+    hipEvent_t ev_before = nullptr, ev_after = nullptr;   // one-shot timing of the split kernel
 };
 
 extern "C" {
@@ -338,10 +341,49 @@ qevict_status qevict_decode_attn(qevict_state* st, int32_t layer, const void* q,
     hipStream_t hs = (hipStream_t)stream;
     const Geo& g = st->lay.g;
     HIP_TRY(launch_append(g, st->bf, layer, (const uint16_t*)k_new, (const uint16_t*)v_new, hs));
+    if (st->ev_before) HIP_TRY(hipEventRecord(st->ev_before, hs));
     HIP_TRY(launch_decode(g, st->bf, layer, (const uint16_t*)q, hs));
+    if (st->ev_after) HIP_TRY(hipEventRecord(st->ev_after, hs));
+    st->ev_before = st->ev_after = nullptr;
     HIP_TRY(launch_combine(g, st->bf, layer, out, hs));
     HIP_TRY(launch_mass(g, st->bf, layer, hs));
     st->steps[layer] += 1;
+    return QEVICT_OK;
+}
+
+qevict_status qevict_time_next_decode(qevict_state* st, void* ev_before, void* ev_after) {
+    if (!st) return fail(QEVICT_E_INVALID, "null state");
+    st->ev_before = (hipEvent_t)ev_before;
+    st->ev_after = (hipEvent_t)ev_after;
+    return QEVICT_OK;
+}
+
+qevict_status qevict_step_bytes(qevict_state* st, int32_t layer, int64_t* kv_bytes, int64_t* io_bytes, void* stream) {
+    qevict_status s = check_layer(st, layer, false);
+    if (s) return s;
+    if (!kv_bytes || !io_bytes) return fail(QEVICT_E_INVALID, "null output");
+    const Geo& g = st->lay.g;
+    HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
+    int64_t kv = 0;
+    std::vector<WinRec> win(g.n_windows);
+    for (int b = 0; b < g.B; ++b) {
+        const int64_t u = unit_of(g, b, layer);
+        UnitHdr hdr;
+        HIP_TRY(hipMemcpy(&hdr, st->bf.hdr + u, sizeof hdr, hipMemcpyDeviceToHost));
+        HIP_TRY(hipMemcpy(win.data(), st->bf.win + u * g.n_windows, win.size() * sizeof(WinRec), hipMemcpyDeviceToHost));
+        const int n = hdr.n + 1;   // the next step attends over one more token
+        const int64_t tok = 4LL * g.h_kv * g.d;
+        kv += (int64_t)(n < g.n_sink ? n : g.n_sink) * tok;
+        for (int w = 0; w < g.n_windows; ++w) {
+            const int start = g.n_sink + w * g.W;
+            if (start >= n) break;
+            const int ntok = n - start < g.W ? n - start : g.W;
+            if (win[w].state == ST_LOCAL || win[w].state == ST_FULL) kv += (int64_t)ntok * tok;
+            else if (win[w].state == ST_QUANT) kv += g.slot_bytes;
+        }
+    }
+    *kv_bytes = kv;
+    *io_bytes = (int64_t)g.B * g.h_q * g.d * (2 + 4) + 2LL * g.B * g.h_kv * g.d * 2;   // q in, o out, k/v in
     return QEVICT_OK;
 }
 
@@ -438,36 +480,64 @@ qevict_status qevict_export_unit(qevict_state* st, int32_t layer, int32_t b, voi
         put(rec, sizeof rec);
         put(&score[w], 8);
     }
+    std::vector<uint8_t> canon(g.slot_bytes);
     for (int w = 0; w < n_created; ++w)
-        if ((win[w].flags & WF_LEDGER) && win[w].slot >= 0)
-            put(slots.data() + (size_t)win[w].slot * g.slot_bytes, g.slot_bytes);
+        if ((win[w].flags & WF_LEDGER) && win[w].slot >= 0) {
+            const uint8_t* sl = slots.data() + (size_t)win[w].slot * g.slot_bytes;
+            std::fill(canon.begin(), canon.end(), 0);
+            for (int h = 0; h < g.h_kv; ++h) {
+                const uint8_t* src = sl + (size_t)h * g.slot_head_bytes;
+                uint8_t* dst = canon.data() + (size_t)h * g.slot_head_bytes;
+                const int cb = g.W * g.d / 4;
+                for (int t = 0; t < g.W; ++t)
+                    for (int c = 0; c < g.d; ++c) {
+                        const int kc = (src[lay_kc_byte(t, c, g.d, g.W)] >> lay_kc_shift(c)) & 3;
+                        const int vc = (src[cb + lay_vc_byte(t, c, g.d, g.W)] >> lay_vc_shift(t)) & 3;
+                        dst[t * (g.d / 4) + c / 4] |= (uint8_t)(kc << (2 * (c % 4)));
+                        dst[cb + t * (g.d / 4) + c / 4] |= (uint8_t)(vc << (2 * (c % 4)));
+                    }
+                memcpy(dst + 2 * cb, src + 2 * cb, (size_t)4 * g.d);     // K offset, K scale
+                const uint16_t* ov = (const uint16_t*)(src + 2 * cb + 4 * g.d);
+                uint16_t* dv = (uint16_t*)(dst + 2 * cb + 4 * g.d);
+                for (int t = 0; t < g.W; ++t) {
+                    dv[t] = ov[lay_vp(t, g.W)];
+                    dv[g.W + t] = ov[g.W + lay_vp(t, g.W)];
+                }
+            }
+            put(canon.data(), g.slot_bytes);
+        }
+    // pages: device layout -> [K/V][h][W][d], tokens >= ntok zeroed
     std::vector<uint16_t> tmp(g.page_elems);
+    const int Ws = sink_width(g.n_sink);
+    auto unpage = [&](const uint16_t* pg, int Wp, int ntok, uint16_t* dst) {
+        for (int kv = 0; kv < 2; ++kv)
+            for (int h = 0; h < g.h_kv; ++h) {
+                const uint16_t* blk = pg + (size_t)(h * 2 + kv) * Wp * g.d;
+                for (int i = 0; i < Wp; ++i)
+                    for (int c = 0; c < g.d; ++c) {
+                        const int o = kv == 0 ? lay_k(i, c, g.d, Wp) : lay_v(i, c, g.d, Wp);
+                        dst[((size_t)(kv * g.h_kv + h) * Wp + i) * g.d + c] = i < ntok ? blk[o] : 0;
+                    }
+            }
+    };
     for (int w = 0; w < n_created; ++w) {
         const int st_ = win[w].state;
         if ((st_ == ST_LOCAL || st_ == ST_FULL) && win[w].page >= 0) {
-            const uint16_t* pg = pages.data() + (size_t)win[w].page * g.page_elems;
             int ntok = hdr.n - (g.n_sink + w * g.W);
             if (ntok > g.W) ntok = g.W;
-            // page layout [h][K/V][W][d] -> export [K/V][h][W][d], tokens >= ntok zeroed
-            for (int kv = 0; kv < 2; ++kv)
-                for (int h = 0; h < g.h_kv; ++h)
-                    for (int i = 0; i < g.W; ++i)
-                        for (int c = 0; c < g.d; ++c)
-                            tmp[((size_t)(kv * g.h_kv + h) * g.W + i) * g.d + c] =
-                                i < ntok ? pg[((size_t)(h * 2 + kv) * g.W + i) * g.d + c] : 0;
+            unpage(pages.data() + (size_t)win[w].page * g.page_elems, g.W, ntok, tmp.data());
             put(tmp.data(), (size_t)g.page_elems * 2);
         }
     }
     {
-        const int ns = g.n_sink > 0 ? g.n_sink : 1;
-        std::vector<uint16_t> sk((size_t)2 * g.h_kv * g.n_sink * g.d);
-        for (int kv = 0; kv < 2; ++kv)
-            for (int h = 0; h < g.h_kv; ++h)
-                for (int i = 0; i < g.n_sink; ++i)
-                    for (int c = 0; c < g.d; ++c)
-                        sk[((size_t)(kv * g.h_kv + h) * g.n_sink + i) * g.d + c] =
-                            i < hdr.n ? sinks[((size_t)(h * 2 + kv) * ns + i) * g.d + c] : 0;
-        put(sk.data(), sk.size() * 2);
+        std::vector<uint16_t> sk((size_t)2 * g.h_kv * Ws * g.d);
+        unpage(sinks.data(), Ws, hdr.n < g.n_sink ? hdr.n : g.n_sink, sk.data());
+        // keep the first n_sink tokens of each block
+        std::vector<uint16_t> out((size_t)2 * g.h_kv * g.n_sink * g.d);
+        for (int b2 = 0; b2 < 2 * g.h_kv; ++b2)
+            memcpy(out.data() + (size_t)b2 * g.n_sink * g.d, sk.data() + (size_t)b2 * Ws * g.d,
+                   (size_t)g.n_sink * g.d * 2);
+        put(out.data(), out.size() * 2);
     }
     if (written) *written = at;
     return QEVICT_OK;

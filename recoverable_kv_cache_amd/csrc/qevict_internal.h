@@ -45,7 +45,7 @@ struct PackItem {    // quantize a window once: source bf16 -> slot
 struct FillItem {    // write a bf16 page: promote from a slot, or copy from the prompt
     int32_t win;
     int32_t dst_page;
-    int32_t src_slot;    // >= 0: promote (dequantize); -1: copy prompt tokens
+    int32_t src_slot;    // >= 0: promote (dequantize); -1: copy prompt tokens; -2: zero page
     int32_t pad;
 };
 
@@ -76,7 +76,7 @@ struct Geo {
     int32_t page_elems;   // bf16 elements per page = h_kv * 2 * W * d
     int32_t slot_head_bytes;  // W*d/2 + 4d + 4W
     int32_t slot_bytes;   // h_kv * slot_head_bytes
-    int32_t sink_elems;   // h_kv * 2 * n_sink * d
+    int32_t sink_elems;   // h_kv * 2 * Ws * d, Ws = sink_width(n_sink)
     uint32_t flags;
 };
 
@@ -98,10 +98,55 @@ struct Bufs {
     float* part_acc;        // [U][n_splits][h_q][d]
     uint16_t* pages;        // [U][n_pages][h_kv][2][W][d]   bf16
     uint8_t* slots;         // [U][n_slots][h_kv][slot_head_bytes]
-    uint16_t* sinks;        // [U][h_kv][2][n_sink][d]       bf16
+    uint16_t* sinks;        // [U][h_kv] pages of Ws tokens (same layout as a window page)
 };
 
 __host__ __device__ inline int64_t unit_of(const Geo& g, int b, int l) { return (int64_t)b * g.L + l; }
+
+// ------------------------------------------------------------------ in-HBM layouts
+// The decode kernel feeds 16x16x16 MFMA tiles straight from HBM, so pages and
+// slots are stored in the order a lane consumes them.  One head of a window of
+// W tokens (NT = W/16 tiles of 16 tokens), D channels, CQ = D/4 channels per
+// lane group, MB = D/16 channel blocks.  t = 16*tile + r, c = CQ*qg + cc.
+//
+// A "chunk" is up to 32 tokens (TPC = min(W, 32)/16 tiles); NCH = W/TPC/16 chunks.
+// bf16 page of one head: K block (W*D) then V block (W*D).
+//   K (t, c): (((ch*16 + r)*4 + qg)*TPC + tc)*CQ + cc        t = 32*ch + 16*tc + r
+//             (a lane reads the CQ channels of its token row for every tile of a chunk)
+//   V (t, c): ((((c%16)*4 + r/4)*NT + tile)*MB + c/16)*4 + r%4
+//             (a lane reads, per tile, 4 tokens x MB channel blocks of one channel row)
+// INT2 slot of one head (same byte count as the canonical record):
+//   K codes [W*D/4]: code (t, c) in byte (((ch*16 + r)*4 + qg)*TPC + tc)*(CQ/4) + cc/4, bits 2*(cc%4)
+//   V codes [W*D/4]: code (t, c) in byte (((c%16)*4 + r/4)*NT + tile)*MB + c/16, bits 2*(r%4)
+//   K offset [D], K scale [D] (fp16, channel order), V offset [W], V scale [W] (fp16) with
+//   token t at ((r/4)*NT + tile)*4 + r%4.
+__host__ __device__ inline int lay_tpc(int W) { return (W < 32 ? W : 32) / 16; }
+__host__ __device__ inline int lay_k(int t, int c, int D, int W) {
+    const int CQ = D / 4, TPC = lay_tpc(W);
+    const int ch = t / (16 * TPC), tc = (t / 16) % TPC, r = t & 15;
+    return (((ch * 16 + r) * 4 + c / CQ) * TPC + tc) * CQ + c % CQ;
+}
+__host__ __device__ inline int lay_v(int t, int c, int D, int W) {
+    const int NT = W / 16, MB = D / 16;
+    return ((((c & 15) * 4 + (t & 15) / 4) * NT + (t >> 4)) * MB + c / 16) * 4 + (t & 3);
+}
+__host__ __device__ inline int lay_kc_byte(int t, int c, int D, int W) {
+    const int CQ = D / 4, TPC = lay_tpc(W);
+    const int ch = t / (16 * TPC), tc = (t / 16) % TPC, r = t & 15;
+    return (((ch * 16 + r) * 4 + c / CQ) * TPC + tc) * (CQ / 4) + (c % CQ) / 4;
+}
+__host__ __device__ inline int lay_kc_shift(int c) { return 2 * (c & 3); }
+__host__ __device__ inline int lay_vc_byte(int t, int c, int D, int W) {
+    const int NT = W / 16, MB = D / 16;
+    return (((c & 15) * 4 + (t & 15) / 4) * NT + (t >> 4)) * MB + c / 16;
+}
+__host__ __device__ inline int lay_vc_shift(int t) { return 2 * (t & 3); }
+__host__ __device__ inline int lay_vp(int t, int W) {
+    const int NT = W / 16;
+    return (((t & 15) / 4) * NT + (t >> 4)) * 4 + (t & 3);
+}
+// tokens held by the sink block: n_sink rounded up to a supported window size
+__host__ __device__ inline int sink_width(int n_sink) { return n_sink <= 16 ? 16 : (n_sink <= 32 ? 32 : 64); }
 
 // ---------------------------------------------------------------- launchers (host side)
 hipError_t launch_init(const Geo& g, const Bufs& bf, const int32_t* prompt_lens_dev, const int32_t* kf_dev,

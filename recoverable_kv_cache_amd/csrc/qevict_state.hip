@@ -47,27 +47,29 @@ __global__ void k_append(Geo g, Bufs bf, int layer, const uint16_t* __restrict__
     const int64_t u = unit_of(g, b, layer);
     UnitHdr* hdr = bf.hdr + u;
     const int p = hdr->n;
-    uint16_t* dst;
-    int64_t head_stride;
+    uint16_t* blk;
+    int Wp, i;
     if (p < g.n_sink) {
-        const int ns = g.n_sink;
-        dst = bf.sinks + u * g.sink_elems + (int64_t)p * g.d;
-        head_stride = (int64_t)ns * g.d;   // K/V blocks of one head are ns*d apart; heads 2*ns*d apart
+        blk = bf.sinks + u * g.sink_elems;
+        Wp = sink_width(g.n_sink);
+        i = p;
     } else {
-        const int w = (p - g.n_sink) / g.W, i = (p - g.n_sink) % g.W;
+        const int w = (p - g.n_sink) / g.W;
+        i = (p - g.n_sink) % g.W;
         const WinRec rec = w < g.n_windows ? bf.win[u * g.n_windows + w] : WinRec{ST_NONE, -1, -1, 0};
         if (rec.state != ST_LOCAL || rec.page < 0) {
             if (threadIdx.x == 0) atomicOr(&hdr->status, QEVICT_DEV_E_WINDOW);
             return;
         }
-        dst = bf.pages + u * (int64_t)g.n_pages * g.page_elems + (int64_t)rec.page * g.page_elems + (int64_t)i * g.d;
-        head_stride = (int64_t)g.W * g.d;
+        blk = bf.pages + u * (int64_t)g.n_pages * g.page_elems + (int64_t)rec.page * g.page_elems;
+        Wp = g.W;
     }
     const int n_el = g.h_kv * g.d;
     for (int e = threadIdx.x; e < n_el; e += blockDim.x) {
         const int h = e / g.d, c = e % g.d;
-        dst[(2 * h) * head_stride + c] = k[(int64_t)b * n_el + e];
-        dst[(2 * h + 1) * head_stride + c] = v[(int64_t)b * n_el + e];
+        uint16_t* kh = blk + (int64_t)(2 * h) * Wp * g.d;
+        kh[lay_k(i, c, g.d, Wp)] = k[(int64_t)b * n_el + e];
+        kh[(int64_t)Wp * g.d + lay_v(i, c, g.d, Wp)] = v[(int64_t)b * n_el + e];
     }
     __syncthreads();
     if (threadIdx.x == 0) hdr->n = p + 1;
@@ -89,14 +91,17 @@ __global__ void k_prefill_setup(Geo g, Bufs bf, int layer, const uint16_t* __res
     const int S = hdr->prompt_len;
     const int n_win = S > g.n_sink ? (S - g.n_sink + g.W - 1) / g.W : 0;
     for (int w = threadIdx.x; w < n_win; w += blockDim.x) bf.win[u * g.n_windows + w].state = ST_PROMPT;
-    const int ns = g.n_sink;
-    const int nsk = S < ns ? S : ns;
+    const int Ws = sink_width(g.n_sink);
+    const int nsk = S < g.n_sink ? S : g.n_sink;
+    uint16_t* sb = bf.sinks + u * g.sink_elems;
+    for (int e = threadIdx.x; e < g.sink_elems; e += blockDim.x) sb[e] = 0;
+    __syncthreads();
     for (int e = threadIdx.x; e < g.h_kv * nsk * g.d; e += blockDim.x) {
         const int h = e / (nsk * g.d), t = (e / g.d) % nsk, c = e % g.d;
         const int64_t src = (((int64_t)b * g.h_kv + h) * g.S_max + t) * g.d + c;
-        uint16_t* dst = bf.sinks + u * g.sink_elems;
-        dst[((int64_t)(2 * h) * ns + t) * g.d + c] = kp[src];
-        dst[((int64_t)(2 * h + 1) * ns + t) * g.d + c] = vp[src];
+        uint16_t* kh = sb + (int64_t)(2 * h) * Ws * g.d;
+        kh[lay_k(t, c, g.d, Ws)] = kp[src];
+        kh[(int64_t)Ws * g.d + lay_v(t, c, g.d, Ws)] = vp[src];
     }
     if (threadIdx.x == 0) {
         hdr->n = S;
@@ -346,7 +351,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
                 else if (ns == ST_QUANT) { a |= 8 | 16; ctr[C_PACKED]++; ctr[C_DEMOTED]++; }
                 else if (ns == ST_EVICTED) ctr[C_EVICTED]++;
             } else if (os == ST_NONE && ns == ST_LOCAL) {
-                a |= 2;
+                a |= 2 | 32;          // fresh recent-region page, zero-filled
             }
             if (ns == ST_FULL) ctr[C_NFULL]++;
             if (ns == ST_QUANT) ctr[C_NQUANT]++;
@@ -446,7 +451,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
             FillItem it;
             it.win = w;
             it.dst_page = my_page[i];
-            it.src_slot = r.state == ST_QUANT ? r.slot : -1;
+            it.src_slot = r.state == ST_QUANT ? r.slot : (r.state == ST_PROMPT ? -1 : -2);
             it.pad = 0;
             bf.fill[u * g.n_windows + flag2[w]] = it;
         }
@@ -580,13 +585,15 @@ __global__ void __launch_bounds__(PK_THREADS) k_pack(Geo g, Bufs bf, int layer, 
             srck = pg + (int64_t)(2 * h) * W * d;
             srcv = pg + (int64_t)(2 * h + 1) * W * d;
         }
+        const bool from_page = !pi.src_prompt;
         if (pi.dst_slot < 0 || (!pi.src_prompt && pi.src_page < 0)) {
             if (threadIdx.x == 0) atomicOr(&hdr->status, QEVICT_DEV_E_POOL);
             continue;
         }
         for (int e = threadIdx.x; e < W * d; e += PK_THREADS) {
-            sk[e] = srck[e];
-            sv[e] = srcv[e];
+            const int t = e / d, c = e % d;
+            sk[e] = srck[from_page ? lay_k(t, c, d, W) : e];
+            sv[e] = srcv[from_page ? lay_v(t, c, d, W) : e];
         }
         __syncthreads();
         uint8_t* slot = bf.slots + u * (int64_t)g.n_slots * g.slot_bytes + (int64_t)pi.dst_slot * g.slot_bytes +
@@ -629,8 +636,8 @@ __global__ void __launch_bounds__(PK_THREADS) k_pack(Geo g, Bufs bf, int layer, 
             const double off = fp16_round_down((double)mn);
             const double scl = fp16_round_up(((double)mx - off) / 3.0);
             if (fabs(off) > 65504.0 || scl > 65504.0) bad = true;
-            offV[i] = fp16_bits_exact(off);
-            sclV[i] = fp16_bits_exact(scl);
+            offV[lay_vp(i, W)] = fp16_bits_exact(off);
+            sclV[lay_vp(i, W)] = fp16_bits_exact(scl);
             for (int c = 0; c < d; ++c) {
                 const double t = 2.0 * ((double)bf16_to_f32(sv[i * d + c]) - off);
                 int code = (t >= scl) + (t >= 3.0 * scl) + (t >= 5.0 * scl);
@@ -640,13 +647,21 @@ __global__ void __launch_bounds__(PK_THREADS) k_pack(Geo g, Bufs bf, int layer, 
         }
         if (bad) atomicOr(&hdr->status, QEVICT_DEV_E_RANGE);
         __syncthreads();
-        // pack 4 codes per byte: element (i, c) -> byte i*d/4 + c/4, bits 2*(c%4)
+        // K codes: 4 consecutive channels of one token per byte (lay_kc_byte)
         for (int e = threadIdx.x; e < W * d / 4; e += PK_THREADS) {
             const int i = e / (d / 4), c4 = e % (d / 4);
             const uint8_t* pk = ck + i * d + 4 * c4;
-            const uint8_t* pv = cv + i * d + 4 * c4;
-            slot[e] = (uint8_t)(pk[0] | (pk[1] << 2) | (pk[2] << 4) | (pk[3] << 6));
-            slot[W * d / 4 + e] = (uint8_t)(pv[0] | (pv[1] << 2) | (pv[2] << 4) | (pv[3] << 6));
+            slot[lay_kc_byte(i, 4 * c4, d, W)] = (uint8_t)(pk[0] | (pk[1] << 2) | (pk[2] << 4) | (pk[3] << 6));
+        }
+        // V codes: one byte = 4 consecutive tokens of one channel (lay_vc_byte)
+        {
+            const int NT = W / 16, MB = d / 16;
+            for (int e = threadIdx.x; e < W * d / 4; e += PK_THREADS) {
+                const int m = e % MB, tile = (e / MB) % NT, qg = (e / (MB * NT)) % 4, r = e / (MB * NT * 4);
+                const int c = 16 * m + r, t0 = 16 * tile + 4 * qg;
+                slot[W * d / 4 + e] = (uint8_t)(cv[t0 * d + c] | (cv[(t0 + 1) * d + c] << 2) |
+                                                 (cv[(t0 + 2) * d + c] << 4) | (cv[(t0 + 3) * d + c] << 6));
+            }
         }
         __syncthreads();
     }
@@ -685,22 +700,28 @@ __global__ void __launch_bounds__(PK_THREADS) k_fill(Geo g, Bufs bf, int layer, 
             const uint16_t* sclV = offV + W;
             for (int e = threadIdx.x; e < W * d; e += PK_THREADS) {
                 const int i = e / d, c = e % d;
-                const int kc = (slot[i * (d / 4) + c / 4] >> (2 * (c % 4))) & 3;
-                const int vc = (slot[W * d / 4 + i * (d / 4) + c / 4] >> (2 * (c % 4))) & 3;
+                const int kc = (slot[lay_kc_byte(i, c, d, W)] >> lay_kc_shift(c)) & 3;
+                const int vc = (slot[W * d / 4 + lay_vc_byte(i, c, d, W)] >> lay_vc_shift(i)) & 3;
+                const int vp = lay_vp(i, W);
                 const double kx = (double)fp16_bits_to_f32(offK[c]) + kc * (double)fp16_bits_to_f32(sclK[c]);
-                const double vx = (double)fp16_bits_to_f32(offV[i]) + vc * (double)fp16_bits_to_f32(sclV[i]);
-                dk[e] = f64_to_bf16(kx);
-                dv[e] = f64_to_bf16(vx);
+                const double vx = (double)fp16_bits_to_f32(offV[vp]) + vc * (double)fp16_bits_to_f32(sclV[vp]);
+                dk[lay_k(i, c, d, W)] = f64_to_bf16(kx);
+                dv[lay_v(i, c, d, W)] = f64_to_bf16(vx);
             }
-        } else {
+        } else if (fi.src_slot == -1) {
             const uint16_t* sk = kp + (((int64_t)b * g.h_kv + h) * g.S_max + start) * d;
             const uint16_t* sv = vp + (((int64_t)b * g.h_kv + h) * g.S_max + start) * d;
             int ntok = S - start;
             if (ntok > W) ntok = W;
             for (int e = threadIdx.x; e < W * d; e += PK_THREADS) {
-                const int i = e / d;
-                dk[e] = i < ntok ? sk[e] : (uint16_t)0;
-                dv[e] = i < ntok ? sv[e] : (uint16_t)0;
+                const int i = e / d, c = e % d;
+                dk[lay_k(i, c, d, W)] = i < ntok ? sk[e] : (uint16_t)0;
+                dv[lay_v(i, c, d, W)] = i < ntok ? sv[e] : (uint16_t)0;
+            }
+        } else {
+            for (int e = threadIdx.x; e < W * d; e += PK_THREADS) {
+                dk[e] = 0;
+                dv[e] = 0;
             }
         }
     }

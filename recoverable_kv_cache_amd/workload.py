@@ -24,6 +24,7 @@ regenerated on its own (``torch.Generator`` seeded from a hash of the key).
 """
 from __future__ import annotations
 
+import functools
 import hashlib
 import math
 from dataclasses import dataclass, field, replace
@@ -111,6 +112,7 @@ def _topic_windows(wl: Workload, layer: int, b: int, prompt_len: int) -> list[in
     return sorted(int(x) for x in perm)
 
 
+@functools.lru_cache(maxsize=4096)
 def _topic_dirs(wl: Workload, layer: int, b: int, device) -> torch.Tensor:
     """Unit directions [h_kv][n_topics][d] (float32)."""
     g = _gen(wl.seed, layer, b, _S_TOPIC_DIR, "cpu")
@@ -119,6 +121,7 @@ def _topic_dirs(wl: Workload, layer: int, b: int, device) -> torch.Tensor:
     return u.to(torch.float32).to(device)
 
 
+@functools.lru_cache(maxsize=4096)
 def _outlier_channels(wl: Workload, layer: int) -> torch.Tensor:
     g = _gen(wl.seed, layer, 0, _S_OUT)
     rows = [torch.randperm(wl.d_head, generator=g)[: wl.n_outlier] for _ in range(wl.h_kv)]
@@ -144,7 +147,7 @@ def prompt(wl: Workload, layer: int, device="cpu") -> tuple[torch.Tensor, torch.
                 k[h][:, outl[h].to(k.device)] *= 10.0
         tw = _topic_windows(wl, layer, b, lens[b])
         if tw:
-            u = _topic_dirs(wl, layer, b, k.device)
+            u = _topic_dirs(wl, layer, b, str(k.device))
             for j, w in enumerate(tw):
                 s0 = wl.n_sink + w * wl.window
                 k[:, s0:s0 + wl.window, :] += wl.beta * u[:, j:j + 1, :]
@@ -187,7 +190,7 @@ def decode_step(wl: Workload, layer: int, step: int, device="cpu") -> tuple[torc
                 k[h][outl[h].to(k.device)] *= 10.0
         if wl.n_topics:
             j, phi = _phase(wl, step)
-            u = _topic_dirs(wl, layer, b, q.device)[:, j, :]          # [h_kv][d]
+            u = _topic_dirs(wl, layer, b, str(q.device))[:, j, :]          # [h_kv][d]
             uq = u.repeat_interleave(G, dim=0)                        # [h_q][d]
             q = math.cos(phi) * q + math.sin(phi) * math.sqrt(d) * uq
         qs.append(q.to(torch.bfloat16))

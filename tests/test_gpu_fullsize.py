@@ -1,0 +1,81 @@
+"""GPU parity at the full size of the 32K Llama-3-8B-shaped workload (one layer, in
+the launch configuration the benchmark times: batch 1, 8 KV heads, same split count).
+
+* Decode + routing in lockstep with the oracle: the initial window scores are a
+  synthetic seeded vector passed to both sides (the oracle cannot afford the
+  ~9 TFLOP fp64 prompt column sums of a 32K prompt), so prefill routing, the 852
+  INT2 packs, 8 decode steps and one routing event are all compared exactly.
+* Prompt column sums at 32K: the row-sum invariant (every causal softmax row
+  sums to one, so sum_w S_bar_0(w) + sink mass = prompt length), sampled row
+  log-sum-exps, and the scores of the last two windows, whose column sums the
+  oracle can compute from 64 rows.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import qevict_oracle as O
+from recoverable_kv_cache_amd import binding as B
+from recoverable_kv_cache_amd import workload as WL
+from tests.gpu_harness import Lockstep
+from tests.oracle_helpers import f64
+
+pytestmark = pytest.mark.gpu
+
+WL32 = WL.LLAMA8B_32K.with_(n_layers=1)
+
+
+def test_llama8b_32k_decode_and_route_lockstep():
+    print("case: 32K decode lockstep", flush=True)
+    n_win = (WL32.prompt_len - WL32.n_sink + WL32.window - 1) // WL32.window
+    si = WL.init_scores(WL32, 0, n_win)
+    ls = Lockstep(WL32, score_init=si)
+    ls.prefill()
+    assert ls.st.info.n_splits == B.plan(B.make_config(WL.LLAMA8B_32K), [32768]).n_splits
+    ex = ls.st.export_unit(0, 0)
+    assert ex.counters["packed"] == ls.units[0].events[0]["packed"] > 800
+    for j in range(8):
+        ls.step(j)
+    print(f"32K: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}", flush=True)
+
+
+def test_llama8b_32k_prefill_column_sums():
+    print("case: 32K prefill column sums", flush=True)
+    S, G = WL32.prompt_len, WL32.h_q // WL32.h_kv
+    st = B.QEvictState(B.make_config(WL32), [S])
+    qp, kp, vp = WL.prompt(WL32, 0, device="cuda")
+    st.prefill_init(0, qp, kp, vp)
+    torch.cuda.synchronize()
+    ex = st.export_unit(0, 0)
+    lse_gpu, col_gpu = st.workspace_views()
+    lse_gpu = lse_gpu.cpu().numpy()[0]
+    col_gpu = col_gpu.cpu().numpy()[0]
+    Q = qp[0].cpu().to(torch.float64).numpy()
+    K = kp[0].cpu().to(torch.float64).numpy()
+    del qp, kp, vp
+    # every causal row sums to one
+    total = ex.score[: ex.n_windows].sum() + ex.sink_mass
+    print(f"row-sum invariant: {total} vs {S}", flush=True)
+    assert abs(total - S) < 1e-5 * S
+    # sampled row LSEs (log2 units)
+    for h, u in [(0, 0), (5, 4095), (17, 20000), (31, S - 1)]:
+        ref = O.row_lse(Q[h][u], K[h // G][: u + 1]) / math.log(2)
+        assert abs(lse_gpu[h, u] - ref) < 1e-4, (h, u)
+    # column sums of the last 64 keys, all heads -> scores of the last two windows
+    t0 = S - 64
+    lse_rows = np.array([[O.row_lse(Q[h][u], K[h // G][: u + 1]) for u in range(t0, S)] for h in range(WL32.h_q)])
+    col_ref = np.zeros((WL32.h_q, 64))
+    for h in range(WL32.h_q):
+        logits = Q[h][t0:] @ K[h // G][t0:].T / math.sqrt(WL32.d_head)      # [u][t]
+        P = np.exp(logits - lse_rows[h][:, None])
+        P[np.triu_indices(64, k=1)] = 0.0                                     # t > u masked
+        col_ref[h] = P.sum(axis=0)
+    err = np.abs(col_gpu[:, t0:] - col_ref).max()
+    print(f"last-64 column-sum err {err:.2e}", flush=True)
+    assert err < 1e-5
+    for w in (ex.n_windows - 2, ex.n_windows - 1):
+        a = WL32.n_sink + w * WL32.window
+        ref = col_ref[:, a - t0: a - t0 + WL32.window].sum() / WL32.h_q
+        assert abs(ex.score[w] - ref) < 1e-4
