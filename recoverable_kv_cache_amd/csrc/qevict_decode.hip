@@ -97,14 +97,14 @@ __global__ void __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(2)
     static_assert(2 * G <= 16, "hi/lo query columns must fit one 16-wide tile");
     __shared__ uint2 lut[256];
     __shared__ AccEntry ent[DMAXE];
-    __shared__ float sq[G][D];
     __shared__ float s_m[DW][16], s_l[DW][16];
     __shared__ float s_acc[DW][G][D];
 
     const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
     const int64_t u = unit_of(g, b, layer);
     const int n = bf.hdr[u].n;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int r = lane & 15, qg = lane >> 4;
     const int W = g.W, Ws = sink_width(g.n_sink);
 
@@ -117,8 +117,6 @@ __global__ void __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(2)
     const int32_t* splits = bf.splits + u * (g.n_splits + 1);
     const int e_begin = splits[split], e_total = splits[split + 1] - e_begin;
     int e0 = e_begin, ne = 0;   // current batch of entries staged in LDS
-    for (int x = threadIdx.x; x < G * D; x += 64 * DW)
-        sq[x / D][x % D] = bf16_to_f32(qin[((int64_t)b * g.h_q + hk * G) * D + x]);
     __syncthreads();
 
     // B operand for bf16 windows: columns r and r + G (r < G) both hold query head r
@@ -133,9 +131,7 @@ __global__ void __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(2)
     const float scale = 1.4426950408889634f / sqrtf((float)D);   // log2(e) / sqrt(d)
     // columns of the INT2 query operand: r < G: high part of q*scl for head r;
     // G <= r < 2G: low part for head r - G; others zero
-    const int qhead = r % G;
     const uint32_t lo_mask = (r >= G && r < 2 * G) ? 0xFFFF0000u : 0u;
-    const float col_on = r < 2 * G ? 1.f : 0.f;
     const bool live = r < 2 * G;       // lanes holding a query column (two copies per head)
     const bool prim = r < G;           // the copy that owns the head's softmax statistics
 
@@ -155,7 +151,10 @@ __global__ void __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(2)
         Job j;
         j.ch = 0;
         for (; i < ne; i += DW) {
-            const AccEntry en = ent[i];
+            AccEntry en = ent[i];
+            en.kind = __builtin_amdgcn_readfirstlane(en.kind);
+            en.idx = __builtin_amdgcn_readfirstlane(en.idx);
+            en.start = __builtin_amdgcn_readfirstlane(en.start);
             int nt;
             if (en.kind == EK_SINK) nt = min(g.n_sink, n);
             else nt = min(W, n - en.start);
@@ -253,8 +252,9 @@ __global__ void __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(2)
                 for (int h2 = 0; h2 < 2; ++h2) {
                     const int cc = 4 * kk + 2 * h2;             // channel pair within the lane group
                     const f2_t sp = h2f(word(scl, cc / 2));
-                    const float x0 = col_on * sq[qhead][qg * CQ + cc] * sp.x;
-                    const float x1 = col_on * sq[qhead][qg * CQ + cc + 1] * sp.y;
+                    const uint32_t qw = word(qB, cc / 2);         // query channels cc, cc + 1 (bf16)
+                    const float x0 = bf16lo(qw) * sp.x;
+                    const float x1 = bf16hi(qw) * sp.y;
                     const float y0 = x0 - __uint_as_float(__float_as_uint(x0) & lo_mask);
                     const float y1 = x1 - __uint_as_float(__float_as_uint(x1) & lo_mask);
                     w2[h2] = bf16x2_trunc(y0, y1);
@@ -267,9 +267,9 @@ __global__ void __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
             for (int x = 0; x < CQ / 4; ++x) {
                 const f2_t op = h2f(word(off, x));
-                const int c = qg * CQ + half * (CQ / 2) + 2 * x;
-                sb = fmaf(sq[qhead][c], op.x, sb);
-                sb = fmaf(sq[qhead][c + 1], op.y, sb);
+                const uint32_t qw = word(qB, half * (CQ / 4) + x);
+                sb = fmaf(bf16lo(qw), op.x, sb);
+                sb = fmaf(bf16hi(qw), op.y, sb);
             }
             sb += xor_lane<G>(sb);                 // high-part lane + low-part lane
             sb += xor_lane<16>(sb);
