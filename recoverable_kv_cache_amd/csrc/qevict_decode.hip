@@ -1,20 +1,23 @@
-// Decode step: split-K attention over the chronological accessible list
-// (sinks, recent windows, Full bf16 windows, Quantized INT2 windows dequantized
-// in registers), then a combine pass that normalises the splits with the global
-// log-sum-exp and turns per-window partial exp-sums into window masses.
+// Decode step: split-K attention over the accessible list (sinks, recent
+// windows, Full bf16 windows, Quantized INT2 windows), then a combine pass that
+// normalises the splits with the global log-sum-exp and turns per-window
+// partial exp-sums into window masses.
 //
 // Source: "QEvict: Recoverable Quantized KV Eviction for Attention-Drift-Robust
-// Long-Context Decoding", §4.1 (accessible-set attention, scale 1/sqrt(d_kv)),
-// §4.2 Eq. 1 (cumulative window score, averaged over the H_q query heads).
+// Long-Context Decoding", §4.1 (accessible-set attention, scale 1/sqrt(d_kv);
+// Quantized windows are dequantized in the execution datatype as
+// off + scl * code, Eq. 5), §4.2 Eq. 1 (cumulative window score, averaged over
+// the H_q query heads).
 //
 // Work split: one workgroup per (split, KV head, sequence); the G query heads of
-// the GQA group share every K/V load.  Inside a wave, a token is handled by LPT
-// lanes that each own CPL contiguous channels; TPI = 64 / LPT tokens are in
-// flight per wave iteration.  Each wave walks whole windows of the split, so it
-// can emit the window's log-sum-exp (log2 domain) without extra passes.
+// the GQA group share every K/V load.  All contractions run on 16x16 MFMA tiles
+// with 16 columns: each query head owns two columns, a "high" and a "low" one,
+// so that bf16 operands can carry fp32-accurate values as a sum of two bf16
+// parts (query times K scale on the key side, probability times V scale on the
+// value side).  With G <= 4 the 16 columns hold two independent column slots,
+// so one wave job covers two INT2 windows at once and the softmax arithmetic of
+// both runs in the same instructions.
 #include <float.h>
-
-#include <type_traits>
 
 #include "qevict_common.h"
 #include "qevict_internal.h"
@@ -22,307 +25,304 @@
 namespace qv {
 
 constexpr int DW = 4;          // waves per workgroup
-constexpr int DMAXE = 512;     // accessible entries of one split, staged in LDS
+constexpr int DMAXE = 256;     // accessible entries of one split, staged in LDS per batch
+constexpr float M_INIT = -1e30f;   // running max before any token (finite: exp2(-inf - M_INIT) = 0)
 
 typedef short s4_t __attribute__((ext_vector_type(4)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef float f2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f4_t mfma16(s4_t a, s4_t b, f4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
+typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-// both fp16 halves of a 32-bit word as fp32 (the word stays a 32-bit value in the IR)
-__device__ __forceinline__ f2_t h2f(uint32_t w) { return __builtin_convertvector(__builtin_bit_cast(h2_t, w), f2_t); }
-__device__ __forceinline__ s4_t s4_of(uint32_t lo, uint32_t hi) {
-    const u2_t v = {lo, hi};
-    return __builtin_bit_cast(s4_t, v);
+
+// D[16x16] += A[16x32] B[32x16]: lane l holds A row l%16 / B column l%16 at k = 8(l/16)+i, D column l%16 rows 4(l/16)+i
+__device__ __forceinline__ f4_t mfma32(u4_t a, u4_t b, f4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8_t, a), __builtin_bit_cast(bf8_t, b), c, 0,
+                                                   0, 0);
 }
+// D[16x16] += A[16x16] B[16x16]: k = 4(l/16)+i
+__device__ __forceinline__ f4_t mfma16(u2_t a, u2_t b, f4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4_t, a), __builtin_bit_cast(s4_t, b), c, 0, 0,
+                                                     0);
+}
+// both fp16 halves of a 32-bit word as fp32
+__device__ __forceinline__ f2_t h2f(uint32_t w) { return __builtin_convertvector(__builtin_bit_cast(h2_t, w), f2_t); }
 // two fp32 -> packed bf16 pair, round to nearest even
 __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
     const f2_t v = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2_t));
 }
-// top 16 bits of two fp32 (bf16 truncation, exact when the values are bf16)
+// top 16 bits of two fp32 (bf16 truncation)
 __device__ __forceinline__ uint32_t bf16x2_trunc(float a, float b) {
     return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
 }
-
-// One unit of work for a wave: up to 32 tokens (one or two 16-token tiles) of one
-// accessible-list entry.  All fields are wave-uniform.
-struct Job {
-    int i;      // entry index within the split (-1: none)
-    int ch;     // chunk of the entry
-    int nch;    // chunks of the entry
-    int kind;   // EK_SINK / EK_PAGE / EK_SLOT
-    int ntok;   // valid tokens of the entry
-    int Wn;     // tokens per page of the entry (W, or the sink width)
-    int idx;    // page / slot id
-};
-
-template <int D>
-struct Raw {                       // per-lane operands of one job, as loaded from HBM (pairs of 32-bit words)
-    // bf16 job (one tile): k = the lane's K row slice (CQ channels), v = its V^T slice (4 tokens x MB blocks).
-    // INT2 job (up to two tiles): words k[0..3] K codes, k[4..7] V codes, k[8..11] V offsets,
-    //           k[12..15] V scales; v[0..CQ/2) K scales, v[CQ/2..3CQ/4) K offsets (first chunk only).
-    u2_t k[8];
-    u2_t v[3 * D / 32];
-};
+// value of the lane at the mirrored position of this lane's SW-wide column group
+// (row_half_mirror for SW = 8, row_mirror for SW = 16): pairs the high column of a
+// head with its low column
+template <int SW>
+__device__ __forceinline__ float mirror(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), SW == 8 ? 0x141 : 0x140, 0xF, 0xF, false));
+}
+// value of lane (l ^ 8) within its row of 16 (row_ror:8): the other column slot
+__device__ __forceinline__ float ror8(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+// LDS traffic between lanes of one wave: the wave's LDS operations execute in
+// order, so only the compiler has to be kept from reordering them
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 template <int N>
-__device__ __forceinline__ void ld4(u2_t* dst, const void* src) {
-    const uint4* p = reinterpret_cast<const uint4*>(src);
+__device__ __forceinline__ void ldw(uint32_t* d, const void* s) {
+    if constexpr (N % 4 == 0) {
 #pragma unroll
-    for (int x = 0; x < N; ++x) {
-        const uint4 t = p[x];
-        dst[2 * x] = u2_t{t.x, t.y};
-        dst[2 * x + 1] = u2_t{t.z, t.w};
+        for (int x = 0; x < N / 4; ++x) {
+            const uint4 t = reinterpret_cast<const uint4*>(s)[x];
+            d[4 * x] = t.x;
+            d[4 * x + 1] = t.y;
+            d[4 * x + 2] = t.z;
+            d[4 * x + 3] = t.w;
+        }
+    } else if constexpr (N == 2) {
+        const uint2 t = *reinterpret_cast<const uint2*>(s);
+        d[0] = t.x;
+        d[1] = t.y;
+    } else {
+        static_assert(N == 1, "word count");
+        d[0] = *reinterpret_cast<const uint32_t*>(s);
     }
 }
-__device__ __forceinline__ void ld2(u2_t* dst, const void* src) {
-    const uint2 t = *reinterpret_cast<const uint2*>(src);
-    dst[0] = u2_t{t.x, t.y};
+template <int N>
+__device__ __forceinline__ void stw(void* p, const uint32_t* w) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int x = 0; x < N / 4; ++x)
+            reinterpret_cast<uint4*>(p)[x] = make_uint4(w[4 * x], w[4 * x + 1], w[4 * x + 2], w[4 * x + 3]);
+    } else if constexpr (N == 2) {
+        *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+    } else {
+        static_assert(N == 1, "word count");
+        *reinterpret_cast<uint32_t*>(p) = w[0];
+    }
 }
-__device__ __forceinline__ uint32_t word(const u2_t* a, int w) { return a[w >> 1][w & 1]; }
-__device__ __forceinline__ s4_t pair_s4(u2_t v) { return __builtin_bit_cast(s4_t, v); }
 
-template <int D, int G>
-__global__ void __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(2))) k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin) {
-    constexpr int CQ = D / 4;      // channels of one lane group on the K side
-    constexpr int KK = D / 16;     // MFMA k-steps over channels
-    constexpr int MB = D / 16;     // 16-channel blocks on the V side
-    constexpr int NKR = D / 16;    // uint4 of K per lane per 2-tile chunk (bf16)
-    static_assert(2 * G <= 16, "hi/lo query columns must fit one 16-wide tile");
+// Static shape of one instantiation: head dim D, query heads per KV head G,
+// tiles per 32-token chunk TPC (1 for 16-token windows, else 2).
+template <int D, int G, int TPC>
+struct DecShape {
+    static constexpr int CQ = D / 4;                 // channels per lane group (key side)
+    static constexpr int KS = D / 32;                // 32-channel MFMA steps (key side)
+    static constexpr int MB = D / 16;                // 16-channel blocks (value side)
+    static constexpr int NSLOT = G <= 4 ? 2 : 1;     // column slots
+    static constexpr int SW = 16 / NSLOT;            // columns per slot
+    static constexpr int ROWS = NSLOT * G;           // (item, head) rows of the query-times-scale products
+    static constexpr int LPR = 64 / ROWS;            // lanes per product row
+    static constexpr int CPL = D / LPR;              // channels per lane in the products
+    static constexpr int NV = 4 * TPC;               // scores per lane per INT2 item
+    // INT2 job words per lane: K codes and V codes of every item, V offsets / scales of
+    // the lane's own item, K scales / offsets of the lane's product channels
+    static constexpr int KCW = TPC * CQ / 16, VCW = MB * TPC / 4, VPW = 2 * TPC, KPW = CPL / 2;
+    static constexpr int O_VC = NSLOT * KCW, O_VO = O_VC + NSLOT * VCW, O_VS = O_VO + VPW, O_KS = O_VS + VPW,
+                         O_KO = O_KS + KPW, QW = O_KO + KPW;
+    // bf16 tile job words per lane: K row (CQ bf16) then V (MB blocks x 4 tokens)
+    static constexpr int FW = CQ / 2 + 2 * MB;
+    static constexpr int RW = QW > FW ? QW : FW;
+    static constexpr int QSTR = D + 8;               // bf16 per LDS operand row (padded)
+    static_assert(KCW >= 1 && VCW >= 1 && KPW >= 1, "shape");
+};
+
+// One unit of wave work.  INT2 job: chunk c of up to NSLOT Quantized windows
+// (entries ia, ib), one per column slot.  bf16 job: tile t of one sink / page entry.
+struct Job {
+    int type;           // 0 none, 1 INT2, 2 bf16
+    int ia, ib, c;      // INT2: batch-local entry indices (ib = -1: slot 1 empty), chunk
+    int sa, sb;         // INT2: slot ids
+    int i, t, kind, idx, ntok, Wn;   // bf16: entry, tile, kind, page id, valid tokens, block width
+};
+
+template <int D, int G, int TPC>
+__global__ void __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(2)))
+k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin) {
+    using S = DecShape<D, G, TPC>;
+    constexpr int CQ = S::CQ, KS = S::KS, MB = S::MB, NSLOT = S::NSLOT, SW = S::SW, LPR = S::LPR, CPL = S::CPL;
+    constexpr int NV = S::NV, QSTR = S::QSTR;
     __shared__ uint2 lut[256];
     __shared__ AccEntry ent[DMAXE];
-    __shared__ float s_m[DW][16], s_l[DW][16];
+    __shared__ __attribute__((aligned(16))) uint16_t qs[DW][16][QSTR];   // per wave: INT2 query operand rows
+    __shared__ __attribute__((aligned(16))) uint16_t qb[16][QSTR];       // bf16 query operand rows
+    __shared__ float kb[DW][16];                                         // per wave: key-offset bias per column
+    __shared__ __attribute__((aligned(16))) float qfl[64][CPL];          // q of each lane's product channels
+    __shared__ float s_m[DW][G], s_l[DW][G];
     __shared__ float s_acc[DW][G][D];
 
     const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
     const int64_t u = unit_of(g, b, layer);
-    const int n = bf.hdr[u].n;
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-    const int r = lane & 15, qg = lane >> 4;
-    const int W = g.W, Ws = sink_width(g.n_sink);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15, qg = lane >> 4;            // MFMA column, lane group
+    const int slot = n / SW, rn = n % SW;
+    const bool hi = rn < G, lo = rn >= SW - G;           // high / low column of head `head`
+    const int head = hi ? rn : (lo ? SW - 1 - rn : 0);
+    const float lof = lo ? 1.f : 0.f;
+    const int W = g.W, Ws = sink_width(g.n_sink), NCH = W / (16 * TPC), NT = W / 16;
+    const float scale = 1.4426950408889634f / sqrtf((float)D);   // log2(e) / sqrt(d)
 
-    // 4 packed 2-bit codes -> 4 bf16 {0, 1, 2, 3}
-    for (int x = threadIdx.x; x < 256; x += 64 * DW) {
-        const uint32_t v0 = 0, v1 = 0x3F80, v2 = 0x4000, v3 = 0x4040;
-        auto bv = [&](int c) { return c == 0 ? v0 : (c == 1 ? v1 : (c == 2 ? v2 : v3)); };
-        lut[x] = make_uint2(bv(x & 3) | (bv((x >> 2) & 3) << 16), bv((x >> 4) & 3) | (bv((x >> 6) & 3) << 16));
-    }
+    // product assignment: row (item pitem, head phead), channels [CPL*pcb, CPL*pcb + CPL)
+    const int prow = lane / LPR, pitem = prow / G, phead = prow % G, pcb = lane % LPR;
+
     const int32_t* splits = bf.splits + u * (g.n_splits + 1);
     const int e_begin = splits[split], e_total = splits[split + 1] - e_begin;
-    int e0 = e_begin, ne = 0;   // current batch of entries staged in LDS
-    __syncthreads();
-
-    // B operand for bf16 windows: columns r and r + G (r < G) both hold query head r
-    // (exact bf16), others zero; the two copies later carry the high and low bf16
-    // parts of the probabilities on the value side
-    u2_t qB[KK];                  // 4 bf16 per k-step
-    ld4<KK / 2>(qB, qin + ((int64_t)b * g.h_q + hk * G + r % G) * D + qg * CQ);
-    if (r >= 2 * G) {
-#pragma unroll
-        for (int x = 0; x < KK; ++x) qB[x] = u2_t{0u, 0u};
+    const int n_tok = bf.hdr[u].n;
+    const uint16_t* qhead = qin + ((int64_t)b * g.h_q + hk * G) * D;
+    // 4 packed 2-bit codes -> 4 bf16 {0, 1, 2, 3}
+    for (int x = threadIdx.x; x < 256; x += 64 * DW) {
+        auto bv = [](int c) -> uint32_t { return c == 0 ? 0u : (c == 1 ? 0x3F80u : (c == 2 ? 0x4000u : 0x4040u)); };
+        lut[x] = make_uint2(bv(x & 3) | (bv((x >> 2) & 3) << 16), bv((x >> 4) & 3) | (bv((x >> 6) & 3) << 16));
     }
-    const float scale = 1.4426950408889634f / sqrtf((float)D);   // log2(e) / sqrt(d)
-    // columns of the INT2 query operand: r < G: high part of q*scl for head r;
-    // G <= r < 2G: low part for head r - G; others zero
-    const uint32_t lo_mask = (r >= G && r < 2 * G) ? 0xFFFF0000u : 0u;
-    const bool live = r < 2 * G;       // lanes holding a query column (two copies per head)
-    const bool prim = r < G;           // the copy that owns the head's softmax statistics
+    // bf16 windows: every live column holds its head's query (exact bf16);
+    // INT2 windows: each lane's product channels of q, as fp32
+    if (wave == 0) {
+        uint32_t w[CQ / 2];
+        ldw<CQ / 2>(w, qhead + head * D + CQ * qg);
+        stw<CQ / 2>(&qb[n][CQ * qg], w);
+        uint32_t w2[CPL / 2];
+        ldw<CPL / 2>(w2, qhead + phead * D + CPL * pcb);
+#pragma unroll
+        for (int x = 0; x < CPL / 2; ++x) {
+            qfl[lane][2 * x] = bf16lo(w2[x]);
+            qfl[lane][2 * x + 1] = bf16hi(w2[x]);
+        }
+    }
 
-    float m_run = -INFINITY, l_run = 0.f, lw = 0.f, vbias = 0.f;
+    float m_run = M_INIT, l_run = 0.f, lw = 0.f, vbias = 0.f;
     f4_t acc[MB];
 #pragma unroll
     for (int m = 0; m < MB; ++m) acc[m] = f4_t{0.f, 0.f, 0.f, 0.f};
-    u2_t qpB[KK];
-    float kbias = 0.f;
 
     const uint16_t* pages = bf.pages + u * (int64_t)g.n_pages * g.page_elems;
-    const uint8_t* slots = bf.slots + u * (int64_t)g.n_slots * g.slot_bytes;
+    const uint8_t* slots = bf.slots + u * (int64_t)g.n_slots * g.slot_bytes + (int64_t)hk * g.slot_head_bytes;
     const uint16_t* sinks = bf.sinks + u * g.sink_elems;
-    float* lse_out = bf.lse_win + u * (int64_t)g.n_acc_max * g.h_q;
+    float* lse_out = bf.lse_win + u * (int64_t)g.n_acc_max * g.h_q + hk * G;
+    int e0 = e_begin, ne = 0;
 
-    auto resolve = [&](int i) __attribute__((always_inline)) -> Job {
+    // ---- job sequence of this wave: INT2 windows in pairs (chunk by chunk), then bf16 tiles
+    auto rfl = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+    auto ent_q = [&](int i) -> int {                 // first INT2 entry at or after i (stride DW)
+        for (; i < ne; i += DW)
+            if (rfl(ent[i].kind) == EK_SLOT && rfl(ent[i].idx) >= 0) return i;
+        return -1;
+    };
+    auto ent_f = [&](int i) -> Job {                 // first bf16 tile job at or after entry i
         Job j;
-        j.ch = 0;
+        j.type = 0;
         for (; i < ne; i += DW) {
-            AccEntry en = ent[i];
-            en.kind = __builtin_amdgcn_readfirstlane(en.kind);
-            en.idx = __builtin_amdgcn_readfirstlane(en.idx);
-            en.start = __builtin_amdgcn_readfirstlane(en.start);
-            int nt;
-            if (en.kind == EK_SINK) nt = min(g.n_sink, n);
-            else nt = min(W, n - en.start);
-            if (nt <= 0 || (en.kind != EK_SINK && en.idx < 0)) continue;
+            const int kind = rfl(ent[i].kind), idx = rfl(ent[i].idx), start = rfl(ent[i].start);
+            if (kind == EK_SLOT) continue;
+            const int nt = kind == EK_SINK ? min(g.n_sink, n_tok) : min(W, n_tok - start);
+            if (nt <= 0 || (kind != EK_SINK && idx < 0)) continue;
+            j.type = 2;
             j.i = i;
-            j.kind = en.kind;
+            j.t = 0;
+            j.kind = kind;
+            j.idx = idx;
             j.ntok = nt;
-            j.Wn = en.kind == EK_SINK ? Ws : W;
-            j.idx = en.idx;
-            j.nch = en.kind == EK_SLOT ? (nt + 31) / 32 : (nt + 15) / 16;   // INT2: 32-token jobs, bf16: 16
+            j.Wn = kind == EK_SINK ? Ws : W;
             return j;
         }
-        j.i = -1;
-        j.kind = EK_PAGE;
-        j.ntok = 0;
-        j.Wn = W;
-        j.idx = 0;
-        j.nch = 0;
         return j;
     };
-    auto next = [&](Job j) __attribute__((always_inline)) -> Job {
-        if (j.i < 0) return j;
-        if (j.ch + 1 < j.nch) {
-            j.ch += 1;
+    auto make_q = [&](int i) -> Job {
+        Job j;
+        j.type = 1;
+        j.ia = i;
+        j.c = 0;
+        j.sa = rfl(ent[i].idx);
+        j.ib = NSLOT == 2 ? ent_q(i + DW) : -1;
+        j.sb = j.ib >= 0 ? rfl(ent[j.ib].idx) : j.sa;
+        return j;
+    };
+    auto first_q = [&]() -> Job {
+        const int i = ent_q(wave);
+        if (i >= 0) return make_q(i);
+        Job j;
+        j.type = 0;
+        j.ia = j.ib = -1;
+        j.c = 0;
+        j.sa = j.sb = 0;
+        return j;
+    };
+    auto next_q = [&](Job j) -> Job {
+        if (j.c + 1 < NCH) {
+            j.c += 1;
             return j;
         }
-        return resolve(j.i + DW);
+        const int i = (NSLOT == 2 && j.ib < 0) ? -1 : ent_q((NSLOT == 2 ? j.ib : j.ia) + DW);
+        if (i >= 0) return make_q(i);
+        j.type = 0;
+        j.c = 0;
+        return j;   // keeps valid slot ids: the tail prefetch reads them harmlessly
+    };
+    auto next_f = [&](Job j) -> Job {
+        if (16 * (j.t + 1) < j.ntok) {
+            j.t += 1;
+            return j;
+        }
+        const Job k = ent_f(j.i + DW);
+        if (k.type != 0) return k;
+        j.type = 0;
+        return j;   // keeps a valid block: the tail prefetch reads it harmlessly
     };
 
-    auto load = [&](const Job& j, Raw<D>& R) __attribute__((always_inline)) {
-        if (j.i < 0) return;
-        const int tpc = lay_tpc(j.Wn), NT = j.Wn / 16;
-        if (j.kind != EK_SLOT) {
-            const uint16_t* kb = (j.kind == EK_SINK ? sinks : pages + (int64_t)j.idx * g.page_elems) +
-                                 (int64_t)(2 * hk) * j.Wn * D;
-            const uint16_t* vb = kb + (int64_t)j.Wn * D;
-            const int tile = j.ch;                                  // one 16-token tile per bf16 job
-            const uint16_t* pk = kb + ((((tile / tpc) * 16 + r) * 4 + qg) * tpc + tile % tpc) * CQ;
-            const uint16_t* pv = vb + (((r * 4 + qg) * NT + tile) * MB) * 4;
-            ld4<CQ / 8>(R.k, pk);
-            ld4<MB / 2>(R.v, pv);
-        } else {
-            const uint8_t* sl = slots + (int64_t)j.idx * g.slot_bytes + (int64_t)hk * g.slot_head_bytes;
-            const uint8_t* kc = sl + (((j.ch * 16 + r) * 4 + qg) * tpc) * (CQ / 4);
-            const uint8_t* vc = sl + W * D / 4 + ((r * 4 + qg) * NT + 2 * j.ch) * MB;
-            const uint16_t* oK = reinterpret_cast<const uint16_t*>(sl + W * D / 2);
-            const uint16_t* oV = oK + 2 * D;
-            const int vpo = (qg * NT + 2 * j.ch) * 4;
-            // K codes: tpc*CQ/4 bytes, V codes: tpc*MB bytes, V offsets / scales: tpc*4 halves each
-            if (tpc == 2) {
-                if constexpr (D == 128) {
-                    ld4<1>(R.k, kc);
-                    ld4<1>(R.k + 2, vc);
-                } else {
-                    ld2(R.k, kc);
-                    ld2(R.k + 2, vc);
-                }
-                ld4<1>(R.k + 4, oV + vpo);
-                ld4<1>(R.k + 6, oV + W + vpo);
-            } else {
-                if constexpr (D == 128) {
-                    ld2(R.k, kc);
-                    ld2(R.k + 2, vc);
-                } else {
-                    R.k[0] = u2_t{*reinterpret_cast<const uint32_t*>(kc), 0u};
-                    R.k[2] = u2_t{*reinterpret_cast<const uint32_t*>(vc), 0u};
-                }
-                ld2(R.k + 4, oV + vpo);
-                ld2(R.k + 6, oV + W + vpo);
+    struct Raw {
+        uint32_t w[S::RW];
+    };
+    auto load_q = [&](const Job& j, Raw& R) __attribute__((always_inline)) {
+        {
+            const uint8_t* sa = slots + (int64_t)j.sa * g.slot_bytes;
+            const uint8_t* sb = slots + (int64_t)j.sb * g.slot_bytes;
+            const int kco = ((j.c * 16 + n) * 4 + qg) * TPC * (CQ / 4);        // K codes: token row n, channel group qg
+            const int vco = W * D / 4 + (((n * 4 + qg) * NCH + j.c) * MB) * TPC;   // V codes: channel row n, tokens of qg
+            ldw<S::KCW>(R.w, sa + kco);
+            ldw<S::VCW>(R.w + S::O_VC, sa + vco);
+            if constexpr (NSLOT == 2) {
+                ldw<S::KCW>(R.w + S::KCW, sb + kco);
+                ldw<S::VCW>(R.w + S::O_VC + S::VCW, sb + vco);
             }
-            if (j.ch == 0) {
-                // K scales of the lane's CQ channels (q * scl for its query column) and
-                // K offsets of half of them (bias)
-                const int half = (r >= G && r < 2 * G) ? 1 : 0;
-                ld4<CQ / 8>(R.v, oK + D + qg * CQ);
-                ld4<CQ / 16>(R.v + CQ / 4, oK + qg * CQ + half * (CQ / 2));
-            }
+            const uint8_t* so = slot == 0 ? sa : sb;                 // the lane's own item
+            const uint16_t* offV = reinterpret_cast<const uint16_t*>(so + W * D / 2) + 2 * D;
+            ldw<S::VPW>(R.w + S::O_VO, offV + (qg * NT + TPC * j.c) * 4);
+            ldw<S::VPW>(R.w + S::O_VS, offV + W + (qg * NT + TPC * j.c) * 4);
+            const uint8_t* sp = pitem == 0 ? sa : sb;                // the item of the lane's products
+            const uint16_t* offK = reinterpret_cast<const uint16_t*>(sp + W * D / 2);
+            ldw<S::KPW>(R.w + S::O_KS, offK + D + CPL * pcb);
+            ldw<S::KPW>(R.w + S::O_KO, offK + CPL * pcb);
+        }
+    };
+    auto load_f = [&](const Job& j, Raw& R) __attribute__((always_inline)) {
+        {
+            const int tpc = lay_tpc(j.Wn), nt16 = j.Wn / 16;
+            const uint16_t* kbase = (j.kind == EK_SINK ? sinks : pages + (int64_t)j.idx * g.page_elems) +
+                                    (int64_t)(2 * hk) * j.Wn * D;
+            const uint16_t* vbase = kbase + (int64_t)j.Wn * D;
+            ldw<CQ / 2>(R.w, kbase + ((((j.t / tpc) * 16 + n) * 4 + qg) * tpc + j.t % tpc) * CQ);
+            ldw<2 * MB>(R.w + CQ / 2, vbase + (((n * 4 + qg) * nt16 + j.t) * MB) * 4);
         }
     };
 
-    auto process = [&](const Job& j, const Raw<D>& R) __attribute__((always_inline)) {
-        const bool quant = j.kind == EK_SLOT;
-        const int tiles = quant ? lay_tpc(j.Wn) : 1;
-        const int base_t = (quant ? 32 : 16) * j.ch;
-        const int nt_here = min(j.ntok - base_t, 16 * tiles);   // valid tokens in this job
-        const int ntiles = (nt_here + 15) / 16;
-        if (quant && j.ch == 0) {
-            // query operand q * scl split into bf16 high + low parts (exact high, truncated low),
-            // and the window's key-offset bias sum_c q_c * off_c (per head, log2 domain later)
-            const u2_t* scl = R.v;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                uint32_t w2[2];
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    const int cc = 4 * kk + 2 * h2;             // channel pair within the lane group
-                    const f2_t sp = h2f(word(scl, cc / 2));
-                    const uint32_t qw = word(qB, cc / 2);         // query channels cc, cc + 1 (bf16)
-                    const float x0 = bf16lo(qw) * sp.x;
-                    const float x1 = bf16hi(qw) * sp.y;
-                    const float y0 = x0 - __uint_as_float(__float_as_uint(x0) & lo_mask);
-                    const float y1 = x1 - __uint_as_float(__float_as_uint(x1) & lo_mask);
-                    w2[h2] = bf16x2_trunc(y0, y1);
-                }
-                qpB[kk] = u2_t{w2[0], w2[1]};
-            }
-            const u2_t* off = R.v + CQ / 4;
-            const int half = (r >= G && r < 2 * G) ? 1 : 0;
-            float sb = 0.f;
-#pragma unroll
-            for (int x = 0; x < CQ / 4; ++x) {
-                const f2_t op = h2f(word(off, x));
-                const uint32_t qw = word(qB, half * (CQ / 4) + x);
-                sb = fmaf(bf16lo(qw), op.x, sb);
-                sb = fmaf(bf16hi(qw), op.y, sb);
-            }
-            sb += xor_lane<G>(sb);                 // high-part lane + low-part lane
-            sb += xor_lane<16>(sb);
-            sb += xor_lane<32>(sb);
-            kbias = sb;
-        }
-        // ---- scores of the chunk: S^T[token][column] = K_tile . Q^T
-        float s[2][4];
-        auto score_tile = [&](auto TCc) __attribute__((always_inline)) {
-            constexpr int tc = decltype(TCc)::value;
-            f4_t c = {0.f, 0.f, 0.f, 0.f};
-            if (!quant) {
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk)
-                    c = mfma16(pair_s4(R.k[tc * (CQ / 4) + kk]), pair_s4(qB[kk]), c);
-            } else {
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) {
-                    constexpr int dummy = 0;
-                    (void)dummy;
-                    const int byte = tc * (CQ / 4) + kk;
-                    const uint32_t code = (word(R.k, byte >> 2) >> (8 * (byte & 3))) & 0xffu;
-                    const uint2 a = lut[code];
-                    c = mfma16(s4_of(a.x, a.y), pair_s4(qpB[kk]), c);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float v = c[i];
-                if (quant) v = v + xor_lane<G>(v) + kbias;
-                const bool valid = tc * 16 + 4 * qg + i < nt_here;
-                s[tc][i] = valid ? v * scale : -INFINITY;
-            }
-        };
-        score_tile(std::integral_constant<int, 0>{});
-        if (ntiles > 1) {
-            score_tile(std::integral_constant<int, 1>{});
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s[1][i] = -INFINITY;
-        }
-        // ---- online softmax per query column (lanes r < G)
-        float mx = -INFINITY;
-#pragma unroll
-        for (int tc = 0; tc < 2; ++tc)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tc][i]);
+    // online softmax over the lane's NVV scores (per column: max over the 4 lane groups)
+    auto softmax = [&](float* s, float* p, int nvv) __attribute__((always_inline)) {
+        float mx = s[0];
+        for (int v = 1; v < nvv; ++v) mx = fmaxf(mx, s[v]);
         mx = fmaxf(mx, xor_lane<16>(mx));
         mx = fmaxf(mx, xor_lane<32>(mx));
-        if (!live) mx = 0.f;
         const float mnew = fmaxf(m_run, mx);
         if (__any(mnew > m_run)) {
-            const float alpha = exp2f(m_run - mnew);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
             l_run *= alpha;
             lw *= alpha;
             vbias *= alpha;
@@ -330,85 +330,220 @@ __global__ void __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(2)
             for (int m = 0; m < MB; ++m) acc[m] *= alpha;
             m_run = mnew;
         }
-        float p[2][4];
         float ps = 0.f;
-#pragma unroll
-        for (int tc = 0; tc < 2; ++tc)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[tc][i] = live ? exp2f(s[tc][i] - m_run) : 0.f;
-                ps += p[tc][i];
-            }
+        for (int v = 0; v < nvv; ++v) {
+            p[v] = __builtin_amdgcn_exp2f(s[v] - m_run);
+            ps += p[v];
+        }
         l_run += ps;
         lw += ps;
-        // ---- O^T[channel][column] += V^T_tile . P
-        auto value_tile = [&](auto TCc) __attribute__((always_inline)) {
-            constexpr int tc = decltype(TCc)::value;
-            float pv[4];
-            if (!quant) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) pv[i] = p[tc][i];
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const f2_t o2 = h2f(word(R.k, 8 + 2 * tc + (i >> 1))), s2 = h2f(word(R.k, 12 + 2 * tc + (i >> 1)));
-                    const float o = (i & 1) ? o2.y : o2.x;
-                    const float sc = (i & 1) ? s2.y : s2.x;
-                    vbias = fmaf(p[tc][i], o, vbias);
-                    pv[i] = p[tc][i] * sc;
-                }
-            }
-            // column r < G: bf16(pv); column r + G: bf16(pv - bf16(pv))
-            const uint32_t h01 = bf16x2_rne(pv[0], pv[1]), h23 = bf16x2_rne(pv[2], pv[3]);
-            uint32_t w01 = h01, w23 = h23;
-            if (!prim) {
-                w01 = bf16x2_rne(pv[0] - bf16lo(h01), pv[1] - bf16hi(h01));
-                w23 = bf16x2_rne(pv[2] - bf16lo(h23), pv[3] - bf16hi(h23));
-            }
-            const s4_t bP = s4_of(w01, w23);
-            if (!quant) {
-#pragma unroll
-                for (int m = 0; m < MB; ++m)
-                    acc[m] = mfma16(pair_s4(R.v[tc * MB + m]), bP, acc[m]);
-            } else {
-#pragma unroll
-                for (int m = 0; m < MB; ++m) {
-                    const int byte = tc * MB + m;
-                    const uint32_t code = (word(R.k, 4 + (byte >> 2)) >> (8 * (byte & 3))) & 0xffu;
-                    const uint2 a = lut[code];
-                    acc[m] = mfma16(s4_of(a.x, a.y), bP, acc[m]);
-                }
-            }
-        };
-        value_tile(std::integral_constant<int, 0>{});
-        if (ntiles > 1) value_tile(std::integral_constant<int, 1>{});
-        if (j.ch + 1 == j.nch) {
-            // window done: log-sum-exp of its attention mass per query head (log2 domain)
-            float t = lw;
-            t += xor_lane<16>(t);
-            t += xor_lane<32>(t);
-            if (qg == 0 && r < G) lse_out[(int64_t)(e0 + j.i) * g.h_q + hk * G + r] = m_run + log2f(t);
+    };
+    // bf16 pair of x: high lanes get bf16(x), low lanes bf16(x - bf16(x))
+    auto hilo = [&](float x0, float x1) -> uint32_t {
+        const uint32_t r = bf16x2_rne(x0, x1);
+        return bf16x2_rne(fmaf(-lof, bf16lo(r), x0), fmaf(-lof, bf16hi(r), x1));
+    };
+    auto lut4 = [&](uint32_t w, int byte) -> u2_t {
+        const uint2 a = lut[(w >> (8 * byte)) & 0xffu];
+        return u2_t{a.x, a.y};
+    };
+    auto lse_store = [&](bool mine, int ie) {
+        float t = lw;
+        t += xor_lane<16>(t);
+        t += xor_lane<32>(t);
+        if (mine) {
+            if (qg == 0 && hi) lse_out[(int64_t)(e0 + ie) * g.h_q + head] = m_run + log2f(t);
             lw = 0.f;
         }
     };
 
-    // entries are staged in LDS in batches; inside a batch each wave runs a software
-    // pipeline in which the next job's loads are in flight while a job is processed
+    auto process_q = [&](const Job& j, const Raw& R) __attribute__((always_inline)) {
+        // (1) q * sclK for every (item, head, channel) once, split into bf16 high + low
+        //     rows of the wave's operand block; key-offset bias sum_c q_c offK_c per row
+        {
+            float bias = 0.f;
+            uint32_t hw[CPL / 2], lw2[CPL / 2];
+            float qf[CPL];
+#pragma unroll
+            for (int x = 0; x < CPL; x += 4) *reinterpret_cast<f4_t*>(&qf[x]) = *reinterpret_cast<const f4_t*>(&qfl[lane][x]);
+#pragma unroll
+            for (int x = 0; x < CPL / 2; ++x) {
+                const f2_t s2 = h2f(R.w[S::O_KS + x]), o2 = h2f(R.w[S::O_KO + x]);
+                const float x0 = qf[2 * x] * s2.x, x1 = qf[2 * x + 1] * s2.y;
+                bias = fmaf(qf[2 * x], o2.x, bias);
+                bias = fmaf(qf[2 * x + 1], o2.y, bias);
+                hw[x] = bf16x2_trunc(x0, x1);
+                lw2[x] = bf16x2_rne(x0 - bf16lo(hw[x]), x1 - bf16hi(hw[x]));
+            }
+            bias = lanes_sum<1, LPR>(bias);
+            wave_lds_fence();
+            stw<CPL / 2>(&qs[wave][pitem * SW + phead][CPL * pcb], hw);
+            stw<CPL / 2>(&qs[wave][pitem * SW + SW - 1 - phead][CPL * pcb], lw2);
+            if (pcb == 0) {
+                kb[wave][pitem * SW + phead] = bias;
+                kb[wave][pitem * SW + SW - 1 - phead] = bias;
+            }
+            wave_lds_fence();
+        }
+        // (2) the lane's column of the operand
+        u4_t bq[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bq[ks] = *reinterpret_cast<const u4_t*>(&qs[wave][n][CQ * qg + 8 * ks]);
+        const float kbs = kb[wave][n] * scale;
+        // (3) scores S^T[token][column] = codes . (q * sclK)
+        float s[NV];
+#pragma unroll
+        for (int tc = 0; tc < TPC; ++tc) {
+            f4_t da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int by = tc * (CQ / 4) + 2 * ks;
+                const uint32_t wa = R.w[by >> 2];
+                const u2_t a0 = lut4(wa, by & 3), a1 = lut4(wa, (by & 3) + 1);
+                da = mfma32(u4_t{a0.x, a0.y, a1.x, a1.y}, bq[ks], da);
+                if constexpr (NSLOT == 2) {
+                    const uint32_t wb = R.w[S::KCW + (by >> 2)];
+                    const u2_t b0 = lut4(wb, by & 3), b1 = lut4(wb, (by & 3) + 1);
+                    db = mfma32(u4_t{b0.x, b0.y, b1.x, b1.y}, bq[ks], db);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v = (NSLOT == 2 && slot) ? db[i] : da[i];
+                v += mirror<SW>(v);                            // high + low query parts
+                s[4 * tc + i] = fmaf(v, scale, kbs);
+            }
+        }
+        if (NSLOT == 2 && j.ib < 0) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) s[v] = slot ? -INFINITY : s[v];
+        }
+        float p[NV];
+        softmax(s, p, NV);
+        // (4) P' = p * sclV (high / low bf16 parts); value-offset bias sum_t p_t offV_t
+        uint32_t P[NV / 2];
+#pragma unroll
+        for (int x = 0; x < NV / 2; ++x) {
+            const f2_t o2 = h2f(R.w[S::O_VO + x]), c2 = h2f(R.w[S::O_VS + x]);
+            vbias = fmaf(p[2 * x], o2.x, vbias);
+            vbias = fmaf(p[2 * x + 1], o2.y, vbias);
+            P[x] = hilo(p[2 * x] * c2.x, p[2 * x + 1] * c2.y);
+        }
+        u4_t pa, pb;
+        if constexpr (TPC == 2) {
+            pa = u4_t{P[0], P[1], P[2], P[3]};
+        } else {
+            pa = u4_t{P[0], P[1], 0u, 0u};
+        }
+        if constexpr (NSLOT == 2) {
+            const u4_t z = {0u, 0u, 0u, 0u};
+            pb = slot ? pa : z;
+            pa = slot ? z : pa;
+        }
+        // (5) O^T[channel][column] += codes^T . P'
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+            u4_t a;
+            if constexpr (TPC == 2) {
+                const int by = 2 * m;
+                const uint32_t w = R.w[S::O_VC + (by >> 2)];
+                const u2_t a0 = lut4(w, by & 3), a1 = lut4(w, (by & 3) + 1);
+                a = u4_t{a0.x, a0.y, a1.x, a1.y};
+            } else {
+                const u2_t a0 = lut4(R.w[S::O_VC + (m >> 2)], m & 3);
+                a = u4_t{a0.x, a0.y, 0u, 0u};
+            }
+            acc[m] = mfma32(a, pa, acc[m]);
+        }
+        if (NSLOT == 2 && j.ib >= 0) {
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+                u4_t a;
+                if constexpr (TPC == 2) {
+                    const int by = 2 * m;
+                    const uint32_t w = R.w[S::O_VC + S::VCW + (by >> 2)];
+                    const u2_t a0 = lut4(w, by & 3), a1 = lut4(w, (by & 3) + 1);
+                    a = u4_t{a0.x, a0.y, a1.x, a1.y};
+                } else {
+                    const u2_t a0 = lut4(R.w[S::O_VC + S::VCW + (m >> 2)], m & 3);
+                    a = u4_t{a0.x, a0.y, 0u, 0u};
+                }
+                acc[m] = mfma32(a, pb, acc[m]);
+            }
+        }
+        // (6) both windows end on their last chunk: log-sum-exp of their mass per head
+        if (j.c + 1 == NCH) lse_store(slot == 0 || j.ib >= 0, slot == 0 ? j.ia : j.ib);
+    };
+
+    auto process_f = [&](const Job& j, const Raw& R) __attribute__((always_inline)) {
+        u4_t bq[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bq[ks] = *reinterpret_cast<const u4_t*>(&qb[n][CQ * qg + 8 * ks]);
+        f4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            d = mfma32(u4_t{R.w[4 * ks], R.w[4 * ks + 1], R.w[4 * ks + 2], R.w[4 * ks + 3]}, bq[ks], d);
+        float s[4], p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool valid = slot == 0 && 16 * j.t + 4 * qg + i < j.ntok;
+            s[i] = valid ? d[i] * scale : -INFINITY;
+        }
+        softmax(s, p, 4);
+        const u2_t P = {hilo(p[0], p[1]), hilo(p[2], p[3])};
+#pragma unroll
+        for (int m = 0; m < MB; ++m) acc[m] = mfma16(u2_t{R.w[CQ / 2 + 2 * m], R.w[CQ / 2 + 2 * m + 1]}, P, acc[m]);
+        if (16 * (j.t + 1) >= j.ntok) lse_store(slot == 0, j.i);
+    };
+
+    // entries are staged in LDS in batches; each wave runs two passes (INT2 pairs,
+    // then bf16 tiles), each a two-deep software pipeline in which the next job's
+    // loads are in flight while a job is processed
     for (int bs = 0; bs < e_total; bs += DMAXE) {
         __syncthreads();
         e0 = e_begin + bs;
         ne = min(DMAXE, e_total - bs);
         for (int x = threadIdx.x; x < ne; x += 64 * DW) ent[x] = bf.acc[u * g.n_acc_max + e0 + x];
         __syncthreads();
-        Raw<D> cur, nxt;
-        Job j = resolve(wave);
-        load(j, cur);
-        while (j.i >= 0) {
-            const Job jn = next(j);
-            load(jn, nxt);          // in flight while the current job is processed
-            process(j, cur);
-            cur = nxt;
-            j = jn;
+        {   // unrolled by two so that the two buffers swap roles without copies
+            Raw ra, rb;
+            Job j = first_q();
+            load_q(j, ra);
+            while (j.type != 0) {
+                Job jn = next_q(j);
+                load_q(jn, rb);
+                process_q(j, ra);
+                j = jn;
+                if (j.type == 0) break;
+                jn = next_q(j);
+                load_q(jn, ra);
+                process_q(j, rb);
+                j = jn;
+            }
+        }
+        {
+            Raw ra, rb;
+            Job j = ent_f(wave);
+            if (j.type == 0) {
+                j.kind = EK_SINK;
+                j.idx = 0;
+                j.t = 0;
+                j.Wn = Ws;
+                j.ntok = 0;
+                j.i = 0;
+            }
+            load_f(j, ra);
+            while (j.type != 0) {
+                Job jn = next_f(j);
+                load_f(jn, rb);
+                process_f(j, ra);
+                j = jn;
+                if (j.type == 0) break;
+                jn = next_f(j);
+                load_f(jn, ra);
+                process_f(j, rb);
+                j = jn;
+            }
         }
     }
 
@@ -419,33 +554,47 @@ __global__ void __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(2)
     float vb = vbias;
     vb += xor_lane<16>(vb);
     vb += xor_lane<32>(vb);
+    float a[MB][4];
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float a = acc[m][i] + xor_lane<G>(acc[m][i]);     // high + low probability columns
-            if (prim) s_acc[wave][r][16 * m + 4 * qg + i] = a + vb;
+        for (int i = 0; i < 4; ++i) a[m][i] = acc[m][i] + mirror<SW>(acc[m][i]) + vb;   // high + low columns
+    float mw = m_run;
+    if constexpr (NSLOT == 2) {
+        const float m1 = ror8(m_run), l1 = ror8(lt);
+        const float M = fmaxf(m_run, m1);
+        const float f0 = exp2f(m_run - M), f1 = exp2f(m1 - M);
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[m][i] = f0 * a[m][i] + f1 * ror8(a[m][i]);
+        lt = f0 * lt + f1 * l1;
+        mw = M;
+    }
+    if (slot == 0 && hi) {
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s_acc[wave][rn][16 * m + 4 * qg + i] = a[m][i];
+        if (qg == 0) {
+            s_m[wave][rn] = mw;
+            s_l[wave][rn] = lt;
         }
-    if (qg == 0) {
-        s_m[wave][r] = m_run;
-        s_l[wave][r] = lt;
     }
     __syncthreads();
     float* pacc = bf.part_acc + ((u * g.n_splits + split) * (int64_t)g.h_q + hk * G) * D;
     float2* pml = bf.part_ml + (u * g.n_splits + split) * (int64_t)g.h_q + hk * G;
     for (int x = threadIdx.x; x < G * D; x += 64 * DW) {
         const int gg = x / D, c = x % D;
-        float M = -INFINITY;
+        float M = s_m[0][gg];
 #pragma unroll
-        for (int w = 0; w < DW; ++w) M = fmaxf(M, s_m[w][gg]);
+        for (int w = 1; w < DW; ++w) M = fmaxf(M, s_m[w][gg]);
         float L = 0.f, A = 0.f;
-        if (M > -INFINITY) {
 #pragma unroll
-            for (int w = 0; w < DW; ++w) {
-                const float f = s_m[w][gg] > -INFINITY ? exp2f(s_m[w][gg] - M) : 0.f;
-                L += f * s_l[w][gg];
-                A += f * s_acc[w][gg][c];
-            }
+        for (int w = 0; w < DW; ++w) {
+            const float f = exp2f(s_m[w][gg] - M);
+            L += f * s_l[w][gg];
+            A += f * s_acc[w][gg][c];
         }
         pacc[(int64_t)gg * D + c] = A;
         if (c == 0) pml[gg] = make_float2(M, L);
@@ -454,14 +603,16 @@ __global__ void __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(2)
 
 hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t* q, hipStream_t s) {
     const dim3 grid(g.n_splits, g.h_kv, g.B), block(64 * DW);
-    const int G = g.h_q / g.h_kv;
-#define QV_DEC(D_, G_)                                                                          \
-    if (g.d == D_ && G == G_) {                                                                 \
-        hipLaunchKernelGGL((k_decode_split<D_, G_>), grid, block, 0, s, g, bf, layer, q);      \
-        return hipGetLastError();                                                               \
+    const int G = g.h_q / g.h_kv, TPC = lay_tpc(g.W);
+#define QV_DEC(D_, G_, T_)                                                                     \
+    if (g.d == D_ && G == G_ && TPC == T_) {                                                   \
+        hipLaunchKernelGGL((k_decode_split<D_, G_, T_>), grid, block, 0, s, g, bf, layer, q); \
+        return hipGetLastError();                                                              \
     }
-    QV_DEC(128, 1) QV_DEC(128, 2) QV_DEC(128, 4) QV_DEC(128, 8)
-    QV_DEC(64, 1) QV_DEC(64, 2) QV_DEC(64, 4) QV_DEC(64, 8)
+    QV_DEC(128, 1, 2) QV_DEC(128, 2, 2) QV_DEC(128, 4, 2) QV_DEC(128, 8, 2)
+    QV_DEC(64, 1, 2) QV_DEC(64, 2, 2) QV_DEC(64, 4, 2) QV_DEC(64, 8, 2)
+    QV_DEC(128, 1, 1) QV_DEC(128, 2, 1) QV_DEC(128, 4, 1) QV_DEC(128, 8, 1)
+    QV_DEC(64, 1, 1) QV_DEC(64, 2, 1) QV_DEC(64, 4, 1) QV_DEC(64, 8, 1)
 #undef QV_DEC
     return hipErrorInvalidValue;
 }

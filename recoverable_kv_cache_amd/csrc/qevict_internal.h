@@ -104,7 +104,7 @@ struct Bufs {
 __host__ __device__ inline int64_t unit_of(const Geo& g, int b, int l) { return (int64_t)b * g.L + l; }
 
 // ------------------------------------------------------------------ in-HBM layouts
-// The decode kernel feeds 16x16x16 MFMA tiles straight from HBM, so pages and
+// The decode kernel feeds MFMA tiles straight from HBM, so pages and
 // slots are stored in the order a lane consumes them.  One head of a window of
 // W tokens (NT = W/16 tiles of 16 tokens), D channels, CQ = D/4 channels per
 // lane group, MB = D/16 channel blocks.  t = 16*tile + r, c = CQ*qg + cc.
@@ -117,7 +117,8 @@ __host__ __device__ inline int64_t unit_of(const Geo& g, int b, int l) { return 
 //             (a lane reads, per tile, 4 tokens x MB channel blocks of one channel row)
 // INT2 slot of one head (same byte count as the canonical record):
 //   K codes [W*D/4]: code (t, c) in byte (((ch*16 + r)*4 + qg)*TPC + tc)*(CQ/4) + cc/4, bits 2*(cc%4)
-//   V codes [W*D/4]: code (t, c) in byte (((c%16)*4 + r/4)*NT + tile)*MB + c/16, bits 2*(r%4)
+//   V codes [W*D/4]: code (t, c) in byte ((((c%16)*4 + r/4)*NCH + ch)*MB + c/16)*TPC + tc, bits 2*(r%4)
+//             (a lane reads, per chunk, MB x TPC bytes: 4 tokens of each tile of the chunk per channel block)
 //   K offset [D], K scale [D] (fp16, channel order), V offset [W], V scale [W] (fp16) with
 //   token t at ((r/4)*NT + tile)*4 + r%4.
 __host__ __device__ inline int lay_tpc(int W) { return (W < 32 ? W : 32) / 16; }
@@ -137,8 +138,9 @@ __host__ __device__ inline int lay_kc_byte(int t, int c, int D, int W) {
 }
 __host__ __device__ inline int lay_kc_shift(int c) { return 2 * (c & 3); }
 __host__ __device__ inline int lay_vc_byte(int t, int c, int D, int W) {
-    const int NT = W / 16, MB = D / 16;
-    return (((c & 15) * 4 + (t & 15) / 4) * NT + (t >> 4)) * MB + c / 16;
+    const int TPC = lay_tpc(W), NCH = W / (16 * TPC), MB = D / 16;
+    const int tile = t >> 4;
+    return ((((c & 15) * 4 + (t & 15) / 4) * NCH + tile / TPC) * MB + c / 16) * TPC + tile % TPC;
 }
 __host__ __device__ inline int lay_vc_shift(int t) { return 2 * (t & 3); }
 __host__ __device__ inline int lay_vp(int t, int W) {

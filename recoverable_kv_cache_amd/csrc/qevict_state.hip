@@ -654,14 +654,11 @@ __global__ void __launch_bounds__(PK_THREADS) k_pack(Geo g, Bufs bf, int layer, 
             slot[lay_kc_byte(i, 4 * c4, d, W)] = (uint8_t)(pk[0] | (pk[1] << 2) | (pk[2] << 4) | (pk[3] << 6));
         }
         // V codes: one byte = 4 consecutive tokens of one channel (lay_vc_byte)
-        {
-            const int NT = W / 16, MB = d / 16;
-            for (int e = threadIdx.x; e < W * d / 4; e += PK_THREADS) {
-                const int m = e % MB, tile = (e / MB) % NT, qg = (e / (MB * NT)) % 4, r = e / (MB * NT * 4);
-                const int c = 16 * m + r, t0 = 16 * tile + 4 * qg;
-                slot[W * d / 4 + e] = (uint8_t)(cv[t0 * d + c] | (cv[(t0 + 1) * d + c] << 2) |
-                                                 (cv[(t0 + 2) * d + c] << 4) | (cv[(t0 + 3) * d + c] << 6));
-            }
+        for (int e = threadIdx.x; e < W * d / 4; e += PK_THREADS) {
+            const int c = e % d, t0 = 4 * (e / d);
+            slot[W * d / 4 + lay_vc_byte(t0, c, d, W)] =
+                (uint8_t)(cv[t0 * d + c] | (cv[(t0 + 1) * d + c] << 2) | (cv[(t0 + 2) * d + c] << 4) |
+                          (cv[(t0 + 3) * d + c] << 6));
         }
         __syncthreads();
     }
