@@ -71,7 +71,7 @@ typedef struct {
     int32_t max_prompt;   /* S_max: prompt buffers are [..][S_max][d] */
     int32_t max_new;      /* N_g: generated tokens; B_total covers prompt_len + max_new */
     uint32_t flags;       /* QEVICT_F_* */
-    int32_t n_splits;     /* decode splits per (sequence, KV head); 0 = choose */
+    int32_t n_splits;     /* decode splits per (sequence, KV head); 0 = choose; capped at 512 / (h_q / h_kv) */
 } qevict_config;
 
 typedef struct {

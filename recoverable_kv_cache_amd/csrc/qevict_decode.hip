@@ -1,7 +1,11 @@
-// Decode step: split-K attention over the accessible list (sinks, recent
-// windows, Full bf16 windows, Quantized INT2 windows), then a combine pass that
-// normalises the splits with the global log-sum-exp and turns per-window
-// partial exp-sums into window masses.
+// Decode step, two launches per layer.  k_decode_split appends the new token to
+// its recent window and runs split-K attention over the accessible list (sinks,
+// recent windows, Full bf16 windows, Quantized INT2 windows); k_finish combines
+// the splits of each query head with the global log-sum-exp, writes each
+// entry's per-head share of this step's window mass, and advances the token
+// count.  The shares are folded into the cumulative scores by the next
+// k_decode_split of the unit (or by the router / an export, whichever comes
+// first), which overlaps that read-modify-write with other work.
 //
 // Source: "QEvict: Recoverable Quantized KV Eviction for Attention-Drift-Robust
 // Long-Context Decoding", §4.1 (accessible-set attention, scale 1/sqrt(d_kv);
@@ -21,6 +25,7 @@
 
 #include "qevict_common.h"
 #include "qevict_internal.h"
+#include "qevict_mass.h"
 
 namespace qv {
 
@@ -142,12 +147,13 @@ struct Job {
     int type;           // 0 none, 1 INT2, 2 bf16
     int ia, ib, c;      // INT2: batch-local entry indices (ib = -1: slot 1 empty), chunk
     int sa, sb;         // INT2: slot ids
-    int i, t, kind, idx, ntok, Wn;   // bf16: entry, tile, kind, page id, valid tokens, block width
+    int i, t, kind, idx, ntok, Wn, start;   // bf16: entry, tile, kind, page id, valid tokens, block width, position 0
 };
 
 template <int D, int G, int TPC>
 __global__ void __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(2)))
-k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin) {
+k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, const uint16_t* __restrict__ knew,
+               const uint16_t* __restrict__ vnew) {
     using S = DecShape<D, G, TPC>;
     constexpr int CQ = S::CQ, KS = S::KS, MB = S::MB, NSLOT = S::NSLOT, SW = S::SW, LPR = S::LPR, CPL = S::CPL;
     constexpr int NV = S::NV, QSTR = S::QSTR;
@@ -159,6 +165,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin) {
     __shared__ __attribute__((aligned(16))) float qfl[64][CPL];          // q of each lane's product channels
     __shared__ float s_m[DW][G], s_l[DW][G];
     __shared__ float s_acc[DW][G][D];
+    __shared__ __attribute__((aligned(16))) uint16_t nkv[2][D];         // the new token's K and V of this KV head
 
     const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
     const int64_t u = unit_of(g, b, layer);
@@ -177,12 +184,46 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin) {
 
     const int32_t* splits = bf.splits + u * (g.n_splits + 1);
     const int e_begin = splits[split], e_total = splits[split + 1] - e_begin;
-    const int n_tok = bf.hdr[u].n;
+    const int n_old = bf.hdr[u].n;       // tokens before this step; the new one sits at position n_old
+    const int pending = bf.hdr[u].mass_pending;
+    const int n_tok = n_old + 1;
     const uint16_t* qhead = qin + ((int64_t)b * g.h_q + hk * G) * D;
     // 4 packed 2-bit codes -> 4 bf16 {0, 1, 2, 3}
     for (int x = threadIdx.x; x < 256; x += 64 * DW) {
         auto bv = [](int c) -> uint32_t { return c == 0 ? 0u : (c == 1 ? 0x3F80u : (c == 2 ? 0x4000u : 0x4040u)); };
         lut[x] = make_uint2(bv(x & 3) | (bv((x >> 2) & 3) << 16), bv((x >> 4) & 3) | (bv((x >> 6) & 3) << 16));
+    }
+    // the new token: staged in LDS for the wave that attends its tile, and written
+    // into its sink / recent-window block by the first split of each KV head
+    if (wave == 1 && lane < D / 2) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(knew + ((int64_t)b * g.h_kv + hk) * D);
+        const uint32_t* srv = reinterpret_cast<const uint32_t*>(vnew + ((int64_t)b * g.h_kv + hk) * D);
+        reinterpret_cast<uint32_t*>(nkv[0])[lane] = src[lane];
+        reinterpret_cast<uint32_t*>(nkv[1])[lane] = srv[lane];
+    }
+    if (split == 0 && wave >= 2) {
+        uint16_t* blk = nullptr;
+        int Wp = W, i = 0;
+        if (n_old < g.n_sink) {
+            blk = bf.sinks + u * g.sink_elems;
+            Wp = Ws;
+            i = n_old;
+        } else {
+            const int w = (n_old - g.n_sink) / W;
+            i = (n_old - g.n_sink) % W;
+            const WinRec rec = w < g.n_windows ? bf.win[u * g.n_windows + w] : WinRec{ST_NONE, -1, -1, 0};
+            if (rec.state == ST_LOCAL && rec.page >= 0)
+                blk = bf.pages + u * (int64_t)g.n_pages * g.page_elems + (int64_t)rec.page * g.page_elems;
+            else if (threadIdx.x == 128)
+                atomicOr(&bf.hdr[u].status, QEVICT_DEV_E_WINDOW);
+        }
+        if (blk) {
+            uint16_t* kh = blk + (int64_t)(2 * hk) * Wp * D;
+            for (int c = threadIdx.x - 128; c < D; c += 128) {
+                kh[lay_k(i, c, D, Wp)] = knew[((int64_t)b * g.h_kv + hk) * D + c];
+                kh[(int64_t)Wp * D + lay_v(i, c, D, Wp)] = vnew[((int64_t)b * g.h_kv + hk) * D + c];
+            }
+        }
     }
     // bf16 windows: every live column holds its head's query (exact bf16);
     // INT2 windows: each lane's product channels of q, as fp32
@@ -224,7 +265,10 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin) {
             const int kind = rfl(ent[i].kind), idx = rfl(ent[i].idx), start = rfl(ent[i].start);
             if (kind == EK_SLOT) continue;
             const int nt = kind == EK_SINK ? min(g.n_sink, n_tok) : min(W, n_tok - start);
-            if (nt <= 0 || (kind != EK_SINK && idx < 0)) continue;
+            if (nt <= 0 || (kind != EK_SINK && idx < 0)) {
+                if (lane < G) lse_out[(int64_t)(e0 + i) * g.h_q + lane] = -INFINITY;   // no tokens yet: no mass
+                continue;
+            }
             j.type = 2;
             j.i = i;
             j.t = 0;
@@ -232,6 +276,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin) {
             j.idx = idx;
             j.ntok = nt;
             j.Wn = kind == EK_SINK ? Ws : W;
+            j.start = kind == EK_SINK ? 0 : start;
             return j;
         }
         return j;
@@ -479,10 +524,30 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin) {
         u4_t bq[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) bq[ks] = *reinterpret_cast<const u4_t*>(&qb[n][CQ * qg + 8 * ks]);
+        uint32_t kw[CQ / 2], vw[2 * MB];
+#pragma unroll
+        for (int x = 0; x < CQ / 2; ++x) kw[x] = R.w[x];
+#pragma unroll
+        for (int x = 0; x < 2 * MB; ++x) vw[x] = R.w[CQ / 2 + x];
+        const int pt = n_old - j.start - 16 * j.t;    // the new token's row in this tile, if any
+        if (pt >= 0 && pt < 16) {
+            // its K row (lanes of token row pt) and its V column entries come from LDS
+            if (n == pt) {
+#pragma unroll
+                for (int x = 0; x < CQ / 2; ++x) kw[x] = reinterpret_cast<const uint32_t*>(&nkv[0][CQ * qg])[x];
+            }
+            if (qg == (pt >> 2)) {
+#pragma unroll
+                for (int m = 0; m < MB; ++m) {
+                    const uint32_t v = nkv[1][16 * m + n];
+                    const int x = 2 * m + ((pt & 3) >> 1);
+                    vw[x] = (pt & 1) ? ((vw[x] & 0xFFFFu) | (v << 16)) : ((vw[x] & 0xFFFF0000u) | v);
+                }
+            }
+        }
         f4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            d = mfma32(u4_t{R.w[4 * ks], R.w[4 * ks + 1], R.w[4 * ks + 2], R.w[4 * ks + 3]}, bq[ks], d);
+        for (int ks = 0; ks < KS; ++ks) d = mfma32(u4_t{kw[4 * ks], kw[4 * ks + 1], kw[4 * ks + 2], kw[4 * ks + 3]}, bq[ks], d);
         float s[4], p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -492,7 +557,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin) {
         softmax(s, p, 4);
         const u2_t P = {hilo(p[0], p[1]), hilo(p[2], p[3])};
 #pragma unroll
-        for (int m = 0; m < MB; ++m) acc[m] = mfma16(u2_t{R.w[CQ / 2 + 2 * m], R.w[CQ / 2 + 2 * m + 1]}, P, acc[m]);
+        for (int m = 0; m < MB; ++m) acc[m] = mfma16(u2_t{vw[2 * m], vw[2 * m + 1]}, P, acc[m]);
         if (16 * (j.t + 1) >= j.ntok) lse_store(slot == 0, j.i);
     };
 
@@ -531,6 +596,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin) {
                 j.Wn = Ws;
                 j.ntok = 0;
                 j.i = 0;
+                j.start = 0;
             }
             load_f(j, ra);
             while (j.type != 0) {
@@ -546,6 +612,11 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin) {
             }
         }
     }
+
+    // ---- the previous step's pending window-mass shares of this split's entries
+    //      (each entry once: the KV head whose index matches its position in the split)
+    if (pending && wave == DW - 1)
+        apply_mass_range(g, bf, u, e_begin + hk + g.h_kv * lane, e_begin + e_total, 64 * g.h_kv);
 
     // ---- wave state -> workgroup partial for this split
     float lt = l_run;
@@ -601,12 +672,13 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin) {
     }
 }
 
-hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t* q, hipStream_t s) {
+hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t* q, const uint16_t* k_new,
+                         const uint16_t* v_new, hipStream_t s) {
     const dim3 grid(g.n_splits, g.h_kv, g.B), block(64 * DW);
     const int G = g.h_q / g.h_kv, TPC = lay_tpc(g.W);
 #define QV_DEC(D_, G_, T_)                                                                     \
     if (g.d == D_ && G == G_ && TPC == T_) {                                                   \
-        hipLaunchKernelGGL((k_decode_split<D_, G_, T_>), grid, block, 0, s, g, bf, layer, q); \
+        hipLaunchKernelGGL((k_decode_split<D_, G_, T_>), grid, block, 0, s, g, bf, layer, q, k_new, v_new); \
         return hipGetLastError();                                                              \
     }
     QV_DEC(128, 1, 2) QV_DEC(128, 2, 2) QV_DEC(128, 4, 2) QV_DEC(128, 8, 2)
@@ -617,98 +689,128 @@ hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t
     return hipErrorInvalidValue;
 }
 
-// ------------------------------------------------------------------------------------ combine
-// o_h = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s ; LSE_h = M + log2 L (log2 domain)
-constexpr int CB_THREADS = 256;
-constexpr int CB_MAXS = 1024;
 
-__global__ void __launch_bounds__(CB_THREADS) k_combine(Geo g, Bufs bf, int layer, float* __restrict__ out) {
-    __shared__ float wsp[CB_MAXS];
-    __shared__ float red[CB_THREADS];
-    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+// ------------------------------------------------------------------------------------ finish
+// One workgroup per (query head, sequence): o_h = sum_s 2^(m_s - M) acc_s / L with
+// L = sum_s 2^(m_s - M) l_s and LSE_h = M + log2 L (log2 domain); the head's share
+// of every entry's window mass, 2^(lse_w,h - LSE_h); the token count.  Every load
+// of the workgroup is issued up front.
+constexpr int FN_THREADS = 256;
+constexpr int FN_MAXS = 512;            // splits (the host caps n_splits below this)
+constexpr int FN_MAXE = 16;             // entries per thread: n_acc_max <= 4096
+
+template <int D>
+__global__ void __launch_bounds__(FN_THREADS) k_finish(Geo g, Bufs bf, int layer, float* __restrict__ out,
+                                                       int score_now) {
+    constexpr int C4 = D / 4, PH = FN_THREADS / C4;    // float4 columns, split phases
+    __shared__ float ws[FN_MAXS], ls[FN_MAXS];
+    __shared__ f4_t part[FN_THREADS];
+    __shared__ float red[FN_THREADS / 64][2];
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t u = unit_of(g, b, layer);
     const int NS = g.n_splits;
-    const float2* pml = bf.part_ml + u * NS * (int64_t)g.h_q + h;
-    const float* pacc = bf.part_acc + (u * NS * (int64_t)g.h_q + h) * g.d;   // + channel below
-    float M = -INFINITY;
-    for (int s = tid; s < NS; s += CB_THREADS) M = fmaxf(M, pml[(int64_t)s * g.h_q].x);
-    red[tid] = M;
-    __syncthreads();
-    for (int o = CB_THREADS / 2; o > 0; o >>= 1) {
-        if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-        __syncthreads();
+    const int n_acc = bf.hdr[u].n_acc;
+    // window log-sum-exps of this head (independent of the combine: loaded first)
+    float lwv[FN_MAXE];
+    const float* lwin = bf.lse_win + u * (int64_t)g.n_acc_max * g.h_q + h;
+#pragma unroll
+    for (int k = 0; k < FN_MAXE; ++k) {
+        const int e = 1 + tid + FN_THREADS * k;
+        lwv[k] = (score_now && e < n_acc) ? lwin[(int64_t)e * g.h_q] : -INFINITY;
     }
-    M = red[0];
+    // split statistics and partial numerators
+    const float2* ml = bf.part_ml + u * NS * (int64_t)g.h_q + h;
+    float mloc = M_INIT;
+    for (int sp = tid; sp < NS; sp += FN_THREADS) {
+        const float2 v = ml[(int64_t)sp * g.h_q];
+        ws[sp] = v.x;
+        ls[sp] = v.y;
+        mloc = fmaxf(mloc, v.x);
+    }
+    const int col = tid % C4, ph = tid / C4;
+    const f4_t* pa = reinterpret_cast<const f4_t*>(bf.part_acc + (u * NS * (int64_t)g.h_q + h) * D) + col;
+    const int64_t sstride = (int64_t)g.h_q * D / 4;   // float4 per split
+    f4_t x[8];
+    int sp0 = ph;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = sp0 + k * PH < NS ? pa[(sp0 + k * PH) * sstride] : f4_t{0.f, 0.f, 0.f, 0.f};
+    // M, weights, L
+    mloc = lanes_max<1, 64>(mloc);
+    if (lane == 0) red[wv][0] = mloc;
+    __syncthreads();
+    float M = red[0][0];
+#pragma unroll
+    for (int w = 1; w < FN_THREADS / 64; ++w) M = fmaxf(M, red[w][0]);
+    float lloc = 0.f;
+    for (int sp = tid; sp < NS; sp += FN_THREADS) {
+        const float f = __builtin_amdgcn_exp2f(ws[sp] - M);
+        ws[sp] = f;
+        lloc += f * ls[sp];
+    }
+    lloc = lanes_sum<1, 64>(lloc);
+    if (lane == 0) red[wv][1] = lloc;
     __syncthreads();
     float L = 0.f;
-    for (int s = tid; s < NS; s += CB_THREADS) {
-        const float2 ml = pml[(int64_t)s * g.h_q];
-        const float f = ml.x > -INFINITY ? exp2f(ml.x - M) : 0.f;
-        wsp[s] = f;
-        L += f * ml.y;
-    }
-    red[tid] = L;
+#pragma unroll
+    for (int w = 0; w < FN_THREADS / 64; ++w) L += red[w][1];
+    f4_t a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        if (sp0 + k * PH < NS) a4 += ws[sp0 + k * PH] * x[k];
+    for (int sp = sp0 + 8 * PH; sp < NS; sp += PH) a4 += ws[sp] * pa[sp * sstride];
+    part[tid] = a4;
     __syncthreads();
-    for (int o = CB_THREADS / 2; o > 0; o >>= 1) {
-        if (tid < o) red[tid] += red[tid + o];
-        __syncthreads();
+    if (tid < C4) {
+        f4_t o = part[tid];
+        for (int p = 1; p < PH; ++p) o += part[p * C4 + tid];
+        reinterpret_cast<f4_t*>(out + ((int64_t)b * g.h_q + h) * D)[tid] = o / L;
     }
-    L = red[0];
-    __syncthreads();
-    const int parts = CB_THREADS / g.d, c = tid % g.d, part = tid / g.d;
-    pacc += c;
-    float A = 0.f;
-    if (part < parts) {
-        int s = part;
-        for (; s + 3 * parts < NS; s += 4 * parts) {
-            const float a0 = pacc[(int64_t)s * g.h_q * g.d], a1 = pacc[(int64_t)(s + parts) * g.h_q * g.d];
-            const float a2 = pacc[(int64_t)(s + 2 * parts) * g.h_q * g.d];
-            const float a3 = pacc[(int64_t)(s + 3 * parts) * g.h_q * g.d];
-            A += wsp[s] * a0 + wsp[s + parts] * a1 + wsp[s + 2 * parts] * a2 + wsp[s + 3 * parts] * a3;
+    const float lse = M + log2f(L);
+    if (tid == 0) bf.lse_glob[u * g.h_q + h] = lse;
+    // this head's share of each entry's window mass (entries without tokens carry -inf)
+    if (score_now) {
+        float* mp = bf.mass_part + u * (int64_t)g.n_acc_max * g.h_q + h;
+#pragma unroll
+        for (int k = 0; k < FN_MAXE; ++k) {
+            const int e = 1 + tid + FN_THREADS * k;
+            if (e < n_acc) mp[(int64_t)e * g.h_q] = __builtin_amdgcn_exp2f(lwv[k] - lse);
         }
-        for (; s < NS; s += parts) A += wsp[s] * pacc[(int64_t)s * g.h_q * g.d];
     }
-    red[tid] = A;
-    __syncthreads();
-    if (tid < g.d) {
-        float t = 0.f;
-        for (int pp = 0; pp < parts; ++pp) t += red[pp * g.d + tid];
-        out[((int64_t)b * g.h_q + h) * g.d + tid] = t / L;
+    if (h == 0 && tid == 0) {
+        UnitHdr* hdr = bf.hdr + u;
+        const int n_old = hdr->n;
+        bool ok = true;
+        if (n_old >= g.n_sink) {
+            const int w = (n_old - g.n_sink) / g.W;
+            ok = w < g.n_windows && bf.win[u * g.n_windows + w].state == ST_LOCAL && bf.win[u * g.n_windows + w].page >= 0;
+        }
+        if (ok) hdr->n = n_old + 1;
+        hdr->mass_pending = score_now;
     }
-    if (tid == 0) bf.lse_glob[u * g.h_q + h] = M + log2f(L);
 }
 
-hipError_t launch_combine(const Geo& g, const Bufs& bf, int layer, float* out, hipStream_t s) {
-    hipLaunchKernelGGL(k_combine, dim3(g.h_q, g.B), dim3(CB_THREADS), 0, s, g, bf, layer, out);
+hipError_t launch_finish(const Geo& g, const Bufs& bf, int layer, float* out, int score_now, hipStream_t s) {
+    if (g.n_splits > FN_MAXS || g.n_acc_max > 1 + FN_THREADS * FN_MAXE) return hipErrorInvalidValue;
+    const dim3 grid(g.h_q, g.B), block(FN_THREADS);
+    if (g.d == 128) hipLaunchKernelGGL(k_finish<128>, grid, block, 0, s, g, bf, layer, out, score_now);
+    else if (g.d == 64) hipLaunchKernelGGL(k_finish<64>, grid, block, 0, s, g, bf, layer, out, score_now);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
-// ------------------------------------------------------------------------------------ window mass
-// u(w) = (1/H_q) sum_h 2^(lse_w,h - LSE_h) = (1/H_q) sum_h sum_{i in w} a_h(i);  S_bar(w) += u(w)
-// One wave per accessible entry, lanes over query heads.
-__global__ void __launch_bounds__(256) k_mass(Geo g, Bufs bf, int layer) {
-    const int b = blockIdx.y;
+// ------------------------------------------------------------------------------------ flush
+// Folds a unit's pending window-mass shares into its scores (before an export).
+__global__ void __launch_bounds__(256) k_flush_mass(Geo g, Bufs bf, int layer, int b) {
     const int64_t u = unit_of(g, b, layer);
-    const UnitHdr* hdr = bf.hdr + u;
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-    if (e == 0 || e >= hdr->n_acc) return;
-    if (g.flags & QEVICT_F_SCORE_ROUTE_ONLY) {
-        const int j = hdr->n - hdr->prompt_len - 1;   // index of the decode step just taken
-        if ((j + 1) % g.omega != 0) return;
-    }
-    const AccEntry en = bf.acc[u * g.n_acc_max + e];
-    if (en.start >= hdr->n) return;
-    double s = 0.0;
-    if (lane < g.h_q) s = (double)exp2f(bf.lse_win[(u * g.n_acc_max + e) * (int64_t)g.h_q + lane] -
-                                        bf.lse_glob[u * g.h_q + lane]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-    if (lane == 0) bf.score[u * g.n_windows + en.win] += s / g.h_q;
+    UnitHdr* hdr = bf.hdr + u;
+    if (!hdr->mass_pending) return;
+    apply_mass_range(g, bf, u, threadIdx.x, hdr->n_acc, blockDim.x);
+    __syncthreads();
+    if (threadIdx.x == 0) hdr->mass_pending = 0;
 }
 
-hipError_t launch_mass(const Geo& g, const Bufs& bf, int layer, hipStream_t s) {
-    const int nb = (g.n_acc_max + 3) / 4;
-    hipLaunchKernelGGL(k_mass, dim3(nb, g.B), dim3(256), 0, s, g, bf, layer);
+hipError_t launch_flush_mass(const Geo& g, const Bufs& bf, int layer, int b, hipStream_t s) {
+    hipLaunchKernelGGL(k_flush_mass, dim3(1), dim3(256), 0, s, g, bf, layer, b);
     return hipGetLastError();
 }
 

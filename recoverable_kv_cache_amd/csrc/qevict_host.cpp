@@ -88,16 +88,17 @@ qevict_status caps_of(const qevict_config* c, int32_t prompt_len, Caps* out) {
     return QEVICT_OK;
 }
 
+constexpr int O_COUNT_MAX = 32;
 struct Layout {
     Geo g;
-    size_t off[20];
+    size_t off[O_COUNT_MAX];
     size_t total;
     size_t export_bytes;
     int32_t max_kf, max_kq;
 };
 
 enum { O_HDR, O_WIN, O_SCORE, O_ACC, O_SPLITS, O_FPAGE, O_FSLOT, O_PACK, O_FILL, O_TARGET, O_LSEW, O_LSEG,
-       O_PML, O_PACC, O_PAGES, O_SLOTS, O_SINKS, O_PLENS, O_KF, O_KQ };
+       O_PML, O_PACC, O_PAGES, O_SLOTS, O_SINKS, O_PLENS, O_KF, O_KQ, O_DONE, O_MPART, O_COUNT };
 
 qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, Layout* lay) {
     qevict_status s = validate(c);
@@ -133,14 +134,17 @@ qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, La
         if (ns > cap) ns = cap;
         if (ns < 1) ns = 1;
     }
-    if (ns > 1024) ns = 1024;
+    // the decode kernel's split combiner stages (m, l) of every (split, query head of a
+    // KV group) in LDS: at most 512 of them
+    const int32_t ns_max = 512 / (c->h_q / c->h_kv);
+    if (ns > ns_max) ns = ns_max;
     g.n_splits = ns;
     g.page_elems = g.h_kv * 2 * g.W * g.d;
     g.slot_head_bytes = g.W * g.d / 2 + 4 * g.d + 4 * g.W;
     g.slot_bytes = g.h_kv * g.slot_head_bytes;
     g.sink_elems = g.h_kv * 2 * sink_width(g.n_sink) * g.d;
     const size_t U = (size_t)g.B * g.L;
-    size_t sz[20];
+    size_t sz[O_COUNT];
     sz[O_HDR] = U * sizeof(UnitHdr);
     sz[O_WIN] = U * g.n_windows * sizeof(WinRec);
     sz[O_SCORE] = U * g.n_windows * sizeof(double);
@@ -159,8 +163,10 @@ qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, La
     sz[O_SLOTS] = U * g.n_slots * (size_t)g.slot_bytes;
     sz[O_SINKS] = U * (size_t)g.sink_elems * 2;
     sz[O_PLENS] = sz[O_KF] = sz[O_KQ] = g.B * sizeof(int32_t);
+    sz[O_DONE] = U * (g.h_kv + 1) * sizeof(int32_t);
+    sz[O_MPART] = U * (size_t)g.n_acc_max * g.h_q * sizeof(float);
     size_t at = 0;
-    for (int i = 0; i < 20; ++i) {
+    for (int i = 0; i < O_COUNT; ++i) {
         lay->off[i] = at;
         at += align256(sz[i]);
     }
@@ -192,6 +198,8 @@ Bufs bind_bufs(const Layout& lay, void* arena) {
     b.pages = (uint16_t*)(a + lay.off[O_PAGES]);
     b.slots = (uint8_t*)(a + lay.off[O_SLOTS]);
     b.sinks = (uint16_t*)(a + lay.off[O_SINKS]);
+    b.done = (int32_t*)(a + lay.off[O_DONE]);
+    b.mass_part = (float*)(a + lay.off[O_MPART]);
     return b;
 }
 
@@ -340,13 +348,15 @@ qevict_status qevict_decode_attn(qevict_state* st, int32_t layer, const void* q,
         return fail(QEVICT_E_CAPACITY, "layer %d already decoded max_new = %d tokens", layer, st->cfg.max_new);
     hipStream_t hs = (hipStream_t)stream;
     const Geo& g = st->lay.g;
-    HIP_TRY(launch_append(g, st->bf, layer, (const uint16_t*)k_new, (const uint16_t*)v_new, hs));
     if (st->ev_before) HIP_TRY(hipEventRecord(st->ev_before, hs));
-    HIP_TRY(launch_decode(g, st->bf, layer, (const uint16_t*)q, hs));
+    HIP_TRY(launch_decode(g, st->bf, layer, (const uint16_t*)q, (const uint16_t*)k_new, (const uint16_t*)v_new, hs));
     if (st->ev_after) HIP_TRY(hipEventRecord(st->ev_after, hs));
     st->ev_before = st->ev_after = nullptr;
-    HIP_TRY(launch_combine(g, st->bf, layer, out, hs));
-    HIP_TRY(launch_mass(g, st->bf, layer, hs));
+    // Eq. 1 accumulates every step; with QEVICT_F_SCORE_ROUTE_ONLY only on the steps that end
+    // a routing interval
+    const int j = st->steps[layer];
+    const int score_now = !(g.flags & QEVICT_F_SCORE_ROUTE_ONLY) || (j + 1) % g.omega == 0;
+    HIP_TRY(launch_finish(g, st->bf, layer, out, score_now, hs));
     st->steps[layer] += 1;
     return QEVICT_OK;
 }
@@ -442,6 +452,7 @@ qevict_status qevict_export_unit(qevict_state* st, int32_t layer, int32_t b, voi
     if (bytes < st->lay.export_bytes) return fail(QEVICT_E_CAPACITY, "export buffer < %zu bytes", st->lay.export_bytes);
     const Geo& g = st->lay.g;
     const int64_t u = unit_of(g, b, layer);
+    HIP_TRY(launch_flush_mass(g, st->bf, layer, b, (hipStream_t)stream));
     HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
     UnitHdr hdr;
     std::vector<WinRec> win(g.n_windows);

@@ -64,7 +64,8 @@ struct UnitHdr {
     int32_t ctr[8];
     int32_t pad0;
     double sink_mass;     // prefill: head-averaged attention mass on the sink prefix
-    int32_t pad[10];      // 128 bytes in all
+    int32_t mass_pending; // 1: the last decode step's window-mass shares are not yet in score[]
+    int32_t pad[9];       // 128 bytes in all
 };
 static_assert(sizeof(UnitHdr) == 128, "UnitHdr layout");
 
@@ -99,6 +100,8 @@ struct Bufs {
     uint16_t* pages;        // [U][n_pages][h_kv][2][W][d]   bf16
     uint8_t* slots;         // [U][n_slots][h_kv][slot_head_bytes]
     uint16_t* sinks;        // [U][h_kv] pages of Ws tokens (same layout as a window page)
+    int32_t* done;          // [U][h_kv + 1] decode completion counters (zero between launches)
+    float* mass_part;       // [U][n_acc_max][h_q] per-head share of each entry's mass (last decode step)
 };
 
 __host__ __device__ inline int64_t unit_of(const Geo& g, int b, int l) { return (int64_t)b * g.L + l; }
@@ -153,10 +156,10 @@ __host__ __device__ inline int sink_width(int n_sink) { return n_sink <= 16 ? 16
 // ---------------------------------------------------------------- launchers (host side)
 hipError_t launch_init(const Geo& g, const Bufs& bf, const int32_t* prompt_lens_dev, const int32_t* kf_dev,
                        const int32_t* kq_dev, hipStream_t s);
-hipError_t launch_append(const Geo& g, const Bufs& bf, int layer, const uint16_t* k, const uint16_t* v, hipStream_t s);
-hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t* q, hipStream_t s);
-hipError_t launch_combine(const Geo& g, const Bufs& bf, int layer, float* out, hipStream_t s);
-hipError_t launch_mass(const Geo& g, const Bufs& bf, int layer, hipStream_t s);
+hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t* q, const uint16_t* k_new,
+                         const uint16_t* v_new, hipStream_t s);
+hipError_t launch_finish(const Geo& g, const Bufs& bf, int layer, float* out, int score_now, hipStream_t s);
+hipError_t launch_flush_mass(const Geo& g, const Bufs& bf, int layer, int b, hipStream_t s);
 hipError_t launch_route(const Geo& g, const Bufs& bf, int layer, int mode, hipStream_t s);
 hipError_t launch_force_targets(const Geo& g, const Bufs& bf, int layer, const int32_t* win_ids, int n, int target,
                                 hipStream_t s);

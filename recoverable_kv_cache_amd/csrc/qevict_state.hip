@@ -1,4 +1,4 @@
-// State kernels: arena initialisation, token append, prefill setup, the
+// State kernels: arena initialisation, prefill setup, the
 // window router (candidate pool + two-stage TopK + migration bookkeeping +
 // chronological compaction) and the INT2 pack / dequantize-promote kernels.
 //
@@ -7,6 +7,7 @@
 // Quantization", Eqs. 4-6), Appendix A Algorithm 1.
 #include "qevict_common.h"
 #include "qevict_internal.h"
+#include "qevict_mass.h"
 
 namespace qv {
 
@@ -31,52 +32,12 @@ __global__ void k_init(Geo g, Bufs bf, const int32_t* plens, const int32_t* kf, 
         bf.target[u * g.n_windows + w] = 0;
     }
     for (int s = threadIdx.x; s <= g.n_splits; s += blockDim.x) bf.splits[u * (g.n_splits + 1) + s] = 0;
+    for (int h = threadIdx.x; h <= g.h_kv; h += blockDim.x) bf.done[u * (g.h_kv + 1) + h] = 0;
 }
 
 hipError_t launch_init(const Geo& g, const Bufs& bf, const int32_t* plens, const int32_t* kf, const int32_t* kq,
                        hipStream_t s) {
     hipLaunchKernelGGL(k_init, dim3(g.B * g.L), dim3(256), 0, s, g, bf, plens, kf, kq);
-    return hipGetLastError();
-}
-
-// ------------------------------------------------------------------------------------ append
-// Writes the new token's K/V (bf16) at position n into the sink prefix or the
-// page of its (recent-region) window, then advances n.
-__global__ void k_append(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v) {
-    const int b = blockIdx.x;
-    const int64_t u = unit_of(g, b, layer);
-    UnitHdr* hdr = bf.hdr + u;
-    const int p = hdr->n;
-    uint16_t* blk;
-    int Wp, i;
-    if (p < g.n_sink) {
-        blk = bf.sinks + u * g.sink_elems;
-        Wp = sink_width(g.n_sink);
-        i = p;
-    } else {
-        const int w = (p - g.n_sink) / g.W;
-        i = (p - g.n_sink) % g.W;
-        const WinRec rec = w < g.n_windows ? bf.win[u * g.n_windows + w] : WinRec{ST_NONE, -1, -1, 0};
-        if (rec.state != ST_LOCAL || rec.page < 0) {
-            if (threadIdx.x == 0) atomicOr(&hdr->status, QEVICT_DEV_E_WINDOW);
-            return;
-        }
-        blk = bf.pages + u * (int64_t)g.n_pages * g.page_elems + (int64_t)rec.page * g.page_elems;
-        Wp = g.W;
-    }
-    const int n_el = g.h_kv * g.d;
-    for (int e = threadIdx.x; e < n_el; e += blockDim.x) {
-        const int h = e / g.d, c = e % g.d;
-        uint16_t* kh = blk + (int64_t)(2 * h) * Wp * g.d;
-        kh[lay_k(i, c, g.d, Wp)] = k[(int64_t)b * n_el + e];
-        kh[(int64_t)Wp * g.d + lay_v(i, c, g.d, Wp)] = v[(int64_t)b * n_el + e];
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) hdr->n = p + 1;
-}
-
-hipError_t launch_append(const Geo& g, const Bufs& bf, int layer, const uint16_t* k, const uint16_t* v, hipStream_t s) {
-    hipLaunchKernelGGL(k_append, dim3(g.B), dim3(256), 0, s, g, bf, layer, k, v);
     return hipGetLastError();
 }
 
@@ -106,6 +67,7 @@ __global__ void k_prefill_setup(Geo g, Bufs bf, int layer, const uint16_t* __res
     if (threadIdx.x == 0) {
         hdr->n = S;
         hdr->n_win = n_win;
+        hdr->mass_pending = 0;
     }
 }
 
@@ -206,6 +168,13 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     const int NW = g.n_windows;
     int* flag = (int*)sm.key;                // scratch aliasing the (not yet used) key array
     int* flag2 = flag + RT_MAXW;
+
+    // ---- 0. the last decode step's window-mass shares enter the scores first
+    if (hdr->mass_pending) {
+        apply_mass_range(g, bf, u, tid, hdr->n_acc, RT_THREADS);
+        __syncthreads();
+        if (tid == 0) hdr->mass_pending = 0;
+    }
 
     // ---- 1. candidate pool (Eq. 4): previous Full ∪ previous Quantized ∪ aged recent windows
     for (int w = tid; w < RT_MAXW; w += RT_THREADS) {
