@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E peak, GB/s
+TIME_EVERY = 8           # per-kernel timing on every 8th timed step
 METRIC = "decode-attn tokens/s + achieved HBM GB/s (% peak) at 32K ctx; route µs/event"
 
 
@@ -38,7 +39,7 @@ def log(*a):
 
 def source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("qevict_decode.hip", "qevict_common.h", "qevict_internal.h"):
+    for f in ("qevict_decode.hip", "qevict_common.h", "qevict_internal.h", "qevict_mass.h"):
         h.update(open(os.path.join(ROOT, "recoverable_kv_cache_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -173,9 +174,11 @@ def main():
     torch.cuda.synchronize()
     kv0 = [st.step_bytes(l) for l in range(wl.n_layers)]
 
-    # ---- timed region: wall-clock events around all steps, events around every
-    # split-K kernel and around every routing event
-    kev = [[(new_event(), new_event()) for _ in range(wl.n_layers)] for _ in range(args.steps)]
+    # ---- timed region: wall-clock events around all steps; the split-K kernels of every
+    # TIME_EVERY-th step carry events stamped by their own dispatch (start / end), and
+    # every routing event is bracketed by events
+    timed_steps = [i for i in range(args.steps) if i % TIME_EVERY == (i // TIME_EVERY) % TIME_EVERY]
+    kev = {i: [(new_event(), new_event()) for _ in range(wl.n_layers)] for i in timed_steps}
     rev = [(new_event(), new_event()) for _ in range(args.steps // wl.omega + 1)]
     start, stop = new_event(), new_event()
     torch.cuda.synchronize()
@@ -183,13 +186,13 @@ def main():
     n_route = 0
     for i in range(args.steps):
         j = args.warmup + i
-        if run_step(j, timing=kev[i], route_ev=rev[n_route]):
+        if run_step(j, timing=kev.get(i), route_ev=rev[n_route]):
             n_route += 1
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     route_ms = [rev[r][0].elapsed_time(rev[r][1]) for r in range(n_route)]
-    kern_ms = [kev[i][l][0].elapsed_time(kev[i][l][1]) for i in range(args.steps) for l in range(wl.n_layers)]
+    kern_ms = [kev[i][l][0].elapsed_time(kev[i][l][1]) for i in timed_steps for l in range(wl.n_layers)]
     kv1 = [st.step_bytes(l) for l in range(wl.n_layers)]
     status = st.poll_status()
     assert status == 0, f"device status {status}"

@@ -71,7 +71,7 @@ typedef struct {
     int32_t max_prompt;   /* S_max: prompt buffers are [..][S_max][d] */
     int32_t max_new;      /* N_g: generated tokens; B_total covers prompt_len + max_new */
     uint32_t flags;       /* QEVICT_F_* */
-    int32_t n_splits;     /* decode splits per (sequence, KV head); 0 = choose; capped at 512 / (h_q / h_kv) */
+    int32_t n_splits;     /* decode splits per (sequence, KV head); 0 = choose; capped at 512 */
 } qevict_config;
 
 typedef struct {
@@ -202,15 +202,18 @@ qevict_status qevict_poll_status(qevict_state* st, uint32_t* status, void* strea
 qevict_status qevict_export_unit(qevict_state* st, int32_t layer, int32_t b, void* host_buf,
                                  size_t bytes, size_t* written, void* stream);
 
-/* Profiling aid: the next qevict_decode_attn call records ev_before (a
- * hipEvent_t) on its stream right before the split-K attention kernel and
- * ev_after right after it; then both are forgotten.  NULL disables. */
+/* Profiling aid: the next qevict_decode_attn call launches its split-K
+ * attention kernel so that its own dispatch stamps ev_before (a hipEvent_t
+ * created with timing) at the kernel's start and ev_after at its end; then
+ * both are forgotten.  Both or neither must be given; NULL disables. */
 qevict_status qevict_time_next_decode(qevict_state* st, void* ev_before, void* ev_after);
 
 /* Bytes the next decode step of `layer` must move, summed over the batch
  * [host outputs]: kv_bytes = bf16 K/V of the sink, recent and Full tokens
  * (4 * h_kv * d per token) + whole INT2 slots of Quantized windows (codes and
- * fp16 parameters); io_bytes = q in (bf16), o out (fp32), k/v in (bf16).  Syncs. */
+ * fp16 parameters) + 32 B per accessible-list entry (the entry and the fp64
+ * window score read and written); io_bytes = q in (bf16), o out (fp32), k/v in
+ * (bf16).  Syncs. */
 qevict_status qevict_step_bytes(qevict_state* st, int32_t layer, int64_t* kv_bytes, int64_t* io_bytes,
                                 void* stream);
 

@@ -260,7 +260,8 @@ class QEvictState:
         _check(self.lib.qevict_promote(self.handle, layer, _ptr(win_ids), win_ids.shape[-1], _stream(stream)))
 
     def time_next_decode(self, ev_before, ev_after):
-        """Record torch.cuda.Event pair around the split-K kernel of the next decode_attn."""
+        """Have the next decode_attn stamp a torch.cuda.Event pair (timing enabled, already recorded once)
+        at the start and the end of its split-K attention kernel."""
         _check(self.lib.qevict_time_next_decode(self.handle, ctypes.c_void_p(ev_before.cuda_event),
                                                 ctypes.c_void_p(ev_after.cuda_event)))
 

@@ -22,6 +22,7 @@
 // so one wave job covers two INT2 windows at once and the softmax arithmetic of
 // both runs in the same instructions.
 #include <float.h>
+#include <hip/hip_ext.h>
 
 #include "qevict_common.h"
 #include "qevict_internal.h"
@@ -611,12 +612,33 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
                 j = jn;
             }
         }
+        // the previous step's pending window-mass shares of this batch's entries: each
+        // entry once, by the KV head whose index matches its position in the split; the
+        // window ids come from LDS, so the shares and the score load in one round trip
+        if (pending && wave == DW - 1) {
+            const int x0 = (hk - bs % g.h_kv + g.h_kv) % g.h_kv;     // position bs + x0 = hk (mod h_kv)
+            for (int x = x0 + g.h_kv * lane; x < ne; x += 64 * g.h_kv) {
+                const int win = ent[x].win;
+                if (win < 0) continue;
+                const float* row = bf.mass_part + (u * g.n_acc_max + e0 + x) * (int64_t)g.h_q;
+                double* sc = bf.score + u * g.n_windows + win;
+                const double s0 = *sc;
+                double sm = 0.0;
+                if ((g.h_q & 3) == 0) {
+                    for (int h = 0; h < g.h_q; h += 4) {
+                        const f4_t v = *reinterpret_cast<const f4_t*>(row + h);
+                        sm += (double)v[0];
+                        sm += (double)v[1];
+                        sm += (double)v[2];
+                        sm += (double)v[3];
+                    }
+                } else {
+                    for (int h = 0; h < g.h_q; ++h) sm += (double)row[h];
+                }
+                *sc = s0 + sm / g.h_q;
+            }
+        }
     }
-
-    // ---- the previous step's pending window-mass shares of this split's entries
-    //      (each entry once: the KV head whose index matches its position in the split)
-    if (pending && wave == DW - 1)
-        apply_mass_range(g, bf, u, e_begin + hk + g.h_kv * lane, e_begin + e_total, 64 * g.h_kv);
 
     // ---- wave state -> workgroup partial for this split
     float lt = l_run;
@@ -673,12 +695,16 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
 }
 
 hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t* q, const uint16_t* k_new,
-                         const uint16_t* v_new, hipStream_t s) {
+                         const uint16_t* v_new, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const dim3 grid(g.n_splits, g.h_kv, g.B), block(64 * DW);
     const int G = g.h_q / g.h_kv, TPC = lay_tpc(g.W);
 #define QV_DEC(D_, G_, T_)                                                                     \
     if (g.d == D_ && G == G_ && TPC == T_) {                                                   \
-        hipLaunchKernelGGL((k_decode_split<D_, G_, T_>), grid, block, 0, s, g, bf, layer, q, k_new, v_new); \
+        if (ev0)                                                                               \
+            hipExtLaunchKernelGGL((k_decode_split<D_, G_, T_>), grid, block, 0, s, ev0, ev1, 0, g, bf, layer, q, \
+                                  k_new, v_new);                                               \
+        else                                                                                   \
+            hipLaunchKernelGGL((k_decode_split<D_, G_, T_>), grid, block, 0, s, g, bf, layer, q, k_new, v_new); \
         return hipGetLastError();                                                              \
     }
     QV_DEC(128, 1, 2) QV_DEC(128, 2, 2) QV_DEC(128, 4, 2) QV_DEC(128, 8, 2)

@@ -98,7 +98,7 @@ struct Layout {
 };
 
 enum { O_HDR, O_WIN, O_SCORE, O_ACC, O_SPLITS, O_FPAGE, O_FSLOT, O_PACK, O_FILL, O_TARGET, O_LSEW, O_LSEG,
-       O_PML, O_PACC, O_PAGES, O_SLOTS, O_SINKS, O_PLENS, O_KF, O_KQ, O_DONE, O_MPART, O_COUNT };
+       O_PML, O_PACC, O_PAGES, O_SLOTS, O_SINKS, O_PLENS, O_KF, O_KQ, O_MPART, O_COUNT };
 
 qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, Layout* lay) {
     qevict_status s = validate(c);
@@ -134,9 +134,8 @@ qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, La
         if (ns > cap) ns = cap;
         if (ns < 1) ns = 1;
     }
-    // the decode kernel's split combiner stages (m, l) of every (split, query head of a
-    // KV group) in LDS: at most 512 of them
-    const int32_t ns_max = 512 / (c->h_q / c->h_kv);
+    // the finish kernel stages (m, l) of every split of a head in LDS: at most 512
+    const int32_t ns_max = 512;
     if (ns > ns_max) ns = ns_max;
     g.n_splits = ns;
     g.page_elems = g.h_kv * 2 * g.W * g.d;
@@ -163,7 +162,6 @@ qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, La
     sz[O_SLOTS] = U * g.n_slots * (size_t)g.slot_bytes;
     sz[O_SINKS] = U * (size_t)g.sink_elems * 2;
     sz[O_PLENS] = sz[O_KF] = sz[O_KQ] = g.B * sizeof(int32_t);
-    sz[O_DONE] = U * (g.h_kv + 1) * sizeof(int32_t);
     sz[O_MPART] = U * (size_t)g.n_acc_max * g.h_q * sizeof(float);
     size_t at = 0;
     for (int i = 0; i < O_COUNT; ++i) {
@@ -198,7 +196,6 @@ Bufs bind_bufs(const Layout& lay, void* arena) {
     b.pages = (uint16_t*)(a + lay.off[O_PAGES]);
     b.slots = (uint8_t*)(a + lay.off[O_SLOTS]);
     b.sinks = (uint16_t*)(a + lay.off[O_SINKS]);
-    b.done = (int32_t*)(a + lay.off[O_DONE]);
     b.mass_part = (float*)(a + lay.off[O_MPART]);
     return b;
 }
@@ -348,9 +345,8 @@ qevict_status qevict_decode_attn(qevict_state* st, int32_t layer, const void* q,
         return fail(QEVICT_E_CAPACITY, "layer %d already decoded max_new = %d tokens", layer, st->cfg.max_new);
     hipStream_t hs = (hipStream_t)stream;
     const Geo& g = st->lay.g;
-    if (st->ev_before) HIP_TRY(hipEventRecord(st->ev_before, hs));
-    HIP_TRY(launch_decode(g, st->bf, layer, (const uint16_t*)q, (const uint16_t*)k_new, (const uint16_t*)v_new, hs));
-    if (st->ev_after) HIP_TRY(hipEventRecord(st->ev_after, hs));
+    HIP_TRY(launch_decode(g, st->bf, layer, (const uint16_t*)q, (const uint16_t*)k_new, (const uint16_t*)v_new, hs,
+                          st->ev_before, st->ev_after));
     st->ev_before = st->ev_after = nullptr;
     // Eq. 1 accumulates every step; with QEVICT_F_SCORE_ROUTE_ONLY only on the steps that end
     // a routing interval
@@ -363,6 +359,7 @@ qevict_status qevict_decode_attn(qevict_state* st, int32_t layer, const void* q,
 
 qevict_status qevict_time_next_decode(qevict_state* st, void* ev_before, void* ev_after) {
     if (!st) return fail(QEVICT_E_INVALID, "null state");
+    if ((ev_before == nullptr) != (ev_after == nullptr)) return fail(QEVICT_E_INVALID, "give both events or neither");
     st->ev_before = (hipEvent_t)ev_before;
     st->ev_after = (hipEvent_t)ev_after;
     return QEVICT_OK;
@@ -391,6 +388,7 @@ qevict_status qevict_step_bytes(qevict_state* st, int32_t layer, int64_t* kv_byt
             if (win[w].state == ST_LOCAL || win[w].state == ST_FULL) kv += (int64_t)ntok * tok;
             else if (win[w].state == ST_QUANT) kv += g.slot_bytes;
         }
+        kv += 32LL * hdr.n_acc;    // accessible-list entry (16 B) + window score read and write (fp64)
     }
     *kv_bytes = kv;
     *io_bytes = (int64_t)g.B * g.h_q * g.d * (2 + 4) + 2LL * g.B * g.h_kv * g.d * 2;   // q in, o out, k/v in

@@ -100,7 +100,6 @@ struct Bufs {
     uint16_t* pages;        // [U][n_pages][h_kv][2][W][d]   bf16
     uint8_t* slots;         // [U][n_slots][h_kv][slot_head_bytes]
     uint16_t* sinks;        // [U][h_kv] pages of Ws tokens (same layout as a window page)
-    int32_t* done;          // [U][h_kv + 1] decode completion counters (zero between launches)
     float* mass_part;       // [U][n_acc_max][h_q] per-head share of each entry's mass (last decode step)
 };
 
@@ -156,8 +155,9 @@ __host__ __device__ inline int sink_width(int n_sink) { return n_sink <= 16 ? 16
 // ---------------------------------------------------------------- launchers (host side)
 hipError_t launch_init(const Geo& g, const Bufs& bf, const int32_t* prompt_lens_dev, const int32_t* kf_dev,
                        const int32_t* kq_dev, hipStream_t s);
+// ev0 / ev1 (optional): events stamped by the split kernel's own dispatch at its start and end
 hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t* q, const uint16_t* k_new,
-                         const uint16_t* v_new, hipStream_t s);
+                         const uint16_t* v_new, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_finish(const Geo& g, const Bufs& bf, int layer, float* out, int score_now, hipStream_t s);
 hipError_t launch_flush_mass(const Geo& g, const Bufs& bf, int layer, int b, hipStream_t s);
 hipError_t launch_route(const Geo& g, const Bufs& bf, int layer, int mode, hipStream_t s);

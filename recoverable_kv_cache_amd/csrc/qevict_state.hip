@@ -32,7 +32,6 @@ __global__ void k_init(Geo g, Bufs bf, const int32_t* plens, const int32_t* kf, 
         bf.target[u * g.n_windows + w] = 0;
     }
     for (int s = threadIdx.x; s <= g.n_splits; s += blockDim.x) bf.splits[u * (g.n_splits + 1) + s] = 0;
-    for (int h = threadIdx.x; h <= g.h_kv; h += blockDim.x) bf.done[u * (g.h_kv + 1) + h] = 0;
 }
 
 hipError_t launch_init(const Geo& g, const Bufs& bf, const int32_t* plens, const int32_t* kf, const int32_t* kq,
