@@ -32,6 +32,7 @@ namespace qv {
 
 constexpr int DW = 4;          // waves per workgroup
 constexpr int DMAXE = 256;     // accessible entries of one split, staged in LDS per batch
+static_assert(DMAXE == 64 * DW, "one staged entry per thread");
 constexpr float M_INIT = -1e30f;   // running max before any token (finite: exp2(-inf - M_INIT) = 0)
 
 typedef short s4_t __attribute__((ext_vector_type(4)));
@@ -75,6 +76,40 @@ __device__ __forceinline__ float mirror(float x) {
 __device__ __forceinline__ float ror8(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
 }
+// Reductions over the 4 lane groups of a column (lanes l, l^16, l^32, l^48) with the
+// gfx950 row-swap permutes: permlane16_swap(x, x) hands every lane the values of rows
+// 2k and 2k+1 at its position, permlane32_swap(x, x) those of both 32-lane halves.  Both
+// lanes of a pair add in the same order, so the result is identical across the group.
+__device__ __forceinline__ float qg_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+__device__ __forceinline__ float qg_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+// sum over aligned groups of N consecutive lanes (N = 8, 16, 32 or 64) with DPP quad
+// swaps, the half-row / row mirrors and the row swaps: no LDS traffic
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+    if constexpr (N >= 8) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
+    if constexpr (N >= 16) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));
+    if constexpr (N >= 32) {
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    }
+    if constexpr (N >= 64) {
+        const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+    }
+    return x;
+}
 // LDS traffic between lanes of one wave: the wave's LDS operations execute in
 // order, so only the compiler has to be kept from reordering them
 __device__ __forceinline__ void wave_lds_fence() {
@@ -82,6 +117,8 @@ __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+
+__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }   // by value
 
 template <int N>
 __device__ __forceinline__ void ldw(uint32_t* d, const void* s) {
@@ -146,6 +183,7 @@ struct DecShape {
 // (entries ia, ib), one per column slot.  bf16 job: tile t of one sink / page entry.
 struct Job {
     int type;           // 0 none, 1 INT2, 2 bf16
+    int k;              // index in the batch's INT2-pair / bf16-entry job table
     int ia, ib, c;      // INT2: batch-local entry indices (ib = -1: slot 1 empty), chunk
     int sa, sb;         // INT2: slot ids
     int i, t, kind, idx, ntok, Wn, start;   // bf16: entry, tile, kind, page id, valid tokens, block width, position 0
@@ -160,6 +198,8 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     constexpr int NV = S::NV, QSTR = S::QSTR;
     __shared__ uint2 lut[256];
     __shared__ AccEntry ent[DMAXE];
+    __shared__ uint8_t jq[DMAXE], jf[DMAXE];   // job tables: INT2 entries, bf16 entries with tokens
+    __shared__ int s_cnt[DW][2];
     __shared__ __attribute__((aligned(16))) uint16_t qs[DW][16][QSTR];   // per wave: INT2 query operand rows
     __shared__ __attribute__((aligned(16))) uint16_t qb[16][QSTR];       // bf16 query operand rows
     __shared__ float kb[DW][16];                                         // per wave: key-offset bias per column
@@ -253,75 +293,65 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     int e0 = e_begin, ne = 0;
 
     // ---- job sequence of this wave: INT2 windows in pairs (chunk by chunk), then bf16 tiles
-    auto rfl = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
-    auto ent_q = [&](int i) -> int {                 // first INT2 entry at or after i (stride DW)
-        for (; i < ne; i += DW)
-            if (rfl(ent[i].kind) == EK_SLOT && rfl(ent[i].idx) >= 0) return i;
-        return -1;
-    };
-    auto ent_f = [&](int i) -> Job {                 // first bf16 tile job at or after entry i
+    auto rfl = [](int x) __attribute__((always_inline)) { return __builtin_amdgcn_readfirstlane(x); };
+    int nq = 0, nf = 0, npair = 0;   // this batch: INT2 entries, bf16 entries with tokens, INT2 pair jobs
+    auto make_q = [&](int k) __attribute__((always_inline)) -> Job {            // INT2 job k: entries jq[NSLOT k .. NSLOT k + NSLOT)
         Job j;
-        j.type = 0;
-        for (; i < ne; i += DW) {
-            const int kind = rfl(ent[i].kind), idx = rfl(ent[i].idx), start = rfl(ent[i].start);
-            if (kind == EK_SLOT) continue;
-            const int nt = kind == EK_SINK ? min(g.n_sink, n_tok) : min(W, n_tok - start);
-            if (nt <= 0 || (kind != EK_SINK && idx < 0)) {
-                if (lane < G) lse_out[(int64_t)(e0 + i) * g.h_q + lane] = -INFINITY;   // no tokens yet: no mass
-                continue;
-            }
-            j.type = 2;
-            j.i = i;
-            j.t = 0;
-            j.kind = kind;
-            j.idx = idx;
-            j.ntok = nt;
-            j.Wn = kind == EK_SINK ? Ws : W;
-            j.start = kind == EK_SINK ? 0 : start;
-            return j;
+        j.k = k;
+        j.c = 0;
+        if (k < npair) {
+            j.type = 1;
+            j.ia = rfl(jq[NSLOT * k]);
+            j.ib = (NSLOT == 2 && NSLOT * k + 1 < nq) ? rfl(jq[NSLOT * k + 1]) : -1;
+            j.sa = rfl(ent[j.ia].idx);
+            j.sb = j.ib >= 0 ? rfl(ent[j.ib].idx) : j.sa;
+        } else {
+            j.type = 0;                          // tail prefetch of slot 0: valid, unused
+            j.ia = j.ib = -1;
+            j.sa = j.sb = 0;
         }
         return j;
     };
-    auto make_q = [&](int i) -> Job {
-        Job j;
-        j.type = 1;
-        j.ia = i;
-        j.c = 0;
-        j.sa = rfl(ent[i].idx);
-        j.ib = NSLOT == 2 ? ent_q(i + DW) : -1;
-        j.sb = j.ib >= 0 ? rfl(ent[j.ib].idx) : j.sa;
-        return j;
-    };
-    auto first_q = [&]() -> Job {
-        const int i = ent_q(wave);
-        if (i >= 0) return make_q(i);
-        Job j;
-        j.type = 0;
-        j.ia = j.ib = -1;
-        j.c = 0;
-        j.sa = j.sb = 0;
-        return j;
-    };
-    auto next_q = [&](Job j) -> Job {
+    auto next_q = [&](Job j) __attribute__((always_inline)) -> Job {
         if (j.c + 1 < NCH) {
             j.c += 1;
             return j;
         }
-        const int i = (NSLOT == 2 && j.ib < 0) ? -1 : ent_q((NSLOT == 2 ? j.ib : j.ia) + DW);
-        if (i >= 0) return make_q(i);
-        j.type = 0;
-        j.c = 0;
-        return j;   // keeps valid slot ids: the tail prefetch reads them harmlessly
+        return make_q(j.k + DW);
     };
-    auto next_f = [&](Job j) -> Job {
+    auto make_f = [&](int k) __attribute__((always_inline)) -> Job {            // bf16 job k: all tiles of entry jf[k], in order
+        Job j;
+        j.k = k;
+        j.t = 0;
+        if (k < nf) {
+            const int i = rfl(jf[k]);
+            const int kind = rfl(ent[i].kind), start = rfl(ent[i].start);
+            j.type = 2;
+            j.i = i;
+            j.kind = kind;
+            j.idx = rfl(ent[i].idx);
+            // (geometry read from the kernel argument, not from captured locals: a select
+            // between two captured locals would become a select between stack addresses)
+            j.ntok = kind == EK_SINK ? imin(g.n_sink, n_tok) : imin(g.W, n_tok - start);
+            j.Wn = kind == EK_SINK ? sink_width(g.n_sink) : g.W;
+            j.start = kind == EK_SINK ? 0 : start;
+        } else {
+            j.type = 0;                          // tail prefetch of the sink block: valid, unused
+            j.i = 0;
+            j.kind = EK_SINK;
+            j.idx = 0;
+            j.ntok = 0;
+            j.Wn = sink_width(g.n_sink);
+            j.start = 0;
+        }
+        return j;
+    };
+    auto next_f = [&](Job j) __attribute__((always_inline)) -> Job {
         if (16 * (j.t + 1) < j.ntok) {
             j.t += 1;
             return j;
         }
-        const Job k = ent_f(j.i + DW);
-        if (k.type != 0) return k;
-        j.type = 0;
-        return j;   // keeps a valid block: the tail prefetch reads it harmlessly
+        return make_f(j.k + DW);
     };
 
     struct Raw {
@@ -364,8 +394,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     auto softmax = [&](float* s, float* p, int nvv) __attribute__((always_inline)) {
         float mx = s[0];
         for (int v = 1; v < nvv; ++v) mx = fmaxf(mx, s[v]);
-        mx = fmaxf(mx, xor_lane<16>(mx));
-        mx = fmaxf(mx, xor_lane<32>(mx));
+        mx = qg_max(mx);
         const float mnew = fmaxf(m_run, mx);
         if (__any(mnew > m_run)) {
             const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
@@ -394,9 +423,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         return u2_t{a.x, a.y};
     };
     auto lse_store = [&](bool mine, int ie) {
-        float t = lw;
-        t += xor_lane<16>(t);
-        t += xor_lane<32>(t);
+        const float t = qg_sum(lw);
         if (mine) {
             if (qg == 0 && hi) lse_out[(int64_t)(e0 + ie) * g.h_q + head] = m_run + log2f(t);
             lw = 0.f;
@@ -421,7 +448,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
                 hw[x] = bf16x2_trunc(x0, x1);
                 lw2[x] = bf16x2_rne(x0 - bf16lo(hw[x]), x1 - bf16hi(hw[x]));
             }
-            bias = lanes_sum<1, LPR>(bias);
+            bias = group_sum<LPR>(bias);
             wave_lds_fence();
             stw<CPL / 2>(&qs[wave][pitem * SW + phead][CPL * pcb], hw);
             stw<CPL / 2>(&qs[wave][pitem * SW + SW - 1 - phead][CPL * pcb], lw2);
@@ -568,12 +595,50 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     for (int bs = 0; bs < e_total; bs += DMAXE) {
         __syncthreads();
         e0 = e_begin + bs;
-        ne = min(DMAXE, e_total - bs);
+        ne = imin(DMAXE, e_total - bs);
         for (int x = threadIdx.x; x < ne; x += 64 * DW) ent[x] = bf.acc[u * g.n_acc_max + e0 + x];
         __syncthreads();
+        // job tables: INT2 entries (paired in order, one pair per job) and bf16 entries
+        // holding tokens; entries without tokens yet get window log-sum-exp -inf (no mass)
+        {
+            const int x = threadIdx.x;           // DMAXE == 64 * DW: one entry per thread
+            bool isq = false, isf = false;
+            if (x < ne) {
+                const AccEntry en = ent[x];
+                if (en.kind == EK_SLOT) {
+                    isq = en.idx >= 0;
+                } else {
+                    const int nt = en.kind == EK_SINK ? imin(g.n_sink, n_tok) : imin(W, n_tok - en.start);
+                    isf = nt > 0 && (en.kind == EK_SINK || en.idx >= 0);
+                    if (!isf)
+                        for (int h = 0; h < G; ++h) lse_out[(int64_t)(e0 + x) * g.h_q + h] = -INFINITY;
+                }
+            }
+            const uint64_t mq = __ballot(isq), mf = __ballot(isf);
+            const int rq = __builtin_amdgcn_mbcnt_hi((uint32_t)(mq >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mq, 0));
+            const int rf = __builtin_amdgcn_mbcnt_hi((uint32_t)(mf >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mf, 0));
+            if (lane == 0) {
+                s_cnt[wave][0] = __popcll(mq);
+                s_cnt[wave][1] = __popcll(mf);
+            }
+            __syncthreads();
+            int oq = 0, of = 0;
+            nq = nf = 0;
+#pragma unroll
+            for (int w = 0; w < DW; ++w) {
+                oq += w < wave ? s_cnt[w][0] : 0;
+                of += w < wave ? s_cnt[w][1] : 0;
+                nq += s_cnt[w][0];
+                nf += s_cnt[w][1];
+            }
+            if (isq) jq[oq + rq] = (uint8_t)x;
+            if (isf) jf[of + rf] = (uint8_t)x;
+            npair = (nq + NSLOT - 1) / NSLOT;
+            __syncthreads();
+        }
         {   // unrolled by two so that the two buffers swap roles without copies
             Raw ra, rb;
-            Job j = first_q();
+            Job j = make_q(wave);
             load_q(j, ra);
             while (j.type != 0) {
                 Job jn = next_q(j);
@@ -589,16 +654,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         }
         {
             Raw ra, rb;
-            Job j = ent_f(wave);
-            if (j.type == 0) {
-                j.kind = EK_SINK;
-                j.idx = 0;
-                j.t = 0;
-                j.Wn = Ws;
-                j.ntok = 0;
-                j.i = 0;
-                j.start = 0;
-            }
+            Job j = make_f(((wave - npair) % DW + DW) % DW);   // bf16 jobs continue the round robin
             load_f(j, ra);
             while (j.type != 0) {
                 Job jn = next_f(j);
@@ -641,12 +697,8 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     }
 
     // ---- wave state -> workgroup partial for this split
-    float lt = l_run;
-    lt += xor_lane<16>(lt);
-    lt += xor_lane<32>(lt);
-    float vb = vbias;
-    vb += xor_lane<16>(vb);
-    vb += xor_lane<32>(vb);
+    float lt = qg_sum(l_run);
+    const float vb = qg_sum(vbias);
     float a[MB][4];
 #pragma unroll
     for (int m = 0; m < MB; ++m)
