@@ -31,8 +31,6 @@
 namespace qv {
 
 constexpr int DW = 4;          // waves per workgroup
-constexpr int DMAXE = 256;     // accessible entries of one split, staged in LDS per batch
-static_assert(DMAXE == 64 * DW, "one staged entry per thread");
 constexpr float M_INIT = -1e30f;   // running max before any token (finite: exp2(-inf - M_INIT) = 0)
 
 typedef short s4_t __attribute__((ext_vector_type(4)));
@@ -196,17 +194,14 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     using S = DecShape<D, G, TPC>;
     constexpr int CQ = S::CQ, KS = S::KS, MB = S::MB, NSLOT = S::NSLOT, SW = S::SW, LPR = S::LPR, CPL = S::CPL;
     constexpr int NV = S::NV, QSTR = S::QSTR;
-    __shared__ uint2 lut[256];
-    __shared__ AccEntry ent[DMAXE];
-    __shared__ uint8_t jq[DMAXE], jf[DMAXE];   // job tables: INT2 entries, bf16 entries with tokens
-    __shared__ int s_cnt[DW][2];
-    __shared__ __attribute__((aligned(16))) uint16_t qs[DW][16][QSTR];   // per wave: INT2 query operand rows
-    __shared__ __attribute__((aligned(16))) uint16_t qb[16][QSTR];       // bf16 query operand rows
+    __shared__ uint2 lut[256];                                           // code byte -> 4 bf16 {0..3}
+    // per wave: rows 0-15 the INT2 query operand of the current job, rows 16-31 the
+    // bf16 query operand (every live column holds its head's query, exact bf16)
+    __shared__ __attribute__((aligned(16))) uint16_t qs[DW][32][QSTR];
     __shared__ float kb[DW][16];                                         // per wave: key-offset bias per column
-    __shared__ __attribute__((aligned(16))) float qfl[64][CPL];          // q of each lane's product channels
     __shared__ float s_m[DW][G], s_l[DW][G];
     __shared__ float s_acc[DW][G][D];
-    __shared__ __attribute__((aligned(16))) uint16_t nkv[2][D];         // the new token's K and V of this KV head
+    __shared__ __attribute__((aligned(16))) uint16_t nkv[DW][2][D];     // per wave: the new token's K and V
 
     const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
     const int64_t u = unit_of(g, b, layer);
@@ -223,25 +218,43 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     // product assignment: row (item pitem, head phead), channels [CPL*pcb, CPL*pcb + CPL)
     const int prow = lane / LPR, pitem = prow / G, phead = prow % G, pcb = lane % LPR;
 
-    const int32_t* splits = bf.splits + u * (g.n_splits + 1);
-    const int e_begin = splits[split], e_total = splits[split + 1] - e_begin;
+    // ---- prologue: one round trip brings the split block (header + first entries, one
+    // per lane), the unit header and the queries; each wave stages its own operands.
+    AccEntry me = bf.split_blk[(u * g.n_splits + split) * SPLIT_BLOCK + lane];
     const int n_old = bf.hdr[u].n;       // tokens before this step; the new one sits at position n_old
     const int pending = bf.hdr[u].mass_pending;
     const int n_tok = n_old + 1;
     const uint16_t* qhead = qin + ((int64_t)b * g.h_q + hk * G) * D;
-    // 4 packed 2-bit codes -> 4 bf16 {0, 1, 2, 3}
-    for (int x = threadIdx.x; x < 256; x += 64 * DW) {
-        auto bv = [](int c) -> uint32_t { return c == 0 ? 0u : (c == 1 ? 0x3F80u : (c == 2 ? 0x4000u : 0x4040u)); };
-        lut[x] = make_uint2(bv(x & 3) | (bv((x >> 2) & 3) << 16), bv((x >> 4) & 3) | (bv((x >> 6) & 3) << 16));
+    float qf[CPL];                                       // q of the lane's product channels, fp32
+    {
+        uint32_t w[CQ / 2];
+        ldw<CQ / 2>(w, qhead + head * D + CQ * qg);
+        uint32_t w2[CPL / 2];
+        ldw<CPL / 2>(w2, qhead + phead * D + CPL * pcb);
+        uint32_t kn = 0, vn = 0;
+        if (lane < D / 2) {
+            kn = reinterpret_cast<const uint32_t*>(knew + ((int64_t)b * g.h_kv + hk) * D)[lane];
+            vn = reinterpret_cast<const uint32_t*>(vnew + ((int64_t)b * g.h_kv + hk) * D)[lane];
+        }
+        // 4 packed 2-bit codes -> 4 bf16 {0, 1, 2, 3}: one table at a fixed LDS address, so a
+        // lookup is one shift of the code byte with the base in the read's immediate offset
+        for (int x = threadIdx.x; x < 256; x += 64 * DW) {
+            auto bv = [](int c) -> uint32_t { return c == 0 ? 0u : (c == 1 ? 0x3F80u : (c == 2 ? 0x4000u : 0x4040u)); };
+            lut[x] = make_uint2(bv(x & 3) | (bv((x >> 2) & 3) << 16), bv((x >> 4) & 3) | (bv((x >> 6) & 3) << 16));
+        }
+        stw<CQ / 2>(&qs[wave][16 + n][CQ * qg], w);
+#pragma unroll
+        for (int x = 0; x < CPL / 2; ++x) {
+            qf[2 * x] = bf16lo(w2[x]);
+            qf[2 * x + 1] = bf16hi(w2[x]);
+        }
+        if (lane < D / 2) {
+            reinterpret_cast<uint32_t*>(nkv[wave][0])[lane] = kn;
+            reinterpret_cast<uint32_t*>(nkv[wave][1])[lane] = vn;
+        }
     }
-    // the new token: staged in LDS for the wave that attends its tile, and written
-    // into its sink / recent-window block by the first split of each KV head
-    if (wave == 1 && lane < D / 2) {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(knew + ((int64_t)b * g.h_kv + hk) * D);
-        const uint32_t* srv = reinterpret_cast<const uint32_t*>(vnew + ((int64_t)b * g.h_kv + hk) * D);
-        reinterpret_cast<uint32_t*>(nkv[0])[lane] = src[lane];
-        reinterpret_cast<uint32_t*>(nkv[1])[lane] = srv[lane];
-    }
+    // the new token goes into its sink / recent-window block (first split of each KV
+    // head); the wave that attends its tile takes it from LDS instead
     if (split == 0 && wave >= 2) {
         uint16_t* blk = nullptr;
         int Wp = W, i = 0;
@@ -266,20 +279,9 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             }
         }
     }
-    // bf16 windows: every live column holds its head's query (exact bf16);
-    // INT2 windows: each lane's product channels of q, as fp32
-    if (wave == 0) {
-        uint32_t w[CQ / 2];
-        ldw<CQ / 2>(w, qhead + head * D + CQ * qg);
-        stw<CQ / 2>(&qb[n][CQ * qg], w);
-        uint32_t w2[CPL / 2];
-        ldw<CPL / 2>(w2, qhead + phead * D + CPL * pcb);
-#pragma unroll
-        for (int x = 0; x < CPL / 2; ++x) {
-            qfl[lane][2 * x] = bf16lo(w2[x]);
-            qfl[lane][2 * x + 1] = bf16hi(w2[x]);
-        }
-    }
+    __syncthreads();                 // the code table (the only state the waves share)
+    const int e_total = __builtin_amdgcn_readlane(me.kind, 0);   // header: entries of the split, first entry
+    const int e_begin = __builtin_amdgcn_readlane(me.idx, 0);
 
     float m_run = M_INIT, l_run = 0.f, lw = 0.f, vbias = 0.f;
     f4_t acc[MB];
@@ -290,21 +292,30 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     const uint8_t* slots = bf.slots + u * (int64_t)g.n_slots * g.slot_bytes + (int64_t)hk * g.slot_head_bytes;
     const uint16_t* sinks = bf.sinks + u * g.sink_elems;
     float* lse_out = bf.lse_win + u * (int64_t)g.n_acc_max * g.h_q + hk * G;
-    int e0 = e_begin, ne = 0;
 
-    // ---- job sequence of this wave: INT2 windows in pairs (chunk by chunk), then bf16 tiles
-    auto rfl = [](int x) __attribute__((always_inline)) { return __builtin_amdgcn_readfirstlane(x); };
-    int nq = 0, nf = 0, npair = 0;   // this batch: INT2 entries, bf16 entries with tokens, INT2 pair jobs
-    auto make_q = [&](int k) __attribute__((always_inline)) -> Job {            // INT2 job k: entries jq[NSLOT k .. NSLOT k + NSLOT)
+    // ---- job sequence of this wave.  A batch is up to SPLIT_BLOCK - 1 entries, one per
+    // lane 1..63.  INT2 entries are paired in order (one pair per job, chunk by chunk),
+    // bf16 entries holding tokens follow (all tiles of an entry in one job); jobs go to
+    // the waves round robin.  The r-th INT2 (bf16) entry is found by a ballot.
+    int xb = 0;                      // split position of lane 1 in the current batch
+    bool isq = false, isf = false;   // this lane's entry: INT2 / bf16 with tokens
+    int rq = 0, rf = 0;              // rank among the batch's INT2 / bf16 entries
+    int nq = 0, nf = 0, npair = 0;
+    auto lane_of = [&](bool sel, int rank, int r) __attribute__((always_inline)) -> int {
+        return (int)__builtin_ctzll(__ballot(sel && rank == r));
+    };
+    auto make_q = [&](int k) __attribute__((always_inline)) -> Job {   // INT2 job k: the batch's INT2 entries NSLOT k, NSLOT k + 1
         Job j;
         j.k = k;
         j.c = 0;
         if (k < npair) {
+            const int la = lane_of(isq, rq, NSLOT * k);
+            const int lb = (NSLOT == 2 && NSLOT * k + 1 < nq) ? lane_of(isq, rq, NSLOT * k + 1) : -1;
             j.type = 1;
-            j.ia = rfl(jq[NSLOT * k]);
-            j.ib = (NSLOT == 2 && NSLOT * k + 1 < nq) ? rfl(jq[NSLOT * k + 1]) : -1;
-            j.sa = rfl(ent[j.ia].idx);
-            j.sb = j.ib >= 0 ? rfl(ent[j.ib].idx) : j.sa;
+            j.sa = __builtin_amdgcn_readlane(me.idx, la);
+            j.sb = lb >= 0 ? __builtin_amdgcn_readlane(me.idx, lb) : j.sa;
+            j.ia = e_begin + xb + la - 1;                       // accessible-list indices
+            j.ib = lb >= 0 ? e_begin + xb + lb - 1 : -1;
         } else {
             j.type = 0;                          // tail prefetch of slot 0: valid, unused
             j.ia = j.ib = -1;
@@ -319,17 +330,17 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         }
         return make_q(j.k + DW);
     };
-    auto make_f = [&](int k) __attribute__((always_inline)) -> Job {            // bf16 job k: all tiles of entry jf[k], in order
+    auto make_f = [&](int k) __attribute__((always_inline)) -> Job {   // bf16 job k: all tiles of the k-th bf16 entry
         Job j;
         j.k = k;
         j.t = 0;
         if (k < nf) {
-            const int i = rfl(jf[k]);
-            const int kind = rfl(ent[i].kind), start = rfl(ent[i].start);
+            const int L = lane_of(isf, rf, k);
+            const int kind = __builtin_amdgcn_readlane(me.kind, L), start = __builtin_amdgcn_readlane(me.start, L);
             j.type = 2;
-            j.i = i;
+            j.i = e_begin + xb + L - 1;
             j.kind = kind;
-            j.idx = rfl(ent[i].idx);
+            j.idx = __builtin_amdgcn_readlane(me.idx, L);
             // (geometry read from the kernel argument, not from captured locals: a select
             // between two captured locals would become a select between stack addresses)
             j.ntok = kind == EK_SINK ? imin(g.n_sink, n_tok) : imin(g.W, n_tok - start);
@@ -357,37 +368,39 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     struct Raw {
         uint32_t w[S::RW];
     };
+    // Every load address is a wave-uniform base (SGPRs) plus an unsigned 32-bit lane
+    // offset, which the hardware adds itself (global loads with an SGPR base).
+    const uint32_t kc_lane = (uint32_t)((n * 4 + qg) * TPC * (CQ / 4));           // K codes: token row n, group qg
+    const uint32_t vc_lane = (uint32_t)(W * D / 4 + (n * 4 + qg) * NCH * MB * TPC); // V codes: channel row n
+    const uint32_t vp_lane = (uint32_t)(W * D / 2 + 4 * D + qg * NT * 8);         // V offsets (V scales + 2W)
+    const uint32_t kp_lane = (uint32_t)(W * D / 2 + CPL * pcb * 2);               // K offsets (K scales + 2D)
     auto load_q = [&](const Job& j, Raw& R) __attribute__((always_inline)) {
-        {
-            const uint8_t* sa = slots + (int64_t)j.sa * g.slot_bytes;
-            const uint8_t* sb = slots + (int64_t)j.sb * g.slot_bytes;
-            const int kco = ((j.c * 16 + n) * 4 + qg) * TPC * (CQ / 4);        // K codes: token row n, channel group qg
-            const int vco = W * D / 4 + (((n * 4 + qg) * NCH + j.c) * MB) * TPC;   // V codes: channel row n, tokens of qg
-            ldw<S::KCW>(R.w, sa + kco);
-            ldw<S::VCW>(R.w + S::O_VC, sa + vco);
-            if constexpr (NSLOT == 2) {
-                ldw<S::KCW>(R.w + S::KCW, sb + kco);
-                ldw<S::VCW>(R.w + S::O_VC + S::VCW, sb + vco);
-            }
-            const uint8_t* so = slot == 0 ? sa : sb;                 // the lane's own item
-            const uint16_t* offV = reinterpret_cast<const uint16_t*>(so + W * D / 2) + 2 * D;
-            ldw<S::VPW>(R.w + S::O_VO, offV + (qg * NT + TPC * j.c) * 4);
-            ldw<S::VPW>(R.w + S::O_VS, offV + W + (qg * NT + TPC * j.c) * 4);
-            const uint8_t* sp = pitem == 0 ? sa : sb;                // the item of the lane's products
-            const uint16_t* offK = reinterpret_cast<const uint16_t*>(sp + W * D / 2);
-            ldw<S::KPW>(R.w + S::O_KS, offK + D + CPL * pcb);
-            ldw<S::KPW>(R.w + S::O_KO, offK + CPL * pcb);
+        const uint32_t oa = (uint32_t)j.sa * (uint32_t)g.slot_bytes, ob = (uint32_t)j.sb * (uint32_t)g.slot_bytes;
+        const uint8_t* ca = slots + oa + (uint32_t)(j.c * 16 * 4 * TPC * (CQ / 4));   // chunk c of item a
+        const uint8_t* cb = slots + ob + (uint32_t)(j.c * 16 * 4 * TPC * (CQ / 4));
+        ldw<S::KCW>(R.w, ca + kc_lane);
+        ldw<S::VCW>(R.w + S::O_VC, slots + oa + (uint32_t)(j.c * MB * TPC) + vc_lane);
+        if constexpr (NSLOT == 2) {
+            ldw<S::KCW>(R.w + S::KCW, cb + kc_lane);
+            ldw<S::VCW>(R.w + S::O_VC + S::VCW, slots + ob + (uint32_t)(j.c * MB * TPC) + vc_lane);
         }
+        // the lane's own item (V parameters) and the item of its products (K parameters)
+        const uint32_t oo = (slot == 0 ? oa : ob) + vp_lane + (uint32_t)(TPC * j.c * 8);
+        ldw<S::VPW>(R.w + S::O_VO, slots + oo);
+        ldw<S::VPW>(R.w + S::O_VS, slots + oo + 2 * W);
+        const uint32_t op = (pitem == 0 ? oa : ob) + kp_lane;
+        ldw<S::KPW>(R.w + S::O_KS, slots + op + 2 * D);
+        ldw<S::KPW>(R.w + S::O_KO, slots + op);
     };
     auto load_f = [&](const Job& j, Raw& R) __attribute__((always_inline)) {
-        {
-            const int tpc = lay_tpc(j.Wn), nt16 = j.Wn / 16;
-            const uint16_t* kbase = (j.kind == EK_SINK ? sinks : pages + (int64_t)j.idx * g.page_elems) +
-                                    (int64_t)(2 * hk) * j.Wn * D;
-            const uint16_t* vbase = kbase + (int64_t)j.Wn * D;
-            ldw<CQ / 2>(R.w, kbase + ((((j.t / tpc) * 16 + n) * 4 + qg) * tpc + j.t % tpc) * CQ);
-            ldw<2 * MB>(R.w + CQ / 2, vbase + (((n * 4 + qg) * nt16 + j.t) * MB) * 4);
-        }
+        const int tpc = lay_tpc(j.Wn), nt16 = j.Wn / 16;
+        const uint8_t* kbase = reinterpret_cast<const uint8_t*>(
+            (j.kind == EK_SINK ? sinks : pages + (int64_t)j.idx * g.page_elems) + (int64_t)(2 * hk) * j.Wn * D);
+        const uint8_t* vbase = kbase + (int64_t)j.Wn * D * 2;
+        const int t0 = j.t / tpc, t1 = j.t % tpc;   // chunk, tile within it
+        ldw<CQ / 2>(R.w, kbase + (uint32_t)(t0 * 16 * 4 * tpc * CQ * 2 + t1 * CQ * 2) +
+                             (uint32_t)(((n * 4 + qg) * tpc) * CQ * 2));
+        ldw<2 * MB>(R.w + CQ / 2, vbase + (uint32_t)(j.t * MB * 8) + (uint32_t)((n * 4 + qg) * nt16 * MB * 8));
     };
 
     // online softmax over the lane's NVV scores (per column: max over the 4 lane groups)
@@ -425,7 +438,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     auto lse_store = [&](bool mine, int ie) {
         const float t = qg_sum(lw);
         if (mine) {
-            if (qg == 0 && hi) lse_out[(int64_t)(e0 + ie) * g.h_q + head] = m_run + log2f(t);
+            if (qg == 0 && hi) lse_out[(int64_t)ie * g.h_q + head] = m_run + log2f(t);
             lw = 0.f;
         }
     };
@@ -436,9 +449,6 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         {
             float bias = 0.f;
             uint32_t hw[CPL / 2], lw2[CPL / 2];
-            float qf[CPL];
-#pragma unroll
-            for (int x = 0; x < CPL; x += 4) *reinterpret_cast<f4_t*>(&qf[x]) = *reinterpret_cast<const f4_t*>(&qfl[lane][x]);
 #pragma unroll
             for (int x = 0; x < CPL / 2; ++x) {
                 const f2_t s2 = h2f(R.w[S::O_KS + x]), o2 = h2f(R.w[S::O_KO + x]);
@@ -551,7 +561,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     auto process_f = [&](const Job& j, const Raw& R) __attribute__((always_inline)) {
         u4_t bq[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bq[ks] = *reinterpret_cast<const u4_t*>(&qb[n][CQ * qg + 8 * ks]);
+        for (int ks = 0; ks < KS; ++ks) bq[ks] = *reinterpret_cast<const u4_t*>(&qs[wave][16 + n][CQ * qg + 8 * ks]);
         uint32_t kw[CQ / 2], vw[2 * MB];
 #pragma unroll
         for (int x = 0; x < CQ / 2; ++x) kw[x] = R.w[x];
@@ -562,12 +572,12 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             // its K row (lanes of token row pt) and its V column entries come from LDS
             if (n == pt) {
 #pragma unroll
-                for (int x = 0; x < CQ / 2; ++x) kw[x] = reinterpret_cast<const uint32_t*>(&nkv[0][CQ * qg])[x];
+                for (int x = 0; x < CQ / 2; ++x) kw[x] = reinterpret_cast<const uint32_t*>(&nkv[wave][0][CQ * qg])[x];
             }
             if (qg == (pt >> 2)) {
 #pragma unroll
                 for (int m = 0; m < MB; ++m) {
-                    const uint32_t v = nkv[1][16 * m + n];
+                    const uint32_t v = nkv[wave][1][16 * m + n];
                     const int x = 2 * m + ((pt & 3) >> 1);
                     vw[x] = (pt & 1) ? ((vw[x] & 0xFFFFu) | (v << 16)) : ((vw[x] & 0xFFFF0000u) | v);
                 }
@@ -589,53 +599,29 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         if (16 * (j.t + 1) >= j.ntok) lse_store(slot == 0, j.i);
     };
 
-    // entries are staged in LDS in batches; each wave runs two passes (INT2 pairs,
-    // then bf16 tiles), each a two-deep software pipeline in which the next job's
-    // loads are in flight while a job is processed
-    for (int bs = 0; bs < e_total; bs += DMAXE) {
-        __syncthreads();
-        e0 = e_begin + bs;
-        ne = imin(DMAXE, e_total - bs);
-        for (int x = threadIdx.x; x < ne; x += 64 * DW) ent[x] = bf.acc[u * g.n_acc_max + e0 + x];
-        __syncthreads();
-        // job tables: INT2 entries (paired in order, one pair per job) and bf16 entries
-        // holding tokens; entries without tokens yet get window log-sum-exp -inf (no mass)
-        {
-            const int x = threadIdx.x;           // DMAXE == 64 * DW: one entry per thread
-            bool isq = false, isf = false;
-            if (x < ne) {
-                const AccEntry en = ent[x];
-                if (en.kind == EK_SLOT) {
-                    isq = en.idx >= 0;
-                } else {
-                    const int nt = en.kind == EK_SINK ? imin(g.n_sink, n_tok) : imin(W, n_tok - en.start);
-                    isf = nt > 0 && (en.kind == EK_SINK || en.idx >= 0);
-                    if (!isf)
-                        for (int h = 0; h < G; ++h) lse_out[(int64_t)(e0 + x) * g.h_q + h] = -INFINITY;
-                }
+    // batches of up to SPLIT_BLOCK - 1 entries: the first from the split block, later
+    // ones (splits longer than a block) straight from the accessible list
+    for (xb = 0; xb == 0 || xb < e_total; xb += SPLIT_BLOCK - 1) {
+        const int x = xb + lane - 1;                     // this lane's position in the split
+        const bool valid = lane >= 1 && x < e_total;
+        if (xb > 0 && valid) me = bf.acc[u * g.n_acc_max + e_begin + x];
+        isq = isf = false;
+        if (valid) {
+            if (me.kind == EK_SLOT) {
+                isq = me.idx >= 0;
+            } else {
+                const int nt = me.kind == EK_SINK ? imin(g.n_sink, n_tok) : imin(W, n_tok - me.start);
+                isf = nt > 0 && (me.kind == EK_SINK || me.idx >= 0);
+                if (!isf && wave == 0)           // no tokens yet: window log-sum-exp -inf, no mass
+                    for (int h = 0; h < G; ++h) lse_out[(int64_t)(e_begin + x) * g.h_q + h] = -INFINITY;
             }
-            const uint64_t mq = __ballot(isq), mf = __ballot(isf);
-            const int rq = __builtin_amdgcn_mbcnt_hi((uint32_t)(mq >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mq, 0));
-            const int rf = __builtin_amdgcn_mbcnt_hi((uint32_t)(mf >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mf, 0));
-            if (lane == 0) {
-                s_cnt[wave][0] = __popcll(mq);
-                s_cnt[wave][1] = __popcll(mf);
-            }
-            __syncthreads();
-            int oq = 0, of = 0;
-            nq = nf = 0;
-#pragma unroll
-            for (int w = 0; w < DW; ++w) {
-                oq += w < wave ? s_cnt[w][0] : 0;
-                of += w < wave ? s_cnt[w][1] : 0;
-                nq += s_cnt[w][0];
-                nf += s_cnt[w][1];
-            }
-            if (isq) jq[oq + rq] = (uint8_t)x;
-            if (isf) jf[of + rf] = (uint8_t)x;
-            npair = (nq + NSLOT - 1) / NSLOT;
-            __syncthreads();
         }
+        const uint64_t mq = __ballot(isq), mf = __ballot(isf);
+        rq = __builtin_amdgcn_mbcnt_hi((uint32_t)(mq >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mq, 0));
+        rf = __builtin_amdgcn_mbcnt_hi((uint32_t)(mf >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mf, 0));
+        nq = __popcll(mq);
+        nf = __popcll(mf);
+        npair = (nq + NSLOT - 1) / NSLOT;
         {   // unrolled by two so that the two buffers swap roles without copies
             Raw ra, rb;
             Job j = make_q(wave);
@@ -669,30 +655,24 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             }
         }
         // the previous step's pending window-mass shares of this batch's entries: each
-        // entry once, by the KV head whose index matches its position in the split; the
-        // window ids come from LDS, so the shares and the score load in one round trip
-        if (pending && wave == DW - 1) {
-            const int x0 = (hk - bs % g.h_kv + g.h_kv) % g.h_kv;     // position bs + x0 = hk (mod h_kv)
-            for (int x = x0 + g.h_kv * lane; x < ne; x += 64 * g.h_kv) {
-                const int win = ent[x].win;
-                if (win < 0) continue;
-                const float* row = bf.mass_part + (u * g.n_acc_max + e0 + x) * (int64_t)g.h_q;
-                double* sc = bf.score + u * g.n_windows + win;
-                const double s0 = *sc;
-                double sm = 0.0;
-                if ((g.h_q & 3) == 0) {
-                    for (int h = 0; h < g.h_q; h += 4) {
-                        const f4_t v = *reinterpret_cast<const f4_t*>(row + h);
-                        sm += (double)v[0];
-                        sm += (double)v[1];
-                        sm += (double)v[2];
-                        sm += (double)v[3];
-                    }
-                } else {
-                    for (int h = 0; h < g.h_q; ++h) sm += (double)row[h];
+        // entry once, by the KV head whose index matches its position in the split
+        if (pending && wave == DW - 1 && valid && x % g.h_kv == hk && me.win >= 0) {
+            const float* row = bf.mass_part + (u * g.n_acc_max + e_begin + x) * (int64_t)g.h_q;
+            double* sc = bf.score + u * g.n_windows + me.win;
+            const double s0 = *sc;
+            double sm = 0.0;
+            if ((g.h_q & 3) == 0) {
+                for (int h = 0; h < g.h_q; h += 4) {
+                    const f4_t v = *reinterpret_cast<const f4_t*>(row + h);
+                    sm += (double)v[0];
+                    sm += (double)v[1];
+                    sm += (double)v[2];
+                    sm += (double)v[3];
                 }
-                *sc = s0 + sm / g.h_q;
+            } else {
+                for (int h = 0; h < g.h_q; ++h) sm += (double)row[h];
             }
+            *sc = s0 + sm / g.h_q;
         }
     }
 

@@ -98,7 +98,7 @@ struct Layout {
 };
 
 enum { O_HDR, O_WIN, O_SCORE, O_ACC, O_SPLITS, O_FPAGE, O_FSLOT, O_PACK, O_FILL, O_TARGET, O_LSEW, O_LSEG,
-       O_PML, O_PACC, O_PAGES, O_SLOTS, O_SINKS, O_PLENS, O_KF, O_KQ, O_MPART, O_COUNT };
+       O_PML, O_PACC, O_PAGES, O_SLOTS, O_SINKS, O_PLENS, O_KF, O_KQ, O_MPART, O_SBLK, O_COUNT };
 
 qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, Layout* lay) {
     qevict_status s = validate(c);
@@ -163,6 +163,7 @@ qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, La
     sz[O_SINKS] = U * (size_t)g.sink_elems * 2;
     sz[O_PLENS] = sz[O_KF] = sz[O_KQ] = g.B * sizeof(int32_t);
     sz[O_MPART] = U * (size_t)g.n_acc_max * g.h_q * sizeof(float);
+    sz[O_SBLK] = U * (size_t)g.n_splits * SPLIT_BLOCK * sizeof(AccEntry);
     size_t at = 0;
     for (int i = 0; i < O_COUNT; ++i) {
         lay->off[i] = at;
@@ -197,6 +198,7 @@ Bufs bind_bufs(const Layout& lay, void* arena) {
     b.slots = (uint8_t*)(a + lay.off[O_SLOTS]);
     b.sinks = (uint16_t*)(a + lay.off[O_SINKS]);
     b.mass_part = (float*)(a + lay.off[O_MPART]);
+    b.split_blk = (AccEntry*)(a + lay.off[O_SBLK]);
     return b;
 }
 

@@ -88,6 +88,7 @@ struct Bufs {
     double* score;          // [U][n_windows]
     AccEntry* acc;          // [U][n_acc_max]
     int32_t* splits;        // [U][n_splits + 1]
+    AccEntry* split_blk;    // [U][n_splits][SPLIT_BLOCK]: {entries, first entry, -1, 0}, then the split's entries
     int32_t* free_pages;    // [U][n_pages]
     int32_t* free_slots;    // [U][n_slots]
     PackItem* pack;         // [U][n_windows]
@@ -104,6 +105,10 @@ struct Bufs {
 };
 
 __host__ __device__ inline int64_t unit_of(const Geo& g, int b, int l) { return (int64_t)b * g.L + l; }
+
+// Each split's header and first SPLIT_BLOCK - 1 accessible-list entries, copied by the
+// router to a fixed place so that a decode wave gets them in one load (one per lane).
+constexpr int SPLIT_BLOCK = 64;
 
 // ------------------------------------------------------------------ in-HBM layouts
 // The decode kernel feeds MFMA tiles straight from HBM, so pages and

@@ -508,6 +508,19 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         }
         splits[s] = pos;
     }
+    __syncthreads();
+    // split blocks: header {entries, first entry, -1, 0} and the first SPLIT_BLOCK - 1 entries
+    {
+        AccEntry* sblk = bf.split_blk + u * g.n_splits * SPLIT_BLOCK;
+        for (int i = tid; i < g.n_splits * SPLIT_BLOCK; i += RT_THREADS) {
+            const int s = i / SPLIT_BLOCK, x = i % SPLIT_BLOCK;
+            const int e0 = splits[s], cnt = splits[s + 1] - e0;
+            AccEntry v = AccEntry{EK_PAGE, -1, -1, 0};
+            if (x == 0) v = AccEntry{cnt, e0, -1, 0};
+            else if (x - 1 < cnt) v = acc[e0 + x - 1];
+            sblk[i] = v;
+        }
+    }
     if (tid == 0) {
         hdr->n_acc = n_acc;
         int nwin = 0;
