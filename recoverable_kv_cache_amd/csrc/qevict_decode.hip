@@ -253,32 +253,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             reinterpret_cast<uint32_t*>(nkv[wave][1])[lane] = vn;
         }
     }
-    // the new token goes into its sink / recent-window block (first split of each KV
-    // head); the wave that attends its tile takes it from LDS instead
-    if (split == 0 && wave >= 2) {
-        uint16_t* blk = nullptr;
-        int Wp = W, i = 0;
-        if (n_old < g.n_sink) {
-            blk = bf.sinks + u * g.sink_elems;
-            Wp = Ws;
-            i = n_old;
-        } else {
-            const int w = (n_old - g.n_sink) / W;
-            i = (n_old - g.n_sink) % W;
-            const WinRec rec = w < g.n_windows ? bf.win[u * g.n_windows + w] : WinRec{ST_NONE, -1, -1, 0};
-            if (rec.state == ST_LOCAL && rec.page >= 0)
-                blk = bf.pages + u * (int64_t)g.n_pages * g.page_elems + (int64_t)rec.page * g.page_elems;
-            else if (threadIdx.x == 128)
-                atomicOr(&bf.hdr[u].status, QEVICT_DEV_E_WINDOW);
-        }
-        if (blk) {
-            uint16_t* kh = blk + (int64_t)(2 * hk) * Wp * D;
-            for (int c = threadIdx.x - 128; c < D; c += 128) {
-                kh[lay_k(i, c, D, Wp)] = knew[((int64_t)b * g.h_kv + hk) * D + c];
-                kh[(int64_t)Wp * D + lay_v(i, c, D, Wp)] = vnew[((int64_t)b * g.h_kv + hk) * D + c];
-            }
-        }
-    }
+    if (split == 0 && hk == 0 && threadIdx.x == 0) bf.hdr[u].pos = n_old;   // for the finish kernel
     __syncthreads();                 // the code table (the only state the waves share)
     const int e_total = __builtin_amdgcn_readlane(me.kind, 0);   // header: entries of the split, first entry
     const int e_begin = __builtin_amdgcn_readlane(me.idx, 0);
@@ -759,7 +734,8 @@ constexpr int FN_MAXE = 16;             // entries per thread: n_acc_max <= 4096
 
 template <int D>
 __global__ void __launch_bounds__(FN_THREADS) k_finish(Geo g, Bufs bf, int layer, float* __restrict__ out,
-                                                       int score_now) {
+                                                       const uint16_t* __restrict__ knew,
+                                                       const uint16_t* __restrict__ vnew, int score_now) {
     constexpr int C4 = D / 4, PH = FN_THREADS / C4;    // float4 columns, split phases
     __shared__ float ws[FN_MAXS], ls[FN_MAXS];
     __shared__ f4_t part[FN_THREADS];
@@ -834,24 +810,50 @@ __global__ void __launch_bounds__(FN_THREADS) k_finish(Geo g, Bufs bf, int layer
             if (e < n_acc) mp[(int64_t)e * g.h_q] = __builtin_amdgcn_exp2f(lwv[k] - lse);
         }
     }
-    if (h == 0 && tid == 0) {
+    // the step's token goes into its sink / recent-window block (one workgroup per KV
+    // head: the first query head of the group); the split kernel read it from its inputs
+    const int G = g.h_q / g.h_kv;
+    if (h % G == 0) {
+        const int hk = h / G;
         UnitHdr* hdr = bf.hdr + u;
-        const int n_old = hdr->n;
+        const int n_old = hdr->pos;      // n is advanced below by head 0's workgroup: not read here
+        uint16_t* blk = nullptr;
+        int Wp = g.W, i = 0;
         bool ok = true;
-        if (n_old >= g.n_sink) {
+        if (n_old < g.n_sink) {
+            blk = bf.sinks + u * g.sink_elems;
+            Wp = sink_width(g.n_sink);
+            i = n_old;
+        } else {
             const int w = (n_old - g.n_sink) / g.W;
-            ok = w < g.n_windows && bf.win[u * g.n_windows + w].state == ST_LOCAL && bf.win[u * g.n_windows + w].page >= 0;
+            i = (n_old - g.n_sink) % g.W;
+            const WinRec rec = w < g.n_windows ? bf.win[u * g.n_windows + w] : WinRec{ST_NONE, -1, -1, 0};
+            ok = rec.state == ST_LOCAL && rec.page >= 0;
+            if (ok) blk = bf.pages + u * (int64_t)g.n_pages * g.page_elems + (int64_t)rec.page * g.page_elems;
         }
-        if (ok) hdr->n = n_old + 1;
-        hdr->mass_pending = score_now;
+        if (blk) {
+            uint16_t* kh = blk + (int64_t)(2 * hk) * Wp * D;
+            for (int c = tid; c < D; c += FN_THREADS) {
+                kh[lay_k(i, c, D, Wp)] = knew[((int64_t)b * g.h_kv + hk) * D + c];
+                kh[(int64_t)Wp * D + lay_v(i, c, D, Wp)] = vnew[((int64_t)b * g.h_kv + hk) * D + c];
+            }
+        }
+        if (tid == 0) {
+            if (!ok) atomicOr(&hdr->status, QEVICT_DEV_E_WINDOW);
+            if (h == 0) {
+                if (ok) hdr->n = n_old + 1;
+                hdr->mass_pending = score_now;
+            }
+        }
     }
 }
 
-hipError_t launch_finish(const Geo& g, const Bufs& bf, int layer, float* out, int score_now, hipStream_t s) {
+hipError_t launch_finish(const Geo& g, const Bufs& bf, int layer, float* out, const uint16_t* k_new,
+                         const uint16_t* v_new, int score_now, hipStream_t s) {
     if (g.n_splits > FN_MAXS || g.n_acc_max > 1 + FN_THREADS * FN_MAXE) return hipErrorInvalidValue;
     const dim3 grid(g.h_q, g.B), block(FN_THREADS);
-    if (g.d == 128) hipLaunchKernelGGL(k_finish<128>, grid, block, 0, s, g, bf, layer, out, score_now);
-    else if (g.d == 64) hipLaunchKernelGGL(k_finish<64>, grid, block, 0, s, g, bf, layer, out, score_now);
+    if (g.d == 128) hipLaunchKernelGGL(k_finish<128>, grid, block, 0, s, g, bf, layer, out, k_new, v_new, score_now);
+    else if (g.d == 64) hipLaunchKernelGGL(k_finish<64>, grid, block, 0, s, g, bf, layer, out, k_new, v_new, score_now);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

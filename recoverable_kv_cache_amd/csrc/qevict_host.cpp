@@ -354,7 +354,7 @@ qevict_status qevict_decode_attn(qevict_state* st, int32_t layer, const void* q,
     // a routing interval
     const int j = st->steps[layer];
     const int score_now = !(g.flags & QEVICT_F_SCORE_ROUTE_ONLY) || (j + 1) % g.omega == 0;
-    HIP_TRY(launch_finish(g, st->bf, layer, out, score_now, hs));
+    HIP_TRY(launch_finish(g, st->bf, layer, out, (const uint16_t*)k_new, (const uint16_t*)v_new, score_now, hs));
     st->steps[layer] += 1;
     return QEVICT_OK;
 }

@@ -65,7 +65,8 @@ struct UnitHdr {
     int32_t pad0;
     double sink_mass;     // prefill: head-averaged attention mass on the sink prefix
     int32_t mass_pending; // 1: the last decode step's window-mass shares are not yet in score[]
-    int32_t pad[9];       // 128 bytes in all
+    int32_t pos;          // decode: position of the step's token (written by the split kernel)
+    int32_t pad[8];       // 128 bytes in all
 };
 static_assert(sizeof(UnitHdr) == 128, "UnitHdr layout");
 
@@ -163,7 +164,8 @@ hipError_t launch_init(const Geo& g, const Bufs& bf, const int32_t* prompt_lens_
 // ev0 / ev1 (optional): events stamped by the split kernel's own dispatch at its start and end
 hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t* q, const uint16_t* k_new,
                          const uint16_t* v_new, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
-hipError_t launch_finish(const Geo& g, const Bufs& bf, int layer, float* out, int score_now, hipStream_t s);
+hipError_t launch_finish(const Geo& g, const Bufs& bf, int layer, float* out, const uint16_t* k_new,
+                         const uint16_t* v_new, int score_now, hipStream_t s);
 hipError_t launch_flush_mass(const Geo& g, const Bufs& bf, int layer, int b, hipStream_t s);
 hipError_t launch_route(const Geo& g, const Bufs& bf, int layer, int mode, hipStream_t s);
 hipError_t launch_force_targets(const Geo& g, const Bufs& bf, int layer, const int32_t* win_ids, int n, int target,
