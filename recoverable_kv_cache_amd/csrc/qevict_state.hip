@@ -144,14 +144,14 @@ struct RouteSmem {
     int misc[8];
 };
 
-// Work of one accessible entry in the decode kernel, in units of ~1/6 of an INT2
-// window chunk (a bf16 16-token tile costs ~7, half a two-window INT2 job ~6): splits
-// are balanced on this rather than on bytes, since bf16 tiles move 6x the bytes of an
-// INT2 window but take only about twice its time.
+// Bytes one accessible entry makes the decode kernel read per KV head; splits are
+// balanced on them.  (Weighting bf16 pages by their compute time instead, which is
+// only ~2.3x that of an INT2 window against ~6x the bytes, measured slower: with the
+// cache streamed from HBM the page loads dominate.)
 __device__ __forceinline__ int per_head_cost(const Geo& g, int kind) {
-    if (kind == EK_SINK) return 7 * ((g.n_sink + 15) / 16);
-    if (kind == EK_PAGE) return 7 * (g.W / 16);
-    return 6 * (g.W < 32 ? 1 : g.W / 32);
+    if (kind == EK_SINK) return 4 * g.n_sink * g.d;
+    if (kind == EK_PAGE) return 4 * g.W * g.d;
+    return g.slot_head_bytes;
 }
 
 // One workgroup per (sequence, layer).
@@ -452,7 +452,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         if (mode == RM_FORCE_Q || mode == RM_FORCE_F) target[w] = 0;
     }
     __syncthreads();
-    // ---- 8. chronological accessible list (Algorithm 1 step 21) and work-balanced splits
+    // ---- 8. chronological accessible list (Algorithm 1 step 21) and byte-balanced splits
     for (int w = tid; w < RT_MAXW; w += RT_THREADS) {
         const int ns = w < NW ? sm.newst[w] : ST_NONE;
         flag[w] = (ns == ST_LOCAL || ns == ST_FULL || ns == ST_QUANT) ? 1 : 0;
@@ -490,7 +490,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         cost[e] = per_head_cost(g, en.kind);
     }
     __syncthreads();
-    const int total = block_scan_excl(cost, sm.wsum);   // cost[e] = work before entry e
+    const int total = block_scan_excl(cost, sm.wsum);   // cost[e] = bytes before entry e
     int32_t* splits = bf.splits + u * (g.n_splits + 1);
     for (int s = tid; s <= g.n_splits; s += RT_THREADS) {
         int pos;
