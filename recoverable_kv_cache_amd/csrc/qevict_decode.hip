@@ -543,7 +543,12 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
 #pragma unroll
         for (int x = 0; x < 2 * MB; ++x) vw[x] = R.w[CQ / 2 + x];
         const int pt = n_old - j.start - 16 * j.t;    // the new token's row in this tile, if any
-        if (pt >= 0 && pt < 16) {
+        if (pt >= 0 && pt < 16 && n_old - j.start < j.ntok) {   // (a sink block's spare rows never hold it)
+            // its block, for the finish kernel that stores the token (one writer per KV head)
+            if (hk == 0 && lane == 0) {
+                bf.hdr[u].tok_page = j.kind == EK_SINK ? -2 : j.idx;
+                bf.hdr[u].tok_at = n_old;
+            }
             // its K row (lanes of token row pt) and its V column entries come from LDS
             if (n == pt) {
 #pragma unroll
@@ -817,19 +822,19 @@ __global__ void __launch_bounds__(FN_THREADS) k_finish(Geo g, Bufs bf, int layer
         const int hk = h / G;
         UnitHdr* hdr = bf.hdr + u;
         const int n_old = hdr->pos;      // n is advanced below by head 0's workgroup: not read here
+        // the block the split kernel attended the token in: found only when its sink /
+        // recent window was accessible (a window the router did not prepare is an error)
+        const bool ok = hdr->tok_at == n_old;
+        const int page = hdr->tok_page;
         uint16_t* blk = nullptr;
         int Wp = g.W, i = 0;
-        bool ok = true;
-        if (n_old < g.n_sink) {
+        if (ok && page == -2) {
             blk = bf.sinks + u * g.sink_elems;
             Wp = sink_width(g.n_sink);
             i = n_old;
-        } else {
-            const int w = (n_old - g.n_sink) / g.W;
+        } else if (ok) {
             i = (n_old - g.n_sink) % g.W;
-            const WinRec rec = w < g.n_windows ? bf.win[u * g.n_windows + w] : WinRec{ST_NONE, -1, -1, 0};
-            ok = rec.state == ST_LOCAL && rec.page >= 0;
-            if (ok) blk = bf.pages + u * (int64_t)g.n_pages * g.page_elems + (int64_t)rec.page * g.page_elems;
+            blk = bf.pages + u * (int64_t)g.n_pages * g.page_elems + (int64_t)page * g.page_elems;
         }
         if (blk) {
             uint16_t* kh = blk + (int64_t)(2 * hk) * Wp * D;

@@ -66,7 +66,9 @@ struct UnitHdr {
     double sink_mass;     // prefill: head-averaged attention mass on the sink prefix
     int32_t mass_pending; // 1: the last decode step's window-mass shares are not yet in score[]
     int32_t pos;          // decode: position of the step's token (written by the split kernel)
-    int32_t pad[8];       // 128 bytes in all
+    int32_t tok_at;       // decode: position whose block the split kernel found (== pos when found)
+    int32_t tok_page;     // decode: page holding that position (-2: the sink block)
+    int32_t pad[6];       // 128 bytes in all
 };
 static_assert(sizeof(UnitHdr) == 128, "UnitHdr layout");
 

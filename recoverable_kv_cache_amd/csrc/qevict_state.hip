@@ -67,6 +67,7 @@ __global__ void k_prefill_setup(Geo g, Bufs bf, int layer, const uint16_t* __res
         hdr->n = S;
         hdr->n_win = n_win;
         hdr->mass_pending = 0;
+        hdr->tok_at = -1;
     }
 }
 
