@@ -737,19 +737,30 @@ constexpr int FN_THREADS = 256;
 constexpr int FN_MAXS = 512;            // splits (the host caps n_splits below this)
 constexpr int FN_MAXE = 16;             // entries per thread: n_acc_max <= 4096
 
+// sum / max over all 64 lanes without LDS (DPP quad swaps, row mirrors, row swaps); every
+// lane gets the same value
+__device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false)));
+    return qg_max(x);
+}
+
 template <int D>
 __global__ void __launch_bounds__(FN_THREADS) k_finish(Geo g, Bufs bf, int layer, float* __restrict__ out,
                                                        const uint16_t* __restrict__ knew,
                                                        const uint16_t* __restrict__ vnew, int score_now) {
-    constexpr int C4 = D / 4, PH = FN_THREADS / C4;    // float4 columns, split phases
-    __shared__ float ws[FN_MAXS], ls[FN_MAXS];
-    __shared__ f4_t part[FN_THREADS];
-    __shared__ float red[FN_THREADS / 64][2];
+    // each wave owns D/16 float4 columns of the output; its lanes split the splits into
+    // 64/(D/16) phases, summed across lanes at the end.  No LDS, no barrier: every wave
+    // also reduces the split maxima / sums itself, and all loads are issued up front.
+    constexpr int CW = D / 16, PH = 64 / CW;
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t u = unit_of(g, b, layer);
     const int NS = g.n_splits;
     const int n_acc = bf.hdr[u].n_acc;
-    // window log-sum-exps of this head (independent of the combine: loaded first)
+    // window log-sum-exps of this head
     float lwv[FN_MAXE];
     const float* lwin = bf.lse_win + u * (int64_t)g.n_acc_max * g.h_q + h;
 #pragma unroll
@@ -757,53 +768,56 @@ __global__ void __launch_bounds__(FN_THREADS) k_finish(Geo g, Bufs bf, int layer
         const int e = 1 + tid + FN_THREADS * k;
         lwv[k] = (score_now && e < n_acc) ? lwin[(int64_t)e * g.h_q] : -INFINITY;
     }
-    // split statistics and partial numerators
+    // split statistics: all splits for the wave-wide M and L, this lane's phase for the weights
     const float2* ml = bf.part_ml + u * NS * (int64_t)g.h_q + h;
-    float mloc = M_INIT;
-    for (int sp = tid; sp < NS; sp += FN_THREADS) {
-        const float2 v = ml[(int64_t)sp * g.h_q];
-        ws[sp] = v.x;
-        ls[sp] = v.y;
-        mloc = fmaxf(mloc, v.x);
+    float2 mlv[FN_MAXS / 64];
+#pragma unroll
+    for (int k = 0; k < FN_MAXS / 64; ++k) {
+        const int sp = lane + 64 * k;
+        mlv[k] = sp < NS ? ml[(int64_t)sp * g.h_q] : make_float2(M_INIT, 0.f);
     }
-    const int col = tid % C4, ph = tid / C4;
+    const int col = wv * CW + lane % CW, ph = lane / CW;
     const f4_t* pa = reinterpret_cast<const f4_t*>(bf.part_acc + (u * NS * (int64_t)g.h_q + h) * D) + col;
     const int64_t sstride = (int64_t)g.h_q * D / 4;   // float4 per split
-    f4_t x[8];
-    int sp0 = ph;
+    constexpr int NX = 8;            // splits of this lane's phase per batch of loads
+    f4_t x[NX];
+    float mx[NX];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = sp0 + k * PH < NS ? pa[(sp0 + k * PH) * sstride] : f4_t{0.f, 0.f, 0.f, 0.f};
-    // M, weights, L
-    mloc = lanes_max<1, 64>(mloc);
-    if (lane == 0) red[wv][0] = mloc;
-    __syncthreads();
-    float M = red[0][0];
-#pragma unroll
-    for (int w = 1; w < FN_THREADS / 64; ++w) M = fmaxf(M, red[w][0]);
-    float lloc = 0.f;
-    for (int sp = tid; sp < NS; sp += FN_THREADS) {
-        const float f = __builtin_amdgcn_exp2f(ws[sp] - M);
-        ws[sp] = f;
-        lloc += f * ls[sp];
+    for (int k = 0; k < NX; ++k) {
+        const int sp = ph + k * PH;
+        x[k] = sp < NS ? pa[sp * sstride] : f4_t{0.f, 0.f, 0.f, 0.f};
+        mx[k] = sp < NS ? ml[(int64_t)sp * g.h_q].x : M_INIT;
     }
-    lloc = lanes_sum<1, 64>(lloc);
-    if (lane == 0) red[wv][1] = lloc;
-    __syncthreads();
+    float M = M_INIT;
+#pragma unroll
+    for (int k = 0; k < FN_MAXS / 64; ++k) M = fmaxf(M, mlv[k].x);
+    M = wave_max(M);
     float L = 0.f;
 #pragma unroll
-    for (int w = 0; w < FN_THREADS / 64; ++w) L += red[w][1];
+    for (int k = 0; k < FN_MAXS / 64; ++k) L += __builtin_amdgcn_exp2f(mlv[k].x - M) * mlv[k].y;
+    L = wave_sum(L);
     f4_t a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-        if (sp0 + k * PH < NS) a4 += ws[sp0 + k * PH] * x[k];
-    for (int sp = sp0 + 8 * PH; sp < NS; sp += PH) a4 += ws[sp] * pa[sp * sstride];
-    part[tid] = a4;
-    __syncthreads();
-    if (tid < C4) {
-        f4_t o = part[tid];
-        for (int p = 1; p < PH; ++p) o += part[p * C4 + tid];
-        reinterpret_cast<f4_t*>(out + ((int64_t)b * g.h_q + h) * D)[tid] = o / L;
+    for (int k = 0; k < NX; ++k) a4 += __builtin_amdgcn_exp2f(mx[k] - M) * x[k];
+    for (int sp0 = ph + NX * PH; sp0 < NS; sp0 += NX * PH) {      // more splits than one batch
+#pragma unroll
+        for (int k = 0; k < NX; ++k) {
+            const int sp = sp0 + k * PH;
+            x[k] = sp < NS ? pa[sp * sstride] : f4_t{0.f, 0.f, 0.f, 0.f};
+            mx[k] = sp < NS ? ml[(int64_t)sp * g.h_q].x : M_INIT;
+        }
+#pragma unroll
+        for (int k = 0; k < NX; ++k) a4 += __builtin_amdgcn_exp2f(mx[k] - M) * x[k];
     }
+    // sum over the phases: lanes l, l + CW, l + 2 CW, ... (row rotations, then row swaps)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float v = a4[i];
+        if constexpr (CW == 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false));
+        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+        a4[i] = qg_sum(v);
+    }
+    if (ph == 0) reinterpret_cast<f4_t*>(out + ((int64_t)b * g.h_q + h) * D)[col] = a4 / L;
     const float lse = M + log2f(L);
     if (tid == 0) bf.lse_glob[u * g.h_q + h] = lse;
     // this head's share of each entry's window mass (entries without tokens carry -inf)
