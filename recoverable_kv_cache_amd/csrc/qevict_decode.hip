@@ -292,7 +292,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             j.ia = e_begin + xb + la - 1;                       // accessible-list indices
             j.ib = lb >= 0 ? e_begin + xb + lb - 1 : -1;
         } else {
-            j.type = 0;                          // tail prefetch of slot 0: valid, unused
+            j.type = 0;                          // no job left
             j.ia = j.ib = -1;
             j.sa = j.sb = 0;
         }
@@ -322,7 +322,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             j.Wn = kind == EK_SINK ? sink_width(g.n_sink) : g.W;
             j.start = kind == EK_SINK ? 0 : start;
         } else {
-            j.type = 0;                          // tail prefetch of the sink block: valid, unused
+            j.type = 0;                          // no job left
             j.i = 0;
             j.kind = EK_SINK;
             j.idx = 0;
@@ -602,36 +602,22 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         nq = __popcll(mq);
         nf = __popcll(mf);
         npair = (nq + NSLOT - 1) / NSLOT;
-        {   // unrolled by two so that the two buffers swap roles without copies
-            Raw ra, rb;
+        {   // one job in flight per wave: the second wave on each SIMD hides its load latency
+            Raw ra;
             Job j = make_q(wave);
-            load_q(j, ra);
             while (j.type != 0) {
-                Job jn = next_q(j);
-                load_q(jn, rb);
+                load_q(j, ra);
                 process_q(j, ra);
-                j = jn;
-                if (j.type == 0) break;
-                jn = next_q(j);
-                load_q(jn, ra);
-                process_q(j, rb);
-                j = jn;
+                j = next_q(j);
             }
         }
         {
-            Raw ra, rb;
+            Raw ra;
             Job j = make_f(((wave - npair) % DW + DW) % DW);   // bf16 jobs continue the round robin
-            load_f(j, ra);
             while (j.type != 0) {
-                Job jn = next_f(j);
-                load_f(jn, rb);
+                load_f(j, ra);
                 process_f(j, ra);
-                j = jn;
-                if (j.type == 0) break;
-                jn = next_f(j);
-                load_f(jn, ra);
-                process_f(j, rb);
-                j = jn;
+                j = next_f(j);
             }
         }
         // the previous step's pending window-mass shares of this batch's entries: each
