@@ -63,17 +63,22 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
 __device__ __forceinline__ uint32_t bf16x2_trunc(float a, float b) {
     return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
 }
+// DPP lane moves.  Every pattern used here reads a lane of the same row of 16, so no
+// lane is out of bounds and bound_ctrl changes no value; with it set the compiler can
+// fold the move into the instruction that consumes it.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
 // value of the lane at the mirrored position of this lane's SW-wide column group
 // (row_half_mirror for SW = 8, row_mirror for SW = 16): pairs the high column of a
 // head with its low column
 template <int SW>
 __device__ __forceinline__ float mirror(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), SW == 8 ? 0x141 : 0x140, 0xF, 0xF, false));
+    return dppf<SW == 8 ? 0x141 : 0x140>(x);
 }
 // value of lane (l ^ 8) within its row of 16 (row_ror:8): the other column slot
-__device__ __forceinline__ float ror8(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
-}
+__device__ __forceinline__ float ror8(float x) { return dppf<0x128>(x); }
 // Reductions over the 4 lane groups of a column (lanes l, l^16, l^32, l^48) with the
 // gfx950 row-swap permutes: permlane16_swap(x, x) hands every lane the values of rows
 // 2k and 2k+1 at its position, permlane32_swap(x, x) those of both 32-lane halves.  Both
@@ -94,10 +99,10 @@ __device__ __forceinline__ float qg_max(float x) {
 // swaps, the half-row / row mirrors and the row swaps: no LDS traffic
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
-    if constexpr (N >= 8) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
-    if constexpr (N >= 16) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));
+    x += dppf<0xB1>(x);                           // quad [1,0,3,2]
+    x += dppf<0x4E>(x);                           // quad [2,3,0,1]
+    if constexpr (N >= 8) x += dppf<0x141>(x);    // row_half_mirror
+    if constexpr (N >= 16) x += dppf<0x140>(x);   // row_mirror
     if constexpr (N >= 32) {
         const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
         x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
@@ -199,7 +204,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     // bf16 query operand (every live column holds its head's query, exact bf16)
     __shared__ __attribute__((aligned(16))) uint16_t qs[DW][32][QSTR];
     __shared__ float kb[DW][16];                                         // per wave: key-offset bias per column
-    __shared__ float s_m[DW][G], s_l[DW][G];
+    __shared__ float s_m[DW][G], s_l[DW][G], s_vb[DW][G];
     __shared__ float s_acc[DW][G][D];
     __shared__ __attribute__((aligned(16))) uint16_t nkv[DW][2][D];     // per wave: the new token's K and V
 
@@ -378,13 +383,18 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         ldw<2 * MB>(R.w + CQ / 2, vbase + (uint32_t)(j.t * MB * 8) + (uint32_t)((n * 4 + qg) * nt16 * MB * 8));
     };
 
-    // online softmax over the lane's NVV scores (per column: max over the 4 lane groups)
+    // online softmax over the lane's NVV scores.  The reference max is shared by every
+    // column of a head (max over the 4 lane groups and both column slots), so the slots
+    // merge by plain addition at the end.  It moves lazily: only when a score exceeds it
+    // by more than 8 (log2 units), so probabilities stay below 2^8 and the rescale of the
+    // accumulators is rare after the wave's first job.
     auto softmax = [&](float* s, float* p, int nvv) __attribute__((always_inline)) {
         float mx = s[0];
         for (int v = 1; v < nvv; ++v) mx = fmaxf(mx, s[v]);
         mx = qg_max(mx);
-        const float mnew = fmaxf(m_run, mx);
-        if (__any(mnew > m_run)) {
+        if constexpr (NSLOT == 2) mx = fmaxf(mx, ror8(mx));
+        if (__any(mx > m_run + 8.f)) {
+            const float mnew = fmaxf(m_run, mx);
             const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
             l_run *= alpha;
             lw *= alpha;
@@ -642,34 +652,39 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         }
     }
 
-    // ---- wave state -> workgroup partial for this split
+    // ---- wave state -> workgroup partial for this split.  All columns of a head share
+    // the reference max, so the head's output is the plain sum of its high and low
+    // columns and of both column slots; the value-offset bias joins once per head in the
+    // block merge.
     float lt = qg_sum(l_run);
-    const float vb = qg_sum(vbias);
+    float vb = qg_sum(vbias);
     float a[MB][4];
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[m][i] = acc[m][i] + mirror<SW>(acc[m][i]) + vb;   // high + low columns
-    float mw = m_run;
-    if constexpr (NSLOT == 2) {
-        const float m1 = ror8(m_run), l1 = ror8(lt);
-        const float M = fmaxf(m_run, m1);
-        const float f0 = exp2f(m_run - M), f1 = exp2f(m1 - M);
+        for (int i = 0; i < 4; ++i) a[m][i] = acc[m][i] + mirror<SW>(acc[m][i]);   // high + low columns
+    if constexpr (NSLOT == 2) {   // row_mirror takes a slot's (high, low) pair to the other slot's
 #pragma unroll
         for (int m = 0; m < MB; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[m][i] = f0 * a[m][i] + f1 * ror8(a[m][i]);
-        lt = f0 * lt + f1 * l1;
-        mw = M;
+            for (int i = 0; i < 4; ++i) a[m][i] += dppf<0x140>(a[m][i]);
+        lt += ror8(lt);
+        vb += ror8(vb);
     }
+    // (the sums stay ahead of the store branch below, where each folds with its lane move)
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(a[m][i]));
     if (slot == 0 && hi) {
 #pragma unroll
         for (int m = 0; m < MB; ++m)
 #pragma unroll
             for (int i = 0; i < 4; ++i) s_acc[wave][rn][16 * m + 4 * qg + i] = a[m][i];
         if (qg == 0) {
-            s_m[wave][rn] = mw;
+            s_m[wave][rn] = m_run;
             s_l[wave][rn] = lt;
+            s_vb[wave][rn] = vb;
         }
     }
     __syncthreads();
@@ -683,9 +698,9 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         float L = 0.f, A = 0.f;
 #pragma unroll
         for (int w = 0; w < DW; ++w) {
-            const float f = exp2f(s_m[w][gg] - M);
+            const float f = __builtin_amdgcn_exp2f(s_m[w][gg] - M);
             L += f * s_l[w][gg];
-            A += f * s_acc[w][gg][c];
+            A += f * (s_acc[w][gg][c] + s_vb[w][gg]);
         }
         pacc[(int64_t)gg * D + c] = A;
         if (c == 0) pml[gg] = make_float2(M, L);
