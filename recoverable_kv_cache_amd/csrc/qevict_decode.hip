@@ -54,6 +54,30 @@ __device__ __forceinline__ f4_t mfma16(u2_t a, u2_t b, f4_t c) {
 }
 // both fp16 halves of a 32-bit word as fp32
 __device__ __forceinline__ f2_t h2f(uint32_t w) { return __builtin_convertvector(__builtin_bit_cast(h2_t, w), f2_t); }
+// x times the fp16 in the low / high half of w, one mixed-precision FMA with a zero
+// addend (the same rounding as converting first and multiplying)
+__device__ __forceinline__ float mul_h_lo(float x, uint32_t w) {
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(w));
+    return r;
+}
+__device__ __forceinline__ float mul_h_hi(float x, uint32_t w) {
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(w));
+    return r;
+}
+// maxima of operands that are never NaN (scores, -inf included): the plain instructions,
+// without the quieting that fmaxf adds for signalling NaNs
+__device__ __forceinline__ float max2(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
 // two fp32 -> packed bf16 pair, round to nearest even
 __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
     const f2_t v = {a, b};
@@ -89,11 +113,11 @@ __device__ __forceinline__ float qg_sum(float x) {
     const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
-__device__ __forceinline__ float qg_max(float x) {
+__device__ __forceinline__ float qg_max(float x) {   // (operands never NaN)
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    x = max2(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+    return max2(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 // sum over aligned groups of N consecutive lanes (N = 8, 16, 32 or 64) with DPP quad
 // swaps, the half-row / row mirrors and the row swaps: no LDS traffic
@@ -201,8 +225,8 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     constexpr int NV = S::NV, QSTR = S::QSTR;
     __shared__ uint2 lut[256];                                           // code byte -> 4 bf16 {0..3}
     // per wave: rows 0-15 the INT2 query operand of the current job, rows 16-31 the
-    // bf16 query operand (every live column holds its head's query, exact bf16)
-    __shared__ __attribute__((aligned(16))) uint16_t qs[DW][32][QSTR];
+    // bf16 query operand (every live column holds its head's query, exact bf16), row 32 zeros
+    __shared__ __attribute__((aligned(16))) uint16_t qs[DW][33][QSTR];
     __shared__ float kb[DW][16];                                         // per wave: key-offset bias per column
     __shared__ float s_m[DW][G], s_l[DW][G], s_vb[DW][G];
     __shared__ float s_acc[DW][G][D];
@@ -230,7 +254,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     const int pending = bf.hdr[u].mass_pending;
     const int n_tok = n_old + 1;
     const uint16_t* qhead = qin + ((int64_t)b * g.h_q + hk * G) * D;
-    float qf[CPL];                                       // q of the lane's product channels, fp32
+    float qf[CPL];                  // q of the lane's product channels times log2(e)/sqrt(d), fp32
     {
         uint32_t w[CQ / 2];
         ldw<CQ / 2>(w, qhead + head * D + CQ * qg);
@@ -248,10 +272,11 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             lut[x] = make_uint2(bv(x & 3) | (bv((x >> 2) & 3) << 16), bv((x >> 4) & 3) | (bv((x >> 6) & 3) << 16));
         }
         stw<CQ / 2>(&qs[wave][16 + n][CQ * qg], w);
+        if (lane < D / 8) reinterpret_cast<uint4*>(&qs[wave][32][0])[lane] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
         for (int x = 0; x < CPL / 2; ++x) {
-            qf[2 * x] = bf16lo(w2[x]);
-            qf[2 * x + 1] = bf16hi(w2[x]);
+            qf[2 * x] = bf16lo(w2[x]) * scale;
+            qf[2 * x + 1] = bf16hi(w2[x]) * scale;
         }
         if (lane < D / 2) {
             reinterpret_cast<uint32_t*>(nkv[wave][0])[lane] = kn;
@@ -390,9 +415,11 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     // accumulators is rare after the wave's first job.
     auto softmax = [&](float* s, float* p, int nvv) __attribute__((always_inline)) {
         float mx = s[0];
-        for (int v = 1; v < nvv; ++v) mx = fmaxf(mx, s[v]);
+        int v = 1;
+        for (; v + 1 < nvv; v += 2) mx = max3(mx, s[v], s[v + 1]);
+        if (v < nvv) mx = max2(mx, s[v]);
         mx = qg_max(mx);
-        if constexpr (NSLOT == 2) mx = fmaxf(mx, ror8(mx));
+        if constexpr (NSLOT == 2) mx = max2(mx, ror8(mx));
         if (__any(mx > m_run + 8.f)) {
             const float mnew = fmaxf(m_run, mx);
             const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
@@ -428,6 +455,8 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         }
     };
 
+    const uint16_t* qrow_a = &qs[wave][(NSLOT == 2 && slot) ? 32 : n][CQ * qg];   // slot 0 columns only
+    const uint16_t* qrow_b = &qs[wave][(NSLOT == 2 && !slot) ? 32 : n][CQ * qg];  // slot 1 columns only
     auto process_q = [&](const Job& j, const Raw& R) __attribute__((always_inline)) {
         // (1) q * sclK for every (item, head, channel) once, split into bf16 high + low
         //     rows of the wave's operand block; key-offset bias sum_c q_c offK_c per row
@@ -436,8 +465,8 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             uint32_t hw[CPL / 2], lw2[CPL / 2];
 #pragma unroll
             for (int x = 0; x < CPL / 2; ++x) {
-                const f2_t s2 = h2f(R.w[S::O_KS + x]), o2 = h2f(R.w[S::O_KO + x]);
-                const float x0 = qf[2 * x] * s2.x, x1 = qf[2 * x + 1] * s2.y;
+                const f2_t o2 = h2f(R.w[S::O_KO + x]);
+                const float x0 = mul_h_lo(qf[2 * x], R.w[S::O_KS + x]), x1 = mul_h_hi(qf[2 * x + 1], R.w[S::O_KS + x]);
                 bias = fmaf(qf[2 * x], o2.x, bias);
                 bias = fmaf(qf[2 * x + 1], o2.y, bias);
                 hw[x] = bf16x2_trunc(x0, x1);
@@ -447,40 +476,38 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             wave_lds_fence();
             stw<CPL / 2>(&qs[wave][pitem * SW + phead][CPL * pcb], hw);
             stw<CPL / 2>(&qs[wave][pitem * SW + SW - 1 - phead][CPL * pcb], lw2);
-            if (pcb == 0) {
-                kb[wave][pitem * SW + phead] = bias;
-                kb[wave][pitem * SW + SW - 1 - phead] = bias;
-            }
+            if (pcb == 0) kb[wave][pitem * SW + phead] = bias;   // (read by the high column)
             wave_lds_fence();
         }
-        // (2) the lane's column of the operand
-        u4_t bq[KS];
+        // (2) the lane's column of the operand, once per window: each window's MFMAs see
+        //     only the columns of its own slot (the other slot's lanes read the zero row), so
+        //     both windows accumulate into one score tile
+        u4_t bqa[KS], bqb[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bq[ks] = *reinterpret_cast<const u4_t*>(&qs[wave][n][CQ * qg + 8 * ks]);
-        const float kbs = kb[wave][n] * scale;
-        // (3) scores S^T[token][column] = codes . (q * sclK)
+        for (int ks = 0; ks < KS; ++ks) {
+            bqa[ks] = *reinterpret_cast<const u4_t*>(qrow_a + 8 * ks);
+            if constexpr (NSLOT == 2) bqb[ks] = *reinterpret_cast<const u4_t*>(qrow_b + 8 * ks);
+        }
+        const float c0 = hi ? kb[wave][n] : 0.f;   // key-offset bias, once per head (high column)
+        // (3) scores S^T[token][column] = codes . (q * sclK) + bias, log2 units
         float s[NV];
 #pragma unroll
         for (int tc = 0; tc < TPC; ++tc) {
-            f4_t da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};
+            f4_t d = {c0, c0, c0, c0};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int by = tc * (CQ / 4) + 2 * ks;
                 const uint32_t wa = R.w[by >> 2];
                 const u2_t a0 = lut4(wa, by & 3), a1 = lut4(wa, (by & 3) + 1);
-                da = mfma32(u4_t{a0.x, a0.y, a1.x, a1.y}, bq[ks], da);
+                d = mfma32(u4_t{a0.x, a0.y, a1.x, a1.y}, bqa[ks], d);
                 if constexpr (NSLOT == 2) {
                     const uint32_t wb = R.w[S::KCW + (by >> 2)];
                     const u2_t b0 = lut4(wb, by & 3), b1 = lut4(wb, (by & 3) + 1);
-                    db = mfma32(u4_t{b0.x, b0.y, b1.x, b1.y}, bq[ks], db);
+                    d = mfma32(u4_t{b0.x, b0.y, b1.x, b1.y}, bqb[ks], d);
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float v = (NSLOT == 2 && slot) ? db[i] : da[i];
-                v += mirror<SW>(v);                            // high + low query parts
-                s[4 * tc + i] = fmaf(v, scale, kbs);
-            }
+            for (int i = 0; i < 4; ++i) s[4 * tc + i] = d[i] + mirror<SW>(d[i]);   // high + low query parts
         }
         if (NSLOT == 2 && j.ib < 0) {
 #pragma unroll
@@ -492,10 +519,10 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         uint32_t P[NV / 2];
 #pragma unroll
         for (int x = 0; x < NV / 2; ++x) {
-            const f2_t o2 = h2f(R.w[S::O_VO + x]), c2 = h2f(R.w[S::O_VS + x]);
+            const f2_t o2 = h2f(R.w[S::O_VO + x]);
             vbias = fmaf(p[2 * x], o2.x, vbias);
             vbias = fmaf(p[2 * x + 1], o2.y, vbias);
-            P[x] = hilo(p[2 * x] * c2.x, p[2 * x + 1] * c2.y);
+            P[x] = hilo(mul_h_lo(p[2 * x], R.w[S::O_VS + x]), mul_h_hi(p[2 * x + 1], R.w[S::O_VS + x]));
         }
         u4_t pa, pb;
         if constexpr (TPC == 2) {
