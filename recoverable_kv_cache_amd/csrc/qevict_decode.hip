@@ -757,117 +757,168 @@ hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t
 
 
 // ------------------------------------------------------------------------------------ finish
-// One workgroup per (query head, sequence): o_h = sum_s 2^(m_s - M) acc_s / L with
-// L = sum_s 2^(m_s - M) l_s and LSE_h = M + log2 L (log2 domain); the head's share
-// of every entry's window mass, 2^(lse_w,h - LSE_h); the token count.  Every load
-// of the workgroup is issued up front.
+// Workgroups 0 .. H_q-1, one per (query head, sequence): o_h = sum_s 2^(m_s - M) acc_s / L
+// with L = sum_s 2^(m_s - M) l_s and LSE_h = M + log2 L (log2 domain), the step's token
+// into its block, the token count.  On scoring steps H_q .. H_q + C - 1 follow, each
+// over a block of entries for all heads: the head's share of every entry's window mass,
+// 2^(lse_w,h - LSE_h), read and written in whole rows of the entry-major arrays.  Those
+// recompute LSE_h from the split statistics with the same per-wave reduction, so both
+// kinds see bitwise the same value.
 constexpr int FN_THREADS = 256;
 constexpr int FN_MAXS = 512;            // splits (the host caps n_splits below this)
-constexpr int FN_MAXE = 16;             // entries per thread: n_acc_max <= 4096
+constexpr int FN_MV = 8;                // mass values per thread in a mass workgroup
 
 // sum / max over all 64 lanes without LDS (DPP quad swaps, row mirrors, row swaps); every
 // lane gets the same value
 __device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
-__device__ __forceinline__ float wave_max(float x) {
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)));
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false)));
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false)));
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false)));
+__device__ __forceinline__ float wave_max(float x) {   // (operands never NaN)
+    x = max2(x, dppf<0xB1>(x));
+    x = max2(x, dppf<0x4E>(x));
+    x = max2(x, dppf<0x141>(x));
+    x = max2(x, dppf<0x140>(x));
     return qg_max(x);
 }
+// Loads in this kernel are unconditional, from clamped addresses (out-of-range positions
+// repeat the last valid one), and the repeats are cancelled arithmetically: they cannot
+// change a maximum, and their sum terms are multiplied by 0.  A load under a per-lane
+// condition (or a select the compiler turns back into one) makes the compiler wait for
+// it on the spot, and the loads would take one round trip each.
+//
+// M and L of head h over all splits, computed by one whole wave (lane = split mod 64)
+__device__ __forceinline__ void head_ml(const float2* ml, int NS, int h_q, int lane, float& M, float& L) {
+    float2 v[FN_MAXS / 64];
+#pragma unroll
+    for (int k = 0; k < FN_MAXS / 64; ++k) v[k] = ml[(int64_t)imin(lane + 64 * k, NS - 1) * h_q];
+    float m = v[0].x;
+#pragma unroll
+    for (int k = 1; k < FN_MAXS / 64; ++k) m = max2(m, v[k].x);
+    M = wave_max(m);
+    float l = 0.f;
+#pragma unroll
+    for (int k = 0; k < FN_MAXS / 64; ++k)
+        l += __builtin_amdgcn_exp2f(v[k].x - M) * (v[k].y * (lane + 64 * k < NS ? 1.f : 0.f));
+    L = wave_sum(l);
+}
+// entries per mass workgroup
+__host__ __device__ inline int fn_epw(int h_q) { return h_q >= FN_THREADS * FN_MV ? 1 : FN_THREADS * FN_MV / h_q; }
 
 template <int D>
 __global__ void __launch_bounds__(FN_THREADS) k_finish(Geo g, Bufs bf, int layer, float* __restrict__ out,
                                                        const uint16_t* __restrict__ knew,
                                                        const uint16_t* __restrict__ vnew, int score_now) {
-    // each wave owns D/16 float4 columns of the output; its lanes split the splits into
-    // 64/(D/16) phases, summed across lanes at the end.  No LDS, no barrier: every wave
-    // also reduces the split maxima / sums itself, and all loads are issued up front.
-    constexpr int CW = D / 16, PH = 64 / CW;
-    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t u = unit_of(g, b, layer);
     const int NS = g.n_splits;
-    const int n_acc = bf.hdr[u].n_acc;
-    // window log-sum-exps of this head
-    float lwv[FN_MAXE];
-    const float* lwin = bf.lse_win + u * (int64_t)g.n_acc_max * g.h_q + h;
+    const float2* mlu = bf.part_ml + u * NS * (int64_t)g.h_q;
+    if ((int)blockIdx.x >= g.h_q) {
+        // ---- mass shares of entries [e0, e1) (entry 0 is the sink block: no window)
+        __shared__ float s_lse[FN_THREADS * FN_MV];
+        const int epw = fn_epw(g.h_q);
+        const int n_acc = bf.hdr[u].n_acc;
+        const int e0 = imin(1 + ((int)blockIdx.x - g.h_q) * epw, n_acc), e1 = imin(e0 + epw, n_acc);
+        const int64_t i0 = (int64_t)e0 * g.h_q, nv = (int64_t)(e1 - e0) * g.h_q;
+        const float* lwin = bf.lse_win + u * (int64_t)g.n_acc_max * g.h_q + i0;
+        if (nv == 0) return;
+        float lv[FN_MV];
 #pragma unroll
-    for (int k = 0; k < FN_MAXE; ++k) {
-        const int e = 1 + tid + FN_THREADS * k;
-        lwv[k] = (score_now && e < n_acc) ? lwin[(int64_t)e * g.h_q] : -INFINITY;
-    }
-    // split statistics: all splits for the wave-wide M and L, this lane's phase for the weights
-    const float2* ml = bf.part_ml + u * NS * (int64_t)g.h_q + h;
-    float2 mlv[FN_MAXS / 64];
+        for (int k = 0; k < FN_MV; ++k) lv[k] = lwin[imin(tid + FN_THREADS * k, (int)nv - 1)];
+        constexpr int NWV = FN_THREADS / 64, HB = 8;   // a wave's heads h = wv + NWV j, HB at a time
+        if (NS <= 64) {
+            // one split per lane: the loads of HB heads are in flight together; the same
+            // reduction as head_ml (its further terms are zeros)
+            for (int h0 = wv; h0 < g.h_q; h0 += NWV * HB) {
+                float2 v[HB];
 #pragma unroll
-    for (int k = 0; k < FN_MAXS / 64; ++k) {
-        const int sp = lane + 64 * k;
-        mlv[k] = sp < NS ? ml[(int64_t)sp * g.h_q] : make_float2(M_INIT, 0.f);
+                for (int j = 0; j < HB; ++j)
+                    v[j] = mlu[(int64_t)imin(lane, NS - 1) * g.h_q + imin(h0 + NWV * j, g.h_q - 1)];
+#pragma unroll
+                for (int j = 0; j < HB; ++j) {
+                    const int h = h0 + NWV * j;
+                    const float M = wave_max(v[j].x);
+                    const float L = wave_sum(__builtin_amdgcn_exp2f(v[j].x - M) * (v[j].y * (lane < NS ? 1.f : 0.f)));
+                    if (h < g.h_q && lane == 0) s_lse[h] = M + log2f(L);
+                }
+            }
+        } else {
+            for (int h = wv; h < g.h_q; h += NWV) {
+                float M, L;
+                head_ml(mlu + h, NS, g.h_q, lane, M, L);
+                if (lane == 0) s_lse[h] = M + log2f(L);
+            }
+        }
+        __syncthreads();
+        float* mp = bf.mass_part + u * (int64_t)g.n_acc_max * g.h_q + i0;
+#pragma unroll
+        for (int k = 0; k < FN_MV; ++k) {
+            const int i = tid + FN_THREADS * k;
+            if (i < nv) mp[i] = __builtin_amdgcn_exp2f(lv[k] - s_lse[(int)((i0 + i) % g.h_q)]);
+        }
+        return;
     }
+    // ---- output of head h: each wave owns D/16 float4 columns; its lanes split the splits
+    // into 64/(D/16) phases, summed across lanes at the end.  No LDS, no barrier: every
+    // wave reduces the split maxima / sums itself, and all loads are issued up front.
+    static_assert(D <= FN_THREADS, "one thread per channel of the token");
+    constexpr int CW = D / 16, PH = 64 / CW;
+    const int h = blockIdx.x;
+    const float2* ml = mlu + h;
     const int col = wv * CW + lane % CW, ph = lane / CW;
     const f4_t* pa = reinterpret_cast<const f4_t*>(bf.part_acc + (u * NS * (int64_t)g.h_q + h) * D) + col;
     const int64_t sstride = (int64_t)g.h_q * D / 4;   // float4 per split
     constexpr int NX = 8;            // splits of this lane's phase per batch of loads
     f4_t x[NX];
-    float mx[NX];
+    float mx[NX], wk[NX];
 #pragma unroll
     for (int k = 0; k < NX; ++k) {
-        const int sp = ph + k * PH;
-        x[k] = sp < NS ? pa[sp * sstride] : f4_t{0.f, 0.f, 0.f, 0.f};
-        mx[k] = sp < NS ? ml[(int64_t)sp * g.h_q].x : M_INIT;
+        const int sp = ph + k * PH, sc = imin(sp, NS - 1);
+        x[k] = pa[sc * sstride];
+        mx[k] = ml[(int64_t)sc * g.h_q].x;
+        wk[k] = sp < NS ? 1.f : 0.f;
     }
-    float M = M_INIT;
-#pragma unroll
-    for (int k = 0; k < FN_MAXS / 64; ++k) M = fmaxf(M, mlv[k].x);
-    M = wave_max(M);
-    float L = 0.f;
-#pragma unroll
-    for (int k = 0; k < FN_MAXS / 64; ++k) L += __builtin_amdgcn_exp2f(mlv[k].x - M) * mlv[k].y;
-    L = wave_sum(L);
+    // the step's token goes into its sink / recent-window block (one workgroup per KV
+    // head: the first query head of the group); its inputs and the block record are read
+    // here, ahead of every store, so that all loads share one round trip
+    const int G = g.h_q / g.h_kv, hk = h / G;
+    const bool tok_wg = h % G == 0;
+    UnitHdr* hdr = bf.hdr + u;
+    // (read through a lane-varying zero index, so the values stay in vector registers and
+    // nothing waits for them before the stores)
+    const int z = (int)__builtin_amdgcn_mbcnt_lo(0u, 0u);
+    const int* hw = reinterpret_cast<const int*>(hdr) + z;
+    const int n_old = hw[offsetof(UnitHdr, pos) / 4];   // n is advanced below by head 0's workgroup
+    const int tok_at = hw[offsetof(UnitHdr, tok_at) / 4], page = hw[offsetof(UnitHdr, tok_page) / 4];
+    const uint16_t kn = knew[((int64_t)b * g.h_kv + hk) * D + imin(tid, D - 1)];
+    const uint16_t vn = vnew[((int64_t)b * g.h_kv + hk) * D + imin(tid, D - 1)];
+    float M, L;
+    head_ml(ml, NS, g.h_q, lane, M, L);
     f4_t a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < NX; ++k) a4 += __builtin_amdgcn_exp2f(mx[k] - M) * x[k];
+    for (int k = 0; k < NX; ++k) a4 += (__builtin_amdgcn_exp2f(mx[k] - M) * wk[k]) * x[k];
     for (int sp0 = ph + NX * PH; sp0 < NS; sp0 += NX * PH) {      // more splits than one batch
 #pragma unroll
         for (int k = 0; k < NX; ++k) {
-            const int sp = sp0 + k * PH;
-            x[k] = sp < NS ? pa[sp * sstride] : f4_t{0.f, 0.f, 0.f, 0.f};
-            mx[k] = sp < NS ? ml[(int64_t)sp * g.h_q].x : M_INIT;
+            const int sp = sp0 + k * PH, sc = imin(sp, NS - 1);
+            x[k] = pa[sc * sstride];
+            mx[k] = ml[(int64_t)sc * g.h_q].x;
+            wk[k] = sp < NS ? 1.f : 0.f;
         }
 #pragma unroll
-        for (int k = 0; k < NX; ++k) a4 += __builtin_amdgcn_exp2f(mx[k] - M) * x[k];
+        for (int k = 0; k < NX; ++k) a4 += (__builtin_amdgcn_exp2f(mx[k] - M) * wk[k]) * x[k];
     }
     // sum over the phases: lanes l, l + CW, l + 2 CW, ... (row rotations, then row swaps)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float v = a4[i];
-        if constexpr (CW == 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false));
-        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+        if constexpr (CW == 4) v += dppf<0x124>(v);
+        v += dppf<0x128>(v);
         a4[i] = qg_sum(v);
     }
     if (ph == 0) reinterpret_cast<f4_t*>(out + ((int64_t)b * g.h_q + h) * D)[col] = a4 / L;
-    const float lse = M + log2f(L);
-    if (tid == 0) bf.lse_glob[u * g.h_q + h] = lse;
-    // this head's share of each entry's window mass (entries without tokens carry -inf)
-    if (score_now) {
-        float* mp = bf.mass_part + u * (int64_t)g.n_acc_max * g.h_q + h;
-#pragma unroll
-        for (int k = 0; k < FN_MAXE; ++k) {
-            const int e = 1 + tid + FN_THREADS * k;
-            if (e < n_acc) mp[(int64_t)e * g.h_q] = __builtin_amdgcn_exp2f(lwv[k] - lse);
-        }
-    }
-    // the step's token goes into its sink / recent-window block (one workgroup per KV
-    // head: the first query head of the group); the split kernel read it from its inputs
-    const int G = g.h_q / g.h_kv;
-    if (h % G == 0) {
-        const int hk = h / G;
-        UnitHdr* hdr = bf.hdr + u;
-        const int n_old = hdr->pos;      // n is advanced below by head 0's workgroup: not read here
+    if (tid == 0) bf.lse_glob[u * g.h_q + h] = M + log2f(L);
+    if (tok_wg) {
         // the block the split kernel attended the token in: found only when its sink /
         // recent window was accessible (a window the router did not prepare is an error)
-        const bool ok = hdr->tok_at == n_old;
-        const int page = hdr->tok_page;
+        const bool ok = tok_at == n_old;
         uint16_t* blk = nullptr;
         int Wp = g.W, i = 0;
         if (ok && page == -2) {
@@ -878,12 +929,10 @@ __global__ void __launch_bounds__(FN_THREADS) k_finish(Geo g, Bufs bf, int layer
             i = (n_old - g.n_sink) % g.W;
             blk = bf.pages + u * (int64_t)g.n_pages * g.page_elems + (int64_t)page * g.page_elems;
         }
-        if (blk) {
+        if (blk && tid < D) {
             uint16_t* kh = blk + (int64_t)(2 * hk) * Wp * D;
-            for (int c = tid; c < D; c += FN_THREADS) {
-                kh[lay_k(i, c, D, Wp)] = knew[((int64_t)b * g.h_kv + hk) * D + c];
-                kh[(int64_t)Wp * D + lay_v(i, c, D, Wp)] = vnew[((int64_t)b * g.h_kv + hk) * D + c];
-            }
+            kh[lay_k(i, tid, D, Wp)] = kn;
+            kh[(int64_t)Wp * D + lay_v(i, tid, D, Wp)] = vn;
         }
         if (tid == 0) {
             if (!ok) atomicOr(&hdr->status, QEVICT_DEV_E_WINDOW);
@@ -897,8 +946,10 @@ __global__ void __launch_bounds__(FN_THREADS) k_finish(Geo g, Bufs bf, int layer
 
 hipError_t launch_finish(const Geo& g, const Bufs& bf, int layer, float* out, const uint16_t* k_new,
                          const uint16_t* v_new, int score_now, hipStream_t s) {
-    if (g.n_splits > FN_MAXS || g.n_acc_max > 1 + FN_THREADS * FN_MAXE) return hipErrorInvalidValue;
-    const dim3 grid(g.h_q, g.B), block(FN_THREADS);
+    if (g.n_splits > FN_MAXS || g.h_q > FN_THREADS * FN_MV) return hipErrorInvalidValue;
+    const int epw = fn_epw(g.h_q);
+    const int n_mass = score_now ? (g.n_acc_max - 1 + epw - 1) / epw : 0;   // entries 1 .. n_acc_max - 1
+    const dim3 grid(g.h_q + n_mass, g.B), block(FN_THREADS);
     if (g.d == 128) hipLaunchKernelGGL(k_finish<128>, grid, block, 0, s, g, bf, layer, out, k_new, v_new, score_now);
     else if (g.d == 64) hipLaunchKernelGGL(k_finish<64>, grid, block, 0, s, g, bf, layer, out, k_new, v_new, score_now);
     else return hipErrorInvalidValue;
