@@ -296,7 +296,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     const uint16_t* pages = bf.pages + u * (int64_t)g.n_pages * g.page_elems;
     const uint8_t* slots = bf.slots + u * (int64_t)g.n_slots * g.slot_bytes + (int64_t)hk * g.slot_head_bytes;
     const uint16_t* sinks = bf.sinks + u * g.sink_elems;
-    float* lse_out = bf.lse_win + u * (int64_t)g.n_acc_max * g.h_q + hk * G;
+    float* lse_out = bf.lse_win + lse_win_off(g, u, n_old & 1) + hk * G;   // this step's half
 
     // ---- job sequence of this wave.  A batch is up to SPLIT_BLOCK - 1 entries, one per
     // lane 1..63.  INT2 entries are paired in order (one pair per job, chunk by chunk),
@@ -657,23 +657,26 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
                 j = next_f(j);
             }
         }
-        // the previous step's pending window-mass shares of this batch's entries: each
-        // entry once, by the KV head whose index matches its position in the split
+        // the previous step's pending window-mass shares of this batch's entries (from its
+        // window and row log-sum-exps, the other half of the window array): each entry
+        // once, by the KV head whose index matches its position in the split
         if (pending && wave == DW - 1 && valid && x % g.h_kv == hk && me.win >= 0) {
-            const float* row = bf.mass_part + (u * g.n_acc_max + e_begin + x) * (int64_t)g.h_q;
+            const float* row = bf.lse_win + lse_win_off(g, u, (n_old - 1) & 1) + (int64_t)(e_begin + x) * g.h_q;
+            const float* lg = bf.lse_glob + u * g.h_q;
             double* sc = bf.score + u * g.n_windows + me.win;
             const double s0 = *sc;
             double sm = 0.0;
             if ((g.h_q & 3) == 0) {
                 for (int h = 0; h < g.h_q; h += 4) {
                     const f4_t v = *reinterpret_cast<const f4_t*>(row + h);
-                    sm += (double)v[0];
-                    sm += (double)v[1];
-                    sm += (double)v[2];
-                    sm += (double)v[3];
+                    const f4_t l = *reinterpret_cast<const f4_t*>(lg + h);
+                    sm += (double)mass_share(v[0], l[0]);
+                    sm += (double)mass_share(v[1], l[1]);
+                    sm += (double)mass_share(v[2], l[2]);
+                    sm += (double)mass_share(v[3], l[3]);
                 }
             } else {
-                for (int h = 0; h < g.h_q; ++h) sm += (double)row[h];
+                for (int h = 0; h < g.h_q; ++h) sm += (double)mass_share(row[h], lg[h]);
             }
             *sc = s0 + sm / g.h_q;
         }
@@ -757,16 +760,13 @@ hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t
 
 
 // ------------------------------------------------------------------------------------ finish
-// Workgroups 0 .. H_q-1, one per (query head, sequence): o_h = sum_s 2^(m_s - M) acc_s / L
-// with L = sum_s 2^(m_s - M) l_s and LSE_h = M + log2 L (log2 domain), the step's token
-// into its block, the token count.  On scoring steps H_q .. H_q + C - 1 follow, each
-// over a block of entries for all heads: the head's share of every entry's window mass,
-// 2^(lse_w,h - LSE_h), read and written in whole rows of the entry-major arrays.  Those
-// recompute LSE_h from the split statistics with the same per-wave reduction, so both
-// kinds see bitwise the same value.
+// One workgroup per (query head, sequence): o_h = sum_s 2^(m_s - M) acc_s / L with
+// L = sum_s 2^(m_s - M) l_s and LSE_h = M + log2 L (log2 domain), the step's token into
+// its block, the token count.  The heads' shares of each window's mass follow from LSE_h
+// and the window log-sum-exps; the next split kernel (or the router / an export) folds
+// them into the scores.
 constexpr int FN_THREADS = 256;
 constexpr int FN_MAXS = 512;            // splits (the host caps n_splits below this)
-constexpr int FN_MV = 8;                // mass values per thread in a mass workgroup
 
 // sum / max over all 64 lanes without LDS (DPP quad swaps, row mirrors, row swaps); every
 // lane gets the same value
@@ -799,8 +799,6 @@ __device__ __forceinline__ void head_ml(const float2* ml, int NS, int h_q, int l
         l += __builtin_amdgcn_exp2f(v[k].x - M) * (v[k].y * (lane + 64 * k < NS ? 1.f : 0.f));
     L = wave_sum(l);
 }
-// entries per mass workgroup
-__host__ __device__ inline int fn_epw(int h_q) { return h_q >= FN_THREADS * FN_MV ? 1 : FN_THREADS * FN_MV / h_q; }
 
 template <int D>
 __global__ void __launch_bounds__(FN_THREADS) k_finish(Geo g, Bufs bf, int layer, float* __restrict__ out,
@@ -810,51 +808,6 @@ __global__ void __launch_bounds__(FN_THREADS) k_finish(Geo g, Bufs bf, int layer
     const int64_t u = unit_of(g, b, layer);
     const int NS = g.n_splits;
     const float2* mlu = bf.part_ml + u * NS * (int64_t)g.h_q;
-    if ((int)blockIdx.x >= g.h_q) {
-        // ---- mass shares of entries [e0, e1) (entry 0 is the sink block: no window)
-        __shared__ float s_lse[FN_THREADS * FN_MV];
-        const int epw = fn_epw(g.h_q);
-        const int n_acc = bf.hdr[u].n_acc;
-        const int e0 = imin(1 + ((int)blockIdx.x - g.h_q) * epw, n_acc), e1 = imin(e0 + epw, n_acc);
-        const int64_t i0 = (int64_t)e0 * g.h_q, nv = (int64_t)(e1 - e0) * g.h_q;
-        const float* lwin = bf.lse_win + u * (int64_t)g.n_acc_max * g.h_q + i0;
-        if (nv == 0) return;
-        float lv[FN_MV];
-#pragma unroll
-        for (int k = 0; k < FN_MV; ++k) lv[k] = lwin[imin(tid + FN_THREADS * k, (int)nv - 1)];
-        constexpr int NWV = FN_THREADS / 64, HB = 8;   // a wave's heads h = wv + NWV j, HB at a time
-        if (NS <= 64) {
-            // one split per lane: the loads of HB heads are in flight together; the same
-            // reduction as head_ml (its further terms are zeros)
-            for (int h0 = wv; h0 < g.h_q; h0 += NWV * HB) {
-                float2 v[HB];
-#pragma unroll
-                for (int j = 0; j < HB; ++j)
-                    v[j] = mlu[(int64_t)imin(lane, NS - 1) * g.h_q + imin(h0 + NWV * j, g.h_q - 1)];
-#pragma unroll
-                for (int j = 0; j < HB; ++j) {
-                    const int h = h0 + NWV * j;
-                    const float M = wave_max(v[j].x);
-                    const float L = wave_sum(__builtin_amdgcn_exp2f(v[j].x - M) * (v[j].y * (lane < NS ? 1.f : 0.f)));
-                    if (h < g.h_q && lane == 0) s_lse[h] = M + log2f(L);
-                }
-            }
-        } else {
-            for (int h = wv; h < g.h_q; h += NWV) {
-                float M, L;
-                head_ml(mlu + h, NS, g.h_q, lane, M, L);
-                if (lane == 0) s_lse[h] = M + log2f(L);
-            }
-        }
-        __syncthreads();
-        float* mp = bf.mass_part + u * (int64_t)g.n_acc_max * g.h_q + i0;
-#pragma unroll
-        for (int k = 0; k < FN_MV; ++k) {
-            const int i = tid + FN_THREADS * k;
-            if (i < nv) mp[i] = __builtin_amdgcn_exp2f(lv[k] - s_lse[(int)((i0 + i) % g.h_q)]);
-        }
-        return;
-    }
     // ---- output of head h: each wave owns D/16 float4 columns; its lanes split the splits
     // into 64/(D/16) phases, summed across lanes at the end.  No LDS, no barrier: every
     // wave reduces the split maxima / sums itself, and all loads are issued up front.
@@ -946,10 +899,8 @@ __global__ void __launch_bounds__(FN_THREADS) k_finish(Geo g, Bufs bf, int layer
 
 hipError_t launch_finish(const Geo& g, const Bufs& bf, int layer, float* out, const uint16_t* k_new,
                          const uint16_t* v_new, int score_now, hipStream_t s) {
-    if (g.n_splits > FN_MAXS || g.h_q > FN_THREADS * FN_MV) return hipErrorInvalidValue;
-    const int epw = fn_epw(g.h_q);
-    const int n_mass = score_now ? (g.n_acc_max - 1 + epw - 1) / epw : 0;   // entries 1 .. n_acc_max - 1
-    const dim3 grid(g.h_q + n_mass, g.B), block(FN_THREADS);
+    if (g.n_splits > FN_MAXS) return hipErrorInvalidValue;
+    const dim3 grid(g.h_q, g.B), block(FN_THREADS);
     if (g.d == 128) hipLaunchKernelGGL(k_finish<128>, grid, block, 0, s, g, bf, layer, out, k_new, v_new, score_now);
     else if (g.d == 64) hipLaunchKernelGGL(k_finish<64>, grid, block, 0, s, g, bf, layer, out, k_new, v_new, score_now);
     else return hipErrorInvalidValue;
@@ -962,7 +913,7 @@ __global__ void __launch_bounds__(256) k_flush_mass(Geo g, Bufs bf, int layer, i
     const int64_t u = unit_of(g, b, layer);
     UnitHdr* hdr = bf.hdr + u;
     if (!hdr->mass_pending) return;
-    apply_mass_range(g, bf, u, threadIdx.x, hdr->n_acc, blockDim.x);
+    apply_mass_range(g, bf, u, hdr->n - 1, threadIdx.x, hdr->n_acc, blockDim.x);   // the step at position n - 1
     __syncthreads();
     if (threadIdx.x == 0) hdr->mass_pending = 0;
 }

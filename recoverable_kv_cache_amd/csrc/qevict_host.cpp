@@ -98,7 +98,7 @@ struct Layout {
 };
 
 enum { O_HDR, O_WIN, O_SCORE, O_ACC, O_SPLITS, O_FPAGE, O_FSLOT, O_PACK, O_FILL, O_TARGET, O_LSEW, O_LSEG,
-       O_PML, O_PACC, O_PAGES, O_SLOTS, O_SINKS, O_PLENS, O_KF, O_KQ, O_MPART, O_SBLK, O_COUNT };
+       O_PML, O_PACC, O_PAGES, O_SLOTS, O_SINKS, O_PLENS, O_KF, O_KQ, O_SBLK, O_COUNT };
 
 qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, Layout* lay) {
     qevict_status s = validate(c);
@@ -154,7 +154,7 @@ qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, La
     sz[O_PACK] = U * g.n_windows * sizeof(PackItem);
     sz[O_FILL] = U * g.n_windows * sizeof(FillItem);
     sz[O_TARGET] = U * g.n_windows;
-    sz[O_LSEW] = U * g.n_acc_max * g.h_q * sizeof(float);
+    sz[O_LSEW] = U * 2 * g.n_acc_max * g.h_q * sizeof(float);   // two halves by position parity
     sz[O_LSEG] = U * g.h_q * sizeof(float);
     sz[O_PML] = U * g.n_splits * g.h_q * sizeof(float2);
     sz[O_PACC] = U * g.n_splits * g.h_q * g.d * sizeof(float);
@@ -162,7 +162,6 @@ qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, La
     sz[O_SLOTS] = U * g.n_slots * (size_t)g.slot_bytes;
     sz[O_SINKS] = U * (size_t)g.sink_elems * 2;
     sz[O_PLENS] = sz[O_KF] = sz[O_KQ] = g.B * sizeof(int32_t);
-    sz[O_MPART] = U * (size_t)g.n_acc_max * g.h_q * sizeof(float);
     sz[O_SBLK] = U * (size_t)g.n_splits * SPLIT_BLOCK * sizeof(AccEntry);
     size_t at = 0;
     for (int i = 0; i < O_COUNT; ++i) {
@@ -197,7 +196,6 @@ Bufs bind_bufs(const Layout& lay, void* arena) {
     b.pages = (uint16_t*)(a + lay.off[O_PAGES]);
     b.slots = (uint8_t*)(a + lay.off[O_SLOTS]);
     b.sinks = (uint16_t*)(a + lay.off[O_SINKS]);
-    b.mass_part = (float*)(a + lay.off[O_MPART]);
     b.split_blk = (AccEntry*)(a + lay.off[O_SBLK]);
     return b;
 }

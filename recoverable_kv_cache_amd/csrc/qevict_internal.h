@@ -97,17 +97,21 @@ struct Bufs {
     PackItem* pack;         // [U][n_windows]
     FillItem* fill;         // [U][n_windows]
     int8_t* target;         // [U][n_windows] forced targets
-    float* lse_win;         // [U][n_acc_max][h_q]   log2 domain
+    float* lse_win;         // [U][2][n_acc_max][h_q] log2 domain, by parity of the step's position
     float* lse_glob;        // [U][h_q]              log2 domain
     float2* part_ml;        // [U][n_splits][h_q]    (m, l), log2 domain
     float* part_acc;        // [U][n_splits][h_q][d]
     uint16_t* pages;        // [U][n_pages][h_kv][2][W][d]   bf16
     uint8_t* slots;         // [U][n_slots][h_kv][slot_head_bytes]
     uint16_t* sinks;        // [U][h_kv] pages of Ws tokens (same layout as a window page)
-    float* mass_part;       // [U][n_acc_max][h_q] per-head share of each entry's mass (last decode step)
 };
 
 __host__ __device__ inline int64_t unit_of(const Geo& g, int b, int l) { return (int64_t)b * g.L + l; }
+// window log-sum-exps of the decode step at a position of parity par: the next step reads
+// them (to fold this step's window mass) while writing its own to the other half
+__host__ __device__ inline int64_t lse_win_off(const Geo& g, int64_t u, int par) {
+    return (u * 2 + par) * (int64_t)g.n_acc_max * g.h_q;
+}
 
 // Each split's header and first SPLIT_BLOCK - 1 accessible-list entries, copied by the
 // router to a fixed place so that a decode wave gets them in one load (one per lane).

@@ -175,7 +175,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
 
     // ---- 0. the last decode step's window-mass shares enter the scores first
     if (hdr->mass_pending) {
-        apply_mass_range(g, bf, u, tid, hdr->n_acc, RT_THREADS);
+        apply_mass_range(g, bf, u, n - 1, tid, hdr->n_acc, RT_THREADS);   // the step at position n - 1
         __syncthreads();
         if (tid == 0) hdr->mass_pending = 0;
     }
