@@ -60,6 +60,31 @@ def test_batched_ragged_prompts_gqa8_d128():
     _print(f"ragged: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}")
 
 
+def test_window64_gqa8_multichunk():
+    """70B-shaped heads at reduced size: W = 64 (an INT2 window spans two 32-token
+    chunks of pair jobs, a bf16 window four tiles), 8 query heads per KV head, d = 128,
+    ragged prompts, drifting queries."""
+    _print("case: window 64, GQA 8")
+    wl = WL.Workload("w64", 1, 2, 16, 2, 128, 1200, 24, 64, 4, 128, 8, 0.30, 0.70, prompt_len_min=700,
+                     n_outlier=2, n_topics=2, topic_period=8)
+    ls = Lockstep(wl).run(24)
+    _print(f"w64: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}")
+
+
+def test_window16_d128_promotions():
+    """Churn-shaped heads at reduced size: W = 16 (one 16-token tile per INT2 chunk),
+    d = 128, GQA 4, flat initial scores and topic drift, so windows are promoted back to
+    bf16 and demoted again."""
+    _print("case: window 16, d 128")
+    wl = WL.Workload("w16", 1, 2, 8, 2, 128, 700, 48, 16, 4, 64, 8, 0.20, 0.70, prompt_len_min=500,
+                     n_outlier=2, n_topics=4, topic_period=16)
+    n_win = math.ceil((wl.prompt_len + wl.n_decode - wl.n_sink) / wl.window)
+    si = torch.zeros((wl.batch, n_win), dtype=torch.float64)
+    ls = Lockstep(wl, score_init=si).run(48)
+    assert sum(e["promoted"] for u in ls.units for e in u.events) > 0
+    _print(f"w16: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}")
+
+
 def test_one_way_and_route_step_scoring_flags():
     _print("case: flags")
     wl = WL.TINY.with_(n_topics=4, topic_period=16, n_decode=32, budget_frac=0.25)
