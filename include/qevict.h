@@ -217,6 +217,18 @@ qevict_status qevict_time_next_decode(qevict_state* st, void* ev_before, void* e
 qevict_status qevict_step_bytes(qevict_state* st, int32_t layer, int64_t* kv_bytes, int64_t* io_bytes,
                                 void* stream);
 
+/* Measurement aid, not part of the method: one launch of a plain streaming read of
+ * `bytes` bytes at device address buf (bytes a positive multiple of 1024 below 2^31,
+ * buf 16-byte aligned), every byte read once with 16-byte loads over 1024 workgroups of
+ * 256 threads, for comparison with the split-K kernel's achieved bandwidth.  sink
+ * (device, 1024 uint32, caller-owned) receives the XOR of the 32-bit words each
+ * workgroup read; the XOR of all 1024 equals that of the buffer's words.  With
+ * ev_before / ev_after (hipEvent_t with timing; both or neither) the kernel's own
+ * dispatch stamps its start and end, as for qevict_time_next_decode.  Enqueues on
+ * `stream`; argument errors return QEVICT_E_INVALID before anything is enqueued. */
+qevict_status qevict_stream_read(const void* buf, size_t bytes, void* sink, void* ev_before, void* ev_after,
+                                 void* stream);
+
 /* Name of the dominant decode kernel (the split-K attention), for profilers. */
 const char* qevict_decode_kernel_name(void);
 

@@ -27,7 +27,7 @@ EXPORTED_SYMBOLS = (
     "qevict_capacities", "qevict_plan", "qevict_create", "qevict_destroy", "qevict_prefill_init",
     "qevict_decode_attn", "qevict_route", "qevict_pack_int2", "qevict_promote", "qevict_poll_status",
     "qevict_export_unit", "qevict_decode_kernel_name", "qevict_last_error", "qevict_time_next_decode",
-    "qevict_step_bytes",
+    "qevict_step_bytes", "qevict_stream_read",
 )
 
 
@@ -86,6 +86,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qevict_export_unit.argtypes = [P, I, I, P, Z, ctypes.POINTER(Z), P]
     lib.qevict_time_next_decode.argtypes = [P, P, P]
     lib.qevict_step_bytes.argtypes = [P, I, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64), P]
+    lib.qevict_stream_read.argtypes = [P, Z, P, P, P, P]
     lib.qevict_decode_kernel_name.restype = ctypes.c_char_p
     lib.qevict_last_error.restype = ctypes.c_char_p
     for name in EXPORTED_SYMBOLS:
@@ -152,6 +153,25 @@ def _stream(stream) -> Optional[int]:
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
+
+
+STREAM_READ_WGS = 1024   # workgroups of qevict_stream_read: one sink word each
+
+
+def stream_read(buf, sink, ev_before=None, ev_after=None, stream=None):
+    """One plain streaming read of the contiguous device tensor ``buf`` (a measurement aid
+    beside the split-K kernel); ``sink`` is an int32 device tensor of STREAM_READ_WGS words
+    that receives one XOR word per workgroup.  Optional torch.cuda.Event pair (timing
+    enabled) stamped by the kernel's own dispatch."""
+    import torch
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf: a contiguous device tensor")
+    _expect(sink, (STREAM_READ_WGS,), "int32", buf.device, "sink")
+    ev0 = None if ev_before is None else ctypes.c_void_p(ev_before.cuda_event)
+    ev1 = None if ev_after is None else ctypes.c_void_p(ev_after.cuda_event)
+    lib = load_library()
+    _check(lib.qevict_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), ev0, ev1,
+                                  _stream(stream)))
 
 
 @dataclass

@@ -357,6 +357,18 @@ qevict_status qevict_decode_attn(qevict_state* st, int32_t layer, const void* q,
     return QEVICT_OK;
 }
 
+qevict_status qevict_stream_read(const void* buf, size_t bytes, void* sink, void* ev_before, void* ev_after,
+                                 void* stream) {
+    if (!buf || !sink) return fail(QEVICT_E_INVALID, "null buffer or sink");
+    if (bytes == 0 || bytes % 1024 != 0 || bytes >= ((size_t)1 << 31))
+        return fail(QEVICT_E_INVALID, "bytes must be a positive multiple of 1024 below 2^31 (got %zu)", bytes);
+    if (((uintptr_t)buf & 15) != 0) return fail(QEVICT_E_INVALID, "buffer not 16-byte aligned");
+    if ((ev_before == nullptr) != (ev_after == nullptr)) return fail(QEVICT_E_INVALID, "give both events or neither");
+    HIP_TRY(launch_stream_read(buf, (uint32_t)bytes, (uint32_t*)sink, (hipStream_t)stream, (hipEvent_t)ev_before,
+                               (hipEvent_t)ev_after));
+    return QEVICT_OK;
+}
+
 qevict_status qevict_time_next_decode(qevict_state* st, void* ev_before, void* ev_after) {
     if (!st) return fail(QEVICT_E_INVALID, "null state");
     if ((ev_before == nullptr) != (ev_after == nullptr)) return fail(QEVICT_E_INVALID, "give both events or neither");

@@ -183,5 +183,10 @@ hipError_t launch_prefill_setup(const Geo& g, const Bufs& bf, int layer, const u
 hipError_t launch_prefill_scores(const Geo& g, const Bufs& bf, int layer, const uint16_t* qp, const uint16_t* kp,
                                  const double* score_init, void* ws, hipStream_t s);
 size_t prefill_ws_bytes(const Geo& g);
+// measurement aid: one streaming read of [buf, buf + bytes), bytes a multiple of 1024;
+// sink receives one XOR word per workgroup (STREAM_READ_WGS of them)
+constexpr int STREAM_READ_WGS = 1024;
+hipError_t launch_stream_read(const void* buf, uint32_t bytes, uint32_t* sink, hipStream_t s, hipEvent_t ev0,
+                              hipEvent_t ev1);
 
 }  // namespace qv

@@ -167,3 +167,22 @@ def test_determinism_bitwise():
         ex = ls.st.export_unit(0, 0)
         outs.append((ex.score.tobytes(), b"".join(ex.ledger[w] for w in sorted(ex.ledger)), ex.state.tobytes()))
     assert outs[0] == outs[1]
+
+
+def test_stream_read_calibration_reads_every_byte():
+    """The streaming-read measurement aid reads every 32-bit word exactly once: the XOR of
+    its per-workgroup words equals the XOR of the buffer (sizes with a ragged tail of
+    pieces, and the size of one llama8b_32k layer step)."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(11)
+    for kib in (1, 4097, 26593):
+        _print(f"case: stream read {kib} KiB")
+        host = torch.randint(-2**31, 2**31 - 1, (kib * 256,), generator=g, dtype=torch.int64).to(torch.int32)
+        buf = host.to(dev)
+        sink = torch.zeros(B.STREAM_READ_WGS, dtype=torch.int32, device=dev)
+        B.stream_read(buf, sink)
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+        assert got == want, (kib, hex(got), hex(want))
+    with pytest.raises(B.QEvictError):
+        B.stream_read(torch.zeros(1000, dtype=torch.uint8, device=dev), sink)   # not a multiple of 1024 bytes
