@@ -40,7 +40,15 @@ reason in the design notes of the repository):
   rounded up from (max - off)/3, code = nearest level with ties up, code 0
   when scl == 0; Quantized-tier values inside attention are the exact
   ``off + code*scl`` (``qexec_bf16`` switches to their bf16 rounding);
-* TopK ties break by ascending window index; routing is per (sequence, layer).
+* TopK ties break by ascending window index; routing is per (sequence, layer);
+* alternative rankers ([QEvict] Appendix J, Eqs. 20-24): u_r(w) is the window's
+  head-averaged mass summed over the decode steps since the previous routing event;
+  "decay" sets S <- lambda*S + u_r and "pnorm" P <- P + u_r^p at each decode-time
+  routing event (not at the prefill routing), starting from S_0 resp. P_0 = S_0^p
+  with S_0 the prefill initialisation; "pnorm" ranks by P, which orders the
+  windows as P^(1/p) does; "keynorm" sets S(w) = -(mean over the window's tokens
+  of the L2 norm of the token's key over all KV heads' channels) when the window
+  enters the candidate pool, from its bf16 keys, and needs no attention mass.
 """
 from __future__ import annotations
 
@@ -82,6 +90,9 @@ class OracleConfig:
     promote: bool = True
     score_every_step: bool = True
     qexec_bf16: bool = False
+    ranker: str = "cum"          # "cum" (Eq. 21, the default), "decay" (Eq. 22), "pnorm" (Eq. 23), "keynorm" (Eq. 24)
+    decay_lambda: float = 0.99
+    pnorm_p: int = 3
 
     @property
     def group(self) -> int:
@@ -300,6 +311,7 @@ class UnitOracle:
         self.sink_v = np.zeros((cfg.h_kv, cfg.n_sink, cfg.d))
         self.win: dict[int, _Window] = {}
         self.score: dict[int, float] = {}
+        self.uacc: dict[int, float] = {}     # decay / pnorm: mass since the previous routing event
         self.events: list[dict] = []
         self.ever_evicted: set[int] = set()
 
@@ -321,6 +333,7 @@ class UnitOracle:
             self.win[w] = _Window(LOCAL, np.zeros((cfg.h_kv, cfg.window, cfg.d)),
                                   np.zeros((cfg.h_kv, cfg.window, cfg.d)))
             self.score[w] = 0.0
+            self.uacc[w] = 0.0
         W = self.win[w]
         assert W.state == LOCAL, "new tokens enter the recent region"
         W.k[:, i] = k
@@ -365,7 +378,9 @@ class UnitOracle:
             self._store(p, kp[:, p], vp[:, p])
         self.n = S
         info = {}
-        if score_init is not None:
+        if cfg.ranker == "keynorm":
+            pass   # the scores come from the keys when the windows enter the candidate pool
+        elif score_init is not None:
             for w in self.win:
                 self.score[w] = float(score_init[w])
         else:
@@ -376,7 +391,10 @@ class UnitOracle:
                 a, b = self.win_start(w), min(self.win_end(w), S)
                 self.score[w] = float(col[:, a:b].sum() / cfg.h_q)
             info["sink_mass"] = float(col[:, :min(cfg.n_sink, S)].sum() / cfg.h_q)
-        info["route"] = self.route()
+        if cfg.ranker == "pnorm":   # P_0 = S_0^p: the initialisation is the first event-level score
+            for w in self.win:
+                self.score[w] = self.score[w] ** cfg.pnorm_p
+        info["route"] = self.route(decode_event=False)
         return info
 
     # --- one decode step ([QEvict] §4.1 attention, §4.2 Eq. 1) ----------------------
@@ -394,13 +412,16 @@ class UnitOracle:
             a = softmax(K[h // G] @ q[h] / math.sqrt(cfg.d))
             A[h] = a
             o[h] = a @ V[h // G]
-        accumulate = cfg.score_every_step or ((self.step + 1) % cfg.omega == 0)
+        accumulate = (cfg.score_every_step or ((self.step + 1) % cfg.omega == 0)) and cfg.ranker != "keynorm"
         mass = {}
         for w in np.unique(owner[owner >= 0]):
             u = float(A[:, owner == w].sum() / cfg.h_q)
             mass[int(w)] = u
             if accumulate:
-                self.score[int(w)] += u
+                if cfg.ranker == "cum":
+                    self.score[int(w)] += u
+                else:
+                    self.uacc[int(w)] += u
         self.step += 1
         tier_mass = {z: np.zeros(cfg.h_q) for z in ("sink", LOCAL, FULL, QUANT)}
         tier_mass["sink"] = A[:, owner < 0].sum(axis=1)
@@ -408,12 +429,37 @@ class UnitOracle:
             tier_mass[self.win[int(w)].state] += A[:, owner == w].sum(axis=1)
         return dict(o=o, mass=mass, tier_mass=tier_mass, probs=A, owner=owner)
 
+    # --- alternative rankers ([QEvict] Appendix J) ------------------------------------
+    def key_norm_score(self, w: int) -> float:
+        """Eq. 24: minus the mean over the window's tokens of ||k_i||_2, the norm taken over
+        every KV head's channels of the token's (bf16) key."""
+        W = self.win[w]
+        norms = [math.sqrt(float(np.sum(W.k[:, i, :] ** 2))) for i in range(self.cfg.window)]
+        return -float(np.mean(norms))
+
+    def fold_interval(self):
+        """At a decode-time routing event: Eq. 22 (decay) or Eq. 23 (pnorm) with the
+        mass u_r gathered since the previous event, which then starts again from 0."""
+        cfg = self.cfg
+        for w in self.win:
+            if cfg.ranker == "decay":
+                self.score[w] = cfg.decay_lambda * self.score[w] + self.uacc[w]
+            elif cfg.ranker == "pnorm":
+                self.score[w] = self.score[w] + self.uacc[w] ** cfg.pnorm_p
+            self.uacc[w] = 0.0
+
     # --- routing ([QEvict] Eqs. 4-6 and Algorithm 1) --------------------------------
-    def route(self) -> dict:
+    def route(self, decode_event: bool = True) -> dict:
+        """A routing event; ``decode_event`` is False only for the one at the end of prefill."""
         cfg, caps = self.cfg, self.caps
         K_f, K_q = caps["K_f"], caps["K_q"]
+        if decode_event and cfg.ranker in ("decay", "pnorm"):
+            self.fold_interval()
         aged = [w for w, W in self.win.items()
                 if W.state == LOCAL and self.win_end(w) <= self.n - cfg.n_local]
+        if cfg.ranker == "keynorm":
+            for w in aged:
+                self.score[w] = self.key_norm_score(w)
         prev_f = [w for w, W in self.win.items() if W.state == FULL]
         prev_q = [w for w, W in self.win.items() if W.state == QUANT]
         cand = prev_f + prev_q + aged

@@ -91,11 +91,11 @@ def test_missing_head_average_is_caught(monkeypatch):
 def test_requantizing_on_redemotion_is_caught(monkeypatch):
     real_route = O.UnitOracle.route
 
-    def requant(self):
+    def requant(self, *a, **kw):
         for W in self.win.values():
             if W.state == O.FULL and W.ledger is not None:
                 W.ledger = None                       # forget the write-once record
-        return real_route(self)
+        return real_route(self, *a, **kw)
 
     monkeypatch.setattr(O.UnitOracle, "route", requant)
     _fails(TS.test_write_once_ledger_and_promoted_values)
