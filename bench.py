@@ -33,6 +33,11 @@ TIME_EVERY = 8           # per-kernel timing on every 8th timed step
 METRIC = "decode-attn tokens/s + achieved HBM GB/s (% peak) at 32K ctx; route µs/event"
 
 
+# --ranker choices -> the library flag that selects them (None: the cumulative score)
+RANKERS = {"cum": None, "decay": "QEVICT_F_RANK_DECAY", "pnorm": "QEVICT_F_RANK_PNORM",
+           "keynorm": "QEVICT_F_RANK_KEYNORM"}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -44,7 +49,7 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(wl, budget_s: float = 20.0) -> dict:
+def cpu_baseline(wl, budget_s: float = 20.0, ranker: str = "cum") -> dict:
     """Time the fp64 oracle's decode step on the host (layer 0, sequence 0), with a
     synthetic initial score instead of the prompt column sums (those alone are
     ~9 TFLOP of fp64 per layer on a 32K prompt)."""
@@ -58,7 +63,7 @@ def cpu_baseline(wl, budget_s: float = 20.0) -> dict:
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
     ocfg = O.OracleConfig(wl.h_q, wl.h_kv, wl.d_head, wl.window, wl.n_sink, wl.n_local, wl.omega,
-                          wl.quant_frac, wl.budget_frac, wl.n_decode)
+                          wl.quant_frac, wl.budget_frac, wl.n_decode, ranker=ranker)
     S = wl.prompt_len
     qp, kp, vp = WL.prompt(wl.with_(batch=1), 0)
     f = lambda t: t.to(torch.float64).numpy()
@@ -129,6 +134,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="llama8b_32k")
     ap.add_argument("--n-splits", type=int, default=0)
+    ap.add_argument("--ranker", choices=sorted(RANKERS), default="cum",
+                    help="window rank key: cumulative mass (Eq. 1) or an Appendix J alternative")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -158,7 +165,7 @@ def main():
     wl = {w.name: w for w in WL.ALL_WORKLOADS}[args.workload]
     if args.steps + args.warmup > wl.n_decode:
         sys.exit(f"--steps + --warmup must be <= {wl.n_decode}")
-    cfg = B.make_config(wl, n_splits=args.n_splits)
+    cfg = B.make_config(wl, n_splits=args.n_splits, flags=getattr(B, RANKERS[args.ranker]) if RANKERS[args.ranker] else 0)
     lens = wl.prompt_lens()
     st = B.QEvictState(cfg, lens, device=dev)
     log(f"[bench] {wl.name}: arena {st.info.arena_bytes / 2**30:.2f} GiB, splits {st.info.n_splits}, "
@@ -255,7 +262,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
-        cpu = cpu_baseline(wl, args.cpu_budget_s)
+        cpu = cpu_baseline(wl, args.cpu_budget_s, args.ranker)
 
     rp = sorted(route_ms)
     line = {
@@ -275,7 +282,7 @@ def main():
                    "d_head": wl.d_head, "prompt_len": wl.prompt_len, "window": wl.window, "n_sink": wl.n_sink,
                    "n_local": wl.n_local, "omega": wl.omega, "budget_frac": wl.budget_frac,
                    "quant_frac": wl.quant_frac, "storage": "bf16 + int2", "n_splits": st.info.n_splits,
-                   "K_f": st.info.max_K_f, "K_q": st.info.max_K_q},
+                   "K_f": st.info.max_K_f, "K_q": st.info.max_K_q, "ranker": args.ranker},
         "decode_attn_tokens_per_s": round(decode_tokens_per_s, 2),
         "route_us_per_event": {"mean": round(statistics.mean(route_ms) * 1e3, 2) if route_ms else None,
                                "p50": round(rp[len(rp) // 2] * 1e3, 2) if rp else None,

@@ -55,6 +55,17 @@ typedef enum {
 /* flags */
 #define QEVICT_F_NO_PROMOTE        1u  /* one-way variant Full -> Quantized -> Evicted (App. K) */
 #define QEVICT_F_SCORE_ROUTE_ONLY  2u  /* accumulate Eq. 1 only at the routing step itself */
+/* Alternative window rankers (App. J), at most one; default: cumulative mass (Eq. 21).
+ * u_r(w) is the window's head-averaged mass since the previous routing event (Eq. 20).
+ * DECAY:   S <- 0.99 * S + u_r at each decode-time routing event (Eq. 22).
+ * PNORM:   the rank key P <- P + u_r^3 (Eq. 23 with p = 3; P orders the windows as
+ *          P^(1/3) does), P_0 = S_0^3 from the prefill initialisation.
+ * KEYNORM: S(w) = -(mean over the window's tokens of the L2 norm of the token's key over
+ *          all KV heads' channels), set when the window enters the candidate pool (Eq. 24);
+ *          no attention mass is accumulated. */
+#define QEVICT_F_RANK_DECAY        4u
+#define QEVICT_F_RANK_PNORM        8u
+#define QEVICT_F_RANK_KEYNORM     16u
 
 typedef struct {
     int32_t batch;        /* B sequences */

@@ -20,6 +20,9 @@ LIB_PATH = os.path.join(HERE, "_lib", "libqevict.so")
 
 QEVICT_F_NO_PROMOTE = 1
 QEVICT_F_SCORE_ROUTE_ONLY = 2
+QEVICT_F_RANK_DECAY = 4      # alternative rankers ([QEvict] Appendix J); at most one
+QEVICT_F_RANK_PNORM = 8
+QEVICT_F_RANK_KEYNORM = 16
 
 DEV_E_POOL, DEV_E_WINDOW, DEV_E_RANGE, DEV_E_LIST = 1, 2, 4, 8
 

@@ -663,7 +663,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         if (pending && wave == DW - 1 && valid && x % g.h_kv == hk && me.win >= 0) {
             const float* row = bf.lse_win + lse_win_off(g, u, (n_old - 1) & 1) + (int64_t)(e_begin + x) * g.h_q;
             const float* lg = bf.lse_glob + u * g.h_q;
-            double* sc = bf.score + u * g.n_windows + me.win;
+            double* sc = mass_target(g, bf) + u * g.n_windows + me.win;
             const double s0 = *sc;
             double sm = 0.0;
             if ((g.h_q & 3) == 0) {

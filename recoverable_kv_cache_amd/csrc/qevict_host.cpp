@@ -58,6 +58,10 @@ qevict_status validate(const qevict_config* c) {
     if (c->n_sink < 0 || c->n_sink > 64) return fail(QEVICT_E_INVALID, "n_sink must be in [0, 64]");
     if (c->n_local < 0) return fail(QEVICT_E_INVALID, "n_local must be >= 0");
     if (c->omega < 1) return fail(QEVICT_E_INVALID, "omega must be >= 1");
+    {
+        const uint32_t rk = c->flags & (QEVICT_F_RANK_DECAY | QEVICT_F_RANK_PNORM | QEVICT_F_RANK_KEYNORM);
+        if (rk & (rk - 1)) return fail(QEVICT_E_INVALID, "at most one ranker flag");
+    }
     if (!(c->quant_frac >= 0.0 && c->quant_frac <= 1.0)) return fail(QEVICT_E_INVALID, "quant_frac must be in [0, 1]");
     if (!(c->budget_frac > 0.0)) return fail(QEVICT_E_INVALID, "budget_frac must be > 0");
     if (c->max_prompt < 0 || c->max_new < 0) return fail(QEVICT_E_INVALID, "max_prompt / max_new must be >= 0");
@@ -98,7 +102,7 @@ struct Layout {
 };
 
 enum { O_HDR, O_WIN, O_SCORE, O_ACC, O_SPLITS, O_FPAGE, O_FSLOT, O_PACK, O_FILL, O_TARGET, O_LSEW, O_LSEG,
-       O_PML, O_PACC, O_PAGES, O_SLOTS, O_SINKS, O_PLENS, O_KF, O_KQ, O_SBLK, O_COUNT };
+       O_PML, O_PACC, O_PAGES, O_SLOTS, O_SINKS, O_PLENS, O_KF, O_KQ, O_SBLK, O_UACC, O_COUNT };
 
 qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, Layout* lay) {
     qevict_status s = validate(c);
@@ -147,6 +151,7 @@ qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, La
     sz[O_HDR] = U * sizeof(UnitHdr);
     sz[O_WIN] = U * g.n_windows * sizeof(WinRec);
     sz[O_SCORE] = U * g.n_windows * sizeof(double);
+    sz[O_UACC] = U * g.n_windows * sizeof(double);
     sz[O_ACC] = U * g.n_acc_max * sizeof(AccEntry);
     sz[O_SPLITS] = U * (g.n_splits + 1) * sizeof(int32_t);
     sz[O_FPAGE] = U * g.n_pages * sizeof(int32_t);
@@ -182,6 +187,7 @@ Bufs bind_bufs(const Layout& lay, void* arena) {
     b.hdr = (UnitHdr*)(a + lay.off[O_HDR]);
     b.win = (WinRec*)(a + lay.off[O_WIN]);
     b.score = (double*)(a + lay.off[O_SCORE]);
+    b.uacc = (double*)(a + lay.off[O_UACC]);
     b.acc = (AccEntry*)(a + lay.off[O_ACC]);
     b.splits = (int32_t*)(a + lay.off[O_SPLITS]);
     b.free_pages = (int32_t*)(a + lay.off[O_FPAGE]);
@@ -351,7 +357,8 @@ qevict_status qevict_decode_attn(qevict_state* st, int32_t layer, const void* q,
     // Eq. 1 accumulates every step; with QEVICT_F_SCORE_ROUTE_ONLY only on the steps that end
     // a routing interval
     const int j = st->steps[layer];
-    const int score_now = !(g.flags & QEVICT_F_SCORE_ROUTE_ONLY) || (j + 1) % g.omega == 0;
+    const int score_now = (!(g.flags & QEVICT_F_SCORE_ROUTE_ONLY) || (j + 1) % g.omega == 0) &&
+                          !(g.flags & QEVICT_F_RANK_KEYNORM);   // the key-norm ranker uses no mass
     HIP_TRY(launch_finish(g, st->bf, layer, out, (const uint16_t*)k_new, (const uint16_t*)v_new, score_now, hs));
     st->steps[layer] += 1;
     return QEVICT_OK;

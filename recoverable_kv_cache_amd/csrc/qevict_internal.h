@@ -88,7 +88,8 @@ struct Geo {
 struct Bufs {
     UnitHdr* hdr;           // [U]
     WinRec* win;            // [U][n_windows]
-    double* score;          // [U][n_windows]
+    double* score;          // [U][n_windows]        the rank key (S, or P for the p-norm ranker)
+    double* uacc;           // [U][n_windows]        decay / p-norm rankers: mass since the previous routing event
     AccEntry* acc;          // [U][n_acc_max]
     int32_t* splits;        // [U][n_splits + 1]
     AccEntry* split_blk;    // [U][n_splits][SPLIT_BLOCK]: {entries, first entry, -1, 0}, then the split's entries
@@ -163,6 +164,16 @@ __host__ __device__ inline int lay_vp(int t, int W) {
 }
 // tokens held by the sink block: n_sink rounded up to a supported window size
 __host__ __device__ inline int sink_width(int n_sink) { return n_sink <= 16 ? 16 : (n_sink <= 32 ? 32 : 64); }
+
+constexpr double RANK_DECAY_LAMBDA = 0.99;   // Eq. 22
+// rankers that fold an interval's mass at each routing event
+__host__ __device__ inline bool rank_interval(const Geo& g) {
+    return (g.flags & (QEVICT_F_RANK_DECAY | QEVICT_F_RANK_PNORM)) != 0;
+}
+// where a decode step's window-mass shares go
+__host__ __device__ inline double* mass_target(const Geo& g, const Bufs& bf) {
+    return rank_interval(g) ? bf.uacc : bf.score;
+}
 
 // ---------------------------------------------------------------- launchers (host side)
 hipError_t launch_init(const Geo& g, const Bufs& bf, const int32_t* prompt_lens_dev, const int32_t* kf_dev,

@@ -4,6 +4,8 @@
 // sum_h share_h(w), with share_h(w) = 2^(window log-sum-exp - row log-sum-exp)
 // of head h (log2 domain, fp32), summed in head order in fp64.  The inputs are the
 // step's window log-sum-exps (by parity of its position) and its row log-sum-exps.
+// With the decay / p-norm rankers the mass goes to the interval accumulator instead
+// (Appendix J, Eq. 20), which each routing event folds into the rank key.
 #pragma once
 
 #include "qevict_internal.h"
@@ -25,8 +27,40 @@ __device__ inline void apply_mass_range(const Geo& g, const Bufs& bf, int64_t u,
         const float* row = lwin + (int64_t)e * g.h_q;
         double sm = 0.0;
         for (int h = 0; h < g.h_q; ++h) sm += (double)mass_share(row[h], lg[h]);
-        if (en.win >= 0) bf.score[u * g.n_windows + en.win] += sm / g.h_q;
+        if (en.win >= 0) mass_target(g, bf)[u * g.n_windows + en.win] += sm / g.h_q;
     }
+}
+
+// sum over the 64 lanes in a fixed order (every lane gets the result)
+__device__ inline double wave_sum_f64(double x) {
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+// The key-norm rank key of window w from its bf16 keys (Eq. 24): minus the mean over its
+// W tokens of the L2 norm of the token's key over all KV heads' channels.  Token norms
+// are computed by whole waves (lanes over (head, channel), fixed order), then summed in
+// token order by one thread; `tokn` is LDS scratch for W doubles.  All threads call.
+template <typename KeyAt>
+__device__ double key_norm_block(const Geo& g, int Wn, KeyAt key_at, double* tokn) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x / 64;
+    for (int i = wave; i < Wn; i += nwaves) {
+        double ss = 0.0;
+        for (int e = lane; e < g.h_kv * g.d; e += 64) {
+            const double x = (double)key_at(i, e / g.d, e % g.d);
+            ss += x * x;
+        }
+        ss = wave_sum_f64(ss);
+        if (lane == 0) tokn[i] = sqrt(ss);
+    }
+    __syncthreads();
+    double r = 0.0;
+    if (tid == 0) {
+        double t = 0.0;
+        for (int i = 0; i < Wn; ++i) t += tokn[i];
+        r = -(t / Wn);
+    }
+    __syncthreads();
+    return r;   // (valid in thread 0)
 }
 
 }  // namespace qv

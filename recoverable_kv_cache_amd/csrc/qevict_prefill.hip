@@ -13,6 +13,7 @@
 // accumulate in fp32 within a 64-row tile and in fp64 across tiles.
 #include "qevict_common.h"
 #include "qevict_internal.h"
+#include "qevict_mass.h"
 
 namespace qv {
 
@@ -211,7 +212,9 @@ __global__ void k_prefill_windows(Geo g, Bufs bf, int layer, const double* __res
             }
             s /= g.h_q;
         }
-        bf.score[u * g.n_windows + w] = s;
+        // (p-norm ranker: P_0 = S_0^3, the initialisation as the first event-level score)
+        bf.score[u * g.n_windows + w] = (g.flags & QEVICT_F_RANK_PNORM) ? s * s * s : s;
+        bf.uacc[u * g.n_windows + w] = 0.0;
     }
     if (threadIdx.x == 0) {
         double s = 0.0;
@@ -227,9 +230,34 @@ __global__ void k_score_copy(Geo g, Bufs bf, int layer, const double* __restrict
     const int64_t u = unit_of(g, b, layer);
     const int S = bf.hdr[u].prompt_len;
     const int n_win = S > g.n_sink ? (S - g.n_sink + g.W - 1) / g.W : 0;
-    for (int w = threadIdx.x; w < g.n_windows; w += blockDim.x)
-        bf.score[u * g.n_windows + w] = w < n_win ? init[(int64_t)b * g.n_windows + w] : 0.0;
+    for (int w = threadIdx.x; w < g.n_windows; w += blockDim.x) {
+        const double s = w < n_win ? init[(int64_t)b * g.n_windows + w] : 0.0;
+        bf.score[u * g.n_windows + w] = (g.flags & QEVICT_F_RANK_PNORM) ? s * s * s : s;
+        bf.uacc[u * g.n_windows + w] = 0.0;
+    }
     if (threadIdx.x == 0) bf.hdr[u].sink_mass = 0.0;
+}
+
+// Key-norm ranker at prefill (Appendix J, Eq. 24): the rank keys of the prompt windows that
+// age at the prefill routing, from the prompt's bf16 keys; the others start at 0 and get
+// theirs from their pages when they age.  One workgroup per (window, sequence).
+__global__ void __launch_bounds__(256) k_prefill_keynorm(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ kp) {
+    __shared__ double tokn[64];
+    const int w = blockIdx.x, b = blockIdx.y;
+    const int64_t u = unit_of(g, b, layer);
+    const int S = bf.hdr[u].prompt_len;
+    const int a = g.n_sink + w * g.W;
+    double r = 0.0;
+    if (a + g.W <= S - g.n_local) {
+        r = key_norm_block(g, g.W, [&](int i, int hk, int c) {
+            return __uint_as_float((uint32_t)kp[(((int64_t)b * g.h_kv + hk) * g.S_max + a + i) * g.d + c] << 16);
+        }, tokn);
+    }
+    if (threadIdx.x == 0) {
+        bf.score[u * g.n_windows + w] = r;
+        bf.uacc[u * g.n_windows + w] = 0.0;
+        if (w == 0) bf.hdr[u].sink_mass = 0.0;
+    }
 }
 
 size_t prefill_ws_bytes(const Geo& g) {
@@ -239,6 +267,10 @@ size_t prefill_ws_bytes(const Geo& g) {
 
 hipError_t launch_prefill_scores(const Geo& g, const Bufs& bf, int layer, const uint16_t* qp, const uint16_t* kp,
                                  const double* score_init, void* ws, hipStream_t s) {
+    if (g.flags & QEVICT_F_RANK_KEYNORM) {   // no attention mass: scores from the prompt keys
+        hipLaunchKernelGGL(k_prefill_keynorm, dim3(g.n_windows, g.B), dim3(256), 0, s, g, bf, layer, kp);
+        return hipGetLastError();
+    }
     if (score_init) {
         hipLaunchKernelGGL(k_score_copy, dim3(g.B), dim3(256), 0, s, g, bf, layer, score_init);
         return hipGetLastError();

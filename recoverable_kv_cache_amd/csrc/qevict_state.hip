@@ -29,6 +29,7 @@ __global__ void k_init(Geo g, Bufs bf, const int32_t* plens, const int32_t* kf, 
     for (int w = threadIdx.x; w < g.n_windows; w += blockDim.x) {
         bf.win[u * g.n_windows + w] = WinRec{ST_NONE, -1, -1, 0};
         bf.score[u * g.n_windows + w] = 0.0;
+        bf.uacc[u * g.n_windows + w] = 0.0;
         bf.target[u * g.n_windows + w] = 0;
     }
     for (int s = threadIdx.x; s <= g.n_splits; s += blockDim.x) bf.splits[u * (g.n_splits + 1) + s] = 0;
@@ -155,6 +156,13 @@ __device__ __forceinline__ int per_head_cost(const Geo& g, int kind) {
     return g.slot_head_bytes;
 }
 
+// Total order of doubles as unsigned integers, ascending; -0 counts as +0 (so equal
+// scores tie and fall to the window index).  Rank keys of every ranker, negative ones
+// (key-norm) included.
+__device__ inline unsigned long long ord_key(double s) {
+    const unsigned long long bits = (unsigned long long)__double_as_longlong(s + 0.0);
+    return (bits >> 63) ? ~bits : (bits | (1ull << 63));
+}
 // One workgroup per (sequence, layer).
 __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer, int mode) {
     extern __shared__ unsigned char smem_raw[];
@@ -179,6 +187,40 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         __syncthreads();
         if (tid == 0) hdr->mass_pending = 0;
     }
+    // ---- 0b. decay / p-norm rankers (Appendix J, Eqs. 22-23): at each decode-time routing
+    //          event the interval's mass enters the rank key and starts again from 0
+    if (mode == RM_ROUTE && rank_interval(g)) {
+        double* ua = bf.uacc + u * g.n_windows;
+        for (int w = tid; w < NW; w += RT_THREADS) {
+            const double x = ua[w];
+            score[w] = (g.flags & QEVICT_F_RANK_DECAY) ? __dadd_rn(__dmul_rn(RANK_DECAY_LAMBDA, score[w]), x)
+                                                       : __dadd_rn(score[w], __dmul_rn(__dmul_rn(x, x), x));
+            ua[w] = 0.0;
+        }
+        __syncthreads();
+    }
+    // ---- 0c. key-norm ranker (Eq. 24): each recent window that ages at this event gets
+    //          its rank key from the keys in its page (prompt windows got theirs at prefill)
+    if (mode == RM_ROUTE && (g.flags & QEVICT_F_RANK_KEYNORM)) {
+        int* list = sm.idx;                          // (scratch before the sort)
+        double* tokn = reinterpret_cast<double*>(sm.key);
+        if (tid == 0) sm.misc[0] = 0;
+        __syncthreads();
+        for (int w = tid; w < NW; w += RT_THREADS)
+            if (win[w].state == ST_LOCAL && g.n_sink + (w + 1) * g.W <= n - g.n_local) list[atomicAdd(&sm.misc[0], 1)] = w;
+        __syncthreads();
+        const int nl = sm.misc[0];
+        for (int k = 0; k < nl; ++k) {
+            const int w = list[k];
+            if (win[w].page < 0) continue;           // (a recent window always has its page)
+            const uint16_t* pg = bf.pages + u * (int64_t)g.n_pages * g.page_elems + (int64_t)win[w].page * g.page_elems;
+            const double r = key_norm_block(g, g.W, [&](int i, int hk, int c) {
+                return __uint_as_float((uint32_t)pg[(int64_t)(2 * hk) * g.W * g.d + lay_k(i, c, g.d, g.W)] << 16);
+            }, tokn);
+            if (tid == 0) score[w] = r;
+        }
+        __syncthreads();
+    }
 
     // ---- 1. candidate pool (Eq. 4): previous Full ∪ previous Quantized ∪ aged recent windows
     for (int w = tid; w < RT_MAXW; w += RT_THREADS) {
@@ -199,7 +241,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     __syncthreads();
     const int n_cand = block_scan_excl(flag, sm.wsum);
     // flag[] now holds positions; flag2[] the candidate bits.  Keys: descending score
-    // then ascending window index == ascending (~bits(score), index) for score >= 0.
+    // then ascending window index == ascending (~ord_key(score), index).
     int cand_w[RT_PER], cand_pos[RT_PER];
 #pragma unroll
     for (int i = 0; i < RT_PER; ++i) {
@@ -215,7 +257,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         const int w = cand_w[i];
         if (w >= 0) {
             const double s = (mode == RM_ROUTE || mode == RM_PREFILL) ? score[w] : 0.0;
-            sm.key[cand_pos[i]] = ~(unsigned long long)__double_as_longlong(s);
+            sm.key[cand_pos[i]] = ~ord_key(s);
             sm.idx[cand_pos[i]] = w;
         }
     }

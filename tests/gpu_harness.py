@@ -58,7 +58,10 @@ def compare_unit(ex: B.UnitExport, unit: O.UnitOracle, tag: str, check_scores=Tr
     np.testing.assert_array_equal(ex.sink_v[:, :ns], bf16_bits(unit.sink_v[:, :ns]))
     if check_scores:
         ref = np.array([unit.score[w] for w in range(n_created)])
-        err = np.abs(ex.score[:n_created] - ref).max() if n_created else 0.0
+        got = np.asarray(ex.score[:n_created], dtype=np.float64)
+        if unit.cfg.ranker == "pnorm":   # rank key P = sum of cubed interval masses: compare P^(1/3)
+            ref, got = np.cbrt(ref), np.cbrt(got)
+        err = np.abs(got - ref).max() if n_created else 0.0
         assert err <= S_TOL, f"{tag}: score error {err}"
         return float(err)
     return 0.0
@@ -72,8 +75,11 @@ class Lockstep:
         self.lens = wl.prompt_lens()
         cfg = B.make_config(wl, n_splits=n_splits, flags=flags, n_layers=n_layers)
         self.st = B.QEvictState(cfg, self.lens, device=device)
+        ranker = ("decay" if flags & B.QEVICT_F_RANK_DECAY else "pnorm" if flags & B.QEVICT_F_RANK_PNORM
+                  else "keynorm" if flags & B.QEVICT_F_RANK_KEYNORM else "cum")
         ocfg = cfg_from(wl, promote=not (flags & B.QEVICT_F_NO_PROMOTE),
-                        score_every_step=not (flags & B.QEVICT_F_SCORE_ROUTE_ONLY), **(ocfg_over or {}))
+                        score_every_step=not (flags & B.QEVICT_F_SCORE_ROUTE_ONLY), ranker=ranker,
+                        **(ocfg_over or {}))
         self.ocfg = ocfg
         self.units = [O.UnitOracle(ocfg, S) for S in self.lens]
         self.score_init = score_init

@@ -186,3 +186,24 @@ def test_stream_read_calibration_reads_every_byte():
         assert got == want, (kib, hex(got), hex(want))
     with pytest.raises(B.QEvictError):
         B.stream_read(torch.zeros(1000, dtype=torch.uint8, device=dev), sink)   # not a multiple of 1024 bytes
+
+
+@pytest.mark.parametrize("flag", ["decay", "pnorm", "keynorm"])
+def test_alternative_rankers_lockstep(flag):
+    """The rankers of [QEvict] Appendix J against the oracle: routing sets, tiers, ledgers
+    and pages bit-exact, rank keys within 1e-4 (cube roots for p-norm).  The tiny case
+    routes every 2 steps under fast topic drift from flat initial scores, where decay and
+    p-norm route differently from the cumulative score and promote windows; then a GQA-8,
+    d = 128 ragged batch."""
+    f = {"decay": B.QEVICT_F_RANK_DECAY, "pnorm": B.QEVICT_F_RANK_PNORM, "keynorm": B.QEVICT_F_RANK_KEYNORM}[flag]
+    _print(f"case: ranker {flag}")
+    wl = WL.TINY.with_(n_topics=4, topic_period=8, n_decode=96, n_outlier=2, budget_frac=0.3, omega=2)
+    si = None if flag == "keynorm" else torch.zeros((1, 64), dtype=torch.float64)
+    ls = Lockstep(wl, score_init=si, flags=f).run(96)
+    if flag != "keynorm":     # (key-norm keys never change, so nothing is promoted)
+        assert sum(e["promoted"] for e in ls.units[0].events) > 0
+    _print(f"{flag} tiny: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}")
+    wl2 = WL.Workload("rank", 1, 2, 16, 2, 128, 700, 24, 32, 4, 64, 8, 0.30, 0.70, prompt_len_min=400,
+                      n_outlier=2, n_topics=2, topic_period=8)
+    ls2 = Lockstep(wl2, flags=f).run(24)
+    _print(f"{flag} gqa8: max o err {ls2.max_o_err:.2e}, max score err {ls2.max_s_err:.2e}")
