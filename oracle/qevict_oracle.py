@@ -37,8 +37,10 @@ reason in the design notes of the repository):
   fp16 offset/scale per (head, channel) for K and per (head, token) for V +
   4 B position + 16 B ledger record;
 * quantization: off = fp16 rounded down from the group minimum, scl = fp16
-  rounded up from (max - off)/3, code = nearest level with ties up, code 0
-  when scl == 0; Quantized-tier values inside attention are the exact
+  rounded up from (max - off)/L with L = 2^b - 1 levels above the offset (b = 2,
+  the INT2 default, or b = 4 for the INT4 tier of [QEvict] Appendix G.3, which
+  changes nothing else), code = nearest level with ties up, code 0 when
+  scl == 0; Quantized-tier values inside attention are the exact
   ``off + code*scl`` (``qexec_bf16`` switches to their bf16 rounding);
 * TopK ties break by ascending window index; routing is per (sequence, layer);
 * alternative rankers ([QEvict] Appendix J, Eqs. 20-24): u_r(w) is the window's
@@ -93,6 +95,7 @@ class OracleConfig:
     ranker: str = "cum"          # "cum" (Eq. 21, the default), "decay" (Eq. 22), "pnorm" (Eq. 23), "keynorm" (Eq. 24)
     decay_lambda: float = 0.99
     pnorm_p: int = 3
+    quant_bits: int = 2          # 2 (INT2, the default) or 4 (INT4, [QEvict] Appendix G.3)
 
     @property
     def group(self) -> int:
@@ -110,10 +113,10 @@ def full_window_bytes(cfg: OracleConfig) -> int:
 
 
 def quant_window_bytes(cfg: OracleConfig) -> int:
-    """M_q: 2-bit codes for K and V, fp16 offset+scale per (head, channel) for K and
+    """M_q: b-bit codes for K and V, fp16 offset+scale per (head, channel) for K and
     per (head, token) for V, a 4-byte start position and a 16-byte ledger record."""
     W, H, d = cfg.window, cfg.h_kv, cfg.d
-    codes = 2 * (W * H * d * 2) // 8
+    codes = 2 * (W * H * d * cfg.quant_bits) // 8
     kparams = 2 * 2 * H * d
     vparams = 2 * 2 * H * W
     return codes + kparams + vparams + 4 + 16
@@ -170,31 +173,37 @@ def ru_fp16(x) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------------------
-# INT2 asymmetric quantization  ([QEvict] §4.3 "Migration-Stable Quantization")
+# INT2 / INT4 asymmetric quantization  ([QEvict] §4.3 "Migration-Stable Quantization";
+# Appendix G.3 for the 4-bit tier)
 # --------------------------------------------------------------------------------------
-def quantize_groups(x: np.ndarray, axis: int):
-    """Quantize groups of ``x`` along ``axis`` to 2-bit codes.
+def quantize_groups(x: np.ndarray, axis: int, bits: int = 2):
+    """Quantize groups of ``x`` along ``axis`` to ``bits``-bit codes (L = 2^bits - 1).
 
-    off = RD_fp16(min), scl = RU_fp16((max - off) / 3); code = number of levels
-    k in {1,2,3} with 2(x - off) >= (2k - 1) scl (nearest level, ties up),
+    off = RD_fp16(min), scl = RU_fp16((max - off) / L); code = number of levels
+    k in {1..L} with 2(x - off) >= (2k - 1) scl (nearest level, ties up),
     code = 0 where scl == 0.  Every operand is a bf16 or fp16 value, so the
-    comparisons are exact in float64; the fp64 quotient by 3 rounds to the same
+    comparisons are exact in float64; the fp64 quotient by L rounds to the same
     fp16 upward value as the exact quotient (it cannot land on an fp16 value
     unless the exact quotient is one).
     """
+    if bits not in (2, 4):
+        raise ValueError("bits must be 2 or 4")
+    L = (1 << bits) - 1
     x = np.asarray(x, dtype=np.float64)
     mn = x.min(axis=axis, keepdims=True)
     mx = x.max(axis=axis, keepdims=True)
     off = rd_fp16(mn)
-    scl = ru_fp16((mx - off) / 3.0)
+    scl = ru_fp16((mx - off) / float(L))
     t = 2.0 * (x - off)
-    codes = (t >= scl).astype(np.uint8) + (t >= 3.0 * scl) + (t >= 5.0 * scl)
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    for k in range(1, L + 1):
+        codes += (t >= (2 * k - 1) * scl)
     codes = np.where(scl == 0.0, 0, codes).astype(np.uint8)
     return codes, np.squeeze(off, axis), np.squeeze(scl, axis)
 
 
 def dequantize(codes: np.ndarray, off: np.ndarray, scl: np.ndarray, axis: int) -> np.ndarray:
-    """x_hat = off + code * scl (exact in float64 for fp16 off/scl and 2-bit codes)."""
+    """x_hat = off + code * scl (exact in float64 for fp16 off/scl and 2- or 4-bit codes)."""
     off = np.expand_dims(off, axis)
     scl = np.expand_dims(scl, axis)
     return off + codes.astype(np.float64) * scl
@@ -202,7 +211,7 @@ def dequantize(codes: np.ndarray, off: np.ndarray, scl: np.ndarray, axis: int) -
 
 @dataclass
 class Ledger:
-    """Write-once INT2 record of one window (Lambda_w in [QEvict] Algorithm 1)."""
+    """Write-once quantized record of one window (Lambda_w in [QEvict] Algorithm 1)."""
 
     k_codes: np.ndarray   # [H_kv][W][d] uint8, groups = channels (axis 1 = tokens)
     k_off: np.ndarray     # [H_kv][d]
@@ -212,6 +221,7 @@ class Ledger:
     v_scl: np.ndarray
     start_pos: int
     dormant: bool = False
+    bits: int = 2
 
     def k_hat(self) -> np.ndarray:
         return dequantize(self.k_codes, self.k_off, self.k_scl, axis=1)
@@ -220,31 +230,35 @@ class Ledger:
         return dequantize(self.v_codes, self.v_off, self.v_scl, axis=2)
 
 
-def quantize_window(k: np.ndarray, v: np.ndarray, start_pos: int) -> Ledger:
+def quantize_window(k: np.ndarray, v: np.ndarray, start_pos: int, bits: int = 2) -> Ledger:
     """Keys per channel across the window's tokens, values per token across channels."""
     if np.any(np.abs(k) > FP16_MAX) or np.any(np.abs(v) > FP16_MAX):
         raise RangeError("K/V value beyond the fp16 range")
-    kc, ko, ks = quantize_groups(k, axis=1)
-    vc, vo, vs = quantize_groups(v, axis=2)
-    return Ledger(kc, ko, ks, vc, vo, vs, start_pos)
+    kc, ko, ks = quantize_groups(k, axis=1, bits=bits)
+    vc, vo, vs = quantize_groups(v, axis=2, bits=bits)
+    return Ledger(kc, ko, ks, vc, vo, vs, start_pos, bits=bits)
 
 
-def pack_codes(codes: np.ndarray) -> np.ndarray:
-    """Canonical 2-bit packing of a [..., d] code array: element c of a row goes to
-    byte c // 4, bits 2*(c % 4) .. 2*(c % 4) + 1."""
+def pack_codes(codes: np.ndarray, bits: int = 2) -> np.ndarray:
+    """Canonical packing of a [..., d] code array, 8/bits codes per byte: element c of
+    a row goes to byte c // (8/bits), bits bits*(c % (8/bits)) upward."""
+    per = 8 // bits
     c = codes.astype(np.uint8)
     d = c.shape[-1]
-    c = c.reshape(c.shape[:-1] + (d // 4, 4))
-    return (c[..., 0] | (c[..., 1] << 2) | (c[..., 2] << 4) | (c[..., 3] << 6)).astype(np.uint8)
+    c = c.reshape(c.shape[:-1] + (d // per, per))
+    out = np.zeros(c.shape[:-1], dtype=np.uint8)
+    for i in range(per):
+        out |= (c[..., i] << (bits * i)).astype(np.uint8)
+    return out
 
 
 def canonical_ledger_bytes(led: Ledger) -> bytes:
-    """Per KV head: K codes [W][d/4], V codes [W][d/4], K off [d], K scl [d],
+    """Per KV head: K codes [W][d*b/8], V codes [W][d*b/8], K off [d], K scl [d],
     V off [W], V scl [W] (fp16 little endian); heads back to back."""
     out = bytearray()
     for h in range(led.k_codes.shape[0]):
-        out += pack_codes(led.k_codes[h]).tobytes()
-        out += pack_codes(led.v_codes[h]).tobytes()
+        out += pack_codes(led.k_codes[h], led.bits).tobytes()
+        out += pack_codes(led.v_codes[h], led.bits).tobytes()
         out += led.k_off[h].astype(np.float16).tobytes()
         out += led.k_scl[h].astype(np.float16).tobytes()
         out += led.v_off[h].astype(np.float16).tobytes()
@@ -490,7 +504,7 @@ class UnitOracle:
             if W.state != QUANT:
                 ctr["demoted"] += 1
                 if W.ledger is None:
-                    W.ledger = quantize_window(W.k, W.v, self.win_start(w))
+                    W.ledger = quantize_window(W.k, W.v, self.win_start(w), cfg.quant_bits)
                     ctr["packed"] += 1
                 else:
                     assert W.ledger.dormant

@@ -57,17 +57,18 @@ def _bf16_group(rng, n, scale=1.0):
 
 @settings(max_examples=300, deadline=None)
 @given(st.integers(0, 2 ** 31 - 1), st.sampled_from([1e-6, 1e-3, 0.5, 1.0, 10.0, 300.0]),
-       st.sampled_from([4, 16, 32, 64, 128]))
-def test_group_quantization_exact_definition(seed, scale, n):
+       st.sampled_from([4, 16, 32, 64, 128]), st.sampled_from([2, 4]))
+def test_group_quantization_exact_definition(seed, scale, n, bits):
     rng = np.random.default_rng(seed)
     x = _bf16_group(rng, n, scale)
-    codes, off, scl = O.quantize_groups(x[None, :], axis=1)
+    L = 2 ** bits - 1
+    codes, off, scl = O.quantize_groups(x[None, :], axis=1, bits=bits)
     codes, off, scl = codes[0], float(off[0]), float(scl[0])
     mn, mx = Fraction(float(x.min())), Fraction(float(x.max()))
-    # off is the largest fp16 value <= min; scl the smallest fp16 value >= (max - off) / 3
+    # off is the largest fp16 value <= min; scl the smallest fp16 value >= (max - off) / L
     i = np.searchsorted(ALL_FP16, float(x.min()), side="right") - 1
     assert off == ALL_FP16[i] and Fraction(off) <= mn
-    target = (mx - Fraction(off)) / 3
+    target = (mx - Fraction(off)) / L
     cand = [f for f in ALL_FP16[np.searchsorted(ALL_FP16, float(target)) - 2:][:6] if Fraction(f) >= target]
     assert scl == min(cand)
     # nearest level, ties to the upper level, found by brute force in exact arithmetic
@@ -75,9 +76,9 @@ def test_group_quantization_exact_definition(seed, scale, n):
         if scl == 0:
             assert c == 0
             continue
-        dist = [abs(Fraction(float(xi)) - (Fraction(off) + k * Fraction(scl))) for k in range(4)]
+        dist = [abs(Fraction(float(xi)) - (Fraction(off) + k * Fraction(scl))) for k in range(L + 1)]
         best = min(dist)
-        assert c == max(k for k in range(4) if dist[k] == best)
+        assert c == max(k for k in range(L + 1) if dist[k] == best)
     # round-trip bound |x - x_hat| <= scl / 2, exact
     xh = O.dequantize(codes[None, :], np.array([off]), np.array([scl]), axis=1)[0]
     for xi, yi in zip(x, xh):
@@ -91,6 +92,30 @@ def test_exactly_recoverable_group():
     assert o[0] == off and sc[0] == s
     np.testing.assert_array_equal(codes[0], [0, 1, 2, 3, 3, 0, 2, 1])
     np.testing.assert_array_equal(O.dequantize(codes, o, sc, axis=1)[0], x)
+
+
+def test_int4_exactly_recoverable_group_uses_all_sixteen_levels():
+    off, s = -3.0, 0.25
+    ks = [0, 15, 7, 8, 1, 14, 3, 12, 5, 10, 2, 13, 4, 11, 6, 9]
+    x = np.array([off + k * s for k in ks])
+    codes, o, sc = O.quantize_groups(x[None], axis=1, bits=4)
+    assert o[0] == off and sc[0] == s
+    np.testing.assert_array_equal(codes[0], ks)
+    np.testing.assert_array_equal(O.dequantize(codes, o, sc, axis=1)[0], x)
+
+
+def test_int4_midpoints_round_up_and_error_shrinks():
+    """Half-way values take the upper of the 16 levels; on the same group the INT4
+    reconstruction error bound scl/2 is a fifth of the INT2 one (range / 15 vs / 3)."""
+    x = np.array([[0.0, 0.5, 1.5, 13.5, 14.5, 15.0, 7.0]])
+    codes, o, sc = O.quantize_groups(x, axis=1, bits=4)
+    assert o[0] == 0.0 and sc[0] == 1.0
+    np.testing.assert_array_equal(codes[0], [0, 1, 2, 14, 15, 15, 7])
+    rng = np.random.default_rng(9)
+    y = O.to_bf16(rng.standard_normal((64, 32)))
+    _, _, s2 = O.quantize_groups(y, axis=1, bits=2)
+    _, _, s4 = O.quantize_groups(y, axis=1, bits=4)
+    assert np.all(s4 * 5 <= s2 * (1 + 2.0 ** -9)) and np.all(s4 * 5 >= s2 * (1 - 2.0 ** -9))
 
 
 def test_midpoints_round_up():
@@ -138,6 +163,25 @@ def test_pack_codes_bit_layout():
     assert packed.tolist() == [[0b00111001, 0xFF]]
 
 
+def test_pack_codes_int4_bit_layout():
+    codes = np.array([[1, 15, 0, 9]], dtype=np.uint8)
+    assert O.pack_codes(codes, 4).tolist() == [[0xF1, 0x90]]
+
+
+def test_canonical_bytes_int4_sizes():
+    rng = np.random.default_rng(3)
+    H, W, d = 2, 16, 64
+    k = O.to_bf16(rng.standard_normal((H, W, d)))
+    v = O.to_bf16(rng.standard_normal((H, W, d)))
+    led = O.quantize_window(k, v, 0, bits=4)
+    assert led.k_codes.max() > 3 and led.k_codes.max() <= 15
+    blob = O.canonical_ledger_bytes(led)
+    per_head = 2 * W * d // 2 + 4 * d + 4 * W
+    assert len(blob) == H * per_head
+    # the first K code byte holds tokens 0's channels 0 and 1, low nibble first
+    assert blob[0] == int(led.k_codes[0, 0, 0]) | (int(led.k_codes[0, 0, 1]) << 4)
+
+
 def test_canonical_bytes_layout_sizes():
     rng = np.random.default_rng(2)
     H, W, d = 3, 16, 64
@@ -157,3 +201,5 @@ def test_range_error_on_huge_values():
     k[0, 0, 0] = 70000.0
     with pytest.raises(O.RangeError):
         O.quantize_window(k, np.zeros((1, 4, 4)), 0)
+    with pytest.raises(ValueError):
+        O.quantize_groups(np.zeros((1, 4)), axis=1, bits=3)

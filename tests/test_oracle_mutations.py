@@ -98,4 +98,22 @@ def test_requantizing_on_redemotion_is_caught(monkeypatch):
         return real_route(self, *a, **kw)
 
     monkeypatch.setattr(O.UnitOracle, "route", requant)
-    _fails(TS.test_write_once_ledger_and_promoted_values)
+    _fails(TS.test_write_once_ledger_and_promoted_values, 2)
+
+
+def test_int4_with_int2_divisor_is_caught(monkeypatch):
+    real = O.quantize_groups
+
+    def three_levels(x, axis, bits=2):
+        codes, off, scl = real(x, axis, 2)                  # the 4-bit request answered with INT2
+        return codes, off, scl
+
+    monkeypatch.setattr(O, "quantize_groups", three_levels)
+    _fails(TC.test_int4_exactly_recoverable_group_uses_all_sixteen_levels)
+
+
+def test_int4_bytes_counted_as_int2_are_caught(monkeypatch):
+    real = O.quant_window_bytes
+    monkeypatch.setattr(O, "quant_window_bytes",
+                        lambda cfg: real(O.OracleConfig(**{**cfg.__dict__, "quant_bits": 2})))
+    _fails(TS.test_quantized_window_bytes_equal_the_stored_record, 4)

@@ -36,14 +36,39 @@ def test_printed_diagnostic_capacities():
         assert (caps["K_f"], caps["K_q"]) == (case["K_f"], case["K_q"]), case["name"]
 
 
-def test_capacities_are_maximal_within_budget():
+@pytest.mark.parametrize("bits", [2, 4])
+def test_capacities_are_maximal_within_budget(bits):
     for wl in WL.ALL_WORKLOADS:
-        cfg = cfg_from(wl)
+        cfg = cfg_from(wl, quant_bits=bits)
         caps = O.capacities(cfg, wl.prompt_len)
         assert caps["K_f"] * caps["M_f"] <= (1 - cfg.quant_frac) * caps["B_hist"] < (caps["K_f"] + 1) * caps["M_f"]
         assert caps["K_q"] * caps["M_q"] <= cfg.quant_frac * caps["B_hist"] < (caps["K_q"] + 1) * caps["M_q"]
         used = (cfg.n_sink + cfg.n_local) * caps["b_tok"] + caps["K_f"] * caps["M_f"] + caps["K_q"] * caps["M_q"]
         assert used <= caps["B_total"]
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_quantized_window_bytes_equal_the_stored_record(bits):
+    """M_q is what a Quantized window actually stores: its canonical record (codes of
+    both tensors + fp16 parameters of every head) + a 4-byte position + the 16-byte
+    ledger entry."""
+    wl = WL.TINY
+    cfg = cfg_from(wl, quant_bits=bits)
+    rng = np.random.default_rng(4)
+    k = O.to_bf16(rng.standard_normal((cfg.h_kv, cfg.window, cfg.d)))
+    v = O.to_bf16(rng.standard_normal((cfg.h_kv, cfg.window, cfg.d)))
+    led = O.quantize_window(k, v, 0, bits=bits)
+    assert O.quant_window_bytes(cfg) == len(O.canonical_ledger_bytes(led)) + 4 + 16
+
+
+def test_int2_retains_more_windows_than_int4():
+    """[QEvict] Appendix G.3: under one byte budget INT2 keeps more historical windows
+    than INT4; the Full tier's share is the same."""
+    for wl in WL.ALL_WORKLOADS:
+        c2 = O.capacities(cfg_from(wl), wl.prompt_len)
+        c4 = O.capacities(cfg_from(wl, quant_bits=4), wl.prompt_len)
+        assert c4["K_f"] == c2["K_f"] and c4["M_q"] > c2["M_q"]
+        assert c4["K_q"] < c2["K_q"] or c2["K_q"] == 0
 
 
 def test_quant_share_goes_to_quantized_tier():
@@ -215,11 +240,12 @@ def test_router_invariants_over_a_run(rho, q):
     assert seen_evicted, "these budgets force eviction"
 
 
-def test_write_once_ledger_and_promoted_values():
+@pytest.mark.parametrize("bits", [2, 4])
+def test_write_once_ledger_and_promoted_values(bits):
     """A window taken F -> Q -> F -> Q keeps the codes of its first demotion, and a
     promoted window holds bf16(x_hat), not its original values."""
     wl = WL.TINY.with_(n_decode=0)
-    cfg = cfg_from(wl, budget_frac=0.25)          # K_f = 1, K_q = 15
+    cfg = cfg_from(wl, budget_frac=0.25, quant_bits=bits)          # K_f = 1
     qp, kp, vp = WL.prompt(wl, 0)
     unit = O.UnitOracle(cfg, 512)
     n_win = 32
@@ -238,6 +264,7 @@ def test_write_once_ledger_and_promoted_values():
     unit.route()
     assert unit.win[w].state == O.QUANT
     first = O.canonical_ledger_bytes(unit.win[w].ledger)
+    assert unit.win[w].ledger.bits == bits and unit.win[w].ledger.k_codes.max() <= 2 ** bits - 1
     # promote: bf16 of the dequantized values, ledger dormant
     unit.score[w] = 1e8
     unit.route()
