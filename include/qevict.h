@@ -66,6 +66,9 @@ typedef enum {
 #define QEVICT_F_RANK_DECAY        4u
 #define QEVICT_F_RANK_PNORM        8u
 #define QEVICT_F_RANK_KEYNORM     16u
+/* INT4 recoverable tier (App. G.3): 4-bit codes (16 levels, scl = RU_fp16((max - off)/15)),
+ * everything else as for INT2; M_q = W*H_kv*d + 4*H_kv*d + 4*W*H_kv + 20 bytes. */
+#define QEVICT_F_INT4             32u
 
 typedef struct {
     int32_t batch;        /* B sequences */

@@ -23,6 +23,7 @@ QEVICT_F_SCORE_ROUTE_ONLY = 2
 QEVICT_F_RANK_DECAY = 4      # alternative rankers ([QEvict] Appendix J); at most one
 QEVICT_F_RANK_PNORM = 8
 QEVICT_F_RANK_KEYNORM = 16
+QEVICT_F_INT4 = 32           # INT4 recoverable tier ([QEvict] Appendix G.3) instead of INT2
 
 DEV_E_POOL, DEV_E_WINDOW, DEV_E_RANGE, DEV_E_LIST = 1, 2, 4, 8
 
@@ -319,7 +320,8 @@ def parse_export(blob: bytes, cfg: Config) -> UnitExport:
     state, has_led, dorm, start = (rec["i"][:, k].copy() for k in range(4))
     score = rec["s"].copy()
     H, W, d, ns = cfg.h_kv, cfg.window, cfg.d_head, cfg.n_sink
-    slot_bytes = H * (W * d // 2 + 4 * d + 4 * W)
+    qb = 4 if cfg.flags & QEVICT_F_INT4 else 2
+    slot_bytes = H * (2 * W * d * qb // 8 + 4 * d + 4 * W)
     ledger = {}
     for w in range(nw):
         if has_led[w]:

@@ -1,6 +1,6 @@
 // Decode step, two launches per layer.  k_decode_split appends the new token to
 // its recent window and runs split-K attention over the accessible list (sinks,
-// recent windows, Full bf16 windows, Quantized INT2 windows); k_finish combines
+// recent windows, Full bf16 windows, Quantized INT2 or INT4 windows); k_finish combines
 // the splits of each query head with the global log-sum-exp, writes each
 // entry's per-head share of this step's window mass, and advances the token
 // count.  The shares are folded into the cumulative scores by the next
@@ -11,7 +11,7 @@
 // Long-Context Decoding", §4.1 (accessible-set attention, scale 1/sqrt(d_kv);
 // Quantized windows are dequantized in the execution datatype as
 // off + scl * code, Eq. 5), §4.2 Eq. 1 (cumulative window score, averaged over
-// the H_q query heads).
+// the H_q query heads); Appendix G.3 (the 4-bit recoverable tier).
 //
 // Work split: one workgroup per (split, KV head, sequence); the G query heads of
 // the GQA group share every K/V load.  All contractions run on 16x16 MFMA tiles
@@ -19,8 +19,10 @@
 // so that bf16 operands can carry fp32-accurate values as a sum of two bf16
 // parts (query times K scale on the key side, probability times V scale on the
 // value side).  With G <= 4 the 16 columns hold two independent column slots,
-// so one wave job covers two INT2 windows at once and the softmax arithmetic of
-// both runs in the same instructions.
+// so one wave job covers two Quantized windows at once and the softmax arithmetic
+// of both runs in the same instructions.  The code width (2 or 4 bits) is a
+// template parameter: it changes only how many code bytes a lane loads and how a
+// byte expands into bf16 integers (4 codes of 2 bits or 2 of 4 bits per lookup).
 #include <float.h>
 #include <hip/hip_ext.h>
 
@@ -183,7 +185,7 @@ __device__ __forceinline__ void stw(void* p, const uint32_t* w) {
 
 // Static shape of one instantiation: head dim D, query heads per KV head G,
 // tiles per 32-token chunk TPC (1 for 16-token windows, else 2).
-template <int D, int G, int TPC>
+template <int D, int G, int TPC, int BITS>
 struct DecShape {
     static constexpr int CQ = D / 4;                 // channels per lane group (key side)
     static constexpr int KS = D / 32;                // 32-channel MFMA steps (key side)
@@ -193,10 +195,10 @@ struct DecShape {
     static constexpr int ROWS = NSLOT * G;           // (item, head) rows of the query-times-scale products
     static constexpr int LPR = 64 / ROWS;            // lanes per product row
     static constexpr int CPL = D / LPR;              // channels per lane in the products
-    static constexpr int NV = 4 * TPC;               // scores per lane per INT2 item
-    // INT2 job words per lane: K codes and V codes of every item, V offsets / scales of
-    // the lane's own item, K scales / offsets of the lane's product channels
-    static constexpr int KCW = TPC * CQ / 16, VCW = MB * TPC / 4, VPW = 2 * TPC, KPW = CPL / 2;
+    static constexpr int NV = 4 * TPC;               // scores per lane per quantized item
+    // quantized job words per lane (BITS-bit codes): K codes and V codes of every item,
+    // V offsets / scales of the lane's own item, K scales / offsets of the lane's product channels
+    static constexpr int KCW = TPC * CQ * BITS / 32, VCW = MB * TPC * BITS / 8, VPW = 2 * TPC, KPW = CPL / 2;
     static constexpr int O_VC = NSLOT * KCW, O_VO = O_VC + NSLOT * VCW, O_VS = O_VO + VPW, O_KS = O_VS + VPW,
                          O_KO = O_KS + KPW, QW = O_KO + KPW;
     // bf16 tile job words per lane: K row (CQ bf16) then V (MB blocks x 4 tokens)
@@ -216,14 +218,14 @@ struct Job {
     int i, t, kind, idx, ntok, Wn, start;   // bf16: entry, tile, kind, page id, valid tokens, block width, position 0
 };
 
-template <int D, int G, int TPC>
+template <int D, int G, int TPC, int BITS>
 __global__ void __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(2)))
 k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, const uint16_t* __restrict__ knew,
                const uint16_t* __restrict__ vnew) {
-    using S = DecShape<D, G, TPC>;
+    using S = DecShape<D, G, TPC, BITS>;
     constexpr int CQ = S::CQ, KS = S::KS, MB = S::MB, NSLOT = S::NSLOT, SW = S::SW, LPR = S::LPR, CPL = S::CPL;
     constexpr int NV = S::NV, QSTR = S::QSTR;
-    __shared__ uint2 lut[256];                                           // code byte -> 4 bf16 {0..3}
+    __shared__ uint2 lut[256];            // code byte -> its 4 (INT2) or 2 (INT4, in .x) codes as bf16 integers
     // per wave: rows 0-15 the INT2 query operand of the current job, rows 16-31 the
     // bf16 query operand (every live column holds its head's query, exact bf16), row 32 zeros
     __shared__ __attribute__((aligned(16))) uint16_t qs[DW][33][QSTR];
@@ -265,11 +267,15 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             kn = reinterpret_cast<const uint32_t*>(knew + ((int64_t)b * g.h_kv + hk) * D)[lane];
             vn = reinterpret_cast<const uint32_t*>(vnew + ((int64_t)b * g.h_kv + hk) * D)[lane];
         }
-        // 4 packed 2-bit codes -> 4 bf16 {0, 1, 2, 3}: one table at a fixed LDS address, so a
-        // lookup is one shift of the code byte with the base in the read's immediate offset
+        // a code byte -> its codes as bf16 integers (4 of 2 bits, or 2 of 4 bits): one table
+        // at a fixed LDS address, so a lookup is one shift of the code byte with the base in
+        // the read's immediate offset
         for (int x = threadIdx.x; x < 256; x += 64 * DW) {
-            auto bv = [](int c) -> uint32_t { return c == 0 ? 0u : (c == 1 ? 0x3F80u : (c == 2 ? 0x4000u : 0x4040u)); };
-            lut[x] = make_uint2(bv(x & 3) | (bv((x >> 2) & 3) << 16), bv((x >> 4) & 3) | (bv((x >> 6) & 3) << 16));
+            auto bv = [](int c) -> uint32_t { return __float_as_uint((float)c) >> 16; };   // exact for c < 256
+            if constexpr (BITS == 2)
+                lut[x] = make_uint2(bv(x & 3) | (bv((x >> 2) & 3) << 16), bv((x >> 4) & 3) | (bv((x >> 6) & 3) << 16));
+            else
+                lut[x] = make_uint2(bv(x & 15) | (bv(x >> 4) << 16), 0u);
         }
         stw<CQ / 2>(&qs[wave][16 + n][CQ * qg], w);
         if (lane < D / 8) reinterpret_cast<uint4*>(&qs[wave][32][0])[lane] = make_uint4(0u, 0u, 0u, 0u);
@@ -375,19 +381,23 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     };
     // Every load address is a wave-uniform base (SGPRs) plus an unsigned 32-bit lane
     // offset, which the hardware adds itself (global loads with an SGPR base).
-    const uint32_t kc_lane = (uint32_t)((n * 4 + qg) * TPC * (CQ / 4));           // K codes: token row n, group qg
-    const uint32_t vc_lane = (uint32_t)(W * D / 4 + (n * 4 + qg) * NCH * MB * TPC); // V codes: channel row n
-    const uint32_t vp_lane = (uint32_t)(W * D / 2 + 4 * D + qg * NT * 8);         // V offsets (V scales + 2W)
-    const uint32_t kp_lane = (uint32_t)(W * D / 2 + CPL * pcb * 2);               // K offsets (K scales + 2D)
+    // (code bytes: a lane's K row of a tile is CQ*BITS/8 bytes, its V bytes per channel
+    // block and tile BITS/2; one tensor's codes W*D*BITS/8)
+    constexpr int KRB = CQ * BITS / 8, VTB = BITS / 2;
+    const uint32_t cbytes = (uint32_t)(W * D * BITS / 8);
+    const uint32_t kc_lane = (uint32_t)((n * 4 + qg) * TPC * KRB);                    // K codes: token row n, group qg
+    const uint32_t vc_lane = cbytes + (uint32_t)((n * 4 + qg) * NCH * MB * TPC * VTB); // V codes: channel row n
+    const uint32_t vp_lane = 2 * cbytes + (uint32_t)(4 * D + qg * NT * 8);            // V offsets (V scales + 2W)
+    const uint32_t kp_lane = 2 * cbytes + (uint32_t)(CPL * pcb * 2);                  // K offsets (K scales + 2D)
     auto load_q = [&](const Job& j, Raw& R) __attribute__((always_inline)) {
         const uint32_t oa = (uint32_t)j.sa * (uint32_t)g.slot_bytes, ob = (uint32_t)j.sb * (uint32_t)g.slot_bytes;
-        const uint8_t* ca = slots + oa + (uint32_t)(j.c * 16 * 4 * TPC * (CQ / 4));   // chunk c of item a
-        const uint8_t* cb = slots + ob + (uint32_t)(j.c * 16 * 4 * TPC * (CQ / 4));
+        const uint8_t* ca = slots + oa + (uint32_t)(j.c * 16 * 4 * TPC * KRB);   // chunk c of item a
+        const uint8_t* cb = slots + ob + (uint32_t)(j.c * 16 * 4 * TPC * KRB);
         ldw<S::KCW>(R.w, ca + kc_lane);
-        ldw<S::VCW>(R.w + S::O_VC, slots + oa + (uint32_t)(j.c * MB * TPC) + vc_lane);
+        ldw<S::VCW>(R.w + S::O_VC, slots + oa + (uint32_t)(j.c * MB * TPC * VTB) + vc_lane);
         if constexpr (NSLOT == 2) {
             ldw<S::KCW>(R.w + S::KCW, cb + kc_lane);
-            ldw<S::VCW>(R.w + S::O_VC + S::VCW, slots + ob + (uint32_t)(j.c * MB * TPC) + vc_lane);
+            ldw<S::VCW>(R.w + S::O_VC + S::VCW, slots + ob + (uint32_t)(j.c * MB * TPC * VTB) + vc_lane);
         }
         // the lane's own item (V parameters) and the item of its products (K parameters)
         const uint32_t oo = (slot == 0 ? oa : ob) + vp_lane + (uint32_t)(TPC * j.c * 8);
@@ -443,9 +453,48 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         const uint32_t r = bf16x2_rne(x0, x1);
         return bf16x2_rne(fmaf(-lof, bf16lo(r), x0), fmaf(-lof, bf16hi(r), x1));
     };
-    auto lut4 = [&](uint32_t w, int byte) -> u2_t {
+    auto lut4 = [&](uint32_t w, int byte) -> u2_t {   // INT2: 4 codes of one byte
         const uint2 a = lut[(w >> (8 * byte)) & 0xffu];
         return u2_t{a.x, a.y};
+    };
+    auto lut2 = [&](uint32_t w, int byte) -> uint32_t {   // INT4: 2 codes of one byte
+        return lut[(w >> (8 * byte)) & 0xffu].x;
+    };
+    // MFMA A operands from a lane's code words.  Key side, tile tc, 32-channel step ks:
+    // channels CQ*qg + 8ks .. + 7 of the lane's token row.  Value side, channel block m:
+    // tokens 4*qg .. + 3 of each tile of the chunk (zeros in the second half when TPC = 1).
+    auto key_codes = [&](const uint32_t* w, int tc, int ks) __attribute__((always_inline)) -> u4_t {
+        if constexpr (BITS == 2) {
+            const int by = tc * (CQ / 4) + 2 * ks;
+            const uint32_t x = w[by >> 2];
+            const u2_t a0 = lut4(x, by & 3), a1 = lut4(x, (by & 3) + 1);
+            return u4_t{a0.x, a0.y, a1.x, a1.y};
+        } else {
+            const uint32_t x = w[tc * (CQ / 8) + ks];
+            return u4_t{lut2(x, 0), lut2(x, 1), lut2(x, 2), lut2(x, 3)};
+        }
+    };
+    auto value_codes = [&](const uint32_t* w, int m) __attribute__((always_inline)) -> u4_t {
+        if constexpr (BITS == 2) {
+            if constexpr (TPC == 2) {
+                const int by = 2 * m;
+                const uint32_t x = w[by >> 2];
+                const u2_t a0 = lut4(x, by & 3), a1 = lut4(x, (by & 3) + 1);
+                return u4_t{a0.x, a0.y, a1.x, a1.y};
+            } else {
+                const u2_t a0 = lut4(w[m >> 2], m & 3);
+                return u4_t{a0.x, a0.y, 0u, 0u};
+            }
+        } else {
+            if constexpr (TPC == 2) {
+                const uint32_t x = w[m];
+                return u4_t{lut2(x, 0), lut2(x, 1), lut2(x, 2), lut2(x, 3)};
+            } else {
+                const uint32_t x = w[m >> 1];
+                const int by = 2 * (m & 1);
+                return u4_t{lut2(x, by), lut2(x, by + 1), 0u, 0u};
+            }
+        }
     };
     auto lse_store = [&](bool mine, int ie) {
         const float t = qg_sum(lw);
@@ -496,15 +545,8 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             f4_t d = {c0, c0, c0, c0};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int by = tc * (CQ / 4) + 2 * ks;
-                const uint32_t wa = R.w[by >> 2];
-                const u2_t a0 = lut4(wa, by & 3), a1 = lut4(wa, (by & 3) + 1);
-                d = mfma32(u4_t{a0.x, a0.y, a1.x, a1.y}, bqa[ks], d);
-                if constexpr (NSLOT == 2) {
-                    const uint32_t wb = R.w[S::KCW + (by >> 2)];
-                    const u2_t b0 = lut4(wb, by & 3), b1 = lut4(wb, (by & 3) + 1);
-                    d = mfma32(u4_t{b0.x, b0.y, b1.x, b1.y}, bqb[ks], d);
-                }
+                d = mfma32(key_codes(R.w, tc, ks), bqa[ks], d);
+                if constexpr (NSLOT == 2) d = mfma32(key_codes(R.w + S::KCW, tc, ks), bqb[ks], d);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) s[4 * tc + i] = d[i] + mirror<SW>(d[i]);   // high + low query parts
@@ -537,34 +579,10 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         }
         // (5) O^T[channel][column] += codes^T . P'
 #pragma unroll
-        for (int m = 0; m < MB; ++m) {
-            u4_t a;
-            if constexpr (TPC == 2) {
-                const int by = 2 * m;
-                const uint32_t w = R.w[S::O_VC + (by >> 2)];
-                const u2_t a0 = lut4(w, by & 3), a1 = lut4(w, (by & 3) + 1);
-                a = u4_t{a0.x, a0.y, a1.x, a1.y};
-            } else {
-                const u2_t a0 = lut4(R.w[S::O_VC + (m >> 2)], m & 3);
-                a = u4_t{a0.x, a0.y, 0u, 0u};
-            }
-            acc[m] = mfma32(a, pa, acc[m]);
-        }
+        for (int m = 0; m < MB; ++m) acc[m] = mfma32(value_codes(R.w + S::O_VC, m), pa, acc[m]);
         if (NSLOT == 2 && j.ib >= 0) {
 #pragma unroll
-            for (int m = 0; m < MB; ++m) {
-                u4_t a;
-                if constexpr (TPC == 2) {
-                    const int by = 2 * m;
-                    const uint32_t w = R.w[S::O_VC + S::VCW + (by >> 2)];
-                    const u2_t a0 = lut4(w, by & 3), a1 = lut4(w, (by & 3) + 1);
-                    a = u4_t{a0.x, a0.y, a1.x, a1.y};
-                } else {
-                    const u2_t a0 = lut4(R.w[S::O_VC + S::VCW + (m >> 2)], m & 3);
-                    a = u4_t{a0.x, a0.y, 0u, 0u};
-                }
-                acc[m] = mfma32(a, pb, acc[m]);
-            }
+            for (int m = 0; m < MB; ++m) acc[m] = mfma32(value_codes(R.w + S::O_VC + S::VCW, m), pb, acc[m]);
         }
         // (6) both windows end on their last chunk: log-sum-exp of their mass per head
         if (j.c + 1 == NCH) lse_store(slot == 0 || j.ib >= 0, slot == 0 ? j.ia : j.ib);
@@ -741,20 +759,22 @@ hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t
                          const uint16_t* v_new, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const dim3 grid(g.n_splits, g.h_kv, g.B), block(64 * DW);
     const int G = g.h_q / g.h_kv, TPC = lay_tpc(g.W);
-#define QV_DEC(D_, G_, T_)                                                                     \
-    if (g.d == D_ && G == G_ && TPC == T_) {                                                   \
+#define QV_DEC1(D_, G_, T_, B_)                                                                \
+    if (g.d == D_ && G == G_ && TPC == T_ && g.qbits == B_) {                                  \
         if (ev0)                                                                               \
-            hipExtLaunchKernelGGL((k_decode_split<D_, G_, T_>), grid, block, 0, s, ev0, ev1, 0, g, bf, layer, q, \
-                                  k_new, v_new);                                               \
+            hipExtLaunchKernelGGL((k_decode_split<D_, G_, T_, B_>), grid, block, 0, s, ev0, ev1, 0, g, bf, layer, \
+                                  q, k_new, v_new);                                            \
         else                                                                                   \
-            hipLaunchKernelGGL((k_decode_split<D_, G_, T_>), grid, block, 0, s, g, bf, layer, q, k_new, v_new); \
+            hipLaunchKernelGGL((k_decode_split<D_, G_, T_, B_>), grid, block, 0, s, g, bf, layer, q, k_new, v_new); \
         return hipGetLastError();                                                              \
     }
+#define QV_DEC(D_, G_, T_) QV_DEC1(D_, G_, T_, 2) QV_DEC1(D_, G_, T_, 4)
     QV_DEC(128, 1, 2) QV_DEC(128, 2, 2) QV_DEC(128, 4, 2) QV_DEC(128, 8, 2)
     QV_DEC(64, 1, 2) QV_DEC(64, 2, 2) QV_DEC(64, 4, 2) QV_DEC(64, 8, 2)
     QV_DEC(128, 1, 1) QV_DEC(128, 2, 1) QV_DEC(128, 4, 1) QV_DEC(128, 8, 1)
     QV_DEC(64, 1, 1) QV_DEC(64, 2, 1) QV_DEC(64, 4, 1) QV_DEC(64, 8, 1)
 #undef QV_DEC
+#undef QV_DEC1
     return hipErrorInvalidValue;
 }
 

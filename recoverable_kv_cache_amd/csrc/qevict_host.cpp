@@ -81,7 +81,8 @@ qevict_status caps_of(const qevict_config* c, int32_t prompt_len, Caps* out) {
     const double B_hist = B_total - (double)((int64_t)(c->n_sink + c->n_local) * b_tok);
     const int64_t W = c->window, H = c->h_kv, d = c->d_head;
     const int64_t M_f = W * b_tok + 8;
-    const int64_t M_q = W * H * d / 2 + 4 * H * d + 4 * W * H + 4 + 16;
+    const int64_t qb = (c->flags & QEVICT_F_INT4) ? 4 : 2;   // bits per code
+    const int64_t M_q = 2 * W * H * d * qb / 8 + 4 * H * d + 4 * W * H + 4 + 16;
     out->B_total = B_total;
     out->B_hist = B_hist;
     out->M_f = M_f;
@@ -143,7 +144,8 @@ qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, La
     if (ns > ns_max) ns = ns_max;
     g.n_splits = ns;
     g.page_elems = g.h_kv * 2 * g.W * g.d;
-    g.slot_head_bytes = g.W * g.d / 2 + 4 * g.d + 4 * g.W;
+    g.qbits = (c->flags & QEVICT_F_INT4) ? 4 : 2;
+    g.slot_head_bytes = 2 * lay_code_bytes(g.W, g.d, g.qbits) + 4 * g.d + 4 * g.W;
     g.slot_bytes = g.h_kv * g.slot_head_bytes;
     g.sink_elems = g.h_kv * 2 * sink_width(g.n_sink) * g.d;
     const size_t U = (size_t)g.B * g.L;
@@ -516,13 +518,14 @@ qevict_status qevict_export_unit(qevict_state* st, int32_t layer, int32_t b, voi
             for (int h = 0; h < g.h_kv; ++h) {
                 const uint8_t* src = sl + (size_t)h * g.slot_head_bytes;
                 uint8_t* dst = canon.data() + (size_t)h * g.slot_head_bytes;
-                const int cb = g.W * g.d / 4;
+                const int qb = g.qbits, P = 8 / qb, mask = (1 << qb) - 1;
+                const int cb = lay_code_bytes(g.W, g.d, qb);
                 for (int t = 0; t < g.W; ++t)
                     for (int c = 0; c < g.d; ++c) {
-                        const int kc = (src[lay_kc_byte(t, c, g.d, g.W)] >> lay_kc_shift(c)) & 3;
-                        const int vc = (src[cb + lay_vc_byte(t, c, g.d, g.W)] >> lay_vc_shift(t)) & 3;
-                        dst[t * (g.d / 4) + c / 4] |= (uint8_t)(kc << (2 * (c % 4)));
-                        dst[cb + t * (g.d / 4) + c / 4] |= (uint8_t)(vc << (2 * (c % 4)));
+                        const int kc = (src[lay_kc_byte(t, c, g.d, g.W, qb)] >> lay_kc_shift(c, qb)) & mask;
+                        const int vc = (src[cb + lay_vc_byte(t, c, g.d, g.W, qb)] >> lay_vc_shift(t, qb)) & mask;
+                        dst[t * (g.d / P) + c / P] |= (uint8_t)(kc << (qb * (c % P)));
+                        dst[cb + t * (g.d / P) + c / P] |= (uint8_t)(vc << (qb * (c % P)));
                     }
                 memcpy(dst + 2 * cb, src + 2 * cb, (size_t)4 * g.d);     // K offset, K scale
                 const uint16_t* ov = (const uint16_t*)(src + 2 * cb + 4 * g.d);

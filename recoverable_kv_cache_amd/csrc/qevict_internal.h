@@ -78,10 +78,11 @@ struct Geo {
     int32_t S_max;        // prompt buffer row stride
     int32_t n_windows, n_pages, n_slots, n_acc_max, n_splits;
     int32_t page_elems;   // bf16 elements per page = h_kv * 2 * W * d
-    int32_t slot_head_bytes;  // W*d/2 + 4d + 4W
+    int32_t slot_head_bytes;  // 2 * code_bytes + 4d + 4W
     int32_t slot_bytes;   // h_kv * slot_head_bytes
     int32_t sink_elems;   // h_kv * 2 * Ws * d, Ws = sink_width(n_sink)
     uint32_t flags;
+    int32_t qbits;        // bits per Quantized-tier code: 2, or 4 with QEVICT_F_INT4
 };
 
 // Device pointers to the per-unit arrays (index by unit = b * L + l).
@@ -130,10 +131,12 @@ constexpr int SPLIT_BLOCK = 64;
 //             (a lane reads the CQ channels of its token row for every tile of a chunk)
 //   V (t, c): ((((c%16)*4 + r/4)*NT + tile)*MB + c/16)*4 + r%4
 //             (a lane reads, per tile, 4 tokens x MB channel blocks of one channel row)
-// INT2 slot of one head (same byte count as the canonical record):
-//   K codes [W*D/4]: code (t, c) in byte (((ch*16 + r)*4 + qg)*TPC + tc)*(CQ/4) + cc/4, bits 2*(cc%4)
-//   V codes [W*D/4]: code (t, c) in byte ((((c%16)*4 + r/4)*NCH + ch)*MB + c/16)*TPC + tc, bits 2*(r%4)
-//             (a lane reads, per chunk, MB x TPC bytes: 4 tokens of each tile of the chunk per channel block)
+// Quantized slot of one head, b-bit codes (b = 2 or 4, P = 8/b codes per byte; same byte
+// count as the canonical record):
+//   K codes [W*D*b/8]: code (t, c) in byte (((ch*16 + r)*4 + qg)*TPC + tc)*(CQ/P) + cc/P, bits b*(cc%P)
+//   V codes [W*D*b/8]: code (t, c) in byte (((((c%16)*4 + r/4)*NCH + ch)*MB + c/16)*TPC + tc)*(4/P) + (r%4)/P,
+//             bits b*(r%P) (a lane reads, per chunk, MB x TPC x 4/P bytes: the 4 tokens of row group
+//             r/4 of each tile of the chunk, per channel block)
 //   K offset [D], K scale [D] (fp16, channel order), V offset [W], V scale [W] (fp16) with
 //   token t at ((r/4)*NT + tile)*4 + r%4.
 __host__ __device__ inline int lay_tpc(int W) { return (W < 32 ? W : 32) / 16; }
@@ -146,18 +149,21 @@ __host__ __device__ inline int lay_v(int t, int c, int D, int W) {
     const int NT = W / 16, MB = D / 16;
     return ((((c & 15) * 4 + (t & 15) / 4) * NT + (t >> 4)) * MB + c / 16) * 4 + (t & 3);
 }
-__host__ __device__ inline int lay_kc_byte(int t, int c, int D, int W) {
-    const int CQ = D / 4, TPC = lay_tpc(W);
+__host__ __device__ inline int lay_kc_byte(int t, int c, int D, int W, int b) {
+    const int CQ = D / 4, TPC = lay_tpc(W), P = 8 / b;
     const int ch = t / (16 * TPC), tc = (t / 16) % TPC, r = t & 15;
-    return (((ch * 16 + r) * 4 + c / CQ) * TPC + tc) * (CQ / 4) + (c % CQ) / 4;
+    return (((ch * 16 + r) * 4 + c / CQ) * TPC + tc) * (CQ / P) + (c % CQ) / P;
 }
-__host__ __device__ inline int lay_kc_shift(int c) { return 2 * (c & 3); }
-__host__ __device__ inline int lay_vc_byte(int t, int c, int D, int W) {
-    const int TPC = lay_tpc(W), NCH = W / (16 * TPC), MB = D / 16;
+__host__ __device__ inline int lay_kc_shift(int c, int b) { return b * (c % (8 / b)); }
+__host__ __device__ inline int lay_vc_byte(int t, int c, int D, int W, int b) {
+    const int TPC = lay_tpc(W), NCH = W / (16 * TPC), MB = D / 16, P = 8 / b;
     const int tile = t >> 4;
-    return ((((c & 15) * 4 + (t & 15) / 4) * NCH + tile / TPC) * MB + c / 16) * TPC + tile % TPC;
+    return (((((c & 15) * 4 + (t & 15) / 4) * NCH + tile / TPC) * MB + c / 16) * TPC + tile % TPC) * (4 / P) +
+           (t & 3) / P;
 }
-__host__ __device__ inline int lay_vc_shift(int t) { return 2 * (t & 3); }
+__host__ __device__ inline int lay_vc_shift(int t, int b) { return b * (t % (8 / b)); }
+// bytes of one tensor's codes of one head
+__host__ __device__ inline int lay_code_bytes(int W, int D, int b) { return W * D * b / 8; }
 __host__ __device__ inline int lay_vp(int t, int W) {
     const int NT = W / 16;
     return (((t & 15) / 4) * NT + (t >> 4)) * 4 + (t & 3);

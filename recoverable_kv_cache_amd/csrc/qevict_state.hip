@@ -582,18 +582,32 @@ hipError_t launch_route(const Geo& g, const Bufs& bf, int layer, int mode, hipSt
     return hipGetLastError();
 }
 
-// ------------------------------------------------------------------------------------ pack (INT2, once)
+// ------------------------------------------------------------------------------------ pack (INT2 / INT4, once)
 // Keys: per (head, channel) over the window's tokens; values: per (head, token)
-// over channels.  off = RD_fp16(min), scl = RU_fp16((max - off)/3), code =
-// #{k in 1..3 : 2(x - off) >= (2k-1) scl}, 0 when scl == 0.  All comparisons in
+// over channels.  With L = 2^b - 1 levels (b = 2, or 4 for the INT4 tier):
+// off = RD_fp16(min), scl = RU_fp16((max - off)/L), code =
+// #{k in 1..L : 2(x - off) >= (2k-1) scl}, 0 when scl == 0.  All comparisons in
 // fp64, where they are exact for bf16 x and fp16 off/scl.
 constexpr int PK_THREADS = 256;
 constexpr int PK_MAXE = 64 * 128;   // W * d
+
+// #{k in 1..L : t >= (2k - 1) scl} for t = 2(x - off) >= 0: the nearest of the levels
+// 0..L, ties up.  A quotient gives the estimate; exact fp64 comparisons with the
+// thresholds on either side settle it.
+__device__ inline int nearest_level(double t, double scl, int L) {
+    if (scl == 0.0) return 0;
+    int k = (int)floor((t / scl + 1.0) * 0.5);
+    k = k < 0 ? 0 : (k > L ? L : k);
+    while (k < L && t >= (double)(2 * k + 1) * scl) ++k;
+    while (k > 0 && t < (double)(2 * k - 1) * scl) --k;
+    return k;
+}
 
 __global__ void __launch_bounds__(PK_THREADS) k_pack(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ kp,
                                                      const uint16_t* __restrict__ vp) {
     __shared__ uint16_t sk[PK_MAXE], sv[PK_MAXE];
     __shared__ uint8_t ck[PK_MAXE], cv[PK_MAXE];
+    __shared__ double p_off[128 + 64], p_scl[128 + 64];   // key channels, then value tokens
     const int l = layer >= 0 ? layer : blockIdx.x % g.L;
     const int b = layer >= 0 ? blockIdx.x : blockIdx.x / g.L;
     const int64_t u = unit_of(g, b, l);
@@ -626,67 +640,63 @@ __global__ void __launch_bounds__(PK_THREADS) k_pack(Geo g, Bufs bf, int layer, 
         __syncthreads();
         uint8_t* slot = bf.slots + u * (int64_t)g.n_slots * g.slot_bytes + (int64_t)pi.dst_slot * g.slot_bytes +
                         (int64_t)h * g.slot_head_bytes;
-        uint16_t* offK = (uint16_t*)(slot + W * d / 2);
+        const int qb = g.qbits, P = 8 / qb, L = (1 << qb) - 1, cbytes = lay_code_bytes(W, d, qb);
+        uint16_t* offK = (uint16_t*)(slot + 2 * cbytes);
         uint16_t* sclK = offK + d;
         uint16_t* offV = sclK + d;
         uint16_t* sclV = offV + W;
         bool bad = false;
-        // keys: one channel per thread
-        for (int c = threadIdx.x; c < d; c += PK_THREADS) {
-            float mn = bf16_to_f32(sk[c]), mx = mn;
-            for (int i = 1; i < W; ++i) {
-                const float x = bf16_to_f32(sk[i * d + c]);
+        // parameters: threads [0, d) take a key channel each (over the W tokens), threads
+        // [d, d + W) a value token each (over the d channels)
+        const int tid = threadIdx.x;
+        if (tid < d + W) {
+            const bool key = tid < d;
+            const int gi = key ? tid : tid - d;
+            const int n_el = key ? W : d;
+            const uint16_t* src = key ? sk + gi : sv + gi * d;
+            const int stride = key ? d : 1;
+            float mn = bf16_to_f32(src[0]), mx = mn;
+            for (int i = 1; i < n_el; ++i) {
+                const float x = bf16_to_f32(src[i * stride]);
                 mn = fminf(mn, x);
                 mx = fmaxf(mx, x);
             }
             if (fabsf(mn) > 65504.f || fabsf(mx) > 65504.f) bad = true;
             const double off = fp16_round_down((double)mn);
-            const double scl = fp16_round_up(((double)mx - off) / 3.0);
+            const double scl = fp16_round_up(((double)mx - off) / (double)L);
             if (fabs(off) > 65504.0 || scl > 65504.0) bad = true;
-            offK[c] = fp16_bits_exact(off);
-            sclK[c] = fp16_bits_exact(scl);
-            for (int i = 0; i < W; ++i) {
-                const double t = 2.0 * ((double)bf16_to_f32(sk[i * d + c]) - off);
-                int code = (t >= scl) + (t >= 3.0 * scl) + (t >= 5.0 * scl);
-                if (scl == 0.0) code = 0;
-                ck[i * d + c] = (uint8_t)code;
+            if (key) {
+                offK[gi] = fp16_bits_exact(off);
+                sclK[gi] = fp16_bits_exact(scl);
+            } else {
+                offV[lay_vp(gi, W)] = fp16_bits_exact(off);
+                sclV[lay_vp(gi, W)] = fp16_bits_exact(scl);
             }
+            p_off[tid] = off;
+            p_scl[tid] = scl;
         }
-        // values: one token per thread
-        for (int i = threadIdx.x; i < W; i += PK_THREADS) {
-            float mn = bf16_to_f32(sv[i * d]), mx = mn;
-            for (int c = 1; c < d; ++c) {
-                const float x = bf16_to_f32(sv[i * d + c]);
-                mn = fminf(mn, x);
-                mx = fmaxf(mx, x);
-            }
-            if (fabsf(mn) > 65504.f || fabsf(mx) > 65504.f) bad = true;
-            const double off = fp16_round_down((double)mn);
-            const double scl = fp16_round_up(((double)mx - off) / 3.0);
-            if (fabs(off) > 65504.0 || scl > 65504.0) bad = true;
-            offV[lay_vp(i, W)] = fp16_bits_exact(off);
-            sclV[lay_vp(i, W)] = fp16_bits_exact(scl);
-            for (int c = 0; c < d; ++c) {
-                const double t = 2.0 * ((double)bf16_to_f32(sv[i * d + c]) - off);
-                int code = (t >= scl) + (t >= 3.0 * scl) + (t >= 5.0 * scl);
-                if (scl == 0.0) code = 0;
-                cv[i * d + c] = (uint8_t)code;
-            }
+        __syncthreads();
+        // codes: every element on its own thread
+        for (int e = tid; e < W * d; e += PK_THREADS) {
+            const int i = e / d, c = e % d;
+            ck[e] = (uint8_t)nearest_level(2.0 * ((double)bf16_to_f32(sk[e]) - p_off[c]), p_scl[c], L);
+            cv[e] = (uint8_t)nearest_level(2.0 * ((double)bf16_to_f32(sv[e]) - p_off[d + i]), p_scl[d + i], L);
         }
         if (bad) atomicOr(&hdr->status, QEVICT_DEV_E_RANGE);
         __syncthreads();
-        // K codes: 4 consecutive channels of one token per byte (lay_kc_byte)
-        for (int e = threadIdx.x; e < W * d / 4; e += PK_THREADS) {
-            const int i = e / (d / 4), c4 = e % (d / 4);
-            const uint8_t* pk = ck + i * d + 4 * c4;
-            slot[lay_kc_byte(i, 4 * c4, d, W)] = (uint8_t)(pk[0] | (pk[1] << 2) | (pk[2] << 4) | (pk[3] << 6));
+        // K codes: P consecutive channels of one token per byte (lay_kc_byte)
+        for (int e = threadIdx.x; e < cbytes; e += PK_THREADS) {
+            const int i = e / (d / P), c0 = P * (e % (d / P));
+            uint32_t byte = 0;
+            for (int x = 0; x < P; ++x) byte |= (uint32_t)ck[i * d + c0 + x] << (qb * x);
+            slot[lay_kc_byte(i, c0, d, W, qb)] = (uint8_t)byte;
         }
-        // V codes: one byte = 4 consecutive tokens of one channel (lay_vc_byte)
-        for (int e = threadIdx.x; e < W * d / 4; e += PK_THREADS) {
-            const int c = e % d, t0 = 4 * (e / d);
-            slot[W * d / 4 + lay_vc_byte(t0, c, d, W)] =
-                (uint8_t)(cv[t0 * d + c] | (cv[(t0 + 1) * d + c] << 2) | (cv[(t0 + 2) * d + c] << 4) |
-                          (cv[(t0 + 3) * d + c] << 6));
+        // V codes: one byte = P consecutive tokens of one channel (lay_vc_byte)
+        for (int e = threadIdx.x; e < cbytes; e += PK_THREADS) {
+            const int c = e % d, t0 = P * (e / d);
+            uint32_t byte = 0;
+            for (int x = 0; x < P; ++x) byte |= (uint32_t)cv[(t0 + x) * d + c] << (qb * x);
+            slot[cbytes + lay_vc_byte(t0, c, d, W, qb)] = (uint8_t)byte;
         }
         __syncthreads();
     }
@@ -719,14 +729,15 @@ __global__ void __launch_bounds__(PK_THREADS) k_fill(Geo g, Bufs bf, int layer, 
         if (fi.src_slot >= 0) {
             const uint8_t* slot = bf.slots + u * (int64_t)g.n_slots * g.slot_bytes +
                                   (int64_t)fi.src_slot * g.slot_bytes + (int64_t)h * g.slot_head_bytes;
-            const uint16_t* offK = (const uint16_t*)(slot + W * d / 2);
+            const int qb = g.qbits, mask = (1 << qb) - 1, cbytes = lay_code_bytes(W, d, qb);
+            const uint16_t* offK = (const uint16_t*)(slot + 2 * cbytes);
             const uint16_t* sclK = offK + d;
             const uint16_t* offV = sclK + d;
             const uint16_t* sclV = offV + W;
             for (int e = threadIdx.x; e < W * d; e += PK_THREADS) {
                 const int i = e / d, c = e % d;
-                const int kc = (slot[lay_kc_byte(i, c, d, W)] >> lay_kc_shift(c)) & 3;
-                const int vc = (slot[W * d / 4 + lay_vc_byte(i, c, d, W)] >> lay_vc_shift(i)) & 3;
+                const int kc = (slot[lay_kc_byte(i, c, d, W, qb)] >> lay_kc_shift(c, qb)) & mask;
+                const int vc = (slot[cbytes + lay_vc_byte(i, c, d, W, qb)] >> lay_vc_shift(i, qb)) & mask;
                 const int vp = lay_vp(i, W);
                 const double kx = (double)fp16_bits_to_f32(offK[c]) + kc * (double)fp16_bits_to_f32(sclK[c]);
                 const double vx = (double)fp16_bits_to_f32(offV[vp]) + vc * (double)fp16_bits_to_f32(sclV[vp]);

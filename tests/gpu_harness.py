@@ -79,6 +79,7 @@ class Lockstep:
                   else "keynorm" if flags & B.QEVICT_F_RANK_KEYNORM else "cum")
         ocfg = cfg_from(wl, promote=not (flags & B.QEVICT_F_NO_PROMOTE),
                         score_every_step=not (flags & B.QEVICT_F_SCORE_ROUTE_ONLY), ranker=ranker,
+                        quant_bits=4 if flags & B.QEVICT_F_INT4 else 2,
                         **(ocfg_over or {}))
         self.ocfg = ocfg
         self.units = [O.UnitOracle(ocfg, S) for S in self.lens]

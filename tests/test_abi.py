@@ -32,12 +32,14 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
-def test_capacities_match_oracle_for_all_workloads():
+@pytest.mark.parametrize("bits", [2, 4])
+def test_capacities_match_oracle_for_all_workloads(bits):
     _lib()
+    flags = B.QEVICT_F_INT4 if bits == 4 else 0
     for wl in WL.ALL_WORKLOADS:
         for S in sorted(set(wl.prompt_lens()))[:3]:
-            c = B.capacities(B.make_config(wl), S)
-            o = O.capacities(cfg_from(wl), S)
+            c = B.capacities(B.make_config(wl, flags=flags), S)
+            o = O.capacities(cfg_from(wl, quant_bits=bits), S)
             assert (c["K_f"], c["K_q"], c["M_f"], c["M_q"]) == (o["K_f"], o["K_q"], o["M_f"], o["M_q"]), wl.name
             assert c["B_total"] == o["B_total"] and c["B_hist"] == o["B_hist"]
 

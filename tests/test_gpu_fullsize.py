@@ -79,3 +79,17 @@ def test_llama8b_32k_prefill_column_sums():
         a = WL32.n_sink + w * WL32.window
         ref = col_ref[:, a - t0: a - t0 + WL32.window].sum() / WL32.h_q
         assert abs(ex.score[w] - ref) < 1e-4
+
+
+def test_llama8b_32k_int4_decode_and_route_lockstep():
+    """The same full-size lockstep with the INT4 recoverable tier."""
+    print("case: 32K int4 decode lockstep", flush=True)
+    n_win = (WL32.prompt_len - WL32.n_sink + WL32.window - 1) // WL32.window
+    si = WL.init_scores(WL32, 0, n_win)
+    ls = Lockstep(WL32, score_init=si, flags=B.QEVICT_F_INT4)
+    ls.prefill()
+    ex = ls.st.export_unit(0, 0)
+    assert ex.counters["packed"] == ls.units[0].events[0]["packed"] > 400
+    for j in range(8):
+        ls.step(j)
+    print(f"32K int4: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}", flush=True)

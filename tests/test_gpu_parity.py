@@ -207,3 +207,37 @@ def test_alternative_rankers_lockstep(flag):
                       n_outlier=2, n_topics=2, topic_period=8)
     ls2 = Lockstep(wl2, flags=f).run(24)
     _print(f"{flag} gqa8: max o err {ls2.max_o_err:.2e}, max score err {ls2.max_s_err:.2e}")
+
+
+INT4_CASES = {
+    # d = 64, W = 16 (one tile per chunk), G = 4, flat initial scores + topic drift: promotions
+    "tiny_drift": (WL.TINY.with_(n_topics=4, topic_period=16, n_decode=64, n_outlier=2, budget_frac=0.30), True, 64),
+    # d = 64, W = 32 (two tiles per chunk), G = 2, ragged batch of 2
+    "d64_w32": (WL.Workload("i4a", 1, 2, 4, 2, 64, 600, 32, 32, 4, 64, 8, 0.35, 0.70, prompt_len_min=350,
+                            n_outlier=2, n_topics=2, topic_period=8), False, 32),
+    # d = 128, W = 32, G = 8 (one column slot), ragged batch
+    "gqa8_d128": (WL.Workload("i4b", 1, 2, 16, 2, 128, 640, 24, 32, 4, 64, 8, 0.30, 0.70, prompt_len_min=300,
+                              n_outlier=2, n_topics=2, topic_period=8), False, 24),
+    # d = 128, W = 64 (two chunks per window), G = 8
+    "w64": (WL.Workload("i4c", 1, 1, 16, 2, 128, 1200, 24, 64, 4, 128, 8, 0.30, 0.70,
+                        n_outlier=2, n_topics=2, topic_period=8), False, 24),
+}
+
+
+@pytest.mark.parametrize("case", list(INT4_CASES))
+def test_int4_tier_lockstep(case):
+    """The INT4 recoverable tier ([QEvict] Appendix G.3): 16-level codes packed, promoted and
+    attended; codes, parameters, ledgers and pages bit-exact, outputs within 2e-3 of ||o||."""
+    wl, flat, steps = INT4_CASES[case]
+    _print(f"case: int4 {case}")
+    si = None
+    if flat:
+        n_win = math.ceil((wl.prompt_len + wl.n_decode - wl.n_sink) / wl.window)
+        si = torch.zeros((wl.batch, n_win), dtype=torch.float64)
+    ls = Lockstep(wl, score_init=si, flags=B.QEVICT_F_INT4).run(steps)
+    assert ls.st.info.max_K_q > 0
+    led = [u.win[w].ledger for u in ls.units for w in u.win if u.win[w].ledger is not None]
+    assert led and max(int(l.k_codes.max()) for l in led) > 3          # codes beyond the INT2 range
+    if flat:
+        assert sum(e["promoted"] for u in ls.units for e in u.events) > 0
+    _print(f"int4 {case}: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}")
