@@ -50,7 +50,16 @@ reason in the design notes of the repository):
   with S_0 the prefill initialisation; "pnorm" ranks by P, which orders the
   windows as P^(1/p) does; "keynorm" sets S(w) = -(mean over the window's tokens
   of the L2 norm of the token's key over all KV heads' channels) when the window
-  enters the candidate pool, from its bf16 keys, and needs no attention mass.
+  enters the candidate pool, from its bf16 keys, and needs no attention mass;
+* RoPE-faithful Quantized tier ([QEvict] §4.3 "Migration-Stable Quantization" and
+  "Cache Execution"; optional, ``rope=True``): queries and keys arrive before RoPE;
+  the cache keeps keys rotated at their absolute positions (bf16 of the exact
+  rotation), as a bf16 model's cache would; a window entering the Quantized tier
+  for the first time is quantized from its stored keys rotated back to the
+  pre-RoPE domain (exact fp64), and attention re-applies RoPE at the ledger's
+  positions to the dequantized keys; a promotion writes bf16 of that re-rotation.
+  The rotation pairs channel i with i + d/2 ("rotate half") and takes its cos/sin
+  from a table given as input (fp32 values, one row per position).
 """
 from __future__ import annotations
 
@@ -96,6 +105,7 @@ class OracleConfig:
     decay_lambda: float = 0.99
     pnorm_p: int = 3
     quant_bits: int = 2          # 2 (INT2, the default) or 4 (INT4, [QEvict] Appendix G.3)
+    rope: bool = False           # inputs before RoPE, Quantized tier in the pre-RoPE domain
 
     @property
     def group(self) -> int:
@@ -267,6 +277,23 @@ def canonical_ledger_bytes(led: Ledger) -> bytes:
 
 
 # --------------------------------------------------------------------------------------
+# rotary position embedding ("rotate half" pairing), exact in float64
+# --------------------------------------------------------------------------------------
+def rope_rotate(x: np.ndarray, pos, cs: np.ndarray, inverse: bool = False) -> np.ndarray:
+    """Rotate x [..., n, d] whose token axis -2 sits at positions ``pos`` [n]: channel
+    pair (i, i + d/2) turns by the angle whose (cos, sin) is cs[pos, i]; ``inverse``
+    turns it back.  No rounding beyond float64."""
+    x = np.asarray(x, dtype=np.float64)
+    h = x.shape[-1] // 2
+    c = cs[np.asarray(pos), :, 0].astype(np.float64)      # [n][h]
+    s = cs[np.asarray(pos), :, 1].astype(np.float64)
+    if inverse:
+        s = -s
+    a, b = x[..., :h], x[..., h:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+# --------------------------------------------------------------------------------------
 # attention pieces
 # --------------------------------------------------------------------------------------
 def softmax(x: np.ndarray, axis: int = -1) -> np.ndarray:
@@ -315,8 +342,12 @@ class _Window:
 class UnitOracle:
     """QEvict state and steps for one (sequence, layer) pair, in float64."""
 
-    def __init__(self, cfg: OracleConfig, prompt_len: int):
+    def __init__(self, cfg: OracleConfig, prompt_len: int, rope_cs: Optional[np.ndarray] = None):
+        """``rope_cs`` [n_pos][d/2][2] (cos, sin) is required with ``cfg.rope``."""
         self.cfg = cfg
+        if cfg.rope and rope_cs is None:
+            raise ValueError("rope=True needs the (cos, sin) table")
+        self.cs = None if rope_cs is None else np.asarray(rope_cs, dtype=np.float64)
         self.prompt_len = prompt_len
         self.caps = capacities(cfg, prompt_len)
         self.n = 0
@@ -353,6 +384,25 @@ class UnitOracle:
         W.k[:, i] = k
         W.v[:, i] = v
 
+    # --- RoPE ([QEvict] §4.3) ----------------------------------------------------------
+    def rotate_in(self, x: np.ndarray, pos) -> np.ndarray:
+        """An input key / query [H][n][d] (or [H][d] at one position) as the cache holds
+        it: bf16 of the exact rotation at ``pos``; unchanged without RoPE."""
+        if not self.cfg.rope:
+            return x
+        if x.ndim == 2:
+            return to_bf16(rope_rotate(x[:, None, :], [pos], self.cs))[:, 0, :]
+        return to_bf16(rope_rotate(x, pos, self.cs))
+
+    def positions(self, w: int) -> np.ndarray:
+        return np.arange(self.win_start(w), self.win_end(w))
+
+    def quant_keys(self, w: int) -> np.ndarray:
+        """Keys of a Quantized window as attention uses them: x_hat, re-rotated at the
+        ledger's positions (exact) with RoPE."""
+        kh = self.win[w].ledger.k_hat()
+        return rope_rotate(kh, self.positions(w), self.cs) if self.cfg.rope else kh
+
     # --- the accessible set (sinks, LOCAL, FULL, QUANT) ------------------------------
     def accessible(self):
         """Returns (owner[n_acc], K[H_kv][n_acc][d], V[H_kv][n_acc][d]) in chronological
@@ -368,7 +418,7 @@ class UnitOracle:
                 continue
             ntok = min(cfg.window, self.n - self.win_start(w))
             if W.state == QUANT:
-                kh, vh = W.ledger.k_hat(), W.ledger.v_hat()
+                kh, vh = self.quant_keys(w), W.ledger.v_hat()
                 if cfg.qexec_bf16:
                     kh, vh = to_bf16(kh), to_bf16(vh)
                 Ks.append(kh[:, :ntok])
@@ -388,6 +438,8 @@ class UnitOracle:
         cfg = self.cfg
         S = qp.shape[1]
         assert S == self.prompt_len
+        if cfg.rope:
+            qp, kp = self.rotate_in(qp, np.arange(S)), self.rotate_in(kp, np.arange(S))
         for p in range(S):
             self._store(p, kp[:, p], vp[:, p])
         self.n = S
@@ -416,6 +468,7 @@ class UnitOracle:
         """q [H_q][d], k/v [H_kv][d].  Appends k, v at position n, attends over the
         accessible set and adds each window's head-averaged mass to S_bar."""
         cfg = self.cfg
+        q, k = self.rotate_in(q, self.n), self.rotate_in(k, self.n)
         self._store(self.n, k, v)
         self.n += 1
         owner, K, V = self.accessible()
@@ -493,7 +546,7 @@ class UnitOracle:
         for w in F:
             W = self.win[w]
             if W.state == QUANT:
-                W.k = to_bf16(W.ledger.k_hat())
+                W.k = to_bf16(self.quant_keys(w))
                 W.v = to_bf16(W.ledger.v_hat())
                 W.ledger.dormant = True
                 ctr["promoted"] += 1
@@ -504,7 +557,8 @@ class UnitOracle:
             if W.state != QUANT:
                 ctr["demoted"] += 1
                 if W.ledger is None:
-                    W.ledger = quantize_window(W.k, W.v, self.win_start(w), cfg.quant_bits)
+                    kq = rope_rotate(W.k, self.positions(w), self.cs, inverse=True) if cfg.rope else W.k
+                    W.ledger = quantize_window(kq, W.v, self.win_start(w), cfg.quant_bits)
                     ctr["packed"] += 1
                 else:
                     assert W.ledger.dormant

@@ -214,3 +214,17 @@ def init_scores(wl: Workload, layer: int, n_windows: int, device="cpu") -> torch
             if w < n_windows:
                 out[b, w] += 100.0
     return out.to(device)
+
+
+ROPE_THETA = 500000.0     # base of the rotary frequencies of the Llama-3 family
+
+
+def rope_table(d: int, n_pos: int, theta: float = ROPE_THETA, device="cpu") -> torch.Tensor:
+    """Rotary (cos, sin) table ``[n_pos][d/2][2]`` (float32) for the "rotate half"
+    pairing: pair i of position p turns by p * theta^(-2i/d).  Angles and their cosines
+    and sines are evaluated in float64 and rounded once to float32; the table is an
+    input of the model, handed unchanged to the library and to the oracle."""
+    i = torch.arange(d // 2, dtype=torch.float64)
+    inv = theta ** (-2.0 * i / d)
+    ang = torch.arange(n_pos, dtype=torch.float64)[:, None] * inv[None, :]
+    return torch.stack([torch.cos(ang), torch.sin(ang)], dim=-1).to(torch.float32).to(device)

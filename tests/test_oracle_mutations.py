@@ -6,6 +6,7 @@ import pytest
 from oracle import qevict_oracle as O
 from tests import test_oracle_codec as TC
 from tests import test_oracle_state as TS
+from tests import test_oracle_rope as TR
 
 
 def _fails(fn, *args):
@@ -117,3 +118,18 @@ def test_int4_bytes_counted_as_int2_are_caught(monkeypatch):
     monkeypatch.setattr(O, "quant_window_bytes",
                         lambda cfg: real(O.OracleConfig(**{**cfg.__dict__, "quant_bits": 2})))
     _fails(TS.test_quantized_window_bytes_equal_the_stored_record, 4)
+
+
+def test_quantizing_rotated_keys_is_caught(monkeypatch):
+    real = O.rope_rotate
+
+    def no_unrotate(x, pos, cs, inverse=False):
+        return np.asarray(x, dtype=np.float64) if inverse else real(x, pos, cs)
+
+    monkeypatch.setattr(O, "rope_rotate", no_unrotate)
+    _fails(TR.test_quantized_in_the_pre_rope_domain_and_promoted_re_rotated)
+
+
+def test_attending_unrotated_quantized_keys_is_caught(monkeypatch):
+    monkeypatch.setattr(O.UnitOracle, "quant_keys", lambda self, w: self.win[w].ledger.k_hat())
+    _fails(TR.test_quantized_windows_attend_with_re_rotated_keys)
