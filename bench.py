@@ -49,7 +49,7 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(wl, budget_s: float = 20.0, ranker: str = "cum", quant_bits: int = 2) -> dict:
+def cpu_baseline(wl, budget_s: float = 20.0, ranker: str = "cum", quant_bits: int = 2, rope_cs=None) -> dict:
     """Time the fp64 oracle's decode step on the host (layer 0, sequence 0), with a
     synthetic initial score instead of the prompt column sums (those alone are
     ~9 TFLOP of fp64 per layer on a 32K prompt)."""
@@ -63,11 +63,12 @@ def cpu_baseline(wl, budget_s: float = 20.0, ranker: str = "cum", quant_bits: in
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
     ocfg = O.OracleConfig(wl.h_q, wl.h_kv, wl.d_head, wl.window, wl.n_sink, wl.n_local, wl.omega,
-                          wl.quant_frac, wl.budget_frac, wl.n_decode, ranker=ranker, quant_bits=quant_bits)
+                          wl.quant_frac, wl.budget_frac, wl.n_decode, ranker=ranker, quant_bits=quant_bits,
+                          rope=rope_cs is not None)
     S = wl.prompt_len
     qp, kp, vp = WL.prompt(wl.with_(batch=1), 0)
     f = lambda t: t.to(torch.float64).numpy()
-    unit = O.UnitOracle(ocfg, S)
+    unit = O.UnitOracle(ocfg, S, rope_cs=None if rope_cs is None else rope_cs.numpy())
     n_win = (S - wl.n_sink + wl.window - 1) // wl.window
     t0 = time.perf_counter()
     unit.prefill(f(qp[0]), f(kp[0]), f(vp[0]), score_init=WL.init_scores(wl, 0, n_win)[0].numpy())
@@ -138,6 +139,8 @@ def main():
                     help="window rank key: cumulative mass (Eq. 1) or an Appendix J alternative")
     ap.add_argument("--quant-bits", type=int, choices=(2, 4), default=2,
                     help="bits per Quantized-tier code: INT2 (default) or INT4")
+    ap.add_argument("--rope", action="store_true",
+                    help="inputs before RoPE, Quantized tier in the pre-RoPE domain (rotary base 500000)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -168,10 +171,14 @@ def main():
     if args.steps + args.warmup > wl.n_decode:
         sys.exit(f"--steps + --warmup must be <= {wl.n_decode}")
     flags = (getattr(B, RANKERS[args.ranker]) if RANKERS[args.ranker] else 0) | \
-        (B.QEVICT_F_INT4 if args.quant_bits == 4 else 0)
+        (B.QEVICT_F_INT4 if args.quant_bits == 4 else 0) | (B.QEVICT_F_ROPE if args.rope else 0)
     cfg = B.make_config(wl, n_splits=args.n_splits, flags=flags)
     lens = wl.prompt_lens()
     st = B.QEvictState(cfg, lens, device=dev)
+    rope_cs = None
+    if args.rope:
+        rope_cs = WL.rope_table(wl.d_head, max(32, wl.prompt_len + wl.n_decode))
+        st.set_rope(rope_cs.to(dev))
     log(f"[bench] {wl.name}: arena {st.info.arena_bytes / 2**30:.2f} GiB, splits {st.info.n_splits}, "
         f"K_f {st.info.max_K_f}, K_q {st.info.max_K_q}")
 
@@ -255,7 +262,8 @@ def main():
     decode_tokens_per_s = wl.batch * args.steps / (decode_ms * 1e-3)
 
     traffic = None
-    tag = "" if (args.quant_bits == 2 and args.ranker == "cum") else f"_int{args.quant_bits}_{args.ranker}"
+    tag = "" if (args.quant_bits == 2 and args.ranker == "cum" and not args.rope) else \
+        f"_int{args.quant_bits}_{args.ranker}{'_rope' if args.rope else ''}"
     tf = os.path.join(ROOT, "profiles", f"decode_split_{wl.name}{tag}_traffic.json")
     if os.path.exists(tf):
         rec = json.load(open(tf))
@@ -267,7 +275,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
-        cpu = cpu_baseline(wl, args.cpu_budget_s, args.ranker, args.quant_bits)
+        cpu = cpu_baseline(wl, args.cpu_budget_s, args.ranker, args.quant_bits, rope_cs)
 
     rp = sorted(route_ms)
     line = {
@@ -287,7 +295,8 @@ def main():
                    "d_head": wl.d_head, "prompt_len": wl.prompt_len, "window": wl.window, "n_sink": wl.n_sink,
                    "n_local": wl.n_local, "omega": wl.omega, "budget_frac": wl.budget_frac,
                    "quant_frac": wl.quant_frac, "storage": f"bf16 + int{args.quant_bits}", "n_splits": st.info.n_splits,
-                   "K_f": st.info.max_K_f, "K_q": st.info.max_K_q, "ranker": args.ranker},
+                   "K_f": st.info.max_K_f, "K_q": st.info.max_K_q, "ranker": args.ranker,
+                   "rope": "inputs before RoPE, base 500000" if args.rope else None},
         "decode_attn_tokens_per_s": round(decode_tokens_per_s, 2),
         "route_us_per_event": {"mean": round(statistics.mean(route_ms) * 1e3, 2) if route_ms else None,
                                "p50": round(rp[len(rp) // 2] * 1e3, 2) if rp else None,

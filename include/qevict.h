@@ -69,6 +69,15 @@ typedef enum {
 /* INT4 recoverable tier (App. G.3): 4-bit codes (16 levels, scl = RU_fp16((max - off)/15)),
  * everything else as for INT2; M_q = W*H_kv*d + 4*H_kv*d + 4*W*H_kv + 20 bytes. */
 #define QEVICT_F_INT4             32u
+/* RoPE-faithful Quantized tier (§4.3 "Migration-Stable Quantization", "Cache Execution"):
+ * queries and keys are handed over BEFORE RoPE and the library rotates them with the
+ * table given to qevict_set_rope ("rotate half": channel pair (i, i + d/2) of position p
+ * turns by the angle whose cos / sin are table[p][i]).  Cached keys (sinks, recent, Full)
+ * are bf16 of the exact rotation at their positions; a window's first demotion quantizes
+ * its cached keys rotated back to the pre-RoPE domain (exact fp64); attention re-applies
+ * RoPE to the dequantized keys at the ledger's positions, and a promotion writes bf16 of
+ * that re-rotation. */
+#define QEVICT_F_ROPE             64u
 
 typedef struct {
     int32_t batch;        /* B sequences */
@@ -143,8 +152,11 @@ void qevict_destroy(qevict_state* st);
  *     completes on `stream`.  When the column sums run it holds, from offset 0,
  *     the row log-sum-exps in log2 units, fp32 [B][h_q][S_max], then (at the
  *     next 256-byte boundary) the per-head column sums, fp64 [B][h_q][S_max].
+ *     With QEVICT_F_ROPE it is required also with score_init (it then holds the
+ *     rotated prompt queries and keys after those arrays).
+ *   With QEVICT_F_ROPE, q_prompt and k_prompt are before RoPE (qevict_set_rope first).
  * Then routes the aged prompt windows (Eqs. 4-5), packs the Quantized ones
- * (INT2, write-once) and copies the Full and recent ones into bf16 pages.
+ * (INT2 or INT4, write-once) and copies the Full and recent ones into bf16 pages.
  */
 qevict_status qevict_prefill_init(qevict_state* st, int32_t layer,
                                   const void* q_prompt, const void* k_prompt, const void* v_prompt,
@@ -153,7 +165,8 @@ qevict_status qevict_prefill_init(qevict_state* st, int32_t layer,
 
 /*
  * One decode step of one layer (§4.1 accessible-set attention, §4.2 Eq. 1).
- *   q [B][h_q][d], k_new / v_new [B][h_kv][d] bf16: the new token's query, key, value.
+ *   q [B][h_q][d], k_new / v_new [B][h_kv][d] bf16: the new token's query, key, value
+ *     (query and key before RoPE with QEVICT_F_ROPE; the library turns them to position n).
  *   out [B][h_q][d] fp32: o = softmax(q K_acc^T / sqrt(d)) V_acc over sinks, the
  *     recent region, Full windows (bf16) and Quantized windows (INT2 values
  *     off + code * scl, dequantized in registers).
@@ -240,6 +253,14 @@ qevict_status qevict_step_bytes(qevict_state* st, int32_t layer, int64_t* kv_byt
  * ev_before / ev_after (hipEvent_t with timing; both or neither) the kernel's own
  * dispatch stamps its start and end, as for qevict_time_next_decode.  Enqueues on
  * `stream`; argument errors return QEVICT_E_INVALID before anything is enqueued. */
+/* RoPE mode (QEVICT_F_ROPE): copy the rotary table into the state.
+ *   cos_sin: [n_pos][d_head/2][2] fp32 (cos, sin) of position p, pair i (channels i and
+ *            i + d_head/2), device or host memory, read before the call returns on `stream`;
+ *            rows >= max(32, max_prompt + max_new) are needed.
+ * Must come before the first qevict_prefill_init.  Errors: QEVICT_E_STATE without the flag,
+ * QEVICT_E_INVALID for a null or short table. */
+qevict_status qevict_set_rope(qevict_state* st, const float* cos_sin, int32_t n_pos, void* stream);
+
 qevict_status qevict_stream_read(const void* buf, size_t bytes, void* sink, void* ev_before, void* ev_after,
                                  void* stream);
 

@@ -24,6 +24,7 @@ QEVICT_F_RANK_DECAY = 4      # alternative rankers ([QEvict] Appendix J); at mos
 QEVICT_F_RANK_PNORM = 8
 QEVICT_F_RANK_KEYNORM = 16
 QEVICT_F_INT4 = 32           # INT4 recoverable tier ([QEvict] Appendix G.3) instead of INT2
+QEVICT_F_ROPE = 64           # inputs before RoPE; Quantized tier in the pre-RoPE domain ([QEvict] §4.3)
 
 DEV_E_POOL, DEV_E_WINDOW, DEV_E_RANGE, DEV_E_LIST = 1, 2, 4, 8
 
@@ -31,7 +32,7 @@ EXPORTED_SYMBOLS = (
     "qevict_capacities", "qevict_plan", "qevict_create", "qevict_destroy", "qevict_prefill_init",
     "qevict_decode_attn", "qevict_route", "qevict_pack_int2", "qevict_promote", "qevict_poll_status",
     "qevict_export_unit", "qevict_decode_kernel_name", "qevict_last_error", "qevict_time_next_decode",
-    "qevict_step_bytes", "qevict_stream_read",
+    "qevict_step_bytes", "qevict_stream_read", "qevict_set_rope",
 )
 
 
@@ -91,6 +92,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qevict_time_next_decode.argtypes = [P, P, P]
     lib.qevict_step_bytes.argtypes = [P, I, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64), P]
     lib.qevict_stream_read.argtypes = [P, Z, P, P, P, P]
+    lib.qevict_set_rope.argtypes = [P, P, I, P]
     lib.qevict_decode_kernel_name.restype = ctypes.c_char_p
     lib.qevict_last_error.restype = ctypes.c_char_p
     for name in EXPORTED_SYMBOLS:
@@ -259,9 +261,14 @@ class QEvictState:
             _expect(q, (c.batch, c.h_q, c.max_prompt, c.d_head), "bfloat16", self.device, "q_prompt")
         else:
             _expect(score_init, (c.batch, self.info.n_windows), "float64", self.device, "score_init")
-        ws = None if score_init is not None else self.ensure_workspace()
+        ws = None if (score_init is not None and not c.flags & QEVICT_F_ROPE) else self.ensure_workspace()
         _check(self.lib.qevict_prefill_init(self.handle, layer, _ptr(q), _ptr(k), _ptr(v), _ptr(score_init),
                                             _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+
+    def set_rope(self, table, stream=None):
+        """RoPE mode: copy the (cos, sin) table ``[n_pos][d/2][2]`` (float32, on the device)."""
+        _expect(table, (table.shape[0], self.cfg.d_head // 2, 2), "float32", self.device, "rope table")
+        _check(self.lib.qevict_set_rope(self.handle, _ptr(table), table.shape[0], _stream(stream)))
 
     def decode_attn(self, layer: int, q, k, v, out, stream=None):
         c = self.cfg

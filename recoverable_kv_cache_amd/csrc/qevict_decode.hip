@@ -185,7 +185,7 @@ __device__ __forceinline__ void stw(void* p, const uint32_t* w) {
 
 // Static shape of one instantiation: head dim D, query heads per KV head G,
 // tiles per 32-token chunk TPC (1 for 16-token windows, else 2).
-template <int D, int G, int TPC, int BITS>
+template <int D, int G, int TPC, int BITS, bool ROPE>
 struct DecShape {
     static constexpr int CQ = D / 4;                 // channels per lane group (key side)
     static constexpr int KS = D / 32;                // 32-channel MFMA steps (key side)
@@ -199,8 +199,9 @@ struct DecShape {
     // quantized job words per lane (BITS-bit codes): K codes and V codes of every item,
     // V offsets / scales of the lane's own item, K scales / offsets of the lane's product channels
     static constexpr int KCW = TPC * CQ * BITS / 32, VCW = MB * TPC * BITS / 8, VPW = 2 * TPC, KPW = CPL / 2;
+    // (RoPE mode: plus the (cos, sin) of the lane's product channels at the chunk's first position)
     static constexpr int O_VC = NSLOT * KCW, O_VO = O_VC + NSLOT * VCW, O_VS = O_VO + VPW, O_KS = O_VS + VPW,
-                         O_KO = O_KS + KPW, QW = O_KO + KPW;
+                         O_KO = O_KS + KPW, O_CS = O_KO + KPW, QW = O_CS + (ROPE ? 2 * CPL : 0);
     // bf16 tile job words per lane: K row (CQ bf16) then V (MB blocks x 4 tokens)
     static constexpr int FW = CQ / 2 + 2 * MB;
     static constexpr int RW = QW > FW ? QW : FW;
@@ -208,21 +209,22 @@ struct DecShape {
     static_assert(KCW >= 1 && VCW >= 1 && KPW >= 1, "shape");
 };
 
-// One unit of wave work.  INT2 job: chunk c of up to NSLOT Quantized windows
+// One unit of wave work.  Quantized job: chunk c of up to NSLOT Quantized windows
 // (entries ia, ib), one per column slot.  bf16 job: tile t of one sink / page entry.
 struct Job {
-    int type;           // 0 none, 1 INT2, 2 bf16
-    int k;              // index in the batch's INT2-pair / bf16-entry job table
-    int ia, ib, c;      // INT2: batch-local entry indices (ib = -1: slot 1 empty), chunk
-    int sa, sb;         // INT2: slot ids
+    int type;           // 0 none, 1 Quantized, 2 bf16
+    int k;              // index in the batch's Quantized-pair / bf16-entry job table
+    int ia, ib, c;      // Quantized: batch-local entry indices (ib = -1: slot 1 empty), chunk
+    int sa, sb;         // Quantized: slot ids
+    int pa, pb;         // Quantized: first positions of the two windows
     int i, t, kind, idx, ntok, Wn, start;   // bf16: entry, tile, kind, page id, valid tokens, block width, position 0
 };
 
-template <int D, int G, int TPC, int BITS>
+template <int D, int G, int TPC, int BITS, bool ROPE>
 __global__ void __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(2)))
 k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, const uint16_t* __restrict__ knew,
                const uint16_t* __restrict__ vnew) {
-    using S = DecShape<D, G, TPC, BITS>;
+    using S = DecShape<D, G, TPC, BITS, ROPE>;
     constexpr int CQ = S::CQ, KS = S::KS, MB = S::MB, NSLOT = S::NSLOT, SW = S::SW, LPR = S::LPR, CPL = S::CPL;
     constexpr int NV = S::NV, QSTR = S::QSTR;
     __shared__ uint2 lut[256];            // code byte -> its 4 (INT2) or 2 (INT4, in .x) codes as bf16 integers
@@ -233,6 +235,10 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     __shared__ float s_m[DW][G], s_l[DW][G], s_vb[DW][G];
     __shared__ float s_acc[DW][G][D];
     __shared__ __attribute__((aligned(16))) uint16_t nkv[DW][2][D];     // per wave: the new token's K and V
+    // RoPE mode: (cos, sin) of positions 0..31 of a chunk (rows of the table), and per wave
+    // the two windows' key parameters (fp16 offset | scale << 16, channel order)
+    __shared__ __attribute__((aligned(16))) float2 ctab[ROPE ? 32 * (D / 2) : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t prm[ROPE ? DW : 1][2][D];
 
     const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
     const int64_t u = unit_of(g, b, layer);
@@ -267,6 +273,41 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             kn = reinterpret_cast<const uint32_t*>(knew + ((int64_t)b * g.h_kv + hk) * D)[lane];
             vn = reinterpret_cast<const uint32_t*>(vnew + ((int64_t)b * g.h_kv + hk) * D)[lane];
         }
+        if constexpr (ROPE) {
+            // the query (this lane's CQ channels of its head) and the step's key (two channels
+            // per lane) turned by RoPE at the new position: exact fp64, one bf16 rounding
+            constexpr int H2 = D / 2;
+            const float2* crow = bf.rope + (int64_t)n_old * H2;
+            uint32_t wp[CQ / 2];
+            const int cq0 = CQ * qg, part = cq0 < H2 ? cq0 + H2 : cq0 - H2;
+            ldw<CQ / 2>(wp, qhead + head * D + part);
+            uint32_t knp = 0;
+            if (lane < D / 2) {
+                const int pl = lane < H2 / 2 ? lane + H2 / 2 : lane - H2 / 2;
+                knp = reinterpret_cast<const uint32_t*>(knew + ((int64_t)b * g.h_kv + hk) * D)[pl];
+            }
+            auto turn = [&](float x, float xp, float2 cs, bool first) -> uint32_t {
+                const double a = (double)x, c = (double)cs.x, sn = (double)cs.y, y = (double)xp;
+                const double r = first ? __dsub_rn(__dmul_rn(a, c), __dmul_rn(y, sn))
+                                       : __dadd_rn(__dmul_rn(a, c), __dmul_rn(y, sn));
+                return (uint32_t)f64_to_bf16(r);
+            };
+#pragma unroll
+            for (int x = 0; x < CQ / 2; ++x) {
+                const int c0 = cq0 + 2 * x;
+                const float2 cs0 = crow[c0 % H2], cs1 = crow[(c0 + 1) % H2];
+                w[x] = turn(bf16lo(w[x]), bf16lo(wp[x]), cs0, c0 < H2) |
+                       (turn(bf16hi(w[x]), bf16hi(wp[x]), cs1, c0 < H2) << 16);
+            }
+            if (lane < D / 2) {
+                const int c0 = 2 * lane;
+                const float2 cs0 = crow[c0 % H2], cs1 = crow[(c0 + 1) % H2];
+                kn = turn(bf16lo(kn), bf16lo(knp), cs0, c0 < H2) | (turn(bf16hi(kn), bf16hi(knp), cs1, c0 < H2) << 16);
+                if (split == 0)   // for the finish kernel, which stores the token
+                    reinterpret_cast<uint32_t*>(bf.krot + (((int64_t)layer * g.B + b) * g.h_kv + hk) * D)[lane] = kn;
+            }
+            for (int x = threadIdx.x; x < 32 * H2; x += 64 * DW) ctab[x] = bf.rope[x];
+        }
         // a code byte -> its codes as bf16 integers (4 of 2 bits, or 2 of 4 bits): one table
         // at a fixed LDS address, so a lookup is one shift of the code byte with the base in
         // the read's immediate offset
@@ -284,6 +325,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             qf[2 * x] = bf16lo(w2[x]) * scale;
             qf[2 * x + 1] = bf16hi(w2[x]) * scale;
         }
+        if constexpr (ROPE) (void)qf;
         if (lane < D / 2) {
             reinterpret_cast<uint32_t*>(nkv[wave][0])[lane] = kn;
             reinterpret_cast<uint32_t*>(nkv[wave][1])[lane] = vn;
@@ -327,10 +369,13 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             j.sb = lb >= 0 ? __builtin_amdgcn_readlane(me.idx, lb) : j.sa;
             j.ia = e_begin + xb + la - 1;                       // accessible-list indices
             j.ib = lb >= 0 ? e_begin + xb + lb - 1 : -1;
+            j.pa = __builtin_amdgcn_readlane(me.start, la);
+            j.pb = lb >= 0 ? __builtin_amdgcn_readlane(me.start, lb) : j.pa;
         } else {
             j.type = 0;                          // no job left
             j.ia = j.ib = -1;
             j.sa = j.sb = 0;
+            j.pa = j.pb = 0;
         }
         return j;
     };
@@ -388,7 +433,14 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     const uint32_t kc_lane = (uint32_t)((n * 4 + qg) * TPC * KRB);                    // K codes: token row n, group qg
     const uint32_t vc_lane = cbytes + (uint32_t)((n * 4 + qg) * NCH * MB * TPC * VTB); // V codes: channel row n
     const uint32_t vp_lane = 2 * cbytes + (uint32_t)(4 * D + qg * NT * 8);            // V offsets (V scales + 2W)
-    const uint32_t kp_lane = 2 * cbytes + (uint32_t)(CPL * pcb * 2);                  // K offsets (K scales + 2D)
+    // the lane's product channels: CPL of them from position CPL*pcb of the key-side channel
+    // order (in RoPE mode all in one half, pairing as in lay_kc_pos)
+    const int pch0 = [&]() {
+        const int pos = CPL * pcb, pqg = pos / CQ, pcc = pos % CQ;
+        if constexpr (!ROPE) return pos;
+        return pcc < CQ / 2 ? pqg * (CQ / 2) + pcc : D / 2 + pqg * (CQ / 2) + pcc - CQ / 2;
+    }();
+    const uint32_t kp_lane = 2 * cbytes + (uint32_t)(pch0 * 2);                       // K offsets (K scales + 2D)
     auto load_q = [&](const Job& j, Raw& R) __attribute__((always_inline)) {
         const uint32_t oa = (uint32_t)j.sa * (uint32_t)g.slot_bytes, ob = (uint32_t)j.sb * (uint32_t)g.slot_bytes;
         const uint8_t* ca = slots + oa + (uint32_t)(j.c * 16 * 4 * TPC * KRB);   // chunk c of item a
@@ -406,6 +458,10 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         const uint32_t op = (pitem == 0 ? oa : ob) + kp_lane;
         ldw<S::KPW>(R.w + S::O_KS, slots + op + 2 * D);
         ldw<S::KPW>(R.w + S::O_KO, slots + op);
+        if constexpr (ROPE) {   // (cos, sin) of the product channels' pairs at the chunk's first position
+            const int A = (pitem == 0 ? j.pa : j.pb) + 32 * j.c;
+            ldw<2 * CPL>(R.w + S::O_CS, bf.rope + (int64_t)A * (D / 2) + pch0 % (D / 2));
+        }
     };
     auto load_f = [&](const Job& j, Raw& R) __attribute__((always_inline)) {
         const int tpc = lay_tpc(j.Wn), nt16 = j.Wn / 16;
@@ -506,10 +562,102 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
 
     const uint16_t* qrow_a = &qs[wave][(NSLOT == 2 && slot) ? 32 : n][CQ * qg];   // slot 0 columns only
     const uint16_t* qrow_b = &qs[wave][(NSLOT == 2 && !slot) ? 32 : n][CQ * qg];  // slot 1 columns only
+    // RoPE mode, key side of a Quantized job (see process_q): the 8 codes of positions
+    // 8ks .. 8ks + 7 of the lane's row of tile tc, as floats
+    auto codes8 = [&](const uint32_t* w, int tc, int ks, float* c) __attribute__((always_inline)) {
+        if constexpr (BITS == 2) {
+            const int by = tc * (CQ / 4) + 2 * ks;
+            const uint32_t x = w[by >> 2];
+            const u2_t a0 = lut4(x, by & 3), a1 = lut4(x, (by & 3) + 1);
+            const uint32_t v[4] = {a0.x, a0.y, a1.x, a1.y};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                c[2 * k] = bf16lo(v[k]);
+                c[2 * k + 1] = bf16hi(v[k]);
+            }
+        } else {
+            const uint32_t x = w[tc * (CQ / 8) + ks];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t v = lut2(x, k);
+                c[2 * k] = bf16lo(v);
+                c[2 * k + 1] = bf16hi(v);
+            }
+        }
+    };
+    // RoPE mode: the turned keys of one item for channel pairs (i, i + D/2), i = i0 .. i0 + 7,
+    // at chunk position u, as bf16 high / low MFMA operands of the first-half and the
+    // second-half channel blocks
+    auto rope_keys = [&](const uint32_t* w, const uint32_t* pr, int tc, int ks, const float2* cs, u4_t& hf, u4_t& lf,
+                         u4_t& hs, u4_t& ls) __attribute__((always_inline)) {
+        float cf[8], cb[8];
+        codes8(w, tc, ks, cf);
+        codes8(w, tc, ks + KS / 2, cb);
+        const int i0 = qg * (CQ / 2) + 8 * ks;
+        uint4 pf0 = *reinterpret_cast<const uint4*>(pr + i0), pf1 = *reinterpret_cast<const uint4*>(pr + i0 + 4);
+        uint4 pb0 = *reinterpret_cast<const uint4*>(pr + D / 2 + i0), pb1 = *reinterpret_cast<const uint4*>(pr + D / 2 + i0 + 4);
+        const uint32_t pf[8] = {pf0.x, pf0.y, pf0.z, pf0.w, pf1.x, pf1.y, pf1.z, pf1.w};
+        const uint32_t pb[8] = {pb0.x, pb0.y, pb0.z, pb0.w, pb1.x, pb1.y, pb1.z, pb1.w};
+        float yf[8], yb[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const f2_t a = h2f(pf[k]), bb = h2f(pb[k]);          // (offset, scale)
+            const float xf = fmaf(cf[k], a.y, a.x), xb = fmaf(cb[k], bb.y, bb.x);
+            yf[k] = xf * cs[k].x - xb * cs[k].y;
+            yb[k] = xb * cs[k].x + xf * cs[k].y;
+        }
+        uint32_t h1[4], l1[4], h2[4], l2[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            h1[k] = bf16x2_rne(yf[2 * k], yf[2 * k + 1]);
+            l1[k] = bf16x2_rne(yf[2 * k] - bf16lo(h1[k]), yf[2 * k + 1] - bf16hi(h1[k]));
+            h2[k] = bf16x2_rne(yb[2 * k], yb[2 * k + 1]);
+            l2[k] = bf16x2_rne(yb[2 * k] - bf16lo(h2[k]), yb[2 * k + 1] - bf16hi(h2[k]));
+        }
+        hf = u4_t{h1[0], h1[1], h1[2], h1[3]};
+        lf = u4_t{l1[0], l1[1], l1[2], l1[3]};
+        hs = u4_t{h2[0], h2[1], h2[2], h2[3]};
+        ls = u4_t{l2[0], l2[1], l2[2], l2[3]};
+    };
+
     auto process_q = [&](const Job& j, const Raw& R) __attribute__((always_inline)) {
         // (1) q * sclK for every (item, head, channel) once, split into bf16 high + low
-        //     rows of the wave's operand block; key-offset bias sum_c q_c offK_c per row
-        {
+        //     rows of the wave's operand block; key-offset bias sum_c q_c offK_c per row.
+        //     RoPE mode: instead the query turned back by the chunk's first position A,
+        //     R(A)^T q, whose product with the keys turned by their offset u in the chunk
+        //     equals q . R(A + u) k; the key parameters go to LDS for the dequantization.
+        if constexpr (ROPE) {
+            constexpr int H2 = D / 2;
+            const bool first = pch0 < H2;
+            const uint16_t* qrow = &qs[wave][16 + phead][0];
+            uint32_t hw[CPL / 2], lw2[CPL / 2];
+#pragma unroll
+            for (int x = 0; x < CPL / 2; ++x) {
+                float qa[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int ch = pch0 + 2 * x + e, pc = first ? ch + H2 : ch - H2;
+                    const float qv = bf16_to_f32(qrow[ch]), qp = bf16_to_f32(qrow[pc]);
+                    const float c = __uint_as_float(R.w[S::O_CS + 4 * x + 2 * e]);
+                    const float sn = __uint_as_float(R.w[S::O_CS + 4 * x + 2 * e + 1]);
+                    qa[e] = (first ? fmaf(qp, sn, qv * c) : fmaf(-qp, sn, qv * c)) * scale;
+                }
+                hw[x] = bf16x2_trunc(qa[0], qa[1]);
+                lw2[x] = bf16x2_rne(qa[0] - bf16lo(hw[x]), qa[1] - bf16hi(hw[x]));
+            }
+            wave_lds_fence();
+            stw<CPL / 2>(&qs[wave][pitem * SW + phead][CPL * pcb], hw);
+            stw<CPL / 2>(&qs[wave][pitem * SW + SW - 1 - phead][CPL * pcb], lw2);
+            if (phead == 0) {
+#pragma unroll
+                for (int x = 0; x < CPL / 2; ++x) {
+                    const uint32_t o = R.w[S::O_KO + x], sc = R.w[S::O_KS + x];
+                    prm[wave][pitem][pch0 + 2 * x] = (o & 0xFFFFu) | (sc << 16);
+                    prm[wave][pitem][pch0 + 2 * x + 1] = (o >> 16) | (sc & 0xFFFF0000u);
+                }
+            }
+            wave_lds_fence();
+        } else {
             float bias = 0.f;
             uint32_t hw[CPL / 2], lw2[CPL / 2];
 #pragma unroll
@@ -537,16 +685,38 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             bqa[ks] = *reinterpret_cast<const u4_t*>(qrow_a + 8 * ks);
             if constexpr (NSLOT == 2) bqb[ks] = *reinterpret_cast<const u4_t*>(qrow_b + 8 * ks);
         }
-        const float c0 = hi ? kb[wave][n] : 0.f;   // key-offset bias, once per head (high column)
-        // (3) scores S^T[token][column] = codes . (q * sclK) + bias, log2 units
+        const float c0 = (hi && !ROPE) ? kb[wave][n] : 0.f;   // key-offset bias, once per head (high column)
+        // (3) scores S^T[token][column] = codes . (q * sclK) + bias, log2 units.  RoPE mode:
+        //     dequantized keys turned by their offset u in the chunk, times R(A)^T q
         float s[NV];
 #pragma unroll
         for (int tc = 0; tc < TPC; ++tc) {
             f4_t d = {c0, c0, c0, c0};
+            if constexpr (ROPE) {
+                const int u = 16 * tc + n;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                d = mfma32(key_codes(R.w, tc, ks), bqa[ks], d);
-                if constexpr (NSLOT == 2) d = mfma32(key_codes(R.w + S::KCW, tc, ks), bqb[ks], d);
+                for (int ks = 0; ks < KS / 2; ++ks) {
+                    const float2* cs = &ctab[u * (D / 2) + qg * (CQ / 2) + 8 * ks];
+                    u4_t hf, lf, hs, ls;
+                    rope_keys(R.w, &prm[wave][0][0], tc, ks, cs, hf, lf, hs, ls);
+                    d = mfma32(hf, bqa[ks], d);
+                    d = mfma32(lf, bqa[ks], d);
+                    d = mfma32(hs, bqa[ks + KS / 2], d);
+                    d = mfma32(ls, bqa[ks + KS / 2], d);
+                    if constexpr (NSLOT == 2) {
+                        rope_keys(R.w + S::KCW, &prm[wave][1][0], tc, ks, cs, hf, lf, hs, ls);
+                        d = mfma32(hf, bqb[ks], d);
+                        d = mfma32(lf, bqb[ks], d);
+                        d = mfma32(hs, bqb[ks + KS / 2], d);
+                        d = mfma32(ls, bqb[ks + KS / 2], d);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    d = mfma32(key_codes(R.w, tc, ks), bqa[ks], d);
+                    if constexpr (NSLOT == 2) d = mfma32(key_codes(R.w + S::KCW, tc, ks), bqb[ks], d);
+                }
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) s[4 * tc + i] = d[i] + mirror<SW>(d[i]);   // high + low query parts
@@ -759,15 +929,18 @@ hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t
                          const uint16_t* v_new, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const dim3 grid(g.n_splits, g.h_kv, g.B), block(64 * DW);
     const int G = g.h_q / g.h_kv, TPC = lay_tpc(g.W);
-#define QV_DEC1(D_, G_, T_, B_)                                                                \
-    if (g.d == D_ && G == G_ && TPC == T_ && g.qbits == B_) {                                  \
+    const bool rope = (g.flags & QEVICT_F_ROPE) != 0;
+#define QV_DEC2(D_, G_, T_, B_, R_)                                                            \
+    if (g.d == D_ && G == G_ && TPC == T_ && g.qbits == B_ && rope == R_) {                    \
         if (ev0)                                                                               \
-            hipExtLaunchKernelGGL((k_decode_split<D_, G_, T_, B_>), grid, block, 0, s, ev0, ev1, 0, g, bf, layer, \
-                                  q, k_new, v_new);                                            \
+            hipExtLaunchKernelGGL((k_decode_split<D_, G_, T_, B_, R_>), grid, block, 0, s, ev0, ev1, 0, g, bf, \
+                                  layer, q, k_new, v_new);                                     \
         else                                                                                   \
-            hipLaunchKernelGGL((k_decode_split<D_, G_, T_, B_>), grid, block, 0, s, g, bf, layer, q, k_new, v_new); \
+            hipLaunchKernelGGL((k_decode_split<D_, G_, T_, B_, R_>), grid, block, 0, s, g, bf, layer, q, k_new, \
+                               v_new);                                                         \
         return hipGetLastError();                                                              \
     }
+#define QV_DEC1(D_, G_, T_, B_) QV_DEC2(D_, G_, T_, B_, false) QV_DEC2(D_, G_, T_, B_, true)
 #define QV_DEC(D_, G_, T_) QV_DEC1(D_, G_, T_, 2) QV_DEC1(D_, G_, T_, 4)
     QV_DEC(128, 1, 2) QV_DEC(128, 2, 2) QV_DEC(128, 4, 2) QV_DEC(128, 8, 2)
     QV_DEC(64, 1, 2) QV_DEC(64, 2, 2) QV_DEC(64, 4, 2) QV_DEC(64, 8, 2)
@@ -775,6 +948,7 @@ hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t
     QV_DEC(64, 1, 1) QV_DEC(64, 2, 1) QV_DEC(64, 4, 1) QV_DEC(64, 8, 1)
 #undef QV_DEC
 #undef QV_DEC1
+#undef QV_DEC2
     return hipErrorInvalidValue;
 }
 
@@ -921,8 +1095,10 @@ hipError_t launch_finish(const Geo& g, const Bufs& bf, int layer, float* out, co
                          const uint16_t* v_new, int score_now, hipStream_t s) {
     if (g.n_splits > FN_MAXS) return hipErrorInvalidValue;
     const dim3 grid(g.h_q, g.B), block(FN_THREADS);
-    if (g.d == 128) hipLaunchKernelGGL(k_finish<128>, grid, block, 0, s, g, bf, layer, out, k_new, v_new, score_now);
-    else if (g.d == 64) hipLaunchKernelGGL(k_finish<64>, grid, block, 0, s, g, bf, layer, out, k_new, v_new, score_now);
+    // RoPE mode: the key the split kernel turned (layer slice of [L][B][h_kv][d])
+    const uint16_t* ks = (g.flags & QEVICT_F_ROPE) ? bf.krot + (int64_t)layer * g.B * g.h_kv * g.d : k_new;
+    if (g.d == 128) hipLaunchKernelGGL(k_finish<128>, grid, block, 0, s, g, bf, layer, out, ks, v_new, score_now);
+    else if (g.d == 64) hipLaunchKernelGGL(k_finish<64>, grid, block, 0, s, g, bf, layer, out, ks, v_new, score_now);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -103,7 +103,7 @@ struct Layout {
 };
 
 enum { O_HDR, O_WIN, O_SCORE, O_ACC, O_SPLITS, O_FPAGE, O_FSLOT, O_PACK, O_FILL, O_TARGET, O_LSEW, O_LSEG,
-       O_PML, O_PACC, O_PAGES, O_SLOTS, O_SINKS, O_PLENS, O_KF, O_KQ, O_SBLK, O_UACC, O_COUNT };
+       O_PML, O_PACC, O_PAGES, O_SLOTS, O_SINKS, O_PLENS, O_KF, O_KQ, O_SBLK, O_UACC, O_ROPE, O_KROT, O_COUNT };
 
 qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, Layout* lay) {
     qevict_status s = validate(c);
@@ -145,6 +145,7 @@ qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, La
     g.n_splits = ns;
     g.page_elems = g.h_kv * 2 * g.W * g.d;
     g.qbits = (c->flags & QEVICT_F_INT4) ? 4 : 2;
+    g.n_rope = (c->flags & QEVICT_F_ROPE) ? std::max(32, c->max_prompt + c->max_new) : 0;
     g.slot_head_bytes = 2 * lay_code_bytes(g.W, g.d, g.qbits) + 4 * g.d + 4 * g.W;
     g.slot_bytes = g.h_kv * g.slot_head_bytes;
     g.sink_elems = g.h_kv * 2 * sink_width(g.n_sink) * g.d;
@@ -170,6 +171,8 @@ qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, La
     sz[O_SINKS] = U * (size_t)g.sink_elems * 2;
     sz[O_PLENS] = sz[O_KF] = sz[O_KQ] = g.B * sizeof(int32_t);
     sz[O_SBLK] = U * (size_t)g.n_splits * SPLIT_BLOCK * sizeof(AccEntry);
+    sz[O_ROPE] = (size_t)g.n_rope * (g.d / 2) * sizeof(float2);
+    sz[O_KROT] = g.n_rope ? U * g.h_kv * (size_t)g.d * 2 : 0;
     size_t at = 0;
     for (int i = 0; i < O_COUNT; ++i) {
         lay->off[i] = at;
@@ -205,6 +208,8 @@ Bufs bind_bufs(const Layout& lay, void* arena) {
     b.slots = (uint8_t*)(a + lay.off[O_SLOTS]);
     b.sinks = (uint16_t*)(a + lay.off[O_SINKS]);
     b.split_blk = (AccEntry*)(a + lay.off[O_SBLK]);
+    b.rope = lay.g.n_rope ? (const float2*)(a + lay.off[O_ROPE]) : nullptr;
+    b.krot = lay.g.n_rope ? (uint16_t*)(a + lay.off[O_KROT]) : nullptr;
     return b;
 }
 
@@ -218,6 +223,7 @@ struct qevict_state {
     std::vector<int32_t> prompt_lens, K_f, K_q;
     std::vector<int32_t> steps;
     std::vector<uint8_t> prefilled;
+    bool rope_set = false;                                // RoPE mode: table copied in
     hipEvent_t ev_before = nullptr, ev_after = nullptr;   // one-shot timing of the split kernel
 };
 
@@ -325,19 +331,22 @@ qevict_status qevict_prefill_init(qevict_state* st, int32_t layer, const void* q
     if (st->prefilled[layer]) return fail(QEVICT_E_STATE, "layer %d already initialised", layer);
     if (st->cfg.max_prompt > 0 && (!k_prompt || !v_prompt))
         return fail(QEVICT_E_INVALID, "null prompt key/value buffer");
-    if (!score_init) {
-        if (st->cfg.max_prompt > 0 && !q_prompt) return fail(QEVICT_E_INVALID, "null prompt query buffer");
-        if (ws_bytes < prefill_ws_bytes(st->lay.g) || (!workspace && prefill_ws_bytes(st->lay.g)))
+    const Geo& g = st->lay.g;
+    const bool rope = (g.flags & QEVICT_F_ROPE) != 0;
+    if (rope && !st->rope_set) return fail(QEVICT_E_STATE, "RoPE mode: qevict_set_rope must come before prefill");
+    if (!score_init && st->cfg.max_prompt > 0 && !q_prompt) return fail(QEVICT_E_INVALID, "null prompt query buffer");
+    if (!score_init || rope) {
+        if (ws_bytes < prefill_ws_bytes(g) || (!workspace && prefill_ws_bytes(g)))
             return fail(QEVICT_E_CAPACITY, "prefill workspace of %zu bytes < %zu required", ws_bytes,
-                        prefill_ws_bytes(st->lay.g));
+                        prefill_ws_bytes(g));
     }
     hipStream_t hs = (hipStream_t)stream;
-    const Geo& g = st->lay.g;
-    HIP_TRY(launch_prefill_setup(g, st->bf, layer, (const uint16_t*)k_prompt, (const uint16_t*)v_prompt, hs));
-    HIP_TRY(launch_prefill_scores(g, st->bf, layer, (const uint16_t*)q_prompt, (const uint16_t*)k_prompt, score_init,
-                                  workspace, hs));
+    const uint16_t *qp = (const uint16_t*)q_prompt, *kp = (const uint16_t*)k_prompt;
+    if (rope) HIP_TRY(launch_rope_prompt(g, st->bf, score_init ? nullptr : qp, kp, workspace, &qp, &kp, hs));
+    HIP_TRY(launch_prefill_setup(g, st->bf, layer, kp, (const uint16_t*)v_prompt, hs));
+    HIP_TRY(launch_prefill_scores(g, st->bf, layer, qp, kp, score_init, workspace, hs));
     HIP_TRY(launch_route(g, st->bf, layer, RM_PREFILL, hs));
-    HIP_TRY(launch_migrate(g, st->bf, layer, (const uint16_t*)k_prompt, (const uint16_t*)v_prompt, hs));
+    HIP_TRY(launch_migrate(g, st->bf, layer, kp, (const uint16_t*)v_prompt, hs));
     st->prefilled[layer] = 1;
     st->steps[layer] = 0;
     return QEVICT_OK;
@@ -363,6 +372,20 @@ qevict_status qevict_decode_attn(qevict_state* st, int32_t layer, const void* q,
                           !(g.flags & QEVICT_F_RANK_KEYNORM);   // the key-norm ranker uses no mass
     HIP_TRY(launch_finish(g, st->bf, layer, out, (const uint16_t*)k_new, (const uint16_t*)v_new, score_now, hs));
     st->steps[layer] += 1;
+    return QEVICT_OK;
+}
+
+qevict_status qevict_set_rope(qevict_state* st, const float* cos_sin, int32_t n_pos, void* stream) {
+    if (!st) return fail(QEVICT_E_INVALID, "null state");
+    const Geo& g = st->lay.g;
+    if (!(g.flags & QEVICT_F_ROPE)) return fail(QEVICT_E_STATE, "the state was created without QEVICT_F_ROPE");
+    if (!cos_sin) return fail(QEVICT_E_INVALID, "null RoPE table");
+    if (n_pos < g.n_rope)
+        return fail(QEVICT_E_INVALID, "RoPE table of %d positions < %d needed (max(32, max_prompt + max_new))", n_pos,
+                    g.n_rope);
+    HIP_TRY(hipMemcpyAsync(st->arena + st->lay.off[O_ROPE], cos_sin, (size_t)g.n_rope * (g.d / 2) * sizeof(float2),
+                           hipMemcpyDefault, (hipStream_t)stream));
+    st->rope_set = true;
     return QEVICT_OK;
 }
 
@@ -522,7 +545,8 @@ qevict_status qevict_export_unit(qevict_state* st, int32_t layer, int32_t b, voi
                 const int cb = lay_code_bytes(g.W, g.d, qb);
                 for (int t = 0; t < g.W; ++t)
                     for (int c = 0; c < g.d; ++c) {
-                        const int kc = (src[lay_kc_byte(t, c, g.d, g.W, qb)] >> lay_kc_shift(c, qb)) & mask;
+                        const int kc = (src[lay_kc_byte(t, c, g.d, g.W, qb, (g.flags & QEVICT_F_ROPE) != 0)] >>
+                                        lay_kc_shift(c, qb)) & mask;
                         const int vc = (src[cb + lay_vc_byte(t, c, g.d, g.W, qb)] >> lay_vc_shift(t, qb)) & mask;
                         dst[t * (g.d / P) + c / P] |= (uint8_t)(kc << (qb * (c % P)));
                         dst[cb + t * (g.d / P) + c / P] |= (uint8_t)(vc << (qb * (c % P)));

@@ -83,6 +83,7 @@ struct Geo {
     int32_t sink_elems;   // h_kv * 2 * Ws * d, Ws = sink_width(n_sink)
     uint32_t flags;
     int32_t qbits;        // bits per Quantized-tier code: 2, or 4 with QEVICT_F_INT4
+    int32_t n_rope;       // rows of the RoPE table (0 without QEVICT_F_ROPE)
 };
 
 // Device pointers to the per-unit arrays (index by unit = b * L + l).
@@ -106,6 +107,8 @@ struct Bufs {
     uint16_t* pages;        // [U][n_pages][h_kv][2][W][d]   bf16
     uint8_t* slots;         // [U][n_slots][h_kv][slot_head_bytes]
     uint16_t* sinks;        // [U][h_kv] pages of Ws tokens (same layout as a window page)
+    const float2* rope;     // RoPE mode: (cos, sin) [n_rope][d/2], n_rope >= max(32, max_prompt + max_new)
+    uint16_t* krot;         // RoPE mode: [U][h_kv][d] the step's key after RoPE (split kernel -> finish)
 };
 
 __host__ __device__ inline int64_t unit_of(const Geo& g, int b, int l) { return (int64_t)b * g.L + l; }
@@ -134,6 +137,7 @@ constexpr int SPLIT_BLOCK = 64;
 // Quantized slot of one head, b-bit codes (b = 2 or 4, P = 8/b codes per byte; same byte
 // count as the canonical record):
 //   K codes [W*D*b/8]: code (t, c) in byte (((ch*16 + r)*4 + qg)*TPC + tc)*(CQ/P) + cc/P, bits b*(cc%P)
+//             ((qg, cc) from lay_kc_pos: c = CQ*qg + cc, or the RoPE pairing)
 //   V codes [W*D*b/8]: code (t, c) in byte (((((c%16)*4 + r/4)*NCH + ch)*MB + c/16)*TPC + tc)*(4/P) + (r%4)/P,
 //             bits b*(r%P) (a lane reads, per chunk, MB x TPC x 4/P bytes: the 4 tokens of row group
 //             r/4 of each tile of the chunk, per channel block)
@@ -149,10 +153,28 @@ __host__ __device__ inline int lay_v(int t, int c, int D, int W) {
     const int NT = W / 16, MB = D / 16;
     return ((((c & 15) * 4 + (t & 15) / 4) * NT + (t >> 4)) * MB + c / 16) * 4 + (t & 3);
 }
-__host__ __device__ inline int lay_kc_byte(int t, int c, int D, int W, int b) {
+// Key channel c -> (lane group qg, position cc in the group's CQ channels).  In RoPE mode
+// a group holds CQ/2 channels of the first half and their RoPE partners c + D/2, so that
+// a lane rotates its keys without exchanging values.
+__host__ __device__ inline void lay_kc_pos(int c, int D, bool rope, int& qg, int& cc) {
+    const int CQ = D / 4;
+    if (!rope) {
+        qg = c / CQ;
+        cc = c % CQ;
+    } else if (c < D / 2) {
+        qg = c / (CQ / 2);
+        cc = c % (CQ / 2);
+    } else {
+        qg = (c - D / 2) / (CQ / 2);
+        cc = CQ / 2 + (c - D / 2) % (CQ / 2);
+    }
+}
+__host__ __device__ inline int lay_kc_byte(int t, int c, int D, int W, int b, bool rope = false) {
     const int CQ = D / 4, TPC = lay_tpc(W), P = 8 / b;
     const int ch = t / (16 * TPC), tc = (t / 16) % TPC, r = t & 15;
-    return (((ch * 16 + r) * 4 + c / CQ) * TPC + tc) * (CQ / P) + (c % CQ) / P;
+    int qg, cc;
+    lay_kc_pos(c, D, rope, qg, cc);
+    return (((ch * 16 + r) * 4 + qg) * TPC + tc) * (CQ / P) + cc / P;
 }
 __host__ __device__ inline int lay_kc_shift(int c, int b) { return b * (c % (8 / b)); }
 __host__ __device__ inline int lay_vc_byte(int t, int c, int D, int W, int b) {
@@ -182,6 +204,10 @@ __host__ __device__ inline double* mass_target(const Geo& g, const Bufs& bf) {
 }
 
 // ---------------------------------------------------------------- launchers (host side)
+size_t rope_ws_offset(const Geo& g);
+size_t rope_ws_bytes(const Geo& g);
+hipError_t launch_rope_prompt(const Geo& g, const Bufs& bf, const uint16_t* qp, const uint16_t* kp, void* ws,
+                              const uint16_t** qr, const uint16_t** kr, hipStream_t s);
 hipError_t launch_init(const Geo& g, const Bufs& bf, const int32_t* prompt_lens_dev, const int32_t* kf_dev,
                        const int32_t* kq_dev, hipStream_t s);
 // ev0 / ev1 (optional): events stamped by the split kernel's own dispatch at its start and end

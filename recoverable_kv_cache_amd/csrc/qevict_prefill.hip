@@ -262,7 +262,50 @@ __global__ void __launch_bounds__(256) k_prefill_keynorm(Geo g, Bufs bf, int lay
 
 size_t prefill_ws_bytes(const Geo& g) {
     const size_t n = (size_t)g.B * g.h_q * g.S_max;
-    return ((n * 4 + 255) & ~size_t(255)) + n * 8;
+    size_t at = ((n * 4 + 255) & ~size_t(255)) + ((n * 8 + 255) & ~size_t(255));
+    if (g.n_rope) at += rope_ws_bytes(g);
+    return at;
+}
+
+// the RoPE-mode prompt copies in the workspace: queries [B][h_q][S_max][d], then keys
+// [B][h_kv][S_max][d] (bf16, rotated)
+size_t rope_ws_offset(const Geo& g) {
+    const size_t n = (size_t)g.B * g.h_q * g.S_max;
+    return ((n * 4 + 255) & ~size_t(255)) + ((n * 8 + 255) & ~size_t(255));
+}
+size_t rope_ws_bytes(const Geo& g) {
+    const size_t nq = (size_t)g.B * g.h_q * g.S_max * g.d * 2, nk = (size_t)g.B * g.h_kv * g.S_max * g.d * 2;
+    return ((nq + 255) & ~size_t(255)) + ((nk + 255) & ~size_t(255));
+}
+
+// RoPE of a prompt tensor [B][H][S_max][d] (bf16 in, bf16 out): each thread turns one
+// channel pair (i, i + d/2) of one position, exactly in fp64, rounded once to bf16.
+__global__ void __launch_bounds__(256) k_rope_prompt(Geo g, Bufs bf, const uint16_t* __restrict__ x,
+                                                      uint16_t* __restrict__ y, int H) {
+    const int h = g.d / 2;
+    const int64_t n_pairs = (int64_t)g.B * H * g.S_max * h;
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n_pairs; e += (int64_t)gridDim.x * blockDim.x) {
+        const int i = (int)(e % h);
+        const int64_t row = e / h;                      // (b, head, p)
+        const int p = (int)(row % g.S_max);
+        const float2 cs = bf.rope[(int64_t)p * h + i];
+        const double a = (double)bf16_to_f32(x[row * g.d + i]), b = (double)bf16_to_f32(x[row * g.d + i + h]);
+        y[row * g.d + i] = f64_to_bf16(__dsub_rn(__dmul_rn(a, (double)cs.x), __dmul_rn(b, (double)cs.y)));
+        y[row * g.d + i + h] = f64_to_bf16(__dadd_rn(__dmul_rn(b, (double)cs.x), __dmul_rn(a, (double)cs.y)));
+    }
+}
+
+hipError_t launch_rope_prompt(const Geo& g, const Bufs& bf, const uint16_t* qp, const uint16_t* kp, void* ws,
+                              const uint16_t** qr, const uint16_t** kr, hipStream_t s) {
+    uint16_t* q_out = (uint16_t*)((char*)ws + rope_ws_offset(g));
+    const size_t nq = (size_t)g.B * g.h_q * g.S_max * g.d * 2;
+    uint16_t* k_out = (uint16_t*)((char*)q_out + ((nq + 255) & ~size_t(255)));
+    *qr = qp ? q_out : nullptr;
+    *kr = k_out;
+    if (g.S_max == 0) return hipSuccess;
+    if (qp) hipLaunchKernelGGL(k_rope_prompt, dim3(2048), dim3(256), 0, s, g, bf, qp, q_out, g.h_q);
+    hipLaunchKernelGGL(k_rope_prompt, dim3(2048), dim3(256), 0, s, g, bf, kp, k_out, g.h_kv);
+    return hipGetLastError();
 }
 
 hipError_t launch_prefill_scores(const Geo& g, const Bufs& bf, int layer, const uint16_t* qp, const uint16_t* kp,

@@ -646,6 +646,18 @@ __global__ void __launch_bounds__(PK_THREADS) k_pack(Geo g, Bufs bf, int layer, 
         uint16_t* offV = sclK + d;
         uint16_t* sclV = offV + W;
         bool bad = false;
+        // keys as quantized: the stored (bf16) values, or in RoPE mode those values turned
+        // back to the pre-RoPE domain at their positions (exact products, one rounding)
+        const bool rope = (g.flags & QEVICT_F_ROPE) != 0;
+        const int hd = d / 2;
+        auto key_at = [&](int t, int c) -> double {
+            if (!rope) return (double)bf16_to_f32(sk[t * d + c]);
+            const int i = c < hd ? c : c - hd;
+            const float2 cs = bf.rope[(int64_t)(start + t) * hd + i];
+            const double a = (double)bf16_to_f32(sk[t * d + i]), b = (double)bf16_to_f32(sk[t * d + i + hd]);
+            return c < hd ? __dadd_rn(__dmul_rn(a, (double)cs.x), __dmul_rn(b, (double)cs.y))
+                          : __dsub_rn(__dmul_rn(b, (double)cs.x), __dmul_rn(a, (double)cs.y));
+        };
         // parameters: threads [0, d) take a key channel each (over the W tokens), threads
         // [d, d + W) a value token each (over the d channels)
         const int tid = threadIdx.x;
@@ -653,17 +665,18 @@ __global__ void __launch_bounds__(PK_THREADS) k_pack(Geo g, Bufs bf, int layer, 
             const bool key = tid < d;
             const int gi = key ? tid : tid - d;
             const int n_el = key ? W : d;
-            const uint16_t* src = key ? sk + gi : sv + gi * d;
-            const int stride = key ? d : 1;
-            float mn = bf16_to_f32(src[0]), mx = mn;
+            auto elem = [&](int i) -> double {
+                return key ? key_at(i, gi) : (double)bf16_to_f32(sv[gi * d + i]);
+            };
+            double mn = elem(0), mx = mn;
             for (int i = 1; i < n_el; ++i) {
-                const float x = bf16_to_f32(src[i * stride]);
-                mn = fminf(mn, x);
-                mx = fmaxf(mx, x);
+                const double x = elem(i);
+                mn = fmin(mn, x);
+                mx = fmax(mx, x);
             }
-            if (fabsf(mn) > 65504.f || fabsf(mx) > 65504.f) bad = true;
-            const double off = fp16_round_down((double)mn);
-            const double scl = fp16_round_up(((double)mx - off) / (double)L);
+            if (fabs(mn) > 65504.0 || fabs(mx) > 65504.0) bad = true;
+            const double off = fp16_round_down(mn);
+            const double scl = fp16_round_up((mx - off) / (double)L);
             if (fabs(off) > 65504.0 || scl > 65504.0) bad = true;
             if (key) {
                 offK[gi] = fp16_bits_exact(off);
@@ -679,7 +692,7 @@ __global__ void __launch_bounds__(PK_THREADS) k_pack(Geo g, Bufs bf, int layer, 
         // codes: every element on its own thread
         for (int e = tid; e < W * d; e += PK_THREADS) {
             const int i = e / d, c = e % d;
-            ck[e] = (uint8_t)nearest_level(2.0 * ((double)bf16_to_f32(sk[e]) - p_off[c]), p_scl[c], L);
+            ck[e] = (uint8_t)nearest_level(2.0 * (key_at(i, c) - p_off[c]), p_scl[c], L);
             cv[e] = (uint8_t)nearest_level(2.0 * ((double)bf16_to_f32(sv[e]) - p_off[d + i]), p_scl[d + i], L);
         }
         if (bad) atomicOr(&hdr->status, QEVICT_DEV_E_RANGE);
@@ -689,7 +702,7 @@ __global__ void __launch_bounds__(PK_THREADS) k_pack(Geo g, Bufs bf, int layer, 
             const int i = e / (d / P), c0 = P * (e % (d / P));
             uint32_t byte = 0;
             for (int x = 0; x < P; ++x) byte |= (uint32_t)ck[i * d + c0 + x] << (qb * x);
-            slot[lay_kc_byte(i, c0, d, W, qb)] = (uint8_t)byte;
+            slot[lay_kc_byte(i, c0, d, W, qb, rope)] = (uint8_t)byte;
         }
         // V codes: one byte = P consecutive tokens of one channel (lay_vc_byte)
         for (int e = threadIdx.x; e < cbytes; e += PK_THREADS) {
@@ -734,12 +747,24 @@ __global__ void __launch_bounds__(PK_THREADS) k_fill(Geo g, Bufs bf, int layer, 
             const uint16_t* sclK = offK + d;
             const uint16_t* offV = sclK + d;
             const uint16_t* sclV = offV + W;
+            const bool rope = (g.flags & QEVICT_F_ROPE) != 0;
+            const int hd = d / 2;
+            auto khat = [&](int i, int c) -> double {   // dequantized key (exact in fp64)
+                const int kc = (slot[lay_kc_byte(i, c, d, W, qb, rope)] >> lay_kc_shift(c, qb)) & mask;
+                return (double)fp16_bits_to_f32(offK[c]) + kc * (double)fp16_bits_to_f32(sclK[c]);
+            };
             for (int e = threadIdx.x; e < W * d; e += PK_THREADS) {
                 const int i = e / d, c = e % d;
-                const int kc = (slot[lay_kc_byte(i, c, d, W, qb)] >> lay_kc_shift(c, qb)) & mask;
                 const int vc = (slot[cbytes + lay_vc_byte(i, c, d, W, qb)] >> lay_vc_shift(i, qb)) & mask;
                 const int vp = lay_vp(i, W);
-                const double kx = (double)fp16_bits_to_f32(offK[c]) + kc * (double)fp16_bits_to_f32(sclK[c]);
+                double kx = khat(i, c);
+                if (rope) {   // RoPE re-applied at the window's positions, then one bf16 rounding
+                    const int pi = c < hd ? c : c - hd;
+                    const float2 cs = bf.rope[(int64_t)(start + i) * hd + pi];
+                    const double xp = khat(i, c < hd ? c + hd : c - hd);
+                    kx = c < hd ? __dsub_rn(__dmul_rn(kx, (double)cs.x), __dmul_rn(xp, (double)cs.y))
+                                : __dadd_rn(__dmul_rn(kx, (double)cs.x), __dmul_rn(xp, (double)cs.y));
+                }
                 const double vx = (double)fp16_bits_to_f32(offV[vp]) + vc * (double)fp16_bits_to_f32(sclV[vp]);
                 dk[lay_k(i, c, d, W)] = f64_to_bf16(kx);
                 dv[lay_v(i, c, d, W)] = f64_to_bf16(vx);

@@ -69,7 +69,7 @@ def compare_unit(ex: B.UnitExport, unit: O.UnitOracle, tag: str, check_scores=Tr
 
 class Lockstep:
     def __init__(self, wl: WL.Workload, layer: int = 0, score_init=None, flags: int = 0, n_splits: int = 0,
-                 ocfg_over=None, device="cuda", n_layers=1):
+                 ocfg_over=None, device="cuda", n_layers=1, rope_theta=WL.ROPE_THETA):
         self.wl = wl
         self.layer = layer
         self.lens = wl.prompt_lens()
@@ -79,10 +79,15 @@ class Lockstep:
                   else "keynorm" if flags & B.QEVICT_F_RANK_KEYNORM else "cum")
         ocfg = cfg_from(wl, promote=not (flags & B.QEVICT_F_NO_PROMOTE),
                         score_every_step=not (flags & B.QEVICT_F_SCORE_ROUTE_ONLY), ranker=ranker,
-                        quant_bits=4 if flags & B.QEVICT_F_INT4 else 2,
+                        quant_bits=4 if flags & B.QEVICT_F_INT4 else 2, rope=bool(flags & B.QEVICT_F_ROPE),
                         **(ocfg_over or {}))
         self.ocfg = ocfg
-        self.units = [O.UnitOracle(ocfg, S) for S in self.lens]
+        self.rope = None
+        if flags & B.QEVICT_F_ROPE:   # the rotary table: an input of both sides
+            self.rope = WL.rope_table(wl.d_head, max(32, wl.prompt_len + wl.n_decode), theta=rope_theta)
+            self.st.set_rope(self.rope.to(device))
+        cs = None if self.rope is None else self.rope.numpy()
+        self.units = [O.UnitOracle(ocfg, S, rope_cs=cs) for S in self.lens]
         self.score_init = score_init
         self.max_o_err = 0.0
         self.max_s_err = 0.0

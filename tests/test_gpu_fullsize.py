@@ -93,3 +93,18 @@ def test_llama8b_32k_int4_decode_and_route_lockstep():
     for j in range(8):
         ls.step(j)
     print(f"32K int4: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}", flush=True)
+
+
+def test_llama8b_32k_rope_decode_and_route_lockstep():
+    """The full-size lockstep with pre-RoPE inputs and the RoPE-faithful Quantized tier
+    (rotary base 500000, positions up to 33 279)."""
+    print("case: 32K rope decode lockstep", flush=True)
+    n_win = (WL32.prompt_len - WL32.n_sink + WL32.window - 1) // WL32.window
+    si = WL.init_scores(WL32, 0, n_win)
+    ls = Lockstep(WL32, score_init=si, flags=B.QEVICT_F_ROPE)
+    ls.prefill()
+    ex = ls.st.export_unit(0, 0)
+    assert ex.counters["packed"] == ls.units[0].events[0]["packed"] > 800
+    for j in range(8):
+        ls.step(j)
+    print(f"32K rope: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}", flush=True)

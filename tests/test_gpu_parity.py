@@ -241,3 +241,37 @@ def test_int4_tier_lockstep(case):
     if flat:
         assert sum(e["promoted"] for u in ls.units for e in u.events) > 0
     _print(f"int4 {case}: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}")
+
+
+ROPE_CASES = {
+    # d = 64, W = 16, G = 4, flat initial scores + drift: promotions re-rotate dequantized keys
+    "tiny_drift": (WL.TINY.with_(n_topics=4, topic_period=16, n_decode=64, n_outlier=2, budget_frac=0.30), True, 0, 64),
+    # d = 128, W = 32, G = 8, ragged batch, INT2
+    "gqa8_d128": (WL.Workload("r2", 1, 2, 16, 2, 128, 640, 24, 32, 4, 64, 8, 0.30, 0.70, prompt_len_min=300,
+                              n_outlier=2, n_topics=2, topic_period=8), False, 0, 24),
+    # d = 128, W = 64, G = 4 (two column slots), INT4
+    "w64_int4": (WL.Workload("r4", 1, 1, 8, 2, 128, 1200, 24, 64, 4, 128, 8, 0.30, 0.70,
+                             n_outlier=2, n_topics=2, topic_period=8), False, B.QEVICT_F_INT4, 24),
+    # d = 64, W = 32, G = 2, INT2
+    "d64_w32": (WL.Workload("r5", 1, 2, 4, 2, 64, 600, 32, 32, 4, 64, 8, 0.35, 0.70, prompt_len_min=350,
+                            n_outlier=2, n_topics=2, topic_period=8), False, 0, 32),
+}
+
+
+@pytest.mark.parametrize("case", list(ROPE_CASES))
+def test_rope_faithful_quantized_tier_lockstep(case):
+    """Queries and keys handed over before RoPE ([QEvict] §4.3): cached keys rotated,
+    the Quantized tier packed from keys turned back to the pre-RoPE domain and re-rotated
+    inside attention and on promotion; routing, codes, ledgers and pages bit-exact,
+    outputs within 2e-3 of ||o||."""
+    wl, flat, extra, steps = ROPE_CASES[case]
+    _print(f"case: rope {case}")
+    si = None
+    if flat:
+        n_win = math.ceil((wl.prompt_len + wl.n_decode - wl.n_sink) / wl.window)
+        si = torch.zeros((wl.batch, n_win), dtype=torch.float64)
+    ls = Lockstep(wl, score_init=si, flags=B.QEVICT_F_ROPE | extra).run(steps)
+    assert any(u.win[w].ledger is not None for u in ls.units for w in u.win)
+    if flat:
+        assert sum(e["promoted"] for u in ls.units for e in u.events) > 0
+    _print(f"rope {case}: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}")
