@@ -253,6 +253,15 @@ qevict_status qevict_step_bytes(qevict_state* st, int32_t layer, int64_t* kv_byt
  * ev_before / ev_after (hipEvent_t with timing; both or neither) the kernel's own
  * dispatch stamps its start and end, as for qevict_time_next_decode.  Enqueues on
  * `stream`; argument errors return QEVICT_E_INVALID before anything is enqueued. */
+/* Diagnostics ([QEvict] Appendix I, Eqs. 12-13): per-head attention mass of the last
+ * decode step of (layer, sequence b) on the sinks and on each window.
+ *   out [h_q][n_windows + 1] fp64, device: column 0 the sinks, column 1 + w window w
+ *   (the step's probabilities summed over the window's tokens), 0 for windows the step
+ *   did not attend (Evicted, not yet created).  Each row sums to 1 up to rounding.
+ * Valid after qevict_decode_attn and before the next routing of that layer
+ * (QEVICT_E_STATE otherwise).  Runs on `stream`. */
+qevict_status qevict_step_mass(qevict_state* st, int32_t layer, int32_t b, double* out, void* stream);
+
 /* RoPE mode (QEVICT_F_ROPE): copy the rotary table into the state.
  *   cos_sin: [n_pos][d_head/2][2] fp32 (cos, sin) of position p, pair i (channels i and
  *            i + d_head/2), device or host memory, read before the call returns on `stream`;

@@ -32,7 +32,7 @@ EXPORTED_SYMBOLS = (
     "qevict_capacities", "qevict_plan", "qevict_create", "qevict_destroy", "qevict_prefill_init",
     "qevict_decode_attn", "qevict_route", "qevict_pack_int2", "qevict_promote", "qevict_poll_status",
     "qevict_export_unit", "qevict_decode_kernel_name", "qevict_last_error", "qevict_time_next_decode",
-    "qevict_step_bytes", "qevict_stream_read", "qevict_set_rope",
+    "qevict_step_bytes", "qevict_stream_read", "qevict_set_rope", "qevict_step_mass",
 )
 
 
@@ -93,6 +93,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qevict_step_bytes.argtypes = [P, I, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64), P]
     lib.qevict_stream_read.argtypes = [P, Z, P, P, P, P]
     lib.qevict_set_rope.argtypes = [P, P, I, P]
+    lib.qevict_step_mass.argtypes = [P, I, I, P, P]
     lib.qevict_decode_kernel_name.restype = ctypes.c_char_p
     lib.qevict_last_error.restype = ctypes.c_char_p
     for name in EXPORTED_SYMBOLS:
@@ -265,6 +266,16 @@ class QEvictState:
         _check(self.lib.qevict_prefill_init(self.handle, layer, _ptr(q), _ptr(k), _ptr(v), _ptr(score_init),
                                             _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
 
+    def step_mass(self, layer: int, b: int, out=None, stream=None):
+        """Per-head mass of the last decode step: ``[h_q][n_windows + 1]`` float64 on the
+        device (column 0 the sinks, 1 + w window w)."""
+        import torch
+        if out is None:
+            out = torch.empty((self.cfg.h_q, self.info.n_windows + 1), dtype=torch.float64, device=self.device)
+        _expect(out, (self.cfg.h_q, self.info.n_windows + 1), "float64", self.device, "step mass")
+        _check(self.lib.qevict_step_mass(self.handle, layer, b, _ptr(out), _stream(stream)))
+        return out
+
     def set_rope(self, table, stream=None):
         """RoPE mode: copy the (cos, sin) table ``[n_pos][d/2][2]`` (float32, on the device)."""
         _expect(table, (table.shape[0], self.cfg.d_head // 2, 2), "float32", self.device, "rope table")
@@ -306,15 +317,17 @@ class QEvictState:
         _check(self.lib.qevict_poll_status(self.handle, ctypes.byref(s), _stream(stream)))
         return s.value
 
-    def export_unit(self, layer: int, b: int, stream=None) -> UnitExport:
+    def export_unit(self, layer: int, b: int, stream=None, tables_only: bool = False) -> UnitExport:
+        """The unit's canonical export; ``tables_only`` parses the header, window records
+        and scores only (ledgers, pages and sinks are left empty)."""
         buf = (ctypes.c_uint8 * self.info.export_bytes)()
         written = ctypes.c_size_t()
         _check(self.lib.qevict_export_unit(self.handle, layer, b, buf, self.info.export_bytes,
                                            ctypes.byref(written), _stream(stream)))
-        return parse_export(bytes(buf)[: written.value], self.cfg)
+        return parse_export(bytes(buf)[: written.value], self.cfg, tables_only)
 
 
-def parse_export(blob: bytes, cfg: Config) -> UnitExport:
+def parse_export(blob: bytes, cfg: Config, tables_only: bool = False) -> UnitExport:
     head = struct.unpack_from("<20i", blob, 0)
     assert head[0] == 0x58564551, "bad export magic"
     n, nw, K_f, K_q, status = head[1:6]
@@ -326,6 +339,10 @@ def parse_export(blob: bytes, cfg: Config) -> UnitExport:
     at += 24 * nw
     state, has_led, dorm, start = (rec["i"][:, k].copy() for k in range(4))
     score = rec["s"].copy()
+    if tables_only:
+        empty = np.zeros((0,), dtype=np.uint16)
+        return UnitExport(n, nw, K_f, K_q, status, ctr, n_acc, prompt_len, sink_mass, state, has_led, dorm, start,
+                          score, {}, {}, empty, empty)
     H, W, d, ns = cfg.h_kv, cfg.window, cfg.d_head, cfg.n_sink
     qb = 4 if cfg.flags & QEVICT_F_INT4 else 2
     slot_bytes = H * (2 * W * d * qb // 8 + 4 * d + 4 * W)

@@ -1119,4 +1119,35 @@ hipError_t launch_flush_mass(const Geo& g, const Bufs& bf, int layer, int b, hip
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------ step mass
+// Per-head attention mass of the last decode step on the sinks and on every window
+// (the a_t(i) of one step summed over a window's tokens, [QEvict] Eq. 1 before the head
+// average; Appendix I uses it per head): out[h][0] sinks, out[h][1 + w] window w, zero for
+// windows the step did not attend.  From that step's window and row log-sum-exps.
+__global__ void __launch_bounds__(256) k_step_mass_clear(Geo g, double* __restrict__ out) {
+    const int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (x < (int64_t)g.h_q * (g.n_windows + 1)) out[x] = 0.0;
+}
+
+__global__ void __launch_bounds__(256) k_step_mass(Geo g, Bufs bf, int layer, int b, double* __restrict__ out) {
+    const int64_t u = unit_of(g, b, layer);
+    const UnitHdr* hdr = bf.hdr + u;
+    const int cols = g.n_windows + 1;
+    const float* lwin = bf.lse_win + lse_win_off(g, u, (hdr->n - 1) & 1);
+    const float* lg = bf.lse_glob + u * g.h_q;
+    const int x = blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= hdr->n_acc * g.h_q) return;
+    const int e = x / g.h_q, h = x % g.h_q;
+    const int w = bf.acc[u * g.n_acc_max + e].win;   // -1: the sinks
+    out[(int64_t)h * cols + 1 + w] = (double)mass_share(lwin[(int64_t)e * g.h_q + h], lg[h]);
+}
+
+hipError_t launch_step_mass(const Geo& g, const Bufs& bf, int layer, int b, double* out, hipStream_t s) {
+    const int64_t n_out = (int64_t)g.h_q * (g.n_windows + 1);
+    hipLaunchKernelGGL(k_step_mass_clear, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s, g, out);
+    const int64_t n_in = (int64_t)g.n_acc_max * g.h_q;
+    hipLaunchKernelGGL(k_step_mass, dim3((unsigned)((n_in + 255) / 256)), dim3(256), 0, s, g, bf, layer, b, out);
+    return hipGetLastError();
+}
+
 }  // namespace qv

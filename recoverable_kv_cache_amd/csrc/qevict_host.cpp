@@ -223,6 +223,7 @@ struct qevict_state {
     std::vector<int32_t> prompt_lens, K_f, K_q;
     std::vector<int32_t> steps;
     std::vector<uint8_t> prefilled;
+    std::vector<uint8_t> step_fresh;                      // per layer: a decode step and no routing since
     bool rope_set = false;                                // RoPE mode: table copied in
     hipEvent_t ev_before = nullptr, ev_after = nullptr;   // one-shot timing of the split kernel
 };
@@ -295,6 +296,7 @@ qevict_status qevict_create(const qevict_config* cfg, const int32_t* prompt_lens
     }
     st->steps.assign(cfg->n_layers, 0);
     st->prefilled.assign(cfg->n_layers, 0);
+    st->step_fresh.assign(cfg->n_layers, 0);
     hipStream_t hs = (hipStream_t)stream;
     char* a = (char*)arena;
     hipError_t e = hipMemcpyAsync(a + lay.off[O_PLENS], st->prompt_lens.data(), cfg->batch * 4, hipMemcpyHostToDevice, hs);
@@ -372,6 +374,7 @@ qevict_status qevict_decode_attn(qevict_state* st, int32_t layer, const void* q,
                           !(g.flags & QEVICT_F_RANK_KEYNORM);   // the key-norm ranker uses no mass
     HIP_TRY(launch_finish(g, st->bf, layer, out, (const uint16_t*)k_new, (const uint16_t*)v_new, score_now, hs));
     st->steps[layer] += 1;
+    st->step_fresh[layer] = 1;
     return QEVICT_OK;
 }
 
@@ -447,6 +450,19 @@ qevict_status qevict_route(qevict_state* st, int32_t layer, void* stream) {
     hipStream_t hs = (hipStream_t)stream;
     HIP_TRY(launch_route(st->lay.g, st->bf, layer, RM_ROUTE, hs));
     HIP_TRY(launch_migrate(st->lay.g, st->bf, layer, nullptr, nullptr, hs));
+    for (int l = 0; l < st->cfg.n_layers; ++l)
+        if (layer == -1 || layer == l) st->step_fresh[l] = 0;
+    return QEVICT_OK;
+}
+
+qevict_status qevict_step_mass(qevict_state* st, int32_t layer, int32_t b, double* out, void* stream) {
+    qevict_status s = check_layer(st, layer, false);
+    if (s) return s;
+    if (b < 0 || b >= st->cfg.batch) return fail(QEVICT_E_INVALID, "sequence %d outside [0, %d)", b, st->cfg.batch);
+    if (!out) return fail(QEVICT_E_INVALID, "null output");
+    if (!st->step_fresh[layer])
+        return fail(QEVICT_E_STATE, "layer %d: no decode step since the last prefill / routing", layer);
+    HIP_TRY(launch_step_mass(st->lay.g, st->bf, layer, b, out, (hipStream_t)stream));
     return QEVICT_OK;
 }
 
@@ -461,6 +477,7 @@ static qevict_status forced(qevict_state* st, int32_t layer, const int32_t* win_
     HIP_TRY(launch_force_targets(st->lay.g, st->bf, layer, win_ids, n, mode == RM_FORCE_Q ? ST_QUANT : ST_FULL, hs));
     HIP_TRY(launch_route(st->lay.g, st->bf, layer, mode, hs));
     HIP_TRY(launch_migrate(st->lay.g, st->bf, layer, nullptr, nullptr, hs));
+    st->step_fresh[layer] = 0;
     return QEVICT_OK;
 }
 

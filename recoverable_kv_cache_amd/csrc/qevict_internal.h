@@ -204,6 +204,7 @@ __host__ __device__ inline double* mass_target(const Geo& g, const Bufs& bf) {
 }
 
 // ---------------------------------------------------------------- launchers (host side)
+hipError_t launch_step_mass(const Geo& g, const Bufs& bf, int layer, int b, double* out, hipStream_t s);
 size_t rope_ws_offset(const Geo& g);
 size_t rope_ws_bytes(const Geo& g);
 hipError_t launch_rope_prompt(const Geo& g, const Bufs& bf, const uint16_t* qp, const uint16_t* kp, void* ws,

@@ -275,3 +275,44 @@ def test_rope_faithful_quantized_tier_lockstep(case):
     if flat:
         assert sum(e["promoted"] for u in ls.units for e in u.events) > 0
     _print(f"rope {case}: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}")
+
+
+@pytest.mark.parametrize("promote", [True, False], ids=["two-way", "one-way"])
+def test_diagnostics_from_the_gpu_state_match_the_oracle(promote):
+    """Appendix I diagnostics from the GPU: a policy state and an uncompressed reference
+    state decode the same tokens; the per-head step masses (qevict_step_mass), tiers and
+    scores they export give the same FMM, churn, tier shares, QSA / R_Q, Global LIR and
+    transitions as the oracle's definitions on the oracle's own run."""
+    from recoverable_kv_cache_amd import diagnostics as D
+    from tests.oracle_helpers import cfg_from, oracle_trace
+    from tests.test_diagnostics import DRIFT, check_library_against_oracle, oracle_summary
+    _print(f"case: diagnostics promote={promote}")
+    wl, steps = DRIFT, 96
+    cfg = cfg_from(wl, budget_frac=0.3, promote=promote)
+    events, masses, pol = oracle_trace(wl, cfg, steps, score_init=np.zeros(64))
+    osum = oracle_summary(events, masses, wl, pol.caps["K_f"])
+    flags = 0 if promote else B.QEVICT_F_NO_PROMOTE
+    sp = B.QEvictState(B.make_config(wl, flags=flags, budget_frac=0.3), wl.prompt_lens())
+    sr = B.QEvictState(B.make_config(wl, budget_frac=4.0, quant_frac=0.0), wl.prompt_lens())
+    qp, kp, vp = (t.cuda() for t in WL.prompt(wl, 0))
+    si = torch.zeros((1, sp.info.n_windows), dtype=torch.float64, device="cuda")
+    for st in (sp, sr):
+        st.prefill_init(0, qp, kp, vp, score_init=si)
+    out = torch.empty((1, wl.h_q, wl.d_head), dtype=torch.float32, device="cuda")
+
+    def run_step(j):
+        q, k, v = (t.cuda() for t in WL.decode_step(wl, 0, j))
+        sp.decode_attn(0, q, k, v, out)
+        sr.decode_attn(0, q, k, v, out)
+
+    tr = D.record(sp, sr, 0, 0, run_step, steps, wl.omega)
+    assert len(tr.state) == len(events)
+    for r, ev in enumerate(events):
+        np.testing.assert_array_equal(tr.state[r], [ev["state"][w] for w in range(len(tr.state[r]))])
+    err = max(float(np.abs(a - b).max()) for a, b in zip(tr.masses, masses))
+    _print(f"step-mass max abs err {err:.2e}")
+    assert err < 1e-5
+    s = check_library_against_oracle(tr, osum, tol=1e-4)
+    _print(f"diagnostics: {s}")
+    with pytest.raises(B.QEvictError):      # no decode step since the last routing
+        sp.step_mass(0, 0)
