@@ -495,13 +495,31 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         if (mode == RM_FORCE_Q || mode == RM_FORCE_F) target[w] = 0;
     }
     __syncthreads();
-    // ---- 8. chronological accessible list (Algorithm 1 step 21) and byte-balanced splits
+    // ---- 8. accessible list (Algorithm 1 step 21) and byte-balanced splits.  The bf16
+    //      pages and the Quantized slots, each in chronological order, are merged so that
+    //      the pages fall evenly among the slots (by rank fraction, (2r + 1) / 2count, pages
+    //      first on ties): every byte-balanced split then holds a like share of both kinds,
+    //      whose costs per byte differ.  Attention does not depend on the order.
     for (int w = tid; w < RT_MAXW; w += RT_THREADS) {
         const int ns = w < NW ? sm.newst[w] : ST_NONE;
-        flag[w] = (ns == ST_LOCAL || ns == ST_FULL || ns == ST_QUANT) ? 1 : 0;
+        flag[w] = (ns == ST_LOCAL || ns == ST_FULL) ? 1 : 0;
+        flag2[w] = ns == ST_QUANT ? 1 : 0;
     }
     __syncthreads();
-    const int n_winacc = block_scan_excl(flag, sm.wsum);
+    const int n_pg = block_scan_excl(flag, sm.wsum);     // flag[w]: rank among the pages
+    const int n_sl = block_scan_excl(flag2, sm.wsum);    // flag2[w]: rank among the slots
+    auto list_pos = [&](int w, bool page) -> int {
+        const long long P = n_pg, S = n_sl;
+        if (page) {
+            const long long r = flag[w], X = (2 * r + 1) * S - P;   // slots strictly before
+            long long c = X > 0 ? (X + 2 * P - 1) / (2 * P) : 0;
+            return (int)(r + (c < S ? c : S));
+        }
+        const long long r = flag2[w], Y = (2 * r + 1) * P - S;      // pages before or tied
+        long long c = Y >= 0 ? Y / (2 * S) + 1 : 0;
+        return (int)(r + (c < P ? c : P));
+    };
+    const int n_winacc = n_pg + n_sl;
     const int base = 1;   // entry 0 is the sink prefix
     int n_acc = base + n_winacc;
     if (n_acc > g.n_acc_max) {
@@ -509,7 +527,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         n_acc = g.n_acc_max;
     }
     AccEntry* acc = bf.acc + u * g.n_acc_max;
-    int* cost = flag2;
+    int* cost = sm.idx;
     for (int e = tid; e < RT_MAXW; e += RT_THREADS) cost[e] = 0;
     __syncthreads();
     if (tid == 0) {
@@ -522,7 +540,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         if (w >= NW) continue;
         const int ns = sm.newst[w];
         if (!(ns == ST_LOCAL || ns == ST_FULL || ns == ST_QUANT)) continue;
-        const int e = base + flag[w];
+        const int e = base + list_pos(w, ns != ST_QUANT);
         if (e >= n_acc) continue;
         AccEntry en;
         en.kind = ns == ST_QUANT ? EK_SLOT : EK_PAGE;
