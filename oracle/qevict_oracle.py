@@ -434,12 +434,15 @@ class UnitOracle:
                 score_init: Optional[np.ndarray] = None) -> dict:
         """qp [H_q][S][d], kp/vp [H_kv][S][d] (bf16 values).  Stores the prompt, sets
         S_bar_0 from the causal column sums (or from ``score_init`` [n_windows] when
-        given), then routes with the aged prompt windows as candidates."""
+        given; qp may then be None), then routes with the aged prompt windows as
+        candidates."""
         cfg = self.cfg
-        S = qp.shape[1]
+        S = kp.shape[1]
         assert S == self.prompt_len
         if cfg.rope:
-            qp, kp = self.rotate_in(qp, np.arange(S)), self.rotate_in(kp, np.arange(S))
+            kp = self.rotate_in(kp, np.arange(S))
+            if qp is not None:
+                qp = self.rotate_in(qp, np.arange(S))
         for p in range(S):
             self._store(p, kp[:, p], vp[:, p])
         self.n = S

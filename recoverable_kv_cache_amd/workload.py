@@ -128,10 +128,11 @@ def _outlier_channels(wl: Workload, layer: int) -> torch.Tensor:
     return torch.stack(rows) if rows and wl.n_outlier > 0 else torch.zeros((wl.h_kv, 0), dtype=torch.long)
 
 
-def prompt(wl: Workload, layer: int, device="cpu") -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+def prompt(wl: Workload, layer: int, device="cpu", with_q: bool = True):
     """Prompt tensors for one layer, bf16, zero-padded past each prompt length.
 
-    Returns ``q [B][H_q][S][d]``, ``k, v [B][H_kv][S][d]`` with ``S = wl.prompt_len``.
+    Returns ``q [B][H_q][S][d]``, ``k, v [B][H_kv][S][d]`` with ``S = wl.prompt_len``
+    (``q`` is None with ``with_q=False``; the keys and values do not depend on it).
     """
     S, d = wl.prompt_len, wl.d_head
     lens = wl.prompt_lens()
@@ -139,7 +140,7 @@ def prompt(wl: Workload, layer: int, device="cpu") -> tuple[torch.Tensor, torch.
     qs, ks, vs = [], [], []
     outl = _outlier_channels(wl, layer)
     for b in range(wl.batch):
-        q = _normal((wl.h_q, S, d), _gen(wl.seed, layer, b, _S_QP, gen_dev), gen_dev)
+        q = _normal((wl.h_q, S, d), _gen(wl.seed, layer, b, _S_QP, gen_dev), gen_dev) if with_q else None
         k = _normal((wl.h_kv, S, d), _gen(wl.seed, layer, b, _S_KP, gen_dev), gen_dev)
         v = _normal((wl.h_kv, S, d), _gen(wl.seed, layer, b, _S_VP, gen_dev), gen_dev)
         if wl.n_outlier:
@@ -153,13 +154,15 @@ def prompt(wl: Workload, layer: int, device="cpu") -> tuple[torch.Tensor, torch.
                 k[:, s0:s0 + wl.window, :] += wl.beta * u[:, j:j + 1, :]
         L = lens[b]
         if L < S:
-            q[:, L:, :] = 0
+            if with_q:
+                q[:, L:, :] = 0
             k[:, L:, :] = 0
             v[:, L:, :] = 0
-        qs.append(q.to(torch.bfloat16))
+        if with_q:
+            qs.append(q.to(torch.bfloat16))
         ks.append(k.to(torch.bfloat16))
         vs.append(v.to(torch.bfloat16))
-    return (torch.stack(qs).to(device), torch.stack(ks).to(device), torch.stack(vs).to(device))
+    return (torch.stack(qs).to(device) if with_q else None, torch.stack(ks).to(device), torch.stack(vs).to(device))
 
 
 def _phase(wl: Workload, step: int) -> tuple[int, float]:

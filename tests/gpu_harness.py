@@ -69,7 +69,8 @@ def compare_unit(ex: B.UnitExport, unit: O.UnitOracle, tag: str, check_scores=Tr
 
 class Lockstep:
     def __init__(self, wl: WL.Workload, layer: int = 0, score_init=None, flags: int = 0, n_splits: int = 0,
-                 ocfg_over=None, device="cuda", n_layers=1, rope_theta=WL.ROPE_THETA):
+                 ocfg_over=None, device="cuda", n_layers=1, rope_theta=WL.ROPE_THETA, sample=None):
+        """``sample``: the sequences the oracle follows and the checks cover (default all)."""
         self.wl = wl
         self.layer = layer
         self.lens = wl.prompt_lens()
@@ -87,7 +88,8 @@ class Lockstep:
             self.rope = WL.rope_table(wl.d_head, max(32, wl.prompt_len + wl.n_decode), theta=rope_theta)
             self.st.set_rope(self.rope.to(device))
         cs = None if self.rope is None else self.rope.numpy()
-        self.units = [O.UnitOracle(ocfg, S, rope_cs=cs) for S in self.lens]
+        self.sample = list(range(wl.batch)) if sample is None else list(sample)
+        self.units = [O.UnitOracle(ocfg, self.lens[b], rope_cs=cs) for b in self.sample]
         self.score_init = score_init
         self.max_o_err = 0.0
         self.max_s_err = 0.0
@@ -95,22 +97,25 @@ class Lockstep:
         self.dev = device
 
     def prefill(self):
-        qp, kp, vp = WL.prompt(self.wl, self.layer)
+        qp, kp, vp = WL.prompt(self.wl, self.layer, with_q=self.score_init is None)
         si = None
         if self.score_init is not None:
             si = torch.zeros((self.wl.batch, self.st.info.n_windows), dtype=torch.float64)
             si[:, : self.score_init.shape[1]] = self.score_init[:, : si.shape[1]]
             si = si.to(self.dev)
-        self.st.prefill_init(0, qp.to(self.dev), kp.to(self.dev), vp.to(self.dev), score_init=si)
-        for b, unit in enumerate(self.units):
+        self.st.prefill_init(0, None if qp is None else qp.to(self.dev), kp.to(self.dev), vp.to(self.dev),
+                             score_init=si)
+        for b, unit in zip(self.sample, self.units):
             S = self.lens[b]
             init = None if self.score_init is None else self.score_init[b].numpy()
-            unit.prefill(f64(qp[b, :, :S]), f64(kp[b, :, :S]), f64(vp[b, :, :S]), score_init=init)
+            unit.prefill(None if qp is None else f64(qp[b, :, :S]), f64(kp[b, :, :S]), f64(vp[b, :, :S]),
+                         score_init=init)
+        del qp, kp, vp
         self.check("prefill")
 
     def check(self, tag, check_scores=True):
         torch.cuda.synchronize()
-        for b, unit in enumerate(self.units):
+        for b, unit in zip(self.sample, self.units):
             ex = self.st.export_unit(0, b)
             e = compare_unit(ex, unit, f"{tag} b={b}", check_scores)
             self.max_s_err = max(self.max_s_err, e)
@@ -120,7 +125,7 @@ class Lockstep:
         out = torch.empty((self.wl.batch, self.wl.h_q, self.wl.d_head), dtype=torch.float32, device=self.dev)
         self.st.decode_attn(0, q.to(self.dev), k.to(self.dev), v.to(self.dev), out)
         o_gpu = out.cpu().numpy().astype(np.float64)
-        for b, unit in enumerate(self.units):
+        for b, unit in zip(self.sample, self.units):
             ref = unit.decode(f64(q[b]), f64(k[b]), f64(v[b]))
             err = rel_err(o_gpu[b], ref["o"])
             self.max_o_err = max(self.max_o_err, err)

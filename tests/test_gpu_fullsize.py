@@ -108,3 +108,45 @@ def test_llama8b_32k_rope_decode_and_route_lockstep():
     for j in range(8):
         ls.step(j)
     print(f"32K rope: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}", flush=True)
+
+
+def _init_scores(wl):
+    n_win = (wl.prompt_len - wl.n_sink + wl.window - 1) // wl.window
+    return WL.init_scores(wl, 0, n_win)
+
+
+def test_batched_16k_b16_sampled_lockstep():
+    """The batched mid-context shape at full size (one layer, batch 16, prompts of 8K-16K,
+    the benchmark's split count for batch 16): the GPU decodes every sequence; the oracle
+    follows sequences 0, 7 and 15 through 8 steps and a routing event (synthetic initial
+    scores: 16 prompts' column sums are beyond the oracle)."""
+    wl = WL.BATCHED_16K.with_(n_layers=1)
+    print("case: batched 16K b16", flush=True)
+    ls = Lockstep(wl, score_init=_init_scores(wl), sample=[0, 7, 15])
+    assert ls.st.info.n_splits == B.plan(B.make_config(WL.BATCHED_16K), wl.prompt_lens()).n_splits
+    ls.run(8)
+    print(f"batched: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}", flush=True)
+
+
+def test_churn_4k_b64_sampled_lockstep_across_a_topic_switch():
+    """The long-generation churn shape at full width (one layer, batch 64, 4K prompts, W = 16):
+    264 decode steps cross the topic switch at step 256 (33 routing events); the oracle
+    follows sequences 0 and 63, and windows move between the tiers."""
+    wl = WL.CHURN_4K.with_(n_layers=1)
+    print("case: churn 4K b64", flush=True)
+    ls = Lockstep(wl, score_init=_init_scores(wl), sample=[0, 63]).run(264, check_every=8)
+    moved = sum(e["promoted"] + e["demoted"] for u in ls.units for e in u.events)
+    print(f"churn: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}, "
+          f"moves {moved}", flush=True)
+    assert ls.events == 33 and moved > 0
+
+
+def test_llama70b_128k_b4_sampled_lockstep():
+    """The 70B-shaped long context at full size (one layer, batch 4, 128K prompts, W = 64,
+    GQA 8, 512 recent): 8 steps and a routing event, the oracle following sequences 0 and 3."""
+    wl = WL.LLAMA70B_128K.with_(n_layers=1)
+    print("case: 70B 128K b4", flush=True)
+    ls = Lockstep(wl, score_init=_init_scores(wl), sample=[0, 3])
+    assert ls.st.info.n_splits == B.plan(B.make_config(WL.LLAMA70B_128K), wl.prompt_lens()).n_splits
+    ls.run(8)
+    print(f"70B: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}", flush=True)
