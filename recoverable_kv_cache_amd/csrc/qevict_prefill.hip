@@ -9,7 +9,7 @@
 // then a second pass with query and key roles swapped):
 //   pass 1: LSE_u = log sum_{t <= u} exp(l(u, t))               (per query row)
 //   pass 2: c_t   = sum_{u >= t} exp(l(u, t) - LSE_u)            (per key column)
-// Both passes run bf16 MFMA 16x16x16 tiles with fp32 accumulation; column sums
+// Both passes run bf16 MFMA 16x16x32 tiles with fp32 accumulation; column sums
 // accumulate in fp32 within a 64-row tile and in fp64 across tiles.
 #include "qevict_common.h"
 #include "qevict_internal.h"
@@ -17,14 +17,16 @@
 
 namespace qv {
 
-typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int PF_TILE = 64;
-constexpr int PF_PAD = 4;   // LDS row padding (bf16 elements)
+constexpr int PF_PAD = 8;   // LDS row padding (bf16 elements; rows stay 16-byte aligned)
 
-__device__ __forceinline__ float4_t mfma16(short4_t a, short4_t b, float4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+__device__ __forceinline__ float4_t mfma32x(short8_t a, short8_t b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(__bf16 __attribute__((ext_vector_type(8))), a),
+                                                   __builtin_bit_cast(__bf16 __attribute__((ext_vector_type(8))), b), c, 0,
+                                                   0, 0);
 }
 
 // Row tile [64][D] of a [.., S_max, D] bf16 buffer into LDS, zero past S.
@@ -57,14 +59,14 @@ __global__ void __launch_bounds__(256) k_prefill_lse(Geo g, Bufs bf, int layer, 
     const uint16_t* Q = qp + ((int64_t)b * g.h_q + h) * g.S_max * D;
     const uint16_t* K = kp + ((int64_t)b * g.h_kv + hk) * g.S_max * D;
     const int r0 = tile * PF_TILE + wave * 16;
-    short4_t qa[D / 16];
+    short8_t qa[D / 32];
     {
         const int row = r0 + lr;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            uint2 v = make_uint2(0, 0);
-            if (row < S) v = *reinterpret_cast<const uint2*>(Q + (int64_t)row * D + kk * 16 + 4 * lq);
-            qa[kk] = *reinterpret_cast<short4_t*>(&v);
+        for (int kk = 0; kk < D / 32; ++kk) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (row < S) v = *reinterpret_cast<const uint4*>(Q + (int64_t)row * D + kk * 32 + 8 * lq);
+            qa[kk] = __builtin_bit_cast(short8_t, v);
         }
     }
     float m[4], l[4];
@@ -84,9 +86,9 @@ __global__ void __launch_bounds__(256) k_prefill_lse(Geo g, Bufs bf, int layer, 
         for (int sub = 0; sub < 4; ++sub) {
             float4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                const short4_t bb = *reinterpret_cast<const short4_t*>(&ks[sub * 16 + lr][kk * 16 + 4 * lq]);
-                c = mfma16(qa[kk], bb, c);
+            for (int kk = 0; kk < D / 32; ++kk) {
+                const short8_t bb = *reinterpret_cast<const short8_t*>(&ks[sub * 16 + lr][kk * 32 + 8 * lq]);
+                c = mfma32x(qa[kk], bb, c);
             }
             sacc[sub] = c;
         }
@@ -102,9 +104,9 @@ __global__ void __launch_bounds__(256) k_prefill_lse(Geo g, Bufs bf, int layer, 
             }
             if (mx == -INFINITY) continue;
             const float mn = fmaxf(m[i], mx);
-            float s = l[i] * (m[i] == -INFINITY ? 0.f : exp2f(m[i] - mn));
+            float s = l[i] * (m[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[i] - mn));
 #pragma unroll
-            for (int sub = 0; sub < 4; ++sub) s += x[sub] == -INFINITY ? 0.f : exp2f(x[sub] - mn);
+            for (int sub = 0; sub < 4; ++sub) s += x[sub] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[sub] - mn);
             l[i] = s;
             m[i] = mn;
         }
@@ -145,14 +147,14 @@ __global__ void __launch_bounds__(256) k_prefill_colsum(Geo g, Bufs bf, int laye
     const uint16_t* K = kp + ((int64_t)b * g.h_kv + hk) * g.S_max * D;
     const float* LS = lse2 + ((int64_t)b * g.h_q + h) * g.S_max;
     const int k0 = ktile * PF_TILE + wave * 16;
-    short4_t ka[D / 16];
+    short8_t ka[D / 32];
     {
         const int key = k0 + lr;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            uint2 v = make_uint2(0, 0);
-            if (key < S) v = *reinterpret_cast<const uint2*>(K + (int64_t)key * D + kk * 16 + 4 * lq);
-            ka[kk] = *reinterpret_cast<short4_t*>(&v);
+        for (int kk = 0; kk < D / 32; ++kk) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (key < S) v = *reinterpret_cast<const uint4*>(K + (int64_t)key * D + kk * 32 + 8 * lq);
+            ka[kk] = __builtin_bit_cast(short8_t, v);
         }
     }
     double cs[4] = {0.0, 0.0, 0.0, 0.0};
@@ -170,16 +172,16 @@ __global__ void __launch_bounds__(256) k_prefill_colsum(Geo g, Bufs bf, int laye
         for (int sub = 0; sub < 4; ++sub) {
             float4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                const short4_t bb = *reinterpret_cast<const short4_t*>(&qs[sub * 16 + lr][kk * 16 + 4 * lq]);
-                c = mfma16(ka[kk], bb, c);
+            for (int kk = 0; kk < D / 32; ++kk) {
+                const short8_t bb = *reinterpret_cast<const short8_t*>(&qs[sub * 16 + lr][kk * 32 + 8 * lq]);
+                c = mfma32x(ka[kk], bb, c);
             }
             const int query = qt * PF_TILE + sub * 16 + lr;
             const float lq_ = ls[sub * 16 + lr];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int key = k0 + 4 * lq + i;
-                if (query >= key && query < S) part[i] += exp2f(fmaf(c[i], scale, -lq_));
+                if (query >= key && query < S) part[i] += __builtin_amdgcn_exp2f(fmaf(c[i], scale, -lq_));
             }
         }
 #pragma unroll
