@@ -316,3 +316,17 @@ def test_diagnostics_from_the_gpu_state_match_the_oracle(promote):
     _print(f"diagnostics: {s}")
     with pytest.raises(B.QEvictError):      # no decode step since the last routing
         sp.step_mass(0, 0)
+
+
+def test_combined_flags_int4_rope_pnorm_one_way():
+    """The options together: INT4 tier, inputs before RoPE, p-norm ranker and the one-way
+    variant, on the drifting tiny workload routed every 2 steps (G = 4, d = 64, W = 16)."""
+    _print("case: combined flags")
+    wl = WL.TINY.with_(n_topics=4, topic_period=8, n_decode=48, n_outlier=2, budget_frac=0.3, omega=2)
+    si = torch.zeros((1, 64), dtype=torch.float64)
+    flags = B.QEVICT_F_INT4 | B.QEVICT_F_ROPE | B.QEVICT_F_RANK_PNORM | B.QEVICT_F_NO_PROMOTE
+    ls = Lockstep(wl, score_init=si, flags=flags).run(48)
+    unit = ls.units[0]
+    assert sum(e["promoted"] for e in unit.events) == 0
+    assert any(W.ledger is not None and W.ledger.bits == 4 for W in unit.win.values())
+    _print(f"combined: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}")
