@@ -92,6 +92,8 @@ __global__ void __launch_bounds__(256) k_prefill_lse(Geo g, Bufs bf, int layer, 
             }
             sacc[sub] = c;
         }
+        // key tiles wholly below the row tile need neither the causal nor the length mask
+        const bool full = (kt + 1) * PF_TILE <= tile * PF_TILE && (kt + 1) * PF_TILE <= S;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = r0 + 4 * lq + i;
@@ -99,14 +101,19 @@ __global__ void __launch_bounds__(256) k_prefill_lse(Geo g, Bufs bf, int layer, 
 #pragma unroll
             for (int sub = 0; sub < 4; ++sub) {
                 const int key = kt * PF_TILE + sub * 16 + lr;
-                x[sub] = (key <= row && key < S) ? sacc[sub][i] * scale : -INFINITY;
+                x[sub] = (full || (key <= row && key < S)) ? sacc[sub][i] * scale : -INFINITY;
                 mx = fmaxf(mx, x[sub]);
             }
             if (mx == -INFINITY) continue;
             const float mn = fmaxf(m[i], mx);
             float s = l[i] * (m[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[i] - mn));
+            if (full) {
 #pragma unroll
-            for (int sub = 0; sub < 4; ++sub) s += x[sub] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[sub] - mn);
+                for (int sub = 0; sub < 4; ++sub) s += __builtin_amdgcn_exp2f(x[sub] - mn);
+            } else {
+#pragma unroll
+                for (int sub = 0; sub < 4; ++sub) s += x[sub] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[sub] - mn);
+            }
             l[i] = s;
             m[i] = mn;
         }
@@ -168,6 +175,7 @@ __global__ void __launch_bounds__(256) k_prefill_colsum(Geo g, Bufs bf, int laye
         }
         __syncthreads();
         float part[4] = {0.f, 0.f, 0.f, 0.f};
+        const bool full = qt > ktile && (qt + 1) * PF_TILE <= S;
 #pragma unroll
         for (int sub = 0; sub < 4; ++sub) {
             float4_t c = {0.f, 0.f, 0.f, 0.f};
@@ -178,10 +186,15 @@ __global__ void __launch_bounds__(256) k_prefill_colsum(Geo g, Bufs bf, int laye
             }
             const int query = qt * PF_TILE + sub * 16 + lr;
             const float lq_ = ls[sub * 16 + lr];
+            if (full) {   // query tile wholly above the key tile and inside the prompt: no masks
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = k0 + 4 * lq + i;
-                if (query >= key && query < S) part[i] += __builtin_amdgcn_exp2f(fmaf(c[i], scale, -lq_));
+                for (int i = 0; i < 4; ++i) part[i] += __builtin_amdgcn_exp2f(fmaf(c[i], scale, -lq_));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = k0 + 4 * lq + i;
+                    if (query >= key && query < S) part[i] += __builtin_amdgcn_exp2f(fmaf(c[i], scale, -lq_));
+                }
             }
         }
 #pragma unroll
