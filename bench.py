@@ -148,7 +148,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path here runs on a single GPU.",
               file=sys.stderr)
         sys.exit(2)
 
