@@ -978,11 +978,13 @@ __device__ __forceinline__ float wave_max(float x) {   // (operands never NaN)
 // condition (or a select the compiler turns back into one) makes the compiler wait for
 // it on the spot, and the loads would take one round trip each.
 //
-// M and L of head h over all splits, computed by one whole wave (lane = split mod 64)
-__device__ __forceinline__ void head_ml(const float2* ml, int NS, int h_q, int lane, float& M, float& L) {
-    float2 v[FN_MAXS / 64];
+// M and L of head h over all splits, computed by one whole wave (lane = split mod 64):
+// the loads, then the reduction
+__device__ __forceinline__ void head_ml_load(const float2* ml, int NS, int h_q, int lane, float2* v) {
 #pragma unroll
     for (int k = 0; k < FN_MAXS / 64; ++k) v[k] = ml[(int64_t)imin(lane + 64 * k, NS - 1) * h_q];
+}
+__device__ __forceinline__ void head_ml(const float2* v, int NS, int lane, float& M, float& L) {
     float m = v[0].x;
 #pragma unroll
     for (int k = 1; k < FN_MAXS / 64; ++k) m = max2(m, v[k].x);
@@ -1036,8 +1038,12 @@ __global__ void __launch_bounds__(FN_THREADS) k_finish(Geo g, Bufs bf, int layer
     const int tok_at = hw[offsetof(UnitHdr, tok_at) / 4], page = hw[offsetof(UnitHdr, tok_page) / 4];
     const uint16_t kn = knew[((int64_t)b * g.h_kv + hk) * D + imin(tid, D - 1)];
     const uint16_t vn = vnew[((int64_t)b * g.h_kv + hk) * D + imin(tid, D - 1)];
+    float2 mlv[FN_MAXS / 64];
+    head_ml_load(ml, NS, g.h_q, lane, mlv);
+    // keep the scheduler from sinking the loads above to their uses (one round trip each)
+    __builtin_amdgcn_sched_barrier(0);
     float M, L;
-    head_ml(ml, NS, g.h_q, lane, M, L);
+    head_ml(mlv, NS, lane, M, L);
     f4_t a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < NX; ++k) a4 += (__builtin_amdgcn_exp2f(mx[k] - M) * wk[k]) * x[k];
