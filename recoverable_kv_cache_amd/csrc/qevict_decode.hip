@@ -228,6 +228,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     constexpr int CQ = S::CQ, KS = S::KS, MB = S::MB, NSLOT = S::NSLOT, SW = S::SW, LPR = S::LPR, CPL = S::CPL;
     constexpr int NV = S::NV, QSTR = S::QSTR;
     __shared__ uint2 lut[256];            // code byte -> its 4 (INT2) or 2 (INT4, in .x) codes as bf16 integers
+    __shared__ uint2 lutk[ROPE ? 256 : 1];  // RoPE mode, key side: the same codes as fp16 integers
     // per wave: rows 0-15 the INT2 query operand of the current job, rows 16-31 the
     // bf16 query operand (every live column holds its head's query, exact bf16), row 32 zeros
     __shared__ __attribute__((aligned(16))) uint16_t qs[DW][33][QSTR];
@@ -317,6 +318,13 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
                 lut[x] = make_uint2(bv(x & 3) | (bv((x >> 2) & 3) << 16), bv((x >> 4) & 3) | (bv((x >> 6) & 3) << 16));
             else
                 lut[x] = make_uint2(bv(x & 15) | (bv(x >> 4) << 16), 0u);
+            if constexpr (ROPE) {
+                auto hv = [](int c) -> uint32_t { return __builtin_bit_cast(uint16_t, (_Float16)c); };   // exact for c < 2048
+                if constexpr (BITS == 2)
+                    lutk[x] = make_uint2(hv(x & 3) | (hv((x >> 2) & 3) << 16), hv((x >> 4) & 3) | (hv((x >> 6) & 3) << 16));
+                else
+                    lutk[x] = make_uint2(hv(x & 15) | (hv(x >> 4) << 16), 0u);
+            }
         }
         stw<CQ / 2>(&qs[wave][16 + n][CQ * qg], w);
         if (lane < D / 8) reinterpret_cast<uint4*>(&qs[wave][32][0])[lane] = make_uint4(0u, 0u, 0u, 0u);
@@ -563,26 +571,20 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     const uint16_t* qrow_a = &qs[wave][(NSLOT == 2 && slot) ? 32 : n][CQ * qg];   // slot 0 columns only
     const uint16_t* qrow_b = &qs[wave][(NSLOT == 2 && !slot) ? 32 : n][CQ * qg];  // slot 1 columns only
     // RoPE mode, key side of a Quantized job (see process_q): the 8 codes of positions
-    // 8ks .. 8ks + 7 of the lane's row of tile tc, as floats
-    auto codes8 = [&](const uint32_t* w, int tc, int ks, float* c) __attribute__((always_inline)) {
+    // 8ks .. 8ks + 7 of the lane's row of tile tc, as 4 pairs of fp16 integers
+    auto codes8 = [&](const uint32_t* w, int tc, int ks, uint32_t* c) __attribute__((always_inline)) {
         if constexpr (BITS == 2) {
             const int by = tc * (CQ / 4) + 2 * ks;
             const uint32_t x = w[by >> 2];
-            const u2_t a0 = lut4(x, by & 3), a1 = lut4(x, (by & 3) + 1);
-            const uint32_t v[4] = {a0.x, a0.y, a1.x, a1.y};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                c[2 * k] = bf16lo(v[k]);
-                c[2 * k + 1] = bf16hi(v[k]);
-            }
+            const uint2 a0 = lutk[(x >> (8 * (by & 3))) & 0xffu], a1 = lutk[(x >> (8 * ((by & 3) + 1))) & 0xffu];
+            c[0] = a0.x;
+            c[1] = a0.y;
+            c[2] = a1.x;
+            c[3] = a1.y;
         } else {
             const uint32_t x = w[tc * (CQ / 8) + ks];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t v = lut2(x, k);
-                c[2 * k] = bf16lo(v);
-                c[2 * k + 1] = bf16hi(v);
-            }
+            for (int k = 0; k < 4; ++k) c[k] = lutk[(x >> (8 * k)) & 0xffu].x;
         }
     };
     // RoPE mode: the turned keys of one item for channel pairs (i, i + D/2), i = i0 .. i0 + 7,
@@ -590,7 +592,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     // second-half channel blocks
     auto rope_keys = [&](const uint32_t* w, const uint32_t* pr, int tc, int ks, const float2* cs, u4_t& hf, u4_t& lf,
                          u4_t& hs, u4_t& ls) __attribute__((always_inline)) {
-        float cf[8], cb[8];
+        uint32_t cf[4], cb[4];
         codes8(w, tc, ks, cf);
         codes8(w, tc, ks + KS / 2, cb);
         const int i0 = qg * (CQ / 2) + 8 * ks;
@@ -601,8 +603,11 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         float yf[8], yb[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const f2_t a = h2f(pf[k]), bb = h2f(pb[k]);          // (offset, scale)
-            const float xf = fmaf(cf[k], a.y, a.x), xb = fmaf(cb[k], bb.y, bb.x);
+            // (offset, scale) and the code, all fp16: one mixed-precision fma each, exact inputs
+            const h2_t a = __builtin_bit_cast(h2_t, pf[k]), bb = __builtin_bit_cast(h2_t, pb[k]);
+            const h2_t c2f = __builtin_bit_cast(h2_t, cf[k >> 1]), c2b = __builtin_bit_cast(h2_t, cb[k >> 1]);
+            const _Float16 chf = (k & 1) ? c2f.y : c2f.x, chb = (k & 1) ? c2b.y : c2b.x;
+            const float xf = fmaf((float)chf, (float)a.y, (float)a.x), xb = fmaf((float)chb, (float)bb.y, (float)bb.x);
             yf[k] = xf * cs[k].x - xb * cs[k].y;
             yb[k] = xb * cs[k].x + xf * cs[k].y;
         }
