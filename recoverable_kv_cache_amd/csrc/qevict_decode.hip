@@ -611,13 +611,23 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             yf[k] = xf * cs[k].x - xb * cs[k].y;
             yb[k] = xb * cs[k].x + xf * cs[k].y;
         }
+        // high parts RNE; each low part y - high is exact in fp32 and comes from a bf16 dot
+        // product of the packed high pair with (-1, -0) or (0, -1), accumulated onto y.
+        // (The first is spelled with -0: hipcc encodes the pair (-1, +0) as the inline
+        // constant -1.0, which the instruction reads as the fp32 word, i.e. as (0, -1).)
+        const bf2_t neg_lo = __builtin_bit_cast(bf2_t, 0x8000BF80u), neg_hi = __builtin_bit_cast(bf2_t, 0xBF800000u);
+        auto rest = [&](uint32_t h, float y0, float y1) -> uint32_t {
+            const bf2_t hb = __builtin_bit_cast(bf2_t, h);
+            return bf16x2_rne(__builtin_amdgcn_fdot2_f32_bf16(hb, neg_lo, y0, false),
+                              __builtin_amdgcn_fdot2_f32_bf16(hb, neg_hi, y1, false));
+        };
         uint32_t h1[4], l1[4], h2[4], l2[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             h1[k] = bf16x2_rne(yf[2 * k], yf[2 * k + 1]);
-            l1[k] = bf16x2_rne(yf[2 * k] - bf16lo(h1[k]), yf[2 * k + 1] - bf16hi(h1[k]));
+            l1[k] = rest(h1[k], yf[2 * k], yf[2 * k + 1]);
             h2[k] = bf16x2_rne(yb[2 * k], yb[2 * k + 1]);
-            l2[k] = bf16x2_rne(yb[2 * k] - bf16lo(h2[k]), yb[2 * k + 1] - bf16hi(h2[k]));
+            l2[k] = rest(h2[k], yb[2 * k], yb[2 * k + 1]);
         }
         hf = u4_t{h1[0], h1[1], h1[2], h1[3]};
         lf = u4_t{l1[0], l1[1], l1[2], l1[3]};
