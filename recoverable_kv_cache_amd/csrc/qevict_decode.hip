@@ -1004,25 +1004,30 @@ __device__ __forceinline__ float wave_max(float x) {   // (operands never NaN)
 // condition (or a select the compiler turns back into one) makes the compiler wait for
 // it on the spot, and the loads would take one round trip each.
 //
-// M and L of head h over all splits, computed by one whole wave (lane = split mod 64):
-// the loads, then the reduction
+// M and L of head h over all splits, computed by one whole wave (lane = split mod 64,
+// NB blocks of 64 splits): the loads, then the reduction, which also leaves in each lane
+// the weights 2^(m_s - M) of its own splits (0 past NS)
+template <int NB>
 __device__ __forceinline__ void head_ml_load(const float2* ml, int NS, int h_q, int lane, float2* v) {
 #pragma unroll
-    for (int k = 0; k < FN_MAXS / 64; ++k) v[k] = ml[(int64_t)imin(lane + 64 * k, NS - 1) * h_q];
+    for (int k = 0; k < NB; ++k) v[k] = ml[(int64_t)imin(lane + 64 * k, NS - 1) * h_q];
 }
-__device__ __forceinline__ void head_ml(const float2* v, int NS, int lane, float& M, float& L) {
+template <int NB>
+__device__ __forceinline__ void head_ml(const float2* v, int NS, int lane, float& M, float& L, float* e) {
     float m = v[0].x;
 #pragma unroll
-    for (int k = 1; k < FN_MAXS / 64; ++k) m = max2(m, v[k].x);
+    for (int k = 1; k < NB; ++k) m = max2(m, v[k].x);
     M = wave_max(m);
     float l = 0.f;
 #pragma unroll
-    for (int k = 0; k < FN_MAXS / 64; ++k)
-        l += __builtin_amdgcn_exp2f(v[k].x - M) * (v[k].y * (lane + 64 * k < NS ? 1.f : 0.f));
+    for (int k = 0; k < NB; ++k) {
+        e[k] = __builtin_amdgcn_exp2f(v[k].x - M) * (lane + 64 * k < NS ? 1.f : 0.f);
+        l += e[k] * v[k].y;
+    }
     L = wave_sum(l);
 }
 
-template <int D>
+template <int D, int NB>
 __global__ void __launch_bounds__(FN_THREADS) k_finish(Geo g, Bufs bf, int layer, float* __restrict__ out,
                                                        const uint16_t* __restrict__ knew,
                                                        const uint16_t* __restrict__ vnew, int score_now) {
@@ -1042,14 +1047,8 @@ __global__ void __launch_bounds__(FN_THREADS) k_finish(Geo g, Bufs bf, int layer
     const int64_t sstride = (int64_t)g.h_q * D / 4;   // float4 per split
     constexpr int NX = 8;            // splits of this lane's phase per batch of loads
     f4_t x[NX];
-    float mx[NX], wk[NX];
 #pragma unroll
-    for (int k = 0; k < NX; ++k) {
-        const int sp = ph + k * PH, sc = imin(sp, NS - 1);
-        x[k] = pa[sc * sstride];
-        mx[k] = ml[(int64_t)sc * g.h_q].x;
-        wk[k] = sp < NS ? 1.f : 0.f;
-    }
+    for (int k = 0; k < NX; ++k) x[k] = pa[imin(ph + k * PH, NS - 1) * sstride];
     // the step's token goes into its sink / recent-window block (one workgroup per KV
     // head: the first query head of the group); its inputs and the block record are read
     // here, ahead of every store, so that all loads share one round trip
@@ -1064,15 +1063,24 @@ __global__ void __launch_bounds__(FN_THREADS) k_finish(Geo g, Bufs bf, int layer
     const int tok_at = hw[offsetof(UnitHdr, tok_at) / 4], page = hw[offsetof(UnitHdr, tok_page) / 4];
     const uint16_t kn = knew[((int64_t)b * g.h_kv + hk) * D + imin(tid, D - 1)];
     const uint16_t vn = vnew[((int64_t)b * g.h_kv + hk) * D + imin(tid, D - 1)];
-    float2 mlv[FN_MAXS / 64];
-    head_ml_load(ml, NS, g.h_q, lane, mlv);
+    float2 mlv[NB];
+    head_ml_load<NB>(ml, NS, g.h_q, lane, mlv);
     // keep the scheduler from sinking the loads above to their uses (one round trip each)
     __builtin_amdgcn_sched_barrier(0);
-    float M, L;
-    head_ml(mlv, NS, lane, M, L);
+    float M, L, e[NB];
+    head_ml<NB>(mlv, NS, lane, M, L, e);
+    // the first batch's split weights come from the lanes that own those splits: split
+    // ph + k*PH sits in block (k*PH)/64 (PH divides 64), lane (ph + k*PH) mod 64
+    float wk[NX];
+#pragma unroll
+    for (int k = 0; k < NX; ++k) {
+        const int blk = (k * PH) / 64;
+        wk[k] = blk < NB ? __shfl(e[blk < NB ? blk : 0], (ph + k * PH) & 63) : 0.f;
+    }
     f4_t a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < NX; ++k) a4 += (__builtin_amdgcn_exp2f(mx[k] - M) * wk[k]) * x[k];
+    for (int k = 0; k < NX; ++k) a4 += wk[k] * x[k];
+    float mx[NX];
     for (int sp0 = ph + NX * PH; sp0 < NS; sp0 += NX * PH) {      // more splits than one batch
 #pragma unroll
         for (int k = 0; k < NX; ++k) {
@@ -1129,9 +1137,21 @@ hipError_t launch_finish(const Geo& g, const Bufs& bf, int layer, float* out, co
     const dim3 grid(g.h_q, g.B), block(FN_THREADS);
     // RoPE mode: the key the split kernel turned (layer slice of [L][B][h_kv][d])
     const uint16_t* ks = (g.flags & QEVICT_F_ROPE) ? bf.krot + (int64_t)layer * g.B * g.h_kv * g.d : k_new;
-    if (g.d == 128) hipLaunchKernelGGL(k_finish<128>, grid, block, 0, s, g, bf, layer, out, ks, v_new, score_now);
-    else if (g.d == 64) hipLaunchKernelGGL(k_finish<64>, grid, block, 0, s, g, bf, layer, out, ks, v_new, score_now);
-    else return hipErrorInvalidValue;
+    const int nb = g.n_splits <= 64 ? 1 : g.n_splits <= 128 ? 2 : g.n_splits <= 256 ? 4 : 8;
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, s, g, bf, layer, out, ks, v_new, score_now); };
+    if (g.d == 128) {
+        if (nb == 1) go(k_finish<128, 1>);
+        else if (nb == 2) go(k_finish<128, 2>);
+        else if (nb == 4) go(k_finish<128, 4>);
+        else go(k_finish<128, 8>);
+    } else if (g.d == 64) {
+        if (nb == 1) go(k_finish<64, 1>);
+        else if (nb == 2) go(k_finish<64, 2>);
+        else if (nb == 4) go(k_finish<64, 4>);
+        else go(k_finish<64, 8>);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
