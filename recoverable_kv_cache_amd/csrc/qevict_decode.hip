@@ -58,15 +58,13 @@ __device__ __forceinline__ f4_t mfma16(u2_t a, u2_t b, f4_t c) {
 __device__ __forceinline__ f2_t h2f(uint32_t w) { return __builtin_convertvector(__builtin_bit_cast(h2_t, w), f2_t); }
 // x times the fp16 in the low / high half of w, one mixed-precision FMA with a zero
 // addend (the same rounding as converting first and multiplying)
+// (plain code, which the compiler selects as one v_fma_mix_f32 and sees in its hazard
+// checks; an inline-asm version gave wrong outputs once v_dot2c_f32_bf16 was used beside it)
 __device__ __forceinline__ float mul_h_lo(float x, uint32_t w) {
-    float r;
-    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(w));
-    return r;
+    return fmaf(x, (float)__builtin_bit_cast(h2_t, w).x, 0.0f);
 }
 __device__ __forceinline__ float mul_h_hi(float x, uint32_t w) {
-    float r;
-    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(w));
-    return r;
+    return fmaf(x, (float)__builtin_bit_cast(h2_t, w).y, 0.0f);
 }
 // maxima of operands that are never NaN (scores, -inf included): the plain instructions,
 // without the quieting that fmaxf adds for signalling NaNs
@@ -88,6 +86,16 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
 // top 16 bits of two fp32 (bf16 truncation)
 __device__ __forceinline__ uint32_t bf16x2_trunc(float a, float b) {
     return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+// x0 - h.lo and x1 - h.hi for a packed bf16 pair h, as one bf16 pair (RNE).  Each difference
+// is exact in fp32 whenever h holds x0, x1 rounded to bf16, and comes from a bf16 dot
+// product of h with (-1, -0) or (0, -1) accumulated onto x.  (hipcc would encode the pair
+// (-1, +0) as the inline constant -1.0, which the instruction reads as the fp32 word, i.e.
+// as (0, -1); -0 keeps it a literal.)
+__device__ __forceinline__ uint32_t bf16x2_rest(uint32_t h, float x0, float x1) {
+    const bf2_t hb = __builtin_bit_cast(bf2_t, h);
+    return bf16x2_rne(__builtin_amdgcn_fdot2_f32_bf16(hb, __builtin_bit_cast(bf2_t, 0x8000BF80u), x0, false),
+                      __builtin_amdgcn_fdot2_f32_bf16(hb, __builtin_bit_cast(bf2_t, 0xBF800000u), x1, false));
 }
 // DPP lane moves.  Every pattern used here reads a lane of the same row of 16, so no
 // lane is out of bounds and bound_ctrl changes no value; with it set the compiler can
@@ -611,23 +619,14 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             yf[k] = xf * cs[k].x - xb * cs[k].y;
             yb[k] = xb * cs[k].x + xf * cs[k].y;
         }
-        // high parts RNE; each low part y - high is exact in fp32 and comes from a bf16 dot
-        // product of the packed high pair with (-1, -0) or (0, -1), accumulated onto y.
-        // (The first is spelled with -0: hipcc encodes the pair (-1, +0) as the inline
-        // constant -1.0, which the instruction reads as the fp32 word, i.e. as (0, -1).)
-        const bf2_t neg_lo = __builtin_bit_cast(bf2_t, 0x8000BF80u), neg_hi = __builtin_bit_cast(bf2_t, 0xBF800000u);
-        auto rest = [&](uint32_t h, float y0, float y1) -> uint32_t {
-            const bf2_t hb = __builtin_bit_cast(bf2_t, h);
-            return bf16x2_rne(__builtin_amdgcn_fdot2_f32_bf16(hb, neg_lo, y0, false),
-                              __builtin_amdgcn_fdot2_f32_bf16(hb, neg_hi, y1, false));
-        };
+        // high parts RNE, low parts exact remainders (bf16x2_rest)
         uint32_t h1[4], l1[4], h2[4], l2[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             h1[k] = bf16x2_rne(yf[2 * k], yf[2 * k + 1]);
-            l1[k] = rest(h1[k], yf[2 * k], yf[2 * k + 1]);
+            l1[k] = bf16x2_rest(h1[k], yf[2 * k], yf[2 * k + 1]);
             h2[k] = bf16x2_rne(yb[2 * k], yb[2 * k + 1]);
-            l2[k] = rest(h2[k], yb[2 * k], yb[2 * k + 1]);
+            l2[k] = bf16x2_rest(h2[k], yb[2 * k], yb[2 * k + 1]);
         }
         hf = u4_t{h1[0], h1[1], h1[2], h1[3]};
         lf = u4_t{l1[0], l1[1], l1[2], l1[3]};

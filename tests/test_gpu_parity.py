@@ -255,6 +255,9 @@ ROPE_CASES = {
     # d = 64, W = 32, G = 2, INT2
     "d64_w32": (WL.Workload("r5", 1, 2, 4, 2, 64, 600, 32, 32, 4, 64, 8, 0.35, 0.70, prompt_len_min=350,
                             n_outlier=2, n_topics=2, topic_period=8), False, 0, 32),
+    # d = 128, W = 16 (one tile per chunk), G = 4, INT2, flat scores + drift (promotions)
+    "w16_d128": (WL.Workload("r6", 1, 2, 8, 2, 128, 700, 48, 16, 4, 64, 8, 0.20, 0.70, prompt_len_min=500,
+                             n_outlier=2, n_topics=4, topic_period=16), True, 0, 48),
 }
 
 
