@@ -92,30 +92,43 @@ __global__ void __launch_bounds__(256) k_prefill_lse(Geo g, Bufs bf, int layer, 
             }
             sacc[sub] = c;
         }
-        // key tiles wholly below the row tile need neither the causal nor the length mask
+        // key tiles wholly below the row tile need neither the causal nor the length mask.
+        // The reference m of a row moves lazily: only when a score exceeds it by more than 8
+        // (log2 units), so terms stay below 2^8 and the rescale is rare after the first tile;
+        // the scale folds into one fma per score (it is positive, so the raw maximum orders
+        // the scaled ones)
         const bool full = (kt + 1) * PF_TILE <= tile * PF_TILE && (kt + 1) * PF_TILE <= S;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = r0 + 4 * lq + i;
-            float x[4], mx = -INFINITY;
-#pragma unroll
-            for (int sub = 0; sub < 4; ++sub) {
-                const int key = kt * PF_TILE + sub * 16 + lr;
-                x[sub] = (full || (key <= row && key < S)) ? sacc[sub][i] * scale : -INFINITY;
-                mx = fmaxf(mx, x[sub]);
-            }
-            if (mx == -INFINITY) continue;
-            const float mn = fmaxf(m[i], mx);
-            float s = l[i] * (m[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[i] - mn));
             if (full) {
+                const float mx = fmaxf(fmaxf(sacc[0][i], sacc[1][i]), fmaxf(sacc[2][i], sacc[3][i])) * scale;
+                if (mx > m[i] + 8.f) {
+                    l[i] *= m[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[i] - mx);
+                    m[i] = mx;
+                }
+                float s = l[i];
 #pragma unroll
-                for (int sub = 0; sub < 4; ++sub) s += __builtin_amdgcn_exp2f(x[sub] - mn);
+                for (int sub = 0; sub < 4; ++sub) s += __builtin_amdgcn_exp2f(fmaf(sacc[sub][i], scale, -m[i]));
+                l[i] = s;
             } else {
+                float x[4], mx = -INFINITY;
 #pragma unroll
-                for (int sub = 0; sub < 4; ++sub) s += x[sub] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[sub] - mn);
+                for (int sub = 0; sub < 4; ++sub) {
+                    const int key = kt * PF_TILE + sub * 16 + lr;
+                    x[sub] = (key <= row && key < S) ? sacc[sub][i] * scale : -INFINITY;
+                    mx = fmaxf(mx, x[sub]);
+                }
+                if (mx == -INFINITY) continue;
+                if (mx > m[i] + 8.f) {
+                    l[i] *= m[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[i] - mx);
+                    m[i] = mx;
+                }
+                float s = l[i];
+#pragma unroll
+                for (int sub = 0; sub < 4; ++sub) s += x[sub] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[sub] - m[i]);
+                l[i] = s;
             }
-            l[i] = s;
-            m[i] = mn;
         }
     }
 #pragma unroll
