@@ -29,18 +29,28 @@ __device__ __forceinline__ float4_t mfma32x(short8_t a, short8_t b, float4_t c) 
                                                    0, 0);
 }
 
-// Row tile [64][D] of a [.., S_max, D] bf16 buffer into LDS, zero past S.
+// Row tile [64][D] of a [.., S_max, D] bf16 buffer, staged through registers so that its
+// loads can be issued a tile ahead: D/32 16-byte chunks per thread of a 256-thread
+// workgroup, zero past S; then stored to LDS.
 template <int D>
-__device__ __forceinline__ void load_tile(uint16_t (*dst)[D + PF_PAD], const uint16_t* __restrict__ src, int row0,
-                                          int S) {
-    constexpr int CH = D / 8;   // 16-byte chunks per row
-    for (int i = threadIdx.x; i < PF_TILE * CH; i += blockDim.x) {
-        const int r = i / CH, c = (i % CH) * 8;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (row0 + r < S) v = *reinterpret_cast<const uint4*>(src + (int64_t)(row0 + r) * D + c);
+__device__ __forceinline__ void tile_regs(uint4* v, const uint16_t* __restrict__ src, int row0, int S) {
+    constexpr int CH = D / 8;
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) {
+        const int i = threadIdx.x + 256 * k, r = i / CH, c = (i % CH) * 8;
+        v[k] = make_uint4(0, 0, 0, 0);
+        if (row0 + r < S) v[k] = *reinterpret_cast<const uint4*>(src + (int64_t)(row0 + r) * D + c);
+    }
+}
+template <int D>
+__device__ __forceinline__ void tile_store(uint16_t (*dst)[D + PF_PAD], const uint4* v) {
+    constexpr int CH = D / 8;
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) {
+        const int i = threadIdx.x + 256 * k, r = i / CH, c = (i % CH) * 8;
         uint2* d2 = reinterpret_cast<uint2*>(&dst[r][c]);
-        d2[0] = make_uint2(v.x, v.y);
-        d2[1] = make_uint2(v.z, v.w);
+        d2[0] = make_uint2(v[k].x, v[k].y);
+        d2[1] = make_uint2(v[k].z, v[k].w);
     }
 }
 
@@ -48,7 +58,7 @@ __device__ __forceinline__ void load_tile(uint16_t (*dst)[D + PF_PAD], const uin
 template <int D>
 __global__ void __launch_bounds__(256) k_prefill_lse(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qp,
                                                     const uint16_t* __restrict__ kp, float* __restrict__ lse2) {
-    __shared__ uint16_t ks[PF_TILE][D + PF_PAD];
+    __shared__ uint16_t ks[2][PF_TILE][D + PF_PAD];   // key tiles, double-buffered
     const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int S = bf.hdr[unit_of(g, b, layer)].prompt_len;
     if (tile * PF_TILE >= S) return;
@@ -77,17 +87,22 @@ __global__ void __launch_bounds__(256) k_prefill_lse(Geo g, Bufs bf, int layer, 
     }
     const int last_row = min(tile * PF_TILE + PF_TILE, S) - 1;
     const int n_kt = last_row / PF_TILE + 1;
+    uint4 pre[D / 32];
+    tile_regs<D>(pre, K, 0, S);
+    tile_store<D>(ks[0], pre);
+    __syncthreads();
     for (int kt = 0; kt < n_kt; ++kt) {
-        __syncthreads();
-        load_tile<D>(ks, K, kt * PF_TILE, S);
-        __syncthreads();
+        // the next key tile's loads go out before this tile's products (one barrier per tile:
+        // the buffer written below was last read before the previous barrier)
+        if (kt + 1 < n_kt) tile_regs<D>(pre, K, (kt + 1) * PF_TILE, S);
+        const uint16_t(*kb)[D + PF_PAD] = ks[kt & 1];
         float4_t sacc[4];
 #pragma unroll
         for (int sub = 0; sub < 4; ++sub) {
             float4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < D / 32; ++kk) {
-                const short8_t bb = *reinterpret_cast<const short8_t*>(&ks[sub * 16 + lr][kk * 32 + 8 * lq]);
+                const short8_t bb = *reinterpret_cast<const short8_t*>(&kb[sub * 16 + lr][kk * 32 + 8 * lq]);
                 c = mfma32x(qa[kk], bb, c);
             }
             sacc[sub] = c;
@@ -130,6 +145,8 @@ __global__ void __launch_bounds__(256) k_prefill_lse(Geo g, Bufs bf, int layer, 
                 l[i] = s;
             }
         }
+        if (kt + 1 < n_kt) tile_store<D>(ks[(kt + 1) & 1], pre);
+        __syncthreads();
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -154,8 +171,8 @@ template <int D>
 __global__ void __launch_bounds__(256) k_prefill_colsum(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qp,
                                                        const uint16_t* __restrict__ kp,
                                                        const float* __restrict__ lse2, double* __restrict__ col) {
-    __shared__ uint16_t qs[PF_TILE][D + PF_PAD];
-    __shared__ float ls[PF_TILE];
+    __shared__ uint16_t qs[2][PF_TILE][D + PF_PAD];   // query tiles and their row LSEs, double-buffered
+    __shared__ float ls[2][PF_TILE];
     const int ktile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int S = bf.hdr[unit_of(g, b, layer)].prompt_len;
     if (ktile * PF_TILE >= S) return;
@@ -179,14 +196,25 @@ __global__ void __launch_bounds__(256) k_prefill_colsum(Geo g, Bufs bf, int laye
     }
     double cs[4] = {0.0, 0.0, 0.0, 0.0};
     const int n_qt = (S - 1) / PF_TILE + 1;
+    uint4 pre[D / 32];
+    float lpre = INFINITY;
+    tile_regs<D>(pre, Q, ktile * PF_TILE, S);
+    if (threadIdx.x < PF_TILE && ktile * PF_TILE + (int)threadIdx.x < S) lpre = LS[ktile * PF_TILE + threadIdx.x];
+    tile_store<D>(qs[0], pre);
+    if (threadIdx.x < PF_TILE) ls[0][threadIdx.x] = lpre;
+    __syncthreads();
     for (int qt = ktile; qt < n_qt; ++qt) {
-        __syncthreads();
-        load_tile<D>(qs, Q, qt * PF_TILE, S);
-        for (int r = threadIdx.x; r < PF_TILE; r += blockDim.x) {
-            const int row = qt * PF_TILE + r;
-            ls[r] = row < S ? LS[row] : INFINITY;
+        // the next query tile's loads go out before this tile's products (one barrier per
+        // tile: the buffer written below was last read before the previous barrier)
+        const int nb = (qt - ktile) & 1;
+        if (qt + 1 < n_qt) {
+            tile_regs<D>(pre, Q, (qt + 1) * PF_TILE, S);
+            lpre = INFINITY;
+            if (threadIdx.x < PF_TILE && (qt + 1) * PF_TILE + (int)threadIdx.x < S)
+                lpre = LS[(qt + 1) * PF_TILE + threadIdx.x];
         }
-        __syncthreads();
+        const uint16_t(*qb)[D + PF_PAD] = qs[nb];
+        const float* lb = ls[nb];
         float part[4] = {0.f, 0.f, 0.f, 0.f};
         const bool full = qt > ktile && (qt + 1) * PF_TILE <= S;
 #pragma unroll
@@ -194,11 +222,11 @@ __global__ void __launch_bounds__(256) k_prefill_colsum(Geo g, Bufs bf, int laye
             float4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < D / 32; ++kk) {
-                const short8_t bb = *reinterpret_cast<const short8_t*>(&qs[sub * 16 + lr][kk * 32 + 8 * lq]);
+                const short8_t bb = *reinterpret_cast<const short8_t*>(&qb[sub * 16 + lr][kk * 32 + 8 * lq]);
                 c = mfma32x(ka[kk], bb, c);
             }
             const int query = qt * PF_TILE + sub * 16 + lr;
-            const float lq_ = ls[sub * 16 + lr];
+            const float lq_ = lb[sub * 16 + lr];
             if (full) {   // query tile wholly above the key tile and inside the prompt: no masks
 #pragma unroll
                 for (int i = 0; i < 4; ++i) part[i] += __builtin_amdgcn_exp2f(fmaf(c[i], scale, -lq_));
@@ -212,6 +240,11 @@ __global__ void __launch_bounds__(256) k_prefill_colsum(Geo g, Bufs bf, int laye
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) cs[i] += (double)part[i];
+        if (qt + 1 < n_qt) {
+            tile_store<D>(qs[nb ^ 1], pre);
+            if (threadIdx.x < PF_TILE) ls[nb ^ 1][threadIdx.x] = lpre;
+        }
+        __syncthreads();
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
