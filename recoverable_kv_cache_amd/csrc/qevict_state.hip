@@ -650,10 +650,26 @@ __global__ void __launch_bounds__(PK_THREADS) k_pack(Geo g, Bufs bf, int layer, 
             if (threadIdx.x == 0) atomicOr(&hdr->status, QEVICT_DEV_E_POOL);
             continue;
         }
-        for (int e = threadIdx.x; e < W * d; e += PK_THREADS) {
-            const int t = e / d, c = e % d;
-            sk[e] = srck[from_page ? lay_k(t, c, d, W) : e];
-            sv[e] = srcv[from_page ? lay_v(t, c, d, W) : e];
+        // staged in batches of SB elements per thread, every load of a batch issued before
+        // the first LDS store (clamped addresses; positions past W*d are not stored)
+        constexpr int SB = 8;
+        for (int e0 = threadIdx.x; e0 < W * d; e0 += SB * PK_THREADS) {
+            uint16_t xk[SB], xv[SB];
+#pragma unroll
+            for (int k = 0; k < SB; ++k) {
+                const int e = min(e0 + k * PK_THREADS, W * d - 1), t = e / d, c = e % d;
+                xk[k] = srck[from_page ? lay_k(t, c, d, W) : e];
+                xv[k] = srcv[from_page ? lay_v(t, c, d, W) : e];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < SB; ++k) {
+                const int e = e0 + k * PK_THREADS;
+                if (e < W * d) {
+                    sk[e] = xk[k];
+                    sv[e] = xv[k];
+                }
+            }
         }
         __syncthreads();
         uint8_t* slot = bf.slots + u * (int64_t)g.n_slots * g.slot_bytes + (int64_t)pi.dst_slot * g.slot_bytes +
@@ -809,7 +825,9 @@ __global__ void __launch_bounds__(PK_THREADS) k_fill(Geo g, Bufs bf, int layer, 
 hipError_t launch_migrate(const Geo& g, const Bufs& bf, int layer, const uint16_t* kp, const uint16_t* vp,
                           hipStream_t s) {
     const int units = layer >= 0 ? g.B : g.B * g.L;
-    const int nb = 64;
+    // workgroups per unit: a prefill (one layer, every prompt window) spreads its items over
+    // about 1024 workgroups in all; a routing event over all layers moves few per unit
+    const int nb = layer >= 0 ? std::max(64, 1024 / std::max(g.B, 1)) : 64;
     hipLaunchKernelGGL(k_pack, dim3(units, nb), dim3(PK_THREADS), 0, s, g, bf, layer, kp, vp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
