@@ -22,6 +22,8 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int PF_TILE = 64;
 constexpr int PF_PAD = 8;   // LDS row padding (bf16 elements; rows stay 16-byte aligned)
+constexpr int PF_GQ = 2;    // query heads per workgroup of the LSE pass (when it divides the GQA group)
+constexpr int PF_KB = 2;    // 16-key blocks per wave of the column-sum pass
 
 __device__ __forceinline__ float4_t mfma32x(short8_t a, short8_t b, float4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(__bf16 __attribute__((ext_vector_type(8))), a),
@@ -55,36 +57,43 @@ __device__ __forceinline__ void tile_store(uint16_t (*dst)[D + PF_PAD], const ui
 }
 
 // ---------------------------------------------------------------- pass 1: row log-sum-exp (log2 domain)
-template <int D>
+// One workgroup: a 64-row query tile (16 rows per wave) of GQ query heads that share one
+// KV head; every key-tile operand read from LDS serves the GQ heads.  Key tiles are
+// double-buffered: the next tile's loads go out before this tile's products, and one
+// barrier per tile separates the last reads of a buffer from its next fill.
+template <int D, int GQ>
 __global__ void __launch_bounds__(256) k_prefill_lse(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qp,
                                                     const uint16_t* __restrict__ kp, float* __restrict__ lse2) {
-    __shared__ uint16_t ks[2][PF_TILE][D + PF_PAD];   // key tiles, double-buffered
-    const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    __shared__ uint16_t ks[2][PF_TILE][D + PF_PAD];
+    const int tile = blockIdx.x, h0 = blockIdx.y * GQ, b = blockIdx.z;
     const int S = bf.hdr[unit_of(g, b, layer)].prompt_len;
     if (tile * PF_TILE >= S) return;
-    const int G = g.h_q / g.h_kv, hk = h / G;
+    const int G = g.h_q / g.h_kv, hk = h0 / G;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lq = lane >> 4;
     const float scale = 1.4426950408889634f / sqrtf((float)D);
-    const uint16_t* Q = qp + ((int64_t)b * g.h_q + h) * g.S_max * D;
     const uint16_t* K = kp + ((int64_t)b * g.h_kv + hk) * g.S_max * D;
     const int r0 = tile * PF_TILE + wave * 16;
-    short8_t qa[D / 32];
-    {
+    short8_t qa[GQ][D / 32];
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+        const uint16_t* Q = qp + ((int64_t)b * g.h_q + h0 + hh) * g.S_max * D;
         const int row = r0 + lr;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
             uint4 v = make_uint4(0, 0, 0, 0);
             if (row < S) v = *reinterpret_cast<const uint4*>(Q + (int64_t)row * D + kk * 32 + 8 * lq);
-            qa[kk] = __builtin_bit_cast(short8_t, v);
+            qa[hh][kk] = __builtin_bit_cast(short8_t, v);
         }
     }
-    float m[4], l[4];
+    float m[GQ][4], l[GQ][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        m[i] = -INFINITY;
-        l[i] = 0.f;
-    }
+    for (int hh = 0; hh < GQ; ++hh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            m[hh][i] = -INFINITY;
+            l[hh][i] = 0.f;
+        }
     const int last_row = min(tile * PF_TILE + PF_TILE, S) - 1;
     const int n_kt = last_row / PF_TILE + 1;
     uint4 pre[D / 32];
@@ -92,20 +101,19 @@ __global__ void __launch_bounds__(256) k_prefill_lse(Geo g, Bufs bf, int layer, 
     tile_store<D>(ks[0], pre);
     __syncthreads();
     for (int kt = 0; kt < n_kt; ++kt) {
-        // the next key tile's loads go out before this tile's products (one barrier per tile:
-        // the buffer written below was last read before the previous barrier)
         if (kt + 1 < n_kt) tile_regs<D>(pre, K, (kt + 1) * PF_TILE, S);
         const uint16_t(*kb)[D + PF_PAD] = ks[kt & 1];
-        float4_t sacc[4];
+        float4_t sacc[GQ][4];
 #pragma unroll
         for (int sub = 0; sub < 4; ++sub) {
-            float4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int hh = 0; hh < GQ; ++hh) sacc[hh][sub] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < D / 32; ++kk) {
                 const short8_t bb = *reinterpret_cast<const short8_t*>(&kb[sub * 16 + lr][kk * 32 + 8 * lq]);
-                c = mfma32x(qa[kk], bb, c);
+#pragma unroll
+                for (int hh = 0; hh < GQ; ++hh) sacc[hh][sub] = mfma32x(qa[hh][kk], bb, sacc[hh][sub]);
             }
-            sacc[sub] = c;
         }
         // key tiles wholly below the row tile need neither the causal nor the length mask.
         // The reference m of a row moves lazily: only when a score exceeds it by more than 8
@@ -114,68 +122,80 @@ __global__ void __launch_bounds__(256) k_prefill_lse(Geo g, Bufs bf, int layer, 
         // the scaled ones)
         const bool full = (kt + 1) * PF_TILE <= tile * PF_TILE && (kt + 1) * PF_TILE <= S;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = r0 + 4 * lq + i;
-            if (full) {
-                const float mx = fmaxf(fmaxf(sacc[0][i], sacc[1][i]), fmaxf(sacc[2][i], sacc[3][i])) * scale;
-                if (mx > m[i] + 8.f) {
-                    l[i] *= m[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[i] - mx);
-                    m[i] = mx;
-                }
-                float s = l[i];
+        for (int hh = 0; hh < GQ; ++hh)
 #pragma unroll
-                for (int sub = 0; sub < 4; ++sub) s += __builtin_amdgcn_exp2f(fmaf(sacc[sub][i], scale, -m[i]));
-                l[i] = s;
-            } else {
-                float x[4], mx = -INFINITY;
+            for (int i = 0; i < 4; ++i) {
+                const int row = r0 + 4 * lq + i;
+                if (full) {
+                    const float mx =
+                        fmaxf(fmaxf(sacc[hh][0][i], sacc[hh][1][i]), fmaxf(sacc[hh][2][i], sacc[hh][3][i])) * scale;
+                    if (mx > m[hh][i] + 8.f) {
+                        l[hh][i] *= m[hh][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[hh][i] - mx);
+                        m[hh][i] = mx;
+                    }
+                    float s = l[hh][i];
 #pragma unroll
-                for (int sub = 0; sub < 4; ++sub) {
-                    const int key = kt * PF_TILE + sub * 16 + lr;
-                    x[sub] = (key <= row && key < S) ? sacc[sub][i] * scale : -INFINITY;
-                    mx = fmaxf(mx, x[sub]);
-                }
-                if (mx == -INFINITY) continue;
-                if (mx > m[i] + 8.f) {
-                    l[i] *= m[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[i] - mx);
-                    m[i] = mx;
-                }
-                float s = l[i];
+                    for (int sub = 0; sub < 4; ++sub) s += __builtin_amdgcn_exp2f(fmaf(sacc[hh][sub][i], scale, -m[hh][i]));
+                    l[hh][i] = s;
+                } else {
+                    float x[4], mx = -INFINITY;
 #pragma unroll
-                for (int sub = 0; sub < 4; ++sub) s += x[sub] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[sub] - m[i]);
-                l[i] = s;
+                    for (int sub = 0; sub < 4; ++sub) {
+                        const int key = kt * PF_TILE + sub * 16 + lr;
+                        x[sub] = (key <= row && key < S) ? sacc[hh][sub][i] * scale : -INFINITY;
+                        mx = fmaxf(mx, x[sub]);
+                    }
+                    if (mx == -INFINITY) continue;
+                    if (mx > m[hh][i] + 8.f) {
+                        l[hh][i] *= m[hh][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[hh][i] - mx);
+                        m[hh][i] = mx;
+                    }
+                    float s = l[hh][i];
+#pragma unroll
+                    for (int sub = 0; sub < 4; ++sub)
+                        s += x[sub] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[sub] - m[hh][i]);
+                    l[hh][i] = s;
+                }
             }
-        }
         if (kt + 1 < n_kt) tile_store<D>(ks[(kt + 1) & 1], pre);
         __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int hh = 0; hh < GQ; ++hh)
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            const float m2 = wave_xor(m[i], o), l2 = wave_xor(l[i], o);
-            const float M = fmaxf(m[i], m2);
-            float s = 0.f;
-            if (M > -INFINITY) {
-                s = (m[i] > -INFINITY ? l[i] * exp2f(m[i] - M) : 0.f) + (m2 > -INFINITY ? l2 * exp2f(m2 - M) : 0.f);
+        for (int i = 0; i < 4; ++i) {
+            float mi = m[hh][i], li = l[hh][i];
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) {
+                const float m2 = wave_xor(mi, o), l2 = wave_xor(li, o);
+                const float M = fmaxf(mi, m2);
+                float s = 0.f;
+                if (M > -INFINITY) {
+                    s = (mi > -INFINITY ? li * exp2f(mi - M) : 0.f) + (m2 > -INFINITY ? l2 * exp2f(m2 - M) : 0.f);
+                }
+                mi = M;
+                li = s;
             }
-            m[i] = M;
-            l[i] = s;
+            const int row = r0 + 4 * lq + i;
+            if (lr == 0 && row < S) lse2[((int64_t)b * g.h_q + h0 + hh) * g.S_max + row] = mi + log2f(li);
         }
-        const int row = r0 + 4 * lq + i;
-        if (lr == 0 && row < S) lse2[((int64_t)b * g.h_q + h) * g.S_max + row] = m[i] + log2f(l[i]);
-    }
 }
 
 // ---------------------------------------------------------------- pass 2: column sums (roles swapped)
-template <int D>
+// One workgroup: 64*KB keys of one query head; wave w holds the 16-key blocks w, w + 4, ...
+// (interleaved, so the causal triangle spreads evenly over the waves), and every query-tile
+// operand read from LDS serves its KB blocks.  Query tiles and their row LSEs are
+// double-buffered as in pass 1.  Per key the column sum runs over the query tiles in order.
+template <int D, int KB>
 __global__ void __launch_bounds__(256) k_prefill_colsum(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qp,
                                                        const uint16_t* __restrict__ kp,
                                                        const float* __restrict__ lse2, double* __restrict__ col) {
-    __shared__ uint16_t qs[2][PF_TILE][D + PF_PAD];   // query tiles and their row LSEs, double-buffered
+    __shared__ uint16_t qs[2][PF_TILE][D + PF_PAD];
     __shared__ float ls[2][PF_TILE];
-    const int ktile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int kgrp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int S = bf.hdr[unit_of(g, b, layer)].prompt_len;
-    if (ktile * PF_TILE >= S) return;
+    const int kg0 = kgrp * PF_TILE * KB;   // first key of the workgroup
+    if (kg0 >= S) return;
     const int G = g.h_q / g.h_kv, hk = h / G;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lq = lane >> 4;
@@ -183,30 +203,32 @@ __global__ void __launch_bounds__(256) k_prefill_colsum(Geo g, Bufs bf, int laye
     const uint16_t* Q = qp + ((int64_t)b * g.h_q + h) * g.S_max * D;
     const uint16_t* K = kp + ((int64_t)b * g.h_kv + hk) * g.S_max * D;
     const float* LS = lse2 + ((int64_t)b * g.h_q + h) * g.S_max;
-    const int k0 = ktile * PF_TILE + wave * 16;
-    short8_t ka[D / 32];
-    {
-        const int key = k0 + lr;
+    short8_t ka[KB][D / 32];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        const int key = kg0 + (kb * 4 + wave) * 16 + lr;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
             uint4 v = make_uint4(0, 0, 0, 0);
             if (key < S) v = *reinterpret_cast<const uint4*>(K + (int64_t)key * D + kk * 32 + 8 * lq);
-            ka[kk] = __builtin_bit_cast(short8_t, v);
+            ka[kb][kk] = __builtin_bit_cast(short8_t, v);
         }
     }
-    double cs[4] = {0.0, 0.0, 0.0, 0.0};
-    const int n_qt = (S - 1) / PF_TILE + 1;
+    double cs[KB][4];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cs[kb][i] = 0.0;
+    const int n_qt = (S - 1) / PF_TILE + 1, qt0 = kg0 / PF_TILE;
     uint4 pre[D / 32];
     float lpre = INFINITY;
-    tile_regs<D>(pre, Q, ktile * PF_TILE, S);
-    if (threadIdx.x < PF_TILE && ktile * PF_TILE + (int)threadIdx.x < S) lpre = LS[ktile * PF_TILE + threadIdx.x];
+    tile_regs<D>(pre, Q, qt0 * PF_TILE, S);
+    if (threadIdx.x < PF_TILE && qt0 * PF_TILE + (int)threadIdx.x < S) lpre = LS[qt0 * PF_TILE + threadIdx.x];
     tile_store<D>(qs[0], pre);
     if (threadIdx.x < PF_TILE) ls[0][threadIdx.x] = lpre;
     __syncthreads();
-    for (int qt = ktile; qt < n_qt; ++qt) {
-        // the next query tile's loads go out before this tile's products (one barrier per
-        // tile: the buffer written below was last read before the previous barrier)
-        const int nb = (qt - ktile) & 1;
+    for (int qt = qt0; qt < n_qt; ++qt) {
+        const int nb = (qt - qt0) & 1;
         if (qt + 1 < n_qt) {
             tile_regs<D>(pre, Q, (qt + 1) * PF_TILE, S);
             lpre = INFINITY;
@@ -215,31 +237,47 @@ __global__ void __launch_bounds__(256) k_prefill_colsum(Geo g, Bufs bf, int laye
         }
         const uint16_t(*qb)[D + PF_PAD] = qs[nb];
         const float* lb = ls[nb];
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
-        const bool full = qt > ktile && (qt + 1) * PF_TILE <= S;
+        float part[KB][4];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part[kb][i] = 0.f;
 #pragma unroll
         for (int sub = 0; sub < 4; ++sub) {
-            float4_t c = {0.f, 0.f, 0.f, 0.f};
+            float4_t c[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) c[kb] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < D / 32; ++kk) {
                 const short8_t bb = *reinterpret_cast<const short8_t*>(&qb[sub * 16 + lr][kk * 32 + 8 * lq]);
-                c = mfma32x(ka[kk], bb, c);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) c[kb] = mfma32x(ka[kb][kk], bb, c[kb]);
             }
             const int query = qt * PF_TILE + sub * 16 + lr;
             const float lq_ = lb[sub * 16 + lr];
-            if (full) {   // query tile wholly above the key tile and inside the prompt: no masks
 #pragma unroll
-                for (int i = 0; i < 4; ++i) part[i] += __builtin_amdgcn_exp2f(fmaf(c[i], scale, -lq_));
-            } else {
+            for (int kb = 0; kb < KB; ++kb) {
+                const int kbs = kg0 + (kb * 4 + wave) * 16;   // first key of the block
+                // (a block whose keys all follow the tile's queries adds exact zeros: skipped)
+                if (qt * PF_TILE + PF_TILE - 1 < kbs) continue;
+                // query tile wholly after the key block and inside the prompt: no masks
+                const bool full = qt * PF_TILE >= kbs + 16 && (qt + 1) * PF_TILE <= S;
+                if (full) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = k0 + 4 * lq + i;
-                    if (query >= key && query < S) part[i] += __builtin_amdgcn_exp2f(fmaf(c[i], scale, -lq_));
+                    for (int i = 0; i < 4; ++i) part[kb][i] += __builtin_amdgcn_exp2f(fmaf(c[kb][i], scale, -lq_));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = kbs + 4 * lq + i;
+                        if (query >= key && query < S) part[kb][i] += __builtin_amdgcn_exp2f(fmaf(c[kb][i], scale, -lq_));
+                    }
                 }
             }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cs[i] += (double)part[i];
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cs[kb][i] += (double)part[kb][i];
         if (qt + 1 < n_qt) {
             tile_store<D>(qs[nb ^ 1], pre);
             if (threadIdx.x < PF_TILE) ls[nb ^ 1][threadIdx.x] = lpre;
@@ -247,13 +285,15 @@ __global__ void __launch_bounds__(256) k_prefill_colsum(Geo g, Bufs bf, int laye
         __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        double v = cs[i];
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
-        const int key = k0 + 4 * lq + i;
-        if (lr == 0 && key < S) col[((int64_t)b * g.h_q + h) * g.S_max + key] = v;
-    }
+        for (int i = 0; i < 4; ++i) {
+            double v = cs[kb][i];
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+            const int key = kg0 + (kb * 4 + wave) * 16 + 4 * lq + i;
+            if (lr == 0 && key < S) col[((int64_t)b * g.h_q + h) * g.S_max + key] = v;
+        }
 }
 
 // ---------------------------------------------------------------- per-window reduction
@@ -386,13 +426,19 @@ hipError_t launch_prefill_scores(const Geo& g, const Bufs& bf, int layer, const 
     const size_t n = (size_t)g.B * g.h_q * g.S_max;
     float* lse2 = (float*)ws;
     double* col = (double*)((char*)ws + ((n * 4 + 255) & ~size_t(255)));
-    const dim3 grid((g.S_max + PF_TILE - 1) / PF_TILE, g.h_q, g.B);
+    // query heads per LSE workgroup (PF_GQ when it divides the GQA group) and 16-key blocks per
+    // wave in the column-sum pass
+    const int G = g.h_q / g.h_kv, gq = G % PF_GQ == 0 ? PF_GQ : 1;
+    const dim3 grid_l((g.S_max + PF_TILE - 1) / PF_TILE, g.h_q / gq, g.B);
+    const dim3 grid_c((g.S_max + PF_TILE * PF_KB - 1) / (PF_TILE * PF_KB), g.h_q, g.B);
     if (g.d == 128) {
-        hipLaunchKernelGGL((k_prefill_lse<128>), grid, dim3(256), 0, s, g, bf, layer, qp, kp, lse2);
-        hipLaunchKernelGGL((k_prefill_colsum<128>), grid, dim3(256), 0, s, g, bf, layer, qp, kp, lse2, col);
+        if (gq == PF_GQ) hipLaunchKernelGGL((k_prefill_lse<128, PF_GQ>), grid_l, dim3(256), 0, s, g, bf, layer, qp, kp, lse2);
+        else hipLaunchKernelGGL((k_prefill_lse<128, 1>), grid_l, dim3(256), 0, s, g, bf, layer, qp, kp, lse2);
+        hipLaunchKernelGGL((k_prefill_colsum<128, PF_KB>), grid_c, dim3(256), 0, s, g, bf, layer, qp, kp, lse2, col);
     } else {
-        hipLaunchKernelGGL((k_prefill_lse<64>), grid, dim3(256), 0, s, g, bf, layer, qp, kp, lse2);
-        hipLaunchKernelGGL((k_prefill_colsum<64>), grid, dim3(256), 0, s, g, bf, layer, qp, kp, lse2, col);
+        if (gq == PF_GQ) hipLaunchKernelGGL((k_prefill_lse<64, PF_GQ>), grid_l, dim3(256), 0, s, g, bf, layer, qp, kp, lse2);
+        else hipLaunchKernelGGL((k_prefill_lse<64, 1>), grid_l, dim3(256), 0, s, g, bf, layer, qp, kp, lse2);
+        hipLaunchKernelGGL((k_prefill_colsum<64, PF_KB>), grid_c, dim3(256), 0, s, g, bf, layer, qp, kp, lse2, col);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
