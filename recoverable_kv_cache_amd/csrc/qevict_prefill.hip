@@ -297,32 +297,42 @@ __global__ void __launch_bounds__(256) k_prefill_colsum(Geo g, Bufs bf, int laye
 }
 
 // ---------------------------------------------------------------- per-window reduction
-__global__ void k_prefill_windows(Geo g, Bufs bf, int layer, const double* __restrict__ col) {
+// Window scores from the column sums: a workgroup takes 64 windows, its four waves a
+// quarter of the query heads each (partial sums over their heads and the window's tokens,
+// then summed in LDS); the first workgroup also sums the sink columns.
+__global__ void __launch_bounds__(256) k_prefill_windows(Geo g, Bufs bf, int layer, const double* __restrict__ col) {
+    __shared__ double part[4][64];
     const int b = blockIdx.x;
     const int64_t u = unit_of(g, b, layer);
     UnitHdr* hdr = bf.hdr + u;
     const int S = hdr->prompt_len;
     const int n_win = S > g.n_sink ? (S - g.n_sink + g.W - 1) / g.W : 0;
-    for (int w = threadIdx.x; w < g.n_windows; w += blockDim.x) {
-        double s = 0.0;
-        if (w < n_win) {
-            const int a = g.n_sink + w * g.W, e = min(a + g.W, S);
-            for (int h = 0; h < g.h_q; ++h) {
-                const double* c = col + ((int64_t)b * g.h_q + h) * g.S_max;
-                for (int t = a; t < e; ++t) s += c[t];
-            }
-            s /= g.h_q;
+    const int w = blockIdx.y * 64 + (threadIdx.x & 63), hg = threadIdx.x >> 6;
+    double s = 0.0;
+    if (col && w < n_win) {
+        const int a = g.n_sink + w * g.W, e = min(a + g.W, S);
+        for (int h = hg; h < g.h_q; h += 4) {
+            const double* c = col + ((int64_t)b * g.h_q + h) * g.S_max;
+#pragma unroll 8
+            for (int t = a; t < e; ++t) s += c[t];
         }
+    }
+    part[hg][threadIdx.x & 63] = s;
+    __syncthreads();
+    if (threadIdx.x < 64 && w < g.n_windows) {
+        double t = 0.0;
+        if (w < n_win) t = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x] + part[3][threadIdx.x]) / g.h_q;
         // (p-norm ranker: P_0 = S_0^3, the initialisation as the first event-level score)
-        bf.score[u * g.n_windows + w] = (g.flags & QEVICT_F_RANK_PNORM) ? s * s * s : s;
+        bf.score[u * g.n_windows + w] = (g.flags & QEVICT_F_RANK_PNORM) ? t * t * t : t;
         bf.uacc[u * g.n_windows + w] = 0.0;
     }
-    if (threadIdx.x == 0) {
-        double s = 0.0;
+    if (blockIdx.y == 0 && threadIdx.x == 0) {
+        double sm = 0.0;
         const int ns = min(g.n_sink, S);
-        for (int h = 0; h < g.h_q; ++h)
-            for (int t = 0; t < ns; ++t) s += col[((int64_t)b * g.h_q + h) * g.S_max + t];
-        hdr->sink_mass = s / g.h_q;
+        if (col)
+            for (int h = 0; h < g.h_q; ++h)
+                for (int t = 0; t < ns; ++t) sm += col[((int64_t)b * g.h_q + h) * g.S_max + t];
+        hdr->sink_mass = sm / g.h_q;
     }
 }
 
@@ -419,8 +429,9 @@ hipError_t launch_prefill_scores(const Geo& g, const Bufs& bf, int layer, const 
         hipLaunchKernelGGL(k_score_copy, dim3(g.B), dim3(256), 0, s, g, bf, layer, score_init);
         return hipGetLastError();
     }
+    const dim3 grid_w(g.B, std::max(1, (g.n_windows + 63) / 64));
     if (g.S_max == 0) {
-        hipLaunchKernelGGL(k_prefill_windows, dim3(g.B), dim3(256), 0, s, g, bf, layer, (const double*)nullptr);
+        hipLaunchKernelGGL(k_prefill_windows, grid_w, dim3(256), 0, s, g, bf, layer, (const double*)nullptr);
         return hipGetLastError();
     }
     const size_t n = (size_t)g.B * g.h_q * g.S_max;
@@ -442,7 +453,7 @@ hipError_t launch_prefill_scores(const Geo& g, const Bufs& bf, int layer, const 
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_prefill_windows, dim3(g.B), dim3(256), 0, s, g, bf, layer, col);
+    hipLaunchKernelGGL(k_prefill_windows, grid_w, dim3(256), 0, s, g, bf, layer, col);
     return hipGetLastError();
 }
 
