@@ -62,7 +62,7 @@ __device__ __forceinline__ void tile_store(uint16_t (*dst)[D + PF_PAD], const ui
 // double-buffered: the next tile's loads go out before this tile's products, and one
 // barrier per tile separates the last reads of a buffer from its next fill.
 template <int D, int GQ>
-__global__ void __launch_bounds__(256) k_prefill_lse(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qp,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k_prefill_lse(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qp,
                                                     const uint16_t* __restrict__ kp, float* __restrict__ lse2) {
     __shared__ uint16_t ks[2][PF_TILE][D + PF_PAD];
     const int tile = blockIdx.x, h0 = blockIdx.y * GQ, b = blockIdx.z;
