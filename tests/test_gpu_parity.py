@@ -93,6 +93,17 @@ def test_one_way_and_route_step_scoring_flags():
     assert sum(e["promoted"] for e in ls.units[0].events) == 0
 
 
+def test_mha_one_query_head_per_kv_head():
+    """Plain multi-head attention (G = 1: the decode kernel's one-head column layout and the
+    prefill passes' one-head workgroups), d = 128, W = 32, ragged batch, topic drift."""
+    _print("case: mha")
+    wl = WL.Workload("mha", 1, 2, 4, 4, 128, 600, 32, 32, 4, 64, 8, 0.30, 0.70, prompt_len_min=350,
+                     n_outlier=2, n_topics=2, topic_period=8)
+    ls = Lockstep(wl).run(32)
+    assert any(u.win[w].ledger is not None for u in ls.units for w in u.win)
+    _print(f"mha: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}")
+
+
 def test_short_prompt_edge_cases():
     """Prompts shorter than the sinks, empty prompts and a prompt that ends on a window edge."""
     for S in (0, 3, 4, 20):
