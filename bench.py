@@ -49,6 +49,54 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def timed_schedule(steps: int, warmup: int, omega: int, every: int = TIME_EVERY) -> list[tuple[int, int, bool, bool]]:
+    """The timed steps as (i, j, routes, sampled): i counts timed steps from 0, j = warmup + i is
+    the decode step index, ``routes`` is true when a routing event follows step j
+    ((j + 1) % omega == 0, after the decode of every layer), and ``sampled`` marks the steps
+    whose split-K launches carry dispatch-stamped events (one in ``every``, rotating through
+    the positions of the block so that every phase of the routing interval is sampled)."""
+    if steps < 0 or warmup < 0 or omega < 1 or every < 1:
+        raise ValueError("steps, warmup >= 0 and omega, every >= 1")
+    return [(i, warmup + i, (warmup + i + 1) % omega == 0, i % every == (i // every) % every)
+            for i in range(steps)]
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def host_workers() -> int:
+    """Threads for drawing inputs on the host: the cores this process may use, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def prompts_in_order(wl, layers, workers: int):
+    """Yield (layer, (q, k, v)) for each layer, drawn on the host (the oracle's streams),
+    with at most ``workers`` layers drawn ahead at a time."""
+    from concurrent.futures import ThreadPoolExecutor
+    from recoverable_kv_cache_amd import workload as WL
+    layers = list(layers)
+    with ThreadPoolExecutor(workers) as ex:
+        futs = {}
+        nxt = 0
+        for l in layers:
+            while nxt < len(layers) and len(futs) < workers:
+                futs[layers[nxt]] = ex.submit(WL.prompt, wl, layers[nxt])
+                nxt += 1
+            yield l, futs.pop(l).result()
+
+
 def cpu_baseline(wl, budget_s: float = 20.0, ranker: str = "cum", quant_bits: int = 2, rope_cs=None) -> dict:
     """Time the fp64 oracle's decode step on the host (layer 0, sequence 0), with a
     synthetic initial score instead of the prompt column sums (those alone are
@@ -65,27 +113,27 @@ def cpu_baseline(wl, budget_s: float = 20.0, ranker: str = "cum", quant_bits: in
     ocfg = O.OracleConfig(wl.h_q, wl.h_kv, wl.d_head, wl.window, wl.n_sink, wl.n_local, wl.omega,
                           wl.quant_frac, wl.budget_frac, wl.n_decode, ranker=ranker, quant_bits=quant_bits,
                           rope=rope_cs is not None)
-    S = wl.prompt_len
-    qp, kp, vp = WL.prompt(wl.with_(batch=1), 0)
+    S = wl.prompt_lens()[0]
+    qp, kp, vp = WL.prompt(wl, 0, with_q=False, seqs=[0])
     f = lambda t: t.to(torch.float64).numpy()
     unit = O.UnitOracle(ocfg, S, rope_cs=None if rope_cs is None else rope_cs.numpy())
-    n_win = (S - wl.n_sink + wl.window - 1) // wl.window
+    n_win = (wl.prompt_len - wl.n_sink + wl.window - 1) // wl.window
     t0 = time.perf_counter()
-    unit.prefill(f(qp[0]), f(kp[0]), f(vp[0]), score_init=WL.init_scores(wl, 0, n_win)[0].numpy())
+    unit.prefill(None, f(kp[0, :, :S]), f(vp[0, :, :S]), score_init=WL.init_scores(wl, 0, n_win)[0].numpy())
     setup_s = time.perf_counter() - t0
-    del qp
+    del kp, vp
     times = []
     j = 0
     t_start = time.perf_counter()
     while j < wl.n_decode and (time.perf_counter() - t_start < budget_s or j < 2):
-        q, k, v = WL.decode_step(wl.with_(batch=1), 0, j)
+        q, k, v = WL.decode_step(wl.with_(batch=1), 0, j)   # sequence 0's streams
         t1 = time.perf_counter()
         unit.decode(f(q[0]), f(k[0]), f(v[0]))
         times.append(time.perf_counter() - t1)
         j += 1
     per_layer_step = statistics.mean(times)
     return {"value": round(wl.batch / (per_layer_step * wl.n_layers), 4), "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"fp64 NumPy oracle, layer 0 / sequence 0 of the same workload, {len(times)} decode steps "
                       f"({per_layer_step * 1e3:.0f} ms per layer-step, setup {setup_s:.1f} s), "
                       f"extrapolated x{wl.n_layers} layers x batch {wl.batch}"}
@@ -182,11 +230,14 @@ def main():
     log(f"[bench] {wl.name}: arena {st.info.arena_bytes / 2**30:.2f} GiB, splits {st.info.n_splits}, "
         f"K_f {st.info.max_K_f}, K_q {st.info.max_K_q}")
 
-    # ---- prefill every layer (column sums on MFMA), inputs generated on the GPU
+    # ---- prefill every layer (column sums on MFMA); the prompts are drawn on the host from
+    # the same streams the oracle reads and copied to the device
+    workers = host_workers()
     torch.cuda.synchronize()
     t_pf = 0.0
-    for l in range(wl.n_layers):
-        qp, kp, vp = WL.prompt(wl, l, device=dev)
+    t_gen = time.perf_counter()
+    for l, (qp, kp, vp) in prompts_in_order(wl, range(wl.n_layers), workers):
+        qp, kp, vp = qp.to(dev), kp.to(dev), vp.to(dev)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         st.prefill_init(l, qp, kp, vp)
@@ -194,15 +245,19 @@ def main():
         t_pf += time.perf_counter() - t0
         del qp, kp, vp
         if l % 8 == 0:
-            log(f"[bench] prefill layer {l} done ({t_pf:.1f} s so far)")
+            log(f"[bench] prefill layer {l} done ({t_pf:.1f} s of prefill, {time.perf_counter() - t_gen:.1f} s so far)")
     assert st.poll_status() == 0, "device status after prefill"
 
-    # ---- decode inputs for every (step, layer), resident in HBM
+    # ---- decode inputs for every (step, layer), drawn on the host and resident in HBM
+    from concurrent.futures import ThreadPoolExecutor
     n_total = args.warmup + args.steps
-    inputs = [[WL.decode_step(wl, l, j, device=dev) for l in range(wl.n_layers)] for j in range(n_total)]
+    with ThreadPoolExecutor(workers) as ex:
+        host_in = list(ex.map(lambda j: [WL.decode_step(wl, l, j) for l in range(wl.n_layers)], range(n_total)))
+    inputs = [[tuple(t.to(dev) for t in qkv) for qkv in row] for row in host_in]
+    del host_in
     out = torch.empty((wl.batch, wl.h_q, wl.d_head), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
-    log("[bench] inputs ready")
+    log(f"[bench] inputs ready ({time.perf_counter() - t_gen:.1f} s)")
 
     def new_event():
         e = torch.cuda.Event(enable_timing=True)
@@ -221,38 +276,34 @@ def main():
             st.route(-1)
             if route_ev is not None:
                 route_ev[1].record()
-            return True
-        return False
 
     for j in range(args.warmup):
         run_step(j)
     torch.cuda.synchronize()
     kv0 = [st.step_bytes(l) for l in range(wl.n_layers)]
 
-    # ---- timed region: wall-clock events around all steps; the split-K kernels of every
-    # TIME_EVERY-th step carry events stamped by their own dispatch (start / end), and
-    # every routing event is bracketed by events
-    timed_steps = [i for i in range(args.steps) if i % TIME_EVERY == (i // TIME_EVERY) % TIME_EVERY]
-    kev = {i: [(new_event(), new_event()) for _ in range(wl.n_layers)] for i in timed_steps}
-    rev = [(new_event(), new_event()) for _ in range(args.steps // wl.omega + 1)]
+    # ---- timed region: wall-clock events around all steps; the split-K kernels of the
+    # sampled steps carry events stamped by their own dispatch (start / end), and every
+    # routing event is bracketed by events
+    sched = timed_schedule(args.steps, args.warmup, wl.omega)
+    kev = {i: [(new_event(), new_event()) for _ in range(wl.n_layers)] for i, _, _, s_ in sched if s_}
+    rev = {i: (new_event(), new_event()) for i, _, r, _ in sched if r}
     start, stop = new_event(), new_event()
     torch.cuda.synchronize()
     start.record()
-    n_route = 0
-    for i in range(args.steps):
-        j = args.warmup + i
-        if run_step(j, timing=kev.get(i), route_ev=rev[n_route]):
-            n_route += 1
+    for i, j, _, _ in sched:
+        run_step(j, timing=kev.get(i), route_ev=rev.get(i))
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    route_ms = [rev[r][0].elapsed_time(rev[r][1]) for r in range(n_route)]
-    kern_ms = [kev[i][l][0].elapsed_time(kev[i][l][1]) for i in timed_steps for l in range(wl.n_layers)]
+    route_ms = [e0.elapsed_time(e1) for e0, e1 in rev.values()]
+    n_route = len(route_ms)
+    kern_ms = [e0.elapsed_time(e1) for evs in kev.values() for e0, e1 in evs]
     kv1 = [st.step_bytes(l) for l in range(wl.n_layers)]
     status = st.poll_status()
     assert status == 0, f"device status {status}"
 
-    avg_kernel_s = statistics.mean(kern_ms) * 1e-3
+    avg_kernel_s = statistics.mean(kern_ms) * 1e-3 if kern_ms else float("nan")
     kv_per_launch = statistics.mean([(a[0] + b[0]) / 2 for a, b in zip(kv0, kv1)])
     io_per_launch = kv0[0][1]
     alg_bytes = kv_per_launch + io_per_launch
@@ -289,7 +340,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": f"bf16 + int{args.quant_bits} operands, fp32 accumulate",
         "data": "synthetic",
         "config": {"workload": wl.name, "layers": wl.n_layers, "batch": wl.batch, "h_q": wl.h_q, "h_kv": wl.h_kv,
                    "d_head": wl.d_head, "prompt_len": wl.prompt_len, "window": wl.window, "n_sink": wl.n_sink,

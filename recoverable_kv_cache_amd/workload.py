@@ -128,18 +128,20 @@ def _outlier_channels(wl: Workload, layer: int) -> torch.Tensor:
     return torch.stack(rows) if rows and wl.n_outlier > 0 else torch.zeros((wl.h_kv, 0), dtype=torch.long)
 
 
-def prompt(wl: Workload, layer: int, device="cpu", with_q: bool = True):
+def prompt(wl: Workload, layer: int, device="cpu", with_q: bool = True, seqs: Optional[Sequence[int]] = None):
     """Prompt tensors for one layer, bf16, zero-padded past each prompt length.
 
     Returns ``q [B][H_q][S][d]``, ``k, v [B][H_kv][S][d]`` with ``S = wl.prompt_len``
     (``q`` is None with ``with_q=False``; the keys and values do not depend on it).
+    ``seqs`` draws only those sequences of the batch, in the given order (their rows are
+    the same as in the whole batch's draw).
     """
     S, d = wl.prompt_len, wl.d_head
     lens = wl.prompt_lens()
     gen_dev = device if str(device).startswith("cuda") else "cpu"
     qs, ks, vs = [], [], []
     outl = _outlier_channels(wl, layer)
-    for b in range(wl.batch):
+    for b in (range(wl.batch) if seqs is None else seqs):
         q = _normal((wl.h_q, S, d), _gen(wl.seed, layer, b, _S_QP, gen_dev), gen_dev) if with_q else None
         k = _normal((wl.h_kv, S, d), _gen(wl.seed, layer, b, _S_KP, gen_dev), gen_dev)
         v = _normal((wl.h_kv, S, d), _gen(wl.seed, layer, b, _S_VP, gen_dev), gen_dev)
@@ -174,32 +176,39 @@ def _phase(wl: Workload, step: int) -> tuple[int, float]:
 
 
 def decode_step(wl: Workload, layer: int, step: int, device="cpu") -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Decode inputs for one step of one layer: ``q [B][H_q][d]``, ``k, v [B][H_kv][d]`` (bf16)."""
+    """Decode inputs for one step of one layer: ``q [B][H_q][d]``, ``k, v [B][H_kv][d]`` (bf16).
+
+    Each sequence draws from its own streams (keyed by layer, sequence and step); the
+    outlier scaling and the drift are then applied to the whole batch at once."""
     d = wl.d_head
     gen_dev = device if str(device).startswith("cuda") else "cpu"
     G = wl.h_q // wl.h_kv
-    outl = _outlier_channels(wl, layer)
     qs, ks, vs = [], [], []
     for b in range(wl.batch):
         # one generator per (layer, b, step) so steps are independent slices
-        gq = _gen(wl.seed, layer, b * 1_000_003 + step, _S_QD, gen_dev)
-        gk = _gen(wl.seed, layer, b * 1_000_003 + step, _S_KD, gen_dev)
-        gv = _gen(wl.seed, layer, b * 1_000_003 + step, _S_VD, gen_dev)
-        q = _normal((wl.h_q, d), gq, gen_dev)
-        k = _normal((wl.h_kv, d), gk, gen_dev)
-        v = _normal((wl.h_kv, d), gv, gen_dev)
-        if wl.n_outlier:
-            for h in range(wl.h_kv):
-                k[h][outl[h].to(k.device)] *= 10.0
-        if wl.n_topics:
-            j, phi = _phase(wl, step)
-            u = _topic_dirs(wl, layer, b, str(q.device))[:, j, :]          # [h_kv][d]
-            uq = u.repeat_interleave(G, dim=0)                        # [h_q][d]
-            q = math.cos(phi) * q + math.sin(phi) * math.sqrt(d) * uq
-        qs.append(q.to(torch.bfloat16))
-        ks.append(k.to(torch.bfloat16))
-        vs.append(v.to(torch.bfloat16))
-    return (torch.stack(qs).to(device), torch.stack(ks).to(device), torch.stack(vs).to(device))
+        key = b * 1_000_003 + step
+        qs.append(_normal((wl.h_q, d), _gen(wl.seed, layer, key, _S_QD, gen_dev), gen_dev))
+        ks.append(_normal((wl.h_kv, d), _gen(wl.seed, layer, key, _S_KD, gen_dev), gen_dev))
+        vs.append(_normal((wl.h_kv, d), _gen(wl.seed, layer, key, _S_VD, gen_dev), gen_dev))
+    q, k, v = torch.stack(qs), torch.stack(ks), torch.stack(vs)
+    if wl.n_outlier:
+        k *= _outlier_scale(wl, layer, str(k.device))
+    if wl.n_topics:
+        j, phi = _phase(wl, step)
+        u = torch.stack([_topic_dirs(wl, layer, b, str(q.device))[:, j, :] for b in range(wl.batch)])
+        uq = u.repeat_interleave(G, dim=1)                           # [B][h_q][d]
+        q = math.cos(phi) * q + math.sin(phi) * math.sqrt(d) * uq
+    return q.to(torch.bfloat16).to(device), k.to(torch.bfloat16).to(device), v.to(torch.bfloat16).to(device)
+
+
+@functools.lru_cache(maxsize=4096)
+def _outlier_scale(wl: Workload, layer: int, device) -> torch.Tensor:
+    """[h_kv][d] float32: 10 on the layer's outlier key channels, 1 elsewhere."""
+    m = torch.ones((wl.h_kv, wl.d_head), dtype=torch.float32)
+    outl = _outlier_channels(wl, layer)
+    for h in range(wl.h_kv):
+        m[h, outl[h]] = 10.0
+    return m.to(device)
 
 
 def init_scores(wl: Workload, layer: int, n_windows: int, device="cpu") -> torch.Tensor:
