@@ -328,6 +328,24 @@ def route_order(cand, scores: dict) -> list:
     return sorted(cand, key=lambda w: (-scores[w], w))
 
 
+def select_tiers(cand, scores: dict, K_f: int, K_q: int, no_full=()) -> tuple[list, list, list]:
+    """Eqs. 4-5 of [QEvict] §4.3: the first K_f candidates in rank order become Full, the
+    next K_q Quantized, the rest Evicted.
+
+    ``no_full`` holds the windows that may not enter the Full tier.  It is empty for the
+    bidirectional policy; the one-way policy of Appendix K passes the windows that are
+    Quantized before the event (they may stay Quantized or be evicted, never return to
+    Full).  Both policies use the same capacities and the same rank order, so the one-way
+    Full tier is the top K_f of the eligible candidates, and the Quantized tier the next
+    K_q of all remaining candidates, Quantized or not, in that same order."""
+    order = route_order(cand, scores)
+    barred = set(no_full)
+    F = [w for w in order if w not in barred][:K_f]
+    chosen = set(F)
+    rest = [w for w in order if w not in chosen]
+    return F, rest[:K_q], rest[K_q:]
+
+
 # --------------------------------------------------------------------------------------
 # one (sequence, layer) unit of QEvict state: C = (S, L, F, Q, E) plus S_bar and Lambda
 # --------------------------------------------------------------------------------------
@@ -533,16 +551,8 @@ class UnitOracle:
         prev_f = [w for w, W in self.win.items() if W.state == FULL]
         prev_q = [w for w, W in self.win.items() if W.state == QUANT]
         cand = prev_f + prev_q + aged
-        if cfg.promote:
-            order = route_order(cand, self.score)
-            F = order[:K_f]
-            Q = order[K_f:K_f + K_q]
-            E = order[K_f + K_q:]
-        else:
-            # one-way variant: a Quantized window cannot return to the Full tier
-            F = route_order([w for w in cand if w not in prev_q], self.score)[:K_f]
-            rest = route_order([w for w in cand if w not in F], self.score)
-            Q, E = rest[:K_q], rest[K_q:]
+        # one-way variant (Appendix K): a Quantized window cannot return to the Full tier
+        F, Q, E = select_tiers(cand, self.score, K_f, K_q, () if cfg.promote else prev_q)
         ctr = dict(aged=len(aged), promoted=0, packed=0, reactivated=0, demoted=0, evicted=len(E),
                    n_full=len(F), n_quant=len(Q))
         # Algorithm 1 steps 5-10: Q -> F dequantizes the ledger and marks it dormant

@@ -133,3 +133,41 @@ def test_quantizing_rotated_keys_is_caught(monkeypatch):
 def test_attending_unrotated_quantized_keys_is_caught(monkeypatch):
     monkeypatch.setattr(O.UnitOracle, "quant_keys", lambda self, w: self.win[w].ledger.k_hat())
     _fails(TR.test_quantized_windows_attend_with_re_rotated_keys)
+
+
+def test_one_way_full_tier_left_short_is_caught(monkeypatch):
+    """Planted: the one-way Full tier taken as the top K_f of all candidates with the Quantized
+    winners dropped (|F| < K_f)."""
+    def short(cand, scores, K_f, K_q, no_full=()):
+        order = O.route_order(cand, scores)
+        F = [w for w in order[:K_f] if w not in set(no_full)]
+        rest = [w for w in order if w not in F]
+        return F, rest[:K_q], rest[K_q:]
+
+    monkeypatch.setattr(O, "select_tiers", short)
+    _fails(TS.test_route_sets_hand_case_one_way)
+
+
+def test_one_way_quantized_windows_ranked_last_are_caught(monkeypatch):
+    """Planted: windows already Quantized forced behind every other candidate for the
+    Quantized tier under the one-way policy."""
+    def last(cand, scores, K_f, K_q, no_full=()):
+        barred = set(no_full)
+        order = O.route_order(cand, scores)
+        F = [w for w in order if w not in barred][:K_f]
+        rest = [w for w in order if w not in F and w not in barred] + [w for w in order if w in barred]
+        return F, rest[:K_q], rest[K_q:]
+
+    monkeypatch.setattr(O, "select_tiers", last)
+    _fails(TS.test_route_sets_hand_case_one_way)
+
+
+def test_one_way_branch_applied_to_the_bidirectional_policy_is_caught(monkeypatch):
+    """Planted: the bidirectional policy barring Quantized windows from Full as well."""
+    real = O.select_tiers
+
+    def always_barred(cand, scores, K_f, K_q, no_full=()):
+        return real(cand, scores, K_f, K_q, [w for w in cand if w in (0, 4)])
+
+    monkeypatch.setattr(O, "select_tiers", always_barred)
+    _fails(TS.test_route_sets_hand_case_bidirectional)

@@ -289,3 +289,52 @@ def test_drift_workload_exercises_promotion():
     unit, _ = run_unit(wl, cfg, collect=False, score_init=np.zeros(32))
     assert sum(e["promoted"] for e in unit.events) > 0
     assert sum(e["packed"] for e in unit.events) > 0
+
+
+def _hand_pool(promote: bool):
+    """A unit with seven windows of four tokens after two sinks (30 positions, four recent):
+    window 0 Quantized (score 10), 1 Full (5), 2 aged recent (8), 3 aged recent (1),
+    4 Quantized (0.5), 5 Full (3), 6 still recent (100, not a candidate); K_f = K_q = 2."""
+    cfg = O.OracleConfig(h_q=2, h_kv=1, d=16, window=4, n_sink=2, n_local=4, omega=1, quant_frac=0.5,
+                         budget_frac=1.0, n_decode=0, promote=promote)
+    rng = np.random.default_rng(7)
+    unit = O.UnitOracle(cfg, 30)
+    for p in range(30):
+        unit._store(p, O.to_bf16(rng.standard_normal((1, 16))), O.to_bf16(rng.standard_normal((1, 16))))
+    unit.n = 30
+    unit.caps = dict(unit.caps, K_f=2, K_q=2)
+    for w in (0, 4):
+        W = unit.win[w]
+        W.ledger = O.quantize_window(W.k, W.v, unit.win_start(w))
+        W.state, W.k, W.v = O.QUANT, None, None
+    for w in (1, 5):
+        unit.win[w].state = O.FULL
+    unit.score.update({0: 10.0, 1: 5.0, 2: 8.0, 3: 1.0, 4: 0.5, 5: 3.0, 6: 100.0})
+    return unit
+
+
+def test_route_sets_hand_case_bidirectional():
+    """Eqs. 4-5 worked by hand: rank order 0 (10), 2 (8), 1 (5), 5 (3), 3 (1), 4 (0.5); window 6
+    has not aged (its end 30 > n - n_local = 26) and is no candidate."""
+    unit = _hand_pool(promote=True)
+    ev = unit.route()
+    assert (ev["F"], ev["Q"], ev["E"]) == ([0, 2], [1, 5], [3, 4])
+    assert (ev["promoted"], ev["packed"], ev["demoted"], ev["evicted"]) == (1, 2, 2, 2)
+    states = {w: unit.win[w].state for w in range(7)}
+    assert states == {0: O.FULL, 1: O.QUANT, 2: O.FULL, 3: O.EVICTED, 4: O.EVICTED, 5: O.QUANT, 6: O.LOCAL}
+    assert unit.win[0].ledger.dormant
+
+
+def test_route_sets_hand_case_one_way():
+    """The one-way policy of [QEvict] Appendix K on the same pool: same capacities and rank
+    order, but Quantized windows 0 and 4 may not enter Full.  Full = the top two of the eligible
+    windows {2 (8), 1 (5), 5 (3), 3 (1)}; Quantized = the next two of everything left in rank
+    order {0 (10), 5 (3), 3 (1), 4 (0.5)}: window 0 outranks all and stays Quantized."""
+    unit = _hand_pool(promote=False)
+    ev = unit.route()
+    assert (ev["F"], ev["Q"], ev["E"]) == ([2, 1], [0, 5], [3, 4])
+    assert (ev["promoted"], ev["packed"], ev["demoted"], ev["evicted"]) == (0, 1, 1, 2)
+    assert len(ev["F"]) == unit.caps["K_f"]               # the Full tier is filled, not left short
+    states = {w: unit.win[w].state for w in range(7)}
+    assert states == {0: O.QUANT, 1: O.FULL, 2: O.FULL, 3: O.EVICTED, 4: O.EVICTED, 5: O.QUANT, 6: O.LOCAL}
+    assert not unit.win[0].ledger.dormant
