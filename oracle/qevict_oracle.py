@@ -422,10 +422,13 @@ class UnitOracle:
         return rope_rotate(kh, self.positions(w), self.cs) if self.cfg.rope else kh
 
     # --- the accessible set (sinks, LOCAL, FULL, QUANT) ------------------------------
-    def accessible(self):
+    def accessible(self, qexec_bf16: Optional[bool] = None):
         """Returns (owner[n_acc], K[H_kv][n_acc][d], V[H_kv][n_acc][d]) in chronological
-        order; owner = -1 for sink tokens, else the window index."""
+        order; owner = -1 for sink tokens, else the window index.  Quantized values are
+        x_hat, or bf16(x_hat) with ``qexec_bf16`` (default: the config's reading R2)."""
         cfg = self.cfg
+        if qexec_bf16 is None:
+            qexec_bf16 = cfg.qexec_bf16
         ns = min(cfg.n_sink, self.n)
         owners = [np.full(ns, -1)]
         Ks = [self.sink_k[:, :ns]]
@@ -437,7 +440,7 @@ class UnitOracle:
             ntok = min(cfg.window, self.n - self.win_start(w))
             if W.state == QUANT:
                 kh, vh = self.quant_keys(w), W.ledger.v_hat()
-                if cfg.qexec_bf16:
+                if qexec_bf16:
                     kh, vh = to_bf16(kh), to_bf16(vh)
                 Ks.append(kh[:, :ntok])
                 Vs.append(vh[:, :ntok])
@@ -492,14 +495,7 @@ class UnitOracle:
         q, k = self.rotate_in(q, self.n), self.rotate_in(k, self.n)
         self._store(self.n, k, v)
         self.n += 1
-        owner, K, V = self.accessible()
-        G = cfg.group
-        o = np.zeros((cfg.h_q, cfg.d))
-        A = np.zeros((cfg.h_q, owner.shape[0]))
-        for h in range(cfg.h_q):
-            a = softmax(K[h // G] @ q[h] / math.sqrt(cfg.d))
-            A[h] = a
-            o[h] = a @ V[h // G]
+        o, A, owner = self.attend(q)
         accumulate = (cfg.score_every_step or ((self.step + 1) % cfg.omega == 0)) and cfg.ranker != "keynorm"
         mass = {}
         for w in np.unique(owner[owner >= 0]):
@@ -515,7 +511,23 @@ class UnitOracle:
         tier_mass["sink"] = A[:, owner < 0].sum(axis=1)
         for w in np.unique(owner[owner >= 0]):
             tier_mass[self.win[int(w)].state] += A[:, owner == w].sum(axis=1)
-        return dict(o=o, mass=mass, tier_mass=tier_mass, probs=A, owner=owner)
+        return dict(o=o, mass=mass, tier_mass=tier_mass, probs=A, owner=owner, q_rot=q)
+
+    def attend(self, q: np.ndarray, qexec_bf16: Optional[bool] = None):
+        """Softmax attention ([QEvict] §4.1) of the queries q [H_q][d] (as the cache holds
+        them: rotated with RoPE) over the current accessible set, logits q.k / sqrt(d).
+        Returns (o [H_q][d], probabilities A [H_q][n_acc], owner [n_acc]); the state is not
+        changed.  ``qexec_bf16`` selects the Quantized values as in ``accessible``."""
+        cfg = self.cfg
+        owner, K, V = self.accessible(qexec_bf16)
+        G = cfg.group
+        o = np.zeros((cfg.h_q, cfg.d))
+        A = np.zeros((cfg.h_q, owner.shape[0]))
+        for h in range(cfg.h_q):
+            a = softmax(K[h // G] @ q[h] / math.sqrt(cfg.d))
+            A[h] = a
+            o[h] = a @ V[h // G]
+        return o, A, owner
 
     # --- alternative rankers ([QEvict] Appendix J) ------------------------------------
     def key_norm_score(self, w: int) -> float:

@@ -171,3 +171,24 @@ def test_one_way_branch_applied_to_the_bidirectional_policy_is_caught(monkeypatc
 
     monkeypatch.setattr(O, "select_tiers", always_barred)
     _fails(TS.test_route_sets_hand_case_bidirectional)
+
+
+def test_bf16_execution_reading_ignored_is_caught(monkeypatch):
+    """Planted: the bf16 execution reading (R2) silently falls back to the exact values."""
+    real = O.UnitOracle.accessible
+    monkeypatch.setattr(O.UnitOracle, "accessible", lambda self, qexec_bf16=None: real(self, False))
+    _fails(TS.test_quantized_execution_readings_against_sdpa, True)
+
+
+def test_bf16_execution_reading_on_keys_only_is_caught(monkeypatch):
+    """Planted: only the Quantized keys rounded to bf16 in the execution reading, values exact."""
+    real = O.UnitOracle.accessible
+
+    def keys_only(self, qexec_bf16=None):
+        owner, K, V = real(self, qexec_bf16)
+        if qexec_bf16:
+            _, _, V = real(self, False)
+        return owner, K, V
+
+    monkeypatch.setattr(O.UnitOracle, "accessible", keys_only)
+    _fails(TS.test_quantized_execution_readings_against_sdpa, True)

@@ -338,3 +338,65 @@ def test_route_sets_hand_case_one_way():
     states = {w: unit.win[w].state for w in range(7)}
     assert states == {0: O.QUANT, 1: O.FULL, 2: O.FULL, 3: O.EVICTED, 4: O.EVICTED, 5: O.QUANT, 6: O.LOCAL}
     assert not unit.win[0].ledger.dormant
+
+
+def _values_from_record(rec: bytes, h_kv: int, W: int, d: int):
+    """Dequantized K, V [h_kv][W][d] read straight from a canonical INT2 record (codes four to
+    a byte, low bits first; fp16 offsets and scales): x = off + code * scl in float64."""
+    cb = W * d // 4
+    per = 2 * cb + 4 * d + 4 * W
+    ks, vs = [], []
+    for h in range(h_kv):
+        b = np.frombuffer(rec, np.uint8, count=per, offset=h * per)
+        codes = lambda x: np.stack([(x >> (2 * j)) & 3 for j in range(4)], -1).reshape(W, d).astype(np.float64)
+        p = np.frombuffer(rec, "<f2", count=2 * d + 2 * W, offset=h * per + 2 * cb).astype(np.float64)
+        koff, kscl, voff, vscl = p[:d], p[d:2 * d], p[2 * d:2 * d + W], p[2 * d + W:]
+        ks.append(koff[None, :] + codes(b[:cb]) * kscl[None, :])
+        vs.append(voff[:, None] + codes(b[cb:2 * cb]) * vscl[:, None])
+    return np.stack(ks), np.stack(vs)
+
+
+@pytest.mark.parametrize("bf16_values", [False, True])
+def test_quantized_execution_readings_against_sdpa(bf16_values):
+    """Reading R2: inside attention a Quantized window holds its exact dequantized values
+    x = off + code * scl, or, in the model's execution dtype, their bf16 rounding.  The oracle's
+    attention over sinks, recent / Full pages and Quantized windows equals torch SDPA over a cache
+    rebuilt from the stored records (values decoded from the record bytes, rounded by torch's
+    bf16 cast for the second reading)."""
+    wl = WL.TINY.with_(n_decode=9)
+    cfg = cfg_from(wl, budget_frac=0.3)
+    qp, kp, vp = WL.prompt(wl, 0)
+    unit = O.UnitOracle(cfg, wl.prompt_len)
+    unit.prefill(f64(qp[0]), f64(kp[0]), f64(vp[0]), score_init=np.arange(64, dtype=np.float64))
+    for j in range(8):
+        q, k, v = WL.decode_step(wl, 0, j)
+        unit.decode(f64(q[0]), f64(k[0]), f64(v[0]))
+    unit.route()
+    q, k, v = WL.decode_step(wl, 0, 8)
+    out = unit.decode(f64(q[0]), f64(k[0]), f64(v[0]))
+    Ks, Vs, n_quant = [torch.from_numpy(unit.sink_k)], [torch.from_numpy(unit.sink_v)], 0
+    for w in sorted(unit.win):
+        W = unit.win[w]
+        if W.state == O.QUANT:
+            kx, vx = (torch.from_numpy(x) for x in _values_from_record(O.canonical_ledger_bytes(W.ledger),
+                                                                       wl.h_kv, wl.window, wl.d_head))
+            if bf16_values:
+                kx, vx = kx.to(torch.bfloat16).to(torch.float64), vx.to(torch.bfloat16).to(torch.float64)
+            Ks.append(kx)
+            Vs.append(vx)
+            n_quant += 1
+        elif W.state in (O.LOCAL, O.FULL):
+            nt = min(wl.window, unit.n - unit.win_start(w))
+            Ks.append(torch.from_numpy(W.k[:, :nt]))
+            Vs.append(torch.from_numpy(W.v[:, :nt]))
+    assert n_quant > 10
+    K, V = torch.cat(Ks, dim=1), torch.cat(Vs, dim=1)
+    G = wl.h_q // wl.h_kv
+    qd = q[0].to(torch.float64)[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qd, K.repeat_interleave(G, 0), V.repeat_interleave(G, 0))
+    o = unit.attend(out["q_rot"], qexec_bf16=bf16_values)[0]
+    np.testing.assert_allclose(o, ref[:, 0].numpy(), rtol=0, atol=1e-12)
+    if not bf16_values:
+        np.testing.assert_array_equal(o, out["o"])       # the step's own output is the exact reading
+    else:
+        assert np.abs(o - out["o"]).max() > 0            # the two readings differ here
