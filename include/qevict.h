@@ -219,6 +219,13 @@ qevict_status qevict_poll_status(qevict_state* st, uint32_t* status, void* strea
  *   per window w < n_windows_created: int32 state (1 recent, 2 Full,
  *     3 Quantized, 4 Evicted), int32 has_ledger, int32 dormant, int32 start_pos,
  *     fp64 score
+ *   the accessible list the decode kernels read (Algorithm 1, last step: the
+ *     effective cache): n_acc entries of 4 x int32 (kind: 0 sink prefix, 1 bf16
+ *     page, 2 Quantized slot; page or slot id; window, -1 for the sinks; first
+ *     position), in the device's order (pages spread among the slots), which
+ *     includes the recent windows prepared for the next omega positions
+ *   the split offsets: (n_splits + 1) x int32, entries [s_i, s_{i+1}) form split i
+ *   per window w < n_windows_created: int32 page id, int32 slot id (-1 if none)
  *   per window with a ledger, in window order: per KV head: K codes [W][d/4],
  *     V codes [W][d/4] (element (i,c) at byte c/4, bits 2(c%4)), K off [d],
  *     K scl [d], V off [W], V scl [W] (fp16)

@@ -202,6 +202,10 @@ class UnitExport:
     kv: dict                   # window -> (K [h_kv][W][d], V) uint16 bf16 bits
     sink_k: np.ndarray
     sink_v: np.ndarray
+    acc: np.ndarray = None     # [n_acc][4] int32: kind (0 sinks, 1 page, 2 slot), page / slot id, window, start
+    splits: np.ndarray = None  # [n_splits + 1] int32 split offsets into the list
+    win_page: np.ndarray = None   # [n_windows] int32 page id of each window (-1 if none)
+    win_slot: np.ndarray = None   # [n_windows] int32 slot id of each window (-1 if none)
 
 
 COUNTER_NAMES = ("aged", "promoted", "packed", "reactivated", "demoted", "evicted", "n_full", "n_quant")
@@ -324,10 +328,10 @@ class QEvictState:
         written = ctypes.c_size_t()
         _check(self.lib.qevict_export_unit(self.handle, layer, b, buf, self.info.export_bytes,
                                            ctypes.byref(written), _stream(stream)))
-        return parse_export(bytes(buf)[: written.value], self.cfg, tables_only)
+        return parse_export(bytes(buf)[: written.value], self.cfg, self.info.n_splits, tables_only)
 
 
-def parse_export(blob: bytes, cfg: Config, tables_only: bool = False) -> UnitExport:
+def parse_export(blob: bytes, cfg: Config, n_splits: int, tables_only: bool = False) -> UnitExport:
     head = struct.unpack_from("<20i", blob, 0)
     assert head[0] == 0x58564551, "bad export magic"
     n, nw, K_f, K_q, status = head[1:6]
@@ -339,10 +343,18 @@ def parse_export(blob: bytes, cfg: Config, tables_only: bool = False) -> UnitExp
     at += 24 * nw
     state, has_led, dorm, start = (rec["i"][:, k].copy() for k in range(4))
     score = rec["s"].copy()
+    acc = np.frombuffer(blob, dtype="<i4", count=4 * n_acc, offset=at).reshape(n_acc, 4).copy()
+    at += 16 * n_acc
+    splits = np.frombuffer(blob, dtype="<i4", count=n_splits + 1, offset=at).copy()
+    at += 4 * (n_splits + 1)
+    ids = np.frombuffer(blob, dtype="<i4", count=2 * nw, offset=at).reshape(nw, 2)
+    win_page, win_slot = ids[:, 0].copy(), ids[:, 1].copy()
+    at += 8 * nw
+    lists = dict(acc=acc, splits=splits, win_page=win_page, win_slot=win_slot)
     if tables_only:
         empty = np.zeros((0,), dtype=np.uint16)
         return UnitExport(n, nw, K_f, K_q, status, ctr, n_acc, prompt_len, sink_mass, state, has_led, dorm, start,
-                          score, {}, {}, empty, empty)
+                          score, {}, {}, empty, empty, **lists)
     H, W, d, ns = cfg.h_kv, cfg.window, cfg.d_head, cfg.n_sink
     qb = 4 if cfg.flags & QEVICT_F_INT4 else 2
     slot_bytes = H * (2 * W * d * qb // 8 + 4 * d + 4 * W)
@@ -360,4 +372,4 @@ def parse_export(blob: bytes, cfg: Config, tables_only: bool = False) -> UnitExp
             at += pe * 2
     sk = np.frombuffer(blob, dtype="<u2", count=2 * H * ns * d, offset=at).reshape(2, H, ns, d)
     return UnitExport(n, nw, K_f, K_q, status, ctr, n_acc, prompt_len, sink_mass, state, has_led, dorm, start,
-                      score, ledger, kv, sk[0].copy(), sk[1].copy())
+                      score, ledger, kv, sk[0].copy(), sk[1].copy(), **lists)

@@ -179,8 +179,10 @@ qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, La
         at += align256(sz[i]);
     }
     lay->total = at;
-    lay->export_bytes = 80 + (size_t)g.n_windows * 24 + (size_t)g.n_windows * g.slot_bytes +
-                        (size_t)g.n_windows * g.page_elems * 2 + (size_t)g.sink_elems * 2;
+    lay->export_bytes = 80 + (size_t)g.n_windows * 24 + (size_t)g.n_acc_max * sizeof(AccEntry) +
+                        (size_t)(g.n_splits + 1) * 4 + (size_t)g.n_windows * 8 +
+                        (size_t)g.n_windows * g.slot_bytes + (size_t)g.n_windows * g.page_elems * 2 +
+                        (size_t)g.sink_elems * 2;
     lay->max_kf = max_kf;
     lay->max_kq = max_kq;
     return QEVICT_OK;
@@ -527,6 +529,12 @@ qevict_status qevict_export_unit(qevict_state* st, int32_t layer, int32_t b, voi
     HIP_TRY(hipMemcpy(pages.data(), st->bf.pages + u * (size_t)g.n_pages * g.page_elems, pages.size() * 2,
                       hipMemcpyDeviceToHost));
     HIP_TRY(hipMemcpy(sinks.data(), st->bf.sinks + u * (size_t)g.sink_elems, sinks.size() * 2, hipMemcpyDeviceToHost));
+    const int32_t n_acc = hdr.n_acc < 0 ? 0 : (hdr.n_acc > g.n_acc_max ? g.n_acc_max : hdr.n_acc);
+    std::vector<AccEntry> acc(n_acc);
+    std::vector<int32_t> splits(g.n_splits + 1);
+    if (n_acc)
+        HIP_TRY(hipMemcpy(acc.data(), st->bf.acc + u * g.n_acc_max, n_acc * sizeof(AccEntry), hipMemcpyDeviceToHost));
+    HIP_TRY(hipMemcpy(splits.data(), st->bf.splits + u * (g.n_splits + 1), splits.size() * 4, hipMemcpyDeviceToHost));
 
     char* o = (char*)host_buf;
     size_t at = 0;
@@ -549,6 +557,17 @@ qevict_status qevict_export_unit(qevict_state* st, int32_t layer, int32_t b, voi
                           g.n_sink + w * g.W};
         put(rec, sizeof rec);
         put(&score[w], 8);
+    }
+    // the accessible list as the decode kernels read it, its split offsets, and the page /
+    // slot id of every created window (so that each entry can be checked against its window)
+    for (const AccEntry& e : acc) {
+        int32_t rec[4] = {e.kind, e.idx, e.win, e.start};
+        put(rec, sizeof rec);
+    }
+    put(splits.data(), splits.size() * 4);
+    for (int w = 0; w < n_created; ++w) {
+        int32_t ids[2] = {win[w].page, win[w].slot};
+        put(ids, sizeof ids);
     }
     std::vector<uint8_t> canon(g.slot_bytes);
     for (int w = 0; w < n_created; ++w)

@@ -2,9 +2,11 @@
 same seeded inputs and compare after every step and every routing event.
 
 Bars (from the decode hot path's parity contract):
-* routing sets, window states, ledger flags, INT2 codes/params and the bf16
-  contents of Full / recent windows: bit-exact;
-* decode outputs: max_i |o_gpu - o_ref| / ||o_ref||_2 <= 2e-3 per (sequence, head);
+* routing sets, window states, ledger flags, INT2 codes/params, the bf16
+  contents of Full / recent windows and the accessible list (as a set): bit-exact;
+* decode outputs: max_i |o_gpu - o_ref| / ||o_ref||_2 <= 2e-3 per (sequence, head)
+  against the exact reading of the Quantized values (x_hat), and against the
+  bf16(x_hat) reading wherever the two readings lie within 1e-3 of each other;
 * window scores S_bar: |gpu - ref| <= 1e-4 absolute.
 """
 from __future__ import annotations
@@ -33,6 +35,40 @@ def rel_err(o_gpu: np.ndarray, o_ref: np.ndarray) -> float:
     return float((num / den).max())
 
 
+def compare_accessible(ex: B.UnitExport, unit: O.UnitOracle, tag: str):
+    """The accessible list ([QEvict] Algorithm 1, last step) against the oracle's accessible
+    set, exactly: one sink entry, then one entry per recent / Full window (a bf16 page) and per
+    Quantized window (a slot) with its first position; the device orders the entries its own
+    way, so they are compared as a set.  Entries of windows that start at or after n are the
+    recent windows prepared for the next positions (pages, at most omega positions ahead).
+    Each entry's page or slot is the one its window record holds; no page or slot is listed
+    twice; the split offsets cover the list in order."""
+    cfg = unit.cfg
+    acc = ex.acc
+    assert acc.shape == (ex.n_acc, 4), f"{tag}: list shape {acc.shape} vs n_acc {ex.n_acc}"
+    sinks = acc[acc[:, 0] == 0]
+    assert sinks.shape[0] == 1 and tuple(sinks[0][2:]) == (-1, 0), f"{tag}: sink entry {sinks}"
+    rows = [tuple(int(x) for x in r) for r in acc[acc[:, 0] != 0]]
+    got = {(k, w, s) for k, _, w, s in rows}
+    assert len(got) == len(rows), f"{tag}: an accessible window is listed twice"
+    kind_of = {O.LOCAL: 1, O.FULL: 1, O.QUANT: 2}
+    ref = {(kind_of[W.state], w, unit.win_start(w)) for w, W in unit.win.items() if W.state in kind_of}
+    created = {e for e in got if e[2] < unit.n}
+    assert created == ref, (f"{tag}: accessible set differs: missing {sorted(ref - created)[:8]}, "
+                            f"extra {sorted(created - ref)[:8]}")
+    for k, w, s in got - created:
+        assert k == 1 and s < unit.n + cfg.omega and s == unit.win_start(w), f"{tag}: prepared entry {(k, w, s)}"
+    for k, idx, w, s in rows:
+        if s < unit.n:
+            own = ex.win_page[w] if k == 1 else ex.win_slot[w]
+            assert idx == own >= 0, f"{tag}: entry of window {w} names {idx}, its record {own}"
+    for k in (1, 2):
+        ids = [idx for kk, idx, _, _ in rows if kk == k]
+        assert len(set(ids)) == len(ids), f"{tag}: a {'page' if k == 1 else 'slot'} is listed twice"
+    sp = ex.splits
+    assert sp[0] == 0 and sp[-1] == ex.n_acc and np.all(np.diff(sp) >= 0), f"{tag}: split offsets {sp}"
+
+
 def compare_unit(ex: B.UnitExport, unit: O.UnitOracle, tag: str, check_scores=True):
     n_created = ex.n_windows
     assert ex.n == unit.n, f"{tag}: n {ex.n} != {unit.n}"
@@ -53,6 +89,7 @@ def compare_unit(ex: B.UnitExport, unit: O.UnitOracle, tag: str, check_scores=Tr
             W = unit.win[w]
             np.testing.assert_array_equal(k, bf16_bits(W.k), err_msg=f"{tag}: window {w} K page")
             np.testing.assert_array_equal(v, bf16_bits(W.v), err_msg=f"{tag}: window {w} V page")
+    compare_accessible(ex, unit, tag)
     ns = min(unit.cfg.n_sink, unit.n)
     np.testing.assert_array_equal(ex.sink_k[:, :ns], bf16_bits(unit.sink_k[:, :ns]))
     np.testing.assert_array_equal(ex.sink_v[:, :ns], bf16_bits(unit.sink_v[:, :ns]))
@@ -92,6 +129,8 @@ class Lockstep:
         self.units = [O.UnitOracle(ocfg, self.lens[b], rope_cs=cs) for b in self.sample]
         self.score_init = score_init
         self.max_o_err = 0.0
+        self.max_o_err_bf16 = 0.0     # against the bf16(x_hat) reading, where it is checked
+        self.max_reading_gap = 0.0    # between the two readings of the oracle
         self.max_s_err = 0.0
         self.events = 0
         self.dev = device
@@ -130,6 +169,17 @@ class Lockstep:
             err = rel_err(o_gpu[b], ref["o"])
             self.max_o_err = max(self.max_o_err, err)
             assert err <= O_TOL, f"step {j} b={b}: output error {err}"
+            # reading R2: the bf16(x_hat) execution reading.  Where the two readings lie within
+            # half the bar of each other the output must be within the bar of both; where they
+            # are further apart (long contexts of Quantized outlier keys) no output can be, and
+            # the gap is recorded instead.
+            o16 = unit.attend(ref["q_rot"], qexec_bf16=True)[0]
+            gap = rel_err(o16, ref["o"])
+            err16 = rel_err(o_gpu[b], o16)
+            self.max_reading_gap = max(self.max_reading_gap, gap)
+            if gap <= O_TOL / 2:
+                self.max_o_err_bf16 = max(self.max_o_err_bf16, err16)
+                assert err16 <= O_TOL, f"step {j} b={b}: output error {err16} against the bf16 reading"
         routed = (j + 1) % self.wl.omega == 0
         if routed:
             self.st.route(0)

@@ -5,10 +5,10 @@ the launch configuration the benchmark times: batch 1, 8 KV heads, same split co
   synthetic seeded vector passed to both sides (the oracle cannot afford the
   ~9 TFLOP fp64 prompt column sums of a 32K prompt), so prefill routing, the 852
   INT2 packs, 8 decode steps and one routing event are all compared exactly.
-* Prompt column sums at 32K: the row-sum invariant (every causal softmax row
-  sums to one, so sum_w S_bar_0(w) + sink mass = prompt length), sampled row
-  log-sum-exps, and the scores of the last two windows, whose column sums the
-  oracle can compute from 64 rows.
+* Prompt column sums at 32K: every row log-sum-exp and column sum of two query
+  heads against fp64, every window score against the GPU's own column sums, and
+  the row-sum invariant (every causal softmax row sums to one, so
+  sum_w S_bar_0(w) + sink mass = prompt length).
 """
 import math
 
@@ -38,47 +38,65 @@ def test_llama8b_32k_decode_and_route_lockstep():
     assert ex.counters["packed"] == ls.units[0].events[0]["packed"] > 800
     for j in range(8):
         ls.step(j)
-    print(f"32K: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}", flush=True)
+    print(f"32K: max o err {ls.max_o_err:.2e} (bf16 reading {ls.max_o_err_bf16:.2e}, gap {ls.max_reading_gap:.2e}), max score err {ls.max_s_err:.2e}", flush=True)
+
+
+def _blocked_column_sums(Q: np.ndarray, K: np.ndarray, lse: np.ndarray, rows: int = 512) -> np.ndarray:
+    """Column sums sum_{u >= t} P[u, t] of one head's causal softmax P = exp(Q K^T / sqrt(d) - lse_u)
+    (fp64), taken over blocks of query rows so that a 32K prompt fits in memory."""
+    S, d = Q.shape
+    col = np.zeros(S)
+    for u0 in range(0, S, rows):
+        u1 = min(S, u0 + rows)
+        P = np.exp(Q[u0:u1] @ K[:u1].T / math.sqrt(d) - lse[u0:u1, None])
+        P[:, u0:][np.triu_indices(u1 - u0, 1)] = 0.0          # key t > query u is masked
+        col[:u1] += P.sum(axis=0)
+    return col
 
 
 def test_llama8b_32k_prefill_column_sums():
+    """Prompt column sums at the full 32K size ([QEvict] §4.2: prompt attention initialises the
+    window scores).  For two query heads of different GQA groups every row log-sum-exp and every
+    one of the 32,768 column sums is compared with fp64 (the oracle's row log-sum-exp, a
+    row-blocked column sum).  Bar: a window's score is the head average of its columns' sums, so
+    it stays within the 1e-4 score bar when, for each head, the absolute column errors summed
+    over each window (and over the sink prefix) stay below 1e-4.  Every exported window score
+    equals the head average of the GPU's own column sums, and every causal row sums to one
+    (fp32 probabilities: each row within 2^-20, so the total within S * 2^-20)."""
     print("case: 32K prefill column sums", flush=True)
-    S, G = WL32.prompt_len, WL32.h_q // WL32.h_kv
+    S, G, W, ns = WL32.prompt_len, WL32.h_q // WL32.h_kv, WL32.window, WL32.n_sink
     st = B.QEvictState(B.make_config(WL32), [S])
     qp, kp, vp = WL.prompt(WL32, 0, device="cuda")
     st.prefill_init(0, qp, kp, vp)
     torch.cuda.synchronize()
-    ex = st.export_unit(0, 0)
+    ex = st.export_unit(0, 0, tables_only=True)
     lse_gpu, col_gpu = st.workspace_views()
     lse_gpu = lse_gpu.cpu().numpy()[0]
     col_gpu = col_gpu.cpu().numpy()[0]
-    Q = qp[0].cpu().to(torch.float64).numpy()
-    K = kp[0].cpu().to(torch.float64).numpy()
+    heads = (5, 30)
+    Q = {h: qp[0, h].cpu().to(torch.float64).numpy() for h in heads}
+    K = {g: kp[0, g].cpu().to(torch.float64).numpy() for g in {h // G for h in heads}}
     del qp, kp, vp
-    # every causal row sums to one
     total = ex.score[: ex.n_windows].sum() + ex.sink_mass
     print(f"row-sum invariant: {total} vs {S}", flush=True)
-    assert abs(total - S) < 1e-5 * S
-    # sampled row LSEs (log2 units)
-    for h, u in [(0, 0), (5, 4095), (17, 20000), (31, S - 1)]:
-        ref = O.row_lse(Q[h][u], K[h // G][: u + 1]) / math.log(2)
-        assert abs(lse_gpu[h, u] - ref) < 1e-4, (h, u)
-    # column sums of the last 64 keys, all heads -> scores of the last two windows
-    t0 = S - 64
-    lse_rows = np.array([[O.row_lse(Q[h][u], K[h // G][: u + 1]) for u in range(t0, S)] for h in range(WL32.h_q)])
-    col_ref = np.zeros((WL32.h_q, 64))
-    for h in range(WL32.h_q):
-        logits = Q[h][t0:] @ K[h // G][t0:].T / math.sqrt(WL32.d_head)      # [u][t]
-        P = np.exp(logits - lse_rows[h][:, None])
-        P[np.triu_indices(64, k=1)] = 0.0                                     # t > u masked
-        col_ref[h] = P.sum(axis=0)
-    err = np.abs(col_gpu[:, t0:] - col_ref).max()
-    print(f"last-64 column-sum err {err:.2e}", flush=True)
-    assert err < 1e-5
-    for w in (ex.n_windows - 2, ex.n_windows - 1):
-        a = WL32.n_sink + w * WL32.window
-        ref = col_ref[:, a - t0: a - t0 + WL32.window].sum() / WL32.h_q
-        assert abs(ex.score[w] - ref) < 1e-4
+    assert abs(total - S) <= S * 2.0 ** -20
+    # the window reduction: each exported score is the head average of the GPU's column sums
+    nw = ex.n_windows
+    win_cols = np.add.reduceat(col_gpu[:, ns:], np.arange(0, S - ns, W), axis=1)[:, :nw]
+    np.testing.assert_allclose(ex.score[:nw], win_cols.mean(axis=0), rtol=1e-12, atol=1e-9)
+    assert abs(ex.sink_mass - col_gpu[:, :ns].sum() / WL32.h_q) <= 1e-9
+    for h in heads:
+        Kg = K[h // G]
+        lse = np.array([O.row_lse(Q[h][u], Kg[: u + 1]) for u in range(S)])
+        lse_err = np.abs(lse_gpu[h] - lse / math.log(2)).max()
+        ref = _blocked_column_sums(Q[h], Kg, lse)
+        d = np.abs(col_gpu[h] - ref)
+        per_win = np.add.reduceat(d[ns:], np.arange(0, S - ns, W))
+        print(f"head {h}: row lse err {lse_err:.2e} (log2), max column err {d.max():.2e}, max per-window "
+              f"sum {per_win.max():.2e}, sink-prefix sum {d[:ns].sum():.2e}, largest column {ref.max():.1f}",
+              flush=True)
+        assert lse_err < 1e-4
+        assert per_win.max() <= 1e-4 and d[:ns].sum() <= 1e-4
 
 
 def test_llama8b_32k_int4_decode_and_route_lockstep():
@@ -92,7 +110,7 @@ def test_llama8b_32k_int4_decode_and_route_lockstep():
     assert ex.counters["packed"] == ls.units[0].events[0]["packed"] > 400
     for j in range(8):
         ls.step(j)
-    print(f"32K int4: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}", flush=True)
+    print(f"32K int4: max o err {ls.max_o_err:.2e} (bf16 reading {ls.max_o_err_bf16:.2e}, gap {ls.max_reading_gap:.2e}), max score err {ls.max_s_err:.2e}", flush=True)
 
 
 def test_llama8b_32k_rope_decode_and_route_lockstep():
@@ -107,7 +125,7 @@ def test_llama8b_32k_rope_decode_and_route_lockstep():
     assert ex.counters["packed"] == ls.units[0].events[0]["packed"] > 800
     for j in range(8):
         ls.step(j)
-    print(f"32K rope: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}", flush=True)
+    print(f"32K rope: max o err {ls.max_o_err:.2e} (bf16 reading {ls.max_o_err_bf16:.2e}, gap {ls.max_reading_gap:.2e}), max score err {ls.max_s_err:.2e}", flush=True)
 
 
 def _init_scores(wl):
@@ -125,7 +143,7 @@ def test_batched_16k_b16_sampled_lockstep():
     ls = Lockstep(wl, score_init=_init_scores(wl), sample=[0, 7, 15])
     assert ls.st.info.n_splits == B.plan(B.make_config(WL.BATCHED_16K), wl.prompt_lens()).n_splits
     ls.run(8)
-    print(f"batched: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}", flush=True)
+    print(f"batched: max o err {ls.max_o_err:.2e} (bf16 reading {ls.max_o_err_bf16:.2e}, gap {ls.max_reading_gap:.2e}), max score err {ls.max_s_err:.2e}", flush=True)
 
 
 def test_churn_4k_b64_sampled_lockstep_across_a_topic_switch():
@@ -136,7 +154,7 @@ def test_churn_4k_b64_sampled_lockstep_across_a_topic_switch():
     print("case: churn 4K b64", flush=True)
     ls = Lockstep(wl, score_init=_init_scores(wl), sample=[0, 63]).run(264, check_every=8)
     moved = sum(e["promoted"] + e["demoted"] for u in ls.units for e in u.events)
-    print(f"churn: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}, "
+    print(f"churn: max o err {ls.max_o_err:.2e} (bf16 reading {ls.max_o_err_bf16:.2e}, gap {ls.max_reading_gap:.2e}), max score err {ls.max_s_err:.2e}, events {ls.events}, "
           f"moves {moved}", flush=True)
     assert ls.events == 33 and moved > 0
 
@@ -149,4 +167,4 @@ def test_llama70b_128k_b4_sampled_lockstep():
     ls = Lockstep(wl, score_init=_init_scores(wl), sample=[0, 3])
     assert ls.st.info.n_splits == B.plan(B.make_config(WL.LLAMA70B_128K), wl.prompt_lens()).n_splits
     ls.run(8)
-    print(f"70B: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}", flush=True)
+    print(f"70B: max o err {ls.max_o_err:.2e} (bf16 reading {ls.max_o_err_bf16:.2e}, gap {ls.max_reading_gap:.2e}), max score err {ls.max_s_err:.2e}", flush=True)

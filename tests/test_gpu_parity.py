@@ -27,7 +27,7 @@ def test_tiny_config_full_lockstep():
     """The tiny single-layer workload: 512-token prompt + 64 decode steps, 8 events."""
     _print("case: tiny full lockstep")
     ls = Lockstep(WL.TINY).run(64)
-    _print(f"tiny: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}")
+    _print(f"tiny: max o err {ls.max_o_err:.2e} (bf16 reading {ls.max_o_err_bf16:.2e}, gap {ls.max_reading_gap:.2e}), max score err {ls.max_s_err:.2e}, events {ls.events}")
 
 
 @pytest.mark.parametrize("rho,q", [(0.25, 0.70), (0.15, 0.70), (1.0, 0.0)], ids=["evict", "no-full-tier", "dense"])
@@ -35,7 +35,7 @@ def test_tiny_budget_variants(rho, q):
     _print(f"case: tiny rho={rho} q={q}")
     wl = WL.TINY.with_(budget_frac=rho, quant_frac=q)
     ls = Lockstep(wl).run(40)
-    _print(f"rho={rho}: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}")
+    _print(f"rho={rho}: max o err {ls.max_o_err:.2e} (bf16 reading {ls.max_o_err_bf16:.2e}, gap {ls.max_reading_gap:.2e}), max score err {ls.max_s_err:.2e}")
 
 
 def test_drift_with_promotions_and_splits():
@@ -57,7 +57,7 @@ def test_batched_ragged_prompts_gqa8_d128():
     wl = WL.Workload("ragged", 1, 3, 16, 2, 128, 640, 24, 32, 4, 64, 8, 0.30, 0.70, prompt_len_min=300,
                      n_outlier=2, n_topics=2, topic_period=8)
     ls = Lockstep(wl).run(24)
-    _print(f"ragged: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}")
+    _print(f"ragged: max o err {ls.max_o_err:.2e} (bf16 reading {ls.max_o_err_bf16:.2e}, gap {ls.max_reading_gap:.2e}), max score err {ls.max_s_err:.2e}")
 
 
 def test_window64_gqa8_multichunk():
@@ -68,7 +68,7 @@ def test_window64_gqa8_multichunk():
     wl = WL.Workload("w64", 1, 2, 16, 2, 128, 1200, 24, 64, 4, 128, 8, 0.30, 0.70, prompt_len_min=700,
                      n_outlier=2, n_topics=2, topic_period=8)
     ls = Lockstep(wl).run(24)
-    _print(f"w64: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}")
+    _print(f"w64: max o err {ls.max_o_err:.2e} (bf16 reading {ls.max_o_err_bf16:.2e}, gap {ls.max_reading_gap:.2e}), max score err {ls.max_s_err:.2e}, events {ls.events}")
 
 
 def test_window16_d128_promotions():
@@ -82,7 +82,7 @@ def test_window16_d128_promotions():
     si = torch.zeros((wl.batch, n_win), dtype=torch.float64)
     ls = Lockstep(wl, score_init=si).run(48)
     assert sum(e["promoted"] for u in ls.units for e in u.events) > 0
-    _print(f"w16: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}")
+    _print(f"w16: max o err {ls.max_o_err:.2e} (bf16 reading {ls.max_o_err_bf16:.2e}, gap {ls.max_reading_gap:.2e}), max score err {ls.max_s_err:.2e}, events {ls.events}")
 
 
 def test_one_way_and_route_step_scoring_flags():
@@ -101,7 +101,7 @@ def test_mha_one_query_head_per_kv_head():
                      n_outlier=2, n_topics=2, topic_period=8)
     ls = Lockstep(wl).run(32)
     assert any(u.win[w].ledger is not None for u in ls.units for w in u.win)
-    _print(f"mha: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}")
+    _print(f"mha: max o err {ls.max_o_err:.2e} (bf16 reading {ls.max_o_err_bf16:.2e}, gap {ls.max_reading_gap:.2e}), max score err {ls.max_s_err:.2e}, events {ls.events}")
 
 
 def test_short_prompt_edge_cases():
@@ -213,7 +213,7 @@ def test_alternative_rankers_lockstep(flag):
     ls = Lockstep(wl, score_init=si, flags=f).run(96)
     if flag != "keynorm":     # (key-norm keys never change, so nothing is promoted)
         assert sum(e["promoted"] for e in ls.units[0].events) > 0
-    _print(f"{flag} tiny: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}")
+    _print(f"{flag} tiny: max o err {ls.max_o_err:.2e} (bf16 reading {ls.max_o_err_bf16:.2e}, gap {ls.max_reading_gap:.2e}), max score err {ls.max_s_err:.2e}, events {ls.events}")
     wl2 = WL.Workload("rank", 1, 2, 16, 2, 128, 700, 24, 32, 4, 64, 8, 0.30, 0.70, prompt_len_min=400,
                       n_outlier=2, n_topics=2, topic_period=8)
     ls2 = Lockstep(wl2, flags=f).run(24)
@@ -251,7 +251,7 @@ def test_int4_tier_lockstep(case):
     assert led and max(int(l.k_codes.max()) for l in led) > 3          # codes beyond the INT2 range
     if flat:
         assert sum(e["promoted"] for u in ls.units for e in u.events) > 0
-    _print(f"int4 {case}: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}")
+    _print(f"int4 {case}: max o err {ls.max_o_err:.2e} (bf16 reading {ls.max_o_err_bf16:.2e}, gap {ls.max_reading_gap:.2e}), max score err {ls.max_s_err:.2e}, events {ls.events}")
 
 
 ROPE_CASES = {
@@ -288,7 +288,7 @@ def test_rope_faithful_quantized_tier_lockstep(case):
     assert any(u.win[w].ledger is not None for u in ls.units for w in u.win)
     if flat:
         assert sum(e["promoted"] for u in ls.units for e in u.events) > 0
-    _print(f"rope {case}: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}")
+    _print(f"rope {case}: max o err {ls.max_o_err:.2e} (bf16 reading {ls.max_o_err_bf16:.2e}, gap {ls.max_reading_gap:.2e}), max score err {ls.max_s_err:.2e}, events {ls.events}")
 
 
 @pytest.mark.parametrize("promote", [True, False], ids=["two-way", "one-way"])
@@ -343,4 +343,4 @@ def test_combined_flags_int4_rope_pnorm_one_way():
     unit = ls.units[0]
     assert sum(e["promoted"] for e in unit.events) == 0
     assert any(W.ledger is not None and W.ledger.bits == 4 for W in unit.win.values())
-    _print(f"combined: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}")
+    _print(f"combined: max o err {ls.max_o_err:.2e} (bf16 reading {ls.max_o_err_bf16:.2e}, gap {ls.max_reading_gap:.2e}), max score err {ls.max_s_err:.2e}, events {ls.events}")
