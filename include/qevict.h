@@ -164,6 +164,25 @@ qevict_status qevict_prefill_init(qevict_state* st, int32_t layer,
                                   void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): qevict_prefill_init with the workspace
+ * taken from a static device array inside the library, QEVICT_NOALLOC_WS_BYTES (32 MiB)
+ * per GPU, held by each GPU the library runs on until the process ends.  Same arguments,
+ * results and ordering as qevict_prefill_init otherwise; allocates nothing.
+ *   Errors: QEVICT_E_CAPACITY (nothing enqueued) when plan.prefill_ws_bytes exceeds
+ *   QEVICT_NOALLOC_WS_BYTES (e.g. a 32K prompt at batch 1 with 32 query heads needs 12 MiB
+ *   and fits; RoPE mode at that size does not); QEVICT_E_STATE unless the device current at
+ *   qevict_create is current; then the errors of qevict_prefill_init.
+ *   Every call on one GPU shares the array: calls that overlap on one GPU (unordered streams,
+ *   threads) race; calls ordered on one stream do not.  Nothing in the array needs to start
+ *   at zero (each call writes every word it reads), so it is never cleared.
+ */
+#define QEVICT_NOALLOC_WS_BYTES ((size_t)32 << 20)
+qevict_status qevict_prefill_init_noalloc(qevict_state* st, int32_t layer, const void* q_prompt,
+                                          const void* k_prompt, const void* v_prompt,
+                                          const double* score_init, void* stream);
+
+/*
  * One decode step of one layer (§4.1 accessible-set attention, §4.2 Eq. 1).
  *   q [B][h_q][d], k_new / v_new [B][h_kv][d] bf16: the new token's query, key, value
  *     (query and key before RoPE with QEVICT_F_ROPE; the library turns them to position n).

@@ -33,7 +33,9 @@ EXPORTED_SYMBOLS = (
     "qevict_decode_attn", "qevict_route", "qevict_pack_int2", "qevict_promote", "qevict_poll_status",
     "qevict_export_unit", "qevict_decode_kernel_name", "qevict_last_error", "qevict_time_next_decode",
     "qevict_step_bytes", "qevict_stream_read", "qevict_set_rope", "qevict_step_mass",
+    "qevict_prefill_init_noalloc",
 )
+NOALLOC_WS_BYTES = 32 << 20    # the static prefill workspace of qevict_prefill_init_noalloc
 
 
 class QEvictError(RuntimeError):
@@ -83,6 +85,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qevict_destroy.argtypes = [P]
     lib.qevict_destroy.restype = None
     lib.qevict_prefill_init.argtypes = [P, I, P, P, P, P, P, Z, P]
+    lib.qevict_prefill_init_noalloc.argtypes = [P, I, P, P, P, P, P]
     lib.qevict_decode_attn.argtypes = [P, I, P, P, P, P, P]
     lib.qevict_route.argtypes = [P, I, P]
     lib.qevict_pack_int2.argtypes = [P, I, P, I, P]
@@ -259,6 +262,19 @@ class QEvictState:
 
     # -- the C ABI -----------------------------------------------------------------------
     def prefill_init(self, layer: int, q, k, v, score_init=None, stream=None):
+        c = self._expect_prompt(q, k, v, score_init)
+        ws = None if (score_init is not None and not c.flags & QEVICT_F_ROPE) else self.ensure_workspace()
+        _check(self.lib.qevict_prefill_init(self.handle, layer, _ptr(q), _ptr(k), _ptr(v), _ptr(score_init),
+                                            _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+
+    def prefill_init_noalloc(self, layer: int, q, k, v, score_init=None, stream=None):
+        """``prefill_init`` through the allocation-free entry point (the library's static
+        workspace; no workspace tensor is made)."""
+        self._expect_prompt(q, k, v, score_init)
+        _check(self.lib.qevict_prefill_init_noalloc(self.handle, layer, _ptr(q), _ptr(k), _ptr(v),
+                                                    _ptr(score_init), _stream(stream)))
+
+    def _expect_prompt(self, q, k, v, score_init):
         c = self.cfg
         _expect(k, (c.batch, c.h_kv, c.max_prompt, c.d_head), "bfloat16", self.device, "k_prompt")
         _expect(v, (c.batch, c.h_kv, c.max_prompt, c.d_head), "bfloat16", self.device, "v_prompt")
@@ -266,9 +282,7 @@ class QEvictState:
             _expect(q, (c.batch, c.h_q, c.max_prompt, c.d_head), "bfloat16", self.device, "q_prompt")
         else:
             _expect(score_init, (c.batch, self.info.n_windows), "float64", self.device, "score_init")
-        ws = None if (score_init is not None and not c.flags & QEVICT_F_ROPE) else self.ensure_workspace()
-        _check(self.lib.qevict_prefill_init(self.handle, layer, _ptr(q), _ptr(k), _ptr(v), _ptr(score_init),
-                                            _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+        return c
 
     def step_mass(self, layer: int, b: int, out=None, stream=None):
         """Per-head mass of the last decode step: ``[h_q][n_windows + 1]`` float64 on the

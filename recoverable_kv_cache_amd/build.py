@@ -14,7 +14,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libqevict.so")
-SOURCES = ["qevict_host.cpp", "qevict_state.hip", "qevict_decode.hip", "qevict_prefill.hip", "qevict_calib.hip"]
+SOURCES = ["qevict_host.cpp", "qevict_state.hip", "qevict_decode.hip", "qevict_prefill.hip", "qevict_calib.hip",
+           "qevict_noalloc.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -228,7 +228,14 @@ struct qevict_state {
     std::vector<uint8_t> step_fresh;                      // per layer: a decode step and no routing since
     bool rope_set = false;                                // RoPE mode: table copied in
     hipEvent_t ev_before = nullptr, ev_after = nullptr;   // one-shot timing of the split kernel
+    int device = -1;                                      // the device current at qevict_create
 };
+
+namespace qv {
+qevict_status set_error(qevict_status s, const char* msg) { return fail(s, "%s", msg); }
+size_t state_prefill_ws_bytes(const qevict_state* st) { return prefill_ws_bytes(st->lay.g); }
+int state_device(const qevict_state* st) { return st->device; }
+}  // namespace qv
 
 extern "C" {
 
@@ -282,7 +289,10 @@ qevict_status qevict_create(const qevict_config* cfg, const int32_t* prompt_lens
     if ((uintptr_t)arena % 256) return fail(QEVICT_E_INVALID, "arena must be 256-byte aligned");
     if (arena_bytes < lay.total)
         return fail(QEVICT_E_CAPACITY, "arena of %zu bytes < %zu required", arena_bytes, lay.total);
+    int device = -1;
+    HIP_TRY(hipGetDevice(&device));
     qevict_state* st = new qevict_state();
+    st->device = device;
     st->cfg = *cfg;
     st->lay = lay;
     st->arena = (char*)arena;

@@ -227,6 +227,10 @@ hipError_t launch_prefill_setup(const Geo& g, const Bufs& bf, int layer, const u
 hipError_t launch_prefill_scores(const Geo& g, const Bufs& bf, int layer, const uint16_t* qp, const uint16_t* kp,
                                  const double* score_init, void* ws, hipStream_t s);
 size_t prefill_ws_bytes(const Geo& g);
+// accessors of the host-side state for entry points in other sources
+qevict_status set_error(qevict_status s, const char* msg);   // message for qevict_last_error; returns s
+size_t state_prefill_ws_bytes(const qevict_state* st);
+int state_device(const qevict_state* st);
 // measurement aid: one streaming read of [buf, buf + bytes), bytes a multiple of 1024;
 // sink receives one XOR word per workgroup (STREAM_READ_WGS of them)
 constexpr int STREAM_READ_WGS = 1024;
