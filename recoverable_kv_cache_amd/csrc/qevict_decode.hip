@@ -157,6 +157,7 @@ __device__ __forceinline__ void wave_lds_fence() {
 
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }   // by value
 
+
 template <int N>
 __device__ __forceinline__ void ldw(uint32_t* d, const void* s) {
     if constexpr (N % 4 == 0) {
@@ -215,6 +216,7 @@ struct DecShape {
     static constexpr int RW = QW > FW ? QW : FW;
     static constexpr int QSTR = D + 8;               // bf16 per LDS operand row (padded)
     static_assert(KCW >= 1 && VCW >= 1 && KPW >= 1, "shape");
+    static constexpr int KCB = 2 * TPC * D * BITS;   // K (or V) code bytes of one chunk of one item
 };
 
 // One unit of wave work.  Quantized job: chunk c of up to NSLOT Quantized windows
@@ -237,9 +239,11 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     constexpr int NV = S::NV, QSTR = S::QSTR;
     __shared__ uint2 lut[256];            // code byte -> its 4 (INT2) or 2 (INT4, in .x) codes as bf16 integers
     __shared__ uint2 lutk[ROPE ? 256 : 1];  // RoPE mode, key side: the same codes as fp16 integers
-    // per wave: rows 0-15 the INT2 query operand of the current job, rows 16-31 the
-    // bf16 query operand (every live column holds its head's query, exact bf16), row 32 zeros
-    __shared__ __attribute__((aligned(16))) uint16_t qs[DW][33][QSTR];
+    // per wave: the Quantized query operand of the current job (16 rows); shared by the waves
+    // (one KV head): rows 0-15 the bf16 query operand (every live column holds its head's
+    // query, exact bf16), row 16 zeros
+    __shared__ __attribute__((aligned(16))) uint16_t qs[DW][16][QSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t qsh[17][QSTR];
     __shared__ float kb[DW][16];                                         // per wave: key-offset bias per column
     __shared__ float s_m[DW][G], s_l[DW][G], s_vb[DW][G];
     __shared__ float s_acc[DW][G][D];
@@ -334,8 +338,10 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
                     lutk[x] = make_uint2(hv(x & 15) | (hv(x >> 4) << 16), 0u);
             }
         }
-        stw<CQ / 2>(&qs[wave][16 + n][CQ * qg], w);
-        if (lane < D / 8) reinterpret_cast<uint4*>(&qs[wave][32][0])[lane] = make_uint4(0u, 0u, 0u, 0u);
+        if (wave == 0) {
+            stw<CQ / 2>(&qsh[n][CQ * qg], w);
+            if (lane < D / 8) reinterpret_cast<uint4*>(&qsh[16][0])[lane] = make_uint4(0u, 0u, 0u, 0u);
+        }
 #pragma unroll
         for (int x = 0; x < CPL / 2; ++x) {
             qf[2 * x] = bf16lo(w2[x]) * scale;
@@ -348,7 +354,6 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         }
     }
     if (split == 0 && hk == 0 && threadIdx.x == 0) bf.hdr[u].pos = n_old;   // for the finish kernel
-    __syncthreads();                 // the code table (the only state the waves share)
     const int e_total = __builtin_amdgcn_readlane(me.kind, 0);   // header: entries of the split, first entry
     const int e_begin = __builtin_amdgcn_readlane(me.idx, 0);
 
@@ -447,7 +452,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     constexpr int KRB = CQ * BITS / 8, VTB = BITS / 2;
     const uint32_t cbytes = (uint32_t)(W * D * BITS / 8);
     const uint32_t kc_lane = (uint32_t)((n * 4 + qg) * TPC * KRB);                    // K codes: token row n, group qg
-    const uint32_t vc_lane = cbytes + (uint32_t)((n * 4 + qg) * NCH * MB * TPC * VTB); // V codes: channel row n
+    const uint32_t vc_lane = cbytes + (uint32_t)((n * 4 + qg) * MB * TPC * VTB);       // V codes: channel row n
     const uint32_t vp_lane = 2 * cbytes + (uint32_t)(4 * D + qg * NT * 8);            // V offsets (V scales + 2W)
     // the lane's product channels: CPL of them from position CPL*pcb of the key-side channel
     // order (in RoPE mode all in one half, pairing as in lay_kc_pos)
@@ -462,10 +467,10 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         const uint8_t* ca = slots + oa + (uint32_t)(j.c * 16 * 4 * TPC * KRB);   // chunk c of item a
         const uint8_t* cb = slots + ob + (uint32_t)(j.c * 16 * 4 * TPC * KRB);
         ldw<S::KCW>(R.w, ca + kc_lane);
-        ldw<S::VCW>(R.w + S::O_VC, slots + oa + (uint32_t)(j.c * MB * TPC * VTB) + vc_lane);
+        ldw<S::VCW>(R.w + S::O_VC, slots + oa + (uint32_t)(j.c * S::KCB) + vc_lane);
         if constexpr (NSLOT == 2) {
             ldw<S::KCW>(R.w + S::KCW, cb + kc_lane);
-            ldw<S::VCW>(R.w + S::O_VC + S::VCW, slots + ob + (uint32_t)(j.c * MB * TPC * VTB) + vc_lane);
+            ldw<S::VCW>(R.w + S::O_VC + S::VCW, slots + ob + (uint32_t)(j.c * S::KCB) + vc_lane);
         }
         // the lane's own item (V parameters) and the item of its products (K parameters)
         const uint32_t oo = (slot == 0 ? oa : ob) + vp_lane + (uint32_t)(TPC * j.c * 8);
@@ -479,15 +484,21 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             ldw<2 * CPL>(R.w + S::O_CS, bf.rope + (int64_t)A * (D / 2) + pch0 % (D / 2));
         }
     };
-    auto load_f = [&](const Job& j, Raw& R) __attribute__((always_inline)) {
+    // a bf16 job's K and V bytes of this lane (CQ * 2 bytes each)
+    auto f_src = [&](const Job& j, const uint8_t*& kl, const uint8_t*& vl) __attribute__((always_inline)) {
         const int tpc = lay_tpc(j.Wn), nt16 = j.Wn / 16;
         const uint8_t* kbase = reinterpret_cast<const uint8_t*>(
             (j.kind == EK_SINK ? sinks : pages + (int64_t)j.idx * g.page_elems) + (int64_t)(2 * hk) * j.Wn * D);
         const uint8_t* vbase = kbase + (int64_t)j.Wn * D * 2;
         const int t0 = j.t / tpc, t1 = j.t % tpc;   // chunk, tile within it
-        ldw<CQ / 2>(R.w, kbase + (uint32_t)(t0 * 16 * 4 * tpc * CQ * 2 + t1 * CQ * 2) +
-                             (uint32_t)(((n * 4 + qg) * tpc) * CQ * 2));
-        ldw<2 * MB>(R.w + CQ / 2, vbase + (uint32_t)(j.t * MB * 8) + (uint32_t)((n * 4 + qg) * nt16 * MB * 8));
+        kl = kbase + (uint32_t)(t0 * 16 * 4 * tpc * CQ * 2 + t1 * CQ * 2) + (uint32_t)(((n * 4 + qg) * tpc) * CQ * 2);
+        vl = vbase + (uint32_t)(j.t * MB * 8) + (uint32_t)((n * 4 + qg) * nt16 * MB * 8);
+    };
+    auto load_f = [&](const Job& j, Raw& R) __attribute__((always_inline)) {
+        const uint8_t *kl, *vl;
+        f_src(j, kl, vl);
+        ldw<CQ / 2>(R.w, kl);
+        ldw<2 * MB>(R.w + CQ / 2, vl);
     };
 
     // online softmax over the lane's NVV scores.  The reference max is shared by every
@@ -576,8 +587,8 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         }
     };
 
-    const uint16_t* qrow_a = &qs[wave][(NSLOT == 2 && slot) ? 32 : n][CQ * qg];   // slot 0 columns only
-    const uint16_t* qrow_b = &qs[wave][(NSLOT == 2 && !slot) ? 32 : n][CQ * qg];  // slot 1 columns only
+    const uint16_t* qrow_a = (NSLOT == 2 && slot) ? &qsh[16][CQ * qg] : &qs[wave][n][CQ * qg];   // slot 0 columns only
+    const uint16_t* qrow_b = (NSLOT == 2 && !slot) ? &qsh[16][CQ * qg] : &qs[wave][n][CQ * qg];  // slot 1 columns only
     // RoPE mode, key side of a Quantized job (see process_q): the 8 codes of positions
     // 8ks .. 8ks + 7 of the lane's row of tile tc, as 4 pairs of fp16 integers
     auto codes8 = [&](const uint32_t* w, int tc, int ks, uint32_t* c) __attribute__((always_inline)) {
@@ -634,7 +645,14 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         ls = u4_t{l2[0], l2[1], l2[2], l2[3]};
     };
 
-    auto process_q = [&](const Job& j, const Raw& R) __attribute__((always_inline)) {
+    // A Quantized job in two parts: products_q writes the job's query operand to LDS and reads
+    // the lane's columns back, scores_q does the rest.
+    struct QOp {
+        u4_t a[DecShape<D, G, TPC, BITS, ROPE>::KS], b[DecShape<D, G, TPC, BITS, ROPE>::KS];
+        float c0;
+    };
+    auto products_q = [&](const Job& j, const Raw& R, QOp& op) __attribute__((always_inline)) {
+        (void)j;
         // (1) q * sclK for every (item, head, channel) once, split into bf16 high + low
         //     rows of the wave's operand block; key-offset bias sum_c q_c offK_c per row.
         //     RoPE mode: instead the query turned back by the chunk's first position A,
@@ -643,7 +661,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         if constexpr (ROPE) {
             constexpr int H2 = D / 2;
             const bool first = pch0 < H2;
-            const uint16_t* qrow = &qs[wave][16 + phead][0];
+            const uint16_t* qrow = &qsh[phead][0];
             uint32_t hw[CPL / 2], lw2[CPL / 2];
 #pragma unroll
             for (int x = 0; x < CPL / 2; ++x) {
@@ -693,13 +711,17 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         // (2) the lane's column of the operand, once per window: each window's MFMAs see
         //     only the columns of its own slot (the other slot's lanes read the zero row), so
         //     both windows accumulate into one score tile
-        u4_t bqa[KS], bqb[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            bqa[ks] = *reinterpret_cast<const u4_t*>(qrow_a + 8 * ks);
-            if constexpr (NSLOT == 2) bqb[ks] = *reinterpret_cast<const u4_t*>(qrow_b + 8 * ks);
+            op.a[ks] = *reinterpret_cast<const u4_t*>(qrow_a + 8 * ks);
+            if constexpr (NSLOT == 2) op.b[ks] = *reinterpret_cast<const u4_t*>(qrow_b + 8 * ks);
         }
-        const float c0 = (hi && !ROPE) ? kb[wave][n] : 0.f;   // key-offset bias, once per head (high column)
+        op.c0 = (hi && !ROPE) ? kb[wave][n] : 0.f;   // key-offset bias, once per head (high column)
+    };
+    auto scores_q = [&](const Job& j, const Raw& R, const QOp& op) __attribute__((always_inline)) {
+        const u4_t* bqa = op.a;
+        const u4_t* bqb = op.b;
+        const float c0 = op.c0;
         // (3) scores S^T[token][column] = codes . (q * sclK) + bias, log2 units.  RoPE mode:
         //     dequantized keys turned by their offset u in the chunk, times R(A)^T q
         float s[NV];
@@ -775,7 +797,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     auto process_f = [&](const Job& j, const Raw& R) __attribute__((always_inline)) {
         u4_t bq[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bq[ks] = *reinterpret_cast<const u4_t*>(&qs[wave][16 + n][CQ * qg + 8 * ks]);
+        for (int ks = 0; ks < KS; ++ks) bq[ks] = *reinterpret_cast<const u4_t*>(&qsh[n][CQ * qg + 8 * ks]);
         uint32_t kw[CQ / 2], vw[2 * MB];
 #pragma unroll
         for (int x = 0; x < CQ / 2; ++x) kw[x] = R.w[x];
@@ -820,9 +842,11 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
 
     // batches of up to SPLIT_BLOCK - 1 entries: the first from the split block, later
     // ones (splits longer than a block) straight from the accessible list
-    for (xb = 0; xb == 0 || xb < e_total; xb += SPLIT_BLOCK - 1) {
-        const int x = xb + lane - 1;                     // this lane's position in the split
-        const bool valid = lane >= 1 && x < e_total;
+    int x = 0;                   // this lane's position in the split
+    bool valid = false;          // this lane holds an entry of the batch
+    auto classify = [&]() __attribute__((always_inline)) {
+        x = xb + lane - 1;
+        valid = lane >= 1 && x < e_total;
         if (xb > 0 && valid) me = bf.acc[u * g.n_acc_max + e_begin + x];
         isq = isf = false;
         if (valid) {
@@ -841,18 +865,29 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         nq = __popcll(mq);
         nf = __popcll(mf);
         npair = (nq + NSLOT - 1) / NSLOT;
+    };
+    // the wave's first bf16 job of a batch: its jobs continue the round robin after the
+    // Quantized pairs
+    auto first_f = [&]() __attribute__((always_inline)) { return make_f(((wave - npair) % DW + DW) % DW); };
+    xb = 0;
+    classify();
+    __syncthreads();                 // the code table and the shared query rows
+    for (xb = 0; xb == 0 || xb < e_total; xb += SPLIT_BLOCK - 1) {
+        if (xb > 0) classify();
         {   // one job in flight per wave: the second wave on each SIMD hides its load latency
             Raw ra;
             Job j = make_q(wave);
             while (j.type != 0) {
+                QOp op;
                 load_q(j, ra);
-                process_q(j, ra);
+                products_q(j, ra, op);
+                scores_q(j, ra, op);
                 j = next_q(j);
             }
         }
         {
             Raw ra;
-            Job j = make_f(((wave - npair) % DW + DW) % DW);   // bf16 jobs continue the round robin
+            Job j = first_f();
             while (j.type != 0) {
                 load_f(j, ra);
                 process_f(j, ra);

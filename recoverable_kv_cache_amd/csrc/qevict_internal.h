@@ -138,9 +138,9 @@ constexpr int SPLIT_BLOCK = 64;
 // count as the canonical record):
 //   K codes [W*D*b/8]: code (t, c) in byte (((ch*16 + r)*4 + qg)*TPC + tc)*(CQ/P) + cc/P, bits b*(cc%P)
 //             ((qg, cc) from lay_kc_pos: c = CQ*qg + cc, or the RoPE pairing)
-//   V codes [W*D*b/8]: code (t, c) in byte (((((c%16)*4 + r/4)*NCH + ch)*MB + c/16)*TPC + tc)*(4/P) + (r%4)/P,
+//   V codes [W*D*b/8]: code (t, c) in byte (((((ch*16 + c%16)*4 + r/4)*MB + c/16)*TPC + tc)*(4/P) + (r%4)/P,
 //             bits b*(r%P) (a lane reads, per chunk, MB x TPC x 4/P bytes: the 4 tokens of row group
-//             r/4 of each tile of the chunk, per channel block)
+//             r/4 of each tile of the chunk, per channel block; each chunk's codes are contiguous)
 //   K offset [D], K scale [D] (fp16, channel order), V offset [W], V scale [W] (fp16) with
 //   token t at ((r/4)*NT + tile)*4 + r%4.
 __host__ __device__ inline int lay_tpc(int W) { return (W < 32 ? W : 32) / 16; }
@@ -178,9 +178,9 @@ __host__ __device__ inline int lay_kc_byte(int t, int c, int D, int W, int b, bo
 }
 __host__ __device__ inline int lay_kc_shift(int c, int b) { return b * (c % (8 / b)); }
 __host__ __device__ inline int lay_vc_byte(int t, int c, int D, int W, int b) {
-    const int TPC = lay_tpc(W), NCH = W / (16 * TPC), MB = D / 16, P = 8 / b;
+    const int TPC = lay_tpc(W), MB = D / 16, P = 8 / b;
     const int tile = t >> 4;
-    return (((((c & 15) * 4 + (t & 15) / 4) * NCH + tile / TPC) * MB + c / 16) * TPC + tile % TPC) * (4 / P) +
+    return (((((tile / TPC) * 16 + (c & 15)) * 4 + (t & 15) / 4) * MB + c / 16) * TPC + tile % TPC) * (4 / P) +
            (t & 3) / P;
 }
 __host__ __device__ inline int lay_vc_shift(int t, int b) { return b * (t % (8 / b)); }
