@@ -902,30 +902,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             const float* lg = bf.lse_glob + u * g.h_q;
             double* sc = mass_target(g, bf) + u * g.n_windows + me.win;
             const double s0 = *sc;
-            double sm = 0.0;
-            if ((g.h_q & 3) == 0) {
-                // batches of 32 heads, every load of a batch issued before its first use
-                // (clamped addresses; heads past h_q are dropped by the select)
-                constexpr int HB = 8;
-                for (int h0 = 0; h0 < g.h_q; h0 += 4 * HB) {
-                    f4_t v[HB], l[HB];
-#pragma unroll
-                    for (int k = 0; k < HB; ++k) {
-                        const int h = imin(h0 + 4 * k, g.h_q - 4);
-                        v[k] = *reinterpret_cast<const f4_t*>(row + h);
-                        l[k] = *reinterpret_cast<const f4_t*>(lg + h);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int k = 0; k < HB; ++k) {
-                        const bool in = h0 + 4 * k < g.h_q;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) sm += in ? (double)mass_share(v[k][i], l[k][i]) : 0.0;
-                    }
-                }
-            } else {
-                for (int h = 0; h < g.h_q; ++h) sm += (double)mass_share(row[h], lg[h]);
-            }
+            const double sm = entry_mass(row, lg, g.h_q);
             *sc = s0 + sm / g.h_q;
         }
     }

@@ -15,6 +15,38 @@ namespace qv {
 // one head's share of an entry's window mass
 __device__ __forceinline__ float mass_share(float lse_w, float lse_row) { return __builtin_amdgcn_exp2f(lse_w - lse_row); }
 
+// sum over the h_q heads, in head order (fp64), of one entry's shares: row = the entry's
+// window log-sum-exps [h_q], lg = the step's row log-sum-exps [h_q].  With h_q a multiple
+// of 4 the loads go in batches of 32 heads, each batch issued before its first use
+// (clamped addresses; heads past h_q add 0), so a batch costs one round trip.
+__device__ __forceinline__ double entry_mass(const float* __restrict__ row, const float* __restrict__ lg, int h_q) {
+    double sm = 0.0;
+    if ((h_q & 3) == 0) {
+        constexpr int HB = 8;
+        for (int h0 = 0; h0 < h_q; h0 += 4 * HB) {
+            float4 v[HB], l[HB];
+#pragma unroll
+            for (int k = 0; k < HB; ++k) {
+                const int h = h0 + 4 * k < h_q - 4 ? h0 + 4 * k : h_q - 4;
+                v[k] = *reinterpret_cast<const float4*>(row + h);
+                l[k] = *reinterpret_cast<const float4*>(lg + h);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < HB; ++k) {
+                const bool in = h0 + 4 * k < h_q;
+                sm += in ? (double)mass_share(v[k].x, l[k].x) : 0.0;
+                sm += in ? (double)mass_share(v[k].y, l[k].y) : 0.0;
+                sm += in ? (double)mass_share(v[k].z, l[k].z) : 0.0;
+                sm += in ? (double)mass_share(v[k].w, l[k].w) : 0.0;
+            }
+        }
+    } else {
+        for (int h = 0; h < h_q; ++h) sm += (double)mass_share(row[h], lg[h]);
+    }
+    return sm;
+}
+
 // adds the pending shares of accessible entries first + k*step (k = 0, 1, ...), e < last,
 // of the decode step at position pos; the sink entry (index 0) has no window and is skipped
 __device__ inline void apply_mass_range(const Geo& g, const Bufs& bf, int64_t u, int pos, int first, int last,
@@ -24,9 +56,7 @@ __device__ inline void apply_mass_range(const Geo& g, const Bufs& bf, int64_t u,
     for (int e = first; e < last; e += step) {
         if (e == 0) continue;
         const AccEntry en = bf.acc[u * g.n_acc_max + e];
-        const float* row = lwin + (int64_t)e * g.h_q;
-        double sm = 0.0;
-        for (int h = 0; h < g.h_q; ++h) sm += (double)mass_share(row[h], lg[h]);
+        const double sm = entry_mass(lwin + (int64_t)e * g.h_q, lg, g.h_q);
         if (en.win >= 0) mass_target(g, bf)[u * g.n_windows + en.win] += sm / g.h_q;
     }
 }

@@ -117,14 +117,17 @@ __device__ int block_scan_excl(int* a, int* wsum) {
     }
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
-    if (tid == 0) {
-        int acc = 0;
-        for (int w = 0; w < RT_THREADS / 64; ++w) {
-            int t = wsum[w];
-            wsum[w] = acc;
-            acc += t;
+    if (wave == 0) {     // exclusive scan of the wave totals by the first wave
+        constexpr int NWV = RT_THREADS / 64;
+        const int t = lane < NWV ? wsum[lane] : 0;
+        int inc = t;
+#pragma unroll
+        for (int o = 1; o < NWV; o <<= 1) {
+            const int y = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += y;
         }
-        wsum[RT_THREADS / 64] = acc;
+        if (lane < NWV) wsum[lane] = inc - t;
+        if (lane == NWV - 1) wsum[NWV] = inc;
     }
     __syncthreads();
     int run = wsum[wave] + incl - s;
@@ -142,6 +145,7 @@ struct RouteSmem {
     unsigned long long key[RT_MAXW];
     int idx[RT_MAXW];
     int8_t newst[RT_MAXW];
+    int8_t oldst[RT_MAXW];        // state of every window before this event
     int wsum[RT_THREADS / 64 + 1];
     int misc[8];
 };
@@ -222,11 +226,21 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         __syncthreads();
     }
 
+    // the window records of this thread's windows w = tid + i * RT_THREADS, read once
+    WinRec rec[RT_PER];
+#pragma unroll
+    for (int i = 0; i < RT_PER; ++i) {
+        const int w = tid + i * RT_THREADS;
+        rec[i] = w < NW ? win[w] : WinRec{ST_NONE, -1, -1, 0};
+        sm.oldst[w] = (int8_t)rec[i].state;
+    }
     // ---- 1. candidate pool (Eq. 4): previous Full ∪ previous Quantized ∪ aged recent windows
-    for (int w = tid; w < RT_MAXW; w += RT_THREADS) {
+#pragma unroll
+    for (int i = 0; i < RT_PER; ++i) {
+        const int w = tid + i * RT_THREADS;
         int c = 0;
         if (w < NW) {
-            const int st = win[w].state;
+            const int st = rec[i].state;
             const bool aged = g.n_sink + (w + 1) * g.W <= n - g.n_local;
             if (mode == RM_ROUTE || mode == RM_PREFILL)
                 c = (st == ST_FULL || st == ST_QUANT || ((st == ST_LOCAL || st == ST_PROMPT) && aged));
@@ -250,8 +264,6 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         cand_pos[i] = flag[w];
     }
     __syncthreads();
-    int P = 1;
-    while (P < n_cand) P <<= 1;
 #pragma unroll
     for (int i = 0; i < RT_PER; ++i) {
         const int w = cand_w[i];
@@ -261,37 +273,107 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
             sm.idx[cand_pos[i]] = w;
         }
     }
-    for (int i = n_cand + tid; i < P; i += RT_THREADS) {
-        sm.key[i] = ~0ull;
-        sm.idx[i] = 0x7fffffff;
-    }
     __syncthreads();
-    // ---- 2. bitonic sort of (key, idx) ascending over P entries: TopK_{K_f} then TopK_{K_q} (Eq. 5)
-    for (int k = 2; k <= P; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < P; i += RT_THREADS) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const unsigned long long ka = sm.key[i], kb = sm.key[ixj];
-                    const int ia = sm.idx[i], ib = sm.idx[ixj];
-                    const bool a_gt_b = ka > kb || (ka == kb && ia > ib);
-                    const bool up = (i & k) == 0;
-                    if (up == a_gt_b) {
-                        sm.key[i] = kb;
-                        sm.key[ixj] = ka;
-                        sm.idx[i] = ib;
-                        sm.idx[ixj] = ia;
+    // ---- 2. order of the candidates by (key, idx) ascending, i.e. (score desc, window asc):
+    //      TopK_{K_f} then TopK_{K_q} (Eq. 5).  Candidate i (its position after the scan) lives
+    //      in lane i mod 64 of a run of 64 (run i / 64 = wave + 16 * slot).  Each run is sorted
+    //      across its lanes by a bitonic network of lane shuffles (no barrier); the sorted runs
+    //      go to LDS; a candidate's rank is its place in its run plus, for every other run, the
+    //      number of that run's candidates before it (binary search).  Ranks are unique, so
+    //      sm.idx[rank] lists the windows in the order of a full sort.
+    {
+        const int lane = tid & 63;
+        unsigned long long kk[RT_PER];
+        int ii[RT_PER];
+#pragma unroll
+        for (int e = 0; e < RT_PER; ++e) {
+            const int i = tid + e * RT_THREADS;
+            kk[e] = i < n_cand ? sm.key[i] : ~0ull;      // sentinels sort after every candidate
+            ii[e] = i < n_cand ? sm.idx[i] : 0x7fffffff;
+        }
+        auto before = [](unsigned long long a, int ia, unsigned long long b, int ib) {
+            return a < b || (a == b && ia < ib);
+        };
+        const int n_runs = (n_cand + 63) / 64;
+#pragma unroll
+        for (int e = 0; e < RT_PER; ++e) {
+            if ((tid >> 6) + 16 * e >= n_runs) continue;   // (wave-uniform: no run here)
+            for (int k = 2; k <= 64; k <<= 1) {
+                for (int j = k >> 1; j > 0; j >>= 1) {
+                    const unsigned long long kp = __shfl_xor(kk[e], j, 64);
+                    const int ip = __shfl_xor(ii[e], j, 64);
+                    // the lower lane of a pair takes the smaller in ascending blocks
+                    const bool take_min = ((lane & j) == 0) == ((lane & k) == 0);
+                    if (take_min == before(kp, ip, kk[e], ii[e])) {
+                        kk[e] = kp;
+                        ii[e] = ip;
                     }
                 }
             }
-            __syncthreads();
         }
+        __syncthreads();          // (the unsorted arrays have been read)
+#pragma unroll
+        for (int e = 0; e < RT_PER; ++e) {
+            const int i = tid + e * RT_THREADS;
+            if ((i >> 6) < n_runs) {
+                sm.key[i] = kk[e];
+                sm.idx[i] = ii[e];
+            }
+        }
+        __syncthreads();
+        int rank[RT_PER];
+#pragma unroll
+        for (int e = 0; e < RT_PER; ++e) {
+            const int i = tid + e * RT_THREADS;
+            rank[e] = -1;
+            if (i >= n_cand) continue;
+            const int my_run = i >> 6;
+            // after the run sort, this lane holds the run's (lane)-th candidate; sentinels
+            // sort last, so lane < the run's candidate count and lane is its place in the run
+            int r = lane;
+            // for each other run, the number of its candidates before this one: a branchless
+            // lower bound of seven halving steps, eight runs at a time so that every step issues
+            // eight independent LDS reads
+            constexpr int RG = 8;
+            for (int q0 = 0; q0 < n_runs; q0 += RG) {
+                int pos[RG];
+#pragma unroll
+                for (int t = 0; t < RG; ++t) pos[t] = 0;
+#pragma unroll
+                for (int st = 64; st >= 1; st >>= 1) {
+#pragma unroll
+                    for (int t = 0; t < RG; ++t) {
+                        const int q = q0 + t;
+                        const int q_len = q < n_runs ? min(64, n_cand - 64 * q) : 0;
+                        if (pos[t] + st <= q_len) {
+                            const int at = 64 * q + pos[t] + st - 1;
+                            if (before(sm.key[at], sm.idx[at], kk[e], ii[e])) pos[t] += st;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < RG; ++t)
+                    if (q0 + t != my_run) r += pos[t];
+            }
+            rank[e] = r;
+        }
+        __syncthreads();          // (every run has been searched)
+#pragma unroll
+        for (int e = 0; e < RT_PER; ++e) {
+            if (rank[e] >= 0) {
+                sm.key[rank[e]] = kk[e];
+                sm.idx[rank[e]] = ii[e];
+            }
+        }
+        __syncthreads();
     }
     // ---- 3. new state of every window
-    for (int w = tid; w < RT_MAXW; w += RT_THREADS) {
+#pragma unroll
+    for (int i = 0; i < RT_PER; ++i) {
+        const int w = tid + i * RT_THREADS;
         int ns = ST_NONE;
         if (w < NW) {
-            const int st = win[w].state;
+            const int st = rec[i].state;
             ns = st;
             if (st == ST_PROMPT) ns = ST_LOCAL;  // non-aged prompt windows enter the recent region
             if (st == ST_NONE && g.n_sink + w * g.W < n + g.omega) ns = ST_LOCAL;   // prepare
@@ -307,7 +389,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
             __syncthreads();
         } else {
             // one-way: Full = best K_f candidates that are not Quantized; Quantized = next K_q of the rest
-            for (int r = tid; r < RT_MAXW; r += RT_THREADS) flag[r] = (r < n_cand && win[sm.idx[r]].state != ST_QUANT);
+            for (int r = tid; r < RT_MAXW; r += RT_THREADS) flag[r] = (r < n_cand && sm.oldst[sm.idx[r]] != ST_QUANT);
             __syncthreads();
             for (int r = tid; r < RT_MAXW; r += RT_THREADS) flag2[r] = flag[r];
             __syncthreads();
@@ -343,7 +425,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         const int w = tid + i * RT_THREADS;
         int a = 0;
         if (w < NW) {
-            const WinRec r = win[w];
+            const WinRec r = rec[i];
             const int os = r.state, ns = sm.newst[w];
             const bool cand = flag2 != nullptr && cand_w[i] >= 0;
             if (cand && (os == ST_LOCAL || os == ST_PROMPT)) ctr[C_AGED]++;
@@ -377,8 +459,12 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     if (tid < 8) sm.misc[tid] = 0;
     __syncthreads();
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-        if (ctr[c]) atomicAdd(&sm.misc[c], ctr[c]);
+    for (int c = 0; c < 8; ++c) {     // wave sums first: one LDS atomic per wave and counter
+        int v = ctr[c];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+        if ((tid & 63) == 0 && v) atomicAdd(&sm.misc[c], v);
+    }
     __syncthreads();
     if (tid < 8) hdr->ctr[tid] = sm.misc[tid];
 
@@ -390,8 +476,8 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
 #pragma unroll
     for (int i = 0; i < RT_PER; ++i) {
         const int w = tid + i * RT_THREADS;
-        my_slot[i] = w < NW ? win[w].slot : -1;
-        my_page[i] = w < NW ? win[w].page : -1;
+        my_slot[i] = w < NW ? rec[i].slot : -1;
+        my_page[i] = w < NW ? rec[i].page : -1;
     }
     __syncthreads();
     for (int pass = 0; pass < 2; ++pass) {      // pass 0: slots, pass 1: pages
@@ -453,7 +539,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     for (int i = 0; i < RT_PER; ++i) {
         const int w = tid + i * RT_THREADS;
         if (w >= NW) continue;
-        const WinRec r = win[w];
+        const WinRec r = rec[i];
         if (act[i] & 16) {
             PackItem it;
             it.win = w;
@@ -481,7 +567,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     for (int i = 0; i < RT_PER; ++i) {
         const int w = tid + i * RT_THREADS;
         if (w >= NW) continue;
-        WinRec r = win[w];
+        WinRec r = rec[i];
         const int ns = sm.newst[w];
         int flags = r.flags;
         if (ns == ST_EVICTED) flags = 0;
@@ -508,16 +594,16 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     __syncthreads();
     const int n_pg = block_scan_excl(flag, sm.wsum);     // flag[w]: rank among the pages
     const int n_sl = block_scan_excl(flag2, sm.wsum);    // flag2[w]: rank among the slots
-    auto list_pos = [&](int w, bool page) -> int {
-        const long long P = n_pg, S = n_sl;
+    auto list_pos = [&](int w, bool page) -> int {   // (counts <= RT_MAXW: 32-bit products)
+        const int P = n_pg, S = n_sl;
         if (page) {
-            const long long r = flag[w], X = (2 * r + 1) * S - P;   // slots strictly before
-            long long c = X > 0 ? (X + 2 * P - 1) / (2 * P) : 0;
-            return (int)(r + (c < S ? c : S));
+            const int r = flag[w], X = (2 * r + 1) * S - P;   // slots strictly before
+            const int c = X > 0 ? (int)(((unsigned)X + 2u * P - 1u) / (2u * P)) : 0;
+            return r + (c < S ? c : S);
         }
-        const long long r = flag2[w], Y = (2 * r + 1) * P - S;      // pages before or tied
-        long long c = Y >= 0 ? Y / (2 * S) + 1 : 0;
-        return (int)(r + (c < P ? c : P));
+        const int r = flag2[w], Y = (2 * r + 1) * P - S;      // pages before or tied
+        const int c = Y >= 0 ? (int)((unsigned)Y / (2u * S)) + 1 : 0;
+        return r + (c < P ? c : P);
     };
     const int n_winacc = n_pg + n_sl;
     const int base = 1;   // entry 0 is the sink prefix
