@@ -51,6 +51,7 @@ typedef enum {
 #define QEVICT_DEV_E_WINDOW 2u   /* decode wrote past the windows prepared by the last route */
 #define QEVICT_DEV_E_RANGE  4u   /* |x| > 65504 in a window being quantized */
 #define QEVICT_DEV_E_LIST   8u   /* accessible list or work list overflow */
+#define QEVICT_DEV_E_SELECT 16u  /* tier selection left open (internal invariant broken) */
 
 /* flags */
 #define QEVICT_F_NO_PROMOTE        1u  /* one-way variant Full -> Quantized -> Evicted (App. K) */

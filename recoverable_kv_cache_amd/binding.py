@@ -26,7 +26,7 @@ QEVICT_F_RANK_KEYNORM = 16
 QEVICT_F_INT4 = 32           # INT4 recoverable tier ([QEvict] Appendix G.3) instead of INT2
 QEVICT_F_ROPE = 64           # inputs before RoPE; Quantized tier in the pre-RoPE domain ([QEvict] §4.3)
 
-DEV_E_POOL, DEV_E_WINDOW, DEV_E_RANGE, DEV_E_LIST = 1, 2, 4, 8
+DEV_E_POOL, DEV_E_WINDOW, DEV_E_RANGE, DEV_E_LIST, DEV_E_SELECT = 1, 2, 4, 8, 16
 
 EXPORTED_SYMBOLS = (
     "qevict_capacities", "qevict_plan", "qevict_create", "qevict_destroy", "qevict_prefill_init",

@@ -99,7 +99,23 @@ constexpr int RT_THREADS = 1024;
 constexpr int RT_MAXW = 4096;           // windows per unit handled by one workgroup
 constexpr int RT_PER = RT_MAXW / RT_THREADS;
 
-// Exclusive scan of a[0..RT_MAXW) in LDS; returns the total.  All threads call.
+// Sum over the 64 lanes of a wave (every lane gets it) with DPP moves and the gfx950 row
+// swaps: no LDS traffic.  Every DPP pattern reads a lane of the same row, so bound_ctrl
+// changes no value.
+__device__ __forceinline__ int wave_sum_i32(int x) {
+    x += __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);    // quad [1,0,3,2]
+    x += __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);    // quad [2,3,0,1]
+    x += __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);   // row_half_mirror
+    x += __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, true);   // row_mirror
+    const auto a = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+    x = (int)(a[0] + a[1]);
+    const auto c = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+    return (int)(c[0] + c[1]);
+}
+
+// Exclusive scan of a[0..RT_MAXW) in LDS; returns the total.  All threads call.  Two counts
+// may share an element as 16-bit fields (lo + (hi << 16)): the fields add independently
+// while each total stays below 2^16 (at most RT_MAXW here).
 __device__ int block_scan_excl(int* a, int* wsum) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int v[RT_PER];
@@ -142,10 +158,9 @@ __device__ int block_scan_excl(int* a, int* wsum) {
 }
 
 struct RouteSmem {
-    unsigned long long key[RT_MAXW];
+    unsigned long long work[RT_MAXW];   // scratch: key-norm sums, tier selection, then flag arrays
     int idx[RT_MAXW];
     int8_t newst[RT_MAXW];
-    int8_t oldst[RT_MAXW];        // state of every window before this event
     int wsum[RT_THREADS / 64 + 1];
     int misc[8];
 };
@@ -167,6 +182,196 @@ __device__ inline unsigned long long ord_key(double s) {
     const unsigned long long bits = (unsigned long long)__double_as_longlong(s + 0.0);
     return (bits >> 63) ? ~bits : (bits | (1ull << 63));
 }
+// ---------------------------------------------------------------- tier selection (Eq. 5)
+// Only tier membership matters: Full = the K_f first candidates in rank order (score
+// descending, window index ascending), Quantized = the next K_q.  Each candidate has the
+// composite key C = (~ord_key(score) << 12) | window, distinct and ascending in rank order;
+// a tier boundary is the composite of rank k (the k-th smallest).  It is found by radix
+// selection: 11-bit digits of C from the top; per pass a digit histogram of the candidates
+// that share the prefix found so far (LDS atomics), then the bin holding rank k (every
+// thread takes two bins; block prefix sum) extends the prefix.  Once that bin holds at most
+// 64 candidates they are gathered and one wave ranks them exactly.  Two selections (member
+// sets and ranks) run side by side.  The loop state is block-uniform and kept in scalar
+// registers.
+using u128 = unsigned __int128;
+constexpr int SEL_BITS = 76;             // 64 key bits + 12 window bits (RT_MAXW = 4096)
+constexpr int SEL_D = 11, SEL_BINS = 1 << SEL_D, SEL_FIN = 64;
+constexpr int SEL_PASSES = (SEL_BITS + SEL_D - 1) / SEL_D;
+constexpr int RT_WAVES = RT_THREADS / 64;
+static_assert(RT_MAXW <= 4096, "window index must fit the 12 low bits of the composite key");
+static_assert(SEL_BINS == 2 * RT_THREADS, "the bin search takes two bins per thread");
+
+struct SelSmem {
+    int wtot[2][RT_WAVES];                 // per-wave totals (counts, then bin sums)
+    unsigned hist[2][SEL_BINS];
+    unsigned long long gk_hi[2][SEL_FIN], gk_lo[2][SEL_FIN];   // gathered composites
+    unsigned long long t_hi[2], t_lo[2];   // the rank-k composites
+    int bin[2], cnt[2], rem[2], gcnt[2];
+};
+enum { SEL_NONE = 0, SEL_ALL = 1, SEL_THR = 2, SEL_SEARCH = 3, SEL_GATHER = 4 };
+
+__device__ __forceinline__ u128 sel_composite(double s, int w) {
+    return ((u128)~ord_key(s) << 12) | (u128)(unsigned)w;
+}
+// top p bits of c (p in [0, SEL_BITS])
+__device__ __forceinline__ u128 sel_prefix(u128 c, int p) { return p == 0 ? (u128)0 : c >> (SEL_BITS - p); }
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Inclusive prefix sum over the 64 lanes of a wave: row shifts within the rows of 16, then
+// the row broadcasts carry the totals of rows 0 and 0-1 upward.  Lanes a DPP move does
+// not write (no source lane, or a row outside row_mask) take 0.
+__device__ __forceinline__ unsigned wave_scan_incl(unsigned x) {
+    x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
+}
+// sum of a[0..RT_WAVES) and of its first `upto` entries (LDS, 16-byte aligned)
+__device__ __forceinline__ void wave_totals(const int* a, int upto, int& all, int& before) {
+    all = 0;
+    before = 0;
+#pragma unroll
+    for (int q = 0; q < RT_WAVES; q += 4) {
+        const int4 x = *reinterpret_cast<const int4*>(a + q);
+        all += x.x + x.y + x.z + x.w;
+        before += (q < upto ? x.x : 0) + (q + 1 < upto ? x.y : 0) + (q + 2 < upto ? x.z : 0) + (q + 3 < upto ? x.w : 0);
+    }
+}
+
+// For each target t in {0, 1}: members mem[t] (bit e: element e of this thread), rank k[t].
+// On return in[t] bit e says that element e is a member of rank <= k[t] among the members.
+// Every pass adds SEL_D bits to the prefix, so at most SEL_PASSES passes run; false (and no
+// element selected) if a selection were still open after them, which the invariants exclude.
+// All threads call; ss aliases free LDS.
+__device__ bool select_two(const u128 (&c)[RT_PER], const int (&mem)[2], const int (&k)[2], int (&in)[2],
+                           SelSmem& ss) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int st[2], p[2] = {0, 0}, rem[2] = {k[0], k[1]};
+    u128 pv[2] = {0, 0}, thr[2] = {0, 0};
+    {   // member counts (two 16-bit fields: at most RT_MAXW each)
+        const int v = wave_sum_i32(__popc(mem[0]) | (__popc(mem[1]) << 16));
+        if (lane == 0) ss.wtot[0][wave] = v;
+        if (tid < 2) ss.gcnt[tid] = 0;
+        __syncthreads();
+        int tot, unused;
+        wave_totals(ss.wtot[0], 0, tot, unused);
+        tot = uni(tot);
+        const int n[2] = {tot & 0xFFFF, tot >> 16};
+#pragma unroll
+        for (int t = 0; t < 2; ++t) st[t] = k[t] <= 0 ? SEL_NONE : (k[t] >= n[t] ? SEL_ALL : SEL_SEARCH);
+    }
+    bool ok = true;
+    for (int pass = 0;; ++pass) {
+        if (st[0] != SEL_SEARCH && st[1] != SEL_SEARCH) break;
+        if (pass == SEL_PASSES) {
+            ok = false;
+            st[0] = st[1] = SEL_NONE;
+            break;
+        }
+        for (int i = tid; i < 2 * SEL_BINS; i += RT_THREADS) (&ss.hist[0][0])[i] = 0;
+        __syncthreads();
+        // histogram of the next digit over the members that share the prefix
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            if (st[t] != SEL_SEARCH) continue;
+            const int dd = min(SEL_D, SEL_BITS - p[t]), sh = SEL_BITS - p[t] - dd;
+#pragma unroll
+            for (int e = 0; e < RT_PER; ++e)
+                if (((mem[t] >> e) & 1) && sel_prefix(c[e], p[t]) == pv[t])
+                    atomicAdd(&ss.hist[t][(unsigned)(c[e] >> sh) & ((1u << dd) - 1)], 1u);
+        }
+        __syncthreads();
+        // the bin of rank rem: bins 2 tid and 2 tid + 1 on thread tid, block prefix sum
+        unsigned h0[2], h1[2], incl[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            if (st[t] != SEL_SEARCH) continue;
+            const uint2 hh = *reinterpret_cast<const uint2*>(&ss.hist[t][2 * tid]);
+            h0[t] = hh.x;
+            h1[t] = hh.y;
+            incl[t] = wave_scan_incl(hh.x + hh.y);
+            if (lane == 63) ss.wtot[t][wave] = (int)incl[t];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            if (st[t] != SEL_SEARCH) continue;
+            int all, wp;
+            wave_totals(ss.wtot[t], wave, all, wp);
+            const unsigned r = (unsigned)rem[t];
+            const unsigned before = (unsigned)wp + incl[t] - h0[t] - h1[t];
+            if (before < r && r <= (unsigned)wp + incl[t]) {      // exactly one thread
+                const bool first = before + h0[t] >= r;
+                ss.bin[t] = 2 * tid + (first ? 0 : 1);
+                ss.cnt[t] = (int)(first ? h0[t] : h1[t]);
+                ss.rem[t] = (int)(r - (first ? before : before + h0[t]));
+            }
+        }
+        __syncthreads();
+        bool gather = false;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            if (st[t] != SEL_SEARCH) continue;
+            const int dd = min(SEL_D, SEL_BITS - p[t]);
+            pv[t] = (pv[t] << dd) | (u128)(unsigned)uni(ss.bin[t]);
+            p[t] += dd;
+            rem[t] = uni(ss.rem[t]);
+            if (uni(ss.cnt[t]) <= SEL_FIN || p[t] == SEL_BITS) {
+                st[t] = SEL_GATHER;
+                gather = true;
+            }
+        }
+        if (!gather) continue;
+        // gather the at most SEL_FIN members of the final bin, then rank them in one wave
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            if (st[t] != SEL_GATHER) continue;
+#pragma unroll
+            for (int e = 0; e < RT_PER; ++e)
+                if (((mem[t] >> e) & 1) && sel_prefix(c[e], p[t]) == pv[t]) {
+                    const int at = atomicAdd(&ss.gcnt[t], 1);
+                    if (at < SEL_FIN) {     // (always: the bin holds at most SEL_FIN members)
+                        ss.gk_hi[t][at] = (unsigned long long)(c[e] >> 64);
+                        ss.gk_lo[t][at] = (unsigned long long)c[e];
+                    }
+                }
+        }
+        __syncthreads();
+        if (wave < 2 && st[wave] == SEL_GATHER) {
+            const int t = wave, m = min(ss.gcnt[t], SEL_FIN);
+            if (lane < m) {
+                const u128 mine = ((u128)ss.gk_hi[t][lane] << 64) | ss.gk_lo[t][lane];
+                int r = 0;
+                for (int j = 0; j < m; ++j) r += (((u128)ss.gk_hi[t][j] << 64) | ss.gk_lo[t][j]) < mine;
+                if (r == rem[t] - 1) {
+                    ss.t_hi[t] = ss.gk_hi[t][lane];
+                    ss.t_lo[t] = ss.gk_lo[t][lane];
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            if (st[t] == SEL_GATHER) {
+                thr[t] = ((u128)ss.t_hi[t] << 64) | ss.t_lo[t];
+                st[t] = SEL_THR;
+            }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        int bits = 0;
+#pragma unroll
+        for (int e = 0; e < RT_PER; ++e)
+            if (((mem[t] >> e) & 1) && (st[t] == SEL_ALL || (st[t] == SEL_THR && c[e] <= thr[t]))) bits |= 1 << e;
+        in[t] = bits;
+    }
+    __syncthreads();   // (ss may be reused)
+    return ok;
+}
+
 // One workgroup per (sequence, layer).
 __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer, int mode) {
     extern __shared__ unsigned char smem_raw[];
@@ -182,15 +387,10 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     const int n = hdr->n;
     const int K_f = hdr->K_f, K_q = hdr->K_q;
     const int NW = g.n_windows;
-    int* flag = (int*)sm.key;                // scratch aliasing the (not yet used) key array
-    int* flag2 = flag + RT_MAXW;
+    int* flag = (int*)sm.work;               // (used after the tier selection)
 
-    // ---- 0. the last decode step's window-mass shares enter the scores first
-    if (hdr->mass_pending) {
-        apply_mass_range(g, bf, u, n - 1, tid, hdr->n_acc, RT_THREADS);   // the step at position n - 1
-        __syncthreads();
-        if (tid == 0) hdr->mass_pending = 0;
-    }
+    // ---- 0. the last decode step's window-mass shares entered the scores in k_route_fold
+    if (tid == 0 && hdr->mass_pending) hdr->mass_pending = 0;
     // ---- 0b. decay / p-norm rankers (Appendix J, Eqs. 22-23): at each decode-time routing
     //          event the interval's mass enters the rank key and starts again from 0
     if (mode == RM_ROUTE && rank_interval(g)) {
@@ -207,7 +407,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     //          its rank key from the keys in its page (prompt windows got theirs at prefill)
     if (mode == RM_ROUTE && (g.flags & QEVICT_F_RANK_KEYNORM)) {
         int* list = sm.idx;                          // (scratch before the sort)
-        double* tokn = reinterpret_cast<double*>(sm.key);
+        double* tokn = reinterpret_cast<double*>(sm.work);
         if (tid == 0) sm.misc[0] = 0;
         __syncthreads();
         for (int w = tid; w < NW; w += RT_THREADS)
@@ -232,9 +432,10 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     for (int i = 0; i < RT_PER; ++i) {
         const int w = tid + i * RT_THREADS;
         rec[i] = w < NW ? win[w] : WinRec{ST_NONE, -1, -1, 0};
-        sm.oldst[w] = (int8_t)rec[i].state;
     }
     // ---- 1. candidate pool (Eq. 4): previous Full ∪ previous Quantized ∪ aged recent windows
+    int candm = 0;               // bit i: window tid + i * RT_THREADS is a candidate
+    u128 ckey[RT_PER];
 #pragma unroll
     for (int i = 0; i < RT_PER; ++i) {
         const int w = tid + i * RT_THREADS;
@@ -249,125 +450,39 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
             else
                 c = target[w] != 0 && st == ST_QUANT;
         }
-        flag[w] = c;
-        flag2[w] = c;
+        candm |= c << i;
+        ckey[i] = sel_composite(c && (mode == RM_ROUTE || mode == RM_PREFILL) ? score[w] : 0.0, w);
     }
-    __syncthreads();
-    const int n_cand = block_scan_excl(flag, sm.wsum);
-    // flag[] now holds positions; flag2[] the candidate bits.  Keys: descending score
-    // then ascending window index == ascending (~ord_key(score), index).
-    int cand_w[RT_PER], cand_pos[RT_PER];
+    // ---- 2. tiers of the candidates (Eq. 5): Full = rank <= K_f, Quantized = the next K_q
+    const bool one_way = (g.flags & QEVICT_F_NO_PROMOTE) != 0;
+    int isF = 0, isQ = 0;
+    if (mode == RM_ROUTE || mode == RM_PREFILL) {
+        static_assert(sizeof(SelSmem) <= sizeof(RouteSmem::work), "selection scratch");
+        SelSmem& ss = *reinterpret_cast<SelSmem*>(sm.work);
+        int in[2];
+        bool sel_ok;
+        if (!one_way) {
+            const int mem[2] = {candm, candm}, kk[2] = {K_f, K_f + K_q};
+            sel_ok = select_two(ckey, mem, kk, in, ss);
+            isF = in[0];
+            isQ = in[1] & ~in[0];
+        } else {
+            // one-way: Full = the best K_f candidates that are not Quantized before the event;
+            // Quantized = the next K_q of all other candidates, in the same order
+            int notq = 0;
 #pragma unroll
-    for (int i = 0; i < RT_PER; ++i) {
-        const int w = tid + i * RT_THREADS;
-        cand_w[i] = flag2[w] ? w : -1;
-        cand_pos[i] = flag[w];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < RT_PER; ++i) {
-        const int w = cand_w[i];
-        if (w >= 0) {
-            const double s = (mode == RM_ROUTE || mode == RM_PREFILL) ? score[w] : 0.0;
-            sm.key[cand_pos[i]] = ~ord_key(s);
-            sm.idx[cand_pos[i]] = w;
+            for (int i = 0; i < RT_PER; ++i) notq |= (rec[i].state != ST_QUANT) << i;
+            const int mem[2] = {candm & notq, 0}, kk[2] = {K_f, 0};
+            sel_ok = select_two(ckey, mem, kk, in, ss);
+            isF = in[0];
+            const int mem2[2] = {candm & ~isF, 0}, kk2[2] = {K_q, 0};
+            sel_ok = select_two(ckey, mem2, kk2, in, ss) && sel_ok;
+            isQ = in[0];
         }
-    }
-    __syncthreads();
-    // ---- 2. order of the candidates by (key, idx) ascending, i.e. (score desc, window asc):
-    //      TopK_{K_f} then TopK_{K_q} (Eq. 5).  Candidate i (its position after the scan) lives
-    //      in lane i mod 64 of a run of 64 (run i / 64 = wave + 16 * slot).  Each run is sorted
-    //      across its lanes by a bitonic network of lane shuffles (no barrier); the sorted runs
-    //      go to LDS; a candidate's rank is its place in its run plus, for every other run, the
-    //      number of that run's candidates before it (binary search).  Ranks are unique, so
-    //      sm.idx[rank] lists the windows in the order of a full sort.
-    {
-        const int lane = tid & 63;
-        unsigned long long kk[RT_PER];
-        int ii[RT_PER];
-#pragma unroll
-        for (int e = 0; e < RT_PER; ++e) {
-            const int i = tid + e * RT_THREADS;
-            kk[e] = i < n_cand ? sm.key[i] : ~0ull;      // sentinels sort after every candidate
-            ii[e] = i < n_cand ? sm.idx[i] : 0x7fffffff;
-        }
-        auto before = [](unsigned long long a, int ia, unsigned long long b, int ib) {
-            return a < b || (a == b && ia < ib);
-        };
-        const int n_runs = (n_cand + 63) / 64;
-#pragma unroll
-        for (int e = 0; e < RT_PER; ++e) {
-            if ((tid >> 6) + 16 * e >= n_runs) continue;   // (wave-uniform: no run here)
-            for (int k = 2; k <= 64; k <<= 1) {
-                for (int j = k >> 1; j > 0; j >>= 1) {
-                    const unsigned long long kp = __shfl_xor(kk[e], j, 64);
-                    const int ip = __shfl_xor(ii[e], j, 64);
-                    // the lower lane of a pair takes the smaller in ascending blocks
-                    const bool take_min = ((lane & j) == 0) == ((lane & k) == 0);
-                    if (take_min == before(kp, ip, kk[e], ii[e])) {
-                        kk[e] = kp;
-                        ii[e] = ip;
-                    }
-                }
-            }
-        }
-        __syncthreads();          // (the unsorted arrays have been read)
-#pragma unroll
-        for (int e = 0; e < RT_PER; ++e) {
-            const int i = tid + e * RT_THREADS;
-            if ((i >> 6) < n_runs) {
-                sm.key[i] = kk[e];
-                sm.idx[i] = ii[e];
-            }
-        }
-        __syncthreads();
-        int rank[RT_PER];
-#pragma unroll
-        for (int e = 0; e < RT_PER; ++e) {
-            const int i = tid + e * RT_THREADS;
-            rank[e] = -1;
-            if (i >= n_cand) continue;
-            const int my_run = i >> 6;
-            // after the run sort, this lane holds the run's (lane)-th candidate; sentinels
-            // sort last, so lane < the run's candidate count and lane is its place in the run
-            int r = lane;
-            // for each other run, the number of its candidates before this one: a branchless
-            // lower bound of seven halving steps, eight runs at a time so that every step issues
-            // eight independent LDS reads
-            constexpr int RG = 8;
-            for (int q0 = 0; q0 < n_runs; q0 += RG) {
-                int pos[RG];
-#pragma unroll
-                for (int t = 0; t < RG; ++t) pos[t] = 0;
-#pragma unroll
-                for (int st = 64; st >= 1; st >>= 1) {
-#pragma unroll
-                    for (int t = 0; t < RG; ++t) {
-                        const int q = q0 + t;
-                        const int q_len = q < n_runs ? min(64, n_cand - 64 * q) : 0;
-                        if (pos[t] + st <= q_len) {
-                            const int at = 64 * q + pos[t] + st - 1;
-                            if (before(sm.key[at], sm.idx[at], kk[e], ii[e])) pos[t] += st;
-                        }
-                    }
-                }
-#pragma unroll
-                for (int t = 0; t < RG; ++t)
-                    if (q0 + t != my_run) r += pos[t];
-            }
-            rank[e] = r;
-        }
-        __syncthreads();          // (every run has been searched)
-#pragma unroll
-        for (int e = 0; e < RT_PER; ++e) {
-            if (rank[e] >= 0) {
-                sm.key[rank[e]] = kk[e];
-                sm.idx[rank[e]] = ii[e];
-            }
-        }
-        __syncthreads();
+        if (!sel_ok && tid == 0) atomicOr(&hdr->status, QEVICT_DEV_E_SELECT);
     }
     // ---- 3. new state of every window
+    const int forced_st = mode == RM_FORCE_Q ? ST_QUANT : ST_FULL;
 #pragma unroll
     for (int i = 0; i < RT_PER; ++i) {
         const int w = tid + i * RT_THREADS;
@@ -377,44 +492,16 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
             ns = st;
             if (st == ST_PROMPT) ns = ST_LOCAL;  // non-aged prompt windows enter the recent region
             if (st == ST_NONE && g.n_sink + w * g.W < n + g.omega) ns = ST_LOCAL;   // prepare
+            if ((candm >> i) & 1) {
+                if (mode == RM_ROUTE || mode == RM_PREFILL)
+                    ns = ((isF >> i) & 1) ? ST_FULL : (((isQ >> i) & 1) ? ST_QUANT : ST_EVICTED);
+                else
+                    ns = forced_st;
+            }
         }
         sm.newst[w] = (int8_t)ns;
     }
     __syncthreads();
-    const bool one_way = (g.flags & QEVICT_F_NO_PROMOTE) != 0;
-    if (mode == RM_ROUTE || mode == RM_PREFILL) {
-        if (!one_way) {
-            for (int r = tid; r < n_cand; r += RT_THREADS)
-                sm.newst[sm.idx[r]] = (int8_t)(r < K_f ? ST_FULL : (r < K_f + K_q ? ST_QUANT : ST_EVICTED));
-            __syncthreads();
-        } else {
-            // one-way: Full = best K_f candidates that are not Quantized; Quantized = next K_q of the rest
-            for (int r = tid; r < RT_MAXW; r += RT_THREADS) flag[r] = (r < n_cand && sm.oldst[sm.idx[r]] != ST_QUANT);
-            __syncthreads();
-            for (int r = tid; r < RT_MAXW; r += RT_THREADS) flag2[r] = flag[r];
-            __syncthreads();
-            block_scan_excl(flag, sm.wsum);
-            for (int r = tid; r < RT_MAXW; r += RT_THREADS) {
-                const bool isF = r < n_cand && flag2[r] && flag[r] < K_f;
-                flag2[r] = isF;
-            }
-            __syncthreads();
-            for (int r = tid; r < RT_MAXW; r += RT_THREADS) flag[r] = (r < n_cand && !flag2[r]);
-            __syncthreads();
-            block_scan_excl(flag, sm.wsum);
-            for (int r = tid; r < n_cand; r += RT_THREADS) {
-                int ns;
-                if (flag2[r]) ns = ST_FULL;
-                else ns = flag[r] < K_q ? ST_QUANT : ST_EVICTED;
-                sm.newst[sm.idx[r]] = (int8_t)ns;
-            }
-            __syncthreads();
-        }
-    } else {
-        const int tgt = mode == RM_FORCE_Q ? ST_QUANT : ST_FULL;
-        for (int r = tid; r < n_cand; r += RT_THREADS) sm.newst[sm.idx[r]] = (int8_t)tgt;
-        __syncthreads();
-    }
 
     // ---- 4. migration actions (Algorithm 1 steps 5-20).  Per window:
     // bit0 free page, bit1 need page, bit2 free slot, bit3 need slot, bit4 pack, bit5 fill
@@ -427,7 +514,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         if (w < NW) {
             const WinRec r = rec[i];
             const int os = r.state, ns = sm.newst[w];
-            const bool cand = flag2 != nullptr && cand_w[i] >= 0;
+            const bool cand = (candm >> i) & 1;
             if (cand && (os == ST_LOCAL || os == ST_PROMPT)) ctr[C_AGED]++;
             if (os == ST_LOCAL || os == ST_FULL) {
                 if (ns == ST_QUANT) {
@@ -459,11 +546,13 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     if (tid < 8) sm.misc[tid] = 0;
     __syncthreads();
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {     // wave sums first: one LDS atomic per wave and counter
-        int v = ctr[c];
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-        if ((tid & 63) == 0 && v) atomicAdd(&sm.misc[c], v);
+    for (int c = 0; c < 8; c += 2) {  // wave sums first (two counters per word, 16-bit fields:
+                                      // a wave's count is at most 4 * 64), one LDS atomic per wave
+        const int v = wave_sum_i32(ctr[c] | (ctr[c + 1] << 16));
+        if ((tid & 63) == 0 && v) {
+            atomicAdd(&sm.misc[c], v & 0xFFFF);
+            atomicAdd(&sm.misc[c + 1], v >> 16);
+        }
     }
     __syncthreads();
     if (tid < 8) hdr->ctr[tid] = sm.misc[tid];
@@ -480,36 +569,38 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         my_page[i] = w < NW ? rec[i].page : -1;
     }
     __syncthreads();
+    int* pushed = sm.idx;     // ids pushed at this event, by stack position - cnt0 (sm.idx is free after step 3)
     for (int pass = 0; pass < 2; ++pass) {      // pass 0: slots, pass 1: pages
         const int fbit = pass == 0 ? 4 : 1, nbit = pass == 0 ? 8 : 2;
         int32_t* stack = pass == 0 ? fslot : fpage;
         const int cap = pass == 0 ? g.n_slots : g.n_pages;
         const int cnt0 = pass == 0 ? nslot_free0 : npage_free0;
+        // one scan for both counts: freed ids (low field) and needed ids (high field)
 #pragma unroll
-        for (int i = 0; i < RT_PER; ++i) flag[tid + i * RT_THREADS] = (act[i] & fbit) ? 1 : 0;
+        for (int i = 0; i < RT_PER; ++i)
+            flag[tid + i * RT_THREADS] = ((act[i] & fbit) ? 1 : 0) | ((act[i] & nbit) ? 0x10000 : 0);
         __syncthreads();
-        const int n_freed = block_scan_excl(flag, sm.wsum);
+        const int tot = block_scan_excl(flag, sm.wsum);
+        const int n_freed = tot & 0xFFFF, n_need = tot >> 16;
 #pragma unroll
         for (int i = 0; i < RT_PER; ++i) {
             if (act[i] & fbit) {
-                const int pos = cnt0 + flag[tid + i * RT_THREADS];
+                const int pos = cnt0 + (flag[tid + i * RT_THREADS] & 0xFFFF);
                 const int id = pass == 0 ? my_slot[i] : my_page[i];
                 if (pos < cap && id >= 0) stack[pos] = id;
+                pushed[pos - cnt0] = id;
                 if (pass == 0) my_slot[i] = -1;
                 else my_page[i] = -1;
             }
         }
         __syncthreads();
-#pragma unroll
-        for (int i = 0; i < RT_PER; ++i) flag[tid + i * RT_THREADS] = (act[i] & nbit) ? 1 : 0;
-        __syncthreads();
-        const int n_need = block_scan_excl(flag, sm.wsum);
         const int avail = min(cnt0 + n_freed, cap);
 #pragma unroll
         for (int i = 0; i < RT_PER; ++i) {
             if (act[i] & nbit) {
-                const int k = flag[tid + i * RT_THREADS];
-                const int id = k < avail ? stack[avail - 1 - k] : -1;
+                const int k = flag[tid + i * RT_THREADS] >> 16;
+                const int at = avail - 1 - k;
+                const int id = k >= avail ? -1 : (at >= cnt0 ? pushed[at - cnt0] : stack[at]);
                 if (pass == 0) my_slot[i] = id;
                 else my_page[i] = id;
             }
@@ -528,13 +619,11 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
 
     // ---- 6. work lists: pack (quantize once) and fill (promote / copy prompt)
 #pragma unroll
-    for (int i = 0; i < RT_PER; ++i) {
-        flag[tid + i * RT_THREADS] = (act[i] & 16) ? 1 : 0;
-        flag2[tid + i * RT_THREADS] = (act[i] & 32) ? 1 : 0;
-    }
+    for (int i = 0; i < RT_PER; ++i)   // pack count (low field), fill count (high field)
+        flag[tid + i * RT_THREADS] = ((act[i] & 16) ? 1 : 0) | ((act[i] & 32) ? 0x10000 : 0);
     __syncthreads();
-    const int n_pack = block_scan_excl(flag, sm.wsum);
-    const int n_fill = block_scan_excl(flag2, sm.wsum);
+    const int tot_pf = block_scan_excl(flag, sm.wsum);
+    const int n_pack = tot_pf & 0xFFFF, n_fill = tot_pf >> 16;
 #pragma unroll
     for (int i = 0; i < RT_PER; ++i) {
         const int w = tid + i * RT_THREADS;
@@ -546,7 +635,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
             it.src_prompt = r.state == ST_PROMPT ? 1 : 0;
             it.src_page = r.page;
             it.dst_slot = my_slot[i];
-            bf.pack[u * g.n_windows + flag[w]] = it;
+            bf.pack[u * g.n_windows + (flag[w] & 0xFFFF)] = it;
         }
         if (act[i] & 32) {
             FillItem it;
@@ -554,7 +643,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
             it.dst_page = my_page[i];
             it.src_slot = r.state == ST_QUANT ? r.slot : (r.state == ST_PROMPT ? -1 : -2);
             it.pad = 0;
-            bf.fill[u * g.n_windows + flag2[w]] = it;
+            bf.fill[u * g.n_windows + (flag[w] >> 16)] = it;
         }
     }
     if (tid == 0) {
@@ -586,22 +675,21 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     //      the pages fall evenly among the slots (by rank fraction, (2r + 1) / 2count, pages
     //      first on ties): every byte-balanced split then holds a like share of both kinds,
     //      whose costs per byte differ.  Attention does not depend on the order.
-    for (int w = tid; w < RT_MAXW; w += RT_THREADS) {
+    for (int w = tid; w < RT_MAXW; w += RT_THREADS) {   // page (low field), slot (high field)
         const int ns = w < NW ? sm.newst[w] : ST_NONE;
-        flag[w] = (ns == ST_LOCAL || ns == ST_FULL) ? 1 : 0;
-        flag2[w] = ns == ST_QUANT ? 1 : 0;
+        flag[w] = ((ns == ST_LOCAL || ns == ST_FULL) ? 1 : 0) | (ns == ST_QUANT ? 0x10000 : 0);
     }
     __syncthreads();
-    const int n_pg = block_scan_excl(flag, sm.wsum);     // flag[w]: rank among the pages
-    const int n_sl = block_scan_excl(flag2, sm.wsum);    // flag2[w]: rank among the slots
+    const int tot_ps = block_scan_excl(flag, sm.wsum);   // flag[w]: rank among the pages / the slots
+    const int n_pg = tot_ps & 0xFFFF, n_sl = tot_ps >> 16;
     auto list_pos = [&](int w, bool page) -> int {   // (counts <= RT_MAXW: 32-bit products)
         const int P = n_pg, S = n_sl;
         if (page) {
-            const int r = flag[w], X = (2 * r + 1) * S - P;   // slots strictly before
+            const int r = flag[w] & 0xFFFF, X = (2 * r + 1) * S - P;   // slots strictly before
             const int c = X > 0 ? (int)(((unsigned)X + 2u * P - 1u) / (2u * P)) : 0;
             return r + (c < S ? c : S);
         }
-        const int r = flag2[w], Y = (2 * r + 1) * P - S;      // pages before or tied
+        const int r = flag[w] >> 16, Y = (2 * r + 1) * P - S;   // pages before or tied
         const int c = Y >= 0 ? (int)((unsigned)Y / (2u * S)) + 1 : 0;
         return r + (c < P ? c : P);
     };
@@ -655,19 +743,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         }
         splits[s] = pos;
     }
-    __syncthreads();
-    // split blocks: header {entries, first entry, -1, 0} and the first SPLIT_BLOCK - 1 entries
-    {
-        AccEntry* sblk = bf.split_blk + u * g.n_splits * SPLIT_BLOCK;
-        for (int i = tid; i < g.n_splits * SPLIT_BLOCK; i += RT_THREADS) {
-            const int s = i / SPLIT_BLOCK, x = i % SPLIT_BLOCK;
-            const int e0 = splits[s], cnt = splits[s + 1] - e0;
-            AccEntry v = AccEntry{EK_PAGE, -1, -1, 0};
-            if (x == 0) v = AccEntry{cnt, e0, -1, 0};
-            else if (x - 1 < cnt) v = acc[e0 + x - 1];
-            sblk[i] = v;
-        }
-    }
+    // (the split blocks are copied by k_split_blocks)
     if (tid == 0) {
         hdr->n_acc = n_acc;
         int nwin = 0;
@@ -679,10 +755,43 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     }
 }
 
+// The last decode step's pending window-mass shares, folded into the scores before routing:
+// one thread per accessible entry, spread over many workgroups (a single workgroup would take
+// microseconds to bring in one unit's log-sum-exp rows).  k_route then clears the flag.
+__global__ void __launch_bounds__(256) k_route_fold(Geo g, Bufs bf, int layer) {
+    const int ub = blockIdx.y;
+    const int b = layer >= 0 ? ub : ub / g.L;
+    const int l = layer >= 0 ? layer : ub % g.L;
+    const int64_t u = unit_of(g, b, l);
+    const UnitHdr* hdr = bf.hdr + u;
+    if (!hdr->mass_pending) return;
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    const int n_acc = hdr->n_acc;
+    apply_mass_range(g, bf, u, hdr->n - 1, e, e < n_acc ? e + 1 : e, 1);   // the step at position n - 1
+}
+
+// Each split's block: header {entries, first entry, -1, 0} and its first SPLIT_BLOCK - 1
+// accessible-list entries, copied after k_route has rebuilt the list and the split offsets.
+__global__ void __launch_bounds__(SPLIT_BLOCK) k_split_blocks(Geo g, Bufs bf, int layer) {
+    const int ub = blockIdx.y;
+    const int b = layer >= 0 ? ub : ub / g.L;
+    const int l = layer >= 0 ? layer : ub % g.L;
+    const int64_t u = unit_of(g, b, l);
+    const int s = blockIdx.x, x = threadIdx.x;
+    const int32_t* splits = bf.splits + u * (g.n_splits + 1);
+    const int e0 = splits[s], cnt = splits[s + 1] - e0;
+    AccEntry v = AccEntry{EK_PAGE, -1, -1, 0};
+    if (x == 0) v = AccEntry{cnt, e0, -1, 0};
+    else if (x - 1 < cnt) v = bf.acc[u * g.n_acc_max + e0 + x - 1];
+    bf.split_blk[(u * g.n_splits + s) * SPLIT_BLOCK + x] = v;
+}
+
 hipError_t launch_route(const Geo& g, const Bufs& bf, int layer, int mode, hipStream_t s) {
-    const int blocks = layer >= 0 ? g.B : g.B * g.L;
+    const int units = layer >= 0 ? g.B : g.B * g.L;
+    hipLaunchKernelGGL(k_route_fold, dim3((g.n_acc_max + 255) / 256, units), dim3(256), 0, s, g, bf, layer);
     const size_t smem = sizeof(RouteSmem);
-    hipLaunchKernelGGL(k_route, dim3(blocks), dim3(RT_THREADS), smem, s, g, bf, layer, mode);
+    hipLaunchKernelGGL(k_route, dim3(units), dim3(RT_THREADS), smem, s, g, bf, layer, mode);
+    hipLaunchKernelGGL(k_split_blocks, dim3(g.n_splits, units), dim3(SPLIT_BLOCK), 0, s, g, bf, layer);
     return hipGetLastError();
 }
 
