@@ -49,6 +49,8 @@ qevict_status validate_accounting(const qevict_config* c) {
 qevict_status validate(const qevict_config* c) {
     if (!c) return fail(QEVICT_E_INVALID, "null config");
     if (c->batch < 1 || c->n_layers < 1) return fail(QEVICT_E_INVALID, "batch and n_layers must be >= 1");
+    if ((int64_t)c->batch * c->n_layers > MIG_MAX_UNITS)
+        return fail(QEVICT_E_INVALID, "batch * n_layers must be <= %d", MIG_MAX_UNITS);
     if (c->h_kv < 1 || c->h_q < c->h_kv || c->h_q % c->h_kv) return fail(QEVICT_E_INVALID, "h_q must be a multiple of h_kv");
     int G = c->h_q / c->h_kv;
     if (G != 1 && G != 2 && G != 4 && G != 8) return fail(QEVICT_E_INVALID, "h_q / h_kv must be 1, 2, 4 or 8");
@@ -359,8 +361,7 @@ qevict_status qevict_prefill_init(qevict_state* st, int32_t layer, const void* q
     if (rope) HIP_TRY(launch_rope_prompt(g, st->bf, score_init ? nullptr : qp, kp, workspace, &qp, &kp, hs));
     HIP_TRY(launch_prefill_setup(g, st->bf, layer, kp, (const uint16_t*)v_prompt, hs));
     HIP_TRY(launch_prefill_scores(g, st->bf, layer, qp, kp, score_init, workspace, hs));
-    HIP_TRY(launch_route(g, st->bf, layer, RM_PREFILL, hs));
-    HIP_TRY(launch_migrate(g, st->bf, layer, kp, (const uint16_t*)v_prompt, hs));
+    HIP_TRY(launch_route(g, st->bf, layer, RM_PREFILL, kp, (const uint16_t*)v_prompt, hs));
     st->prefilled[layer] = 1;
     st->steps[layer] = 0;
     return QEVICT_OK;
@@ -460,8 +461,7 @@ qevict_status qevict_route(qevict_state* st, int32_t layer, void* stream) {
     for (int l = 0; l < st->cfg.n_layers; ++l)
         if ((layer == -1 || layer == l) && !st->prefilled[l]) return fail(QEVICT_E_STATE, "layer %d has no prefill", l);
     hipStream_t hs = (hipStream_t)stream;
-    HIP_TRY(launch_route(st->lay.g, st->bf, layer, RM_ROUTE, hs));
-    HIP_TRY(launch_migrate(st->lay.g, st->bf, layer, nullptr, nullptr, hs));
+    HIP_TRY(launch_route(st->lay.g, st->bf, layer, RM_ROUTE, nullptr, nullptr, hs));
     for (int l = 0; l < st->cfg.n_layers; ++l)
         if (layer == -1 || layer == l) st->step_fresh[l] = 0;
     return QEVICT_OK;
@@ -487,8 +487,7 @@ static qevict_status forced(qevict_state* st, int32_t layer, const int32_t* win_
     if (n == 0) return QEVICT_OK;
     hipStream_t hs = (hipStream_t)stream;
     HIP_TRY(launch_force_targets(st->lay.g, st->bf, layer, win_ids, n, mode == RM_FORCE_Q ? ST_QUANT : ST_FULL, hs));
-    HIP_TRY(launch_route(st->lay.g, st->bf, layer, mode, hs));
-    HIP_TRY(launch_migrate(st->lay.g, st->bf, layer, nullptr, nullptr, hs));
+    HIP_TRY(launch_route(st->lay.g, st->bf, layer, mode, nullptr, nullptr, hs));
     st->step_fresh[layer] = 0;
     return QEVICT_OK;
 }

@@ -121,6 +121,8 @@ __host__ __device__ inline int64_t lse_win_off(const Geo& g, int64_t u, int par)
 // Each split's header and first SPLIT_BLOCK - 1 accessible-list entries, copied by the
 // router to a fixed place so that a decode wave gets them in one load (one per lane).
 constexpr int SPLIT_BLOCK = 64;
+// (sequence, layer) units one routing launch may cover (batch * n_layers)
+constexpr int MIG_MAX_UNITS = 4096;
 
 // ------------------------------------------------------------------ in-HBM layouts
 // The decode kernel feeds MFMA tiles straight from HBM, so pages and
@@ -217,11 +219,10 @@ hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t
 hipError_t launch_finish(const Geo& g, const Bufs& bf, int layer, float* out, const uint16_t* k_new,
                          const uint16_t* v_new, int score_now, hipStream_t s);
 hipError_t launch_flush_mass(const Geo& g, const Bufs& bf, int layer, int b, hipStream_t s);
-hipError_t launch_route(const Geo& g, const Bufs& bf, int layer, int mode, hipStream_t s);
+hipError_t launch_route(const Geo& g, const Bufs& bf, int layer, int mode, const uint16_t* kp, const uint16_t* vp,
+                        hipStream_t s);
 hipError_t launch_force_targets(const Geo& g, const Bufs& bf, int layer, const int32_t* win_ids, int n, int target,
                                 hipStream_t s);
-hipError_t launch_migrate(const Geo& g, const Bufs& bf, int layer, const uint16_t* kp, const uint16_t* vp,
-                          hipStream_t s);
 hipError_t launch_prefill_setup(const Geo& g, const Bufs& bf, int layer, const uint16_t* kp, const uint16_t* vp,
                                 hipStream_t s);
 hipError_t launch_prefill_scores(const Geo& g, const Bufs& bf, int layer, const uint16_t* qp, const uint16_t* kp,

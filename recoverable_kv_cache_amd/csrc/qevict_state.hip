@@ -7,6 +7,8 @@
 // Quantization", Eqs. 4-6), Appendix A Algorithm 1.
 #include "qevict_common.h"
 #include "qevict_internal.h"
+
+#include <type_traits>
 #include "qevict_mass.h"
 
 namespace qv {
@@ -99,69 +101,125 @@ constexpr int RT_THREADS = 1024;
 constexpr int RT_MAXW = 4096;           // windows per unit handled by one workgroup
 constexpr int RT_PER = RT_MAXW / RT_THREADS;
 
-// Sum over the 64 lanes of a wave (every lane gets it) with DPP moves and the gfx950 row
-// swaps: no LDS traffic.  Every DPP pattern reads a lane of the same row, so bound_ctrl
-// changes no value.
+// Reduction over the 64 lanes of a wave (every lane gets the result) with DPP moves and
+// the gfx950 row swaps: no LDS traffic.  Every DPP pattern reads a lane of the same row,
+// so bound_ctrl changes no value.  op: associative and commutative.
+template <typename Op>
+__device__ __forceinline__ unsigned wave_reduce_u32(unsigned x, Op op) {
+    x = op(x, (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true));    // quad [1,0,3,2]
+    x = op(x, (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true));    // quad [2,3,0,1]
+    x = op(x, (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, true));   // row_half_mirror
+    x = op(x, (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, true));   // row_mirror
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = op(a[0], a[1]);
+    const auto c = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return op(c[0], c[1]);
+}
+// min and max over aligned groups of G consecutive lanes (G a power of two, at most 64);
+// every lane of a group gets its group's results.  Quad permutes, then the mirrors within
+// 8 and within 16 lanes, then the row swaps: each step stays inside the group.
+template <int G>
+__device__ __forceinline__ void group_minmax(float& mn, float& mx) {
+    auto dpp = [](float v, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), decltype(ctrl)::value, 0xF, 0xF, true));
+    };
+    if constexpr (G >= 2) {
+        mn = fminf(mn, dpp(mn, std::integral_constant<int, 0xB1>{}));
+        mx = fmaxf(mx, dpp(mx, std::integral_constant<int, 0xB1>{}));
+    }
+    if constexpr (G >= 4) {
+        mn = fminf(mn, dpp(mn, std::integral_constant<int, 0x4E>{}));
+        mx = fmaxf(mx, dpp(mx, std::integral_constant<int, 0x4E>{}));
+    }
+    if constexpr (G >= 8) {
+        mn = fminf(mn, dpp(mn, std::integral_constant<int, 0x141>{}));
+        mx = fmaxf(mx, dpp(mx, std::integral_constant<int, 0x141>{}));
+    }
+    if constexpr (G >= 16) {
+        mn = fminf(mn, dpp(mn, std::integral_constant<int, 0x140>{}));
+        mx = fmaxf(mx, dpp(mx, std::integral_constant<int, 0x140>{}));
+    }
+    if constexpr (G >= 32) {
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
+        const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mn = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+        mx = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    }
+    if constexpr (G >= 64) {
+        const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
+        const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mn = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+        mx = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    }
+}
+
 __device__ __forceinline__ int wave_sum_i32(int x) {
-    x += __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);    // quad [1,0,3,2]
-    x += __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);    // quad [2,3,0,1]
-    x += __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);   // row_half_mirror
-    x += __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, true);   // row_mirror
-    const auto a = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
-    x = (int)(a[0] + a[1]);
-    const auto c = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
-    return (int)(c[0] + c[1]);
+    return (int)wave_reduce_u32((unsigned)x, [](unsigned p, unsigned q) { return p + q; });
+}
+__device__ __forceinline__ unsigned wave_and_u32(unsigned x) {
+    return wave_reduce_u32(x, [](unsigned p, unsigned q) { return p & q; });
+}
+__device__ __forceinline__ unsigned wave_or_u32(unsigned x) {
+    return wave_reduce_u32(x, [](unsigned p, unsigned q) { return p | q; });
+}
+
+constexpr int RT_WAVES = RT_THREADS / 64;
+
+// Inclusive prefix sum over the 64 lanes of a wave: row shifts within the rows of 16, then
+// the row broadcasts carry the totals of rows 0 and 0-1 upward.  Lanes a DPP move does
+// not write (no source lane, or a row outside row_mask) take 0.
+__device__ __forceinline__ unsigned wave_scan_incl(unsigned x) {
+    x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
+}
+// sum of a[0..RT_WAVES) and of its first `upto` entries (LDS, 16-byte aligned)
+__device__ __forceinline__ void wave_totals(const int* a, int upto, int& all, int& before) {
+    all = 0;
+    before = 0;
+#pragma unroll
+    for (int q = 0; q < RT_WAVES; q += 4) {
+        const int4 x = *reinterpret_cast<const int4*>(a + q);
+        all += x.x + x.y + x.z + x.w;
+        before += (q < upto ? x.x : 0) + (q + 1 < upto ? x.y : 0) + (q + 2 < upto ? x.z : 0) + (q + 3 < upto ? x.w : 0);
+    }
 }
 
 // Exclusive scan of a[0..RT_MAXW) in LDS; returns the total.  All threads call.  Two counts
 // may share an element as 16-bit fields (lo + (hi << 16)): the fields add independently
-// while each total stays below 2^16 (at most RT_MAXW here).
+// while each total stays below 2^16 (at most RT_MAXW here).  wsum: RT_WAVES ints of LDS,
+// 16-byte aligned.
 __device__ int block_scan_excl(int* a, int* wsum) {
+    static_assert(RT_PER == 4, "four elements per thread");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int v[RT_PER];
-    int s = 0;
-#pragma unroll
-    for (int i = 0; i < RT_PER; ++i) {
-        v[i] = a[tid * RT_PER + i];
-        s += v[i];
-    }
-    int incl = s;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
-    }
+    const int4 v = *reinterpret_cast<const int4*>(a + tid * RT_PER);
+    const int s = v.x + v.y + v.z + v.w;
+    const int incl = (int)wave_scan_incl((unsigned)s);
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
-    if (wave == 0) {     // exclusive scan of the wave totals by the first wave
-        constexpr int NWV = RT_THREADS / 64;
-        const int t = lane < NWV ? wsum[lane] : 0;
-        int inc = t;
-#pragma unroll
-        for (int o = 1; o < NWV; o <<= 1) {
-            const int y = __shfl_up(inc, o, 64);
-            if (lane >= o) inc += y;
-        }
-        if (lane < NWV) wsum[lane] = inc - t;
-        if (lane == NWV - 1) wsum[NWV] = inc;
-    }
+    int all, before;
+    wave_totals(wsum, wave, all, before);
+    int4 o;
+    o.x = before + incl - s;
+    o.y = o.x + v.x;
+    o.z = o.y + v.y;
+    o.w = o.z + v.z;
+    *reinterpret_cast<int4*>(a + tid * RT_PER) = o;
     __syncthreads();
-    int run = wsum[wave] + incl - s;
-#pragma unroll
-    for (int i = 0; i < RT_PER; ++i) {
-        a[tid * RT_PER + i] = run;
-        run += v[i];
-    }
-    const int total = wsum[RT_THREADS / 64];
-    __syncthreads();
-    return total;
+    return all;
 }
 
+constexpr int RT_PF = 1024;            // top entries of each free stack read ahead
 struct RouteSmem {
     unsigned long long work[RT_MAXW];   // scratch: key-norm sums, tier selection, then flag arrays
     int idx[RT_MAXW];
+    int top_slot[RT_PF], top_page[RT_PF];   // free-stack entries cnt0 - 1 - k, k < RT_PF
     int8_t newst[RT_MAXW];
-    int wsum[RT_THREADS / 64 + 1];
+    alignas(16) int wsum[RT_WAVES];
     int misc[8];
 };
 
@@ -197,12 +255,12 @@ using u128 = unsigned __int128;
 constexpr int SEL_BITS = 76;             // 64 key bits + 12 window bits (RT_MAXW = 4096)
 constexpr int SEL_D = 11, SEL_BINS = 1 << SEL_D, SEL_FIN = 64;
 constexpr int SEL_PASSES = (SEL_BITS + SEL_D - 1) / SEL_D;
-constexpr int RT_WAVES = RT_THREADS / 64;
 static_assert(RT_MAXW <= 4096, "window index must fit the 12 low bits of the composite key");
 static_assert(SEL_BINS == 2 * RT_THREADS, "the bin search takes two bins per thread");
 
 struct SelSmem {
     int wtot[2][RT_WAVES];                 // per-wave totals (counts, then bin sums)
+    unsigned wand[RT_WAVES], wor[RT_WAVES];
     unsigned hist[2][SEL_BINS];
     unsigned long long gk_hi[2][SEL_FIN], gk_lo[2][SEL_FIN];   // gathered composites
     unsigned long long t_hi[2], t_lo[2];   // the rank-k composites
@@ -217,30 +275,6 @@ __device__ __forceinline__ u128 sel_composite(double s, int w) {
 __device__ __forceinline__ u128 sel_prefix(u128 c, int p) { return p == 0 ? (u128)0 : c >> (SEL_BITS - p); }
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Inclusive prefix sum over the 64 lanes of a wave: row shifts within the rows of 16, then
-// the row broadcasts carry the totals of rows 0 and 0-1 upward.  Lanes a DPP move does
-// not write (no source lane, or a row outside row_mask) take 0.
-__device__ __forceinline__ unsigned wave_scan_incl(unsigned x) {
-    x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
-    x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
-    x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
-    x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
-    x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
-    x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
-    return x;
-}
-// sum of a[0..RT_WAVES) and of its first `upto` entries (LDS, 16-byte aligned)
-__device__ __forceinline__ void wave_totals(const int* a, int upto, int& all, int& before) {
-    all = 0;
-    before = 0;
-#pragma unroll
-    for (int q = 0; q < RT_WAVES; q += 4) {
-        const int4 x = *reinterpret_cast<const int4*>(a + q);
-        all += x.x + x.y + x.z + x.w;
-        before += (q < upto ? x.x : 0) + (q + 1 < upto ? x.y : 0) + (q + 2 < upto ? x.z : 0) + (q + 3 < upto ? x.w : 0);
-    }
-}
-
 // For each target t in {0, 1}: members mem[t] (bit e: element e of this thread), rank k[t].
 // On return in[t] bit e says that element e is a member of rank <= k[t] among the members.
 // Every pass adds SEL_D bits to the prefix, so at most SEL_PASSES passes run; false (and no
@@ -251,9 +285,25 @@ __device__ bool select_two(const u128 (&c)[RT_PER], const int (&mem)[2], const i
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int st[2], p[2] = {0, 0}, rem[2] = {k[0], k[1]};
     u128 pv[2] = {0, 0}, thr[2] = {0, 0};
-    {   // member counts (two 16-bit fields: at most RT_MAXW each)
+    {   // member counts (two 16-bit fields: at most RT_MAXW each), and the bits that all
+        // members share at the top of their composites (AND == OR over the top 32 bits):
+        // the first digit starts below them
+        unsigned ka = ~0u, ko = 0u;
+#pragma unroll
+        for (int e = 0; e < RT_PER; ++e)
+            if (((mem[0] | mem[1]) >> e) & 1) {
+                const unsigned top = (unsigned)(c[e] >> (SEL_BITS - 32));
+                ka &= top;
+                ko |= top;
+            }
         const int v = wave_sum_i32(__popc(mem[0]) | (__popc(mem[1]) << 16));
-        if (lane == 0) ss.wtot[0][wave] = v;
+        ka = wave_and_u32(ka);
+        ko = wave_or_u32(ko);
+        if (lane == 0) {
+            ss.wtot[0][wave] = v;
+            ss.wand[wave] = ka;
+            ss.wor[wave] = ko;
+        }
         if (tid < 2) ss.gcnt[tid] = 0;
         __syncthreads();
         int tot, unused;
@@ -261,7 +311,18 @@ __device__ bool select_two(const u128 (&c)[RT_PER], const int (&mem)[2], const i
         tot = uni(tot);
         const int n[2] = {tot & 0xFFFF, tot >> 16};
 #pragma unroll
-        for (int t = 0; t < 2; ++t) st[t] = k[t] <= 0 ? SEL_NONE : (k[t] >= n[t] ? SEL_ALL : SEL_SEARCH);
+        for (int q = 0; q < RT_WAVES; ++q) {
+            ka &= ss.wand[q];
+            ko |= ss.wor[q];
+        }
+        const unsigned diff = (unsigned)uni((int)(ka ^ ko)), kau = (unsigned)uni((int)ka);
+        const int p0 = diff == 0 ? 32 : __clz(diff);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            st[t] = k[t] <= 0 ? SEL_NONE : (k[t] >= n[t] ? SEL_ALL : SEL_SEARCH);
+            p[t] = p0;
+            pv[t] = p0 == 0 ? (u128)0 : (u128)(kau >> (32 - p0));
+        }
     }
     bool ok = true;
     for (int pass = 0;; ++pass) {
@@ -389,8 +450,32 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     const int NW = g.n_windows;
     int* flag = (int*)sm.work;               // (used after the tier selection)
 
-    // ---- 0. the last decode step's window-mass shares entered the scores in k_route_fold
-    if (tid == 0 && hdr->mass_pending) hdr->mass_pending = 0;
+    // ---- 0. the last decode step's window-mass shares (Eq. 1), folded before routing: one
+    //         thread per accessible entry, the entry's mass to LDS by window.  With the
+    //         cumulative ranker the sums join the rank keys as they are read (below);
+    //         the other rankers take them in global memory first.
+    const bool fold = hdr->mass_pending != 0;
+    const bool cum_fold = fold && !rank_interval(g) && !(g.flags & QEVICT_F_RANK_KEYNORM);
+    double* mwin = reinterpret_cast<double*>(sm.work);      // RT_MAXW doubles
+    if (fold) {
+        for (int w = tid; w < RT_MAXW; w += RT_THREADS) mwin[w] = 0.0;
+        __syncthreads();
+        const float* lwin = bf.lse_win + lse_win_off(g, u, (n - 1) & 1);   // the step at position n - 1
+        const float* lg = bf.lse_glob + u * g.h_q;
+        const int n_acc = hdr->n_acc;
+        for (int e = 1 + tid; e < n_acc; e += RT_THREADS) {   // (entry 0: the sinks, no window)
+            const AccEntry en = bf.acc[u * g.n_acc_max + e];
+            if (en.win >= 0 && en.win < NW) mwin[en.win] = entry_mass(lwin + (int64_t)e * g.h_q, lg, g.h_q) / g.h_q;
+        }
+        __syncthreads();
+        if (tid == 0) hdr->mass_pending = 0;
+        if (!cum_fold) {
+            double* tgt = mass_target(g, bf) + u * NW;
+            for (int w = tid; w < NW; w += RT_THREADS)
+                if (mwin[w] != 0.0) tgt[w] += mwin[w];
+            __syncthreads();
+        }
+    }
     // ---- 0b. decay / p-norm rankers (Appendix J, Eqs. 22-23): at each decode-time routing
     //          event the interval's mass enters the rank key and starts again from 0
     if (mode == RM_ROUTE && rank_interval(g)) {
@@ -426,12 +511,27 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         __syncthreads();
     }
 
-    // the window records of this thread's windows w = tid + i * RT_THREADS, read once
+    // the window records and rank keys of this thread's windows w = tid + i * RT_THREADS,
+    // read once (all loads issued together)
     WinRec rec[RT_PER];
+    double sc[RT_PER];
 #pragma unroll
     for (int i = 0; i < RT_PER; ++i) {
         const int w = tid + i * RT_THREADS;
         rec[i] = w < NW ? win[w] : WinRec{ST_NONE, -1, -1, 0};
+        sc[i] = w < NW ? score[w] : 0.0;
+    }
+    if (cum_fold) {   // S_bar(w) += the step's mass (windows with an entry)
+#pragma unroll
+        for (int i = 0; i < RT_PER; ++i) {
+            const int w = tid + i * RT_THREADS;
+            const double m = w < NW ? mwin[w] : 0.0;
+            if (m != 0.0) {
+                sc[i] += m;
+                score[w] = sc[i];
+            }
+        }
+        __syncthreads();   // (mwin aliases the selection scratch)
     }
     // ---- 1. candidate pool (Eq. 4): previous Full ∪ previous Quantized ∪ aged recent windows
     int candm = 0;               // bit i: window tid + i * RT_THREADS is a candidate
@@ -451,7 +551,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
                 c = target[w] != 0 && st == ST_QUANT;
         }
         candm |= c << i;
-        ckey[i] = sel_composite(c && (mode == RM_ROUTE || mode == RM_PREFILL) ? score[w] : 0.0, w);
+        ckey[i] = sel_composite(c && (mode == RM_ROUTE || mode == RM_PREFILL) ? sc[i] : 0.0, w);
     }
     // ---- 2. tiers of the candidates (Eq. 5): Full = rank <= K_f, Quantized = the next K_q
     const bool one_way = (g.flags & QEVICT_F_NO_PROMOTE) != 0;
@@ -755,44 +855,58 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     }
 }
 
-// The last decode step's pending window-mass shares, folded into the scores before routing:
-// one thread per accessible entry, spread over many workgroups (a single workgroup would take
-// microseconds to bring in one unit's log-sum-exp rows).  k_route then clears the flag.
-__global__ void __launch_bounds__(256) k_route_fold(Geo g, Bufs bf, int layer) {
-    const int ub = blockIdx.y;
-    const int b = layer >= 0 ? ub : ub / g.L;
-    const int l = layer >= 0 ? layer : ub % g.L;
-    const int64_t u = unit_of(g, b, l);
-    const UnitHdr* hdr = bf.hdr + u;
-    if (!hdr->mass_pending) return;
-    const int e = blockIdx.x * blockDim.x + threadIdx.x;
-    const int n_acc = hdr->n_acc;
-    apply_mass_range(g, bf, u, hdr->n - 1, e, e < n_acc ? e + 1 : e, 1);   // the step at position n - 1
-}
 
-// Each split's block: header {entries, first entry, -1, 0} and its first SPLIT_BLOCK - 1
-// accessible-list entries, copied after k_route has rebuilt the list and the split offsets.
-__global__ void __launch_bounds__(SPLIT_BLOCK) k_split_blocks(Geo g, Bufs bf, int layer) {
-    const int ub = blockIdx.y;
-    const int b = layer >= 0 ? ub : ub / g.L;
-    const int l = layer >= 0 ? layer : ub % g.L;
-    const int64_t u = unit_of(g, b, l);
-    const int s = blockIdx.x, x = threadIdx.x;
-    const int32_t* splits = bf.splits + u * (g.n_splits + 1);
-    const int e0 = splits[s], cnt = splits[s + 1] - e0;
-    AccEntry v = AccEntry{EK_PAGE, -1, -1, 0};
-    if (x == 0) v = AccEntry{cnt, e0, -1, 0};
-    else if (x - 1 < cnt) v = bf.acc[u * g.n_acc_max + e0 + x - 1];
-    bf.split_blk[(u * g.n_splits + s) * SPLIT_BLOCK + x] = v;
-}
+// ------------------------------------------------------------------------------------ migration work lists
+// A routing launch covers units ub = 0..n_units-1 (layer >= 0: (ub, layer); else (ub / L,
+// ub % L)).  The pack / fill items of all its units form one list, unit by unit, which the
+// workgroups of a migration kernel share (few items per routing event: a grid sized by
+// unit would be almost all empty workgroups).  Every workgroup reads the per-unit counts
+// and keeps their running sums in LDS; a list index finds its unit by binary search.
+constexpr int PK_THREADS = 1024;  // threads of the migration kernels (one item per workgroup: latency)
 
-hipError_t launch_route(const Geo& g, const Bufs& bf, int layer, int mode, hipStream_t s) {
-    const int units = layer >= 0 ? g.B : g.B * g.L;
-    hipLaunchKernelGGL(k_route_fold, dim3((g.n_acc_max + 255) / 256, units), dim3(256), 0, s, g, bf, layer);
-    const size_t smem = sizeof(RouteSmem);
-    hipLaunchKernelGGL(k_route, dim3(units), dim3(RT_THREADS), smem, s, g, bf, layer, mode);
-    hipLaunchKernelGGL(k_split_blocks, dim3(g.n_splits, units), dim3(SPLIT_BLOCK), 0, s, g, bf, layer);
-    return hipGetLastError();
+__device__ __forceinline__ int64_t mig_unit(const Geo& g, int layer, int ub, int& b) {
+    b = layer >= 0 ? ub : ub / g.L;
+    const int l = layer >= 0 ? layer : ub % g.L;
+    return unit_of(g, b, l);
+}
+// pre[ub] = items of units before ub, pre[n_units] = all items; count(u) = a unit's items.
+// All PK_THREADS threads call.
+template <typename Count>
+__device__ int mig_prefix(const Geo& g, int layer, int n_units, int* pre, int* wtot, Count count) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int per = (n_units + PK_THREADS - 1) / PK_THREADS, u0 = tid * per;
+    int s = 0;
+    for (int k = 0; k < per; ++k) {
+        const int ub = u0 + k;
+        int b;
+        if (ub < n_units) s += count(mig_unit(g, layer, ub, b));
+    }
+    const int incl = (int)wave_scan_incl((unsigned)s);
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    int run = incl - s;
+    for (int q = 0; q < wave; ++q) run += wtot[q];
+    for (int k = 0; k < per; ++k) {
+        const int ub = u0 + k;
+        int b;
+        if (ub < n_units) {
+            pre[ub] = run;
+            run += count(mig_unit(g, layer, ub, b));
+        }
+    }
+    if (tid == PK_THREADS - 1) pre[n_units] = run;
+    __syncthreads();
+    return pre[n_units];
+}
+// the unit of list index i: the last ub with pre[ub] <= i
+__device__ __forceinline__ int mig_find(const int* pre, int n_units, int i) {
+    int lo = 0, hi = n_units - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= i) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
 }
 
 // ------------------------------------------------------------------------------------ pack (INT2 / INT4, once)
@@ -801,108 +915,180 @@ hipError_t launch_route(const Geo& g, const Bufs& bf, int layer, int mode, hipSt
 // off = RD_fp16(min), scl = RU_fp16((max - off)/L), code =
 // #{k in 1..L : 2(x - off) >= (2k-1) scl}, 0 when scl == 0.  All comparisons in
 // fp64, where they are exact for bf16 x and fp16 off/scl.
-constexpr int PK_THREADS = 256;
+//
+// One workgroup per (window, KV head) item: the bf16 keys and values come into LDS in
+// [token][channel] order by 16-byte loads; the parameters are min / max reductions with
+// every thread taking a slice (a key channel's tokens, a value token's channels), combined
+// across lanes; then each thread produces code bytes of the slot, computing the codes of
+// each byte where it is written.  A workgroup of 1024 threads takes one item at a time:
+// a routing event moves few windows, and their latency is what counts.
 constexpr int PK_MAXE = 64 * 128;   // W * d
 
-// #{k in 1..L : t >= (2k - 1) scl} for t = 2(x - off) >= 0: the nearest of the levels
-// 0..L, ties up.  A quotient gives the estimate; exact fp64 comparisons with the
-// thresholds on either side settle it.
-__device__ inline int nearest_level(double t, double scl, int L) {
-    if (scl == 0.0) return 0;
-    int k = (int)floor((t / scl + 1.0) * 0.5);
-    k = k < 0 ? 0 : (k > L ? L : k);
-    while (k < L && t >= (double)(2 * k + 1) * scl) ++k;
-    while (k > 0 && t < (double)(2 * k - 1) * scl) --k;
-    return k;
+// position (token t, channel c) of the element at offset o of a page's key block (lay_k)
+__device__ __forceinline__ void page_k_pos(int o, int D, int W, int& t, int& c) {
+    const int CQ = D / 4, TPC = lay_tpc(W);
+    const int cq = o % CQ;
+    int x = o / CQ;
+    const int tc = x % TPC;
+    x /= TPC;
+    const int qg = x % 4;
+    x /= 4;
+    const int r = x % 16, ch = x / 16;
+    t = (ch * TPC + tc) * 16 + r;
+    c = qg * CQ + cq;
+}
+// the same for a page's value block (lay_v)
+__device__ __forceinline__ void page_v_pos(int o, int D, int W, int& t, int& c) {
+    const int NT = W / 16, MB = D / 16;
+    const int t3 = o & 3;
+    int x = o >> 2;
+    const int cb = x % MB;
+    x /= MB;
+    const int tt = x % NT;
+    x /= NT;
+    const int tq = x % 4, c15 = x / 4;
+    t = tt * 16 + tq * 4 + t3;
+    c = cb * 16 + c15;
+}
+// key code byte B (lay_kc_byte): its token and the channel of its first code; the code at
+// bits b*j (j < 8/b) is that of channel kc_chan(.., j)
+__device__ __forceinline__ void kc_byte_pos(int B, int D, int W, int b, int& t, int& qg, int& cc0) {
+    const int CQ = D / 4, TPC = lay_tpc(W), P = 8 / b, CQP = CQ / P;
+    cc0 = (B % CQP) * P;
+    int x = B / CQP;
+    const int tc = x % TPC;
+    x /= TPC;
+    qg = x % 4;
+    x /= 4;
+    const int r = x % 16, ch = x / 16;
+    t = (ch * TPC + tc) * 16 + r;
+}
+__device__ __forceinline__ int kc_chan(int qg, int cc, int D, bool rope) {   // inverse of lay_kc_pos
+    const int CQ = D / 4;
+    if (!rope) return qg * CQ + cc;
+    return cc < CQ / 2 ? qg * (CQ / 2) + cc : D / 2 + qg * (CQ / 2) + (cc - CQ / 2);
+}
+// value code byte B (lay_vc_byte): its channel and the token of its first code; the code at
+// bits b*j is that of token t0 + j
+__device__ __forceinline__ void vc_byte_pos(int B2, int D, int W, int b, int& t0, int& c) {
+    const int TPC = lay_tpc(W), MB = D / 16, P = 8 / b, Q = 4 / P;
+    const int sub = B2 % Q;
+    int x = B2 / Q;
+    const int tt = x % TPC;
+    x /= TPC;
+    const int cb = x % MB;
+    x /= MB;
+    const int tq = x % 4;
+    x /= 4;
+    const int c15 = x % 16, tch = x / 16;
+    t0 = (tch * TPC + tt) * 16 + tq * 4 + sub * P;
+    c = cb * 16 + c15;
 }
 
-__global__ void __launch_bounds__(PK_THREADS) k_pack(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ kp,
-                                                     const uint16_t* __restrict__ vp) {
-    __shared__ uint16_t sk[PK_MAXE], sv[PK_MAXE];
-    __shared__ uint8_t ck[PK_MAXE], cv[PK_MAXE];
-    __shared__ double p_off[128 + 64], p_scl[128 + 64];   // key channels, then value tokens
-    const int l = layer >= 0 ? layer : blockIdx.x % g.L;
-    const int b = layer >= 0 ? blockIdx.x : blockIdx.x / g.L;
-    const int64_t u = unit_of(g, b, l);
-    UnitHdr* hdr = bf.hdr + u;
-    const int n_items = hdr->n_pack * g.h_kv;
-    const int W = g.W, d = g.d;
-    for (int it = blockIdx.y; it < n_items; it += gridDim.y) {
+// the level of t2 = 2(x - off) >= 0 among 0..L (nearest, ties up): an estimate from the
+// reciprocal of the scale (inv = 0 when scl = 0), settled by exact fp64 comparisons with the
+// thresholds on either side (the estimate is off by at most one: the product carries two
+// roundings).  Branch-free.
+__device__ __forceinline__ int nearest_level(double t2, double scl, double inv, int L) {
+    int k = (int)((t2 * inv + 1.0) * 0.5);
+    k = k > L ? L : k;
+    k += (k < L && t2 >= (double)(2 * k + 1) * scl) ? 1 : 0;
+    k -= (k > 0 && t2 < (double)(2 * k - 1) * scl) ? 1 : 0;
+    return scl == 0.0 ? 0 : k;
+}
+
+// The same launch copies each split's block (header {entries, first entry, -1, 0} and its
+// first SPLIT_BLOCK - 1 accessible-list entries) from the list k_route has rebuilt.
+// W, d, QB: the window, head dimension and code bits (one instance per supported shape, so
+// that the layout arithmetic is shifts and masks)
+template <int W, int d, int QB>
+__global__ void __launch_bounds__(PK_THREADS) k_pack(Geo g, Bufs bf, int layer, int n_units,
+                                                     const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp) {
+    __shared__ __align__(16) uint16_t sk[PK_MAXE];
+    __shared__ __align__(16) uint16_t sv[PK_MAXE];
+    __shared__ double p_off[128 + 64], p_scl[128 + 64], p_inv[128 + 64];   // key channels, then value tokens
+    __shared__ uint16_t p_bits[2 * (128 + 64)];
+    __shared__ int pre[MIG_MAX_UNITS + 1];
+    __shared__ int wtot[PK_THREADS / 64];
+    constexpr int WD = W * d;
+    const int tid = threadIdx.x;
+    const bool rope = (g.flags & QEVICT_F_ROPE) != 0;
+    constexpr int hd = d / 2;
+    const int total = mig_prefix(g, layer, n_units, pre, wtot, [&](int64_t u) { return bf.hdr[u].n_pack * g.h_kv; });
+    // (a barrier opens every item but the first: one closing each item would also wait for
+    // the item's global stores)
+    for (int it_all = blockIdx.x; it_all < total; it_all += gridDim.x) {
+        if (it_all != (int)blockIdx.x) __syncthreads();
+        const int ub = mig_find(pre, n_units, it_all), it = it_all - pre[ub];
+        int b;
+        const int64_t u = mig_unit(g, layer, ub, b);
+        UnitHdr* hdr = bf.hdr + u;
         const PackItem pi = bf.pack[u * g.n_windows + it / g.h_kv];
         const int h = it % g.h_kv;
         const int start = g.n_sink + pi.win * W;
-        const uint16_t *srck, *srcv;
-        if (pi.src_prompt) {
-            srck = kp + (((int64_t)b * g.h_kv + h) * g.S_max + start) * d;
-            srcv = vp + (((int64_t)b * g.h_kv + h) * g.S_max + start) * d;
-        } else {
-            const uint16_t* pg = bf.pages + u * (int64_t)g.n_pages * g.page_elems + (int64_t)pi.src_page * g.page_elems;
-            srck = pg + (int64_t)(2 * h) * W * d;
-            srcv = pg + (int64_t)(2 * h + 1) * W * d;
-        }
-        const bool from_page = !pi.src_prompt;
         if (pi.dst_slot < 0 || (!pi.src_prompt && pi.src_page < 0)) {
-            if (threadIdx.x == 0) atomicOr(&hdr->status, QEVICT_DEV_E_POOL);
+            if (tid == 0) atomicOr(&hdr->status, QEVICT_DEV_E_POOL);
             continue;
         }
-        // staged in batches of SB elements per thread, every load of a batch issued before
-        // the first LDS store (clamped addresses; positions past W*d are not stored)
-        constexpr int SB = 8;
-        for (int e0 = threadIdx.x; e0 < W * d; e0 += SB * PK_THREADS) {
-            uint16_t xk[SB], xv[SB];
-#pragma unroll
-            for (int k = 0; k < SB; ++k) {
-                const int e = min(e0 + k * PK_THREADS, W * d - 1), t = e / d, c = e % d;
-                xk[k] = srck[from_page ? lay_k(t, c, d, W) : e];
-                xv[k] = srcv[from_page ? lay_v(t, c, d, W) : e];
+        // ---- stage keys and values, [token][channel]
+        if (pi.src_prompt) {
+            const uint16_t* srck = kp + (((int64_t)b * g.h_kv + h) * g.S_max + start) * d;
+            const uint16_t* srcv = vp + (((int64_t)b * g.h_kv + h) * g.S_max + start) * d;
+            if ((((uintptr_t)srck | (uintptr_t)srcv) & 15) == 0) {
+                for (int o = 8 * tid; o < WD; o += 8 * PK_THREADS) {
+                    const uint4 xk = *reinterpret_cast<const uint4*>(srck + o);
+                    const uint4 xv = *reinterpret_cast<const uint4*>(srcv + o);
+                    *reinterpret_cast<uint4*>(sk + o) = xk;
+                    *reinterpret_cast<uint4*>(sv + o) = xv;
+                }
+            } else {   // (a caller buffer that is not 16-byte aligned)
+                for (int e = tid; e < WD; e += PK_THREADS) {
+                    sk[e] = srck[e];
+                    sv[e] = srcv[e];
+                }
             }
-            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            const uint16_t* pg = bf.pages + u * (int64_t)g.n_pages * g.page_elems + (int64_t)pi.src_page * g.page_elems;
+            const uint16_t* srck = pg + (int64_t)(2 * h) * WD;
+            const uint16_t* srcv = pg + (int64_t)(2 * h + 1) * WD;
+            for (int o = 8 * tid; o < WD; o += 8 * PK_THREADS) {
+                const uint4 xk = *reinterpret_cast<const uint4*>(srck + o);
+                const uint4 xv = *reinterpret_cast<const uint4*>(srcv + o);
+                int t, c;
+                page_k_pos(o, d, W, t, c);          // 8 consecutive channels of token t
+                *reinterpret_cast<uint4*>(sk + t * d + c) = xk;
+                page_v_pos(o, d, W, t, c);          // tokens t..t+3 of channels c and c + 16
+                const uint32_t w4[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-            for (int k = 0; k < SB; ++k) {
-                const int e = e0 + k * PK_THREADS;
-                if (e < W * d) {
-                    sk[e] = xk[k];
-                    sv[e] = xv[k];
+                for (int j = 0; j < 8; ++j) {
+                    const int tj = t + (j & 3), cj = c + 16 * (j >> 2);
+                    sv[tj * d + cj] = (uint16_t)(w4[j >> 1] >> (16 * (j & 1)));
                 }
             }
         }
         __syncthreads();
         uint8_t* slot = bf.slots + u * (int64_t)g.n_slots * g.slot_bytes + (int64_t)pi.dst_slot * g.slot_bytes +
                         (int64_t)h * g.slot_head_bytes;
-        const int qb = g.qbits, P = 8 / qb, L = (1 << qb) - 1, cbytes = lay_code_bytes(W, d, qb);
-        uint16_t* offK = (uint16_t*)(slot + 2 * cbytes);
+        constexpr int qb = QB, P = 8 / qb, L = (1 << qb) - 1, cbytes = W * d * qb / 8;
+        // the fp16 parameters, in slot order (offK[d], sclK[d], offV[W], sclV[W]), go to LDS
+        // first and to the slot with the codes
+        uint16_t* params16 = (uint16_t*)(slot + 2 * cbytes);
+        uint16_t* offK = p_bits;
         uint16_t* sclK = offK + d;
         uint16_t* offV = sclK + d;
         uint16_t* sclV = offV + W;
-        bool bad = false;
         // keys as quantized: the stored (bf16) values, or in RoPE mode those values turned
         // back to the pre-RoPE domain at their positions (exact products, one rounding)
-        const bool rope = (g.flags & QEVICT_F_ROPE) != 0;
-        const int hd = d / 2;
         auto key_at = [&](int t, int c) -> double {
             if (!rope) return (double)bf16_to_f32(sk[t * d + c]);
             const int i = c < hd ? c : c - hd;
             const float2 cs = bf.rope[(int64_t)(start + t) * hd + i];
-            const double a = (double)bf16_to_f32(sk[t * d + i]), b = (double)bf16_to_f32(sk[t * d + i + hd]);
-            return c < hd ? __dadd_rn(__dmul_rn(a, (double)cs.x), __dmul_rn(b, (double)cs.y))
-                          : __dsub_rn(__dmul_rn(b, (double)cs.x), __dmul_rn(a, (double)cs.y));
+            const double a = (double)bf16_to_f32(sk[t * d + i]), bb = (double)bf16_to_f32(sk[t * d + i + hd]);
+            return c < hd ? __dadd_rn(__dmul_rn(a, (double)cs.x), __dmul_rn(bb, (double)cs.y))
+                          : __dsub_rn(__dmul_rn(bb, (double)cs.x), __dmul_rn(a, (double)cs.y));
         };
-        // parameters: threads [0, d) take a key channel each (over the W tokens), threads
-        // [d, d + W) a value token each (over the d channels)
-        const int tid = threadIdx.x;
-        if (tid < d + W) {
-            const bool key = tid < d;
-            const int gi = key ? tid : tid - d;
-            const int n_el = key ? W : d;
-            auto elem = [&](int i) -> double {
-                return key ? key_at(i, gi) : (double)bf16_to_f32(sv[gi * d + i]);
-            };
-            double mn = elem(0), mx = mn;
-            for (int i = 1; i < n_el; ++i) {
-                const double x = elem(i);
-                mn = fmin(mn, x);
-                mx = fmax(mx, x);
-            }
+        bool bad = false;
+        auto set_params = [&](bool key, int gi, double mn, double mx) {
             if (fabs(mn) > 65504.0 || fabs(mx) > 65504.0) bad = true;
             const double off = fp16_round_down(mn);
             const double scl = fp16_round_up((mx - off) / (double)L);
@@ -914,119 +1100,271 @@ __global__ void __launch_bounds__(PK_THREADS) k_pack(Geo g, Bufs bf, int layer, 
                 offV[lay_vp(gi, W)] = fp16_bits_exact(off);
                 sclV[lay_vp(gi, W)] = fp16_bits_exact(scl);
             }
-            p_off[tid] = off;
-            p_scl[tid] = scl;
+            const int pi_ = key ? gi : d + gi;
+            p_off[pi_] = off;
+            p_scl[pi_] = scl;
+            p_inv[pi_] = scl == 0.0 ? 0.0 : 1.0 / scl;
+        };
+        // ---- key parameters: KT threads per channel, each over W / KT tokens.  bf16 keys: min
+        //      and max in fp32 (exact); RoPE-mode keys are fp64 values
+        {
+            constexpr int KT = PK_THREADS / d, nt = W / KT;
+            const int c = tid / KT, part = tid % KT;
+            double mn, mx;
+            if (!rope) {
+                float fmn = bf16_to_f32(sk[part * nt * d + c]), fmx = fmn;
+                for (int i = 1; i < nt; ++i) {
+                    const float x = bf16_to_f32(sk[(part * nt + i) * d + c]);
+                    fmn = fminf(fmn, x);
+                    fmx = fmaxf(fmx, x);
+                }
+                group_minmax<KT>(fmn, fmx);
+                mn = fmn;
+                mx = fmx;
+            } else {
+                mn = key_at(part * nt, c);
+                mx = mn;
+                for (int i = 1; i < nt; ++i) {
+                    const double x = key_at(part * nt + i, c);
+                    mn = fmin(mn, x);
+                    mx = fmax(mx, x);
+                }
+                for (int m = 1; m < KT; m <<= 1) {
+                    mn = fmin(mn, __shfl_xor(mn, m, 64));
+                    mx = fmax(mx, __shfl_xor(mx, m, 64));
+                }
+            }
+            if (part == 0) set_params(true, c, mn, mx);
         }
-        __syncthreads();
-        // codes: every element on its own thread
-        for (int e = tid; e < W * d; e += PK_THREADS) {
-            const int i = e / d, c = e % d;
-            ck[e] = (uint8_t)nearest_level(2.0 * (key_at(i, c) - p_off[c]), p_scl[c], L);
-            cv[e] = (uint8_t)nearest_level(2.0 * ((double)bf16_to_f32(sv[e]) - p_off[d + i]), p_scl[d + i], L);
+        // ---- value parameters: VT threads per token, each over d / VT channels (fp32, exact)
+        {
+            constexpr int VT = PK_THREADS / W, nc = d / VT;
+            const int t = tid / VT, part = tid % VT;
+            const uint16_t* row = sv + t * d + part * nc;
+            float mn = bf16_to_f32(row[0]), mx = mn;
+            for (int i = 1; i < nc; ++i) {
+                const float x = bf16_to_f32(row[i]);
+                mn = fminf(mn, x);
+                mx = fmaxf(mx, x);
+            }
+            group_minmax<VT>(mn, mx);
+            if (part == 0) set_params(false, t, mn, mx);
         }
         if (bad) atomicOr(&hdr->status, QEVICT_DEV_E_RANGE);
         __syncthreads();
-        // K codes: P consecutive channels of one token per byte (lay_kc_byte)
-        for (int e = threadIdx.x; e < cbytes; e += PK_THREADS) {
-            const int i = e / (d / P), c0 = P * (e % (d / P));
-            uint32_t byte = 0;
-            for (int x = 0; x < P; ++x) byte |= (uint32_t)ck[i * d + c0 + x] << (qb * x);
-            slot[lay_kc_byte(i, c0, d, W, qb, rope)] = (uint8_t)byte;
+        // ---- codes, a key byte (P channels of one token) and a value byte (P tokens of one
+        //      channel) per thread and round
+        for (int B = tid; B < cbytes; B += PK_THREADS) {
+            int t, qg, cc0;
+            kc_byte_pos(B, d, W, qb, t, qg, cc0);
+            uint32_t bk = 0, bv = 0;
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                const int c = kc_chan(qg, cc0 + j, d, rope);
+                bk |= (uint32_t)nearest_level(2.0 * (key_at(t, c) - p_off[c]), p_scl[c], p_inv[c], L) << (qb * j);
+            }
+            int t0, c;
+            vc_byte_pos(B, d, W, qb, t0, c);
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                const int tt = t0 + j;
+                const double x = (double)bf16_to_f32(sv[tt * d + c]);
+                bv |= (uint32_t)nearest_level(2.0 * (x - p_off[d + tt]), p_scl[d + tt], p_inv[d + tt], L) << (qb * j);
+            }
+            slot[B] = (uint8_t)bk;
+            slot[cbytes + B] = (uint8_t)bv;
         }
-        // V codes: one byte = P consecutive tokens of one channel (lay_vc_byte)
-        for (int e = threadIdx.x; e < cbytes; e += PK_THREADS) {
-            const int c = e % d, t0 = P * (e / d);
-            uint32_t byte = 0;
-            for (int x = 0; x < P; ++x) byte |= (uint32_t)cv[(t0 + x) * d + c] << (qb * x);
-            slot[cbytes + lay_vc_byte(t0, c, d, W, qb)] = (uint8_t)byte;
+        for (int i = tid; i < 2 * (d + W); i += PK_THREADS) params16[i] = p_bits[i];
+    }
+    // ---- split blocks (after the items: no barrier follows these stores)
+    {   // two blocks per thread and round, their loads issued together
+        constexpr int PER = PK_THREADS / SPLIT_BLOCK;
+        const int n_blk = n_units * g.n_splits, x = tid % SPLIT_BLOCK, stride = gridDim.x * PER;
+        for (int k0 = blockIdx.x * PER + tid / SPLIT_BLOCK; k0 < n_blk; k0 += 2 * stride) {
+            int64_t uu[2];
+            int ss[2], e0[2], cnt[2];
+            bool ok[2];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int k = k0 + r * stride;
+                ok[r] = k < n_blk;
+                int b;
+                uu[r] = mig_unit(g, layer, ok[r] ? k / g.n_splits : 0, b);
+                ss[r] = k % g.n_splits;
+                const int32_t* splits = bf.splits + uu[r] * (g.n_splits + 1);
+                e0[r] = ok[r] ? splits[ss[r]] : 0;
+                cnt[r] = ok[r] ? splits[ss[r] + 1] - e0[r] : 0;
+            }
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                if (!ok[r]) continue;
+                AccEntry v = AccEntry{EK_PAGE, -1, -1, 0};
+                if (x == 0) v = AccEntry{cnt[r], e0[r], -1, 0};
+                else if (x - 1 < cnt[r]) v = bf.acc[uu[r] * g.n_acc_max + e0[r] + x - 1];
+                bf.split_blk[(uu[r] * g.n_splits + ss[r]) * SPLIT_BLOCK + x] = v;
+            }
         }
-        __syncthreads();
     }
 }
 
 // ------------------------------------------------------------------------------------ fill (promote / copy)
 // Promotion writes bf16(off + code*scl), rounded once from the exact fp64 value
 // (§4.3: promotion reconstructs the same low-bit approximation in the execution
-// datatype).  Prefill copies prompt tokens into pages.
-__global__ void __launch_bounds__(PK_THREADS) k_fill(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ kp,
-                                                     const uint16_t* __restrict__ vp) {
-    const int l = layer >= 0 ? layer : blockIdx.x % g.L;
-    const int b = layer >= 0 ? blockIdx.x : blockIdx.x / g.L;
-    const int64_t u = unit_of(g, b, l);
-    UnitHdr* hdr = bf.hdr + u;
-    const int n_items = hdr->n_fill * g.h_kv;
-    const int W = g.W, d = g.d;
-    const int S = hdr->prompt_len;
-    for (int it = blockIdx.y; it < n_items; it += gridDim.y) {
+// datatype).  Prefill copies prompt tokens into pages.  One workgroup per (window, KV
+// head) item; the slot comes into LDS by 32-bit loads, and every thread writes whole
+// 16-byte runs of the page (8 consecutive elements of its key / value block).
+template <int W, int d, int QB>
+__global__ void __launch_bounds__(PK_THREADS) k_fill(Geo g, Bufs bf, int layer, int n_units,
+                                                     const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp) {
+    constexpr int MAXW = (2 * PK_MAXE / 2 + 4 * (128 + 64)) / 4;   // slot head words at W*d = 8192, INT4
+    __shared__ uint32_t sw[MAXW];
+    __shared__ int pre[MIG_MAX_UNITS + 1];
+    __shared__ int wtot[PK_THREADS / 64];
+    constexpr int WD = W * d;
+    const int tid = threadIdx.x;
+    const int total = mig_prefix(g, layer, n_units, pre, wtot, [&](int64_t u) { return bf.hdr[u].n_fill * g.h_kv; });
+    for (int it_all = blockIdx.x; it_all < total; it_all += gridDim.x) {
+        if (it_all != (int)blockIdx.x) __syncthreads();   // (sw is restaged: the previous item's reads are done)
+        const int ub = mig_find(pre, n_units, it_all), it = it_all - pre[ub];
+        int b;
+        const int64_t u = mig_unit(g, layer, ub, b);
+        UnitHdr* hdr = bf.hdr + u;
+        const int S = hdr->prompt_len;
         const FillItem fi = bf.fill[u * g.n_windows + it / g.h_kv];
         const int h = it % g.h_kv;
         if (fi.dst_page < 0) {
-            if (threadIdx.x == 0) atomicOr(&hdr->status, QEVICT_DEV_E_POOL);
+            if (tid == 0) atomicOr(&hdr->status, QEVICT_DEV_E_POOL);
             continue;
         }
         uint16_t* pg = bf.pages + u * (int64_t)g.n_pages * g.page_elems + (int64_t)fi.dst_page * g.page_elems;
-        uint16_t* dk = pg + (int64_t)(2 * h) * W * d;
-        uint16_t* dv = pg + (int64_t)(2 * h + 1) * W * d;
+        uint16_t* dk = pg + (int64_t)(2 * h) * WD;
+        uint16_t* dv = pg + (int64_t)(2 * h + 1) * WD;
         const int start = g.n_sink + fi.win * W;
         if (fi.src_slot >= 0) {
             const uint8_t* slot = bf.slots + u * (int64_t)g.n_slots * g.slot_bytes +
                                   (int64_t)fi.src_slot * g.slot_bytes + (int64_t)h * g.slot_head_bytes;
-            const int qb = g.qbits, mask = (1 << qb) - 1, cbytes = lay_code_bytes(W, d, qb);
-            const uint16_t* offK = (const uint16_t*)(slot + 2 * cbytes);
+            constexpr int qb = QB, mask = (1 << qb) - 1, cbytes = W * d * qb / 8;
+            const int nw = (2 * cbytes + 4 * (d + W)) / 4;
+            for (int q = tid; q < nw; q += PK_THREADS) sw[q] = reinterpret_cast<const uint32_t*>(slot)[q];
+            __syncthreads();
+            const uint8_t* sb = reinterpret_cast<const uint8_t*>(sw);
+            const uint16_t* offK = reinterpret_cast<const uint16_t*>(sb + 2 * cbytes);
             const uint16_t* sclK = offK + d;
             const uint16_t* offV = sclK + d;
             const uint16_t* sclV = offV + W;
             const bool rope = (g.flags & QEVICT_F_ROPE) != 0;
-            const int hd = d / 2;
+            constexpr int hd = d / 2;
             auto khat = [&](int i, int c) -> double {   // dequantized key (exact in fp64)
-                const int kc = (slot[lay_kc_byte(i, c, d, W, qb, rope)] >> lay_kc_shift(c, qb)) & mask;
+                const int kc = (sb[lay_kc_byte(i, c, d, W, qb, rope)] >> lay_kc_shift(c, qb)) & mask;
                 return (double)fp16_bits_to_f32(offK[c]) + kc * (double)fp16_bits_to_f32(sclK[c]);
             };
-            for (int e = threadIdx.x; e < W * d; e += PK_THREADS) {
-                const int i = e / d, c = e % d;
-                const int vc = (slot[cbytes + lay_vc_byte(i, c, d, W, qb)] >> lay_vc_shift(i, qb)) & mask;
-                const int vp = lay_vp(i, W);
-                double kx = khat(i, c);
-                if (rope) {   // RoPE re-applied at the window's positions, then one bf16 rounding
-                    const int pi = c < hd ? c : c - hd;
-                    const float2 cs = bf.rope[(int64_t)(start + i) * hd + pi];
-                    const double xp = khat(i, c < hd ? c + hd : c - hd);
-                    kx = c < hd ? __dsub_rn(__dmul_rn(kx, (double)cs.x), __dmul_rn(xp, (double)cs.y))
-                                : __dadd_rn(__dmul_rn(kx, (double)cs.x), __dmul_rn(xp, (double)cs.y));
+            for (int vi = tid; vi < 2 * WD / 8; vi += PK_THREADS) {   // key runs, then value runs
+                const bool is_v = vi >= WD / 8;
+                const int o = 8 * (is_v ? vi - WD / 8 : vi);
+                int t, c;
+                uint16_t r[8];
+                if (!is_v) {
+                    page_k_pos(o, d, W, t, c);          // 8 consecutive channels of token t
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int cj = c + j;
+                        double kx = khat(t, cj);
+                        if (rope) {   // RoPE re-applied at the window's positions, then one bf16 rounding
+                            const int pi = cj < hd ? cj : cj - hd;
+                            const float2 cs = bf.rope[(int64_t)(start + t) * hd + pi];
+                            const double xp = khat(t, cj < hd ? cj + hd : cj - hd);
+                            kx = cj < hd ? __dsub_rn(__dmul_rn(kx, (double)cs.x), __dmul_rn(xp, (double)cs.y))
+                                         : __dadd_rn(__dmul_rn(kx, (double)cs.x), __dmul_rn(xp, (double)cs.y));
+                        }
+                        r[j] = f64_to_bf16(kx);
+                    }
+                } else {
+                    page_v_pos(o, d, W, t, c);          // tokens t..t+3 of channels c and c + 16
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int tj = t + (j & 3), cj = c + 16 * (j >> 2);
+                        const int vc = (sb[cbytes + lay_vc_byte(tj, cj, d, W, qb)] >> lay_vc_shift(tj, qb)) & mask;
+                        const int vpp = lay_vp(tj, W);
+                        r[j] = f64_to_bf16((double)fp16_bits_to_f32(offV[vpp]) + vc * (double)fp16_bits_to_f32(sclV[vpp]));
+                    }
                 }
-                const double vx = (double)fp16_bits_to_f32(offV[vp]) + vc * (double)fp16_bits_to_f32(sclV[vp]);
-                dk[lay_k(i, c, d, W)] = f64_to_bf16(kx);
-                dv[lay_v(i, c, d, W)] = f64_to_bf16(vx);
+                *reinterpret_cast<uint4*>((is_v ? dv : dk) + o) =
+                    make_uint4((uint32_t)r[0] | ((uint32_t)r[1] << 16), (uint32_t)r[2] | ((uint32_t)r[3] << 16),
+                               (uint32_t)r[4] | ((uint32_t)r[5] << 16), (uint32_t)r[6] | ((uint32_t)r[7] << 16));
             }
         } else if (fi.src_slot == -1) {
             const uint16_t* sk = kp + (((int64_t)b * g.h_kv + h) * g.S_max + start) * d;
             const uint16_t* sv = vp + (((int64_t)b * g.h_kv + h) * g.S_max + start) * d;
             int ntok = S - start;
             if (ntok > W) ntok = W;
-            for (int e = threadIdx.x; e < W * d; e += PK_THREADS) {
-                const int i = e / d, c = e % d;
-                dk[lay_k(i, c, d, W)] = i < ntok ? sk[e] : (uint16_t)0;
-                dv[lay_v(i, c, d, W)] = i < ntok ? sv[e] : (uint16_t)0;
+            for (int o = 8 * tid; o < WD; o += 8 * PK_THREADS) {
+                int t, c;
+                page_k_pos(o, d, W, t, c);
+                uint16_t xk[8], xv[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) xk[j] = t < ntok ? sk[t * d + c + j] : (uint16_t)0;
+                page_v_pos(o, d, W, t, c);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int tj = t + (j & 3), cj = c + 16 * (j >> 2);
+                    xv[j] = tj < ntok ? sv[tj * d + cj] : (uint16_t)0;
+                }
+                uint32_t pk[4], pv[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pk[j] = (uint32_t)xk[2 * j] | ((uint32_t)xk[2 * j + 1] << 16);
+                    pv[j] = (uint32_t)xv[2 * j] | ((uint32_t)xv[2 * j + 1] << 16);
+                }
+                *reinterpret_cast<uint4*>(dk + o) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+                *reinterpret_cast<uint4*>(dv + o) = make_uint4(pv[0], pv[1], pv[2], pv[3]);
             }
         } else {
-            for (int e = threadIdx.x; e < W * d; e += PK_THREADS) {
-                dk[e] = 0;
-                dv[e] = 0;
+            for (int o = 8 * tid; o < WD; o += 8 * PK_THREADS) {
+                *reinterpret_cast<uint4*>(dk + o) = make_uint4(0, 0, 0, 0);
+                *reinterpret_cast<uint4*>(dv + o) = make_uint4(0, 0, 0, 0);
             }
         }
     }
 }
 
-hipError_t launch_migrate(const Geo& g, const Bufs& bf, int layer, const uint16_t* kp, const uint16_t* vp,
-                          hipStream_t s) {
+template <int W, int d, int QB>
+static void launch_mig_t(dim3 grid, const Geo& g, const Bufs& bf, int layer, int units, const uint16_t* kp,
+                         const uint16_t* vp, hipStream_t s) {
+    hipLaunchKernelGGL((k_pack<W, d, QB>), grid, dim3(PK_THREADS), 0, s, g, bf, layer, units, kp, vp);
+    hipLaunchKernelGGL((k_fill<W, d, QB>), grid, dim3(PK_THREADS), 0, s, g, bf, layer, units, kp, vp);
+}
+template <int W, int d>
+static void launch_mig_q(dim3 grid, const Geo& g, const Bufs& bf, int layer, int units, const uint16_t* kp,
+                         const uint16_t* vp, hipStream_t s) {
+    if (g.qbits == 4) launch_mig_t<W, d, 4>(grid, g, bf, layer, units, kp, vp, s);
+    else launch_mig_t<W, d, 2>(grid, g, bf, layer, units, kp, vp, s);
+}
+template <int W>
+static void launch_mig_d(dim3 grid, const Geo& g, const Bufs& bf, int layer, int units, const uint16_t* kp,
+                         const uint16_t* vp, hipStream_t s) {
+    if (g.d == 64) launch_mig_q<W, 64>(grid, g, bf, layer, units, kp, vp, s);
+    else launch_mig_q<W, 128>(grid, g, bf, layer, units, kp, vp, s);
+}
+// (the shapes the configuration accepts: W 16 / 32 / 64, d 64 / 128, 2 / 4 code bits)
+static void launch_mig(dim3 grid, const Geo& g, const Bufs& bf, int layer, int units, const uint16_t* kp,
+                       const uint16_t* vp, hipStream_t s) {
+    if (g.W == 16) launch_mig_d<16>(grid, g, bf, layer, units, kp, vp, s);
+    else if (g.W == 32) launch_mig_d<32>(grid, g, bf, layer, units, kp, vp, s);
+    else launch_mig_d<64>(grid, g, bf, layer, units, kp, vp, s);
+}
+
+// Routing (every unit of the layer, or of all layers with layer = -1) and the migrations it
+// decides: k_route, then k_pack (with the split blocks of the new list), then k_fill (a
+// page freed by a demotion at this event may take a promotion: the pack reads it first).
+hipError_t launch_route(const Geo& g, const Bufs& bf, int layer, int mode, const uint16_t* kp, const uint16_t* vp,
+                        hipStream_t s) {
     const int units = layer >= 0 ? g.B : g.B * g.L;
-    // workgroups per unit: a prefill (one layer, every prompt window) spreads its items over
-    // about 1024 workgroups in all; a routing event over all layers moves few per unit
-    const int nb = layer >= 0 ? std::max(64, 1024 / std::max(g.B, 1)) : 64;
-    hipLaunchKernelGGL(k_pack, dim3(units, nb), dim3(PK_THREADS), 0, s, g, bf, layer, kp, vp);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_fill, dim3(units, nb), dim3(PK_THREADS), 0, s, g, bf, layer, kp, vp);
+    if (units > MIG_MAX_UNITS) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_route, dim3(units), dim3(RT_THREADS), sizeof(RouteSmem), s, g, bf, layer, mode);
+    // workgroups: a prefill (one layer, every prompt window) spreads its items over 1024;
+    // a routing event moves a few windows per unit
+    const int nb = layer >= 0 ? 1024 : std::min(1024, std::max(256, 8 * units));
+    launch_mig(dim3(nb), g, bf, layer, units, kp, vp, s);
     return hipGetLastError();
 }
 
