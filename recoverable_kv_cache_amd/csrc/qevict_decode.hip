@@ -66,18 +66,12 @@ __device__ __forceinline__ float mul_h_lo(float x, uint32_t w) {
 __device__ __forceinline__ float mul_h_hi(float x, uint32_t w) {
     return fmaf(x, (float)__builtin_bit_cast(h2_t, w).y, 0.0f);
 }
-// maxima of operands that are never NaN (scores, -inf included): the plain instructions,
-// without the quieting that fmaxf adds for signalling NaNs
-__device__ __forceinline__ float max2(float a, float b) {
-    float r;
-    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-    return r;
-}
-__device__ __forceinline__ float max3(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
+// maxima of operands that are never NaN (scores, -inf included), through compiler builtins
+// (no inline assembly: the backend tracks the hazards with the lane permutes around them).
+// max2 is the median of (a, b, +inf): one v_med3_f32, where fmaxf would first quiet
+// operands that come from lane moves.
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max3(float a, float b, float c) { return max2(max2(a, b), c); }
 // two fp32 -> packed bf16 pair, round to nearest even
 __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
     const f2_t v = {a, b};
