@@ -210,6 +210,8 @@ qevict_status qevict_decode_attn(qevict_state* st, int32_t layer, const void* q,
 qevict_status qevict_route(qevict_state* st, int32_t layer, void* stream);
 
 /*
+ * [QEvict] §4.3 and Algorithm 1 (the demotion steps of the migration: Full or aged
+ * recent -> Quantized, the ledger written once and reactivated later).
  * Demote chosen windows to the Quantized tier (first time: pack INT2 codes and
  * create the ledger; dormant ledger: reactivate) and release their bf16 pages.
  * win_ids [B][n] int32 device array, -1 = unused entry; windows must be Full
@@ -271,15 +273,6 @@ qevict_status qevict_time_next_decode(qevict_state* st, void* ev_before, void* e
 qevict_status qevict_step_bytes(qevict_state* st, int32_t layer, int64_t* kv_bytes, int64_t* io_bytes,
                                 void* stream);
 
-/* Measurement aid, not part of the method: one launch of a plain streaming read of
- * `bytes` bytes at device address buf (bytes a positive multiple of 1024 below 2^31,
- * buf 16-byte aligned), every byte read once with 16-byte loads over 1024 workgroups of
- * 256 threads, for comparison with the split-K kernel's achieved bandwidth.  sink
- * (device, 1024 uint32, caller-owned) receives the XOR of the 32-bit words each
- * workgroup read; the XOR of all 1024 equals that of the buffer's words.  With
- * ev_before / ev_after (hipEvent_t with timing; both or neither) the kernel's own
- * dispatch stamps its start and end, as for qevict_time_next_decode.  Enqueues on
- * `stream`; argument errors return QEVICT_E_INVALID before anything is enqueued. */
 /* Diagnostics ([QEvict] Appendix I, Eqs. 12-13): per-head attention mass of the last
  * decode step of (layer, sequence b) on the sinks and on each window.
  *   out [h_q][n_windows + 1] fp64, device: column 0 the sinks, column 1 + w window w
@@ -297,6 +290,15 @@ qevict_status qevict_step_mass(qevict_state* st, int32_t layer, int32_t b, doubl
  * QEVICT_E_INVALID for a null or short table. */
 qevict_status qevict_set_rope(qevict_state* st, const float* cos_sin, int32_t n_pos, void* stream);
 
+/* Measurement aid, not part of the method: one launch of a plain streaming read of
+ * `bytes` bytes at device address buf (bytes a positive multiple of 1024 below 2^31,
+ * buf 16-byte aligned), every byte read once with 16-byte loads over 1024 workgroups of
+ * 256 threads, for comparison with the split-K kernel's achieved bandwidth.  sink
+ * (device, 1024 uint32, caller-owned) receives the XOR of the 32-bit words each
+ * workgroup read; the XOR of all 1024 equals that of the buffer's words.  With
+ * ev_before / ev_after (hipEvent_t with timing; both or neither) the kernel's own
+ * dispatch stamps its start and end, as for qevict_time_next_decode.  Enqueues on
+ * `stream`; argument errors return QEVICT_E_INVALID before anything is enqueued. */
 qevict_status qevict_stream_read(const void* buf, size_t bytes, void* sink, void* ev_before, void* ev_after,
                                  void* stream);
 

@@ -219,6 +219,27 @@ Bufs bind_bufs(const Layout& lay, void* arena) {
 
 }  // namespace
 
+namespace qv {
+// prefill workspace: row log-sum-exps fp32 [B][h_q][S_max], column sums fp64 [B][h_q][S_max]
+size_t prefill_ws_bytes(const Geo& g) {
+    const size_t n = (size_t)g.B * g.h_q * g.S_max;
+    size_t at = ((n * 4 + 255) & ~size_t(255)) + ((n * 8 + 255) & ~size_t(255));
+    if (g.n_rope) at += rope_ws_bytes(g);
+    return at;
+}
+
+// the RoPE-mode prompt copies in the workspace: queries [B][h_q][S_max][d], then keys
+// [B][h_kv][S_max][d] (bf16, rotated)
+size_t rope_ws_offset(const Geo& g) {
+    const size_t n = (size_t)g.B * g.h_q * g.S_max;
+    return ((n * 4 + 255) & ~size_t(255)) + ((n * 8 + 255) & ~size_t(255));
+}
+size_t rope_ws_bytes(const Geo& g) {
+    const size_t nq = (size_t)g.B * g.h_q * g.S_max * g.d * 2, nk = (size_t)g.B * g.h_kv * g.S_max * g.d * 2;
+    return ((nq + 255) & ~size_t(255)) + ((nk + 255) & ~size_t(255));
+}
+}  // namespace qv
+
 struct qevict_state {
     qevict_config cfg;
     Layout lay;
@@ -545,6 +566,12 @@ qevict_status qevict_export_unit(qevict_state* st, int32_t layer, int32_t b, voi
         HIP_TRY(hipMemcpy(acc.data(), st->bf.acc + u * g.n_acc_max, n_acc * sizeof(AccEntry), hipMemcpyDeviceToHost));
     HIP_TRY(hipMemcpy(splits.data(), st->bf.splits + u * (g.n_splits + 1), splits.size() * 4, hipMemcpyDeviceToHost));
 
+    // the records index the host copies of the pools below: a page or slot id outside its pool
+    // (a device state that no kernel of this library writes) is reported, not followed
+    for (int w = 0; w < g.n_windows; ++w)
+        if (win[w].page < -1 || win[w].page >= g.n_pages || win[w].slot < -1 || win[w].slot >= g.n_slots)
+            return fail(QEVICT_E_STATE, "device state of layer %d, sequence %d: window %d names page %d / slot %d",
+                        layer, b, w, win[w].page, win[w].slot);
     char* o = (char*)host_buf;
     size_t at = 0;
     auto put = [&](const void* p, size_t nb) {

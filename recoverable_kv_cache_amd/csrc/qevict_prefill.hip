@@ -371,24 +371,6 @@ __global__ void __launch_bounds__(256) k_prefill_keynorm(Geo g, Bufs bf, int lay
     }
 }
 
-size_t prefill_ws_bytes(const Geo& g) {
-    const size_t n = (size_t)g.B * g.h_q * g.S_max;
-    size_t at = ((n * 4 + 255) & ~size_t(255)) + ((n * 8 + 255) & ~size_t(255));
-    if (g.n_rope) at += rope_ws_bytes(g);
-    return at;
-}
-
-// the RoPE-mode prompt copies in the workspace: queries [B][h_q][S_max][d], then keys
-// [B][h_kv][S_max][d] (bf16, rotated)
-size_t rope_ws_offset(const Geo& g) {
-    const size_t n = (size_t)g.B * g.h_q * g.S_max;
-    return ((n * 4 + 255) & ~size_t(255)) + ((n * 8 + 255) & ~size_t(255));
-}
-size_t rope_ws_bytes(const Geo& g) {
-    const size_t nq = (size_t)g.B * g.h_q * g.S_max * g.d * 2, nk = (size_t)g.B * g.h_kv * g.S_max * g.d * 2;
-    return ((nq + 255) & ~size_t(255)) + ((nk + 255) & ~size_t(255));
-}
-
 // RoPE of a prompt tensor [B][H][S_max][d] (bf16 in, bf16 out): each thread turns one
 // channel pair (i, i + d/2) of one position, exactly in fp64, rounded once to bf16.
 __global__ void __launch_bounds__(256) k_rope_prompt(Geo g, Bufs bf, const uint16_t* __restrict__ x,
