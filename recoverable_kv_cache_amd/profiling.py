@@ -3,12 +3,15 @@
     python -m recoverable_kv_cache_amd.profiling trace  <run_kernel_stats.csv> <out.md> "<command>"
     python -m recoverable_kv_cache_amd.profiling traffic <fetch_dir> <write_dir> <copy_fetch_dir> <copy_write_dir> \
         <kernel substring> <workload> <out.json> <out.md> "<commands>"
+    python -m recoverable_kv_cache_amd.profiling sq <out.md> <kernel substring> <workload> "<commands>" <dir> [<dir> ...]
 
 ``trace`` tabulates per-kernel calls and durations.  ``traffic`` turns the
 ``FETCH_SIZE`` / ``WRITE_SIZE`` counters (KiB per dispatch) of the decode split
 kernel into HBM bytes per launch, each scaled by what the same counter reads for
 a plain 1 GiB device copy (read 1 GiB, write 1 GiB), and records the hash of the
 kernel sources so that ``bench.py`` only reports it while the kernel is unchanged.
+``sq`` tabulates shader-sequencer counters of that kernel (one pass per directory, at most
+8 SQ counters each), per dispatch, with the ratios read from them.
 """
 from __future__ import annotations
 
@@ -95,10 +98,63 @@ def traffic_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, kernel_sub, wo
         fo.write("Commands:\n\n" + "\n".join(f"    {c}" for c in commands.split(" ;; ")) + "\n")
 
 
+def _counters(d: str, kernel_sub: str) -> dict[str, list[float]]:
+    per: dict[str, dict[str, float]] = {}
+    for r in _rows(d, "counter_collection.csv"):
+        name = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
+        if kernel_sub not in name:
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id") or "0"
+        c = r.get("Counter_Name")
+        per.setdefault(c, {})
+        per[c][key] = per[c].get(key, 0.0) + float(r["Counter_Value"])
+    return {c: list(v.values()) for c, v in per.items()}
+
+
+def sq_summary(out_md: str, kernel_sub: str, workload: str, commands: str, *dirs: str) -> None:
+    vals: dict[str, float] = {}
+    n_disp: dict[str, int] = {}
+    for d in dirs:
+        for c, v in _counters(d, kernel_sub).items():
+            vals[c] = statistics.mean(v)
+            n_disp[c] = len(v)
+    if not vals:
+        raise SystemExit("no counters of " + kernel_sub)
+    lines = [f"# Shader-sequencer counters of `{kernel_sub}` ({workload})", "",
+             "rocprofv3 `--pmc`, one pass per group of counters; means per dispatch (sums over the chip).", "",
+             "| counter | per dispatch | dispatches |", "|---|---:|---:|"]
+    for c in sorted(vals):
+        lines.append(f"| {c} | {vals[c]:,.0f} | {n_disp[c]} |")
+    g = vals.get
+    ratios = []
+    if g("SQ_WAVES"):
+        for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SMEM"):
+            if g(c) is not None:
+                ratios.append((f"{c} per wave", g(c) / g("SQ_WAVES")))
+    if g("SQ_WAVE_CYCLES") and g("SQ_WAVES"):
+        ratios.append(("wave lifetime, cycles (SQ_WAVE_CYCLES / SQ_WAVES)", g("SQ_WAVE_CYCLES") / g("SQ_WAVES")))
+    if g("SQ_WAVE_CYCLES"):
+        for c in ("SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM",
+                  "SQ_ACTIVE_INST_ANY"):
+            if g(c) is not None:
+                ratios.append((f"{c} / SQ_WAVE_CYCLES", g(c) / g("SQ_WAVE_CYCLES")))
+    if g("SQ_BUSY_CYCLES") and g("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
+        ratios.append(("SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CYCLES", g("SQ_VALU_MFMA_BUSY_CYCLES") / g("SQ_BUSY_CYCLES")))
+    if g("SQ_INSTS_LDS") and g("SQ_LDS_BANK_CONFLICT") is not None:
+        ratios.append(("SQ_LDS_BANK_CONFLICT cycles per LDS instruction", g("SQ_LDS_BANK_CONFLICT") / g("SQ_INSTS_LDS")))
+    if ratios:
+        lines += ["", "| ratio | value |", "|---|---:|"] + [f"| {k} | {v:.3f} |" for k, v in ratios]
+    lines += ["", "Commands:", ""] + [f"    {c}" for c in commands.split(" ;; ")]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "trace":
         trace_summary(sys.argv[2], sys.argv[3], sys.argv[4])
     elif sys.argv[1] == "traffic":
         traffic_summary(*sys.argv[2:11])
+    elif sys.argv[1] == "sq":
+        sq_summary(*sys.argv[2:])
     else:
         raise SystemExit(__doc__)
