@@ -818,6 +818,19 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
                 }
             }
         }
+        if (16 * (j.t + 1) > j.ntok) {
+            // a tile past the block's last token: its rows beyond hold whatever the page held
+            // before (a fresh page is not cleared), so their values are zeroed (their
+            // probabilities are 0, and 0 * NaN would not be)
+            const int r0 = 16 * j.t + 4 * qg;
+            const uint32_t m0 = (r0 < j.ntok ? 0x0000FFFFu : 0u) | (r0 + 1 < j.ntok ? 0xFFFF0000u : 0u);
+            const uint32_t m1 = (r0 + 2 < j.ntok ? 0x0000FFFFu : 0u) | (r0 + 3 < j.ntok ? 0xFFFF0000u : 0u);
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+                vw[2 * m] &= m0;
+                vw[2 * m + 1] &= m1;
+            }
+        }
         f4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) d = mfma32(u4_t{kw[4 * ks], kw[4 * ks + 1], kw[4 * ks + 2], kw[4 * ks + 3]}, bq[ks], d);

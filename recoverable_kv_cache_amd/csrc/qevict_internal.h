@@ -45,7 +45,7 @@ struct PackItem {    // quantize a window once: source bf16 -> slot
 struct FillItem {    // write a bf16 page: promote from a slot, or copy from the prompt
     int32_t win;
     int32_t dst_page;
-    int32_t src_slot;    // >= 0: promote (dequantize); -1: copy prompt tokens; -2: zero page
+    int32_t src_slot;    // >= 0: promote (dequantize); -1: copy prompt tokens
     int32_t pad;
 };
 

@@ -344,3 +344,48 @@ def test_combined_flags_int4_rope_pnorm_one_way():
     assert sum(e["promoted"] for e in unit.events) == 0
     assert any(W.ledger is not None and W.ledger.bits == 4 for W in unit.win.values())
     _print(f"combined: max o err {ls.max_o_err:.2e} (bf16 reading {ls.max_o_err_bf16:.2e}, gap {ls.max_reading_gap:.2e}), max score err {ls.max_s_err:.2e}, events {ls.events}")
+
+
+def _selection_scores(kind: str, n: int) -> torch.Tensor:
+    """Initial window scores that stress the router's tier selection (radix select over the
+    composite key of score and window index)."""
+    g = torch.Generator().manual_seed(7)
+    if kind == "all_equal":          # every key ties: the window index decides
+        s = torch.full((n,), 0.5, dtype=torch.float64)
+    elif kind == "two_values":
+        s = torch.where(torch.arange(n) % 3 == 0, 2.0, 1.0).to(torch.float64)
+    elif kind == "ulp_apart":        # keys that differ only in their last mantissa bits
+        s = torch.from_numpy(1.0 + (np.arange(n) % 7) * np.finfo(np.float64).eps)
+        s = s[torch.randperm(n, generator=g)]
+    elif kind == "signed_zeros":     # negative keys, +0 and -0 (which tie), positive keys
+        v = torch.randn(n, generator=g, dtype=torch.float64)
+        v[::5] = 0.0
+        v[1::5] = -0.0
+        s = v
+    elif kind == "wide_range":       # from subnormals to 1e300
+        e = torch.randint(-320, 300, (n,), generator=g).to(torch.float64)
+        s = torch.pow(torch.tensor(10.0, dtype=torch.float64), e)
+    else:
+        raise ValueError(kind)
+    return s
+
+
+@pytest.mark.parametrize("kind", ["all_equal", "two_values", "ulp_apart", "signed_zeros", "wide_range"])
+@pytest.mark.parametrize("one_way", [False, True], ids=["two-way", "one-way"])
+def test_tier_selection_edge_cases(kind, one_way):
+    """The prefill routing of 4K-token prompts (about 250 candidates per unit, more than one
+    selection pass) with initial scores built to stress the radix selection: the tier sets
+    bit-exact against the oracle's full sort, then two routing events."""
+    _print(f"case: tier selection {kind} one_way={one_way}")
+    wl = WL.Workload("selection", 1, 2, 4, 1, 64, 4096, 16, 16, 4, 64, 8, 0.40, 0.70, n_outlier=2)
+    n_win = (wl.prompt_len - wl.n_sink + wl.window - 1) // wl.window
+    si = torch.stack([_selection_scores(kind, n_win), _selection_scores(kind, n_win).flip(0)])
+    flags = B.QEVICT_F_NO_PROMOTE if one_way else 0
+    ls = Lockstep(wl, score_init=si, flags=flags)
+    ls.prefill()
+    # (later events depend on mass sums that the two sides round differently; where initial
+    # keys tie or sit an ulp apart, only the prefill routing is a fair exact comparison)
+    if kind in ("two_values", "signed_zeros", "wide_range"):
+        for j in range(16):
+            ls.step(j, check_every=8)
+    _print(f"selection {kind}: events {ls.events}")
