@@ -111,6 +111,17 @@ def _counters(d: str, kernel_sub: str) -> dict[str, list[float]]:
     return {c: list(v.values()) for c, v in per.items()}
 
 
+def _gpu_units(d: str) -> tuple[int, int]:
+    """(SIMDs, shader engines) of the GPU agent, from the run's agent_info.csv (0, 0 if absent)."""
+    try:
+        for r in _rows(d, "agent_info.csv"):
+            if int(r.get("Simd_Count") or 0) > 0:
+                return int(r["Simd_Count"]), int(r.get("Num_Shader_Banks") or 0)
+    except FileNotFoundError:
+        pass
+    return 0, 0
+
+
 def sq_summary(out_md: str, kernel_sub: str, workload: str, commands: str, *dirs: str) -> None:
     vals: dict[str, float] = {}
     n_disp: dict[str, int] = {}
@@ -121,25 +132,34 @@ def sq_summary(out_md: str, kernel_sub: str, workload: str, commands: str, *dirs
     if not vals:
         raise SystemExit("no counters of " + kernel_sub)
     lines = [f"# Shader-sequencer counters of `{kernel_sub}` ({workload})", "",
-             "rocprofv3 `--pmc`, one pass per group of counters; means per dispatch (sums over the chip).", "",
+             "rocprofv3 `--pmc`, one pass per group of counters; means per dispatch (sums over the chip). "
+             "SQ_WAVE_CYCLES, SQ_WAIT_* and SQ_ACTIVE_INST_* count quad-cycles (4 cycles).", "",
              "| counter | per dispatch | dispatches |", "|---|---:|---:|"]
     for c in sorted(vals):
         lines.append(f"| {c} | {vals[c]:,.0f} | {n_disp[c]} |")
     g = vals.get
+    n_simd, n_se = _gpu_units(dirs[0])
     ratios = []
+    # SQ_WAVE_CYCLES, SQ_WAIT_ANY, SQ_ACTIVE_INST_* count quad-cycles; SQ_BUSY_CYCLES counts cycles per
+    # shader engine; SQ_VALU_MFMA_BUSY_CYCLES cycles per SIMD (all summed over the chip)
     if g("SQ_WAVES"):
         for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SMEM"):
             if g(c) is not None:
                 ratios.append((f"{c} per wave", g(c) / g("SQ_WAVES")))
-    if g("SQ_WAVE_CYCLES") and g("SQ_WAVES"):
-        ratios.append(("wave lifetime, cycles (SQ_WAVE_CYCLES / SQ_WAVES)", g("SQ_WAVE_CYCLES") / g("SQ_WAVES")))
+        if g("SQ_WAVE_CYCLES"):
+            ratios.append(("wave lifetime, cycles (4 SQ_WAVE_CYCLES / SQ_WAVES)", 4 * g("SQ_WAVE_CYCLES") / g("SQ_WAVES")))
     if g("SQ_WAVE_CYCLES"):
-        for c in ("SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM",
-                  "SQ_ACTIVE_INST_ANY"):
+        for c in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY"):
             if g(c) is not None:
-                ratios.append((f"{c} / SQ_WAVE_CYCLES", g(c) / g("SQ_WAVE_CYCLES")))
-    if g("SQ_BUSY_CYCLES") and g("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
-        ratios.append(("SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CYCLES", g("SQ_VALU_MFMA_BUSY_CYCLES") / g("SQ_BUSY_CYCLES")))
+                ratios.append((f"{c} / SQ_WAVE_CYCLES (share of wave time)", g(c) / g("SQ_WAVE_CYCLES")))
+    if g("SQ_BUSY_CYCLES") and n_simd and n_se:
+        simd_cycles = g("SQ_BUSY_CYCLES") / n_se * n_simd
+        ratios.append(("kernel cycles per shader engine (SQ_BUSY_CYCLES / engines)", g("SQ_BUSY_CYCLES") / n_se))
+        for c, name in (("SQ_ACTIVE_INST_VALU", "VALU"), ("SQ_ACTIVE_INST_LDS", "LDS"), ("SQ_ACTIVE_INST_VMEM", "VMEM")):
+            if g(c) is not None:
+                ratios.append((f"{name} issue share of SIMD cycles (4 {c} / SIMD cycles)", 4 * g(c) / simd_cycles))
+        if g("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
+            ratios.append(("MFMA busy share of SIMD cycles", g("SQ_VALU_MFMA_BUSY_CYCLES") / simd_cycles))
     if g("SQ_INSTS_LDS") and g("SQ_LDS_BANK_CONFLICT") is not None:
         ratios.append(("SQ_LDS_BANK_CONFLICT cycles per LDS instruction", g("SQ_LDS_BANK_CONFLICT") / g("SQ_INSTS_LDS")))
     if ratios:
