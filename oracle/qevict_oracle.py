@@ -567,7 +567,7 @@ class UnitOracle:
         F, Q, E = select_tiers(cand, self.score, K_f, K_q, () if cfg.promote else prev_q)
         ctr = dict(aged=len(aged), promoted=0, packed=0, reactivated=0, demoted=0, evicted=len(E),
                    n_full=len(F), n_quant=len(Q))
-        # Algorithm 1 steps 5-10: Q -> F dequantizes the ledger and marks it dormant
+        # Algorithm 1, promotion: Q -> F dequantizes the ledger and marks it dormant
         for w in F:
             W = self.win[w]
             if W.state == QUANT:
@@ -576,7 +576,7 @@ class UnitOracle:
                 W.ledger.dormant = True
                 ctr["promoted"] += 1
             W.state = FULL
-        # steps 11-17: first entry quantizes once; a dormant record is reactivated
+        # Algorithm 1, demotion: first entry quantizes once; a dormant record is reactivated
         for w in Q:
             W = self.win[w]
             if W.state != QUANT:
@@ -591,7 +591,7 @@ class UnitOracle:
                     ctr["reactivated"] += 1
                 W.k = W.v = None
             W.state = QUANT
-        # steps 18-20: release and delete the record
+        # Algorithm 1, eviction: release and delete the record
         for w in E:
             W = self.win[w]
             W.state, W.k, W.v, W.ledger = EVICTED, None, None, None

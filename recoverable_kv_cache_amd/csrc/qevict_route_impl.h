@@ -418,7 +418,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     }
     __syncthreads();
 
-    // ---- 4. migration actions (Algorithm 1 steps 5-20).  Per window:
+    // ---- 4. migration actions (Algorithm 1: promotion, demotion, eviction).  Per window:
     // bit0 free page, bit1 need page, bit2 free slot, bit3 need slot, bit4 pack, bit5 fill
     int act[RT_PER];
     int ctr[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -484,7 +484,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         my_page[i] = w < NW ? rec[i].page : -1;
     }
     __syncthreads();
-    int* pushed = sm.idx;     // ids pushed at this event, by stack position - cnt0 (sm.idx is free after step 3)
+    int* pushed = sm.idx;     // ids pushed at this event, by stack position - cnt0 (sm.idx is free after phase 3)
     for (int pass = 0; pass < 2; ++pass) {      // pass 0: slots, pass 1: pages
         const int fbit = pass == 0 ? 4 : 1, nbit = pass == 0 ? 8 : 2;
         int32_t* stack = pass == 0 ? fslot : fpage;
@@ -585,7 +585,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         if (mode == RM_FORCE_Q || mode == RM_FORCE_F) target[w] = 0;
     }
     __syncthreads();
-    // ---- 8. accessible list (Algorithm 1 step 21) and byte-balanced splits.  The bf16
+    // ---- 8. accessible list (Algorithm 1: the accessible set after migration) and byte-balanced splits.  The bf16
     //      pages and the Quantized slots, each in chronological order, are merged so that
     //      the pages fall evenly among the slots (by rank fraction, (2r + 1) / 2count, pages
     //      first on ties): every byte-balanced split then holds a like share of both kinds,
@@ -658,7 +658,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         }
         splits[s] = pos;
     }
-    // (the split blocks are copied by k_split_blocks)
+    // (the split blocks are copied by the pack launch that follows)
     if (tid == 0) {
         hdr->n_acc = n_acc;
         int nwin = 0;
