@@ -640,7 +640,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         cost[e] = per_head_cost(g, en.kind);
     }
     __syncthreads();
-    const int total = block_scan_excl(cost, sm.wsum);   // cost[e] = bytes before entry e
+    const int total = block_scan_excl(cost, sm.wsum);   // cost[e] = cost of the entries before e
     int32_t* splits = bf.splits + u * (g.n_splits + 1);
     for (int s = tid; s <= g.n_splits; s += RT_THREADS) {
         int pos;
@@ -654,6 +654,9 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
                 if (cost[mid] < tgt) lo = mid + 1;
                 else hi = mid;
             }
+            // the boundary nearer the target (cost[n_acc] would be the total)
+            const long long c_hi = lo < n_acc ? cost[lo] : total;
+            if (lo > 0 && tgt - cost[lo - 1] < c_hi - tgt) lo -= 1;
             pos = lo;
         }
         splits[s] = pos;

@@ -171,14 +171,15 @@ __device__ __forceinline__ unsigned wave_scan_incl(unsigned x) {
     x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
     return x;
 }
-// Bytes one accessible entry makes the decode kernel read per KV head; splits are
-// balanced on them.  (Weighting bf16 pages by their compute time instead, which is
-// only ~2.3x that of an INT2 window against ~6x the bytes, measured slower: with the
-// cache streamed from HBM the page loads dominate.)
+// Cost of one accessible entry for a decode wave, in halves of a job: a Quantized
+// window is half of a pair job, a bf16 page of W tokens takes about as long as a pair
+// job of W-token windows, the sink block its share of a page.  Splits are balanced on
+// these, so that each workgroup's four waves get a like number of jobs (a workgroup
+// ends with its slowest wave).
 __device__ __forceinline__ int per_head_cost(const Geo& g, int kind) {
-    if (kind == EK_SINK) return 4 * g.n_sink * g.d;
-    if (kind == EK_PAGE) return 4 * g.W * g.d;
-    return g.slot_head_bytes;
+    if (kind == EK_SINK) return max(1, 4 * sink_width(g.n_sink) / g.W);
+    if (kind == EK_PAGE) return 4;
+    return 2;
 }
 
 // Total order of doubles as unsigned integers, ascending; -0 counts as +0 (so equal
