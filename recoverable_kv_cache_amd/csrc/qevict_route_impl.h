@@ -585,11 +585,12 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         if (mode == RM_FORCE_Q || mode == RM_FORCE_F) target[w] = 0;
     }
     __syncthreads();
-    // ---- 8. accessible list (Algorithm 1: the accessible set after migration) and byte-balanced splits.  The bf16
+    // ---- 8. accessible list (Algorithm 1: the accessible set after migration) and its splits.  The bf16
     //      pages and the Quantized slots, each in chronological order, are merged so that
     //      the pages fall evenly among the slots (by rank fraction, (2r + 1) / 2count, pages
-    //      first on ties): every byte-balanced split then holds a like share of both kinds,
-    //      whose costs per byte differ.  Attention does not depend on the order.
+    //      first on ties): every split then holds a like share of both kinds, whose costs
+    //      per byte differ.  Attention does not depend on the order.  The splits cut the
+    //      list at equal shares of the entries' job costs (per_head_cost).
     for (int w = tid; w < RT_MAXW; w += RT_THREADS) {   // page (low field), slot (high field)
         const int ns = w < NW ? sm.newst[w] : ST_NONE;
         flag[w] = ((ns == ST_LOCAL || ns == ST_FULL) ? 1 : 0) | (ns == ST_QUANT ? 0x10000 : 0);
