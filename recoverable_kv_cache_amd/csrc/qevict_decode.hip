@@ -719,8 +719,35 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         // (3) scores S^T[token][column] = codes . (q * sclK) + bias, log2 units.  RoPE mode:
         //     dequantized keys turned by their offset u in the chunk, times R(A)^T q
         float s[NV];
+        if constexpr (!ROPE) {
+            // every code-table lookup of the key side goes out before the first MFMA, so that
+            // their LDS latencies overlap (consumed one MFMA behind, they form a chain of 2*KS*TPC*NSLOT
+            // round trips); the two tiles' chains then alternate
+            u4_t kc[TPC][KS][NSLOT];
 #pragma unroll
-        for (int tc = 0; tc < TPC; ++tc) {
+            for (int tc = 0; tc < TPC; ++tc)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    kc[tc][ks][0] = key_codes(R.w, tc, ks);
+                    if constexpr (NSLOT == 2) kc[tc][ks][NSLOT - 1] = key_codes(R.w + S::KCW, tc, ks);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            f4_t d[TPC];
+#pragma unroll
+            for (int tc = 0; tc < TPC; ++tc) d[tc] = f4_t{c0, c0, c0, c0};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int sl = 0; sl < NSLOT; ++sl)
+#pragma unroll
+                    for (int tc = 0; tc < TPC; ++tc) d[tc] = mfma32(kc[tc][ks][sl], sl ? bqb[ks] : bqa[ks], d[tc]);
+#pragma unroll
+            for (int tc = 0; tc < TPC; ++tc)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[4 * tc + i] = d[tc][i] + mirror<SW>(d[tc][i]);   // high + low query parts
+        }
+#pragma unroll
+        for (int tc = 0; tc < (ROPE ? TPC : 0); ++tc) {
             f4_t d = {c0, c0, c0, c0};
             if constexpr (ROPE) {
                 const int u = 16 * tc + n;
@@ -740,12 +767,6 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
                         d = mfma32(hs, bqb[ks + KS / 2], d);
                         d = mfma32(ls, bqb[ks + KS / 2], d);
                     }
-                }
-            } else {
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    d = mfma32(key_codes(R.w, tc, ks), bqa[ks], d);
-                    if constexpr (NSLOT == 2) d = mfma32(key_codes(R.w + S::KCW, tc, ks), bqb[ks], d);
                 }
             }
 #pragma unroll
@@ -778,11 +799,22 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             pa = slot ? z : pa;
         }
         // (5) O^T[channel][column] += codes^T . P'
+        //     (each slot's lookups all go out before its MFMAs, as on the key side)
+        {
+            u4_t vc[MB];
 #pragma unroll
-        for (int m = 0; m < MB; ++m) acc[m] = mfma32(value_codes(R.w + S::O_VC, m), pa, acc[m]);
+            for (int m = 0; m < MB; ++m) vc[m] = value_codes(R.w + S::O_VC, m);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < MB; ++m) acc[m] = mfma32(vc[m], pa, acc[m]);
+        }
         if (NSLOT == 2 && j.ib >= 0) {
+            u4_t vc[MB];
 #pragma unroll
-            for (int m = 0; m < MB; ++m) acc[m] = mfma32(value_codes(R.w + S::O_VC + S::VCW, m), pb, acc[m]);
+            for (int m = 0; m < MB; ++m) vc[m] = value_codes(R.w + S::O_VC + S::VCW, m);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < MB; ++m) acc[m] = mfma32(vc[m], pb, acc[m]);
         }
         // (6) both windows end on their last chunk: log-sum-exp of their mass per head
         if (j.c + 1 == NCH) lse_store(slot == 0 || j.ib >= 0, slot == 0 ? j.ia : j.ib);
