@@ -189,6 +189,9 @@ def main():
                     help="bits per Quantized-tier code: INT2 (default) or INT4")
     ap.add_argument("--rope", action="store_true",
                     help="inputs before RoPE, Quantized tier in the pre-RoPE domain (rotary base 500000)")
+    ap.add_argument("--combine", choices=("auto", "launch"), default="auto",
+                    help="auto: a decode step is one launch when each (sequence, KV head) has one split; "
+                         "launch: always the separate finish launch (QEVICT_F_SEPARATE_FINISH)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -219,7 +222,8 @@ def main():
     if args.steps + args.warmup > wl.n_decode:
         sys.exit(f"--steps + --warmup must be <= {wl.n_decode}")
     flags = (getattr(B, RANKERS[args.ranker]) if RANKERS[args.ranker] else 0) | \
-        (B.QEVICT_F_INT4 if args.quant_bits == 4 else 0) | (B.QEVICT_F_ROPE if args.rope else 0)
+        (B.QEVICT_F_INT4 if args.quant_bits == 4 else 0) | (B.QEVICT_F_ROPE if args.rope else 0) | \
+        (B.QEVICT_F_SEPARATE_FINISH if args.combine == "launch" else 0)
     cfg = B.make_config(wl, n_splits=args.n_splits, flags=flags)
     lens = wl.prompt_lens()
     st = B.QEvictState(cfg, lens, device=dev)
@@ -347,7 +351,8 @@ def main():
                    "n_local": wl.n_local, "omega": wl.omega, "budget_frac": wl.budget_frac,
                    "quant_frac": wl.quant_frac, "storage": f"bf16 + int{args.quant_bits}", "n_splits": st.info.n_splits,
                    "K_f": st.info.max_K_f, "K_q": st.info.max_K_q, "ranker": args.ranker,
-                   "rope": "inputs before RoPE, base 500000" if args.rope else None},
+                   "rope": "inputs before RoPE, base 500000" if args.rope else None,
+                   "finish": "in the split kernel" if st.info.combine_in_kernel else "second launch"},
         "decode_attn_tokens_per_s": round(decode_tokens_per_s, 2),
         "route_us_per_event": {"mean": round(statistics.mean(route_ms) * 1e3, 2) if route_ms else None,
                                "p50": round(rp[len(rp) // 2] * 1e3, 2) if rp else None,

@@ -79,6 +79,12 @@ typedef enum {
  * RoPE to the dequantized keys at the ledger's positions, and a promotion writes bf16 of
  * that re-rotation. */
 #define QEVICT_F_ROPE             64u
+/* With one split per (sequence, KV head) (n_splits = 1, the automatic choice once
+ * B * h_kv >= 512) a decode step is one kernel launch: each split-kernel workgroup writes its
+ * heads' output and log-sum-exps and the step's token itself, and the last of a sequence's
+ * h_kv workgroups advances its token count.  This flag keeps the second (finish) launch that
+ * otherwise combines the splits. */
+#define QEVICT_F_SEPARATE_FINISH 128u
 
 typedef struct {
     int32_t batch;        /* B sequences */
@@ -108,6 +114,7 @@ typedef struct {
     int32_t n_acc_max;           /* accessible-list capacity */
     int32_t n_splits;            /* decode splits actually used */
     int32_t max_K_f, max_K_q;    /* largest capacities over the batch */
+    int32_t combine_in_kernel;   /* 1: a decode step is one kernel launch (QEVICT_F_SEPARATE_FINISH) */
 } qevict_plan_info;
 
 typedef struct qevict_state qevict_state;

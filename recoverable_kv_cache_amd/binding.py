@@ -25,6 +25,7 @@ QEVICT_F_RANK_PNORM = 8
 QEVICT_F_RANK_KEYNORM = 16
 QEVICT_F_INT4 = 32           # INT4 recoverable tier ([QEvict] Appendix G.3) instead of INT2
 QEVICT_F_ROPE = 64           # inputs before RoPE; Quantized tier in the pre-RoPE domain ([QEvict] §4.3)
+QEVICT_F_SEPARATE_FINISH = 128   # keep the finish launch even with one split per (sequence, KV head)
 
 DEV_E_POOL, DEV_E_WINDOW, DEV_E_RANGE, DEV_E_LIST, DEV_E_SELECT = 1, 2, 4, 8, 16
 
@@ -60,7 +61,7 @@ class PlanInfo(ctypes.Structure):
         ("arena_bytes", ctypes.c_size_t), ("prefill_ws_bytes", ctypes.c_size_t),
         ("export_bytes", ctypes.c_size_t), ("n_windows", ctypes.c_int32), ("n_pages", ctypes.c_int32),
         ("n_slots", ctypes.c_int32), ("n_acc_max", ctypes.c_int32), ("n_splits", ctypes.c_int32),
-        ("max_K_f", ctypes.c_int32), ("max_K_q", ctypes.c_int32),
+        ("max_K_f", ctypes.c_int32), ("max_K_q", ctypes.c_int32), ("combine_in_kernel", ctypes.c_int32),
     ]
 
 

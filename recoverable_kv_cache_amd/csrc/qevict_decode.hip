@@ -1,9 +1,9 @@
-// Decode step, two launches per layer.  k_decode_split appends the new token to
-// its recent window and runs split-K attention over the accessible list (sinks,
-// recent windows, Full bf16 windows, Quantized INT2 or INT4 windows); k_finish combines
-// the splits of each query head with the global log-sum-exp, writes each
-// entry's per-head share of this step's window mass, and advances the token
-// count.  The shares are folded into the cumulative scores by the next
+// Decode step, two launches per layer (one when each (sequence, KV head) has a single
+// split).  k_decode_split appends the new token to its recent window and runs split-K
+// attention over the accessible list (sinks, recent windows, Full bf16 windows, Quantized
+// INT2 or INT4 windows); k_finish combines the splits of each query head with the global
+// log-sum-exp, writes each entry's per-head share of this step's window mass, and advances
+// the token count (with a single split the split kernel does all of that itself).  The shares are folded into the cumulative scores by the next
 // k_decode_split of the unit (or by the router / an export, whichever comes
 // first), which overlaps that read-modify-write with other work.
 //
@@ -227,7 +227,7 @@ struct Job {
 template <int D, int G, int TPC, int BITS, bool ROPE>
 __global__ void __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(2)))
 k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, const uint16_t* __restrict__ knew,
-               const uint16_t* __restrict__ vnew) {
+               const uint16_t* __restrict__ vnew, float* __restrict__ out, int score_now) {
     using S = DecShape<D, G, TPC, BITS, ROPE>;
     constexpr int CQ = S::CQ, KS = S::KS, MB = S::MB, NSLOT = S::NSLOT, SW = S::SW, LPR = S::LPR, CPL = S::CPL;
     constexpr int NV = S::NV, QSTR = S::QSTR;
@@ -242,6 +242,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
     __shared__ float s_m[DW][G], s_l[DW][G], s_vb[DW][G];
     __shared__ float s_acc[DW][G][D];
     __shared__ __attribute__((aligned(16))) uint16_t nkv[DW][2][D];     // per wave: the new token's K and V
+    __shared__ int s_tok[2];             // one split per group: position and block the token was attended in
     // RoPE mode: (cos, sin) of positions 0..31 of a chunk (rows of the table), and per wave
     // the two windows' key parameters (fp16 offset | scale << 16, channel order)
     __shared__ __attribute__((aligned(16))) float2 ctab[ROPE ? 32 * (D / 2) : 1];
@@ -318,6 +319,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         // a code byte -> its codes as bf16 integers (4 of 2 bits, or 2 of 4 bits): one table
         // at a fixed LDS address, so a lookup is one shift of the code byte with the base in
         // the read's immediate offset
+        if (threadIdx.x == 0) s_tok[0] = s_tok[1] = -1;
         for (int x = threadIdx.x; x < 256; x += 64 * DW) {
             auto bv = [](int c) -> uint32_t { return __float_as_uint((float)c) >> 16; };   // exact for c < 256
             if constexpr (BITS == 2)
@@ -831,10 +833,17 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         for (int x = 0; x < 2 * MB; ++x) vw[x] = R.w[CQ / 2 + x];
         const int pt = n_old - j.start - 16 * j.t;    // the new token's row in this tile, if any
         if (pt >= 0 && pt < 16 && n_old - j.start < j.ntok) {   // (a sink block's spare rows never hold it)
-            // its block, for the finish kernel that stores the token (one writer per KV head)
-            if (hk == 0 && lane == 0) {
-                bf.hdr[u].tok_page = j.kind == EK_SINK ? -2 : j.idx;
-                bf.hdr[u].tok_at = n_old;
+            // its block, for whoever stores the token: this workgroup at its end (one split per
+            // group) or the finish kernel (one writer per unit)
+            if (lane == 0) {
+                const int tp = j.kind == EK_SINK ? -2 : j.idx;
+                if (g.fuse) {
+                    s_tok[0] = n_old;
+                    s_tok[1] = tp;
+                } else if (hk == 0) {
+                    bf.hdr[u].tok_page = tp;
+                    bf.hdr[u].tok_at = n_old;
+                }
             }
             // its K row (lanes of token row pt) and its V column entries come from LDS
             if (n == pt) {
@@ -938,7 +947,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         // once, by the KV head whose index matches its position in the split
         if (pending && wave == DW - 1 && valid && x % g.h_kv == hk && me.win >= 0) {
             const float* row = bf.lse_win + lse_win_off(g, u, (n_old - 1) & 1) + (int64_t)(e_begin + x) * g.h_q;
-            const float* lg = bf.lse_glob + u * g.h_q;
+            const float* lg = bf.lse_glob + lse_glob_off(g, u, (n_old - 1) & 1);
             double* sc = mass_target(g, bf) + u * g.n_windows + me.win;
             const double s0 = *sc;
             const double sm = entry_mass(row, lg, g.h_q);
@@ -982,8 +991,12 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         }
     }
     __syncthreads();
+    // One split per group (g.fuse): the merge is the heads' output, and this workgroup also
+    // does what the finish kernel does otherwise.  Else: the split's partial.
     float* pacc = bf.part_acc + ((u * g.n_splits + split) * (int64_t)g.h_q + hk * G) * D;
     float2* pml = bf.part_ml + (u * g.n_splits + split) * (int64_t)g.h_q + hk * G;
+    float* og = out + ((int64_t)b * g.h_q + hk * G) * D;
+    float* lseg = bf.lse_glob + lse_glob_off(g, u, n_old & 1) + hk * G;
     for (int x = threadIdx.x; x < G * D; x += 64 * DW) {
         const int gg = x / D, c = x % D;
         float M = s_m[0][gg];
@@ -996,13 +1009,51 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             L += f * s_l[w][gg];
             A += f * (s_acc[w][gg][c] + s_vb[w][gg]);
         }
-        pacc[(int64_t)gg * D + c] = A;
-        if (c == 0) pml[gg] = make_float2(M, L);
+        if (g.fuse) {
+            og[(int64_t)gg * D + c] = A / L;
+            if (c == 0) lseg[gg] = M + log2f(L);
+        } else {
+            pacc[(int64_t)gg * D + c] = A;
+            if (c == 0) pml[gg] = make_float2(M, L);
+        }
+    }
+    if (!g.fuse) return;
+    // ---- the step's token into the block this workgroup attended it in (a window the
+    // router did not prepare is an error); then the last of the unit's h_kv workgroups to
+    // get here advances the unit's token count (every workgroup of the unit has read it by
+    // then: the count is an atomic, so the workgroups may run on any XCDs).
+    const int tok_at = s_tok[0], page = s_tok[1];
+    const bool ok = tok_at == n_old;
+    if (ok && threadIdx.x < D) {
+        uint16_t* blk;
+        int Wp = g.W, i;
+        if (page == -2) {
+            blk = bf.sinks + u * g.sink_elems;
+            Wp = sink_width(g.n_sink);
+            i = n_old;
+        } else {
+            i = (n_old - g.n_sink) % g.W;
+            blk = bf.pages + u * (int64_t)g.n_pages * g.page_elems + (int64_t)page * g.page_elems;
+        }
+        uint16_t* kh = blk + (int64_t)(2 * hk) * Wp * D;
+        kh[lay_k(i, threadIdx.x, D, Wp)] = nkv[0][0][threadIdx.x];
+        kh[(int64_t)Wp * D + lay_v(i, threadIdx.x, D, Wp)] = nkv[0][1][threadIdx.x];
+    }
+    if (threadIdx.x == 0) {
+        if (!ok) atomicOr(&bf.hdr[u].status, QEVICT_DEV_E_WINDOW);
+        const uint32_t done = __hip_atomic_fetch_add(bf.unit_arr + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+        if (done == (uint32_t)g.h_kv) {
+            __hip_atomic_store(bf.unit_arr + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (ok) bf.hdr[u].n = n_old + 1;
+            bf.hdr[u].mass_pending = score_now;
+        }
     }
 }
 
 hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t* q, const uint16_t* k_new,
-                         const uint16_t* v_new, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+                         const uint16_t* v_new, float* out, int score_now, hipStream_t s, hipEvent_t ev0,
+                         hipEvent_t ev1) {
+    if (g.fuse && (g.n_splits != 1 || !out)) return hipErrorInvalidValue;
     const dim3 grid(g.n_splits, g.h_kv, g.B), block(64 * DW);
     const int G = g.h_q / g.h_kv, TPC = lay_tpc(g.W);
     const bool rope = (g.flags & QEVICT_F_ROPE) != 0;
@@ -1010,10 +1061,10 @@ hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t
     if (g.d == D_ && G == G_ && TPC == T_ && g.qbits == B_ && rope == R_) {                    \
         if (ev0)                                                                               \
             hipExtLaunchKernelGGL((k_decode_split<D_, G_, T_, B_, R_>), grid, block, 0, s, ev0, ev1, 0, g, bf, \
-                                  layer, q, k_new, v_new);                                     \
+                                  layer, q, k_new, v_new, out, score_now);                     \
         else                                                                                   \
             hipLaunchKernelGGL((k_decode_split<D_, G_, T_, B_, R_>), grid, block, 0, s, g, bf, layer, q, k_new, \
-                               v_new);                                                         \
+                               v_new, out, score_now);                                         \
         return hipGetLastError();                                                              \
     }
 #define QV_DEC1(D_, G_, T_, B_) QV_DEC2(D_, G_, T_, B_, false) QV_DEC2(D_, G_, T_, B_, true)
@@ -1151,7 +1202,7 @@ __global__ void __launch_bounds__(FN_THREADS) k_finish(Geo g, Bufs bf, int layer
         a4[i] = qg_sum(v);
     }
     if (ph == 0) reinterpret_cast<f4_t*>(out + ((int64_t)b * g.h_q + h) * D)[col] = a4 / L;
-    if (tid == 0) bf.lse_glob[u * g.h_q + h] = M + log2f(L);
+    if (tid == 0) bf.lse_glob[lse_glob_off(g, u, n_old & 1) + h] = M + log2f(L);
     if (tok_wg) {
         // the block the split kernel attended the token in: found only when its sink /
         // recent window was accessible (a window the router did not prepare is an error)
@@ -1236,7 +1287,7 @@ __global__ void __launch_bounds__(256) k_step_mass(Geo g, Bufs bf, int layer, in
     const UnitHdr* hdr = bf.hdr + u;
     const int cols = g.n_windows + 1;
     const float* lwin = bf.lse_win + lse_win_off(g, u, (hdr->n - 1) & 1);
-    const float* lg = bf.lse_glob + u * g.h_q;
+    const float* lg = bf.lse_glob + lse_glob_off(g, u, (hdr->n - 1) & 1);
     const int x = blockIdx.x * blockDim.x + threadIdx.x;
     if (x >= hdr->n_acc * g.h_q) return;
     const int e = x / g.h_q, h = x % g.h_q;

@@ -105,7 +105,8 @@ struct Layout {
 };
 
 enum { O_HDR, O_WIN, O_SCORE, O_ACC, O_SPLITS, O_FPAGE, O_FSLOT, O_PACK, O_FILL, O_TARGET, O_LSEW, O_LSEG,
-       O_PML, O_PACC, O_PAGES, O_SLOTS, O_SINKS, O_PLENS, O_KF, O_KQ, O_SBLK, O_UACC, O_ROPE, O_KROT, O_COUNT };
+       O_PML, O_PACC, O_PAGES, O_SLOTS, O_SINKS, O_PLENS, O_KF, O_KQ, O_SBLK, O_UACC, O_ROPE, O_KROT, O_UARR,
+       O_COUNT };
 
 qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, Layout* lay) {
     qevict_status s = validate(c);
@@ -147,6 +148,8 @@ qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, La
     g.n_splits = ns;
     g.page_elems = g.h_kv * 2 * g.W * g.d;
     g.qbits = (c->flags & QEVICT_F_INT4) ? 4 : 2;
+    // one split per (sequence, KV head): the split kernel finishes the step itself
+    g.fuse = g.n_splits == 1 && !(c->flags & QEVICT_F_SEPARATE_FINISH);
     g.n_rope = (c->flags & QEVICT_F_ROPE) ? std::max(32, c->max_prompt + c->max_new) : 0;
     g.slot_head_bytes = 2 * lay_code_bytes(g.W, g.d, g.qbits) + 4 * g.d + 4 * g.W;
     g.slot_bytes = g.h_kv * g.slot_head_bytes;
@@ -165,7 +168,7 @@ qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, La
     sz[O_FILL] = U * g.n_windows * sizeof(FillItem);
     sz[O_TARGET] = U * g.n_windows;
     sz[O_LSEW] = U * 2 * g.n_acc_max * g.h_q * sizeof(float);   // two halves by position parity
-    sz[O_LSEG] = U * g.h_q * sizeof(float);
+    sz[O_LSEG] = U * 2 * g.h_q * sizeof(float);                  // two halves by position parity
     sz[O_PML] = U * g.n_splits * g.h_q * sizeof(float2);
     sz[O_PACC] = U * g.n_splits * g.h_q * g.d * sizeof(float);
     sz[O_PAGES] = U * g.n_pages * (size_t)g.page_elems * 2;
@@ -175,6 +178,7 @@ qevict_status make_layout(const qevict_config* c, const int32_t* prompt_lens, La
     sz[O_SBLK] = U * (size_t)g.n_splits * SPLIT_BLOCK * sizeof(AccEntry);
     sz[O_ROPE] = (size_t)g.n_rope * (g.d / 2) * sizeof(float2);
     sz[O_KROT] = g.n_rope ? U * g.h_kv * (size_t)g.d * 2 : 0;
+    sz[O_UARR] = U * sizeof(uint32_t);
     size_t at = 0;
     for (int i = 0; i < O_COUNT; ++i) {
         lay->off[i] = at;
@@ -214,6 +218,7 @@ Bufs bind_bufs(const Layout& lay, void* arena) {
     b.split_blk = (AccEntry*)(a + lay.off[O_SBLK]);
     b.rope = lay.g.n_rope ? (const float2*)(a + lay.off[O_ROPE]) : nullptr;
     b.krot = lay.g.n_rope ? (uint16_t*)(a + lay.off[O_KROT]) : nullptr;
+    b.unit_arr = (uint32_t*)(a + lay.off[O_UARR]);
     return b;
 }
 
@@ -298,6 +303,7 @@ qevict_status qevict_plan(const qevict_config* cfg, const int32_t* prompt_lens, 
     out->n_splits = lay.g.n_splits;
     out->max_K_f = lay.max_kf;
     out->max_K_q = lay.max_kq;
+    out->combine_in_kernel = lay.g.fuse;
     return QEVICT_OK;
 }
 
@@ -398,15 +404,16 @@ qevict_status qevict_decode_attn(qevict_state* st, int32_t layer, const void* q,
         return fail(QEVICT_E_CAPACITY, "layer %d already decoded max_new = %d tokens", layer, st->cfg.max_new);
     hipStream_t hs = (hipStream_t)stream;
     const Geo& g = st->lay.g;
-    HIP_TRY(launch_decode(g, st->bf, layer, (const uint16_t*)q, (const uint16_t*)k_new, (const uint16_t*)v_new, hs,
-                          st->ev_before, st->ev_after));
-    st->ev_before = st->ev_after = nullptr;
     // Eq. 1 accumulates every step; with QEVICT_F_SCORE_ROUTE_ONLY only on the steps that end
     // a routing interval
     const int j = st->steps[layer];
     const int score_now = (!(g.flags & QEVICT_F_SCORE_ROUTE_ONLY) || (j + 1) % g.omega == 0) &&
                           !(g.flags & QEVICT_F_RANK_KEYNORM);   // the key-norm ranker uses no mass
-    HIP_TRY(launch_finish(g, st->bf, layer, out, (const uint16_t*)k_new, (const uint16_t*)v_new, score_now, hs));
+    HIP_TRY(launch_decode(g, st->bf, layer, (const uint16_t*)q, (const uint16_t*)k_new, (const uint16_t*)v_new, out,
+                          score_now, hs, st->ev_before, st->ev_after));
+    st->ev_before = st->ev_after = nullptr;
+    if (!g.fuse)
+        HIP_TRY(launch_finish(g, st->bf, layer, out, (const uint16_t*)k_new, (const uint16_t*)v_new, score_now, hs));
     st->steps[layer] += 1;
     st->step_fresh[layer] = 1;
     return QEVICT_OK;

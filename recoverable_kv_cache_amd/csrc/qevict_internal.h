@@ -84,6 +84,7 @@ struct Geo {
     uint32_t flags;
     int32_t qbits;        // bits per Quantized-tier code: 2, or 4 with QEVICT_F_INT4
     int32_t n_rope;       // rows of the RoPE table (0 without QEVICT_F_ROPE)
+    int32_t fuse;         // 1: one split per group, and the split kernel also finishes the step
 };
 
 // Device pointers to the per-unit arrays (index by unit = b * L + l).
@@ -101,7 +102,7 @@ struct Bufs {
     FillItem* fill;         // [U][n_windows]
     int8_t* target;         // [U][n_windows] forced targets
     float* lse_win;         // [U][2][n_acc_max][h_q] log2 domain, by parity of the step's position
-    float* lse_glob;        // [U][h_q]              log2 domain
+    float* lse_glob;        // [U][2][h_q]           log2 domain, by parity of the step's position
     float2* part_ml;        // [U][n_splits][h_q]    (m, l), log2 domain
     float* part_acc;        // [U][n_splits][h_q][d]
     uint16_t* pages;        // [U][n_pages][h_kv][2][W][d]   bf16
@@ -109,6 +110,7 @@ struct Bufs {
     uint16_t* sinks;        // [U][h_kv] pages of Ws tokens (same layout as a window page)
     const float2* rope;     // RoPE mode: (cos, sin) [n_rope][d/2], n_rope >= max(32, max_prompt + max_new)
     uint16_t* krot;         // RoPE mode: [U][h_kv][d] the step's key after RoPE (split kernel -> finish)
+    uint32_t* unit_arr;     // [U]  one split per group: the unit's workgroups done with a step
 };
 
 __host__ __device__ inline int64_t unit_of(const Geo& g, int b, int l) { return (int64_t)b * g.L + l; }
@@ -116,6 +118,12 @@ __host__ __device__ inline int64_t unit_of(const Geo& g, int b, int l) { return 
 // them (to fold this step's window mass) while writing its own to the other half
 __host__ __device__ inline int64_t lse_win_off(const Geo& g, int64_t u, int par) {
     return (u * 2 + par) * (int64_t)g.n_acc_max * g.h_q;
+}
+// the heads' log-sum-exps of the step at a position of parity par (same double buffering: a
+// split kernel that finishes the step itself writes them while its other workgroups still
+// read the previous step's)
+__host__ __device__ inline int64_t lse_glob_off(const Geo& g, int64_t u, int par) {
+    return (u * 2 + par) * (int64_t)g.h_q;
 }
 
 // Each split's header and first SPLIT_BLOCK - 1 accessible-list entries, copied by the
@@ -213,9 +221,12 @@ hipError_t launch_rope_prompt(const Geo& g, const Bufs& bf, const uint16_t* qp, 
                               const uint16_t** qr, const uint16_t** kr, hipStream_t s);
 hipError_t launch_init(const Geo& g, const Bufs& bf, const int32_t* prompt_lens_dev, const int32_t* kf_dev,
                        const int32_t* kq_dev, hipStream_t s);
-// ev0 / ev1 (optional): events stamped by the split kernel's own dispatch at its start and end
+// ev0 / ev1 (optional): events stamped by the split kernel's own dispatch at its start and end.
+// With g.fuse (one split per group) the split kernel also finishes the step (out, score_now as
+// for launch_finish); otherwise launch_finish follows.
 hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t* q, const uint16_t* k_new,
-                         const uint16_t* v_new, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+                         const uint16_t* v_new, float* out, int score_now, hipStream_t s, hipEvent_t ev0 = nullptr,
+                         hipEvent_t ev1 = nullptr);
 hipError_t launch_finish(const Geo& g, const Bufs& bf, int layer, float* out, const uint16_t* k_new,
                          const uint16_t* v_new, int score_now, hipStream_t s);
 hipError_t launch_flush_mass(const Geo& g, const Bufs& bf, int layer, int b, hipStream_t s);

@@ -52,7 +52,7 @@ __device__ __forceinline__ double entry_mass(const float* __restrict__ row, cons
 __device__ inline void apply_mass_range(const Geo& g, const Bufs& bf, int64_t u, int pos, int first, int last,
                                         int step) {
     const float* lwin = bf.lse_win + lse_win_off(g, u, pos & 1);
-    const float* lg = bf.lse_glob + u * g.h_q;
+    const float* lg = bf.lse_glob + lse_glob_off(g, u, pos & 1);
     for (int e = first; e < last; e += step) {
         if (e == 0) continue;
         const AccEntry en = bf.acc[u * g.n_acc_max + e];

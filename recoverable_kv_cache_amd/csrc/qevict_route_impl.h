@@ -276,7 +276,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         for (int w = tid; w < RT_MAXW; w += RT_THREADS) mwin[w] = 0.0;
         __syncthreads();
         const float* lwin = bf.lse_win + lse_win_off(g, u, (n - 1) & 1);   // the step at position n - 1
-        const float* lg = bf.lse_glob + u * g.h_q;
+        const float* lg = bf.lse_glob + lse_glob_off(g, u, (n - 1) & 1);
         const int n_acc = hdr->n_acc;
         for (int e = 1 + tid; e < n_acc; e += RT_THREADS) {   // (entry 0: the sinks, no window)
             const AccEntry en = bf.acc[u * g.n_acc_max + e];

@@ -35,6 +35,7 @@ __global__ void k_init(Geo g, Bufs bf, const int32_t* plens, const int32_t* kf, 
         bf.target[u * g.n_windows + w] = 0;
     }
     for (int s = threadIdx.x; s <= g.n_splits; s += blockDim.x) bf.splits[u * (g.n_splits + 1) + s] = 0;
+    if (threadIdx.x == 0) bf.unit_arr[u] = 0u;
 }
 
 hipError_t launch_init(const Geo& g, const Bufs& bf, const int32_t* plens, const int32_t* kf, const int32_t* kq,

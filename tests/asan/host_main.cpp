@@ -50,6 +50,18 @@ static void check_plans() {
     qevict_config c = base_config();
     EXPECT(qevict_plan(&c, lens, &info) == QEVICT_OK);
     EXPECT(info.arena_bytes > 0 && info.export_bytes > 0 && info.n_windows > 0 && info.n_splits > 0);
+    // a decode step is one launch exactly when each (sequence, KV head) has one split, unless
+    // the flag asks for the finish launch
+    EXPECT(info.combine_in_kernel == (info.n_splits == 1));
+    {
+        qevict_config x = c;
+        x.n_splits = 6;
+        EXPECT(qevict_plan(&x, lens, &info) == QEVICT_OK && info.combine_in_kernel == 0);
+        x.n_splits = 1;
+        EXPECT(qevict_plan(&x, lens, &info) == QEVICT_OK && info.combine_in_kernel == 1);
+        x.flags = QEVICT_F_SEPARATE_FINISH;
+        EXPECT(qevict_plan(&x, lens, &info) == QEVICT_OK && info.combine_in_kernel == 0);
+    }
     // every field outside what the kernels support
     struct Bad {
         const char* what;

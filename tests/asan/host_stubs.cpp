@@ -58,8 +58,8 @@ hipError_t launch_init(const Geo& g, const Bufs& bf, const int32_t* plens, const
     }
     return hipSuccess;
 }
-hipError_t launch_decode(const Geo&, const Bufs&, int, const uint16_t*, const uint16_t*, const uint16_t*, hipStream_t,
-                         hipEvent_t, hipEvent_t) {
+hipError_t launch_decode(const Geo&, const Bufs&, int, const uint16_t*, const uint16_t*, const uint16_t*, float*, int,
+                         hipStream_t, hipEvent_t, hipEvent_t) {
     return hipSuccess;
 }
 hipError_t launch_finish(const Geo&, const Bufs&, int, float*, const uint16_t*, const uint16_t*, int, hipStream_t) {

@@ -60,6 +60,26 @@ def test_batched_ragged_prompts_gqa8_d128():
     _print(f"ragged: max o err {ls.max_o_err:.2e} (bf16 reading {ls.max_o_err_bf16:.2e}, gap {ls.max_reading_gap:.2e}), max score err {ls.max_s_err:.2e}")
 
 
+@pytest.mark.parametrize("n_splits", [1, 3], ids=["one-split", "three-splits"])
+def test_single_launch_step_and_finish_launch(n_splits):
+    """With one split per (sequence, KV head) a decode step is one launch: the split kernel
+    writes the output, the log-sum-exps and the token, and the last of a sequence's KV heads
+    advances its count; QEVICT_F_SEPARATE_FINISH keeps the finish launch.  Both follow the
+    oracle through drift, promotions and routing events (two sequences, 4 KV heads)."""
+    wl = WL.Workload("one_launch_b2", 1, 2, 16, 4, 64, 768, 40, 16, 4, 64, 8, 0.30, 0.70, prompt_len_min=600,
+                     n_outlier=2, n_topics=3, topic_period=12)
+    si = torch.zeros((2, 64), dtype=torch.float64)
+    for flags in (0, B.QEVICT_F_SEPARATE_FINISH):
+        _print(f"case: n_splits={n_splits} flags={flags}")
+        ls = Lockstep(wl, score_init=si, flags=flags, n_splits=n_splits)
+        assert ls.st.info.n_splits == n_splits
+        assert ls.st.info.combine_in_kernel == int(n_splits == 1 and not flags)
+        ls.run(40)
+        _print(f"n_splits={n_splits} flags={flags}: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}")
+        assert ls.st.poll_status() == 0
+        assert sum(e["promoted"] for e in ls.units[0].events) + sum(e["promoted"] for e in ls.units[1].events) > 0
+
+
 def test_window64_gqa8_multichunk():
     """70B-shaped heads at reduced size: W = 64 (an INT2 window spans two 32-token
     chunks of pair jobs, a bf16 window four tiles), 8 query heads per KV head, d = 128,
