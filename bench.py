@@ -268,13 +268,15 @@ def main():
         e.record()
         return e
 
-    def run_step(j, timing=None, route_ev=None):
+    def run_step(j, timing=None, route_ev=None, route_k=None):
         for l in range(wl.n_layers):
             if timing is not None:
                 st.time_next_decode(timing[l][0], timing[l][1])
             q, k, v = inputs[j][l]
             st.decode_attn(l, q, k, v, out)
         if (j + 1) % wl.omega == 0:
+            if route_k is not None:
+                st.time_next_route(route_k[0], route_k[1])
             if route_ev is not None:
                 route_ev[0].record()
             st.route(-1)
@@ -288,19 +290,22 @@ def main():
 
     # ---- timed region: wall-clock events around all steps; the split-K kernels of the
     # sampled steps carry events stamped by their own dispatch (start / end), and every
-    # routing event is bracketed by events
+    # routing event is bracketed by events, and also timed by events its kernels' dispatches
+    # stamp (the routing kernel's start, the migration kernel's end)
     sched = timed_schedule(args.steps, args.warmup, wl.omega)
     kev = {i: [(new_event(), new_event()) for _ in range(wl.n_layers)] for i, _, _, s_ in sched if s_}
     rev = {i: (new_event(), new_event()) for i, _, r, _ in sched if r}
+    rkev = {i: (new_event(), new_event()) for i, _, r, _ in sched if r}
     start, stop = new_event(), new_event()
     torch.cuda.synchronize()
     start.record()
     for i, j, _, _ in sched:
-        run_step(j, timing=kev.get(i), route_ev=rev.get(i))
+        run_step(j, timing=kev.get(i), route_ev=rev.get(i), route_k=rkev.get(i))
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    route_ms = [e0.elapsed_time(e1) for e0, e1 in rev.values()]
+    route_ms = [e0.elapsed_time(e1) for e0, e1 in rev.values()]   # between stream events
+    route_k_ms = [e0.elapsed_time(e1) for e0, e1 in rkev.values()]   # kernels' own dispatch stamps
     n_route = len(route_ms)
     kern_ms = [e0.elapsed_time(e1) for evs in kev.values() for e0, e1 in evs]
     kv1 = [st.step_bytes(l) for l in range(wl.n_layers)]
@@ -332,7 +337,11 @@ def main():
         log("[bench] cpu baseline (oracle) ...")
         cpu = cpu_baseline(wl, args.cpu_budget_s, args.ranker, args.quant_bits, rope_cs)
 
-    rp = sorted(route_ms)
+    def stats_us(ms):
+        s_ = sorted(ms)
+        return {"mean": round(statistics.mean(s_) * 1e3, 2) if s_ else None,
+                "p50": round(s_[len(s_) // 2] * 1e3, 2) if s_ else None,
+                "p99": round(s_[min(len(s_) - 1, math.ceil(0.99 * len(s_)) - 1)] * 1e3, 2) if s_ else None}
     line = {
         "metric": METRIC,
         "value": round(tokens_per_s, 2),
@@ -354,10 +363,11 @@ def main():
                    "rope": "inputs before RoPE, base 500000" if args.rope else None,
                    "finish": "in the split kernel" if st.info.combine_in_kernel else "second launch"},
         "decode_attn_tokens_per_s": round(decode_tokens_per_s, 2),
-        "route_us_per_event": {"mean": round(statistics.mean(route_ms) * 1e3, 2) if route_ms else None,
-                               "p50": round(rp[len(rp) // 2] * 1e3, 2) if rp else None,
-                               "p99": round(rp[min(len(rp) - 1, math.ceil(0.99 * len(rp)) - 1)] * 1e3, 2) if rp else None,
-                               "events": n_route, "scope": f"all {wl.n_layers} layers x batch {wl.batch}"},
+        "route_us_per_event": {**stats_us(route_k_ms), "events": n_route,
+                               "scope": f"all {wl.n_layers} layers x batch {wl.batch}",
+                               "timing": "routing kernel's dispatch start to migration kernel's dispatch end"},
+        "route_us_per_event_stream_events": {**stats_us(route_ms),
+                                             "timing": "hipEventRecord before and after the routing call"},
         "hbm_gbps_split_kernel": round(achieved_gbps, 1),
         "hbm_frac_of_peak": round(achieved_gbps / HBM_PEAK_GBPS, 4),
         "prefill_s": round(t_pf, 3),

@@ -244,7 +244,8 @@ qevict_status qevict_poll_status(qevict_state* st, uint32_t* status, void* strea
  *     status, counters[8] of the last routing event (aged, promoted, packed,
  *     reactivated, demoted, evicted, n_full, n_quant), n_acc, prompt_len,
  *     fp64 head-averaged prefill attention mass on the sink prefix (2 words),
- *     2 reserved words
+ *     the count of promotions that took a page a demotion's pack read at the same
+ *     routing event (written after that pack), 1 reserved word
  *   per window w < n_windows_created: int32 state (1 recent, 2 Full,
  *     3 Quantized, 4 Evicted), int32 has_ledger, int32 dormant, int32 start_pos,
  *     fp64 score
@@ -270,6 +271,13 @@ qevict_status qevict_export_unit(qevict_state* st, int32_t layer, int32_t b, voi
  * created with timing) at the kernel's start and ev_after at its end; then
  * both are forgotten.  Both or neither must be given; NULL disables. */
 qevict_status qevict_time_next_decode(qevict_state* st, void* ev_before, void* ev_after);
+
+/* Profiling aid: the next qevict_route call launches its routing kernel so that its
+ * dispatch stamps ev_before (a hipEvent_t created with timing) at the kernel's start, and
+ * its migration kernel so that that dispatch stamps ev_after at its end: the GPU span of
+ * the routing event, without event packets of their own in the stream; then both are
+ * forgotten.  Both or neither must be given; NULL disables. */
+qevict_status qevict_time_next_route(qevict_state* st, void* ev_before, void* ev_after);
 
 /* Bytes the next decode step of `layer` must move, summed over the batch
  * [host outputs]: kv_bytes = bf16 K/V of the sink, recent and Full tokens

@@ -33,6 +33,7 @@ EXPORTED_SYMBOLS = (
     "qevict_capacities", "qevict_plan", "qevict_create", "qevict_destroy", "qevict_prefill_init",
     "qevict_decode_attn", "qevict_route", "qevict_pack_int2", "qevict_promote", "qevict_poll_status",
     "qevict_export_unit", "qevict_decode_kernel_name", "qevict_last_error", "qevict_time_next_decode",
+    "qevict_time_next_route",
     "qevict_step_bytes", "qevict_stream_read", "qevict_set_rope", "qevict_step_mass",
     "qevict_prefill_init_noalloc",
 )
@@ -94,6 +95,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qevict_poll_status.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
     lib.qevict_export_unit.argtypes = [P, I, I, P, Z, ctypes.POINTER(Z), P]
     lib.qevict_time_next_decode.argtypes = [P, P, P]
+    lib.qevict_time_next_route.argtypes = [P, P, P]
     lib.qevict_step_bytes.argtypes = [P, I, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64), P]
     lib.qevict_stream_read.argtypes = [P, Z, P, P, P, P]
     lib.qevict_set_rope.argtypes = [P, P, I, P]
@@ -326,6 +328,12 @@ class QEvictState:
         _check(self.lib.qevict_time_next_decode(self.handle, ctypes.c_void_p(ev_before.cuda_event),
                                                 ctypes.c_void_p(ev_after.cuda_event)))
 
+    def time_next_route(self, ev_before, ev_after):
+        """Have the next route stamp a torch.cuda.Event pair (timing enabled, already recorded once)
+        at the start of its routing kernel and the end of its migration kernel."""
+        _check(self.lib.qevict_time_next_route(self.handle, ctypes.c_void_p(ev_before.cuda_event),
+                                               ctypes.c_void_p(ev_after.cuda_event)))
+
     def step_bytes(self, layer: int, stream=None) -> tuple[int, int]:
         kv, io = ctypes.c_int64(), ctypes.c_int64()
         _check(self.lib.qevict_step_bytes(self.handle, layer, ctypes.byref(kv), ctypes.byref(io), _stream(stream)))
@@ -351,6 +359,7 @@ def parse_export(blob: bytes, cfg: Config, n_splits: int, tables_only: bool = Fa
     assert head[0] == 0x58564551, "bad export magic"
     n, nw, K_f, K_q, status = head[1:6]
     ctr = dict(zip(COUNTER_NAMES, head[6:14]))
+    ctr["paired_fills"] = head[18]   # promotions into a page a pack read at the same event
     n_acc, prompt_len = head[14], head[15]
     sink_mass = struct.unpack_from("<d", blob, 64)[0]
     at = 80

@@ -256,6 +256,7 @@ struct qevict_state {
     std::vector<uint8_t> step_fresh;                      // per layer: a decode step and no routing since
     bool rope_set = false;                                // RoPE mode: table copied in
     hipEvent_t ev_before = nullptr, ev_after = nullptr;   // one-shot timing of the split kernel
+    hipEvent_t rev_before = nullptr, rev_after = nullptr; // one-shot timing of a routing event
     int device = -1;                                      // the device current at qevict_create
 };
 
@@ -453,6 +454,14 @@ qevict_status qevict_time_next_decode(qevict_state* st, void* ev_before, void* e
     return QEVICT_OK;
 }
 
+qevict_status qevict_time_next_route(qevict_state* st, void* ev_before, void* ev_after) {
+    if (!st) return fail(QEVICT_E_INVALID, "null state");
+    if ((ev_before == nullptr) != (ev_after == nullptr)) return fail(QEVICT_E_INVALID, "give both events or neither");
+    st->rev_before = (hipEvent_t)ev_before;
+    st->rev_after = (hipEvent_t)ev_after;
+    return QEVICT_OK;
+}
+
 qevict_status qevict_step_bytes(qevict_state* st, int32_t layer, int64_t* kv_bytes, int64_t* io_bytes, void* stream) {
     qevict_status s = check_layer(st, layer, false);
     if (s) return s;
@@ -489,7 +498,8 @@ qevict_status qevict_route(qevict_state* st, int32_t layer, void* stream) {
     for (int l = 0; l < st->cfg.n_layers; ++l)
         if ((layer == -1 || layer == l) && !st->prefilled[l]) return fail(QEVICT_E_STATE, "layer %d has no prefill", l);
     hipStream_t hs = (hipStream_t)stream;
-    HIP_TRY(launch_route(st->lay.g, st->bf, layer, RM_ROUTE, nullptr, nullptr, hs));
+    HIP_TRY(launch_route(st->lay.g, st->bf, layer, RM_ROUTE, nullptr, nullptr, hs, st->rev_before, st->rev_after));
+    st->rev_before = st->rev_after = nullptr;
     for (int l = 0; l < st->cfg.n_layers; ++l)
         if (layer == -1 || layer == l) st->step_fresh[l] = 0;
     return QEVICT_OK;
@@ -594,6 +604,7 @@ qevict_status qevict_export_unit(qevict_state* st, int32_t layer, int32_t b, voi
     head[14] = hdr.n_acc;
     head[15] = hdr.prompt_len;
     memcpy(&head[16], &hdr.sink_mass, 8);
+    head[18] = hdr.paired;
     put(head, sizeof head);
     for (int w = 0; w < n_created; ++w) {
         int32_t rec[4] = {win[w].state, (win[w].flags & WF_LEDGER) ? 1 : 0, (win[w].flags & WF_DORMANT) ? 1 : 0,

@@ -40,13 +40,15 @@ struct PackItem {    // quantize a window once: source bf16 -> slot
     int32_t src_prompt;  // 1: caller prompt buffer, 0: page
     int32_t src_page;
     int32_t dst_slot;
+    int32_t then_fill;   // >= 0: the fill item that reuses src_page at this event (runs after this pack)
+    int32_t pad[3];
 };
 
 struct FillItem {    // write a bf16 page: promote from a slot, or copy from the prompt
     int32_t win;
     int32_t dst_page;
     int32_t src_slot;    // >= 0: promote (dequantize); -1: copy prompt tokens
-    int32_t pad;
+    int32_t after_pack;  // 1: dst_page was freed by a window packed at this event (run by that pack item)
 };
 
 struct UnitHdr {
@@ -62,7 +64,7 @@ struct UnitHdr {
     int32_t K_f;
     int32_t K_q;
     int32_t ctr[8];
-    int32_t pad0;
+    int32_t paired;       // fill items run as the second half of a pack item (reused page), since creation
     double sink_mass;     // prefill: head-averaged attention mass on the sink prefix
     int32_t mass_pending; // 1: the last decode step's window-mass shares are not yet in score[]
     int32_t pos;          // decode: position of the step's token (written by the split kernel)
@@ -230,8 +232,10 @@ hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t
 hipError_t launch_finish(const Geo& g, const Bufs& bf, int layer, float* out, const uint16_t* k_new,
                          const uint16_t* v_new, int score_now, hipStream_t s);
 hipError_t launch_flush_mass(const Geo& g, const Bufs& bf, int layer, int b, hipStream_t s);
+// ev0 / ev1 (optional): stamped by the dispatch of the routing kernel at its start and of the
+// migration kernel at its end
 hipError_t launch_route(const Geo& g, const Bufs& bf, int layer, int mode, const uint16_t* kp, const uint16_t* vp,
-                        hipStream_t s);
+                        hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_force_targets(const Geo& g, const Bufs& bf, int layer, const int32_t* win_ids, int n, int target,
                                 hipStream_t s);
 hipError_t launch_prefill_setup(const Geo& g, const Bufs& bf, int layer, const uint16_t* kp, const uint16_t* vp,

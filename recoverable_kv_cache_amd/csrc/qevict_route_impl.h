@@ -485,6 +485,12 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     }
     __syncthreads();
     int* pushed = sm.idx;     // ids pushed at this event, by stack position - cnt0 (sm.idx is free after phase 3)
+    // pages: the window that took each page pushed at this event (-1: none), by push position
+    int* taker = flag + RT_MAXW;
+    constexpr int PACKED = 0x40000000;   // (pages) pushed by a window packed at this event
+    int my_push[RT_PER], my_taken_from[RT_PER];
+#pragma unroll
+    for (int i = 0; i < RT_PER; ++i) my_push[i] = my_taken_from[i] = -1;
     for (int pass = 0; pass < 2; ++pass) {      // pass 0: slots, pass 1: pages
         const int fbit = pass == 0 ? 4 : 1, nbit = pass == 0 ? 8 : 2;
         int32_t* stack = pass == 0 ? fslot : fpage;
@@ -503,7 +509,11 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
                 const int pos = cnt0 + (flag[tid + i * RT_THREADS] & 0xFFFF);
                 const int id = pass == 0 ? my_slot[i] : my_page[i];
                 if (pos < cap && id >= 0) stack[pos] = id;
-                pushed[pos - cnt0] = id;
+                pushed[pos - cnt0] = id | (pass == 1 && (act[i] & 16) && id >= 0 ? PACKED : 0);
+                if (pass == 1) {
+                    taker[pos - cnt0] = -1;
+                    my_push[i] = pos - cnt0;
+                }
                 if (pass == 0) my_slot[i] = -1;
                 else my_page[i] = -1;
             }
@@ -515,7 +525,14 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
             if (act[i] & nbit) {
                 const int k = flag[tid + i * RT_THREADS] >> 16;
                 const int at = avail - 1 - k;
-                const int id = k >= avail ? -1 : (at >= cnt0 ? pushed[at - cnt0] : stack[at]);
+                int id = k >= avail ? -1 : (at >= cnt0 ? pushed[at - cnt0] : stack[at]);
+                if (id >= 0 && (id & PACKED)) {   // a page the pack of its window reads at this event
+                    id &= ~PACKED;
+                    if (act[i] & 32) {            // ... and a fill writes (a fresh recent page is
+                        taker[at - cnt0] = tid + i * RT_THREADS;   // written only by later steps)
+                        my_taken_from[i] = at - cnt0;
+                    }
+                }
                 if (pass == 0) my_slot[i] = id;
                 else my_page[i] = id;
             }
@@ -532,7 +549,13 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         __syncthreads();
     }
 
-    // ---- 6. work lists: pack (quantize once) and fill (promote / copy prompt)
+    // ---- 6. work lists: pack (quantize once) and fill (promote / copy prompt).  A page freed by
+    //      a window packed at this event and taken by a promotion at this event is written only
+    //      after that pack has read it: the fill item runs as the pack item's second half.
+    int my_taker[RT_PER];
+#pragma unroll
+    for (int i = 0; i < RT_PER; ++i) my_taker[i] = my_push[i] >= 0 && (act[i] & 16) ? taker[my_push[i]] : -1;
+    __syncthreads();   // (taker lives in the upper half of the scan array)
 #pragma unroll
     for (int i = 0; i < RT_PER; ++i)   // pack count (low field), fill count (high field)
         flag[tid + i * RT_THREADS] = ((act[i] & 16) ? 1 : 0) | ((act[i] & 32) ? 0x10000 : 0);
@@ -550,6 +573,8 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
             it.src_prompt = r.state == ST_PROMPT ? 1 : 0;
             it.src_page = r.page;
             it.dst_slot = my_slot[i];
+            it.then_fill = my_taker[i] >= 0 ? (flag[my_taker[i]] >> 16) : -1;
+            it.pad[0] = it.pad[1] = it.pad[2] = 0;
             bf.pack[u * g.n_windows + (flag[w] & 0xFFFF)] = it;
         }
         if (act[i] & 32) {
@@ -557,8 +582,9 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
             it.win = w;
             it.dst_page = my_page[i];
             it.src_slot = r.state == ST_QUANT ? r.slot : -1;   // promote, or copy the prompt tokens
-            it.pad = 0;
+            it.after_pack = my_taken_from[i] >= 0 ? 1 : 0;
             bf.fill[u * g.n_windows + (flag[w] >> 16)] = it;
+            if (it.after_pack) atomicAdd(&hdr->paired, 1);
         }
     }
     if (tid == 0) {

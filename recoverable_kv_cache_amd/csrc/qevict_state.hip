@@ -9,6 +9,8 @@
 #include "qevict_internal.h"
 
 #include <type_traits>
+#include <hip/hip_ext.h>
+
 #include "qevict_mass.h"
 
 namespace qv {
@@ -208,41 +210,14 @@ namespace rt256 {
 // workgroups of a migration kernel share (few items per routing event: a grid sized by
 // unit would be almost all empty workgroups).  Every workgroup reads the per-unit counts
 // and keeps their running sums in LDS; a list index finds its unit by binary search.
-constexpr int PK_THREADS = 1024;  // threads of the migration kernels (one item per workgroup: latency)
+// (512 threads: with 1024 a thread has 128 registers, and the pack and fill items of one
+// kernel then spill)
+constexpr int PK_THREADS = 512;   // threads of the migration kernel (one item per workgroup: latency)
 
 __device__ __forceinline__ int64_t mig_unit(const Geo& g, int layer, int ub, int& b) {
     b = layer >= 0 ? ub : ub / g.L;
     const int l = layer >= 0 ? layer : ub % g.L;
     return unit_of(g, b, l);
-}
-// pre[ub] = items of units before ub, pre[n_units] = all items; count(u) = a unit's items.
-// All PK_THREADS threads call.
-template <typename Count>
-__device__ int mig_prefix(const Geo& g, int layer, int n_units, int* pre, int* wtot, Count count) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int per = (n_units + PK_THREADS - 1) / PK_THREADS, u0 = tid * per;
-    int s = 0;
-    for (int k = 0; k < per; ++k) {
-        const int ub = u0 + k;
-        int b;
-        if (ub < n_units) s += count(mig_unit(g, layer, ub, b));
-    }
-    const int incl = (int)wave_scan_incl((unsigned)s);
-    if (lane == 63) wtot[wave] = incl;
-    __syncthreads();
-    int run = incl - s;
-    for (int q = 0; q < wave; ++q) run += wtot[q];
-    for (int k = 0; k < per; ++k) {
-        const int ub = u0 + k;
-        int b;
-        if (ub < n_units) {
-            pre[ub] = run;
-            run += count(mig_unit(g, layer, ub, b));
-        }
-    }
-    if (tid == PK_THREADS - 1) pre[n_units] = run;
-    __syncthreads();
-    return pre[n_units];
 }
 // the unit of list index i: the last ub with pre[ub] <= i
 __device__ __forceinline__ int mig_find(const int* pre, int n_units, int i) {
@@ -266,7 +241,7 @@ __device__ __forceinline__ int mig_find(const int* pre, int n_units, int i) {
 // [token][channel] order by 16-byte loads; the parameters are min / max reductions with
 // every thread taking a slice (a key channel's tokens, a value token's channels), combined
 // across lanes; then each thread produces code bytes of the slot, computing the codes of
-// each byte where it is written.  A workgroup of 1024 threads takes one item at a time:
+// each byte where it is written.  A workgroup of 512 threads takes one item at a time:
 // a routing event moves few windows, and their latency is what counts.
 constexpr int PK_MAXE = 64 * 128;   // W * d
 
@@ -343,38 +318,45 @@ __device__ __forceinline__ int nearest_level(double t2, double scl, double inv, 
     return scl == 0.0 ? 0 : k;
 }
 
-// The same launch copies each split's block (header {entries, first entry, -1, 0} and its
-// first SPLIT_BLOCK - 1 accessible-list entries) from the list k_route has rebuilt.
 // W, d, QB: the window, head dimension and code bits (one instance per supported shape, so
 // that the layout arithmetic is shifts and masks)
+// LDS of the migration kernel: a pack item's bf16 staging and parameters, or a fill item's
+// slot words (the two never hold data at the same time), and the work-list sums
+struct MigSmem {
+    union {
+        struct {
+            uint16_t sk[PK_MAXE];
+            uint16_t sv[PK_MAXE];
+        } p;
+        uint32_t sw[(2 * PK_MAXE / 2 + 4 * (128 + 64)) / 4];   // slot head words at W*d = 8192, INT4
+    } st;
+    double p_off[128 + 64], p_scl[128 + 64], p_inv[128 + 64];   // key channels, then value tokens
+    uint16_t p_bits[2 * (128 + 64)];
+    int pre[MIG_MAX_UNITS + 1];     // pack items of the units before each unit
+    int pre_f[MIG_MAX_UNITS + 1];   // fill items of the units before each unit
+    int wtot[PK_THREADS / 64], wtot2[PK_THREADS / 64];
+};
+
+// One pack item: head h of window pi.win of unit u into slot pi.dst_slot.  All threads call.
 template <int W, int d, int QB>
-__global__ void __launch_bounds__(PK_THREADS) k_pack(Geo g, Bufs bf, int layer, int n_units,
-                                                     const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp) {
-    __shared__ __align__(16) uint16_t sk[PK_MAXE];
-    __shared__ __align__(16) uint16_t sv[PK_MAXE];
-    __shared__ double p_off[128 + 64], p_scl[128 + 64], p_inv[128 + 64];   // key channels, then value tokens
-    __shared__ uint16_t p_bits[2 * (128 + 64)];
-    __shared__ int pre[MIG_MAX_UNITS + 1];
-    __shared__ int wtot[PK_THREADS / 64];
+__device__ void pack_item(const Geo& g, const Bufs& bf, int64_t u, int b, const PackItem& pi, int h,
+                          const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp, MigSmem& sm) {
+    uint16_t* sk = sm.st.p.sk;
+    uint16_t* sv = sm.st.p.sv;
+    double* p_off = sm.p_off;
+    double* p_scl = sm.p_scl;
+    double* p_inv = sm.p_inv;
+    uint16_t* p_bits = sm.p_bits;
     constexpr int WD = W * d;
     const int tid = threadIdx.x;
     const bool rope = (g.flags & QEVICT_F_ROPE) != 0;
     constexpr int hd = d / 2;
-    const int total = mig_prefix(g, layer, n_units, pre, wtot, [&](int64_t u) { return bf.hdr[u].n_pack * g.h_kv; });
-    // (a barrier opens every item but the first: one closing each item would also wait for
-    // the item's global stores)
-    for (int it_all = blockIdx.x; it_all < total; it_all += gridDim.x) {
-        if (it_all != (int)blockIdx.x) __syncthreads();
-        const int ub = mig_find(pre, n_units, it_all), it = it_all - pre[ub];
-        int b;
-        const int64_t u = mig_unit(g, layer, ub, b);
-        UnitHdr* hdr = bf.hdr + u;
-        const PackItem pi = bf.pack[u * g.n_windows + it / g.h_kv];
-        const int h = it % g.h_kv;
+    UnitHdr* hdr = bf.hdr + u;
+    {
         const int start = g.n_sink + pi.win * W;
         if (pi.dst_slot < 0 || (!pi.src_prompt && pi.src_page < 0)) {
             if (tid == 0) atomicOr(&hdr->status, QEVICT_DEV_E_POOL);
-            continue;
+            return;
         }
         // ---- stage keys and values, [token][channel]
         if (pi.src_prompt) {
@@ -522,35 +504,6 @@ __global__ void __launch_bounds__(PK_THREADS) k_pack(Geo g, Bufs bf, int layer, 
         }
         for (int i = tid; i < 2 * (d + W); i += PK_THREADS) params16[i] = p_bits[i];
     }
-    // ---- split blocks (after the items: no barrier follows these stores)
-    {   // two blocks per thread and round, their loads issued together
-        constexpr int PER = PK_THREADS / SPLIT_BLOCK;
-        const int n_blk = n_units * g.n_splits, x = tid % SPLIT_BLOCK, stride = gridDim.x * PER;
-        for (int k0 = blockIdx.x * PER + tid / SPLIT_BLOCK; k0 < n_blk; k0 += 2 * stride) {
-            int64_t uu[2];
-            int ss[2], e0[2], cnt[2];
-            bool ok[2];
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int k = k0 + r * stride;
-                ok[r] = k < n_blk;
-                int b;
-                uu[r] = mig_unit(g, layer, ok[r] ? k / g.n_splits : 0, b);
-                ss[r] = k % g.n_splits;
-                const int32_t* splits = bf.splits + uu[r] * (g.n_splits + 1);
-                e0[r] = ok[r] ? splits[ss[r]] : 0;
-                cnt[r] = ok[r] ? splits[ss[r] + 1] - e0[r] : 0;
-            }
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                if (!ok[r]) continue;
-                AccEntry v = AccEntry{EK_PAGE, -1, -1, 0};
-                if (x == 0) v = AccEntry{cnt[r], e0[r], -1, 0};
-                else if (x - 1 < cnt[r]) v = bf.acc[uu[r] * g.n_acc_max + e0[r] + x - 1];
-                bf.split_blk[(uu[r] * g.n_splits + ss[r]) * SPLIT_BLOCK + x] = v;
-            }
-        }
-    }
 }
 
 // ------------------------------------------------------------------------------------ fill (promote / copy)
@@ -559,28 +512,19 @@ __global__ void __launch_bounds__(PK_THREADS) k_pack(Geo g, Bufs bf, int layer, 
 // datatype).  Prefill copies prompt tokens into pages.  One workgroup per (window, KV
 // head) item; the slot comes into LDS by 32-bit loads, and every thread writes whole
 // 16-byte runs of the page (8 consecutive elements of its key / value block).
+// One fill item: head h of window fi.win of unit u into page fi.dst_page.  All threads call.
 template <int W, int d, int QB>
-__global__ void __launch_bounds__(PK_THREADS) k_fill(Geo g, Bufs bf, int layer, int n_units,
-                                                     const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp) {
-    constexpr int MAXW = (2 * PK_MAXE / 2 + 4 * (128 + 64)) / 4;   // slot head words at W*d = 8192, INT4
-    __shared__ uint32_t sw[MAXW];
-    __shared__ int pre[MIG_MAX_UNITS + 1];
-    __shared__ int wtot[PK_THREADS / 64];
+__device__ void fill_item(const Geo& g, const Bufs& bf, int64_t u, int b, const FillItem& fi, int h,
+                          const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp, MigSmem& smem) {
+    uint32_t* sw = smem.st.sw;
     constexpr int WD = W * d;
     const int tid = threadIdx.x;
-    const int total = mig_prefix(g, layer, n_units, pre, wtot, [&](int64_t u) { return bf.hdr[u].n_fill * g.h_kv; });
-    for (int it_all = blockIdx.x; it_all < total; it_all += gridDim.x) {
-        if (it_all != (int)blockIdx.x) __syncthreads();   // (sw is restaged: the previous item's reads are done)
-        const int ub = mig_find(pre, n_units, it_all), it = it_all - pre[ub];
-        int b;
-        const int64_t u = mig_unit(g, layer, ub, b);
-        UnitHdr* hdr = bf.hdr + u;
+    UnitHdr* hdr = bf.hdr + u;
+    {
         const int S = hdr->prompt_len;
-        const FillItem fi = bf.fill[u * g.n_windows + it / g.h_kv];
-        const int h = it % g.h_kv;
         if (fi.dst_page < 0) {
             if (tid == 0) atomicOr(&hdr->status, QEVICT_DEV_E_POOL);
-            continue;
+            return;
         }
         uint16_t* pg = bf.pages + u * (int64_t)g.n_pages * g.page_elems + (int64_t)fi.dst_page * g.page_elems;
         uint16_t* dk = pg + (int64_t)(2 * h) * WD;
@@ -668,50 +612,170 @@ __global__ void __launch_bounds__(PK_THREADS) k_fill(Geo g, Bufs bf, int layer, 
     }
 }
 
+// The migrations of a routing event in one launch: the pack items, each followed by the fill
+// item that reuses its source page at this event (if any: a promotion may take a page that a
+// demotion frees, and must write it only after the pack has read it); then the other fill
+// items, which touch no page a pack reads; then each split's block (header {entries, first
+// entry, -1, 0} and its first SPLIT_BLOCK - 1 accessible-list entries) of the list k_route
+// has rebuilt.
+template <int W, int d, int QB>
+__global__ void __launch_bounds__(PK_THREADS) k_migrate(Geo g, Bufs bf, int layer, int n_units,
+                                                        const uint16_t* __restrict__ kp,
+                                                        const uint16_t* __restrict__ vp) {
+    __shared__ MigSmem sm;
+    const int tid = threadIdx.x;
+    // the list: all pack items (unit by unit), then all fill items; each unit's counts are
+    // read once, and both running sums kept in LDS
+    {
+        constexpr int MAXPER = (MIG_MAX_UNITS + PK_THREADS - 1) / PK_THREADS;
+        const int lane = tid & 63, wave = tid >> 6;
+        const int per = (n_units + PK_THREADS - 1) / PK_THREADS, u0 = tid * per;
+        int cp[MAXPER], cf[MAXPER], sp = 0, sf = 0;
+#pragma unroll
+        for (int k = 0; k < MAXPER; ++k) {
+            cp[k] = cf[k] = 0;
+            if (k < per && u0 + k < n_units) {
+                int b;
+                const UnitHdr* hd = bf.hdr + mig_unit(g, layer, u0 + k, b);
+                cp[k] = hd->n_pack * g.h_kv;
+                cf[k] = hd->n_fill * g.h_kv;
+            }
+            sp += cp[k];
+            sf += cf[k];
+        }
+        const int ip = (int)wave_scan_incl((unsigned)sp), jf = (int)wave_scan_incl((unsigned)sf);
+        if (lane == 63) {
+            sm.wtot[wave] = ip;
+            sm.wtot2[wave] = jf;
+        }
+        __syncthreads();
+        int rp = ip - sp, rf = jf - sf;
+        for (int q = 0; q < wave; ++q) {
+            rp += sm.wtot[q];
+            rf += sm.wtot2[q];
+        }
+#pragma unroll
+        for (int k = 0; k < MAXPER; ++k) {
+            if (k < per && u0 + k < n_units) {
+                sm.pre[u0 + k] = rp;
+                sm.pre_f[u0 + k] = rf;
+            }
+            rp += cp[k];
+            rf += cf[k];
+        }
+        if (tid == PK_THREADS - 1) {
+            sm.pre[n_units] = rp;
+            sm.pre_f[n_units] = rf;
+        }
+        __syncthreads();
+    }
+    const int tp = sm.pre[n_units], tf = sm.pre_f[n_units];
+    // (a barrier opens every item but the first: one closing each item would also wait for
+    // the item's global stores)
+    bool first = true;
+    auto open_item = [&]() {
+        if (!first) __syncthreads();
+        first = false;
+    };
+    for (int it_all = blockIdx.x; it_all < tp + tf; it_all += gridDim.x) {
+        const bool is_pack = it_all < tp;
+        const int* pre = is_pack ? sm.pre : sm.pre_f;
+        const int ia = is_pack ? it_all : it_all - tp;
+        const int ub = mig_find(pre, n_units, ia), it = ia - pre[ub];
+        int b;
+        const int64_t u = mig_unit(g, layer, ub, b);
+        const int h = it % g.h_kv;
+        FillItem fi;
+        bool do_fill;
+        if (is_pack) {
+            const PackItem pi = bf.pack[u * g.n_windows + it / g.h_kv];
+            open_item();
+            pack_item<W, d, QB>(g, bf, u, b, pi, h, kp, vp, sm);
+            do_fill = pi.then_fill >= 0;
+            if (do_fill) fi = bf.fill[u * g.n_windows + pi.then_fill];
+        } else {
+            fi = bf.fill[u * g.n_windows + it / g.h_kv];
+            do_fill = !fi.after_pack;
+        }
+        if (do_fill) {
+            open_item();   // (after a pack: also, every read of its page is done)
+            fill_item<W, d, QB>(g, bf, u, b, fi, h, kp, vp, sm);
+        }
+    }
+    // ---- split blocks (after the items: no barrier follows these stores)
+    {   // two blocks per thread and round, their loads issued together
+        constexpr int PER = PK_THREADS / SPLIT_BLOCK;
+        const int n_blk = n_units * g.n_splits, x = tid % SPLIT_BLOCK, stride = gridDim.x * PER;
+        for (int k0 = blockIdx.x * PER + tid / SPLIT_BLOCK; k0 < n_blk; k0 += 2 * stride) {
+            int64_t uu[2];
+            int ss[2], e0[2], cnt[2];
+            bool ok[2];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int k = k0 + r * stride;
+                ok[r] = k < n_blk;
+                int b;
+                uu[r] = mig_unit(g, layer, ok[r] ? k / g.n_splits : 0, b);
+                ss[r] = k % g.n_splits;
+                const int32_t* splits = bf.splits + uu[r] * (g.n_splits + 1);
+                e0[r] = ok[r] ? splits[ss[r]] : 0;
+                cnt[r] = ok[r] ? splits[ss[r] + 1] - e0[r] : 0;
+            }
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                if (!ok[r]) continue;
+                AccEntry v = AccEntry{EK_PAGE, -1, -1, 0};
+                if (x == 0) v = AccEntry{cnt[r], e0[r], -1, 0};
+                else if (x - 1 < cnt[r]) v = bf.acc[uu[r] * g.n_acc_max + e0[r] + x - 1];
+                bf.split_blk[(uu[r] * g.n_splits + ss[r]) * SPLIT_BLOCK + x] = v;
+            }
+        }
+    }
+}
+
 template <int W, int d, int QB>
 static void launch_mig_t(dim3 grid, const Geo& g, const Bufs& bf, int layer, int units, const uint16_t* kp,
-                         const uint16_t* vp, hipStream_t s) {
-    hipLaunchKernelGGL((k_pack<W, d, QB>), grid, dim3(PK_THREADS), 0, s, g, bf, layer, units, kp, vp);
-    hipLaunchKernelGGL((k_fill<W, d, QB>), grid, dim3(PK_THREADS), 0, s, g, bf, layer, units, kp, vp);
+                         const uint16_t* vp, hipStream_t s, hipEvent_t ev1) {
+    hipExtLaunchKernelGGL((k_migrate<W, d, QB>), grid, dim3(PK_THREADS), 0, s, nullptr, ev1, 0, g, bf, layer, units, kp,
+                          vp);
 }
 template <int W, int d>
 static void launch_mig_q(dim3 grid, const Geo& g, const Bufs& bf, int layer, int units, const uint16_t* kp,
-                         const uint16_t* vp, hipStream_t s) {
-    if (g.qbits == 4) launch_mig_t<W, d, 4>(grid, g, bf, layer, units, kp, vp, s);
-    else launch_mig_t<W, d, 2>(grid, g, bf, layer, units, kp, vp, s);
+                         const uint16_t* vp, hipStream_t s, hipEvent_t ev1) {
+    if (g.qbits == 4) launch_mig_t<W, d, 4>(grid, g, bf, layer, units, kp, vp, s, ev1);
+    else launch_mig_t<W, d, 2>(grid, g, bf, layer, units, kp, vp, s, ev1);
 }
 template <int W>
 static void launch_mig_d(dim3 grid, const Geo& g, const Bufs& bf, int layer, int units, const uint16_t* kp,
-                         const uint16_t* vp, hipStream_t s) {
-    if (g.d == 64) launch_mig_q<W, 64>(grid, g, bf, layer, units, kp, vp, s);
-    else launch_mig_q<W, 128>(grid, g, bf, layer, units, kp, vp, s);
+                         const uint16_t* vp, hipStream_t s, hipEvent_t ev1) {
+    if (g.d == 64) launch_mig_q<W, 64>(grid, g, bf, layer, units, kp, vp, s, ev1);
+    else launch_mig_q<W, 128>(grid, g, bf, layer, units, kp, vp, s, ev1);
 }
 // (the shapes the configuration accepts: W 16 / 32 / 64, d 64 / 128, 2 / 4 code bits)
 static void launch_mig(dim3 grid, const Geo& g, const Bufs& bf, int layer, int units, const uint16_t* kp,
-                       const uint16_t* vp, hipStream_t s) {
-    if (g.W == 16) launch_mig_d<16>(grid, g, bf, layer, units, kp, vp, s);
-    else if (g.W == 32) launch_mig_d<32>(grid, g, bf, layer, units, kp, vp, s);
-    else launch_mig_d<64>(grid, g, bf, layer, units, kp, vp, s);
+                       const uint16_t* vp, hipStream_t s, hipEvent_t ev1) {
+    if (g.W == 16) launch_mig_d<16>(grid, g, bf, layer, units, kp, vp, s, ev1);
+    else if (g.W == 32) launch_mig_d<32>(grid, g, bf, layer, units, kp, vp, s, ev1);
+    else launch_mig_d<64>(grid, g, bf, layer, units, kp, vp, s, ev1);
 }
 
 // Routing (every unit of the layer, or of all layers with layer = -1) and the migrations it
-// decides: k_route, then k_pack (with the split blocks of the new list), then k_fill (a
-// page freed by a demotion at this event may take a promotion: the pack reads it first).
+// decides: k_route, then k_migrate (packs, fills, the split blocks of the new list).
 hipError_t launch_route(const Geo& g, const Bufs& bf, int layer, int mode, const uint16_t* kp, const uint16_t* vp,
-                        hipStream_t s) {
+                        hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const int units = layer >= 0 ? g.B : g.B * g.L;
     if (units > MIG_MAX_UNITS || g.n_windows > rt1024::RT_MAXW) return hipErrorInvalidValue;
     // units of at most 1024 windows: 256-thread workgroups, eight per CU instead of two
     if (g.n_windows <= rt256::RT_MAXW)
-        hipLaunchKernelGGL(rt256::k_route, dim3(units), dim3(rt256::RT_THREADS), sizeof(rt256::RouteSmem), s, g, bf,
-                           layer, mode);
+        hipExtLaunchKernelGGL(rt256::k_route, dim3(units), dim3(rt256::RT_THREADS), sizeof(rt256::RouteSmem), s, ev0,
+                              nullptr, 0, g, bf, layer, mode);
     else
-        hipLaunchKernelGGL(rt1024::k_route, dim3(units), dim3(rt1024::RT_THREADS), sizeof(rt1024::RouteSmem), s, g,
-                           bf, layer, mode);
+        hipExtLaunchKernelGGL(rt1024::k_route, dim3(units), dim3(rt1024::RT_THREADS), sizeof(rt1024::RouteSmem), s,
+                              ev0, nullptr, 0, g, bf, layer, mode);
     // workgroups: a prefill (one layer, every prompt window) spreads its items over 1024;
     // a routing event moves a few windows per unit
     const int nb = layer >= 0 ? 1024 : std::min(1024, std::max(256, 8 * units));
-    launch_mig(dim3(nb), g, bf, layer, units, kp, vp, s);
+    launch_mig(dim3(nb), g, bf, layer, units, kp, vp, s, ev1);
     return hipGetLastError();
 }
 

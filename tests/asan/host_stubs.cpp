@@ -66,7 +66,8 @@ hipError_t launch_finish(const Geo&, const Bufs&, int, float*, const uint16_t*, 
     return hipSuccess;
 }
 hipError_t launch_flush_mass(const Geo&, const Bufs&, int, int, hipStream_t) { return hipSuccess; }
-hipError_t launch_route(const Geo&, const Bufs&, int, int, const uint16_t*, const uint16_t*, hipStream_t) {
+hipError_t launch_route(const Geo&, const Bufs&, int, int, const uint16_t*, const uint16_t*, hipStream_t, hipEvent_t,
+                        hipEvent_t) {
     return hipSuccess;
 }
 hipError_t launch_force_targets(const Geo&, const Bufs&, int, const int32_t*, int, int, hipStream_t) {

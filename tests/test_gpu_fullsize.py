@@ -157,6 +157,8 @@ def test_churn_4k_b64_sampled_lockstep_across_a_topic_switch():
     print(f"churn: max o err {ls.max_o_err:.2e} (bf16 reading {ls.max_o_err_bf16:.2e}, gap {ls.max_reading_gap:.2e}), max score err {ls.max_s_err:.2e}, events {ls.events}, "
           f"moves {moved}", flush=True)
     assert ls.events == 33 and moved > 0
+    print("churn: fills after a pack of their page", [ls.st.export_unit(0, b).counters["paired_fills"] for b in (0, 63)],
+          flush=True)
 
 
 def test_llama70b_128k_b4_sampled_lockstep():

@@ -49,6 +49,7 @@ def test_drift_with_promotions_and_splits():
     assert sum(e["promoted"] for e in unit.events) > 0
     ex = ls.st.export_unit(0, 0)
     assert ex.counters["n_full"] == unit.events[-1]["n_full"]
+    _print(f"drift: promotions {sum(e['promoted'] for e in unit.events)}, fills after a pack of their page {ex.counters['paired_fills']}")
 
 
 def test_batched_ragged_prompts_gqa8_d128():
@@ -78,6 +79,7 @@ def test_single_launch_step_and_finish_launch(n_splits):
         _print(f"n_splits={n_splits} flags={flags}: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}")
         assert ls.st.poll_status() == 0
         assert sum(e["promoted"] for e in ls.units[0].events) + sum(e["promoted"] for e in ls.units[1].events) > 0
+        _print("fills after a pack of their page:", [ls.st.export_unit(0, b).counters["paired_fills"] for b in range(2)])
 
 
 def test_window64_gqa8_multichunk():
