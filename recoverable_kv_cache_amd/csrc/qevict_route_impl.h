@@ -260,9 +260,23 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     WinRec* win = bf.win + u * g.n_windows;
     double* score = bf.score + u * g.n_windows;
     int8_t* target = bf.target + u * g.n_windows;
+    const int NW = g.n_windows;
+    // Loads that depend on nothing read here go first, with the header, so that they share
+    // one round trip: the accessible entry this thread folds first, and the window records
+    // and rank keys of its windows w = tid + i * RT_THREADS (the rank keys again below when
+    // a ranker rewrites them in memory first).
+    const int e_first = 1 + tid;
+    const AccEntry en_first = bf.acc[u * g.n_acc_max + (e_first < g.n_acc_max ? e_first : g.n_acc_max - 1)];
+    WinRec rec[RT_PER];
+    double sc[RT_PER];
+#pragma unroll
+    for (int i = 0; i < RT_PER; ++i) {
+        const int w = tid + i * RT_THREADS;
+        rec[i] = w < NW ? win[w] : WinRec{ST_NONE, -1, -1, 0};
+        sc[i] = w < NW ? score[w] : 0.0;
+    }
     const int n = hdr->n;
     const int K_f = hdr->K_f, K_q = hdr->K_q;
-    const int NW = g.n_windows;
     int* flag = (int*)sm.work;               // (used after the tier selection)
 
     // ---- 0. the last decode step's window-mass shares (Eq. 1), folded before routing: one
@@ -278,8 +292,8 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         const float* lwin = bf.lse_win + lse_win_off(g, u, (n - 1) & 1);   // the step at position n - 1
         const float* lg = bf.lse_glob + lse_glob_off(g, u, (n - 1) & 1);
         const int n_acc = hdr->n_acc;
-        for (int e = 1 + tid; e < n_acc; e += RT_THREADS) {   // (entry 0: the sinks, no window)
-            const AccEntry en = bf.acc[u * g.n_acc_max + e];
+        for (int e = e_first; e < n_acc; e += RT_THREADS) {   // (entry 0: the sinks, no window)
+            const AccEntry en = e == e_first ? en_first : bf.acc[u * g.n_acc_max + e];
             if (en.win >= 0 && en.win < NW) mwin[en.win] = entry_mass(lwin + (int64_t)e * g.h_q, lg, g.h_q) / g.h_q;
         }
         __syncthreads();
@@ -326,15 +340,12 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
         __syncthreads();
     }
 
-    // the window records and rank keys of this thread's windows w = tid + i * RT_THREADS,
-    // read once (all loads issued together)
-    WinRec rec[RT_PER];
-    double sc[RT_PER];
+    if (mode == RM_ROUTE && (rank_interval(g) || (g.flags & QEVICT_F_RANK_KEYNORM))) {
 #pragma unroll
-    for (int i = 0; i < RT_PER; ++i) {
-        const int w = tid + i * RT_THREADS;
-        rec[i] = w < NW ? win[w] : WinRec{ST_NONE, -1, -1, 0};
-        sc[i] = w < NW ? score[w] : 0.0;
+        for (int i = 0; i < RT_PER; ++i) {   // (rewritten above)
+            const int w = tid + i * RT_THREADS;
+            sc[i] = w < NW ? score[w] : 0.0;
+        }
     }
     if (cum_fold) {   // S_bar(w) += the step's mass (windows with an entry)
 #pragma unroll
@@ -669,6 +680,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     __syncthreads();
     const int total = block_scan_excl(cost, sm.wsum);   // cost[e] = cost of the entries before e
     int32_t* splits = bf.splits + u * (g.n_splits + 1);
+    int* spos = flag + RT_MAXW;    // the boundaries, for the split blocks below (flag is free here)
     for (int s = tid; s <= g.n_splits; s += RT_THREADS) {
         int pos;
         if (s == 0) pos = 0;
@@ -687,8 +699,18 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
             pos = lo;
         }
         splits[s] = pos;
+        spos[s] = pos;
     }
-    // (the split blocks are copied by the pack launch that follows)
+    __syncthreads();   // (also: the list entries above are visible to the whole workgroup)
+    // each split's block: header {entries, first entry, -1, 0}, then its first SPLIT_BLOCK - 1
+    // entries (padding past them), one entry per thread
+    for (int k = tid; k < g.n_splits * SPLIT_BLOCK; k += RT_THREADS) {
+        const int sp = k / SPLIT_BLOCK, x = k % SPLIT_BLOCK, e0 = spos[sp], cnt = spos[sp + 1] - e0;
+        AccEntry v = AccEntry{EK_PAGE, -1, -1, 0};
+        if (x == 0) v = AccEntry{cnt, e0, -1, 0};
+        else if (x - 1 < cnt) v = acc[e0 + x - 1];
+        bf.split_blk[(u * g.n_splits + sp) * SPLIT_BLOCK + x] = v;
+    }
     if (tid == 0) {
         hdr->n_acc = n_acc;
         int nwin = 0;

@@ -615,9 +615,7 @@ __device__ void fill_item(const Geo& g, const Bufs& bf, int64_t u, int b, const 
 // The migrations of a routing event in one launch: the pack items, each followed by the fill
 // item that reuses its source page at this event (if any: a promotion may take a page that a
 // demotion frees, and must write it only after the pack has read it); then the other fill
-// items, which touch no page a pack reads; then each split's block (header {entries, first
-// entry, -1, 0} and its first SPLIT_BLOCK - 1 accessible-list entries) of the list k_route
-// has rebuilt.
+// items, which touch no page a pack reads.
 template <int W, int d, int QB>
 __global__ void __launch_bounds__(PK_THREADS) k_migrate(Geo g, Bufs bf, int layer, int n_units,
                                                         const uint16_t* __restrict__ kp,
@@ -702,35 +700,6 @@ __global__ void __launch_bounds__(PK_THREADS) k_migrate(Geo g, Bufs bf, int laye
             fill_item<W, d, QB>(g, bf, u, b, fi, h, kp, vp, sm);
         }
     }
-    // ---- split blocks (after the items: no barrier follows these stores)
-    {   // two blocks per thread and round, their loads issued together
-        constexpr int PER = PK_THREADS / SPLIT_BLOCK;
-        const int n_blk = n_units * g.n_splits, x = tid % SPLIT_BLOCK, stride = gridDim.x * PER;
-        for (int k0 = blockIdx.x * PER + tid / SPLIT_BLOCK; k0 < n_blk; k0 += 2 * stride) {
-            int64_t uu[2];
-            int ss[2], e0[2], cnt[2];
-            bool ok[2];
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int k = k0 + r * stride;
-                ok[r] = k < n_blk;
-                int b;
-                uu[r] = mig_unit(g, layer, ok[r] ? k / g.n_splits : 0, b);
-                ss[r] = k % g.n_splits;
-                const int32_t* splits = bf.splits + uu[r] * (g.n_splits + 1);
-                e0[r] = ok[r] ? splits[ss[r]] : 0;
-                cnt[r] = ok[r] ? splits[ss[r] + 1] - e0[r] : 0;
-            }
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                if (!ok[r]) continue;
-                AccEntry v = AccEntry{EK_PAGE, -1, -1, 0};
-                if (x == 0) v = AccEntry{cnt[r], e0[r], -1, 0};
-                else if (x - 1 < cnt[r]) v = bf.acc[uu[r] * g.n_acc_max + e0[r] + x - 1];
-                bf.split_blk[(uu[r] * g.n_splits + ss[r]) * SPLIT_BLOCK + x] = v;
-            }
-        }
-    }
 }
 
 template <int W, int d, int QB>
@@ -760,7 +729,7 @@ static void launch_mig(dim3 grid, const Geo& g, const Bufs& bf, int layer, int u
 }
 
 // Routing (every unit of the layer, or of all layers with layer = -1) and the migrations it
-// decides: k_route, then k_migrate (packs, fills, the split blocks of the new list).
+// decides: k_route (which also writes the new list's split blocks), then k_migrate (packs and fills).
 hipError_t launch_route(const Geo& g, const Bufs& bf, int layer, int mode, const uint16_t* kp, const uint16_t* vp,
                         hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const int units = layer >= 0 ? g.B : g.B * g.L;
