@@ -224,7 +224,8 @@ struct Job {
     int i, t, kind, idx, ntok, Wn, start;   // bf16: entry, tile, kind, page id, valid tokens, block width, position 0
 };
 
-template <int D, int G, int TPC, int BITS, bool ROPE>
+// FIN: one split per group, and the workgroup also finishes the step (no finish launch)
+template <int D, int G, int TPC, int BITS, bool ROPE, bool FIN>
 __global__ void __launch_bounds__(64 * DW) __attribute__((amdgpu_waves_per_eu(2)))
 k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, const uint16_t* __restrict__ knew,
                const uint16_t* __restrict__ vnew, float* __restrict__ out, int score_now) {
@@ -837,7 +838,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             // group) or the finish kernel (one writer per unit)
             if (lane == 0) {
                 const int tp = j.kind == EK_SINK ? -2 : j.idx;
-                if (g.fuse) {
+                if constexpr (FIN) {
                     s_tok[0] = n_old;
                     s_tok[1] = tp;
                 } else if (hk == 0) {
@@ -991,7 +992,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
         }
     }
     __syncthreads();
-    // One split per group (g.fuse): the merge is the heads' output, and this workgroup also
+    // One split per group (FIN): the merge is the heads' output, and this workgroup also
     // does what the finish kernel does otherwise.  Else: the split's partial.
     float* pacc = bf.part_acc + ((u * g.n_splits + split) * (int64_t)g.h_q + hk * G) * D;
     float2* pml = bf.part_ml + (u * g.n_splits + split) * (int64_t)g.h_q + hk * G;
@@ -1009,7 +1010,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             L += f * s_l[w][gg];
             A += f * (s_acc[w][gg][c] + s_vb[w][gg]);
         }
-        if (g.fuse) {
+        if constexpr (FIN) {
             og[(int64_t)gg * D + c] = A / L;
             if (c == 0) lseg[gg] = M + log2f(L);
         } else {
@@ -1017,7 +1018,7 @@ k_decode_split(Geo g, Bufs bf, int layer, const uint16_t* __restrict__ qin, cons
             if (c == 0) pml[gg] = make_float2(M, L);
         }
     }
-    if (!g.fuse) return;
+    if constexpr (!FIN) return;
     // ---- the step's token into the block this workgroup attended it in (a window the
     // router did not prepare is an error); then the last of the unit's h_kv workgroups to
     // get here advances the unit's token count (every workgroup of the unit has read it by
@@ -1056,17 +1057,18 @@ hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t
     if (g.fuse && (g.n_splits != 1 || !out)) return hipErrorInvalidValue;
     const dim3 grid(g.n_splits, g.h_kv, g.B), block(64 * DW);
     const int G = g.h_q / g.h_kv, TPC = lay_tpc(g.W);
-    const bool rope = (g.flags & QEVICT_F_ROPE) != 0;
-#define QV_DEC2(D_, G_, T_, B_, R_)                                                            \
-    if (g.d == D_ && G == G_ && TPC == T_ && g.qbits == B_ && rope == R_) {                    \
+    const bool rope = (g.flags & QEVICT_F_ROPE) != 0, fin = g.fuse != 0;
+#define QV_DEC3(D_, G_, T_, B_, R_, F_)                                                        \
+    if (g.d == D_ && G == G_ && TPC == T_ && g.qbits == B_ && rope == R_ && fin == F_) {       \
         if (ev0)                                                                               \
-            hipExtLaunchKernelGGL((k_decode_split<D_, G_, T_, B_, R_>), grid, block, 0, s, ev0, ev1, 0, g, bf, \
+            hipExtLaunchKernelGGL((k_decode_split<D_, G_, T_, B_, R_, F_>), grid, block, 0, s, ev0, ev1, 0, g, bf, \
                                   layer, q, k_new, v_new, out, score_now);                     \
         else                                                                                   \
-            hipLaunchKernelGGL((k_decode_split<D_, G_, T_, B_, R_>), grid, block, 0, s, g, bf, layer, q, k_new, \
+            hipLaunchKernelGGL((k_decode_split<D_, G_, T_, B_, R_, F_>), grid, block, 0, s, g, bf, layer, q, k_new, \
                                v_new, out, score_now);                                         \
         return hipGetLastError();                                                              \
     }
+#define QV_DEC2(D_, G_, T_, B_, R_) QV_DEC3(D_, G_, T_, B_, R_, false) QV_DEC3(D_, G_, T_, B_, R_, true)
 #define QV_DEC1(D_, G_, T_, B_) QV_DEC2(D_, G_, T_, B_, false) QV_DEC2(D_, G_, T_, B_, true)
 #define QV_DEC(D_, G_, T_) QV_DEC1(D_, G_, T_, 2) QV_DEC1(D_, G_, T_, 4)
     QV_DEC(128, 1, 2) QV_DEC(128, 2, 2) QV_DEC(128, 4, 2) QV_DEC(128, 8, 2)
@@ -1076,6 +1078,7 @@ hipError_t launch_decode(const Geo& g, const Bufs& bf, int layer, const uint16_t
 #undef QV_DEC
 #undef QV_DEC1
 #undef QV_DEC2
+#undef QV_DEC3
     return hipErrorInvalidValue;
 }
 
