@@ -287,14 +287,20 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     const bool cum_fold = fold && !rank_interval(g) && !(g.flags & QEVICT_F_RANK_KEYNORM);
     double* mwin = reinterpret_cast<double*>(sm.work);      // RT_MAXW doubles
     if (fold) {
-        for (int w = tid; w < RT_MAXW; w += RT_THREADS) mwin[w] = 0.0;
-        __syncthreads();
         const float* lwin = bf.lse_win + lse_win_off(g, u, (n - 1) & 1);   // the step at position n - 1
         const float* lg = bf.lse_glob + lse_glob_off(g, u, (n - 1) & 1);
         const int n_acc = hdr->n_acc;
-        for (int e = e_first; e < n_acc; e += RT_THREADS) {   // (entry 0: the sinks, no window)
-            const AccEntry en = e == e_first ? en_first : bf.acc[u * g.n_acc_max + e];
-            if (en.win >= 0 && en.win < NW) mwin[en.win] = entry_mass(lwin + (int64_t)e * g.h_q, lg, g.h_q) / g.h_q;
+        // (entry 0: the sinks, no window.)  The mass of an entry is computed whether or not it
+        // has a window, so that its row's loads need not wait for the entry; the first entry's
+        // loads are in flight while the table is cleared.
+        const double m_first = e_first < n_acc ? entry_mass(lwin + (int64_t)e_first * g.h_q, lg, g.h_q) / g.h_q : 0.0;
+        for (int w = tid; w < RT_MAXW; w += RT_THREADS) mwin[w] = 0.0;
+        __syncthreads();
+        if (e_first < n_acc && en_first.win >= 0 && en_first.win < NW) mwin[en_first.win] = m_first;
+        for (int e = e_first + RT_THREADS; e < n_acc; e += RT_THREADS) {
+            const AccEntry en = bf.acc[u * g.n_acc_max + e];
+            const double m = entry_mass(lwin + (int64_t)e * g.h_q, lg, g.h_q) / g.h_q;
+            if (en.win >= 0 && en.win < NW) mwin[en.win] = m;
         }
         __syncthreads();
         if (tid == 0) hdr->mass_pending = 0;
