@@ -92,3 +92,17 @@ def test_kernel_name_and_error_string():
     lib = _lib()
     assert lib.qevict_decode_kernel_name().decode().startswith("qevict_decode")
     assert isinstance(lib.qevict_last_error(), bytes)
+
+
+def test_timing_hooks_refuse_a_null_state():
+    lib = _lib()
+    for fn in (lib.qevict_time_next_decode, lib.qevict_time_next_route):
+        assert fn(None, None, None) == -1
+
+
+def test_plan_reports_single_launch_steps_at_one_split():
+    _lib()
+    wl = WL.CHURN_4K
+    assert B.plan(B.make_config(wl), wl.prompt_lens()).combine_in_kernel == 1       # B * h_kv = 512: one split
+    assert B.plan(B.make_config(WL.LLAMA8B_32K), [32768]).combine_in_kernel == 0
+    assert B.plan(B.make_config(wl, flags=B.QEVICT_F_SEPARATE_FINISH), wl.prompt_lens()).combine_in_kernel == 0

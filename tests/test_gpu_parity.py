@@ -50,6 +50,7 @@ def test_drift_with_promotions_and_splits():
     ex = ls.st.export_unit(0, 0)
     assert ex.counters["n_full"] == unit.events[-1]["n_full"]
     _print(f"drift: promotions {sum(e['promoted'] for e in unit.events)}, fills after a pack of their page {ex.counters['paired_fills']}")
+    assert ex.counters["paired_fills"] > 0
 
 
 def test_batched_ragged_prompts_gqa8_d128():
@@ -79,7 +80,9 @@ def test_single_launch_step_and_finish_launch(n_splits):
         _print(f"n_splits={n_splits} flags={flags}: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}")
         assert ls.st.poll_status() == 0
         assert sum(e["promoted"] for e in ls.units[0].events) + sum(e["promoted"] for e in ls.units[1].events) > 0
-        _print("fills after a pack of their page:", [ls.st.export_unit(0, b).counters["paired_fills"] for b in range(2)])
+        paired = [ls.st.export_unit(0, b).counters["paired_fills"] for b in range(2)]
+        _print("fills after a pack of their page:", paired)
+        assert sum(paired) > 0   # (a promotion took a page a pack of the same event read: that path ran)
 
 
 def test_window64_gqa8_multichunk():
@@ -189,6 +192,27 @@ def test_prefill_column_sums_mid_size():
     ref = np.array([unit.score[w] for w in range(ex.n_windows)])
     assert np.abs(ex.score[: ex.n_windows] - ref).max() < 1e-4
     assert abs(ex.score[: ex.n_windows].sum() + ex.sink_mass - 1536) < 1e-3
+
+
+def test_route_timing_events_stamp_the_routing_launches():
+    """qevict_time_next_route: the next routing call's kernels stamp a timing event pair (the
+    routing kernel's start, the migration kernel's end); then the events are forgotten."""
+    _print("case: route timing events")
+    ls = Lockstep(WL.TINY.with_(budget_frac=0.25)).run(8)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    torch.cuda.synchronize()
+    ls.st.time_next_route(e0, e1)
+    ls.st.route(-1)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3
+    _print(f"route event: {us:.1f} us")
+    assert 0.0 < us < 1e5
+    ls.st.route(-1)   # (not timed: the pair was forgotten)
+    torch.cuda.synchronize()
+    assert e0.elapsed_time(e1) * 1e3 == us
+    assert ls.st.poll_status() == 0
 
 
 def test_determinism_bitwise():
