@@ -194,6 +194,32 @@ def test_prefill_column_sums_mid_size():
     assert abs(ex.score[: ex.n_windows].sum() + ex.sink_mass - 1536) < 1e-3
 
 
+SINGLE_LAUNCH_CASES = {
+    # name: (workload, flags)
+    "int4": (WL.Workload("one_launch_int4", 1, 2, 16, 4, 64, 768, 32, 16, 4, 64, 8, 0.30, 0.70, prompt_len_min=600,
+                         n_outlier=2, n_topics=3, topic_period=12), B.QEVICT_F_INT4),
+    "rope": (WL.Workload("one_launch_rope", 1, 2, 16, 4, 64, 768, 32, 16, 4, 64, 8, 0.30, 0.70, prompt_len_min=600,
+                         n_outlier=2, n_topics=3, topic_period=12), B.QEVICT_F_ROPE),
+    "mha_d128": (WL.Workload("one_launch_mha", 1, 2, 4, 4, 128, 640, 32, 32, 4, 64, 8, 0.30, 0.70,
+                             n_topics=2, topic_period=8), 0),
+    "gqa8_d128_w64": (WL.Workload("one_launch_gqa8", 1, 3, 16, 2, 128, 900, 32, 64, 4, 64, 8, 0.30, 0.70,
+                                  prompt_len_min=500, n_topics=2, topic_period=8), 0),
+}
+
+
+@pytest.mark.parametrize("case", list(SINGLE_LAUNCH_CASES))
+def test_single_launch_step_variants(case):
+    """One split per (sequence, KV head): the split kernel finishes the step for the INT4 and
+    RoPE-faithful tiers and other head shapes, in lockstep with the oracle."""
+    wl, flags = SINGLE_LAUNCH_CASES[case]
+    _print(f"case: single launch {case}")
+    ls = Lockstep(wl, flags=flags, n_splits=1)
+    assert ls.st.info.combine_in_kernel == 1
+    ls.run(32)
+    _print(f"{case}: max o err {ls.max_o_err:.2e}, max score err {ls.max_s_err:.2e}, events {ls.events}")
+    assert ls.st.poll_status() == 0
+
+
 def test_route_timing_events_stamp_the_routing_launches():
     """qevict_time_next_route: the next routing call's kernels stamp a timing event pair (the
     routing kernel's start, the migration kernel's end); then the events are forgotten."""
