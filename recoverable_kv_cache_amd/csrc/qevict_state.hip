@@ -318,12 +318,11 @@ __device__ __forceinline__ int nearest_level(double t2, double scl, double inv, 
     return scl == 0.0 ? 0 : k;
 }
 
-// W, d, QB: the window, head dimension and code bits (one instance per supported shape, so
-// that the layout arithmetic is shifts and masks)
 // LDS of the migration kernel: a pack item's bf16 staging and parameters, or a fill item's
-// slot words (the two never hold data at the same time), and the work-list sums
-struct MigSmem {
-    union {
+// slot words (the two never hold data at the same time), and the work-list sums.  (The
+// staging takes 16-byte LDS stores: 16-byte alignment.)
+struct alignas(16) MigSmem {
+    union alignas(16) {
         struct {
             uint16_t sk[PK_MAXE];
             uint16_t sv[PK_MAXE];
@@ -338,6 +337,8 @@ struct MigSmem {
 };
 
 // One pack item: head h of window pi.win of unit u into slot pi.dst_slot.  All threads call.
+// W, d, QB: the window, head dimension and code bits (one instance per supported shape, so
+// that the layout arithmetic is shifts and masks)
 template <int W, int d, int QB>
 __device__ void pack_item(const Geo& g, const Bufs& bf, int64_t u, int b, const PackItem& pi, int h,
                           const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp, MigSmem& sm) {
