@@ -261,39 +261,54 @@ __global__ void __launch_bounds__(RT_THREADS) k_route(Geo g, Bufs bf, int layer,
     double* score = bf.score + u * g.n_windows;
     int8_t* target = bf.target + u * g.n_windows;
     const int NW = g.n_windows;
-    // Loads that depend on nothing read here go first, with the header, so that they share
+    // Loads that depend on nothing read here go first, with the header's, so that they share
     // one round trip: the accessible entry this thread folds first, and the window records
     // and rank keys of its windows w = tid + i * RT_THREADS (the rank keys again below when
-    // a ranker rewrites them in memory first).
+    // a ranker rewrites them in memory first).  Every load is unconditional, from a clamped
+    // index, and out-of-range values are replaced afterwards: a load under a per-thread
+    // condition would be waited for on the spot, one round trip each.
     const int e_first = 1 + tid;
     const AccEntry en_first = bf.acc[u * g.n_acc_max + (e_first < g.n_acc_max ? e_first : g.n_acc_max - 1)];
     WinRec rec[RT_PER];
     double sc[RT_PER];
 #pragma unroll
     for (int i = 0; i < RT_PER; ++i) {
-        const int w = tid + i * RT_THREADS;
-        rec[i] = w < NW ? win[w] : WinRec{ST_NONE, -1, -1, 0};
-        sc[i] = w < NW ? score[w] : 0.0;
+        const int w = tid + i * RT_THREADS, wc = w < NW ? w : NW - 1;
+        rec[i] = win[wc];
+        sc[i] = score[wc];
     }
-    const int n = hdr->n;
-    const int K_f = hdr->K_f, K_q = hdr->K_q;
+    const UnitHdr hd = *hdr;             // (one batch of scalar loads)
+    const int n = hd.n;
+    const int K_f = hd.K_f, K_q = hd.K_q;
+    const int n_acc_old = hd.n_acc;
+    const bool fold = hd.mass_pending != 0;
+#pragma unroll
+    for (int i = 0; i < RT_PER; ++i) {
+        const bool in = tid + i * RT_THREADS < NW;
+        rec[i].state = in ? rec[i].state : ST_NONE;
+        rec[i].page = in ? rec[i].page : -1;
+        rec[i].slot = in ? rec[i].slot : -1;
+        rec[i].flags = in ? rec[i].flags : 0;
+        sc[i] = in ? sc[i] : 0.0;
+    }
     int* flag = (int*)sm.work;               // (used after the tier selection)
 
     // ---- 0. the last decode step's window-mass shares (Eq. 1), folded before routing: one
     //         thread per accessible entry, the entry's mass to LDS by window.  With the
     //         cumulative ranker the sums join the rank keys as they are read (below);
     //         the other rankers take them in global memory first.
-    const bool fold = hdr->mass_pending != 0;
     const bool cum_fold = fold && !rank_interval(g) && !(g.flags & QEVICT_F_RANK_KEYNORM);
     double* mwin = reinterpret_cast<double*>(sm.work);      // RT_MAXW doubles
+    // (entry 0: the sinks, no window.)  The mass of an entry is computed whether or not it has
+    // a window (or a fold is pending), so that its row's loads wait for neither; the first
+    // entry's loads (from a clamped row, unconditional) are in flight while the table is cleared.
+    const float* lwin = bf.lse_win + lse_win_off(g, u, (n - 1) & 1);   // the step at position n - 1
+    const float* lg = bf.lse_glob + lse_glob_off(g, u, (n - 1) & 1);
+    const double m_row = entry_mass(lwin + (int64_t)(e_first < g.n_acc_max ? e_first : g.n_acc_max - 1) * g.h_q, lg,
+                                    g.h_q) / g.h_q;
     if (fold) {
-        const float* lwin = bf.lse_win + lse_win_off(g, u, (n - 1) & 1);   // the step at position n - 1
-        const float* lg = bf.lse_glob + lse_glob_off(g, u, (n - 1) & 1);
-        const int n_acc = hdr->n_acc;
-        // (entry 0: the sinks, no window.)  The mass of an entry is computed whether or not it
-        // has a window, so that its row's loads need not wait for the entry; the first entry's
-        // loads are in flight while the table is cleared.
-        const double m_first = e_first < n_acc ? entry_mass(lwin + (int64_t)e_first * g.h_q, lg, g.h_q) / g.h_q : 0.0;
+        const int n_acc = n_acc_old;
+        const double m_first = e_first < n_acc ? m_row : 0.0;
         for (int w = tid; w < RT_MAXW; w += RT_THREADS) mwin[w] = 0.0;
         __syncthreads();
         if (e_first < n_acc && en_first.win >= 0 && en_first.win < NW) mwin[en_first.win] = m_first;
